@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the GDN-2 forward and decode paths.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark.  It draws random numbers and shapes them into tensors; it holds none
+of the recurrence's arithmetic.
+
+Recipe (every workload):
+  * NumPy ``default_rng(seed)`` (PCG64), draws in float64, in the fixed order
+    q, k, v, alpha-logit, b-logit, w-logit, S0.
+  * q and k are L2-normalised per (token, head) in float64 before the cast:
+    the pages place this normalisation outside the recurrence (Gated DeltaNet-2
+    blog, aixai.ru, section "how it is implemented in practice").
+  * v ~ N(0, 1); alpha = sigmoid(N(3, 1)) per key channel; b = sigmoid(N(0, 1))
+    per key channel; w = sigmoid(N(0, 1)) per value channel; S0 ~ N(0, 0.1^2)
+    (standard deviation 0.1) when a nonzero initial state is asked for.
+  * The float64 draws are cast to the storage dtype with torch (bf16 is
+    round-to-nearest-even).  Consumers read the stored tensors back; nobody
+    uses the pre-rounding values.
+
+All tensors are returned on the CPU, token-major ``[B, T, H, d]``.  The state is
+``[N, H, dk, dv]`` float32 (key channel = row, value channel = column).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _l2norm(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, 1e-30)
+
+
+def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DTYPES[dtype]).contiguous()
+
+
+def packed_lengths(seed: int, total: int = 32768, lo: int = 256, hi: int = 8192) -> list[int]:
+    """Sequence lengths drawn uniformly from {lo..hi} until their sum reaches
+    ``total``; the last one is truncated so the sum is exactly ``total``."""
+    rng = np.random.default_rng(seed)
+    lens: list[int] = []
+    acc = 0
+    while acc < total:
+        n = int(rng.integers(lo, hi + 1))
+        n = min(n, total - acc)
+        lens.append(n)
+        acc += n
+    return lens
+
+
+def cu_seqlens_from(lengths: list[int]) -> torch.Tensor:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return torch.from_numpy(cu)
+
+
+def make_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                      s0: str | None = None, num_seqs: int | None = None,
+                      scalar_beta: bool = False) -> dict:
+    """Inputs of one chunked-forward call.
+
+    ``s0``: None (no initial state), "zero" (explicit zeros) or "normal"
+    (N(0, 0.1^2)).  ``num_seqs`` is the number of state slots (B for fixed
+    length, the sequence count for packed input).  ``scalar_beta`` replaces
+    b and w by one shared scalar beta = sigmoid(N(0,1)) per (batch, token,
+    head), broadcast over channels (the collapsed-gate case).
+    """
+    rng = np.random.default_rng(seed)
+    q = _l2norm(rng.standard_normal((B, T, H, dk)))
+    k = _l2norm(rng.standard_normal((B, T, H, dk)))
+    v = rng.standard_normal((B, T, H, dv))
+    alpha = _sigmoid(rng.normal(3.0, 1.0, (B, T, H, dk)))
+    if scalar_beta:
+        beta = _sigmoid(rng.standard_normal((B, T, H, 1)))
+        b = np.broadcast_to(beta, (B, T, H, dk))
+        w = np.broadcast_to(beta, (B, T, H, dv))
+    else:
+        b = _sigmoid(rng.standard_normal((B, T, H, dk)))
+        w = _sigmoid(rng.standard_normal((B, T, H, dv)))
+    n = B if num_seqs is None else num_seqs
+    out = {
+        "q": _cast(q, dtype), "k": _cast(k, dtype), "v": _cast(v, dtype),
+        "alpha": _cast(alpha, dtype), "b": _cast(b, dtype), "w": _cast(w, dtype),
+    }
+    if s0 is None:
+        out["S0"] = None
+    elif s0 == "zero":
+        out["S0"] = torch.zeros((n, H, dk, dv), dtype=torch.float32)
+    elif s0 == "normal":
+        out["S0"] = torch.from_numpy(rng.normal(0.0, 0.1, (n, H, dk, dv))).float().contiguous()
+    else:
+        raise ValueError(f"unknown s0 mode {s0!r}")
+    return out
+
+
+def make_decode_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                       steps: int) -> dict:
+    """``steps`` distinct single-token inputs ``[steps, N, H, d]`` plus a state
+    ``S ~ N(0, 0.1^2)`` of shape ``[N, H, dk, dv]`` float32."""
+    rng = np.random.default_rng(seed)
+    q = _l2norm(rng.standard_normal((steps, N, H, dk)))
+    k = _l2norm(rng.standard_normal((steps, N, H, dk)))
+    v = rng.standard_normal((steps, N, H, dv))
+    alpha = _sigmoid(rng.normal(3.0, 1.0, (steps, N, H, dk)))
+    b = _sigmoid(rng.standard_normal((steps, N, H, dk)))
+    w = _sigmoid(rng.standard_normal((steps, N, H, dv)))
+    S = rng.normal(0.0, 0.1, (N, H, dk, dv))
+    return {
+        "q": _cast(q, dtype), "k": _cast(k, dtype), "v": _cast(v, dtype),
+        "alpha": _cast(alpha, dtype), "b": _cast(b, dtype), "w": _cast(w, dtype),
+        "S": torch.from_numpy(S).float().contiguous(),
+    }
+
+
+# The five workloads (shapes, dtypes, seeds).  Config 3's packed lengths come
+# from ``packed_lengths(3)``; its sweep uses fixed-length batches with
+# B * T = 32768.
+CONFIGS = {
+    0: dict(B=1, H=1, T=64, dk=16, dv=16, chunk=16, dtype="f32", seed=0, s0="zero"),
+    1: dict(B=2, H=4, T=512, dk=64, dv=64, chunk=64, dtype="f32", seed=1, s0="normal"),
+    2: dict(B=8, H=16, T=4096, dk=128, dv=128, chunk=64, dtype="bf16", seed=2, s0=None),
+    3: dict(B=1, H=16, T=32768, dk=128, dv=128, chunk=64, dtype="bf16", seed=3, s0=None,
+            packed=True),
+    4: dict(N=256, H=16, dk=128, dv=128, dtype="bf16", seed=4, steps=16),
+}
+
+SWEEP_T = (2048, 4096, 8192, 16384, 32768)
