@@ -1,0 +1,165 @@
+"""Python binding of libgdn2, the MI355X (gfx950) forward hot path of the
+Gated DeltaNet-2 recurrence.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgdn2.so`` (built in-tree by ``gated_delta_rule_07_amd.build``).
+PyTorch provides device memory and the current HIP stream.  There is no CPU
+fallback: without the library or a GPU these functions raise.
+
+    o, S_final = chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk=64)
+    o = decode_step(q, k, v, alpha, b, w, S)      # S updated in place
+
+Shapes: q, k, alpha, b [B, T, H, dk]; v, w [B, T, H, dv] (packed sequences:
+B = 1 and ``cu_seqlens`` int32 [N + 1] on the device); states [N, H, dk, dv]
+float32.  Inputs are float32 or bfloat16 and must all have the same dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+
+GDN2_F32, GDN2_BF16 = 0, 1
+FLAG_RECURRENT = 1 << 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+_lib = None
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libgdn2: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libgdn2.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; run `python -m gated_delta_rule_07_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
+        L.gdn2_chunk_fwd_workspace_bytes.restype = sz
+        L.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
+        L.gdn2_chunk_fwd.restype = i
+        L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
+        L.gdn2_decode_step.restype = i
+        L.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
+        L.gdn2_status_string.restype = ctypes.c_char_p
+        L.gdn2_status_string.argtypes = [i]
+        L.gdn2_last_error.restype = ctypes.c_char_p
+        L.gdn2_last_error.argtypes = []
+        L.gdn2_abi_version.restype = i
+        L.gdn2_profile_enable.restype = i
+        L.gdn2_profile_enable.argtypes = [i]
+        L.gdn2_profile_read.restype = i
+        L.gdn2_profile_read.argtypes = [i, ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), i]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Gdn2Error(status, lib().gdn2_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GDN2_F32
+    if t.dtype == torch.bfloat16:
+        return GDN2_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _require_device(*ts) -> None:
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("libgdn2 takes contiguous device tensors")
+
+
+def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chunk: int,
+                    dtype: torch.dtype) -> int:
+    code = GDN2_BF16 if dtype == torch.bfloat16 else GDN2_F32
+    return int(lib().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, chunk, code))
+
+
+def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
+              recurrent: bool = False, out=None, S_final=None, workspace=None,
+              want_final: bool = True):
+    """Chunked forward (or the token-recurrent kernel when ``recurrent``).
+    Returns (o, S_final); S_final is None when ``want_final`` is False."""
+    _require_device(q, k, v, alpha, b, w, S0, cu_seqlens)
+    dt = _dtype_code(q)
+    for t in (k, v, alpha, b, w):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, alpha, b, w must share one dtype")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (N, H, dk, dv)):
+        raise ValueError(f"S0 must be float32 [{N}, {H}, {dk}, {dv}]")
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    Sf = S_final
+    if Sf is None and want_final:
+        Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    flags = FLAG_RECURRENT if recurrent else 0
+    ws_bytes = 0
+    if not recurrent:
+        ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel()
+    _check(lib().gdn2_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, dt, flags,
+        _ptr(o), _ptr(Sf), _ptr(workspace), ws_bytes, _stream()))
+    return o, Sf
+
+
+def decode_step(q, k, v, alpha, b, w, S, out=None):
+    """One decode step: inputs [N, H, d]; S [N, H, dk, dv] float32, updated in place."""
+    _require_device(q, k, v, alpha, b, w, S)
+    dt = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError(f"S must be float32 [{N}, {H}, {dk}, {dv}]")
+    o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _check(lib().gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                  _ptr(S), _ptr(o), N, H, dk, dv, dt, _stream()))
+    return o
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib().gdn2_profile_enable(1 if on else 0))
+
+
+def profile_read(reset: bool = True) -> dict:
+    """{kernel name: (total ms, launches)} since the last reset."""
+    n = ctypes.c_int(0)
+    cap = 16
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int * cap)()
+    _check(lib().gdn2_profile_read(cap, names, ms, cnt, ctypes.byref(n), 1 if reset else 0))
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(n.value, cap))}

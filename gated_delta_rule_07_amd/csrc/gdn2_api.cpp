@@ -1,0 +1,400 @@
+// gdn2_api.cpp -- the C ABI of libgdn2 (include/gdn2.h): argument checks,
+// workspace planning, kernel selection and launches on the caller's stream.
+// No memory is allocated and the stream is never synchronised.
+#include "../../include/gdn2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "gdn2_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn2_status_t fail(gdn2_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gdn2_status_t ok() {
+  g_last_error.clear();
+  return GDN2_OK;
+}
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 64; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ------------------------------------------------------------- profiling --
+// Kernel names are string literals of this file, so the pointers handed out
+// by gdn2_profile_read stay valid for the life of the library.
+struct prof_rec {
+  const char *name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<prof_rec> g_prof_pending;
+std::vector<std::pair<const char *, std::pair<double, int>>> g_prof_total;
+
+struct prof_scope {
+  hipStream_t st;
+  bool on;
+  prof_rec rec;
+  prof_scope(const char *name, hipStream_t s) : st(s), on(false) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on)
+      return;
+    if (hipEventCreate(&rec.start) != hipSuccess)
+      return;
+    if (hipEventCreate(&rec.stop) != hipSuccess) {
+      (void)hipEventDestroy(rec.start);
+      return;
+    }
+    rec.name = name;
+    on = hipEventRecord(rec.start, st) == hipSuccess;
+    if (!on) {
+      (void)hipEventDestroy(rec.start);
+      (void)hipEventDestroy(rec.stop);
+    }
+  }
+  ~prof_scope() {
+    if (!on)
+      return;
+    (void)hipEventRecord(rec.stop, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending.push_back(rec);
+  }
+};
+
+// --------------------------------------------------------------- dispatch --
+template <typename IO, int D, int C> size_t block_bytes() { return gdn2::chunk_block_bytes<IO, D, C>(); }
+
+size_t chunk_block_bytes_rt(gdn2_dtype_t dt, int d, int c) {
+#define GDN2_BB(IO, D, C) \
+  if (d == D && c == C)   \
+    return block_bytes<IO, D, C>();
+  if (dt == GDN2_F32) {
+    GDN2_BB(float, 16, 16) GDN2_BB(float, 32, 16) GDN2_BB(float, 64, 16) GDN2_BB(float, 128, 16)
+    GDN2_BB(float, 16, 64) GDN2_BB(float, 32, 64) GDN2_BB(float, 64, 64) GDN2_BB(float, 128, 64)
+  } else {
+    GDN2_BB(gdn2::bf16_t, 16, 16) GDN2_BB(gdn2::bf16_t, 32, 16) GDN2_BB(gdn2::bf16_t, 64, 16)
+    GDN2_BB(gdn2::bf16_t, 128, 16) GDN2_BB(gdn2::bf16_t, 16, 64) GDN2_BB(gdn2::bf16_t, 32, 64)
+    GDN2_BB(gdn2::bf16_t, 64, 64) GDN2_BB(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_BB
+  return 0;
+}
+
+template <typename IO, int D, int C>
+hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (a.cu) {
+    prof_scope p("chunk_table", st);
+    e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("chunk_prep", st);
+    e = gdn2::launch_chunk_prep<IO, D, C>(a, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("chunk_scan", st);
+    e = gdn2::launch_chunk_scan<IO, D, C>(a, st);
+  }
+  return e;
+}
+
+hipError_t dispatch_chunk(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, hipStream_t st) {
+#define GDN2_RC(IO, D, C) \
+  if (d == D && c == C)   \
+    return run_chunk<IO, D, C>(a, C, st);
+  if (dt == GDN2_F32) {
+    GDN2_RC(float, 16, 16) GDN2_RC(float, 32, 16) GDN2_RC(float, 64, 16) GDN2_RC(float, 128, 16)
+    GDN2_RC(float, 16, 64) GDN2_RC(float, 32, 64) GDN2_RC(float, 64, 64) GDN2_RC(float, 128, 64)
+  } else {
+    GDN2_RC(gdn2::bf16_t, 16, 16) GDN2_RC(gdn2::bf16_t, 32, 16) GDN2_RC(gdn2::bf16_t, 64, 16)
+    GDN2_RC(gdn2::bf16_t, 128, 16) GDN2_RC(gdn2::bf16_t, 16, 64) GDN2_RC(gdn2::bf16_t, 32, 64)
+    GDN2_RC(gdn2::bf16_t, 64, 64) GDN2_RC(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_RC
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_recurrent(gdn2_dtype_t dt, int d, const void *q, const void *k, const void *v,
+                              const void *al, const void *b, const void *w, const float *S0,
+                              const int32_t *cu, int T, int H, int N, void *o, float *Sf,
+                              hipStream_t st) {
+  prof_scope p("recurrent", st);
+#define GDN2_RR(IO, D) \
+  if (d == D)          \
+    return gdn2::launch_recurrent<IO, D>(q, k, v, al, b, w, S0, cu, T, H, N, o, Sf, st);
+  if (dt == GDN2_F32) {
+    GDN2_RR(float, 16) GDN2_RR(float, 32) GDN2_RR(float, 64) GDN2_RR(float, 128)
+  } else {
+    GDN2_RR(gdn2::bf16_t, 16) GDN2_RR(gdn2::bf16_t, 32) GDN2_RR(gdn2::bf16_t, 64)
+    GDN2_RR(gdn2::bf16_t, 128)
+  }
+#undef GDN2_RR
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_decode(gdn2_dtype_t dt, int d, const void *q, const void *k, const void *v,
+                           const void *al, const void *b, const void *w, float *S, void *o, int N,
+                           int H, hipStream_t st) {
+  prof_scope p("decode", st);
+#define GDN2_DD(IO, D) \
+  if (d == D)          \
+    return gdn2::launch_decode<IO, D>(q, k, v, al, b, w, S, o, N, H, st);
+  if (dt == GDN2_F32) {
+    GDN2_DD(float, 16) GDN2_DD(float, 32) GDN2_DD(float, 64) GDN2_DD(float, 128)
+  } else {
+    GDN2_DD(gdn2::bf16_t, 16) GDN2_DD(gdn2::bf16_t, 32) GDN2_DD(gdn2::bf16_t, 64)
+    GDN2_DD(gdn2::bf16_t, 128)
+  }
+#undef GDN2_DD
+  return hipErrorInvalidValue;
+}
+
+int num_slots_for(int B, int T, int num_seqs, int chunk, bool packed) {
+  if (packed)
+    return (T + chunk - 1) / chunk + num_seqs;  // upper bound: sum of ceil(len/C)
+  return B * ((T + chunk - 1) / chunk);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
+                                      gdn2_dtype_t dt) {
+  if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
+    return 0;
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return 0;
+  // num_seqs > 0 asks for packed input (B must then be 1); the bound returned
+  // covers both the packed and the fixed-length layout of these sizes.
+  const int n = num_seqs > 0 ? num_seqs : B;
+  const size_t slots_fixed = static_cast<size_t>(num_slots_for(B, T, B, chunk, false));
+  const size_t slots_packed = static_cast<size_t>(num_slots_for(B, T, n, chunk, true));
+  const size_t slots = slots_packed > slots_fixed ? slots_packed : slots_fixed;
+  const size_t table = align256(static_cast<size_t>(n + 1) * sizeof(int32_t));
+  return table + slots * static_cast<size_t>(H) * chunk_block_bytes_rt(dt, dk, chunk);
+}
+
+gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
+                             const void *b, const void *w, const float *S0,
+                             const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                             int num_seqs, int chunk, gdn2_dtype_t dt, uint32_t flags, void *o,
+                             float *S_final, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unknown dtype %d", static_cast<int>(dt));
+  if (flags & ~static_cast<uint32_t>(GDN2_FLAG_RECURRENT))
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: unknown flags 0x%x", flags);
+  if (B <= 0 || T < 0 || H <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: bad sizes B=%d T=%d H=%d", B, T, H);
+  if (dk != dv || !supported_dim(dk))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
+                dk, dv);
+  if (!supported_chunk(chunk))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unsupported chunk %d (need 16 or 64)", chunk);
+  const bool packed = cu_seqlens != nullptr;
+  int N;
+  if (packed) {
+    if (B != 1)
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: packed input needs B == 1 (got %d)", B);
+    if (num_seqs <= 0)
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: packed input needs num_seqs > 0");
+    N = num_seqs;
+  } else {
+    if (num_seqs != 0 && num_seqs != B)
+      return fail(GDN2_ERR_INVALID_ARGUMENT,
+                  "gdn2_chunk_fwd: num_seqs=%d must be 0 or B=%d without cu_seqlens", num_seqs, B);
+    N = B;
+  }
+  if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !o))
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: null input or output pointer");
+  const void *ptrs[] = {q, k, v, alpha, b, w, S0, o, S_final, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p))
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: pointers must be 16-byte aligned");
+  const long long elems = static_cast<long long>(B) * T * H * dk;
+  if (elems > (1LL << 40))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: problem too large");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (flags & GDN2_FLAG_RECURRENT) {
+    const hipError_t e = dispatch_recurrent(dt, dk, q, k, v, alpha, b, w, S0, cu_seqlens, T, H, N,
+                                            o, S_final, st);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+
+  const size_t need_exact = [&] {
+    const size_t table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
+    return table + static_cast<size_t>(num_slots_for(B, T, N, chunk, packed)) * H *
+                       chunk_block_bytes_rt(dt, dk, chunk);
+  }();
+  if (workspace_bytes < need_exact || (need_exact > 0 && !workspace))
+    return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                "gdn2_chunk_fwd: workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need_exact);
+
+  gdn2::chunk_args a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.al = alpha;
+  a.b = b;
+  a.w = w;
+  a.S0 = S0;
+  a.cu = cu_seqlens;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.num_seqs = N;
+  a.num_slots = num_slots_for(B, T, N, chunk, packed);
+  a.o = o;
+  a.S_final = S_final;
+  a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
+  char *ws = static_cast<char *>(workspace);
+  if (packed) {
+    a.offsets = reinterpret_cast<int32_t *>(ws);
+    a.blocks = ws + align256(static_cast<size_t>(N + 1) * sizeof(int32_t));
+  } else {
+    a.offsets = nullptr;
+    a.blocks = ws;
+  }
+  if (T == 0) {
+    // no tokens: the scan kernel alone copies S0 (or zeros) to S_final
+    a.num_slots = 0;
+  }
+  const hipError_t e = dispatch_chunk(dt, dk, chunk, a, st);
+  if (e != hipSuccess)
+    return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gdn2_status_t gdn2_decode_step(const void *q, const void *k, const void *v, const void *alpha,
+                               const void *b, const void *w, float *S, void *o, int N, int H,
+                               int dk, int dv, gdn2_dtype_t dt, void *stream) {
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_decode_step: unknown dtype %d", static_cast<int>(dt));
+  if (N <= 0 || H <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: bad sizes N=%d H=%d", N, H);
+  if (dk != dv || !supported_dim(dk))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_decode_step: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
+                dk, dv);
+  if (!q || !k || !v || !alpha || !b || !w || !S || !o)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: null pointer");
+  const void *ptrs[] = {q, k, v, alpha, b, w, S, o};
+  for (const void *p : ptrs)
+    if (!aligned16(p))
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: pointers must be 16-byte aligned");
+  if (static_cast<long long>(N) * H > (1LL << 31) - 1)
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_decode_step: too many sequence-heads");
+  const hipError_t e = dispatch_decode(dt, dk, q, k, v, alpha, b, w, S, o, N, H,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(GDN2_ERR_HIP, "gdn2_decode_step: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char *gdn2_status_string(gdn2_status_t status) {
+  switch (status) {
+  case GDN2_OK:
+    return "ok";
+  case GDN2_ERR_INVALID_ARGUMENT:
+    return "invalid argument";
+  case GDN2_ERR_UNSUPPORTED:
+    return "unsupported";
+  case GDN2_ERR_WORKSPACE_TOO_SMALL:
+    return "workspace too small";
+  case GDN2_ERR_HIP:
+    return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *gdn2_last_error(void) { return g_last_error.c_str(); }
+
+int gdn2_abi_version(void) { return GDN2_ABI_VERSION; }
+
+gdn2_status_t gdn2_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return ok();
+}
+
+gdn2_status_t gdn2_profile_read(int max_kernels, const char **names, double *total_ms, int *counts,
+                                int *n_kernels, int reset) {
+  std::vector<prof_rec> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    pend.swap(g_prof_pending);
+  }
+  for (prof_rec &r : pend) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess)
+      e = hipEventElapsedTime(&ms, r.start, r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_profile_read: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    bool found = false;
+    for (auto &kv : g_prof_total) {
+      if (kv.first == r.name) {
+        kv.second.first += ms;
+        kv.second.second += 1;
+        found = true;
+        break;
+      }
+    }
+    if (!found)
+      g_prof_total.push_back({r.name, {static_cast<double>(ms), 1}});
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int n = 0;
+  for (auto &kv : g_prof_total) {
+    if (n < max_kernels) {
+      if (names)
+        names[n] = kv.first;
+      if (total_ms)
+        total_ms[n] = kv.second.first;
+      if (counts)
+        counts[n] = kv.second.second;
+    }
+    ++n;
+  }
+  if (n_kernels)
+    *n_kernels = n;
+  if (reset)
+    g_prof_total.clear();
+  return ok();
+}
+
+}  // extern "C"

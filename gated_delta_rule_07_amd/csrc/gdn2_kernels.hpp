@@ -1,0 +1,43 @@
+// gdn2_kernels.hpp -- host-side declarations of the libgdn2 kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// Everything the chunked forward's kernels need.  All pointers are device
+// pointers.  The workspace holds, for packed input, the per-sequence chunk
+// offsets (offsets[n] = index of sequence n's first chunk, offsets[N] = total
+// chunk count) followed by one block of per-chunk intermediates for every
+// (chunk slot, head).
+struct chunk_args {
+  const void *q, *k, *v, *al, *b, *w;
+  const float *S0;
+  const int32_t *cu;  // packed sequence starts [N+1] or nullptr
+  int32_t *offsets;   // [N+1] in the workspace (packed input only)
+  int B, T, H, num_seqs, num_slots;
+  void *o;
+  float *S_final;
+  char *blocks;      // num_slots * H blocks of blk_bytes each
+  size_t blk_bytes;
+};
+
+template <typename IO, int D, int C> size_t chunk_block_bytes();
+template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st);
+template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st);
+hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st);
+
+template <typename IO, int D>
+hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,
+                         const void *b, const void *w, float *S, void *o, int N, int H,
+                         hipStream_t st);
+template <typename IO, int D>
+hipError_t launch_recurrent(const void *q, const void *k, const void *v, const void *al,
+                            const void *b, const void *w, const float *S0, const int32_t *cu,
+                            int T, int H, int num_seqs, void *o, float *S_final, hipStream_t st);
+
+}  // namespace gdn2

@@ -1,0 +1,139 @@
+/*
+ * gdn2.h -- C ABI of libgdn2, the MI355X (gfx950) forward hot path of the
+ * Gated DeltaNet-2 (GDN-2) sequence-mixing recurrence.
+ *
+ * The operation (one head; state S is dk x dv float32, row i = key channel,
+ * column j = value channel).  For every token t, in order:
+ *
+ *   D   = Diag(alpha_t) S          per-key-channel decay, applied first
+ *   z   = w_t (.) v_t - D^T (b_t (.) k_t)
+ *   S   = D + k_t z^T
+ *   o_t = S^T q_t                  (read after the update, no 1/sqrt(dk))
+ *
+ * Sources: the formal paragraph of the aixai.ru blog ("Gated DeltaNet-2",
+ * section on why one scalar cannot serve both decisions: decay first, the
+ * erase gate b weights the key coordinates used for the read, the write gate
+ * w weights the candidate value); aiexpert.news/pt (method paragraph: b_t in
+ * [0,1]^dk on the key axis, w_t in [0,1]^dv on the value axis, per-channel
+ * decay kept from KDA, exact reduction to KDA when b and w collapse to one
+ * scalar); aixai.ru, implementation section (chunkwise parallel form, q and k
+ * L2-normalised outside the kernel).  The pages print no formula; the rule
+ * above is the plainest reading that reduces to KDA, Gated DeltaNet and
+ * DeltaNet exactly.  No gate is clamped: b in [0,2] is accepted (aixai.ru,
+ * ablation section).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *     token-major: q, k, alpha, b are [B, T, H, dk]; v, w, o are [B, T, H, dv].
+ *     With packed sequences (cu_seqlens != NULL) B must be 1 and T is the total
+ *     token count.  States are [N, H, dk, dv] float32 (row-major dk x dv per
+ *     head).  Pointers must be 16-byte aligned.
+ *   - The element type of q, k, v, alpha, b, w and o is given by `dt`
+ *     (float32 or bfloat16); arithmetic is float32 and states are float32.
+ *     bfloat16 outputs are rounded to nearest even.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every kernel is enqueued on it; the library never synchronises it and
+ *     allocates no memory.
+ *   - Errors that the host can detect (null pointer, unsupported size or
+ *     dtype, workspace too small, inconsistent sizes) are returned before any
+ *     launch, with a message in gdn2_last_error().  A failed launch returns
+ *     GDN2_ERR_HIP.  Conditions only the device could see (a non-monotone
+ *     cu_seqlens, NaN/Inf inputs) are not detected: NaN propagates to the
+ *     outputs of its sequence and head.
+ *   - Supported sizes: dk == dv in {16, 32, 64, 128}; chunk in {16, 64}.
+ *   - Numerical domain of the chunked path: the per-channel decay accumulated
+ *     over any 16 consecutive tokens (aligned to 16 within a chunk) must stay
+ *     above about 2^-120, i.e. the product of those 16 alphas; beyond that the
+ *     factorised decay overflows float32.  The recurrent path has no such
+ *     limit.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN2_ABI_VERSION 1
+
+typedef enum {
+    GDN2_OK = 0,
+    GDN2_ERR_INVALID_ARGUMENT = 1,
+    GDN2_ERR_UNSUPPORTED = 2,
+    GDN2_ERR_WORKSPACE_TOO_SMALL = 3,
+    GDN2_ERR_HIP = 4
+} gdn2_status_t;
+
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
+
+/* flags of gdn2_chunk_fwd */
+#define GDN2_FLAG_RECURRENT (1u << 1) /* token-by-token kernel instead of the
+                                         chunked kernels (cross-check path) */
+
+/* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
+ * the sizes are unsupported).  With cu_seqlens, pass the packed total T and
+ * the sequence count num_seqs; without, num_seqs is ignored (it is B). */
+size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk, gdn2_dtype_t dt);
+
+/* Chunkwise-parallel forward over whole sequences (aixai.ru blog, section on
+ * how it is implemented in practice: chunks with matrix products inside,
+ * in-chunk auxiliary WY matrices; aiexpert.news/pt: chunkwise WY algorithm
+ * with the decay absorbed into the erase factors).
+ *   q, k, v, alpha, b, w : inputs (see conventions).
+ *   S0        : initial states [N, H, dk, dv] float32, or NULL for zeros.
+ *   cu_seqlens: device int32 [N + 1] with cu_seqlens[0] = 0 and
+ *               cu_seqlens[N] = T (packed sequences, B = 1), or NULL for B
+ *               sequences of length T (then N = B).  Chunks restart at every
+ *               sequence boundary.
+ *   B, T, H, dk, dv, num_seqs, chunk, dt : sizes; chunk is the chunk length.
+ *   flags     : 0 or GDN2_FLAG_RECURRENT.
+ *   o         : output [B, T, H, dv], element type dt.
+ *   S_final   : final states [N, H, dk, dv] float32, or NULL.  May alias S0.
+ *   workspace : device scratch of at least
+ *               gdn2_chunk_fwd_workspace_bytes(...) bytes (NULL allowed when
+ *               that is 0).  Its contents on entry are irrelevant.
+ * T == 0 is allowed: nothing but S_final = S0 (or zeros) is written. */
+gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
+                             const void *b, const void *w, const float *S0,
+                             const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                             int num_seqs, int chunk, gdn2_dtype_t dt, uint32_t flags, void *o,
+                             float *S_final, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* One recurrent decode step for N sequences x H heads at constant memory
+ * (aixai.ru blog: constant-memory decoding; needhelp.icu/de, section on the
+ * attention bottleneck).  q, k, alpha, b are [N, H, dk]; v, w, o are
+ * [N, H, dv] (element type dt); S is [N, H, dk, dv] float32 and is updated
+ * in place.  o may not alias any input. */
+gdn2_status_t gdn2_decode_step(const void *q, const void *k, const void *v, const void *alpha,
+                               const void *b, const void *w, float *S, void *o, int N, int H,
+                               int dk, int dv, gdn2_dtype_t dt, void *stream);
+
+/* Static text of a status code. */
+const char *gdn2_status_string(gdn2_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *gdn2_last_error(void);
+
+/* GDN2_ABI_VERSION of the loaded library. */
+int gdn2_abi_version(void);
+
+/* Kernel timing for benchmarks.  While enabled, every kernel launch made by
+ * gdn2_chunk_fwd / gdn2_decode_step is bracketed by two HIP events recorded
+ * on the launch stream.  gdn2_profile_read synchronises those events and
+ * returns, per kernel name, the summed time in milliseconds and the launch
+ * count; reset != 0 clears the record.  Enabling creates events (not device
+ * memory); it is not for use under graph capture. */
+gdn2_status_t gdn2_profile_enable(int on);
+gdn2_status_t gdn2_profile_read(int max_kernels, const char **names, double *total_ms,
+                                int *counts, int *n_kernels, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

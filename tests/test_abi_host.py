@@ -1,0 +1,100 @@
+"""Host-side checks of libgdn2 that need no GPU: the library loads, exports
+every function include/gdn2.h declares, and rejects bad arguments with the
+documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import gated_delta_rule_07_amd as g
+    if not os.path.exists(g.LIB_PATH):
+        pytest.fail("libgdn2.so is not built (run __graft_entry__.build())")
+    return g.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gdn2.h but not exported"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.gdn2_abi_version() == 1
+    assert L.gdn2_status_string(0) == b"ok"
+    assert L.gdn2_status_string(3) == b"workspace too small"
+    assert L.gdn2_status_string(99) == b"unknown status"
+
+
+F32, BF16 = 0, 1
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case fails validation first
+
+
+def call_fwd(L, *, ptr=FAKE, B=1, T=64, H=1, dk=16, dv=16, N=0, chunk=16, dt=F32, flags=0,
+             cu=None, ws=FAKE, ws_bytes=1 << 40, S0=None, q=None):
+    p = ptr
+    return L.gdn2_chunk_fwd(q if q is not None else p, p, p, p, p, p, S0, cu, B, T, H, dk, dv, N,
+                            chunk, dt, flags, p, None, ws, ws_bytes, None)
+
+
+def test_fwd_rejects_before_launch(L):
+    assert call_fwd(L, dk=24, dv=24) == 2
+    assert call_fwd(L, dk=64, dv=32) == 2
+    assert call_fwd(L, chunk=32) == 2
+    assert call_fwd(L, dt=7) == 2
+    assert call_fwd(L, B=0) == 1
+    assert call_fwd(L, T=-1) == 1
+    assert call_fwd(L, flags=1 << 7) == 1
+    assert call_fwd(L, ptr=0) == 1
+    assert call_fwd(L, q=FAKE + 4) == 1                       # misaligned
+    assert call_fwd(L, N=3) == 1                              # num_seqs without cu_seqlens
+    assert call_fwd(L, cu=FAKE, B=2, N=2) == 1                # packed needs B == 1
+    assert call_fwd(L, cu=FAKE, N=0) == 1                     # packed needs num_seqs
+    assert call_fwd(L, ws_bytes=100) == 3
+    assert b"workspace" in L.gdn2_last_error()
+    assert call_fwd(L, ws=0) == 3
+
+
+def test_workspace_bytes(L):
+    f = L.gdn2_chunk_fwd_workspace_bytes
+    # config 2: 8 x 64 chunks x 16 heads of bf16 intermediates, plus the table
+    w = f(8, 4096, 16, 128, 128, 0, 64, BF16)
+    assert 8 * 64 * 16 * 80 * 1024 <= w <= 8 * 64 * 16 * 82 * 1024 + 4096
+    assert f(8, 4096, 16, 128, 64, 0, 64, BF16) == 0
+    assert f(1, 100, 2, 64, 64, 5, 16, F32) >= f(1, 100, 2, 64, 64, 0, 16, F32)
+
+
+def test_decode_rejects_before_launch(L):
+    p = FAKE
+    assert L.gdn2_decode_step(p, p, p, p, p, p, p, p, 4, 2, 16, 16, 5, None) == 2
+    assert L.gdn2_decode_step(p, p, p, p, p, p, p, p, 0, 2, 16, 16, 0, None) == 1
+    assert L.gdn2_decode_step(p, p, p, p, p, p, None, p, 4, 2, 16, 16, 0, None) == 1
+    assert L.gdn2_decode_step(p, p, p, p, p, p, p, p, 4, 2, 48, 48, 0, None) == 2
+
+
+def test_profile_read_empty(L):
+    n = ctypes.c_int(-1)
+    assert L.gdn2_profile_read(0, None, None, None, ctypes.byref(n), 1) == 0
+    assert n.value == 0
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "gdn2.h"\nint main(void){ return gdn2_abi_version() == 0; }\n')
+    import subprocess
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -1,0 +1,284 @@
+"""GPU parity of libgdn2 against the float64 CPU oracle (MI355X only).
+
+Every case runs the HIP kernels through the C ABI (via the thin Python
+binding) on seeded synthetic inputs and compares element by element with the
+oracle on the same stored inputs.  Tolerances (max |x - ref| / max |ref| per
+tensor): 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs, for o and
+S_final separately.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn2_inputs as gi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("q", "k", "v", "alpha", "b", "w")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_07_amd as mod
+    mod.lib()
+    return mod
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def to_dev(inp):
+    return {kk: (vv.cuda() if isinstance(vv, torch.Tensor) else vv) for kk, vv in inp.items()}
+
+
+def gpu_fwd(g, inp, chunk, cu=None, recurrent=False, S0=None):
+    d = to_dev(inp)
+    o, Sf = g.chunk_fwd(*(d[n] for n in NAMES), S0=(S0.cuda() if S0 is not None else d.get("S0")),
+                        cu_seqlens=None if cu is None else cu.cuda(), chunk=chunk, recurrent=recurrent)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), Sf.cpu().numpy()
+
+
+def check(o, Sf, o_ref, S_ref, tol, label=""):
+    eo, es = rel_err(o, o_ref), rel_err(Sf, S_ref)
+    print(f"{label} err_o={eo:.3e} err_S={es:.3e}", flush=True)
+    assert eo <= tol, f"{label}: o error {eo:.3e} > {tol}"
+    assert es <= tol, f"{label}: S_final error {es:.3e} > {tol}"
+
+
+def make(cfg, **over):
+    c = dict(gi.CONFIGS[cfg])
+    c.update(over)
+    return c, gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"], c["seed"],
+                                   s0=c["s0"])
+
+
+# ------------------------------------------------------------ small configs
+@pytest.mark.parametrize("recurrent", [False, True])
+def test_config0(g, recurrent):
+    c, inp = make(0)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    for s0 in (inp["S0"], None):  # explicit zeros and NULL
+        inp2 = dict(inp, S0=s0)
+        o, Sf = gpu_fwd(g, inp2, c["chunk"], recurrent=recurrent)
+        check(o, Sf, o_ref, S_ref, TOL["f32"], f"cfg0 rec={recurrent} s0={'zeros' if s0 is not None else 'NULL'}")
+
+
+@pytest.mark.parametrize("recurrent", [False, True])
+def test_config1(g, recurrent):
+    c, inp = make(1)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, inp, c["chunk"], recurrent=recurrent)
+    check(o, Sf, o_ref, S_ref, TOL["f32"], f"cfg1 rec={recurrent}")
+
+
+def test_config1b_collapsed_gates(g):
+    """b = w = beta (KDA case): the GPU matches the oracle, which is pinned to
+    textbook KDA on the CPU."""
+    c = gi.CONFIGS[1]
+    inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], "f32", c["seed"],
+                               s0="normal", scalar_beta=True)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, inp, 64)
+    check(o, Sf, o_ref, S_ref, TOL["f32"], "cfg1b")
+
+
+@pytest.mark.parametrize("dtype,d,chunk,T", [("bf16", 128, 64, 200), ("bf16", 64, 16, 77),
+                                               ("f32", 128, 64, 130), ("f32", 32, 64, 64),
+                                               ("bf16", 16, 16, 33), ("f32", 64, 16, 1)])
+def test_ragged_shapes(g, dtype, d, chunk, T):
+    inp = gi.make_chunk_inputs(2, T, 3, d, d, dtype, seed=100 + T, s0="normal")
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, inp, chunk)
+    check(o, Sf, o_ref, S_ref, TOL[dtype], f"ragged {dtype} d={d} C={chunk} T={T}")
+
+
+def test_chunk_size_invariance(g):
+    inp = gi.make_chunk_inputs(1, 256, 2, 64, 64, "f32", seed=7, s0="normal")
+    o16, S16 = gpu_fwd(g, inp, 16)
+    o64, S64 = gpu_fwd(g, inp, 64)
+    orec, Srec = gpu_fwd(g, inp, 64, recurrent=True)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    for o, S, lab in ((o16, S16, "C16"), (o64, S64, "C64"), (orec, Srec, "rec")):
+        check(o, S, o_ref, S_ref, TOL["f32"], lab)
+
+
+def test_erase_gate_up_to_two(g):
+    """b in [0, 2] (the extended erase range): nothing is clamped."""
+    inp = gi.make_chunk_inputs(1, 128, 2, 64, 64, "f32", seed=8, s0="normal")
+    inp["b"] = (inp["b"] * 2.0).contiguous()
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, inp, 64)
+    check(o, Sf, o_ref, S_ref, TOL["f32"], "b*2")
+
+
+# ----------------------------------------------------------- packed input
+def test_packed_small_with_empty_sequences(g):
+    lens = [70, 0, 1, 64, 130, 0, 15]
+    cu = gi.cu_seqlens_from(lens)
+    T = int(cu[-1])
+    inp = gi.make_chunk_inputs(1, T, 2, 64, 64, "f32", seed=9, s0="normal", num_seqs=len(lens))
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], cu_seqlens=cu)
+    for chunk in (16, 64):
+        o, Sf = gpu_fwd(g, inp, chunk, cu=cu)
+        check(o, Sf, o_ref, S_ref, TOL["f32"], f"packed C={chunk}")
+    o, Sf = gpu_fwd(g, inp, 64, cu=cu, recurrent=True)
+    check(o, Sf, o_ref, S_ref, TOL["f32"], "packed rec")
+
+
+def test_config3_packed_sampled(g):
+    """Config 3: 32768 packed tokens, H=16, d=128, bf16.  The oracle checks
+    every head of two sequences (the shortest and the last one)."""
+    lens = gi.packed_lengths(3)
+    cu = gi.cu_seqlens_from(lens)
+    c = gi.CONFIGS[3]
+    inp = gi.make_chunk_inputs(1, c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], s0=None,
+                               num_seqs=len(lens))
+    o, Sf = gpu_fwd(g, inp, 64, cu=cu)
+    picks = sorted({int(np.argmin(lens)), len(lens) - 1})
+    for n in picks:
+        a, bnd = int(cu[n]), int(cu[n + 1])
+        sub = {x: inp[x][:, a:bnd] for x in NAMES}
+        o_ref, S_ref = oracle.fwd(*(sub[x] for x in NAMES))
+        check(o[:, a:bnd], Sf[n:n + 1], o_ref, S_ref, TOL["bf16"], f"cfg3 seq{n} len={bnd - a}")
+
+
+def test_varlen_equals_separate_runs(g):
+    lens = [100, 37, 64]
+    cu = gi.cu_seqlens_from(lens)
+    inp = gi.make_chunk_inputs(1, int(cu[-1]), 2, 128, 128, "bf16", seed=10, s0="normal",
+                               num_seqs=3)
+    o, Sf = gpu_fwd(g, inp, 64, cu=cu)
+    for n in range(3):
+        a, bnd = int(cu[n]), int(cu[n + 1])
+        sub = {x: inp[x][:, a:bnd].contiguous() for x in NAMES}
+        sub["S0"] = inp["S0"][n:n + 1].contiguous()
+        o1, S1 = gpu_fwd(g, sub, 64)
+        np.testing.assert_array_equal(o[:, a:bnd], o1)
+        np.testing.assert_array_equal(Sf[n:n + 1], S1)
+
+
+# -------------------------------------------------------- headline config
+def test_config2_sampled_units(g):
+    """Config 2 at full size (B=8, T=4096, H=16, d=128, bf16) in the launch
+    configuration the benchmark times; the oracle recomputes four (batch,
+    head) units end to end."""
+    c, inp = make(2)
+    o, Sf = gpu_fwd(g, inp, 64)
+    assert np.isfinite(o).all() and np.isfinite(Sf).all()
+    for (bb, hh) in ((0, 0), (3, 7), (5, 15), (7, 9)):
+        sub = {x: inp[x][bb:bb + 1, :, hh:hh + 1].contiguous() for x in NAMES}
+        o_ref, S_ref = oracle.fwd(*(sub[x] for x in NAMES))
+        check(o[bb:bb + 1, :, hh:hh + 1], Sf[bb:bb + 1, hh:hh + 1], o_ref, S_ref, TOL["bf16"],
+              f"cfg2 b={bb} h={hh}")
+
+
+def test_sweep_endpoints_sampled(g):
+    """T sweep at B*T = 32768: the two end points, one unit each."""
+    for T in (2048, 32768):
+        B = 32768 // T
+        inp = gi.make_chunk_inputs(B, T, 16, 128, 128, "bf16", seed=30 + B, s0=None)
+        o, Sf = gpu_fwd(g, inp, 64)
+        bb, hh = B - 1, 5
+        sub = {x: inp[x][bb:bb + 1, :, hh:hh + 1].contiguous() for x in NAMES}
+        o_ref, S_ref = oracle.fwd(*(sub[x] for x in NAMES))
+        check(o[bb:bb + 1, :, hh:hh + 1], Sf[bb:bb + 1, hh:hh + 1], o_ref, S_ref, TOL["bf16"],
+              f"sweep T={T}")
+
+
+# ------------------------------------------------------------- properties
+def test_state_aliasing_and_split_resume(g):
+    inp = gi.make_chunk_inputs(2, 192, 2, 64, 64, "f32", seed=11, s0="normal")
+    d = to_dev(inp)
+    o_full, S_full = g.chunk_fwd(*(d[n] for n in NAMES), S0=d["S0"])
+    T1 = 80
+    first = {n: d[n][:, :T1].contiguous() for n in NAMES}
+    second = {n: d[n][:, T1:].contiguous() for n in NAMES}
+    S = d["S0"].clone()
+    o1, _ = g.chunk_fwd(*(first[n] for n in NAMES), S0=S, S_final=S)  # in place
+    o2, _ = g.chunk_fwd(*(second[n] for n in NAMES), S0=S, S_final=S)
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat([o1, o2], 1).cpu().numpy(), o_full.cpu().numpy()) < 1e-5
+    assert rel_err(S.cpu().numpy(), S_full.cpu().numpy()) < 1e-5
+
+
+def test_zero_length_and_short(g):
+    inp = gi.make_chunk_inputs(2, 0, 2, 16, 16, "f32", seed=12, s0="normal")
+    d = to_dev(inp)
+    o, Sf = g.chunk_fwd(*(d[n] for n in NAMES), S0=d["S0"], chunk=16)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    np.testing.assert_array_equal(Sf.cpu().numpy(), inp["S0"].numpy())
+    o, Sf = g.chunk_fwd(*(d[n] for n in NAMES), chunk=16)
+    torch.cuda.synchronize()
+    assert float(Sf.abs().max()) == 0.0
+
+
+def test_nan_propagates_within_unit(g):
+    inp = gi.make_chunk_inputs(1, 96, 2, 64, 64, "f32", seed=13, s0="normal")
+    inp["v"][0, 50, 1, 3] = float("nan")
+    o, Sf = gpu_fwd(g, inp, 64)
+    assert np.isfinite(o[0, :, 0]).all() and np.isfinite(Sf[0, 0]).all()  # other head clean
+    assert np.isfinite(o[0, :48, 1]).all()                              # earlier chunk clean
+    assert np.isnan(o[0, 50:, 1]).any() and np.isnan(Sf[0, 1]).any()
+
+
+def test_deterministic(g):
+    c, inp = make(1)
+    o1, S1 = gpu_fwd(g, inp, 64)
+    o2, S2 = gpu_fwd(g, inp, 64)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("f32", 16)])
+def test_decode_small(g, dtype, d):
+    dd = gi.make_decode_inputs(5, 3, d, d, dtype, seed=40 + d, steps=6)
+    S_gpu = dd["S"].cuda()
+    S_ref = dd["S"].double().numpy()
+    tol = TOL[dtype]
+    for t in range(6):
+        step = {n: dd[n][t].contiguous() for n in NAMES}
+        o = g.decode_step(*(step[n].cuda() for n in NAMES), S_gpu)
+        o_ref, S_ref = oracle.decode(*(step[n] for n in NAMES), S_ref)
+        torch.cuda.synchronize()
+        check(o.float().cpu().numpy(), S_gpu.cpu().numpy(), o_ref, S_ref, tol, f"decode {dtype} d={d} t={t}")
+
+
+def test_decode_config4_16_steps(g):
+    c = gi.CONFIGS[4]
+    dd = gi.make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], steps=c["steps"])
+    S_gpu = dd["S"].cuda()
+    S_ref = dd["S"].double().numpy()
+    dev = {n: dd[n].cuda() for n in NAMES}
+    outs = []
+    for t in range(c["steps"]):
+        outs.append(g.decode_step(*(dev[n][t] for n in NAMES), S_gpu))
+    torch.cuda.synchronize()
+    for t in range(c["steps"]):
+        o_ref, S_ref = oracle.decode(*(dd[n][t] for n in NAMES), S_ref)
+        eo = rel_err(outs[t].float().cpu().numpy(), o_ref)
+        assert eo <= TOL["bf16"], f"step {t}: o error {eo:.3e}"
+    es = rel_err(S_gpu.cpu().numpy(), S_ref)
+    print(f"cfg4 16 steps err_S={es:.3e}", flush=True)
+    assert es <= TOL["bf16"]
+
+
+def test_decode_steps_equal_chunk_forward(g):
+    """T decode steps on the GPU agree with one chunked forward on the GPU."""
+    dd = gi.make_decode_inputs(2, 2, 64, 64, "f32", seed=50, steps=40)
+    S = dd["S"].cuda()
+    outs = [g.decode_step(*(dd[n][t].cuda() for n in NAMES), S) for t in range(40)]
+    seq = {n: dd[n].permute(1, 0, 2, 3).contiguous().cuda() for n in NAMES}
+    o, Sf = g.chunk_fwd(*(seq[n] for n in NAMES), S0=dd["S"].cuda(), chunk=16)
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(outs, 1).cpu().numpy(), o.cpu().numpy()) < 1e-4
+    assert rel_err(S.cpu().numpy(), Sf.cpu().numpy()) < 1e-4
