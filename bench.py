@@ -1,0 +1,281 @@
+"""Benchmark of the GDN-2 forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one gdn2_chunk_fwd call over the 1.3B-scale training-shape layer
+(B=8, T=4096, H=16, dk=dv=128, chunk 64, bf16 inputs, fp32 state and
+accumulation, S0 = 0) with the inputs already resident in HBM.  `value` is
+tokens/s over the K timed steps (bracketed by device synchronisations).
+
+In the same run (reported next to the headline, not in `value`):
+  * per-kernel durations from HIP events recorded on the launch stream
+    (libgdn2's timing hooks) and the roofline of the dominant kernel;
+  * the path as a whole against its algorithmic bytes and FLOPs;
+  * the T sweep at B*T = 32768 (T = 2K .. 32K) and the packed-sequence
+    workload (lengths uniform in [256, 8192], 32768 tokens);
+  * the decode step (256 sequences x 16 heads, 256 MiB fp32 state updated in
+    place), warm and with two alternating state buffers (512 MiB, more than
+    the 256 MB last-level cache);
+  * the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn2_inputs as gi  # noqa: E402
+
+NAMES = ("q", "k", "v", "alpha", "b", "w")
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak, TFLOP/s
+
+
+def flops_per_token_head(d: int, C: int) -> float:
+    """Algorithmic FLOPs of the chunked form per token and head (dk = dv = d):
+    A and P products, the triangular inverse, W/Ut, the state read-outs and the
+    state update, counted once (no dense-tile padding)."""
+    return 2.0 * (3 * d * d + ((3 * C - 1) / 2) * d + C * d + C * C / 6)
+
+
+# Algorithmic HBM bytes per token and head (bf16 elements, d = 128):
+#   path : read q, k, v, alpha, b, w once, write o once
+#   prep : read the six inputs, write -W, Q', Kbar^T, Ut, O_intra (bf16) and
+#          gamma_C (fp32, one d-vector per chunk)
+#   scan : read -W, Q', Kbar^T, Ut, O_intra and gamma_C, write o
+def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
+    gam = d * 4 / C
+    return {
+        "path": 6 * d * elem + d * elem,
+        "chunk_prep": 6 * d * elem + 5 * d * elem + gam,
+        "chunk_scan": 5 * d * elem + gam + d * elem,
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "gated_delta_rule_07_amd", "csrc"))):
+        with open(os.path.join(ROOT, "gated_delta_rule_07_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def timed_steps(fn, steps: int, warmup: int) -> float:
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(inp: dict, H: int, budget_s: float) -> dict:
+    """The oracle on all (batch, head) units of the workload but only the first
+    T' tokens of each sequence, T' chosen so the run takes roughly budget_s."""
+    import oracle
+    threads = oracle.max_threads()
+    B = inp["q"].shape[0]
+
+    def run(Tp):
+        sub = {x: inp[x][:, :Tp].contiguous() for x in NAMES}
+        t0 = time.perf_counter()
+        oracle.fwd(*(sub[x] for x in NAMES))
+        return time.perf_counter() - t0
+
+    Tc = 64
+    dt = run(Tc)
+    rate = B * H * Tc / dt                     # token-heads per second
+    T = inp["q"].shape[1]
+    Tp = int(max(64, min(T, (rate * budget_s / (B * H)) // 64 * 64)))
+    reps, total = 0, 0.0
+    while total < budget_s and reps < 64:      # repeat the sample until the budget is spent
+        total += run(Tp)
+        reps += 1
+    return {"value": B * Tp * reps / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 token-by-token oracle on all {B}x{H} (batch, head) units of the "
+                      f"workload, first {Tp} of {T} tokens each, {reps} run(s), {total:.1f} s"}
+
+
+def load_traffic(kernel: str) -> dict | None:
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_config2.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every (sequence, head) is independent; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import gated_delta_rule_07_amd as g
+
+    B, T, H, d, C = 8, 4096, 16, 128, 64
+    inp = gi.make_chunk_inputs(B, T, H, d, d, "bf16", seed=2, s0=None)
+    dev = {x: inp[x].cuda() for x in NAMES}
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
+    Sf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(g.workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    g.profile_enable(True)
+    step()
+    torch.cuda.synchronize()
+    g.profile_read(reset=True)
+    sec = timed_steps(step, args.steps, args.warmup)
+    prof = g.profile_read(reset=True)
+    g.profile_enable(False)
+    launches = args.steps + args.warmup
+    kern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in prof.items()}
+
+    tok_heads = B * T * H
+    fl = flops_per_token_head(d, C) * tok_heads
+    byt = bytes_per_token_head(d, C)
+    dominant = max(kern, key=lambda k: kern[k]["avg_us"])
+    dom_us = kern[dominant]["avg_us"]
+    dom_bytes = byt[dominant] * tok_heads
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    tr = load_traffic(dominant)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": (tr["bytes_per_launch"] if tr else None),
+                "kernel": dominant, "algorithmic_bytes_per_launch": int(dom_bytes)}
+
+    out = {
+        "metric": "GDN-2 chunk fwd tokens/s + % bf16 MFMA peak (H16 d128 T4K); decode % HBM",
+        "value": round(B * T / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "GDN-2 chunked forward, 1.3B-scale layer shape", "B": B, "T": T,
+                   "H": H, "dk": d, "dv": d, "chunk": C, "inputs": "bf16", "state": "fp32",
+                   "S0": "zero", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "path": {"tflops": round(fl / sec / 1e12, 2),
+                 "mfma_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "algorithmic_bytes": int(byt["path"] * tok_heads),
+                 "hbm_frac": round(byt["path"] * tok_heads / sec / 1e9 / HBM_PEAK_GBS, 4),
+                 "flops_per_token_head": flops_per_token_head(d, C)},
+        "kernels": kern,
+    }
+
+    if not args.no_extras:
+        # T sweep at B*T = 32768 and the packed workload reuse the same tokens
+        sweep = {}
+        for Ts in gi.SWEEP_T:
+            Bs = 32768 // Ts
+            view = {x: dev[x].view(Bs, Ts, H, d) for x in NAMES}
+            o2 = o.view(Bs, Ts, H, d)
+            Sf2 = torch.empty((Bs, H, d, d), dtype=torch.float32, device="cuda")
+            sec_s = timed_steps(lambda: g.chunk_fwd(*(view[x] for x in NAMES), chunk=C, out=o2,
+                                                    S_final=Sf2, workspace=ws), 20, 3)
+            sweep[str(Ts)] = round(32768 / sec_s, 1)
+        vals = list(sweep.values())
+        out["sweep_tokens_per_s"] = sweep
+        out["sweep_flatness_min_over_max"] = round(min(vals) / max(vals), 3)
+
+        lens = gi.packed_lengths(3)
+        cu = gi.cu_seqlens_from(lens).cuda()
+        packed = {x: dev[x].view(1, 32768, H, d) for x in NAMES}
+        Sp = torch.empty((len(lens), H, d, d), dtype=torch.float32, device="cuda")
+        wsp = torch.empty(g.workspace_bytes(1, 32768, H, d, d, len(lens), C, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        sec_p = timed_steps(lambda: g.chunk_fwd(*(packed[x] for x in NAMES), cu_seqlens=cu,
+                                                chunk=C, out=o.view(1, 32768, H, d), S_final=Sp,
+                                                workspace=wsp), 20, 3)
+        out["packed"] = {"tokens_per_s": round(32768 / sec_p, 1), "num_seqs": len(lens),
+                         "ms": round(sec_p * 1e3, 4)}
+
+        # decode: 256 sequences x 16 heads, 16 distinct step inputs cycled
+        c4 = gi.CONFIGS[4]
+        dd = gi.make_decode_inputs(c4["N"], c4["H"], d, d, "bf16", c4["seed"], steps=c4["steps"])
+        ddev = {x: dd[x].cuda() for x in NAMES}
+        S_a = dd["S"].cuda()
+        S_b = dd["S"].cuda().clone()
+        od = torch.empty((c4["N"], c4["H"], d), dtype=torch.bfloat16, device="cuda")
+        step_bytes = c4["N"] * c4["H"] * (2 * d * d * 4 + 7 * d * 2)
+        counter = [0]
+
+        def dstep(states):
+            i = counter[0]
+            counter[0] += 1
+            g.decode_step(*(ddev[x][i % c4["steps"]] for x in NAMES), states[i % len(states)],
+                          out=od)
+
+        g.profile_enable(True)
+        sec_d = timed_steps(lambda: dstep([S_a]), args.decode_steps, 10)
+        dprof = g.profile_read(reset=True)
+        sec_dc = timed_steps(lambda: dstep([S_a, S_b]), args.decode_steps, 10)
+        dprof_c = g.profile_read(reset=True)
+        g.profile_enable(False)
+        dk_us = 1e3 * dprof["decode"][0] / dprof["decode"][1]
+        dkc_us = 1e3 * dprof_c["decode"][0] / dprof_c["decode"][1]
+        out["decode"] = {
+            "workload": "256 sequences x 16 heads, d=128, bf16 inputs, fp32 state in place",
+            "steps": args.decode_steps, "us_per_step": round(sec_d * 1e6, 2),
+            "kernel_us": round(dk_us, 2),
+            "algorithmic_bytes_per_step": step_bytes,
+            "GBps": round(step_bytes / (dk_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(step_bytes / (dk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "two_state_buffers": {"kernel_us": round(dkc_us, 2),
+                                  "GBps": round(step_bytes / (dkc_us * 1e-6) / 1e9, 1),
+                                  "hbm_frac": round(step_bytes / (dkc_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp, H, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

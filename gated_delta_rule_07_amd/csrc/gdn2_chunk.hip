@@ -93,16 +93,21 @@ template <> struct raw4<bf16_t> {
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Per (chunk slot, head) block of intermediates, all tiles fragment-ordered.
+// The first SHARED bytes (-W, Q', Kbar^T, gamma_C) are what every column
+// slice of the state scan needs; they are copied to LDS as one block.  A
+// operands of the scan are stored with their 16-wide k tiles paired
+// (tile_off), so one 16-byte load yields a 16x16x32 operand.
 template <typename IO, int D, int C> struct blk_layout {
   static constexpr int NB = C / 16, NK = D / 16;
   static constexpr size_t TB = frag<IO>::TILE_BYTES;
-  static constexpr size_t WN = 0;                   // [NB][NK] RowFrag(-W)
-  static constexpr size_t QP = WN + NB * NK * TB;   // [NB][NK] RowFrag(Q')
-  static constexpr size_t KB = QP + NB * NK * TB;   // [NK][NB] RowFrag(Kbar^T)
-  static constexpr size_t UT = KB + NK * NB * TB;   // [NB][NK] ColFrag(Ut)
+  static constexpr size_t WN = 0;                   // rows tt, k tiles over dk: RowFrag(-W)
+  static constexpr size_t QP = WN + NB * NK * TB;   // rows tt, k tiles over dk: RowFrag(Q')
+  static constexpr size_t KB = QP + NB * NK * TB;   // rows dk tile, k tiles over tokens: RowFrag(Kbar^T)
+  static constexpr size_t GAM = KB + NK * NB * TB;  // [D] float gamma_C
+  static constexpr size_t SHARED = (GAM + D * sizeof(float) + 1023) & ~static_cast<size_t>(1023);
+  static constexpr size_t UT = SHARED;              // [NB][NK] ColFrag(Ut)
   static constexpr size_t OI = UT + NB * NK * TB;   // [NB][NK] ColFrag(O_intra)
-  static constexpr size_t GAM = OI + NB * NK * TB;  // [D] float gamma_C
-  static constexpr size_t BYTES = align256(GAM + D * sizeof(float));
+  static constexpr size_t BYTES = align256(OI + NB * NK * TB);
 };
 
 template <typename IO, int D, int C> size_t chunk_block_bytes() { return blk_layout<IO, D, C>::BYTES; }
@@ -138,29 +143,42 @@ __device__ __forceinline__ bool locate_chunk(int slot, const chunk_args &a, int 
 }
 
 template <typename IO, int D, int C> struct prep_smem {
-  static constexpr int NB = C / 16, NK = D / 16, NP = NB * (NB - 1) / 2;
+  static constexpr int NB = C / 16, NK = D / 16;
+  static constexpr int NP = NB * (NB - 1) / 2;  // sub-block pairs J < I
+  static constexpr int NT = NB * (NB + 1) / 2;  // sub-block pairs J <= I
+  static constexpr int NKS = (NP > NB ? NP : NB);
   static constexpr int TB = frag<IO>::TILE_BYTES;
   float tot[NB][D];                  // per-sub-block sum of log2(alpha)
   float f1[NB][D];                   // exp2(rho_I): decay from chunk start to sub-block I
   float f2[NB][D];                   // exp2(g_C - rho_I): decay from sub-block I to chunk end
-  float sig[NP > 0 ? NP : 1][D];     // exp2(rho_I - rho_J), J < I
+  float sig[NP > 0 ? NP : 1][D];     // exp2(rho_I - rho_J) <= 1 for the pair (I, J), J < I
   float ad[NB][16][16];              // diagonal blocks of A, row-major
-  alignas(16) unsigned char khw[NB][NK][TB];  // RowFrag(Khat) tiles, then ColFrag(W)
-  alignas(16) unsigned char ecu[NB][NK][TB];  // ColFrag(E) tiles, then ColFrag(Ut)
-  alignas(16) unsigned char u[NB][NK][TB];    // ColFrag(U) tiles
-  alignas(16) unsigned char tc[NB][NB][TB];   // ColFrag(T_IJ) tiles
+  // RowFrag(Khat_J * sig_IJ) for each pair (I, J), k tiles paired; after the
+  // A/P products the same bytes hold RowFrag(Qchk) tiles [NB][NK]
+  alignas(16) unsigned char khs[NKS][NK][TB];
+  alignas(16) unsigned char ec[NB][NK][TB];  // ColFrag(E_J), one tile per 16 channels
+  alignas(16) unsigned char pr[NT][TB];      // RowFrag(P_IJ)
+  alignas(16) unsigned char tcol[NT][TB];    // ColFrag(T_IJ)
+  alignas(16) unsigned char trow[NT][TB];    // RowFrag(T_IJ)
 };
 
 __device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
+__device__ __forceinline__ constexpr int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // Kernel 1: per-chunk prep + in-chunk WY/UT factor.  grid: num_slots * H,
-// block: 64 * C/16 threads (one wave per 16-token sub-block).
+// block: 64 * C/16 threads.  Wave I owns the 16-token sub-block I for the
+// row-wise phases (loads, decay prefix sums, A and P rows, T rows) and
+// column tiles [I*CTW, I*CTW + CTW) of dk and dv for the column-wise phases
+// (W, Ut, Q', O_intra), so every wave does the same amount of matrix work.
 template <typename IO, int D, int C>
 __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_args a) {
   constexpr int NB = C / 16, NK = D / 16;
+  constexpr int CTW = (NK >= NB) ? NK / NB : 1;  // column tiles per wave
   typedef frag<IO> F;
+  typedef frag2<IO> F2;
   typedef blk_layout<IO, D, C> L;
-  __shared__ prep_smem<IO, D, C> sm;
+  typedef prep_smem<IO, D, C> SM;
+  __shared__ SM sm;
 
   const int h = blockIdx.x % a.H;
   const int slot = blockIdx.x / a.H;
@@ -170,23 +188,23 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
     return;  // whole workgroup leaves together
   (void)seq;
   const int tid = threadIdx.x;
-  const int I = tid >> 6;  // sub-block of this wave
+  const int I = tid >> 6;  // sub-block (row phases) of this wave
   const int lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
   const int t = 16 * I + m;  // token within the chunk
   const bool valid = t < len;
-  const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
+  const int ct0 = I * CTW;    // first column tile (column phases)
+  const bool owner = ct0 < NK;
   unsigned char *blk = reinterpret_cast<unsigned char *>(a.blocks) +
                        (static_cast<size_t>(slot) * a.H + h) * a.blk_bytes;
-  const IO *qp = static_cast<const IO *>(a.q) + row * D;
-  const IO *kp = static_cast<const IO *>(a.k) + row * D;
-  const IO *vp = static_cast<const IO *>(a.v) + row * D;
-  const IO *ap = static_cast<const IO *>(a.al) + row * D;
-  const IO *bp = static_cast<const IO *>(a.b) + row * D;
-  const IO *wp = static_cast<const IO *>(a.w) + row * D;
+  auto row_of = [&](int tok) { return static_cast<size_t>(t0 + tok) * a.H + h; };
+  const IO *qp = static_cast<const IO *>(a.q) + row_of(valid ? t : 0) * D;
+  const IO *kp = static_cast<const IO *>(a.k) + row_of(valid ? t : 0) * D;
+  const IO *ap = static_cast<const IO *>(a.al) + row_of(valid ? t : 0) * D;
+  const IO *bp = static_cast<const IO *>(a.b) + row_of(valid ? t : 0) * D;
 
   // ---------------- phase 1: loads, log-decay prefix sums, block totals
-  raw4<IO> rq[NK], rk[NK], rb[NK], rv[NK], rw[NK];
+  raw4<IO> rq[NK], rk[NK], rb[NK];
   f32x4 gl[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
@@ -195,15 +213,32 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
       rq[kk] = raw4<IO>::ld(qp + c0);
       rk[kk] = raw4<IO>::ld(kp + c0);
       rb[kk] = raw4<IO>::ld(bp + c0);
-      rv[kk] = raw4<IO>::ld(vp + c0);
-      rw[kk] = raw4<IO>::ld(wp + c0);
       const f32x4 al = raw4<IO>::ld(ap + c0).f();
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         gl[kk][i] = fast_log2(al[i]);
     } else {
-      rq[kk] = rk[kk] = rb[kk] = rv[kk] = rw[kk] = raw4<IO>::fill(0.f);
+      rq[kk] = rk[kk] = rb[kk] = raw4<IO>::fill(0.f);
       gl[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // values and write gates of every sub-block, for this wave's column tiles
+  raw4<IO> rv[NB][CTW], rw[NB][CTW];
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    const int tj = 16 * J + m;
+    const bool vj = owner && tj < len;
+    const IO *vp = static_cast<const IO *>(a.v) + row_of(vj ? tj : 0) * D;
+    const IO *wp = static_cast<const IO *>(a.w) + row_of(vj ? tj : 0) * D;
+#pragma unroll
+    for (int j = 0; j < CTW; ++j) {
+      const int c0 = 16 * (ct0 + j) + 4 * g;
+      if (vj) {
+        rv[J][j] = raw4<IO>::ld(vp + c0);
+        rw[J][j] = raw4<IO>::ld(wp + c0);
+      } else {
+        rv[J][j] = rw[J][j] = raw4<IO>::fill(0.f);
+      }
     }
   }
 #pragma unroll
@@ -232,8 +267,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
     }
     sm.f1[J][c] = fast_exp2(rho);
     sm.f2[J][c] = fast_exp2(suf);
-    // sigma(I2, J) = exp2(rho_I2 - rho_J) <= 1 for I2 > J
-    float part = 0.f;
+    float part = 0.f;  // sum of tot over sub-blocks J .. I2-1
 #pragma unroll
     for (int I2 = 1; I2 < NB; ++I2) {
       if (I2 > J) {
@@ -248,8 +282,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
 
   // ---------------- phase 1b: decayed, gated operands
   const F eye = identity_colfrag<IO>(lane);
-  f32x4 er[NK], qr[NK], qc[NK];
-  F khf[NK];
+  F ef[NK], qf[NK], khf[NK], qcf[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const int c0 = 16 * kk + 4 * g;
@@ -262,37 +295,70 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
       fi[i] = fast_exp2(-gl[kk][i]);  // e^{rho_I - g_t} >= 1
     }
     const f32x4 kf = rk[kk].f();
-    er[kk] = rb[kk].f() * kf * f;
-    qr[kk] = rq[kk].f() * f;
-    qc[kk] = qr[kk] * f1v;
+    const f32x4 er = rb[kk].f() * kf * f;
+    const f32x4 qr = rq[kk].f() * f;
     const f32x4 kh = kf * fi;
+    ef[kk] = F::from(er);
+    qf[kk] = F::from(qr);
     khf[kk] = F::from(kh);
-    khf[kk].st(sm.khw[I][kk], lane);
-    F::from(transpose_frag(F::from(er[kk] * f1v), eye)).st(sm.ecu[I][kk], lane);
-    F::from(transpose_frag(F::from(rw[kk].f() * rv[kk].f()), eye)).st(sm.u[I][kk], lane);
-    F::from(transpose_frag(F::from(kh * f2v), eye)).st(blk + L::KB + (kk * NB + I) * L::TB, lane);
+    qcf[kk] = F::from(qr * f1v);
+    // keys of this sub-block rescaled to the reference point of each later one
+#pragma unroll
+    for (int I2 = 1; I2 < NB; ++I2) {
+      if (I2 > I) {
+        const f32x4 s = *reinterpret_cast<const f32x4 *>(&sm.sig[pair_index(I2, I)][c0]);
+        F::from(kh * s).st(&sm.khs[pair_index(I2, I)][0][0] + tile_off<IO, NK>(0, kk, lane), 0);
+      }
+    }
+    F::from(transpose_frag(F::from(er * f1v), eye)).st(sm.ec[I][kk], lane);
+    F::from(transpose_frag(F::from(kh * f2v), eye)).st(blk + L::KB + tile_off<IO, NB>(kk, I, lane), 0);
   }
+  // ColFrag(U_J) = ColFrag(w (.) v) of the own column tiles
+  F ucol[NB][CTW];
+#pragma unroll
+  for (int J = 0; J < NB; ++J)
+#pragma unroll
+    for (int j = 0; j < CTW; ++j)
+      ucol[J][j] = F::from(transpose_frag(F::from(rw[J][j].f() * rv[J][j].f()), eye));
   __syncthreads();
 
-  // ---------------- phase 2: A and P rows of sub-block I (as RowFrag)
+  // ---------------- phase 2: A and P rows of sub-block I, as RowFrag
   f32x4 accA[NB], accP[NB];
 #pragma unroll
   for (int J = 0; J < NB; ++J) {
     accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
     accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (J < I) {
+      const unsigned char *kb = &sm.khs[pair_index(I, J)][0][0];
+      if constexpr (NK % 2 == 0) {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const F aop = F::ld(sm.khw[J][kk], lane);
-        const f32x4 s = *reinterpret_cast<const f32x4 *>(&sm.sig[pair_index(I, J)][16 * kk + 4 * g]);
-        mma16(accA[J], aop, F::from(er[kk] * s));
-        mma16(accP[J], aop, F::from(qr[kk] * s));
+        for (int kp = 0; kp < NK / 2; ++kp) {
+          const F2 a2 = F2::ld(kb + tile_off<IO, NK>(0, 2 * kp, 0), lane);
+          mma32(accA[J], a2, F2::make(ef[2 * kp], ef[2 * kp + 1]));
+          mma32(accP[J], a2, F2::make(qf[2 * kp], qf[2 * kp + 1]));
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const F a1 = F::ld(kb + tile_off<IO, NK>(0, kk, 0), lane);
+          mma16(accA[J], a1, ef[kk]);
+          mma16(accP[J], a1, qf[kk]);
+        }
       }
     } else if (J == I) {
+      if constexpr (NK % 2 == 0) {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        mma16(accA[J], khf[kk], F::from(er[kk]));
-        mma16(accP[J], khf[kk], F::from(qr[kk]));
+        for (int kp = 0; kp < NK / 2; ++kp) {
+          const F2 a2 = F2::make(khf[2 * kp], khf[2 * kp + 1]);
+          mma32(accA[J], a2, F2::make(ef[2 * kp], ef[2 * kp + 1]));
+          mma32(accP[J], a2, F2::make(qf[2 * kp], qf[2 * kp + 1]));
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          mma16(accA[J], khf[kk], ef[kk]);
+          mma16(accP[J], khf[kk], qf[kk]);
+        }
       }
       // lane (t = m, g) holds row t, columns s = 4g + i of the diagonal block
 #pragma unroll
@@ -304,8 +370,19 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
       }
       *reinterpret_cast<f32x4 *>(&sm.ad[I][m][4 * g]) = accA[J];
     }
+    if (J <= I)
+      F::from(accP[J]).st(sm.pr[tri_index(I, J)], lane);
   }
+  F af[NB];
+#pragma unroll
+  for (int K = 0; K < NB; ++K)
+    af[K] = F::from(accA[K]);
   __syncthreads();
+  // the rescaled keys are consumed: their bytes now hold RowFrag(Qchk)
+  unsigned char *qc_tiles = &sm.khs[0][0][0];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    qcf[kk].st(qc_tiles + (I * NK + kk) * SM::TB, lane);
 
   // ---------------- phase 3: T = (I + A)^{-1}
   {
@@ -323,14 +400,12 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       tii[i] = (g == 0) ? x[i] : (g == 1) ? x[4 + i] : (g == 2) ? x[8 + i] : x[12 + i];
-    F::from(tii).st(sm.tc[I][I], lane);
+    const F tf = F::from(tii);
+    tf.st(sm.tcol[tri_index(I, I)], lane);
+    F::from(transpose_frag(tf, eye)).st(sm.trow[tri_index(I, I)], lane);
   }
   __syncthreads();
-  const F trow_ii = F::from(transpose_frag(F::ld(sm.tc[I][I], lane), eye));
-  F af[NB];
-#pragma unroll
-  for (int K = 0; K < NB; ++K)
-    af[K] = F::from(accA[K]);
+  const F trow_ii = F::ld(sm.trow[tri_index(I, I)], lane);
 #pragma unroll
   for (int l = 1; l < NB; ++l) {
     if (I >= l) {
@@ -339,91 +414,86 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
 #pragma unroll
       for (int K = 0; K < NB; ++K)
         if (K >= J && K < I)
-          mma16(acc, af[K], F::ld(sm.tc[K][J], lane));
+          mma16(acc, af[K], F::ld(sm.tcol[tri_index(K, J)], lane));
       f32x4 tij = {0.f, 0.f, 0.f, 0.f};
       mma16(tij, trow_ii, F::from(acc));
-      F::from(-tij).st(sm.tc[I][J], lane);
+      const F tf = F::from(-tij);
+      tf.st(sm.tcol[tri_index(I, J)], lane);
+      F::from(transpose_frag(tf, eye)).st(sm.trow[tri_index(I, J)], lane);
     }
     __syncthreads();
   }
 
-  // ---------------- phase 4: W = T E, Ut = T U (rows of sub-block I)
-  F trow[NB];
+  // ---------------- phases 4-5, by column tile: W = T E, Ut = T U,
+  // Q' = Qchk - P W (computed as Q'^T so it lands as RowFrag), O_intra = P Ut
+  if (owner) {
 #pragma unroll
-  for (int J = 0; J < NB; ++J)
-    trow[J] = (J <= I) ? F::from(transpose_frag(F::ld(sm.tc[I][J], lane), eye)) : F::zero();
-  f32x4 accW[NK], accU[NK];
+    for (int j = 0; j < CTW; ++j) {
+      const int ct = ct0 + j;
+      F wc[NB], uc[NB];
 #pragma unroll
-  for (int ct = 0; ct < NK; ++ct) {
-    accW[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accU[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int I2 = 0; I2 < NB; ++I2) {
+        f32x4 w = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      if (J <= I) {
-        mma16(accW[ct], trow[J], F::ld(sm.ecu[J][ct], lane));
-        mma16(accU[ct], trow[J], F::ld(sm.u[J][ct], lane));
+        for (int J = 0; J <= I2; ++J) {
+          const F tr = F::ld(sm.trow[tri_index(I2, J)], lane);
+          mma16(w, tr, F::ld(sm.ec[J][ct], lane));
+          mma16(u, tr, ucol[J][j]);
+        }
+        wc[I2] = F::from(w);
+        uc[I2] = F::from(u);
+        uc[I2].st(blk + L::UT + (I2 * NK + ct) * L::TB, lane);
+        F::from(transpose_frag(wc[I2], eye)).neg().st(blk + L::WN + tile_off<IO, NK>(I2, ct, lane), 0);
+      }
+#pragma unroll
+      for (int I2 = 0; I2 < NB; ++I2) {
+        f32x4 q = F::ld(qc_tiles + (I2 * NK + ct) * SM::TB, lane).to_f32();
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J <= I2; ++J) {
+          const F p = F::ld(sm.pr[tri_index(I2, J)], lane);
+          mma16(q, wc[J], p.neg());
+          mma16(o, p, uc[J]);
+        }
+        F::from(q).st(blk + L::QP + tile_off<IO, NK>(I2, ct, lane), 0);
+        F::from(o).st(blk + L::OI + (I2 * NK + ct) * L::TB, lane);
       }
     }
   }
-#pragma unroll
-  for (int ct = 0; ct < NK; ++ct) {
-    F::from(accU[ct]).st(blk + L::UT + (I * NK + ct) * L::TB, lane);
-    F::from(transpose_frag(F::from(accW[ct]), eye)).neg().st(blk + L::WN + (I * NK + ct) * L::TB, lane);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int ct = 0; ct < NK; ++ct) {
-    F::from(accW[ct]).st(sm.khw[I][ct], lane);
-    F::from(accU[ct]).st(sm.ecu[I][ct], lane);
-  }
-  __syncthreads();
-
-  // ---------------- phase 5: Q' = Qchk - P W (transposed), O_intra = P Ut
-  F pf[NB], pn[NB];
-#pragma unroll
-  for (int J = 0; J < NB; ++J) {
-    pf[J] = F::from(accP[J]);
-    pn[J] = pf[J].neg();
-  }
-#pragma unroll
-  for (int ct = 0; ct < NK; ++ct) {
-    f32x4 acc = qc[ct];
-#pragma unroll
-    for (int J = 0; J < NB; ++J)
-      if (J <= I)
-        mma16(acc, F::ld(sm.khw[J][ct], lane), pn[J]);
-    F::from(acc).st(blk + L::QP + (I * NK + ct) * L::TB, lane);
-  }
-#pragma unroll
-  for (int vt = 0; vt < NK; ++vt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int J = 0; J < NB; ++J)
-      if (J <= I)
-        mma16(acc, pf[J], F::ld(sm.ecu[J][vt], lane));
-    F::from(acc).st(blk + L::OI + (I * NK + vt) * L::TB, lane);
-  }
 }
 
-// Kernel 2: sequential state scan + output.  One wave per (sequence, head,
-// 16-column slice of dv).  grid: units_pad * D/16 with units_pad = N*H
-// rounded up to a multiple of 8; the 8 XCDs receive consecutive workgroup
-// ids round-robin, so all slices of one head land on the same XCD and share
-// its L2 for the per-chunk W, Q', Kbar tiles.
-template <typename IO, int D, int C>
-__global__ void __launch_bounds__(64) gdn2_chunk_scan_kernel(chunk_args a) {
-  constexpr int NB = C / 16, NK = D / 16;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Kernel 2: sequential state scan + output.  A workgroup of NW waves owns one
+// (sequence, head) and NW 16-column slices of dv; wave w keeps its slice of
+// the state S (dk x 16, float32) in matrix-core accumulators for the whole
+// sequence.  Per chunk, the shared -W, Q', Kbar^T, gamma_C block (49 KB for
+// bf16, d = 128, C = 64) is copied HBM -> LDS with global_load_lds (no
+// register staging) one chunk ahead, into the other of NBUF buffers, while
+// the waves compute the current chunk:
+//   Z = Ut - W S,  O = O_intra + Q' S  (written to o),  S <- Diag(gamma_C) S + Kbar^T Z.
+// Grid: units_pad * (D/16/NW) workgroups, units_pad = N*H rounded up to 8;
+// consecutive ids go to the 8 XCDs round-robin and all column groups of one
+// head share an XCD (and its L2).
+template <typename IO, int D, int C, int NW, int NBUF>
+__global__ void __launch_bounds__(64 * NW) gdn2_chunk_scan_kernel(chunk_args a) {
+  constexpr int NB = C / 16, NK = D / 16, NG = NK / NW;
   typedef frag<IO> F;
+  typedef frag2<IO> F2;
   typedef blk_layout<IO, D, C> L;
+  constexpr int NDMA = static_cast<int>(L::SHARED / 1024);  // 1 KB per wave instruction
+  __shared__ __attribute__((aligned(16))) unsigned char sbuf[NBUF][L::SHARED];
+
   const int x = blockIdx.x;
   const int xcd = x & 7, s8 = x >> 3;
-  const int unit = (s8 / NK) * 8 + xcd;
-  const int vt = s8 % NK;
+  const int unit = (s8 / NG) * 8 + xcd;
+  const int cg = s8 % NG;
   if (unit >= a.num_seqs * a.H)
     return;
   const int n = unit / a.H, h = unit - n * a.H;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
+  const int vt = cg * NW + wave;
   int c_begin, nchunks;
   long tstart, tend;
   if (a.cu) {
@@ -438,6 +508,15 @@ __global__ void __launch_bounds__(64) gdn2_chunk_scan_kernel(chunk_args a) {
     tstart = static_cast<long>(n) * a.T;
     tend = tstart + a.T;
   }
+  const unsigned char *blocks = reinterpret_cast<const unsigned char *>(a.blocks);
+  auto blk_of = [&](int c) { return blocks + (static_cast<size_t>(c_begin + c) * a.H + h) * a.blk_bytes; };
+  auto dma = [&](int c, int buf) {
+    const unsigned char *src = blk_of(c);
+    for (int i = wave; i < NDMA; i += NW)
+      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
+                                       (lds_void_t *)(&sbuf[buf][i * 1024]), 16, 0, 0);
+  };
+
   const int col = 16 * vt + m;
   f32x4 S[NK];
 #pragma unroll
@@ -447,39 +526,93 @@ __global__ void __launch_bounds__(64) gdn2_chunk_scan_kernel(chunk_args a) {
       S[kk][i] = a.S0 ? a.S0[(static_cast<size_t>(unit) * D + 16 * kk + 4 * g + i) * D + col] : 0.f;
   IO *out = static_cast<IO *>(a.o);
 
+  F ut[NB], oi[NB];
+  if (nchunks > 0) {
+    dma(0, 0);
+    const unsigned char *blk = blk_of(0);
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) {
+      ut[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane);
+      oi[tt] = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane);
+    }
+  }
   for (int c = 0; c < nchunks; ++c) {
-    const unsigned char *blk = reinterpret_cast<const unsigned char *>(a.blocks) +
-                               (static_cast<size_t>(c_begin + c) * a.H + h) * a.blk_bytes;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // chunk c's block is in sbuf[c % NBUF]; nobody still reads the other buffer
+    F utc[NB], oic[NB];
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) {
+      utc[tt] = ut[tt];
+      oic[tt] = oi[tt];
+    }
+    if (NBUF > 1 && c + 1 < nchunks) {
+      dma(c + 1, (c + 1) % NBUF);
+      const unsigned char *blk = blk_of(c + 1);
+#pragma unroll
+      for (int tt = 0; tt < NB; ++tt) {
+        ut[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane);
+        oi[tt] = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane);
+      }
+    }
+    const unsigned char *sb = sbuf[c % NBUF];
     const long t0 = tstart + static_cast<long>(c) * C;
     const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
+
     F sf[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
       sf[kk] = F::from(S[kk]);
-    f32x4 Z[NB];
+    F zf[NB];
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
-      Z[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane).to_f32();
-      f32x4 O = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane).to_f32();
+      f32x4 z = utc[tt].to_f32();
+      f32x4 o = oic[tt].to_f32();
+      if constexpr (NK % 2 == 0) {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        mma16(Z[tt], F::ld(blk + L::WN + (tt * NK + kk) * L::TB, lane), sf[kk]);
-        mma16(O, F::ld(blk + L::QP + (tt * NK + kk) * L::TB, lane), sf[kk]);
+        for (int k2 = 0; k2 < NK / 2; ++k2) {
+          const F2 sb2 = F2::make(sf[2 * k2], sf[2 * k2 + 1]);
+          mma32(z, F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane), sb2);
+          mma32(o, F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane), sb2);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          mma16(z, F::ld(sb + L::WN + tile_off<IO, NK>(tt, kk, 0), lane), sf[kk]);
+          mma16(o, F::ld(sb + L::QP + tile_off<IO, NK>(tt, kk, 0), lane), sf[kk]);
+        }
       }
+      zf[tt] = F::from(z);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * tt + 4 * g + i;
         if (t < len)
-          out[(static_cast<size_t>(t0 + t) * a.H + h) * D + col] = io<IO>::from_f(O[i]);
+          out[(static_cast<size_t>(t0 + t) * a.H + h) * D + col] = io<IO>::from_f(o[i]);
       }
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const f32x4 gam = *reinterpret_cast<const f32x4 *>(blk + L::GAM + (16 * kk + 4 * g) * sizeof(float));
+      const f32x4 gam = *reinterpret_cast<const f32x4 *>(sb + L::GAM + (16 * kk + 4 * g) * sizeof(float));
       S[kk] *= gam;
+      if constexpr (NB % 2 == 0) {
 #pragma unroll
-      for (int tt = 0; tt < NB; ++tt)
-        mma16(S[kk], F::ld(blk + L::KB + (kk * NB + tt) * L::TB, lane), F::from(Z[tt]));
+        for (int t2 = 0; t2 < NB / 2; ++t2)
+          mma32(S[kk], F2::ld(sb + L::KB + tile_off<IO, NB>(kk, 2 * t2, 0), lane),
+                F2::make(zf[2 * t2], zf[2 * t2 + 1]));
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt)
+          mma16(S[kk], F::ld(sb + L::KB + tile_off<IO, NB>(kk, tt, 0), lane), zf[tt]);
+      }
+    }
+    if (NBUF == 1 && c + 1 < nchunks) {
+      __syncthreads();  // everyone is done with the only buffer
+      dma(c + 1, 0);
+      const unsigned char *blk = blk_of(c + 1);
+#pragma unroll
+      for (int tt = 0; tt < NB; ++tt) {
+        ut[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane);
+        oi[tt] = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane);
+      }
     }
   }
   if (a.S_final) {
@@ -530,11 +663,29 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
   return hipGetLastError();
 }
 
-template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st) {
+template <typename IO, int D, int C, int NW>
+hipError_t launch_scan_nw(const chunk_args &a, hipStream_t st) {
+  typedef blk_layout<IO, D, C> L;
+  constexpr int NBUF = (2 * L::SHARED <= 150 * 1024) ? 2 : 1;
   const int units = a.num_seqs * a.H;
   const int units_pad = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C>), dim3(units_pad * (D / 16)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NW, NBUF>), dim3(units_pad * (D / 16 / NW)),
+                     dim3(64 * NW), 0, st, a);
   return hipGetLastError();
+}
+
+// Workgroups share the per-chunk block in LDS across NW = 4 waves when that
+// still gives at least one workgroup per compute unit; with few (sequence,
+// head) units (long sequences, small batch) every wave gets its own
+// workgroup so that all of them can run.
+template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st) {
+  constexpr int NK = D / 16;
+  const long wgs4 = static_cast<long>(a.num_seqs) * a.H * NK / 4;
+  if constexpr (NK >= 4) {
+    if (wgs4 >= 256)
+      return launch_scan_nw<IO, D, C, 4>(a, st);
+  }
+  return launch_scan_nw<IO, D, C, 1>(a, st);
 }
 
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st) {

@@ -22,6 +22,7 @@ namespace gdn2 {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
 
 // ---------------------------------------------------------------- scalars --
@@ -74,11 +75,8 @@ template <typename T> struct frag;
 template <> struct frag<bf16_t> {
   s16x4 v;
   __device__ static __forceinline__ frag from(f32x4 x) {
-    frag f;
-    f.v[0] = static_cast<short>(f2bf(x[0]));
-    f.v[1] = static_cast<short>(f2bf(x[1]));
-    f.v[2] = static_cast<short>(f2bf(x[2]));
-    f.v[3] = static_cast<short>(f2bf(x[3]));
+    frag f;  // two v_cvt_pk_bf16_f32 (round to nearest even)
+    f.v = __builtin_bit_cast(s16x4, __builtin_convertvector(x, bf16x4));
     return f;
   }
   __device__ static __forceinline__ frag zero() {
@@ -87,15 +85,12 @@ template <> struct frag<bf16_t> {
     return f;
   }
   __device__ __forceinline__ f32x4 to_f32() const {
-    f32x4 r;
-    for (int i = 0; i < 4; ++i)
-      r[i] = bf2f(static_cast<bf16_t>(v[i]));
-    return r;
+    return __builtin_convertvector(__builtin_bit_cast(bf16x4, v), f32x4);
   }
   __device__ __forceinline__ frag neg() const {
-    frag f;
-    for (int i = 0; i < 4; ++i)
-      f.v[i] = static_cast<short>(v[i] ^ static_cast<short>(0x8000));
+    frag f;  // flip the sign bits of the four halves
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+    f.v = __builtin_bit_cast(s16x4, __builtin_bit_cast(u32x2, v) ^ u32x2{0x80008000u, 0x80008000u});
     return f;
   }
   // fragment-ordered memory (LDS or global): 8 bytes per lane
@@ -147,6 +142,62 @@ __device__ __forceinline__ void mma16(f32x4 &acc, const frag<float> &a, const fr
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc, 0, 0, 0);
+}
+
+// Two fragments of adjacent 16-wide k tiles, stored interleaved per lane
+// (lane's tile-0 values, then its tile-1 values) so one vector load fetches
+// both.  mma32 adds A * B over the 32 k values of the pair: for bf16 it is a
+// single v_mfma_f32_16x16x32_bf16 whose k slot (g, i) is taken to mean k tile
+// i / 4, index 4g + i % 4 in both operands -- any assignment of k values to
+// slots gives the same sum as long as A and B agree, and this one makes a
+// pair of ColFrag accumulators a valid B operand with no data movement.
+template <typename T> struct frag2 {
+  frag<T> lo, hi;
+  __device__ static __forceinline__ frag2 ld(const void *base, int lane);
+  __device__ static __forceinline__ frag2 make(const frag<T> &a, const frag<T> &b) {
+    frag2 f;
+    f.lo = a;
+    f.hi = b;
+    return f;
+  }
+};
+
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+template <> __device__ __forceinline__ frag2<bf16_t> frag2<bf16_t>::ld(const void *base, int lane) {
+  const s16x8 x = reinterpret_cast<const s16x8 *>(base)[lane];  // one 16-byte load
+  frag2 f;
+  f.lo.v = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+  f.hi.v = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+  return f;
+}
+template <> __device__ __forceinline__ frag2<float> frag2<float>::ld(const void *base, int lane) {
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(base) + 2 * lane;
+  frag2 f;
+  f.lo.v = p[0];
+  f.hi.v = p[1];
+  return f;
+}
+
+__device__ __forceinline__ void mma32(f32x4 &acc, const frag2<bf16_t> &a, const frag2<bf16_t> &b) {
+  const s16x8 av = __builtin_shufflevector(a.lo.v, a.hi.v, 0, 1, 2, 3, 4, 5, 6, 7);
+  const s16x8 bv = __builtin_shufflevector(b.lo.v, b.hi.v, 0, 1, 2, 3, 4, 5, 6, 7);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x4 &acc, const frag2<float> &a, const frag2<float> &b) {
+  mma16(acc, a.lo, b.lo);
+  mma16(acc, a.hi, b.hi);
+}
+
+// Byte offset of the fragment of tile (r, kk) for `lane` in a tile array with
+// NKK k tiles per row r: k tiles are paired (frag2 order) when NKK is even.
+template <typename T, int NKK>
+__host__ __device__ constexpr size_t tile_off(int r, int kk, int lane) {
+  return (NKK % 2 == 0)
+             ? ((static_cast<size_t>(r * (NKK / 2) + kk / 2) * 64 + lane) * 2 + (kk & 1)) * sizeof(frag<T>)
+             : (static_cast<size_t>(r * NKK + kk) * 64 + lane) * sizeof(frag<T>);
 }
 
 // ColFrag of the 16x16 identity for this lane
