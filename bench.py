@@ -53,10 +53,12 @@ def flops_per_token_head(d: int, C: int) -> float:
 #   prep : read the six inputs, write -W, Q', Kbar^T, Ut, O_intra (bf16) and
 #          gamma_C (fp32, one d-vector per chunk)
 #   scan : read -W, Q', Kbar^T, Ut, O_intra and gamma_C, write o
+#   fused: the path itself (inputs once, o once)
 def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
     gam = d * 4 / C
     return {
         "path": 6 * d * elem + d * elem,
+        "chunk_fused": 6 * d * elem + d * elem,
         "chunk_prep": 6 * d * elem + 5 * d * elem + gam,
         "chunk_scan": 5 * d * elem + gam + d * elem,
     }
@@ -130,6 +132,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "two_pass"],
+                    help="chunked kernels to time (default: the library's own choice)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -154,7 +158,8 @@ def main() -> int:
                      device="cuda")
 
     def step():
-        g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws)
+        g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws,
+                    path=args.path)
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -215,7 +220,7 @@ def main() -> int:
             o2 = o.view(Bs, Ts, H, d)
             Sf2 = torch.empty((Bs, H, d, d), dtype=torch.float32, device="cuda")
             sec_s = timed_steps(lambda: g.chunk_fwd(*(view[x] for x in NAMES), chunk=C, out=o2,
-                                                    S_final=Sf2, workspace=ws), 20, 3)
+                                                    S_final=Sf2, workspace=ws, path=args.path), 20, 3)
             sweep[str(Ts)] = round(32768 / sec_s, 1)
         vals = list(sweep.values())
         out["sweep_tokens_per_s"] = sweep
@@ -229,7 +234,7 @@ def main() -> int:
                           dtype=torch.uint8, device="cuda")
         sec_p = timed_steps(lambda: g.chunk_fwd(*(packed[x] for x in NAMES), cu_seqlens=cu,
                                                 chunk=C, out=o.view(1, 32768, H, d), S_final=Sp,
-                                                workspace=wsp), 20, 3)
+                                                workspace=wsp, path=args.path), 20, 3)
         out["packed"] = {"tokens_per_s": round(32768 / sec_p, 1), "num_seqs": len(lens),
                          "ms": round(sec_p * 1e3, 4)}
 

@@ -25,6 +25,9 @@ LIB_PATH = os.path.join(_HERE, "libgdn2.so")
 
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_RECURRENT = 1 << 1
+FLAG_TWO_PASS = 1 << 2
+FLAG_FUSED = 1 << 3
+PATHS = {"auto": 0, "recurrent": FLAG_RECURRENT, "two_pass": FLAG_TWO_PASS, "fused": FLAG_FUSED}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
 _lib = None
@@ -100,9 +103,13 @@ def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chu
 
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
               recurrent: bool = False, out=None, S_final=None, workspace=None,
-              want_final: bool = True):
-    """Chunked forward (or the token-recurrent kernel when ``recurrent``).
-    Returns (o, S_final); S_final is None when ``want_final`` is False."""
+              want_final: bool = True, path: str = "auto"):
+    """Chunked forward.  ``path`` selects the kernels: "auto" (the library
+    chooses), "fused" (single pass), "two_pass", or "recurrent" (token by
+    token; also selected by ``recurrent=True``).  Returns (o, S_final);
+    S_final is None when ``want_final`` is False."""
+    if recurrent:
+        path = "recurrent"
     _require_device(q, k, v, alpha, b, w, S0, cu_seqlens)
     dt = _dtype_code(q)
     for t in (k, v, alpha, b, w):
@@ -122,9 +129,9 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
     Sf = S_final
     if Sf is None and want_final:
         Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    flags = FLAG_RECURRENT if recurrent else 0
+    flags = PATHS[path]
     ws_bytes = 0
-    if not recurrent:
+    if path != "recurrent":
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)

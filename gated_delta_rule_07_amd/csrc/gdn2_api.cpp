@@ -99,14 +99,38 @@ size_t chunk_block_bytes_rt(gdn2_dtype_t dt, int d, int c) {
   return 0;
 }
 
+// Path choice for the chunked forward.  0 = two-pass, otherwise the column
+// group count NG of the single-pass kernel.
+template <typename IO, int D, int C> int choose_fused(long units, uint32_t flags) {
+  const bool f1 = gdn2::fused_supported<IO, D, C, 1>();
+  const bool f2 = gdn2::fused_supported<IO, D, C, 2>();
+  if (flags & GDN2_FLAG_TWO_PASS)
+    return 0;
+  if (flags & GDN2_FLAG_FUSED)
+    return (units >= 192 || !f2) ? (f1 ? 1 : -1) : 2;
+  // Default: two-pass.  On MI355X the single-pass kernel is bound by the
+  // serial latency of its per-chunk phases (one workgroup per head cannot hide
+  // it), and measured slower than the two-pass kernels at every shape of the
+  // benchmark (B*T = 32768, H = 16, d = 128), so it is opt-in.
+  (void)units;
+  return 0;
+}
+
 template <typename IO, int D, int C>
-hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, hipStream_t st) {
+hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, uint32_t flags, hipStream_t st) {
   hipError_t e = hipSuccess;
+  const int ng = choose_fused<IO, D, C>(static_cast<long>(a.num_seqs) * a.H, flags);
+  if (ng < 0)
+    return hipErrorInvalidConfiguration;
   if (a.cu) {
     prof_scope p("chunk_table", st);
     e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
     if (e != hipSuccess)
       return e;
+  }
+  if (ng > 0) {
+    prof_scope p("chunk_fused", st);
+    return ng == 1 ? gdn2::launch_fused<IO, D, C, 1>(a, st) : gdn2::launch_fused<IO, D, C, 2>(a, st);
   }
   {
     prof_scope p("chunk_prep", st);
@@ -121,10 +145,11 @@ hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, hipStream_t st) {
   return e;
 }
 
-hipError_t dispatch_chunk(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, hipStream_t st) {
+hipError_t dispatch_chunk(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, uint32_t flags,
+                          hipStream_t st) {
 #define GDN2_RC(IO, D, C) \
   if (d == D && c == C)   \
-    return run_chunk<IO, D, C>(a, C, st);
+    return run_chunk<IO, D, C>(a, C, flags, st);
   if (dt == GDN2_F32) {
     GDN2_RC(float, 16, 16) GDN2_RC(float, 32, 16) GDN2_RC(float, 64, 16) GDN2_RC(float, 128, 16)
     GDN2_RC(float, 16, 64) GDN2_RC(float, 32, 64) GDN2_RC(float, 64, 64) GDN2_RC(float, 128, 64)
@@ -135,6 +160,22 @@ hipError_t dispatch_chunk(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args 
   }
 #undef GDN2_RC
   return hipErrorInvalidValue;
+}
+
+bool fused_available(gdn2_dtype_t dt, int d, int c) {
+#define GDN2_FA(IO, D, C) \
+  if (d == D && c == C)   \
+    return gdn2::fused_supported<IO, D, C, 1>();
+  if (dt == GDN2_F32) {
+    GDN2_FA(float, 16, 16) GDN2_FA(float, 32, 16) GDN2_FA(float, 64, 16) GDN2_FA(float, 128, 16)
+    GDN2_FA(float, 16, 64) GDN2_FA(float, 32, 64) GDN2_FA(float, 64, 64) GDN2_FA(float, 128, 64)
+  } else {
+    GDN2_FA(gdn2::bf16_t, 16, 16) GDN2_FA(gdn2::bf16_t, 32, 16) GDN2_FA(gdn2::bf16_t, 64, 16)
+    GDN2_FA(gdn2::bf16_t, 128, 16) GDN2_FA(gdn2::bf16_t, 16, 64) GDN2_FA(gdn2::bf16_t, 32, 64)
+    GDN2_FA(gdn2::bf16_t, 64, 64) GDN2_FA(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_FA
+  return false;
 }
 
 hipError_t dispatch_recurrent(gdn2_dtype_t dt, int d, const void *q, const void *k, const void *v,
@@ -208,8 +249,14 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
                              void *stream) {
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unknown dtype %d", static_cast<int>(dt));
-  if (flags & ~static_cast<uint32_t>(GDN2_FLAG_RECURRENT))
+  const uint32_t known = GDN2_FLAG_RECURRENT | GDN2_FLAG_TWO_PASS | GDN2_FLAG_FUSED;
+  if (flags & ~known)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: unknown flags 0x%x", flags);
+  {
+    const uint32_t paths = flags & known;
+    if (paths & (paths - 1))
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: flags 0x%x name more than one path", flags);
+  }
   if (B <= 0 || T < 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: bad sizes B=%d T=%d H=%d", B, T, H);
   if (dk != dv || !supported_dim(dk))
@@ -290,7 +337,10 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     // no tokens: the scan kernel alone copies S0 (or zeros) to S_final
     a.num_slots = 0;
   }
-  const hipError_t e = dispatch_chunk(dt, dk, chunk, a, st);
+  if ((flags & GDN2_FLAG_FUSED) && !fused_available(dt, dk, chunk))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: no single-pass kernel for dtype %d, dk=%d, chunk=%d",
+                static_cast<int>(dt), dk, chunk);
+  const hipError_t e = dispatch_chunk(dt, dk, chunk, a, flags, st);
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -1,184 +1,29 @@
-// gdn2_chunk.hip -- chunkwise-parallel GDN-2 forward for gfx950.
+// gdn2_chunk.hip -- two-pass chunkwise GDN-2 forward for gfx950.
 //
-// The recurrence (see gdn2_recurrent.hip) is re-parallelised over chunks of C
-// tokens, as the pages describe: split the sequence into chunks, use matrix
-// products inside each chunk, build in-chunk WY auxiliary matrices with the
-// erase gate inside the key products and the write gate inside the delta
-// values, and absorb the per-channel decay into the erase factors (aixai.ru
-// blog, implementation section; aiexpert.news/pt, method paragraph).
-//
-// Derivation used here (one head, one chunk, tokens t = 1..C, entering state
-// S0).  With g_t the running sum of log alpha from the chunk start and
-// gamma_t = exp(g_t) (per key channel), write S_t = Diag(gamma_t) X_t.  Then
-// X_t = X_{t-1} + khat_t z_t^T with khat_t = k_t / gamma_t, and
-//   z_t = w_t (.) v_t - X_{t-1}^T echk_t,   echk_t = b_t (.) k_t (.) gamma_t.
-// Collecting the C delta values z_t in Z (C x dv):
-//   (I + A) Z = U - E S0,  A = strict_lower(E Khat^T),  U_t = w_t (.) v_t
-//   Z = Ut - W S0          with T = (I + A)^{-1}, W = T E, Ut = T U
-//   O = Qchk S0 + P Z      with Qchk_t = q_t (.) gamma_t, P = lower_incl(Qchk Khat^T)
-//     = Q' S0 + O_intra    with Q' = Qchk - P W, O_intra = P Ut
-//   S_C = Diag(gamma_C) S0 + Kbar^T Z,   Kbar_t = k_t (.) gamma_C / gamma_t.
-// W, Ut, Q', O_intra, Kbar and gamma_C depend only on the chunk's own inputs
-// (kernel 1, fully parallel over chunks and heads); the entering state only
-// enters through three state-sized products per chunk (kernel 2, sequential
-// over chunks, parallel over sequences, heads and 16-column slices of dv).
-//
-// Numerics of the decay factorisation: every factor exp(g_t - g_s) with s <= t
-// is at most 1, but splitting it as gamma_t / gamma_s can overflow.  A and P
-// are therefore built per 16-token sub-block with the reference point at the
-// start of the row's own sub-block I:
-//   A[t][s] = sum_c (b k_t e^{g_t - rho_I}) (e^{rho_I - rho_J}) (k_s e^{rho_J - g_s})
-// for s in sub-block J <= I, rho_J = g just before sub-block J.  The first and
-// middle factors are <= 1; the last is bounded by the decay over one 16-token
-// sub-block.  E, Qchk and Kbar use the chunk start / chunk end and are <= 1.
-//
-// Matrix products use the fragment convention of gdn2_device.hpp.  Kernel 1
-// runs one wave per 16-token sub-block (4 waves for C = 64):
-//   phase 1  loads, log2(alpha), in-wave prefix sum over tokens, block totals
-//   phase 2  A and P sub-block rows (matrix cores)
-//   phase 3  T = (I + A)^{-1}: 16x16 diagonal inverses by forward substitution
-//            (every lane solves one column), off-diagonal blocks level by
-//            level with T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ (matrix cores)
-//   phase 4  W = T E, Ut = T U
-//   phase 5  Q' = Qchk - P W (computed transposed, so that it lands in the
-//            operand layout kernel 2 reads), O_intra = P Ut
-// Intermediates go to the workspace in fragment order, so kernel 2 reads every
-// operand with one coalesced 8- or 16-byte load per lane and keeps the state
-// in matrix-core accumulators for the whole sequence.
-#include "gdn2_device.hpp"
-#include "gdn2_kernels.hpp"
+// Pass 1 (gdn2_chunk_prep_kernel) runs the per-chunk phases of gdn2_wy.hpp for
+// every (chunk, head) in parallel and writes the chunk's -W, Q', Kbar^T,
+// gamma_C, Ut and O_intra to the workspace in fragment order.  Pass 2
+// (gdn2_chunk_scan_kernel) walks the chunks of each sequence in order with
+// the state in matrix-core accumulators.  This path keeps the whole GPU busy
+// when there are few (sequence, head) units (long sequences, small batch);
+// gdn2_fused.hip does both passes in one workgroup per head and avoids the
+// workspace round trip when there are enough units.  gdn2_chunk_table_kernel
+// builds the per-sequence chunk offsets of packed input.
+#include "gdn2_wy.hpp"
 
 namespace gdn2 {
 
-// raw 4-element loads (kept packed until first use)
-template <typename IO> struct raw4;
-template <> struct raw4<float> {
-  f32x4 x;
-  __device__ static __forceinline__ raw4 ld(const float *p) {
-    raw4 r;
-    r.x = *reinterpret_cast<const f32x4 *>(p);
-    return r;
-  }
-  __device__ static __forceinline__ raw4 fill(float v) {
-    raw4 r;
-    r.x = f32x4{v, v, v, v};
-    return r;
-  }
-  __device__ __forceinline__ f32x4 f() const { return x; }
-};
-template <> struct raw4<bf16_t> {
-  uint2 x;
-  __device__ static __forceinline__ raw4 ld(const bf16_t *p) {
-    raw4 r;
-    r.x = *reinterpret_cast<const uint2 *>(p);
-    return r;
-  }
-  __device__ static __forceinline__ raw4 fill(float v) {
-    const uint32_t h = f2bf(v);
-    raw4 r;
-    r.x.x = h | (h << 16);
-    r.x.y = r.x.x;
-    return r;
-  }
-  __device__ __forceinline__ f32x4 f() const {
-    f32x4 r;
-    r[0] = __builtin_bit_cast(float, x.x << 16);
-    r[1] = __builtin_bit_cast(float, x.x & 0xffff0000u);
-    r[2] = __builtin_bit_cast(float, x.y << 16);
-    r[3] = __builtin_bit_cast(float, x.y & 0xffff0000u);
-    return r;
-  }
-};
-
-__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-// Per (chunk slot, head) block of intermediates, all tiles fragment-ordered.
-// The first SHARED bytes (-W, Q', Kbar^T, gamma_C) are what every column
-// slice of the state scan needs; they are copied to LDS as one block.  A
-// operands of the scan are stored with their 16-wide k tiles paired
-// (tile_off), so one 16-byte load yields a 16x16x32 operand.
-template <typename IO, int D, int C> struct blk_layout {
-  static constexpr int NB = C / 16, NK = D / 16;
-  static constexpr size_t TB = frag<IO>::TILE_BYTES;
-  static constexpr size_t WN = 0;                   // rows tt, k tiles over dk: RowFrag(-W)
-  static constexpr size_t QP = WN + NB * NK * TB;   // rows tt, k tiles over dk: RowFrag(Q')
-  static constexpr size_t KB = QP + NB * NK * TB;   // rows dk tile, k tiles over tokens: RowFrag(Kbar^T)
-  static constexpr size_t GAM = KB + NK * NB * TB;  // [D] float gamma_C
-  static constexpr size_t SHARED = (GAM + D * sizeof(float) + 1023) & ~static_cast<size_t>(1023);
-  static constexpr size_t UT = SHARED;              // [NB][NK] ColFrag(Ut)
-  static constexpr size_t OI = UT + NB * NK * TB;   // [NB][NK] ColFrag(O_intra)
-  static constexpr size_t BYTES = align256(OI + NB * NK * TB);
-};
-
 template <typename IO, int D, int C> size_t chunk_block_bytes() { return blk_layout<IO, D, C>::BYTES; }
 
-// chunk slot -> (sequence, first token (flat index), valid length)
-template <int C>
-__device__ __forceinline__ bool locate_chunk(int slot, const chunk_args &a, int &seq, long &t0,
-                                             int &len) {
-  if (a.cu) {
-    const int total = a.offsets[a.num_seqs];
-    if (slot >= total)
-      return false;
-    int lo = 0, hi = a.num_seqs - 1;  // largest n with offsets[n] <= slot
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.offsets[mid] <= slot)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    seq = lo;
-    t0 = static_cast<long>(a.cu[lo]) + static_cast<long>(slot - a.offsets[lo]) * C;
-    const long rem = static_cast<long>(a.cu[lo + 1]) - t0;
-    len = rem < C ? static_cast<int>(rem) : C;
-    return true;
-  }
-  const int nc = (a.T + C - 1) / C;
-  seq = slot / nc;
-  const int c = slot - seq * nc;
-  t0 = static_cast<long>(seq) * a.T + static_cast<long>(c) * C;
-  len = (a.T - c * C) < C ? (a.T - c * C) : C;
-  return seq < a.num_seqs;
-}
-
-template <typename IO, int D, int C> struct prep_smem {
-  static constexpr int NB = C / 16, NK = D / 16;
-  static constexpr int NP = NB * (NB - 1) / 2;  // sub-block pairs J < I
-  static constexpr int NT = NB * (NB + 1) / 2;  // sub-block pairs J <= I
-  static constexpr int NKS = (NP > NB ? NP : NB);
-  static constexpr int TB = frag<IO>::TILE_BYTES;
-  float tot[NB][D];                  // per-sub-block sum of log2(alpha)
-  float f1[NB][D];                   // exp2(rho_I): decay from chunk start to sub-block I
-  float f2[NB][D];                   // exp2(g_C - rho_I): decay from sub-block I to chunk end
-  float sig[NP > 0 ? NP : 1][D];     // exp2(rho_I - rho_J) <= 1 for the pair (I, J), J < I
-  float ad[NB][16][16];              // diagonal blocks of A, row-major
-  // RowFrag(Khat_J * sig_IJ) for each pair (I, J), k tiles paired; after the
-  // A/P products the same bytes hold RowFrag(Qchk) tiles [NB][NK]
-  alignas(16) unsigned char khs[NKS][NK][TB];
-  alignas(16) unsigned char ec[NB][NK][TB];  // ColFrag(E_J), one tile per 16 channels
-  alignas(16) unsigned char pr[NT][TB];      // RowFrag(P_IJ)
-  alignas(16) unsigned char tcol[NT][TB];    // ColFrag(T_IJ)
-  alignas(16) unsigned char trow[NT][TB];    // RowFrag(T_IJ)
-};
-
-__device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
-__device__ __forceinline__ constexpr int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
-
-// Kernel 1: per-chunk prep + in-chunk WY/UT factor.  grid: num_slots * H,
-// block: 64 * C/16 threads.  Wave I owns the 16-token sub-block I for the
-// row-wise phases (loads, decay prefix sums, A and P rows, T rows) and
-// column tiles [I*CTW, I*CTW + CTW) of dk and dv for the column-wise phases
-// (W, Ut, Q', O_intra), so every wave does the same amount of matrix work.
+// Pass 1.  grid: num_slots * H, block: 64 * C/16 threads (see gdn2_wy.hpp for
+// the work split between waves).
 template <typename IO, int D, int C>
 __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_args a) {
   constexpr int NB = C / 16, NK = D / 16;
   constexpr int CTW = (NK >= NB) ? NK / NB : 1;  // column tiles per wave
   typedef frag<IO> F;
-  typedef frag2<IO> F2;
   typedef blk_layout<IO, D, C> L;
-  typedef prep_smem<IO, D, C> SM;
-  __shared__ SM sm;
+  __shared__ wy_smem<IO, D, C> sm;
 
   const int h = blockIdx.x % a.H;
   const int slot = blockIdx.x / a.H;
@@ -188,275 +33,46 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
     return;  // whole workgroup leaves together
   (void)seq;
   const int tid = threadIdx.x;
-  const int I = tid >> 6;  // sub-block (row phases) of this wave
+  const int I = tid >> 6;
   const int lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int t = 16 * I + m;  // token within the chunk
-  const bool valid = t < len;
-  const int ct0 = I * CTW;    // first column tile (column phases)
+  const int ct0 = I * CTW;
   const bool owner = ct0 < NK;
   unsigned char *blk = reinterpret_cast<unsigned char *>(a.blocks) +
                        (static_cast<size_t>(slot) * a.H + h) * a.blk_bytes;
-  auto row_of = [&](int tok) { return static_cast<size_t>(t0 + tok) * a.H + h; };
-  const IO *qp = static_cast<const IO *>(a.q) + row_of(valid ? t : 0) * D;
-  const IO *kp = static_cast<const IO *>(a.k) + row_of(valid ? t : 0) * D;
-  const IO *ap = static_cast<const IO *>(a.al) + row_of(valid ? t : 0) * D;
-  const IO *bp = static_cast<const IO *>(a.b) + row_of(valid ? t : 0) * D;
 
-  // ---------------- phase 1: loads, log-decay prefix sums, block totals
-  raw4<IO> rq[NK], rk[NK], rb[NK];
-  f32x4 gl[NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const int c0 = 16 * kk + 4 * g;
-    if (valid) {
-      rq[kk] = raw4<IO>::ld(qp + c0);
-      rk[kk] = raw4<IO>::ld(kp + c0);
-      rb[kk] = raw4<IO>::ld(bp + c0);
-      const f32x4 al = raw4<IO>::ld(ap + c0).f();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gl[kk][i] = fast_log2(al[i]);
-    } else {
-      rq[kk] = rk[kk] = rb[kk] = raw4<IO>::fill(0.f);
-      gl[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  // values and write gates of every sub-block, for this wave's column tiles
+  wy_rows<IO, D> r;
+  wy_load_rows<IO, D>(a, t0, len, h, 16 * I + m, g, r);
   raw4<IO> rv[NB][CTW], rw[NB][CTW];
-#pragma unroll
-  for (int J = 0; J < NB; ++J) {
-    const int tj = 16 * J + m;
-    const bool vj = owner && tj < len;
-    const IO *vp = static_cast<const IO *>(a.v) + row_of(vj ? tj : 0) * D;
-    const IO *wp = static_cast<const IO *>(a.w) + row_of(vj ? tj : 0) * D;
-#pragma unroll
-    for (int j = 0; j < CTW; ++j) {
-      const int c0 = 16 * (ct0 + j) + 4 * g;
-      if (vj) {
-        rv[J][j] = raw4<IO>::ld(vp + c0);
-        rw[J][j] = raw4<IO>::ld(wp + c0);
-      } else {
-        rv[J][j] = rw[J][j] = raw4<IO>::fill(0.f);
-      }
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      gl[kk][i] = row16_inclusive_scan(gl[kk][i]);
-  if (m == 15) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      *reinterpret_cast<f32x4 *>(&sm.tot[I][16 * kk + 4 * g]) = gl[kk];
-  }
-  __syncthreads();
-
-  // per-channel decay factors between sub-block boundaries
-  for (int idx = tid; idx < NB * D; idx += 64 * NB) {
-    const int J = idx / D, c = idx - J * D;
-    float rho = 0.f, suf = 0.f;
-#pragma unroll
-    for (int K = 0; K < NB; ++K) {
-      const float x = sm.tot[K][c];
-      if (K < J)
-        rho += x;
-      else
-        suf += x;
-    }
-    sm.f1[J][c] = fast_exp2(rho);
-    sm.f2[J][c] = fast_exp2(suf);
-    float part = 0.f;  // sum of tot over sub-blocks J .. I2-1
-#pragma unroll
-    for (int I2 = 1; I2 < NB; ++I2) {
-      if (I2 > J) {
-        part += sm.tot[I2 - 1][c];
-        sm.sig[pair_index(I2, J)][c] = fast_exp2(part);
-      }
-    }
-    if (J == 0)
-      reinterpret_cast<float *>(blk + L::GAM)[c] = fast_exp2(suf);
-  }
-  __syncthreads();
-
-  // ---------------- phase 1b: decayed, gated operands
+  wy_load_vw<IO, D, C, CTW>(a, t0, len, h, ct0, owner, m, g, rv, rw);
+  f32x4 gl[NK];
+  wy_decay<IO, D, C>(sm, r, gl, I, tid, reinterpret_cast<float *>(blk + L::GAM));
   const F eye = identity_colfrag<IO>(lane);
-  F ef[NK], qf[NK], khf[NK], qcf[NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const int c0 = 16 * kk + 4 * g;
-    const f32x4 f1v = *reinterpret_cast<const f32x4 *>(&sm.f1[I][c0]);
-    const f32x4 f2v = *reinterpret_cast<const f32x4 *>(&sm.f2[I][c0]);
-    f32x4 f, fi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = fast_exp2(gl[kk][i]);    // e^{g_t - rho_I} <= 1
-      fi[i] = fast_exp2(-gl[kk][i]);  // e^{rho_I - g_t} >= 1
-    }
-    const f32x4 kf = rk[kk].f();
-    const f32x4 er = rb[kk].f() * kf * f;
-    const f32x4 qr = rq[kk].f() * f;
-    const f32x4 kh = kf * fi;
-    ef[kk] = F::from(er);
-    qf[kk] = F::from(qr);
-    khf[kk] = F::from(kh);
-    qcf[kk] = F::from(qr * f1v);
-    // keys of this sub-block rescaled to the reference point of each later one
-#pragma unroll
-    for (int I2 = 1; I2 < NB; ++I2) {
-      if (I2 > I) {
-        const f32x4 s = *reinterpret_cast<const f32x4 *>(&sm.sig[pair_index(I2, I)][c0]);
-        F::from(kh * s).st(&sm.khs[pair_index(I2, I)][0][0] + tile_off<IO, NK>(0, kk, lane), 0);
-      }
-    }
-    F::from(transpose_frag(F::from(er * f1v), eye)).st(sm.ec[I][kk], lane);
-    F::from(transpose_frag(F::from(kh * f2v), eye)).st(blk + L::KB + tile_off<IO, NB>(kk, I, lane), 0);
-  }
-  // ColFrag(U_J) = ColFrag(w (.) v) of the own column tiles
+  wy_ops<IO, D> op;
+  wy_operands<IO, D, C>(sm, r, gl, I, lane, eye, blk + L::KB, op);
   F ucol[NB][CTW];
-#pragma unroll
-  for (int J = 0; J < NB; ++J)
-#pragma unroll
-    for (int j = 0; j < CTW; ++j)
-      ucol[J][j] = F::from(transpose_frag(F::from(rw[J][j].f() * rv[J][j].f()), eye));
+  wy_values<IO, NB, CTW>(rv, rw, eye, ucol);
   __syncthreads();
-
-  // ---------------- phase 2: A and P rows of sub-block I, as RowFrag
-  f32x4 accA[NB], accP[NB];
-#pragma unroll
-  for (int J = 0; J < NB; ++J) {
-    accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (J < I) {
-      const unsigned char *kb = &sm.khs[pair_index(I, J)][0][0];
-      if constexpr (NK % 2 == 0) {
-#pragma unroll
-        for (int kp = 0; kp < NK / 2; ++kp) {
-          const F2 a2 = F2::ld(kb + tile_off<IO, NK>(0, 2 * kp, 0), lane);
-          mma32(accA[J], a2, F2::make(ef[2 * kp], ef[2 * kp + 1]));
-          mma32(accP[J], a2, F2::make(qf[2 * kp], qf[2 * kp + 1]));
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          const F a1 = F::ld(kb + tile_off<IO, NK>(0, kk, 0), lane);
-          mma16(accA[J], a1, ef[kk]);
-          mma16(accP[J], a1, qf[kk]);
-        }
-      }
-    } else if (J == I) {
-      if constexpr (NK % 2 == 0) {
-#pragma unroll
-        for (int kp = 0; kp < NK / 2; ++kp) {
-          const F2 a2 = F2::make(khf[2 * kp], khf[2 * kp + 1]);
-          mma32(accA[J], a2, F2::make(ef[2 * kp], ef[2 * kp + 1]));
-          mma32(accP[J], a2, F2::make(qf[2 * kp], qf[2 * kp + 1]));
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          mma16(accA[J], khf[kk], ef[kk]);
-          mma16(accP[J], khf[kk], qf[kk]);
-        }
-      }
-      // lane (t = m, g) holds row t, columns s = 4g + i of the diagonal block
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!(4 * g + i < m))
-          accA[J][i] = 0.f;
-        if (!(4 * g + i <= m))
-          accP[J][i] = 0.f;
-      }
-      *reinterpret_cast<f32x4 *>(&sm.ad[I][m][4 * g]) = accA[J];
-    }
-    if (J <= I)
-      F::from(accP[J]).st(sm.pr[tri_index(I, J)], lane);
-  }
   F af[NB];
-#pragma unroll
-  for (int K = 0; K < NB; ++K)
-    af[K] = F::from(accA[K]);
-  __syncthreads();
-  // the rescaled keys are consumed: their bytes now hold RowFrag(Qchk)
-  unsigned char *qc_tiles = &sm.khs[0][0][0];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-    qcf[kk].st(qc_tiles + (I * NK + kk) * SM::TB, lane);
-
-  // ---------------- phase 3: T = (I + A)^{-1}
-  {
-    // diagonal block: lane column c = m, rows kept: 4g .. 4g+3
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == m) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < i; ++j)
-        acc -= sm.ad[I][i][j] * x[j];
-      x[i] = acc;
-    }
-    f32x4 tii;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      tii[i] = (g == 0) ? x[i] : (g == 1) ? x[4 + i] : (g == 2) ? x[8 + i] : x[12 + i];
-    const F tf = F::from(tii);
-    tf.st(sm.tcol[tri_index(I, I)], lane);
-    F::from(transpose_frag(tf, eye)).st(sm.trow[tri_index(I, I)], lane);
-  }
-  __syncthreads();
-  const F trow_ii = F::ld(sm.trow[tri_index(I, I)], lane);
-#pragma unroll
-  for (int l = 1; l < NB; ++l) {
-    if (I >= l) {
-      const int J = I - l;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int K = 0; K < NB; ++K)
-        if (K >= J && K < I)
-          mma16(acc, af[K], F::ld(sm.tcol[tri_index(K, J)], lane));
-      f32x4 tij = {0.f, 0.f, 0.f, 0.f};
-      mma16(tij, trow_ii, F::from(acc));
-      const F tf = F::from(-tij);
-      tf.st(sm.tcol[tri_index(I, J)], lane);
-      F::from(transpose_frag(tf, eye)).st(sm.trow[tri_index(I, J)], lane);
-    }
-    __syncthreads();
-  }
-
-  // ---------------- phases 4-5, by column tile: W = T E, Ut = T U,
-  // Q' = Qchk - P W (computed as Q'^T so it lands as RowFrag), O_intra = P Ut
+  wy_products<IO, D, C>(sm, op, I, lane, af);
+  wy_inverse<IO, D, C>(sm, af, I, lane, eye);
   if (owner) {
+    wy_tp<IO, C> tp;
+    wy_load_tp<IO, D, C>(sm, lane, tp);
 #pragma unroll
     for (int j = 0; j < CTW; ++j) {
       const int ct = ct0 + j;
-      F wc[NB], uc[NB];
+      wy_wq<IO, D, C>(sm, tp, ct, lane, eye, blk + L::WN, blk + L::QP);
+      F uc_j[NB];
+#pragma unroll
+      for (int J = 0; J < NB; ++J)
+        uc_j[J] = ucol[J][j];
+      f32x4 ut[NB], oi[NB];
+      wy_uo<IO, C>(tp, uc_j, ut, oi);
 #pragma unroll
       for (int I2 = 0; I2 < NB; ++I2) {
-        f32x4 w = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int J = 0; J <= I2; ++J) {
-          const F tr = F::ld(sm.trow[tri_index(I2, J)], lane);
-          mma16(w, tr, F::ld(sm.ec[J][ct], lane));
-          mma16(u, tr, ucol[J][j]);
-        }
-        wc[I2] = F::from(w);
-        uc[I2] = F::from(u);
-        uc[I2].st(blk + L::UT + (I2 * NK + ct) * L::TB, lane);
-        F::from(transpose_frag(wc[I2], eye)).neg().st(blk + L::WN + tile_off<IO, NK>(I2, ct, lane), 0);
-      }
-#pragma unroll
-      for (int I2 = 0; I2 < NB; ++I2) {
-        f32x4 q = F::ld(qc_tiles + (I2 * NK + ct) * SM::TB, lane).to_f32();
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int J = 0; J <= I2; ++J) {
-          const F p = F::ld(sm.pr[tri_index(I2, J)], lane);
-          mma16(q, wc[J], p.neg());
-          mma16(o, p, uc[J]);
-        }
-        F::from(q).st(blk + L::QP + tile_off<IO, NK>(I2, ct, lane), 0);
-        F::from(o).st(blk + L::OI + (I2 * NK + ct) * L::TB, lane);
+        F::from(ut[I2]).st(blk + L::UT + (I2 * NK + ct) * L::TB, lane);
+        F::from(oi[I2]).st(blk + L::OI + (I2 * NK + ct) * L::TB, lane);
       }
     }
   }

@@ -30,6 +30,8 @@ template <typename IO, int D, int C> size_t chunk_block_bytes();
 template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st);
 template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st);
+template <typename IO, int D, int C, int NG> bool fused_supported();
+template <typename IO, int D, int C, int NG> hipError_t launch_fused(const chunk_args &a, hipStream_t st);
 
 template <typename IO, int D>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,

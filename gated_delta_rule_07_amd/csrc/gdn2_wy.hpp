@@ -1,0 +1,555 @@
+// gdn2_wy.hpp -- the per-chunk part of the chunkwise GDN-2 forward, shared by
+// the two-pass path (gdn2_chunk.hip) and the fused path (gdn2_fused.hip).
+//
+// The recurrence (gdn2_recurrent.hip) is re-parallelised over chunks of C
+// tokens, as the pages describe: split the sequence into chunks, use matrix
+// products inside each chunk, build in-chunk WY auxiliary matrices with the
+// erase gate inside the key products and the write gate inside the delta
+// values, and absorb the per-channel decay into the erase factors (aixai.ru
+// blog, implementation section; aiexpert.news/pt, method paragraph).
+//
+// Derivation used here (one head, one chunk, tokens t = 1..C, entering state
+// S0).  With g_t the running sum of log alpha from the chunk start and
+// gamma_t = exp(g_t) (per key channel), write S_t = Diag(gamma_t) X_t.  Then
+// X_t = X_{t-1} + khat_t z_t^T with khat_t = k_t / gamma_t, and
+//   z_t = w_t (.) v_t - X_{t-1}^T echk_t,   echk_t = b_t (.) k_t (.) gamma_t.
+// Collecting the C delta values z_t in Z (C x dv):
+//   (I + A) Z = U - E S0,  A = strict_lower(E Khat^T),  U_t = w_t (.) v_t
+//   Z = Ut - W S0          with T = (I + A)^{-1}, W = T E, Ut = T U
+//   O = Qchk S0 + P Z      with Qchk_t = q_t (.) gamma_t, P = lower_incl(Qchk Khat^T)
+//     = Q' S0 + O_intra    with Q' = Qchk - P W, O_intra = P Ut
+//   S_C = Diag(gamma_C) S0 + Kbar^T Z,   Kbar_t = k_t (.) gamma_C / gamma_t.
+// W, Ut, Q', O_intra, Kbar and gamma_C depend only on the chunk's own inputs;
+// the entering state only enters through three state-sized products.
+//
+// Numerics of the decay factorisation: every factor exp(g_t - g_s) with s <= t
+// is at most 1, but splitting it as gamma_t / gamma_s can overflow.  A and P
+// are therefore built per 16-token sub-block with the reference point at the
+// start of the row's own sub-block I:
+//   A[t][s] = sum_c (b k_t e^{g_t - rho_I}) (k_s e^{rho_J - g_s}) e^{rho_I - rho_J}
+// for s in sub-block J <= I, rho_J = g just before sub-block J; the last
+// factor is applied to the keys of sub-block J (one rescaled copy per later
+// sub-block, shared by A and P).  The first and last factors are <= 1; the
+// middle one is bounded by the decay over one 16-token sub-block.  E, Qchk
+// and Kbar use the chunk start / chunk end and are <= 1.
+//
+// Work split inside a workgroup of C/16 waves (the "wy" phases below):
+//   rows     wave I owns the 16-token sub-block I: loads of q, k, alpha, b,
+//            log2(alpha) and its prefix sum over tokens (DPP row scan), the
+//            decayed/gated operands, the A and P rows of sub-block I, and the
+//            rows of T = (I + A)^{-1} (16x16 diagonal inverse by forward
+//            substitution, one column per lane; off-diagonal blocks level by
+//            level with T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on matrix cores)
+//   columns  wave I owns a range of 16-wide column tiles of dk (W, Q') and of
+//            dv (Ut, O_intra), so the matrix work of phases 4-5 is balanced.
+// Matrix products use the fragment convention of gdn2_device.hpp; results are
+// produced directly in the layout their consumer reads.
+#pragma once
+
+#include "gdn2_device.hpp"
+#include "gdn2_kernels.hpp"
+
+namespace gdn2 {
+
+// raw 4-element loads (kept packed until first use)
+template <typename IO> struct raw4;
+template <> struct raw4<float> {
+  f32x4 x;
+  __device__ static __forceinline__ raw4 ld(const float *p) {
+    raw4 r;
+    r.x = *reinterpret_cast<const f32x4 *>(p);
+    return r;
+  }
+  __device__ static __forceinline__ raw4 fill(float v) {
+    raw4 r;
+    r.x = f32x4{v, v, v, v};
+    return r;
+  }
+  __device__ __forceinline__ f32x4 f() const { return x; }
+};
+template <> struct raw4<bf16_t> {
+  uint2 x;
+  __device__ static __forceinline__ raw4 ld(const bf16_t *p) {
+    raw4 r;
+    r.x = *reinterpret_cast<const uint2 *>(p);
+    return r;
+  }
+  __device__ static __forceinline__ raw4 fill(float v) {
+    const uint32_t h = f2bf(v);
+    raw4 r;
+    r.x.x = h | (h << 16);
+    r.x.y = r.x.x;
+    return r;
+  }
+  __device__ __forceinline__ f32x4 f() const {
+    f32x4 r;
+    r[0] = __builtin_bit_cast(float, x.x << 16);
+    r[1] = __builtin_bit_cast(float, x.x & 0xffff0000u);
+    r[2] = __builtin_bit_cast(float, x.y << 16);
+    r[3] = __builtin_bit_cast(float, x.y & 0xffff0000u);
+    return r;
+  }
+};
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Per (chunk, head) block of intermediates, all tiles fragment-ordered.  The
+// first SHARED bytes (-W, Q', Kbar^T, gamma_C) are what every column slice of
+// the state scan needs; the scan copies them to LDS as one block.  A operands
+// of the scan are stored with their 16-wide k tiles paired (tile_off), so one
+// 16-byte load yields a 16x16x32 operand.  The fused kernel keeps the same
+// SHARED layout in LDS.
+template <typename IO, int D, int C> struct blk_layout {
+  static constexpr int NB = C / 16, NK = D / 16;
+  static constexpr size_t TB = frag<IO>::TILE_BYTES;
+  static constexpr size_t WN = 0;                   // rows tt, k tiles over dk: RowFrag(-W)
+  static constexpr size_t QP = WN + NB * NK * TB;   // rows tt, k tiles over dk: RowFrag(Q')
+  static constexpr size_t KB = QP + NB * NK * TB;   // rows dk tile, k tiles over tokens: RowFrag(Kbar^T)
+  static constexpr size_t GAM = KB + NK * NB * TB;  // [D] float gamma_C
+  static constexpr size_t SHARED = (GAM + D * sizeof(float) + 1023) & ~static_cast<size_t>(1023);
+  static constexpr size_t UT = SHARED;              // [NB][NK] ColFrag(Ut)
+  static constexpr size_t OI = UT + NB * NK * TB;   // [NB][NK] ColFrag(O_intra)
+  static constexpr size_t BYTES = align256(OI + NB * NK * TB);
+};
+
+// chunk slot -> (sequence, first token (flat index), valid length)
+template <int C>
+__device__ __forceinline__ bool locate_chunk(int slot, const chunk_args &a, int &seq, long &t0,
+                                             int &len) {
+  if (a.cu) {
+    const int total = a.offsets[a.num_seqs];
+    if (slot >= total)
+      return false;
+    int lo = 0, hi = a.num_seqs - 1;  // largest n with offsets[n] <= slot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.offsets[mid] <= slot)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    seq = lo;
+    t0 = static_cast<long>(a.cu[lo]) + static_cast<long>(slot - a.offsets[lo]) * C;
+    const long rem = static_cast<long>(a.cu[lo + 1]) - t0;
+    len = rem < C ? static_cast<int>(rem) : C;
+    return true;
+  }
+  const int nc = (a.T + C - 1) / C;
+  seq = slot / nc;
+  const int c = slot - seq * nc;
+  t0 = static_cast<long>(seq) * a.T + static_cast<long>(c) * C;
+  len = (a.T - c * C) < C ? (a.T - c * C) : C;
+  return seq < a.num_seqs;
+}
+
+// sequence n -> (first chunk slot, chunk count, first token, end token)
+template <int C>
+__device__ __forceinline__ void sequence_range(int n, const chunk_args &a, int &c_begin, int &nchunks,
+                                               long &tstart, long &tend) {
+  if (a.cu) {
+    c_begin = a.offsets[n];
+    nchunks = a.offsets[n + 1] - c_begin;
+    tstart = a.cu[n];
+    tend = a.cu[n + 1];
+  } else {
+    const int nc = (a.T + C - 1) / C;
+    c_begin = n * nc;
+    nchunks = nc;
+    tstart = static_cast<long>(n) * a.T;
+    tend = tstart + a.T;
+  }
+}
+
+template <typename IO, int D, int C> struct wy_smem {
+  static constexpr int NB = C / 16, NK = D / 16;
+  static constexpr int NP = NB * (NB - 1) / 2;  // sub-block pairs J < I
+  static constexpr int NT = NB * (NB + 1) / 2;  // sub-block pairs J <= I
+  static constexpr int NKS = (NP > NB ? NP : NB);
+  static constexpr int TB = frag<IO>::TILE_BYTES;
+  float tot[NB][D];                  // per-sub-block sum of log2(alpha)
+  float f1[NB][D];                   // exp2(rho_I): decay from chunk start to sub-block I
+  float f2[NB][D];                   // exp2(g_C - rho_I): decay from sub-block I to chunk end
+  float sig[NP > 0 ? NP : 1][D];     // exp2(rho_I - rho_J) <= 1 for the pair (I, J), J < I
+  float ad[NB][16][16];              // diagonal blocks of A, row-major
+  // RowFrag(Khat_J * sig_IJ) for each pair (I, J), k tiles paired; after the
+  // A/P products the same bytes hold RowFrag(Qchk) tiles [NB][NK]
+  alignas(16) unsigned char khs[NKS][NK][TB];
+  alignas(16) unsigned char ec[NB][NK][TB];  // ColFrag(E_J), one tile per 16 channels
+  alignas(16) unsigned char pr[NT][TB];      // RowFrag(P_IJ)
+  alignas(16) unsigned char tcol[NT][TB];    // ColFrag(T_IJ)
+  alignas(16) unsigned char trow[NT][TB];    // RowFrag(T_IJ)
+};
+
+__device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
+__device__ __forceinline__ constexpr int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// Per-wave registers of one chunk's row phases.
+template <typename IO, int D> struct wy_rows {
+  static constexpr int NK = D / 16;
+  raw4<IO> q[NK], k[NK], b[NK], al[NK];
+};
+
+// Loads row t (of the chunk starting at token t0) of q, k, b, alpha: this
+// lane's four channels 16kk + 4g .. +3 of every 16-channel tile.  Rows past
+// the valid length read as zeros (alpha as one, i.e. no decay).
+template <typename IO, int D>
+__device__ __forceinline__ void wy_load_rows(const chunk_args &a, long t0, int len, int h, int t, int g,
+                                             wy_rows<IO, D> &r) {
+  constexpr int NK = D / 16;
+  const bool valid = t < len;
+  const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const int c0 = 16 * kk + 4 * g;
+    if (valid) {
+      r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
+      r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
+      r.b[kk] = raw4<IO>::ld(static_cast<const IO *>(a.b) + row * D + c0);
+      r.al[kk] = raw4<IO>::ld(static_cast<const IO *>(a.al) + row * D + c0);
+    } else {
+      r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
+      r.al[kk] = raw4<IO>::fill(1.f);
+    }
+  }
+}
+
+// Loads v and w of all C tokens for NVW column tiles starting at vt0
+// (RowFrag layout: lane (m, g) holds row 16J + m, columns 16vt + 4g .. +3).
+template <typename IO, int D, int C, int NVW>
+__device__ __forceinline__ void wy_load_vw(const chunk_args &a, long t0, int len, int h, int vt0,
+                                           bool owner, int m, int g, raw4<IO> (&v)[C / 16][NVW],
+                                           raw4<IO> (&w)[C / 16][NVW]) {
+  constexpr int NB = C / 16;
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    const int tj = 16 * J + m;
+    const bool vj = owner && tj < len;
+    const size_t row = static_cast<size_t>(t0 + (vj ? tj : 0)) * a.H + h;
+#pragma unroll
+    for (int j = 0; j < NVW; ++j) {
+      const int c0 = 16 * (vt0 + j) + 4 * g;
+      if (vj) {
+        v[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.v) + row * D + c0);
+        w[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.w) + row * D + c0);
+      } else {
+        v[J][j] = w[J][j] = raw4<IO>::fill(0.f);
+      }
+    }
+  }
+}
+
+// Phase 1: log2(alpha), prefix sums over the tokens of each sub-block, and the
+// per-channel factors between sub-block boundaries.  On return gl holds the
+// in-sub-block prefix sums g_t - rho_I.  gam_out[c] = gamma_C (may be LDS or
+// global memory).  Contains two workgroup barriers.
+template <typename IO, int D, int C>
+__device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO, D> &r, f32x4 (&gl)[D / 16],
+                                         int I, int tid, float *gam_out) {
+  constexpr int NB = C / 16, NK = D / 16;
+  const int lane = tid & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const f32x4 al = r.al[kk].f();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      gl[kk][i] = row16_inclusive_scan(fast_log2(al[i]));
+  }
+  if (m == 15) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      *reinterpret_cast<f32x4 *>(&sm.tot[I][16 * kk + 4 * g]) = gl[kk];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NB * D; idx += 64 * NB) {
+    const int J = idx / D, c = idx - J * D;
+    float rho = 0.f, suf = 0.f;
+#pragma unroll
+    for (int K = 0; K < NB; ++K) {
+      const float x = sm.tot[K][c];
+      if (K < J)
+        rho += x;
+      else
+        suf += x;
+    }
+    sm.f1[J][c] = fast_exp2(rho);
+    sm.f2[J][c] = fast_exp2(suf);
+    float part = 0.f;  // sum of tot over sub-blocks J .. I2-1
+#pragma unroll
+    for (int I2 = 1; I2 < NB; ++I2) {
+      if (I2 > J) {
+        part += sm.tot[I2 - 1][c];
+        sm.sig[pair_index(I2, J)][c] = fast_exp2(part);
+      }
+    }
+    if (J == 0)
+      gam_out[c] = fast_exp2(suf);
+  }
+  __syncthreads();
+}
+
+// Register operands of the A and P products for sub-block I.
+template <typename IO, int D> struct wy_ops {
+  static constexpr int NK = D / 16;
+  frag<IO> ef[NK], qf[NK], khf[NK], qcf[NK];
+};
+
+// Phase 1b: decayed, gated operands of sub-block I.  Writes the rescaled keys
+// for later sub-blocks and ColFrag(E) to LDS, and RowFrag(Kbar^T) tiles to
+// kb_out (the KB region of a block layout, LDS or global).
+template <typename IO, int D, int C>
+__device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows<IO, D> &r,
+                                            const f32x4 (&gl)[D / 16], int I, int lane,
+                                            const frag<IO> &eye, unsigned char *kb_out,
+                                            wy_ops<IO, D> &op) {
+  constexpr int NB = C / 16, NK = D / 16;
+  typedef frag<IO> F;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const int c0 = 16 * kk + 4 * g;
+    const f32x4 f1v = *reinterpret_cast<const f32x4 *>(&sm.f1[I][c0]);
+    const f32x4 f2v = *reinterpret_cast<const f32x4 *>(&sm.f2[I][c0]);
+    f32x4 f, fi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = fast_exp2(gl[kk][i]);    // e^{g_t - rho_I} <= 1
+      fi[i] = fast_exp2(-gl[kk][i]);  // e^{rho_I - g_t} >= 1
+    }
+    const f32x4 kf = r.k[kk].f();
+    const f32x4 er = r.b[kk].f() * kf * f;
+    const f32x4 qr = r.q[kk].f() * f;
+    const f32x4 kh = kf * fi;
+    op.ef[kk] = F::from(er);
+    op.qf[kk] = F::from(qr);
+    op.khf[kk] = F::from(kh);
+    op.qcf[kk] = F::from(qr * f1v);
+    // keys of this sub-block rescaled to the reference point of each later one
+#pragma unroll
+    for (int I2 = 1; I2 < NB; ++I2) {
+      if (I2 > I) {
+        const f32x4 s = *reinterpret_cast<const f32x4 *>(&sm.sig[pair_index(I2, I)][c0]);
+        F::from(kh * s).st(&sm.khs[pair_index(I2, I)][0][0] + tile_off<IO, NK>(0, kk, lane), 0);
+      }
+    }
+    F::from(transpose_frag(F::from(er * f1v), eye)).st(sm.ec[I][kk], lane);
+    F::from(transpose_frag(F::from(kh * f2v), eye)).st(kb_out + tile_off<IO, NB>(kk, I, lane), 0);
+  }
+}
+
+// ColFrag(U_J) = ColFrag(w (.) v) for NVW column tiles and every sub-block.
+template <typename IO, int NB, int NVW>
+__device__ __forceinline__ void wy_values(const raw4<IO> (&v)[NB][NVW], const raw4<IO> (&w)[NB][NVW],
+                                          const frag<IO> &eye, frag<IO> (&ucol)[NB][NVW]) {
+#pragma unroll
+  for (int J = 0; J < NB; ++J)
+#pragma unroll
+    for (int j = 0; j < NVW; ++j)
+      ucol[J][j] = frag<IO>::from(transpose_frag(frag<IO>::from(w[J][j].f() * v[J][j].f()), eye));
+}
+
+// Phase 2: A and P rows of sub-block I.  RowFrag(A_IK) stays in registers
+// (af), RowFrag(P_IJ) and the diagonal A block go to LDS.  Ends with a
+// barrier, after which RowFrag(Qchk) replaces the rescaled keys in LDS.
+template <typename IO, int D, int C>
+__device__ __forceinline__ void wy_products(wy_smem<IO, D, C> &sm, const wy_ops<IO, D> &op, int I, int lane,
+                                            frag<IO> (&af)[C / 16]) {
+  constexpr int NB = C / 16, NK = D / 16;
+  typedef frag<IO> F;
+  typedef frag2<IO> F2;
+  const int m = lane & 15, g = lane >> 4;
+  f32x4 accA[NB], accP[NB];
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (J < I) {
+      const unsigned char *kb = &sm.khs[pair_index(I, J)][0][0];
+      if constexpr (NK % 2 == 0) {
+#pragma unroll
+        for (int kp = 0; kp < NK / 2; ++kp) {
+          const F2 a2 = F2::ld(kb + tile_off<IO, NK>(0, 2 * kp, 0), lane);
+          mma32(accA[J], a2, F2::make(op.ef[2 * kp], op.ef[2 * kp + 1]));
+          mma32(accP[J], a2, F2::make(op.qf[2 * kp], op.qf[2 * kp + 1]));
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const F a1 = F::ld(kb + tile_off<IO, NK>(0, kk, 0), lane);
+          mma16(accA[J], a1, op.ef[kk]);
+          mma16(accP[J], a1, op.qf[kk]);
+        }
+      }
+    } else if (J == I) {
+      if constexpr (NK % 2 == 0) {
+#pragma unroll
+        for (int kp = 0; kp < NK / 2; ++kp) {
+          const F2 a2 = F2::make(op.khf[2 * kp], op.khf[2 * kp + 1]);
+          mma32(accA[J], a2, F2::make(op.ef[2 * kp], op.ef[2 * kp + 1]));
+          mma32(accP[J], a2, F2::make(op.qf[2 * kp], op.qf[2 * kp + 1]));
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          mma16(accA[J], op.khf[kk], op.ef[kk]);
+          mma16(accP[J], op.khf[kk], op.qf[kk]);
+        }
+      }
+      // lane (t = m, g) holds row t, columns s = 4g + i of the diagonal block
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!(4 * g + i < m))
+          accA[J][i] = 0.f;
+        if (!(4 * g + i <= m))
+          accP[J][i] = 0.f;
+      }
+      *reinterpret_cast<f32x4 *>(&sm.ad[I][m][4 * g]) = accA[J];
+    }
+    if (J <= I)
+      F::from(accP[J]).st(sm.pr[tri_index(I, J)], lane);
+  }
+#pragma unroll
+  for (int K = 0; K < NB; ++K)
+    af[K] = F::from(accA[K]);
+  __syncthreads();
+  unsigned char *qc_tiles = &sm.khs[0][0][0];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    op.qcf[kk].st(qc_tiles + (I * NK + kk) * wy_smem<IO, D, C>::TB, lane);
+}
+
+// Phase 3: T = (I + A)^{-1} into LDS (ColFrag and RowFrag of every block).
+// Contains NB workgroup barriers; the last one publishes all of T.
+template <typename IO, int D, int C>
+__device__ __forceinline__ void wy_inverse(wy_smem<IO, D, C> &sm, const frag<IO> (&af)[C / 16], int I, int lane,
+                                           const frag<IO> &eye) {
+  constexpr int NB = C / 16;
+  typedef frag<IO> F;
+  const int m = lane & 15, g = lane >> 4;
+  {
+    // diagonal block: lane column c = m, rows kept: 4g .. 4g+3
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == m) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j)
+        acc -= sm.ad[I][i][j] * x[j];
+      x[i] = acc;
+    }
+    f32x4 tii;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      tii[i] = (g == 0) ? x[i] : (g == 1) ? x[4 + i] : (g == 2) ? x[8 + i] : x[12 + i];
+    const F tf = F::from(tii);
+    tf.st(sm.tcol[tri_index(I, I)], lane);
+    F::from(transpose_frag(tf, eye)).st(sm.trow[tri_index(I, I)], lane);
+  }
+  __syncthreads();
+  if constexpr (NB > 1) {
+    const F trow_ii = F::ld(sm.trow[tri_index(I, I)], lane);
+#pragma unroll
+    for (int l = 1; l < NB; ++l) {
+      if (I >= l) {
+        const int J = I - l;
+        F tk[NB];
+#pragma unroll
+        for (int K = 0; K < NB; ++K)
+          tk[K] = (K >= J && K < I) ? F::ld(sm.tcol[tri_index(K, J)], lane) : F::zero();
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = 0; K < NB; ++K)
+          if (K >= J && K < I)
+            mma16(acc, af[K], tk[K]);
+        f32x4 tij = {0.f, 0.f, 0.f, 0.f};
+        mma16(tij, trow_ii, F::from(acc));
+        const F tf = F::from(-tij);
+        tf.st(sm.tcol[tri_index(I, J)], lane);
+        F::from(transpose_frag(tf, eye)).st(sm.trow[tri_index(I, J)], lane);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// T and P tiles of a chunk, loaded once by every wave for phases 4-5 (all
+// operand loads are issued before the products that use them).
+template <typename IO, int C> struct wy_tp {
+  static constexpr int NT = (C / 16) * (C / 16 + 1) / 2;
+  frag<IO> tr[NT];  // RowFrag(T_IJ)
+  frag<IO> p[NT];   // RowFrag(P_IJ)
+};
+
+template <typename IO, int D, int C>
+__device__ __forceinline__ void wy_load_tp(const wy_smem<IO, D, C> &sm, int lane, wy_tp<IO, C> &tp) {
+#pragma unroll
+  for (int i = 0; i < wy_tp<IO, C>::NT; ++i) {
+    tp.tr[i] = frag<IO>::ld(sm.trow[i], lane);
+    tp.p[i] = frag<IO>::ld(sm.pr[i], lane);
+  }
+}
+
+// Phases 4-5 for one dk column tile ct: W = T E and Q' = Qchk - P W (the latter
+// computed as Q'^T = Qchk^T - W^T P^T so that it lands as RowFrag).  Writes
+// RowFrag(-W) and RowFrag(Q') tiles to wn_out / qp_out (block layout, LDS or
+// global, k tiles paired).
+template <typename IO, int D, int C>
+__device__ __forceinline__ void wy_wq(const wy_smem<IO, D, C> &sm, const wy_tp<IO, C> &tp, int ct, int lane,
+                                      const frag<IO> &eye, unsigned char *__restrict__ wn_out,
+                                      unsigned char *__restrict__ qp_out) {
+  constexpr int NB = C / 16, NK = D / 16;
+  typedef frag<IO> F;
+  const unsigned char *qc_tiles = &sm.khs[0][0][0];
+  F ecf[NB], qcf[NB];
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    ecf[J] = F::ld(sm.ec[J][ct], lane);
+    qcf[J] = F::ld(qc_tiles + (J * NK + ct) * wy_smem<IO, D, C>::TB, lane);
+  }
+  F wc[NB];
+#pragma unroll
+  for (int I2 = 0; I2 < NB; ++I2) {
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J <= I2; ++J)
+      mma16(w, tp.tr[tri_index(I2, J)], ecf[J]);
+    wc[I2] = F::from(w);
+  }
+#pragma unroll
+  for (int I2 = 0; I2 < NB; ++I2) {
+    f32x4 q = qcf[I2].to_f32();
+#pragma unroll
+    for (int J = 0; J <= I2; ++J)
+      mma16(q, wc[J], tp.p[tri_index(I2, J)].neg());
+    F::from(transpose_frag(wc[I2], eye)).neg().st(wn_out + tile_off<IO, NK>(I2, ct, lane), 0);
+    F::from(q).st(qp_out + tile_off<IO, NK>(I2, ct, lane), 0);
+  }
+}
+
+// Phases 4-5 for one dv column tile: Ut = T U and O_intra = P Ut, returned as
+// ColFrag float accumulators (ut[I], oi[I] for the 16 rows of sub-block I).
+template <typename IO, int C>
+__device__ __forceinline__ void wy_uo(const wy_tp<IO, C> &tp, const frag<IO> (&ucol)[C / 16],
+                                      f32x4 (&ut)[C / 16], f32x4 (&oi)[C / 16]) {
+  constexpr int NB = C / 16;
+  typedef frag<IO> F;
+  F uc[NB];
+#pragma unroll
+  for (int I2 = 0; I2 < NB; ++I2) {
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J <= I2; ++J)
+      mma16(u, tp.tr[tri_index(I2, J)], ucol[J]);
+    ut[I2] = u;
+    uc[I2] = F::from(u);
+  }
+#pragma unroll
+  for (int I2 = 0; I2 < NB; ++I2) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J <= I2; ++J)
+      mma16(o, tp.p[tri_index(I2, J)], uc[J]);
+    oi[I2] = o;
+  }
+}
+
+}  // namespace gdn2

@@ -72,6 +72,11 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
 /* flags of gdn2_chunk_fwd */
 #define GDN2_FLAG_RECURRENT (1u << 1) /* token-by-token kernel instead of the
                                          chunked kernels (cross-check path) */
+#define GDN2_FLAG_TWO_PASS (1u << 2)  /* chunked path: force the two-pass kernels */
+#define GDN2_FLAG_FUSED (1u << 3)     /* chunked path: force the single-pass kernel
+                                         (GDN2_ERR_UNSUPPORTED where it has none:
+                                         chunk 64 needs dk in {64, 128}, and
+                                         float32 with dk = 128 needs chunk 16) */
 
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and
@@ -90,7 +95,12 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               sequences of length T (then N = B).  Chunks restart at every
  *               sequence boundary.
  *   B, T, H, dk, dv, num_seqs, chunk, dt : sizes; chunk is the chunk length.
- *   flags     : 0 or GDN2_FLAG_RECURRENT.
+ *   flags     : 0, or one of GDN2_FLAG_RECURRENT, GDN2_FLAG_TWO_PASS,
+ *               GDN2_FLAG_FUSED.  With 0 the library runs the two-pass
+ *               chunked kernels (all chunks in parallel, then the state
+ *               scan); GDN2_FLAG_FUSED runs the single-pass kernel (one
+ *               workgroup per head walks its chunks, no workspace traffic).
+ *               All choices compute the same recurrence.
  *   o         : output [B, T, H, dv], element type dt.
  *   S_final   : final states [N, H, dk, dv] float32, or NULL.  May alias S0.
  *   workspace : device scratch of at least
