@@ -11,6 +11,8 @@
 // builds the per-sequence chunk offsets of packed input.
 #include "gdn2_wy.hpp"
 
+#include <type_traits>
+
 namespace gdn2 {
 
 template <typename IO, int D, int C> size_t chunk_block_bytes() { return blk_layout<IO, D, C>::BYTES; }
@@ -59,6 +61,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
   if (owner) {
     wy_tp<IO, C> tp;
     wy_load_tp<IO, D, C>(sm, lane, tp);
+    F ut[CTW][NB], oi[CTW][NB];
 #pragma unroll
     for (int j = 0; j < CTW; ++j) {
       const int ct = ct0 + j;
@@ -67,49 +70,107 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
 #pragma unroll
       for (int J = 0; J < NB; ++J)
         uc_j[J] = ucol[J][j];
-      f32x4 ut[NB], oi[NB];
-      wy_uo<IO, C>(tp, uc_j, ut, oi);
+      f32x4 u4[NB], o4[NB];
+      wy_uo<IO, C, true>(tp, uc_j, u4, o4);
 #pragma unroll
       for (int I2 = 0; I2 < NB; ++I2) {
-        F::from(ut[I2]).st(blk + L::UT + (I2 * NK + ct) * L::TB, lane);
-        F::from(oi[I2]).st(blk + L::OI + (I2 * NK + ct) * L::TB, lane);
+        ut[j][I2] = F::from(u4[I2]);
+        oi[j][I2] = F::from(o4[I2]);
+      }
+    }
+#pragma unroll
+    for (int I2 = 0; I2 < NB; ++I2) {
+      if constexpr (CTW % 2 == 0 && NK % 2 == 0) {
+#pragma unroll
+        for (int j = 0; j < CTW; j += 2) {  // ct0 is even: one 16-byte store per tile pair
+          frag2<IO>::make(ut[j][I2], ut[j + 1][I2]).st(blk + L::UT + tile_off<IO, NK>(I2, ct0 + j, 0), lane);
+          frag2<IO>::make(oi[j][I2], oi[j + 1][I2]).st(blk + L::OI + tile_off<IO, NK>(I2, ct0 + j, 0), lane);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) {
+          ut[j][I2].st_at(blk + L::UT + tile_off<IO, NK>(I2, ct0 + j, lane));
+          oi[j][I2].st_at(blk + L::OI + tile_off<IO, NK>(I2, ct0 + j, lane));
+        }
       }
     }
   }
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
+// Work split of the state scan for one (sequence, head): the dv tiles go to
+// NGRP = NK / NT workgroups of NT tiles each (NT is chosen at launch from the
+// number of units), each with NCW compute waves of CPW 16-column state slices
+// and NLW loader waves.  Each LDS buffer holds the SHARED part of one chunk's
+// block and, when a tile row of the workgroup's columns is a whole number of
+// KB (UO_LDS), the workgroup's Ut and O_intra tiles (rows tt, TF tiles each:
+// its NT tiles rounded out to whole stored pairs).
+template <typename IO, int D, int C, int NT> struct scan_cfg {
+  typedef blk_layout<IO, D, C> L;
+  static constexpr int NB = C / 16, NK = D / 16;
+  static_assert(NT >= 1 && NT <= NK && NK % NT == 0, "tiles per workgroup");
+  static constexpr int CPW = (sizeof(IO) == 2 && NT >= 2) ? 2 : 1;
+  static constexpr int NCW = NT / CPW;
+  static constexpr int NGRP = NK / NT;
+  static constexpr int NTW = NT;                     // dv tiles per workgroup
+  // tiles staged per row: the workgroup's tiles rounded out to whole pairs
+  // (dv tiles are stored paired when NK is even)
+  static constexpr int TF = (NK % 2 == 0) ? (NT + 1) / 2 * 2 : NT;
+  static constexpr size_t RB = TF * L::TB;           // one staged tile row of Ut
+  static constexpr bool UO_LDS = RB % 1024 == 0;
+  static constexpr int RPP = static_cast<int>(RB / 1024);
+  static constexpr size_t BUF = L::SHARED + (UO_LDS ? 2 * NB * RB : 0);
+  static constexpr int NPS = static_cast<int>(L::SHARED / 1024);
+  static constexpr int NPIECE = static_cast<int>(BUF / 1024);  // 1 KB per wave load
+  static constexpr int NLW = NPIECE < 4 ? NPIECE : (NPIECE + 12) / 13 > 4 ? (NPIECE + 12) / 13 : 4;
+  static constexpr int PPW = (NPIECE + NLW - 1) / NLW;         // pieces per loader wave
+  static constexpr int RSETS = PPW <= 16 ? 2 : 1;              // loader register buffers
+  static constexpr int NBUF = (2 * BUF <= 160 * 1024) ? 2 : 1;
+};
 
-// Kernel 2: sequential state scan + output.  A workgroup of NW waves owns one
-// (sequence, head) and NW 16-column slices of dv; wave w keeps its slice of
-// the state S (dk x 16, float32) in matrix-core accumulators for the whole
-// sequence.  Per chunk, the shared -W, Q', Kbar^T, gamma_C block (49 KB for
-// bf16, d = 128, C = 64) is copied HBM -> LDS with global_load_lds (no
-// register staging) one chunk ahead, into the other of NBUF buffers, while
-// the waves compute the current chunk:
+// Pass 2: sequential state scan + output.  For chunk c of a (sequence, head):
 //   Z = Ut - W S,  O = O_intra + Q' S  (written to o),  S <- Diag(gamma_C) S + Kbar^T Z.
-// Grid: units_pad * (D/16/NW) workgroups, units_pad = N*H rounded up to 8;
-// consecutive ids go to the 8 XCDs round-robin and all column groups of one
-// head share an XCD (and its L2).
-template <typename IO, int D, int C, int NW, int NBUF>
-__global__ void __launch_bounds__(64 * NW) gdn2_chunk_scan_kernel(chunk_args a) {
-  constexpr int NB = C / 16, NK = D / 16, NG = NK / NW;
+// Every 16-column slice of S evolves on its own given the chunk's -W, Q',
+// Kbar^T and gamma_C (the SHARED part of the block), so the dv columns are
+// split over NGRP workgroups x NCW compute waves, each keeping its CPW slices
+// of S (dk x 16, float32) in matrix-core accumulators for the whole sequence.
+// NLW loader waves move each chunk's operands (65 KB for bf16, d = 128,
+// C = 64) HBM -> registers -> LDS two chunks ahead of the compute waves (one
+// LDS buffer ahead, one register set ahead), so that the wide loads are
+// spread over several waves and never stall the waves doing the products; a
+// compute wave issues no global load inside the loop.  O is accumulated
+// transposed (O^T = S^T Q'^T, the same registers with the operands swapped),
+// which leaves four consecutive columns of one row in each lane: one 8-byte
+// store per lane and tile.  One LDS-only barrier per chunk (two with a single
+// LDS buffer); global stores are never waited for inside the loop, and the
+// body of a full chunk has no branch.
+// Grid: units_pad * NGRP workgroups, units_pad = N*H rounded up to 8;
+// consecutive ids go to the 8 XCDs round-robin and all workgroups of one head
+// share an XCD (and its L2).
+template <typename IO, int D, int C, int NT>
+__global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<IO, D, C, NT>::NLW))
+    gdn2_chunk_scan_kernel(chunk_args a) {
+  typedef scan_cfg<IO, D, C, NT> K;
+  constexpr int NB = C / 16, NK = D / 16;
+  constexpr int NCW = K::NCW, CPW = K::CPW, NGRP = K::NGRP, NLW = K::NLW, PPW = K::PPW, NTW = K::NTW,
+                TF = K::TF;
+  constexpr int NPIECE = K::NPIECE, NPS = K::NPS, RPP = K::RPP, NBUF = K::NBUF;
+  constexpr size_t RB = K::RB;
   typedef frag<IO> F;
   typedef frag2<IO> F2;
   typedef blk_layout<IO, D, C> L;
-  constexpr int NDMA = static_cast<int>(L::SHARED / 1024);  // 1 KB per wave instruction
-  __shared__ __attribute__((aligned(16))) unsigned char sbuf[NBUF][L::SHARED];
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  __shared__ __attribute__((aligned(16))) unsigned char sbuf[NBUF][K::BUF];
 
   const int x = blockIdx.x;
   const int xcd = x & 7, s8 = x >> 3;
-  const int unit = (s8 / NG) * 8 + xcd;
-  const int cg = s8 % NG;
+  const int unit = (s8 / NGRP) * 8 + xcd;
+  const int grp = s8 % NGRP;
   if (unit >= a.num_seqs * a.H)
-    return;
+    return;  // whole workgroup
   const int n = unit / a.H, h = unit - n * a.H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int m = lane & 15, g = lane >> 4;
-  const int vt = cg * NW + wave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int vtg = grp * NTW;                          // first dv tile of the workgroup
+  const int vtf = (NK % 2 == 0) ? (vtg & ~1) : vtg;   // first staged dv tile
   int c_begin, nchunks;
   long tstart, tend;
   if (a.cu) {
@@ -126,108 +187,267 @@ __global__ void __launch_bounds__(64 * NW) gdn2_chunk_scan_kernel(chunk_args a) 
   }
   const unsigned char *blocks = reinterpret_cast<const unsigned char *>(a.blocks);
   auto blk_of = [&](int c) { return blocks + (static_cast<size_t>(c_begin + c) * a.H + h) * a.blk_bytes; };
-  auto dma = [&](int c, int buf) {
-    const unsigned char *src = blk_of(c);
-    for (int i = wave; i < NDMA; i += NW)
-      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
-                                       (lds_void_t *)(&sbuf[buf][i * 1024]), 16, 0, 0);
-  };
 
-  const int col = 16 * vt + m;
-  f32x4 S[NK];
+  if (wave >= NCW) {
+    // ---- loader wave: pieces lw, lw + NLW, ... of an LDS buffer
+    if (nchunks == 0)
+      return;  // the compute waves take no barrier either
+    const int lw = wave - NCW;
+    // byte offset in the block of LDS piece p (SHARED, then Ut rows, then O_intra rows)
+    auto piece_src = [&](int p) -> size_t {
+      if (p < NPS)
+        return static_cast<size_t>(p) * 1024;
+      const int q = p - NPS;
+      const int region = q / (NB * RPP), rem = q % (NB * RPP);
+      return (region ? L::OI : L::UT) + tile_off<IO, NK>(rem / RPP, vtf, 0) + static_cast<size_t>(rem % RPP) * 1024;
+    };
+    int src_off[PPW];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[kk][i] = a.S0 ? a.S0[(static_cast<size_t>(unit) * D + 16 * kk + 4 * g + i) * D + col] : 0.f;
-  IO *out = static_cast<IO *>(a.o);
-
-  F ut[NB], oi[NB];
-  if (nchunks > 0) {
-    dma(0, 0);
-    const unsigned char *blk = blk_of(0);
-#pragma unroll
-    for (int tt = 0; tt < NB; ++tt) {
-      ut[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane);
-      oi[tt] = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane);
+    for (int p = 0; p < PPW; ++p) {
+      const int piece = lw + p * NLW;
+      src_off[p] = piece < NPIECE ? static_cast<int>(piece_src(piece)) : 0;
     }
-  }
-  for (int c = 0; c < nchunks; ++c) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // chunk c's block is in sbuf[c % NBUF]; nobody still reads the other buffer
-    F utc[NB], oic[NB];
+    u32x4 ra[PPW], rb[PPW];
+    // Always issues PPW loads (past the last chunk: the first bytes of the
+    // last block again) so the number of loads in flight is fixed.
+    auto gload = [&](int c, u32x4(&r)[PPW]) {
+      const bool valid = c < nchunks;
+      const unsigned char *src = blk_of(valid ? c : nchunks - 1);
 #pragma unroll
-    for (int tt = 0; tt < NB; ++tt) {
-      utc[tt] = ut[tt];
-      oic[tt] = oi[tt];
-    }
-    if (NBUF > 1 && c + 1 < nchunks) {
-      dma(c + 1, (c + 1) % NBUF);
-      const unsigned char *blk = blk_of(c + 1);
+      for (int p = 0; p < PPW; ++p)
+        r[p] = *reinterpret_cast<const u32x4 *>(src + (valid ? src_off[p] : 0) + lane * 16);
+    };
+    auto lstore = [&](int buf, const u32x4(&r)[PPW]) {
 #pragma unroll
-      for (int tt = 0; tt < NB; ++tt) {
-        ut[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane);
-        oi[tt] = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane);
+      for (int p = 0; p < PPW; ++p) {
+        const int piece = lw + p * NLW;
+        if (piece < NPIECE)
+          *reinterpret_cast<u32x4 *>(&sbuf[buf][piece * 1024 + lane * 16]) = r[p];
+      }
+    };
+    gload(0, ra);
+    lstore(0, ra);
+    if constexpr (K::RSETS == 2) {
+      gload(1, rb);
+      lds_barrier();  // chunk 0 is in buffer 0
+      for (int c = 0; c < nchunks; c += 2) {
+        gload(c + 2, ra);  // ra held chunk c (already in LDS)
+        if constexpr (NBUF == 1)
+          lds_barrier();  // compute waves are done with the only buffer
+        if (c + 1 < nchunks)
+          lstore((c + 1) % NBUF, rb);
+        lds_barrier();  // chunk c + 1 is in LDS, chunk c's buffer is free
+        if (c + 1 >= nchunks)
+          break;
+        gload(c + 3, rb);
+        if constexpr (NBUF == 1)
+          lds_barrier();
+        if (c + 2 < nchunks)
+          lstore((c + 2) % NBUF, ra);
+        lds_barrier();
+      }
+    } else {
+      lds_barrier();
+      for (int c = 0; c < nchunks; ++c) {
+        gload(c + 1, ra);
+        if constexpr (NBUF == 1)
+          lds_barrier();
+        if (c + 1 < nchunks)
+          lstore((c + 1) % NBUF, ra);
+        lds_barrier();
       }
     }
-    const unsigned char *sb = sbuf[c % NBUF];
-    const long t0 = tstart + static_cast<long>(c) * C;
-    const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
+    return;
+  }
 
-    F sf[NK];
+  // ---- compute wave: dv tiles vt0 .. vt0 + CPW - 1
+  const int m = lane & 15, g = lane >> 4;
+  const F eye = identity_colfrag<IO>(lane);
+  const int vt0 = vtg + wave * CPW;
+  f32x4 S[NK][CPW];
+  if (a.S0) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      sf[kk] = F::from(S[kk]);
-    F zf[NB];
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[kk][j][i] = a.S0[(static_cast<size_t>(unit) * D + 16 * kk + 4 * g + i) * D + 16 * (vt0 + j) + m];
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        S[kk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Ut and O_intra tiles of chunk c from global memory (when they are not
+  // staged in LDS; past the last chunk: the last again)
+  auto tload = [&](int c, F(&u)[NB][CPW], F(&o)[NB][CPW]) {
+    const unsigned char *blk = blk_of(c < nchunks ? c : nchunks - 1);
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        u[tt][j] = F::ld_at(blk + L::UT + tile_off<IO, NK>(tt, vt0 + j, lane));
+        o[tt][j] = F::ld_at(blk + L::OI + tile_off<IO, NK>(tt, vt0 + j, lane));
+      }
+  };
+  // Ut and O_intra tiles of row tt from an LDS buffer
+  auto uo_row_lds = [&](const unsigned char *sb, int tt, F(&u)[CPW], F(&o)[CPW]) {
+    const unsigned char *ur = sb + L::SHARED + tt * RB;
+    const unsigned char *orow = sb + L::SHARED + (NB + tt) * RB;
+    if constexpr (CPW % 2 == 0) {  // vt0 - vtf is even
+#pragma unroll
+      for (int j = 0; j < CPW; j += 2) {
+        const F2 u2 = F2::ld(ur + tile_off<IO, TF>(0, vt0 + j - vtf, 0), lane);
+        const F2 o2 = F2::ld(orow + tile_off<IO, TF>(0, vt0 + j - vtf, 0), lane);
+        u[j] = u2.lo;
+        u[j + 1] = u2.hi;
+        o[j] = o2.lo;
+        o[j + 1] = o2.hi;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        u[j] = F::ld_at(ur + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
+        o[j] = F::ld_at(orow + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
+      }
+    }
+  };
+
+  // One chunk: products, o stores (rows < len unless FULL) and state update.
+  auto chunk_step = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], const F(&ocur)[NB][CPW], long t0,
+                        int len, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    // o goes through a global-address-space pointer so that the compiler
+    // knows these stores never alias the LDS operands it wants to hoist
+    typedef __attribute__((address_space(1))) typename io<IO>::elem gelem;
+    gelem *gout = (gelem *)(a.o);
+    F sf[NK][CPW];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        sf[kk][j] = F::from(S[kk][j]);
+    F zf[NB][CPW];
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
-      f32x4 z = utc[tt].to_f32();
-      f32x4 o = oic[tt].to_f32();
+      f32x4 z[CPW], ot[CPW];
+      F ut[CPW], oi[CPW];
+      if constexpr (K::UO_LDS) {
+        uo_row_lds(sb, tt, ut, oi);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          ut[j] = ucur[tt][j];
+          oi[j] = ocur[tt][j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        if constexpr (sizeof(IO) == 2) {
+          // start from Ut and O_intra^T with an identity product instead of
+          // unpacking bf16 on the vector ALU (which the products wait for);
+          // same product shape as the rest of the chain (see mma32)
+          z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (NK % 2 == 0) {
+            mma32(z[j], F2::make(eye, F::zero()), F2::make(ut[j], ut[j]));
+            mma32(ot[j], F2::make(eye, F::zero()), F2::make(oi[j], oi[j]));
+          } else {
+            mma16(z[j], eye, ut[j]);
+            mma16(ot[j], eye, oi[j]);
+          }
+        } else {
+          z[j] = ut[j].to_f32();
+          ot[j] = oi[j].to_f32();
+        }
+      }
       if constexpr (NK % 2 == 0) {
 #pragma unroll
         for (int k2 = 0; k2 < NK / 2; ++k2) {
-          const F2 sb2 = F2::make(sf[2 * k2], sf[2 * k2 + 1]);
-          mma32(z, F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane), sb2);
-          mma32(o, F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane), sb2);
+          const F2 w2 = F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+          const F2 q2 = F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+#pragma unroll
+          for (int j = 0; j < CPW; ++j) {
+            const F2 s2 = F2::make(sf[2 * k2][j], sf[2 * k2 + 1][j]);
+            mma32(z[j], w2, s2);
+            mma32(ot[j], s2, q2);
+          }
         }
       } else {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          mma16(z, F::ld(sb + L::WN + tile_off<IO, NK>(tt, kk, 0), lane), sf[kk]);
-          mma16(o, F::ld(sb + L::QP + tile_off<IO, NK>(tt, kk, 0), lane), sf[kk]);
+          const F w1 = F::ld(sb + L::WN + tile_off<IO, NK>(tt, kk, 0), lane);
+          const F q1 = F::ld(sb + L::QP + tile_off<IO, NK>(tt, kk, 0), lane);
+#pragma unroll
+          for (int j = 0; j < CPW; ++j) {
+            mma16(z[j], w1, sf[kk][j]);
+            mma16(ot[j], sf[kk][j], q1);
+          }
         }
       }
-      zf[tt] = F::from(z);
+      const int t = 16 * tt + m;  // this lane's row of the O tile
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tt + 4 * g + i;
-        if (t < len)
-          out[(static_cast<size_t>(t0 + t) * a.H + h) * D + col] = io<IO>::from_f(o[i]);
+      for (int j = 0; j < CPW; ++j) {
+        zf[tt][j] = F::from(z[j]);
+        if (FULL || t < len)
+          store4_global(gout + (static_cast<size_t>(t0 + t) * a.H + h) * D + 16 * (vt0 + j) + 4 * g, ot[j]);
       }
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const f32x4 gam = *reinterpret_cast<const f32x4 *>(sb + L::GAM + (16 * kk + 4 * g) * sizeof(float));
-      S[kk] *= gam;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        S[kk][j] *= gam;
       if constexpr (NB % 2 == 0) {
 #pragma unroll
-        for (int t2 = 0; t2 < NB / 2; ++t2)
-          mma32(S[kk], F2::ld(sb + L::KB + tile_off<IO, NB>(kk, 2 * t2, 0), lane),
-                F2::make(zf[2 * t2], zf[2 * t2 + 1]));
+        for (int t2 = 0; t2 < NB / 2; ++t2) {
+          const F2 kb2 = F2::ld(sb + L::KB + tile_off<IO, NB>(kk, 2 * t2, 0), lane);
+#pragma unroll
+          for (int j = 0; j < CPW; ++j)
+            mma32(S[kk][j], kb2, F2::make(zf[2 * t2][j], zf[2 * t2 + 1][j]));
+        }
       } else {
 #pragma unroll
-        for (int tt = 0; tt < NB; ++tt)
-          mma16(S[kk], F::ld(sb + L::KB + tile_off<IO, NB>(kk, tt, 0), lane), zf[tt]);
+        for (int tt = 0; tt < NB; ++tt) {
+          const F kb1 = F::ld(sb + L::KB + tile_off<IO, NB>(kk, tt, 0), lane);
+#pragma unroll
+          for (int j = 0; j < CPW; ++j)
+            mma16(S[kk][j], kb1, zf[tt][j]);
+        }
       }
     }
-    if (NBUF == 1 && c + 1 < nchunks) {
-      __syncthreads();  // everyone is done with the only buffer
-      dma(c + 1, 0);
-      const unsigned char *blk = blk_of(c + 1);
+  };
+
+  if (nchunks > 0) {
+    F ucur[NB][CPW], ocur[NB][CPW];
+    if constexpr (!K::UO_LDS)
+      tload(0, ucur, ocur);
+    lds_barrier();  // chunk 0 is in buffer 0
+    for (int c = 0; c < nchunks; ++c) {
+      const unsigned char *sb = sbuf[c % NBUF];
+      const long t0 = tstart + static_cast<long>(c) * C;
+      const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
+      F unxt[NB][CPW], onxt[NB][CPW];
+      if constexpr (!K::UO_LDS)
+        tload(c + 1, unxt, onxt);
+      if (len == C)
+        chunk_step(sb, ucur, ocur, t0, len, std::true_type{});
+      else
+        chunk_step(sb, ucur, ocur, t0, len, std::false_type{});
+      if constexpr (NBUF == 1)
+        lds_barrier();  // done with the only buffer
+      lds_barrier();    // chunk c + 1 is in LDS
+      if constexpr (!K::UO_LDS) {
 #pragma unroll
-      for (int tt = 0; tt < NB; ++tt) {
-        ut[tt] = F::ld(blk + L::UT + (tt * NK + vt) * L::TB, lane);
-        oi[tt] = F::ld(blk + L::OI + (tt * NK + vt) * L::TB, lane);
+        for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+          for (int j = 0; j < CPW; ++j) {
+            ucur[tt][j] = unxt[tt][j];
+            ocur[tt][j] = onxt[tt][j];
+          }
       }
     }
   }
@@ -235,8 +455,10 @@ __global__ void __launch_bounds__(64 * NW) gdn2_chunk_scan_kernel(chunk_args a) 
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a.S_final[(static_cast<size_t>(unit) * D + 16 * kk + 4 * g + i) * D + col] = S[kk][i];
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.S_final[(static_cast<size_t>(unit) * D + 16 * kk + 4 * g + i) * D + 16 * (vt0 + j) + m] = S[kk][j][i];
   }
 }
 
@@ -279,29 +501,31 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
   return hipGetLastError();
 }
 
-template <typename IO, int D, int C, int NW>
-hipError_t launch_scan_nw(const chunk_args &a, hipStream_t st) {
-  typedef blk_layout<IO, D, C> L;
-  constexpr int NBUF = (2 * L::SHARED <= 150 * 1024) ? 2 : 1;
+template <typename IO, int D, int C, int NT> hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
+  typedef scan_cfg<IO, D, C, NT> K;
   const int units = a.num_seqs * a.H;
   const int units_pad = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NW, NBUF>), dim3(units_pad * (D / 16 / NW)),
-                     dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT>), dim3(units_pad * K::NGRP),
+                     dim3(64 * (K::NCW + K::NLW)), 0, st, a);
   return hipGetLastError();
 }
 
-// Workgroups share the per-chunk block in LDS across NW = 4 waves when that
-// still gives at least one workgroup per compute unit; with few (sequence,
-// head) units (long sequences, small batch) every wave gets its own
-// workgroup so that all of them can run.
+// Every workgroup takes a whole compute unit (its LDS buffers), so the
+// columns of a head are split as finely as the 256 compute units allow: few
+// (sequence, head) units get more, narrower workgroups, which shortens the
+// sequential per-chunk path; many units get 4 tiles per workgroup.
 template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st) {
   constexpr int NK = D / 16;
-  const long wgs4 = static_cast<long>(a.num_seqs) * a.H * NK / 4;
-  if constexpr (NK >= 4) {
-    if (wgs4 >= 256)
-      return launch_scan_nw<IO, D, C, 4>(a, st);
+  const long units = static_cast<long>(a.num_seqs) * a.H;
+  if (units * NK <= 256)
+    return launch_scan_nt<IO, D, C, 1>(a, st);
+  if constexpr (NK >= 2) {
+    if (NK < 4 || units * (NK / 2) <= 256)
+      return launch_scan_nt<IO, D, C, 2>(a, st);
   }
-  return launch_scan_nw<IO, D, C, 1>(a, st);
+  if constexpr (NK >= 4)
+    return launch_scan_nt<IO, D, C, 4>(a, st);
+  return launch_scan_nt<IO, D, C, 1>(a, st);
 }
 
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st) {

@@ -69,6 +69,21 @@ template <> struct io<bf16_t> {
   }
 };
 
+// Four consecutive elements to global memory through an address-space(1)
+// pointer (the compiler may then reorder LDS accesses around the store).
+typedef __attribute__((address_space(1))) float gfloat_t;
+typedef __attribute__((address_space(1))) bf16_t gbf16_t;
+__device__ __forceinline__ void store4_global(gfloat_t *p, f32x4 x) {
+  *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(p) = x;
+}
+__device__ __forceinline__ void store4_global(gbf16_t *p, f32x4 x) {
+  typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+  u32x2 u;
+  u.x = static_cast<uint32_t>(f2bf(x[0])) | (static_cast<uint32_t>(f2bf(x[1])) << 16);
+  u.y = static_cast<uint32_t>(f2bf(x[2])) | (static_cast<uint32_t>(f2bf(x[3])) << 16);
+  *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(p) = u;
+}
+
 // -------------------------------------------------------------- fragments --
 // Operand fragment in the matrix-core input type.
 template <typename T> struct frag;
@@ -102,6 +117,13 @@ template <> struct frag<bf16_t> {
   __device__ __forceinline__ void st(void *tile, int lane) const {
     reinterpret_cast<s16x4 *>(tile)[lane] = v;
   }
+  // this lane's 8 bytes at an address computed by the caller
+  __device__ static __forceinline__ frag ld_at(const void *p) {
+    frag f;
+    f.v = *reinterpret_cast<const s16x4 *>(p);
+    return f;
+  }
+  __device__ __forceinline__ void st_at(void *p) const { *reinterpret_cast<s16x4 *>(p) = v; }
   static constexpr int TILE_BYTES = 64 * 8;
 };
 template <> struct frag<float> {
@@ -130,6 +152,12 @@ template <> struct frag<float> {
   __device__ __forceinline__ void st(void *tile, int lane) const {
     reinterpret_cast<f32x4 *>(tile)[lane] = v;
   }
+  __device__ static __forceinline__ frag ld_at(const void *p) {
+    frag f;
+    f.v = *reinterpret_cast<const f32x4 *>(p);
+    return f;
+  }
+  __device__ __forceinline__ void st_at(void *p) const { *reinterpret_cast<f32x4 *>(p) = v; }
   static constexpr int TILE_BYTES = 64 * 16;
 };
 
@@ -144,6 +172,14 @@ __device__ __forceinline__ void mma16(f32x4 &acc, const frag<float> &a, const fr
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc, 0, 0, 0);
 }
 
+// Product shapes and accumulators.  On gfx950 an accumulator written by a
+// 16x16x16 bf16 product and read as the accumulator (srcC) of a 16x16x32 bf16
+// product, or the other way round, needs at least 5 wait states in between
+// (measured: with fewer, two of the four result registers are stale), and the
+// compiler does not insert them.  Every accumulator chain in this library
+// therefore uses a single product shape, or passes through a vector-ALU op
+// (whose hazards the compiler does handle) when the shape changes.
+//
 // Two fragments of adjacent 16-wide k tiles, stored interleaved per lane
 // (lane's tile-0 values, then its tile-1 values) so one vector load fetches
 // both.  mma32 adds A * B over the 32 k values of the pair: for bf16 it is a
@@ -154,6 +190,7 @@ __device__ __forceinline__ void mma16(f32x4 &acc, const frag<float> &a, const fr
 template <typename T> struct frag2 {
   frag<T> lo, hi;
   __device__ static __forceinline__ frag2 ld(const void *base, int lane);
+  __device__ __forceinline__ void st(void *base, int lane) const;
   __device__ static __forceinline__ frag2 make(const frag<T> &a, const frag<T> &b) {
     frag2 f;
     f.lo = a;
@@ -178,6 +215,15 @@ template <> __device__ __forceinline__ frag2<float> frag2<float>::ld(const void 
   f.lo.v = p[0];
   f.hi.v = p[1];
   return f;
+}
+
+template <> __device__ __forceinline__ void frag2<bf16_t>::st(void *base, int lane) const {
+  reinterpret_cast<s16x8 *>(base)[lane] = __builtin_shufflevector(lo.v, hi.v, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <> __device__ __forceinline__ void frag2<float>::st(void *base, int lane) const {
+  f32x4 *p = reinterpret_cast<f32x4 *>(base) + 2 * lane;
+  p[0] = lo.v;
+  p[1] = hi.v;
 }
 
 __device__ __forceinline__ void mma32(f32x4 &acc, const frag2<bf16_t> &a, const frag2<bf16_t> &b) {
@@ -216,6 +262,16 @@ __device__ __forceinline__ f32x4 transpose_frag(const frag<T> &x, const frag<T> 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   mma16(acc, x, eye);
   return acc;
+}
+
+// ------------------------------------------------------------- barriers --
+// Workgroup barrier that orders LDS accesses only: LDS writes issued before it
+// are complete and visible after it, but outstanding global loads and stores
+// are not waited for (unlike __syncthreads()).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ------------------------------------------------------------ wave scans --

@@ -151,14 +151,19 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
         }
 #pragma unroll
         for (int j = 0; j < NVW; ++j) {
-          f32x4 z = ut[j][tt];
-          f32x4 o = oi[j][tt];
+          // ut / oi come out of 16x16x16 products: they are added on the
+          // vector ALU rather than used as the accumulator of the 16x16x32
+          // chain (see mma32)
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k2 = 0; k2 < NK / 2; ++k2) {
             const F2 sb2 = F2::make(sf[j][2 * k2], sf[j][2 * k2 + 1]);
             mma32(z, wa[k2], sb2);
             mma32(o, qa[k2], sb2);
           }
+          z += ut[j][tt];
+          o += oi[j][tt];
           zf[j][tt] = F::from(z);
           po[j][tt] = o;
         }

@@ -107,8 +107,8 @@ template <typename IO, int D, int C> struct blk_layout {
   static constexpr size_t KB = QP + NB * NK * TB;   // rows dk tile, k tiles over tokens: RowFrag(Kbar^T)
   static constexpr size_t GAM = KB + NK * NB * TB;  // [D] float gamma_C
   static constexpr size_t SHARED = (GAM + D * sizeof(float) + 1023) & ~static_cast<size_t>(1023);
-  static constexpr size_t UT = SHARED;              // [NB][NK] ColFrag(Ut)
-  static constexpr size_t OI = UT + NB * NK * TB;   // [NB][NK] ColFrag(O_intra)
+  static constexpr size_t UT = SHARED;              // rows tt, dv tiles paired: ColFrag(Ut)
+  static constexpr size_t OI = UT + NB * NK * TB;   // rows tt, dv tiles paired: RowFrag(O_intra)
   static constexpr size_t BYTES = align256(OI + NB * NK * TB);
 };
 
@@ -526,8 +526,11 @@ __device__ __forceinline__ void wy_wq(const wy_smem<IO, D, C> &sm, const wy_tp<I
 }
 
 // Phases 4-5 for one dv column tile: Ut = T U and O_intra = P Ut, returned as
-// ColFrag float accumulators (ut[I], oi[I] for the 16 rows of sub-block I).
-template <typename IO, int C>
+// float accumulators (ut[I], oi[I] for the 16 rows of sub-block I).  ut is
+// ColFrag; oi is ColFrag, or RowFrag when OI_ROW (computed as O_intra^T =
+// Ut^T P^T by swapping the operands, which puts 4 consecutive columns of one
+// row in each lane).
+template <typename IO, int C, bool OI_ROW = false>
 __device__ __forceinline__ void wy_uo(const wy_tp<IO, C> &tp, const frag<IO> (&ucol)[C / 16],
                                       f32x4 (&ut)[C / 16], f32x4 (&oi)[C / 16]) {
   constexpr int NB = C / 16;
@@ -546,8 +549,12 @@ __device__ __forceinline__ void wy_uo(const wy_tp<IO, C> &tp, const frag<IO> (&u
   for (int I2 = 0; I2 < NB; ++I2) {
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int J = 0; J <= I2; ++J)
-      mma16(o, tp.p[tri_index(I2, J)], uc[J]);
+    for (int J = 0; J <= I2; ++J) {
+      if constexpr (OI_ROW)
+        mma16(o, uc[J], tp.p[tri_index(I2, J)]);
+      else
+        mma16(o, tp.p[tri_index(I2, J)], uc[J]);
+    }
     oi[I2] = o;
   }
 }

@@ -110,6 +110,22 @@ def test_ragged_shapes(g, dtype, d, chunk, T, path):
     check(o, Sf, o_ref, S_ref, TOL[dtype], f"ragged {path} {dtype} d={d} C={chunk} T={T}")
 
 
+# The state scan splits the dv columns of a head over 1, 2 or 4 tiles per
+# workgroup depending on how many (sequence, head) units there are: these
+# batch sizes land in each of the three splits (d = 128: <= 32 / <= 64 / more
+# units; d = 64: <= 64 / <= 128 / more).
+SPLITS = [("bf16", 128, 2), ("bf16", 128, 3), ("bf16", 128, 5), ("f32", 64, 4), ("f32", 64, 6),
+          ("f32", 64, 9)]
+
+
+@pytest.mark.parametrize("dtype,d,B", SPLITS)
+def test_scan_column_splits(g, dtype, d, B):
+    inp = gi.make_chunk_inputs(B, 150, 16, d, d, dtype, seed=300 + B, s0="normal")
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, inp, 64, path="two_pass")
+    check(o, Sf, o_ref, S_ref, TOL[dtype], f"split {dtype} d={d} units={16 * B}")
+
+
 def test_chunk_size_invariance(g):
     inp = gi.make_chunk_inputs(1, 256, 2, 64, 64, "f32", seed=7, s0="normal")
     o16, S16 = gpu_fwd(g, inp, 16)
