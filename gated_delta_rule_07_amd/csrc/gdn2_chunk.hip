@@ -514,18 +514,24 @@ template <typename IO, int D, int C, int NT> hipError_t launch_scan_nt(const chu
 // columns of a head are split as finely as the 256 compute units allow: few
 // (sequence, head) units get more, narrower workgroups, which shortens the
 // sequential per-chunk path; many units get 4 tiles per workgroup.
+// float32 inputs with d = 128, C = 64 keep one tile per workgroup: their
+// wider fragments would not fit in the registers of the larger workgroups.
 template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st) {
   constexpr int NK = D / 16;
   const long units = static_cast<long>(a.num_seqs) * a.H;
-  if (units * NK <= 256)
+  if constexpr (sizeof(IO) == 4 && D * C >= 128 * 64) {
     return launch_scan_nt<IO, D, C, 1>(a, st);
-  if constexpr (NK >= 2) {
-    if (NK < 4 || units * (NK / 2) <= 256)
-      return launch_scan_nt<IO, D, C, 2>(a, st);
+  } else {
+    if (units * NK <= 256)
+      return launch_scan_nt<IO, D, C, 1>(a, st);
+    if constexpr (NK >= 2) {
+      if (NK < 4 || units * (NK / 2) <= 256)
+        return launch_scan_nt<IO, D, C, 2>(a, st);
+    }
+    if constexpr (NK >= 4)
+      return launch_scan_nt<IO, D, C, 4>(a, st);
+    return launch_scan_nt<IO, D, C, 1>(a, st);
   }
-  if constexpr (NK >= 4)
-    return launch_scan_nt<IO, D, C, 4>(a, st);
-  return launch_scan_nt<IO, D, C, 1>(a, st);
 }
 
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st) {
