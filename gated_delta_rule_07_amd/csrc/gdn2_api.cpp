@@ -58,9 +58,11 @@ struct prof_scope {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on)
       return;
-    if (hipEventCreate(&rec.start) != hipSuccess)
+    // no system-scope fence: a fenced event would write back the L2 between
+    // the two passes and slow down the very launches being timed
+    if (hipEventCreateWithFlags(&rec.start, hipEventDisableSystemFence) != hipSuccess)
       return;
-    if (hipEventCreate(&rec.stop) != hipSuccess) {
+    if (hipEventCreateWithFlags(&rec.stop, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(rec.start);
       return;
     }
