@@ -310,7 +310,7 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
                 "gdn2_chunk_fwd: workspace of %zu bytes is smaller than the %zu needed",
                 workspace_bytes, need_exact);
 
-  gdn2::chunk_args a;
+  gdn2::chunk_args a{};
   a.q = q;
   a.k = k;
   a.v = v;
