@@ -16,6 +16,8 @@ In the same run (reported next to the headline, not in `value`):
   * the decode step (256 sequences x 16 heads, 256 MiB fp32 state updated in
     place), warm and with two alternating state buffers (512 MiB, more than
     the 256 MB last-level cache);
+  * the same layer as KDA (b = w = beta per token and head) and as Gated
+    DeltaNet (also a per-(token, head) decay), and GDN-2's time over KDA's;
   * the CPU oracle timed on a bounded sample of the same workload.
 Prints one JSON line.
 """
@@ -225,6 +227,27 @@ def main() -> int:
         vals = list(sweep.values())
         out["sweep_tokens_per_s"] = sweep
         out["sweep_flatness_min_over_max"] = round(min(vals) / max(vals), 3)
+
+        # the same layer with per-(token, head) gates: KDA (b = w = beta) and
+        # Gated DeltaNet (also a per-(token, head) decay).  The three are
+        # timed interleaved, 3 rounds of 20 steps, and the medians reported;
+        # GDN-2's time over KDA's is the measured cost of its two per-channel
+        # gates.
+        beta = dev["b"][..., 0].contiguous()
+        alpha_s = dev["alpha"][..., 0].contiguous()
+        vins = {"gdn2": dev, "kda": dict(dev, b=beta, w=beta),
+                "gated_deltanet": dict(dev, b=beta, w=beta, alpha=alpha_s)}
+        secs = {name: [] for name in vins}
+        for _ in range(3):
+            for name, vin in vins.items():
+                secs[name].append(timed_steps(
+                    lambda: g.chunk_fwd(*(vin[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws,
+                                        path=args.path), 20, 3))
+        med = {name: float(np.median(v)) for name, v in secs.items()}
+        variants = {name: {"tokens_per_s": round(B * T / t, 1), "ms": round(t * 1e3, 4)} for name, t in med.items()}
+        variants["gdn2_over_kda_time"] = round(med["gdn2"] / med["kda"], 4)
+        variants["gdn2_throughput_vs_gated_deltanet"] = round(med["gated_deltanet"] / med["gdn2"], 4)
+        out["gate_variants"] = variants
 
         lens = gi.packed_lengths(3)
         cu = gi.cu_seqlens_from(lens).cuda()

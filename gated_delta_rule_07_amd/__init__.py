@@ -12,6 +12,9 @@ fallback: without the library or a GPU these functions raise.
 Shapes: q, k, alpha, b [B, T, H, dk]; v, w [B, T, H, dv] (packed sequences:
 B = 1 and ``cu_seqlens`` int32 [N + 1] on the device); states [N, H, dk, dv]
 float32.  Inputs are float32 or bfloat16 and must all have the same dtype.
+In ``chunk_fwd``, b, w and alpha may instead be [B, T, H] (one value per
+token and head, shared by its channels): b = w = beta is KDA, with a
+[B, T, H] alpha too it is Gated DeltaNet.
 """
 from __future__ import annotations
 
@@ -27,6 +30,9 @@ GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_RECURRENT = 1 << 1
 FLAG_TWO_PASS = 1 << 2
 FLAG_FUSED = 1 << 3
+FLAG_SCALAR_B = 1 << 4
+FLAG_SCALAR_W = 1 << 5
+FLAG_SCALAR_ALPHA = 1 << 6
 PATHS = {"auto": 0, "recurrent": FLAG_RECURRENT, "two_pass": FLAG_TWO_PASS, "fused": FLAG_FUSED}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
@@ -117,6 +123,13 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
             raise TypeError("q, k, v, alpha, b, w must share one dtype")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    gate_flags = 0
+    for t, flag, name, full in ((b, FLAG_SCALAR_B, "b", dk), (w, FLAG_SCALAR_W, "w", dv),
+                                (alpha, FLAG_SCALAR_ALPHA, "alpha", dk)):
+        if tuple(t.shape) == (B, T, H):
+            gate_flags |= flag
+        elif tuple(t.shape) != (B, T, H, full):
+            raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}] or [{B}, {T}, {H}]")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
@@ -129,7 +142,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
     Sf = S_final
     if Sf is None and want_final:
         Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    flags = PATHS[path]
+    flags = PATHS[path] | gate_flags
     ws_bytes = 0
     if path != "recurrent":
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)

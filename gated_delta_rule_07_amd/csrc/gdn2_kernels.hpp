@@ -24,7 +24,12 @@ struct chunk_args {
   float *S_final;
   char *blocks;      // num_slots * H blocks of blk_bytes each
   size_t blk_bytes;
+  uint32_t gates;    // GATE_* bits: inputs given per (token, head) instead of per channel
 };
+
+// chunk_args::gates: b, w or alpha is one value per (token, head), laid out
+// [B, T, H] (or [1, T_total, H] packed), shared by all of its channels.
+constexpr uint32_t GATE_SCALAR_B = 1u, GATE_SCALAR_W = 2u, GATE_SCALAR_ALPHA = 4u;
 
 template <typename IO, int D, int C> size_t chunk_block_bytes();
 template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st);

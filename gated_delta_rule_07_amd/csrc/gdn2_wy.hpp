@@ -65,6 +65,7 @@ template <> struct raw4<float> {
     r.x = f32x4{v, v, v, v};
     return r;
   }
+  __device__ static __forceinline__ raw4 splat(float e) { return fill(e); }
   __device__ __forceinline__ f32x4 f() const { return x; }
 };
 template <> struct raw4<bf16_t> {
@@ -74,10 +75,11 @@ template <> struct raw4<bf16_t> {
     r.x = *reinterpret_cast<const uint2 *>(p);
     return r;
   }
-  __device__ static __forceinline__ raw4 fill(float v) {
-    const uint32_t h = f2bf(v);
+  __device__ static __forceinline__ raw4 fill(float v) { return splat(f2bf(v)); }
+  // four copies of one stored element
+  __device__ static __forceinline__ raw4 splat(bf16_t e) {
     raw4 r;
-    r.x.x = h | (h << 16);
+    r.x.x = static_cast<uint32_t>(e) | (static_cast<uint32_t>(e) << 16);
     r.x.y = r.x.x;
     return r;
   }
@@ -191,21 +193,31 @@ template <typename IO, int D> struct wy_rows {
 
 // Loads row t (of the chunk starting at token t0) of q, k, b, alpha: this
 // lane's four channels 16kk + 4g .. +3 of every 16-channel tile.  Rows past
-// the valid length read as zeros (alpha as one, i.e. no decay).
+// the valid length read as zeros (alpha as one, i.e. no decay).  With
+// GATE_SCALAR_B / GATE_SCALAR_ALPHA, b / alpha are one element per (token,
+// head), repeated over the channels.
 template <typename IO, int D>
 __device__ __forceinline__ void wy_load_rows(const chunk_args &a, long t0, int len, int h, int t, int g,
                                              wy_rows<IO, D> &r) {
   constexpr int NK = D / 16;
   const bool valid = t < len;
   const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
+  // per-(token, head) gates: one element for all channels of the row
+  IO bs = io<IO>::from_f(0.f), as = io<IO>::from_f(1.f);
+  if (valid && (a.gates & GATE_SCALAR_B))
+    bs = static_cast<const IO *>(a.b)[row];
+  if (valid && (a.gates & GATE_SCALAR_ALPHA))
+    as = static_cast<const IO *>(a.al)[row];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const int c0 = 16 * kk + 4 * g;
     if (valid) {
       r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
       r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
-      r.b[kk] = raw4<IO>::ld(static_cast<const IO *>(a.b) + row * D + c0);
-      r.al[kk] = raw4<IO>::ld(static_cast<const IO *>(a.al) + row * D + c0);
+      r.b[kk] = (a.gates & GATE_SCALAR_B) ? raw4<IO>::splat(bs)
+                                          : raw4<IO>::ld(static_cast<const IO *>(a.b) + row * D + c0);
+      r.al[kk] = (a.gates & GATE_SCALAR_ALPHA) ? raw4<IO>::splat(as)
+                                               : raw4<IO>::ld(static_cast<const IO *>(a.al) + row * D + c0);
     } else {
       r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
       r.al[kk] = raw4<IO>::fill(1.f);
@@ -215,6 +227,7 @@ __device__ __forceinline__ void wy_load_rows(const chunk_args &a, long t0, int l
 
 // Loads v and w of all C tokens for NVW column tiles starting at vt0
 // (RowFrag layout: lane (m, g) holds row 16J + m, columns 16vt + 4g .. +3).
+// With GATE_SCALAR_W, w is one element per (token, head).
 template <typename IO, int D, int C, int NVW>
 __device__ __forceinline__ void wy_load_vw(const chunk_args &a, long t0, int len, int h, int vt0,
                                            bool owner, int m, int g, raw4<IO> (&v)[C / 16][NVW],
@@ -225,12 +238,16 @@ __device__ __forceinline__ void wy_load_vw(const chunk_args &a, long t0, int len
     const int tj = 16 * J + m;
     const bool vj = owner && tj < len;
     const size_t row = static_cast<size_t>(t0 + (vj ? tj : 0)) * a.H + h;
+    IO ws = io<IO>::from_f(0.f);
+    if (vj && (a.gates & GATE_SCALAR_W))
+      ws = static_cast<const IO *>(a.w)[row];
 #pragma unroll
     for (int j = 0; j < NVW; ++j) {
       const int c0 = 16 * (vt0 + j) + 4 * g;
       if (vj) {
         v[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.v) + row * D + c0);
-        w[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.w) + row * D + c0);
+        w[J][j] = (a.gates & GATE_SCALAR_W) ? raw4<IO>::splat(ws)
+                                            : raw4<IO>::ld(static_cast<const IO *>(a.w) + row * D + c0);
       } else {
         v[J][j] = w[J][j] = raw4<IO>::fill(0.f);
       }

@@ -77,6 +77,18 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
                                          (GDN2_ERR_UNSUPPORTED where it has none:
                                          chunk 64 needs dk in {64, 128}, and
                                          float32 with dk = 128 needs chunk 16) */
+/* Gate layout flags (chunked paths only; GDN2_ERR_UNSUPPORTED with
+ * GDN2_FLAG_RECURRENT).  Each makes one input a single value per (token,
+ * head), laid out [B, T, H] (packed: [1, T, H]) in dtype dt and shared by all
+ * channels of that token and head.  b = w = beta with both gate flags is KDA
+ * (aiexpert.news/pt, method paragraph: GDN-2 reduces exactly to KDA when both
+ * gates collapse to one scalar); adding GDN2_FLAG_SCALAR_ALPHA gives Gated
+ * DeltaNet (needhelp.icu/de, section on the generalisation hierarchy).  One
+ * gate flag alone gives the single-gate ablations (aixai.ru blog, ablation
+ * paragraph). */
+#define GDN2_FLAG_SCALAR_B (1u << 4)     /* b is [B, T, H] */
+#define GDN2_FLAG_SCALAR_W (1u << 5)     /* w is [B, T, H] */
+#define GDN2_FLAG_SCALAR_ALPHA (1u << 6) /* alpha is [B, T, H] */
 
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and
@@ -95,12 +107,13 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               sequences of length T (then N = B).  Chunks restart at every
  *               sequence boundary.
  *   B, T, H, dk, dv, num_seqs, chunk, dt : sizes; chunk is the chunk length.
- *   flags     : 0, or one of GDN2_FLAG_RECURRENT, GDN2_FLAG_TWO_PASS,
- *               GDN2_FLAG_FUSED.  With 0 the library runs the two-pass
- *               chunked kernels (all chunks in parallel, then the state
- *               scan); GDN2_FLAG_FUSED runs the single-pass kernel (one
- *               workgroup per head walks its chunks, no workspace traffic).
- *               All choices compute the same recurrence.
+ *   flags     : at most one of GDN2_FLAG_RECURRENT, GDN2_FLAG_TWO_PASS,
+ *               GDN2_FLAG_FUSED, plus any of the gate layout flags.  With no
+ *               path flag the library runs the two-pass chunked kernels (all
+ *               chunks in parallel, then the state scan); GDN2_FLAG_FUSED
+ *               runs the single-pass kernel (one workgroup per head walks its
+ *               chunks, no workspace traffic).  All choices compute the same
+ *               recurrence.
  *   o         : output [B, T, H, dv], element type dt.
  *   S_final   : final states [N, H, dk, dv] float32, or NULL.  May alias S0.
  *   workspace : device scratch of at least

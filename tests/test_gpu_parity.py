@@ -126,6 +126,36 @@ def test_scan_column_splits(g, dtype, d, B):
     check(o, Sf, o_ref, S_ref, TOL[dtype], f"split {dtype} d={d} units={16 * B}")
 
 
+# Gates given per (token, head) ([B, T, H]) instead of per channel: the GPU
+# reads the compact tensors, the oracle gets the same values repeated over the
+# channels.  kda: b = w = beta; gdn: plus a per-(token, head) alpha; b_only /
+# w_only: the single-gate ablations.
+GATE_CASES = {"kda": ("b", "w"), "gdn": ("b", "w", "alpha"), "b_only": ("b",), "w_only": ("w",)}
+
+
+@pytest.mark.parametrize("path", ["two_pass", "fused"])
+@pytest.mark.parametrize("dtype,d,T", [("f32", 64, 190), ("bf16", 128, 200)])
+@pytest.mark.parametrize("case", list(GATE_CASES))
+def test_per_token_gates(g, case, dtype, d, T, path):
+    inp = gi.make_chunk_inputs(2, T, 3, d, d, dtype, seed=400 + T, s0="normal",
+                               scalar_beta=(case in ("kda", "gdn")))
+    full, compact = dict(inp), dict(inp)
+    for x in GATE_CASES[case]:
+        s = inp[x][..., 0].contiguous()           # one value per (batch, token, head)
+        compact[x] = s
+        full[x] = s[..., None].expand_as(inp[x]).contiguous()
+    o_ref, S_ref = oracle.fwd(*(full[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, compact, 64, path=path)
+    check(o, Sf, o_ref, S_ref, TOL[dtype], f"gates {case} {path} {dtype} d={d}")
+
+
+def test_per_token_gates_rejected_on_recurrent_path(g):
+    inp = gi.make_chunk_inputs(1, 32, 1, 16, 16, "f32", seed=5)
+    inp["b"] = inp["b"][..., 0].contiguous()
+    with pytest.raises(g.Gdn2Error):
+        gpu_fwd(g, inp, 16, recurrent=True)
+
+
 def test_chunk_size_invariance(g):
     inp = gi.make_chunk_inputs(1, 256, 2, 64, 64, "f32", seed=7, s0="normal")
     o16, S16 = gpu_fwd(g, inp, 16)
