@@ -14,7 +14,9 @@ B = 1 and ``cu_seqlens`` int32 [N + 1] on the device); states [N, H, dk, dv]
 float32.  Inputs are float32 or bfloat16 and must all have the same dtype.
 In ``chunk_fwd``, b, w and alpha may instead be [B, T, H] (one value per
 token and head, shared by its channels): b = w = beta is KDA, with a
-[B, T, H] alpha too it is Gated DeltaNet.
+[B, T, H] alpha too it is Gated DeltaNet.  With ``layer_prep=True`` the
+inputs are the raw layer projections: q, k not normalised, b and w logits,
+and alpha the float32 natural-log decay (float32 whatever the other dtype).
 """
 from __future__ import annotations
 
@@ -33,6 +35,7 @@ FLAG_FUSED = 1 << 3
 FLAG_SCALAR_B = 1 << 4
 FLAG_SCALAR_W = 1 << 5
 FLAG_SCALAR_ALPHA = 1 << 6
+FLAG_LAYER_PREP = 1 << 0
 PATHS = {"auto": 0, "recurrent": FLAG_RECURRENT, "two_pass": FLAG_TWO_PASS, "fused": FLAG_FUSED}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
@@ -109,7 +112,7 @@ def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chu
 
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
               recurrent: bool = False, out=None, S_final=None, workspace=None,
-              want_final: bool = True, path: str = "auto"):
+              want_final: bool = True, path: str = "auto", layer_prep: bool = False):
     """Chunked forward.  ``path`` selects the kernels: "auto" (the library
     chooses), "fused" (single pass), "two_pass", or "recurrent" (token by
     token; also selected by ``recurrent=True``).  Returns (o, S_final);
@@ -118,9 +121,11 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
         path = "recurrent"
     _require_device(q, k, v, alpha, b, w, S0, cu_seqlens)
     dt = _dtype_code(q)
-    for t in (k, v, alpha, b, w):
+    for t in (k, v, b, w) + (() if layer_prep else (alpha,)):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, alpha, b, w must share one dtype")
+    if layer_prep and alpha.dtype != torch.float32:
+        raise TypeError("with layer_prep, alpha is the float32 log-decay")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     gate_flags = 0
@@ -142,7 +147,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
     Sf = S_final
     if Sf is None and want_final:
         Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    flags = PATHS[path] | gate_flags
+    flags = PATHS[path] | gate_flags | (FLAG_LAYER_PREP if layer_prep else 0)
     ws_bytes = 0
     if path != "recurrent":
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)

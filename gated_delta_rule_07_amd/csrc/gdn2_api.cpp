@@ -252,7 +252,7 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unknown dtype %d", static_cast<int>(dt));
   const uint32_t path_flags = GDN2_FLAG_RECURRENT | GDN2_FLAG_TWO_PASS | GDN2_FLAG_FUSED;
-  const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA;
+  const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
   if (flags & ~(path_flags | gate_flags))
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: unknown flags 0x%x", flags);
   {
@@ -261,7 +261,8 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: flags 0x%x name more than one path", flags);
   }
   if ((flags & GDN2_FLAG_RECURRENT) && (flags & gate_flags))
-    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: the token-by-token path takes per-channel gates only");
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd: the token-by-token path takes neither per-(token, head) gates nor layer prep");
   if (B <= 0 || T < 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: bad sizes B=%d T=%d H=%d", B, T, H);
   if (dk != dv || !supported_dim(dk))
@@ -332,7 +333,8 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
   a.gates = ((flags & GDN2_FLAG_SCALAR_B) ? gdn2::GATE_SCALAR_B : 0u) |
             ((flags & GDN2_FLAG_SCALAR_W) ? gdn2::GATE_SCALAR_W : 0u) |
-            ((flags & GDN2_FLAG_SCALAR_ALPHA) ? gdn2::GATE_SCALAR_ALPHA : 0u);
+            ((flags & GDN2_FLAG_SCALAR_ALPHA) ? gdn2::GATE_SCALAR_ALPHA : 0u) |
+            ((flags & GDN2_FLAG_LAYER_PREP) ? gdn2::GATE_LAYER_PREP : 0u);
   char *ws = static_cast<char *>(workspace);
   if (packed) {
     a.offsets = reinterpret_cast<int32_t *>(ws);

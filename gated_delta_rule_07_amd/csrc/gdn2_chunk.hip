@@ -19,8 +19,9 @@ template <typename IO, int D, int C> size_t chunk_block_bytes() { return blk_lay
 
 // Pass 1.  grid: num_slots * H, block: 64 * C/16 threads (see gdn2_wy.hpp for
 // the work split between waves).
-template <typename IO, int D, int C>
-__global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_args a) {
+template <typename IO, int D, int C, int GM>
+__global__ void __launch_bounds__(64 * (C / 16)) __attribute__((amdgpu_waves_per_eu(2)))
+gdn2_chunk_prep_kernel(chunk_args a) {
   constexpr int NB = C / 16, NK = D / 16;
   constexpr int CTW = (NK >= NB) ? NK / NB : 1;  // column tiles per wave
   typedef frag<IO> F;
@@ -43,17 +44,18 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_chunk_prep_kernel(chunk_ar
   unsigned char *blk = reinterpret_cast<unsigned char *>(a.blocks) +
                        (static_cast<size_t>(slot) * a.H + h) * a.blk_bytes;
 
-  wy_rows<IO, D> r;
-  wy_load_rows<IO, D>(a, t0, len, h, 16 * I + m, g, r);
+  constexpr bool LP = GM == GM_LAYER;
+  wy_rows<IO, D, LP> r;
+  wy_load_rows<IO, D, GM>(a, t0, len, h, 16 * I + m, g, r);
   raw4<IO> rv[NB][CTW], rw[NB][CTW];
-  wy_load_vw<IO, D, C, CTW>(a, t0, len, h, ct0, owner, m, g, rv, rw);
+  wy_load_vw<IO, D, C, CTW, GM>(a, t0, len, h, ct0, owner, m, g, rv, rw);
   f32x4 gl[NK];
-  wy_decay<IO, D, C>(sm, r, gl, I, tid, reinterpret_cast<float *>(blk + L::GAM));
+  wy_decay<IO, D, C, LP>(sm, r, gl, I, tid, reinterpret_cast<float *>(blk + L::GAM));
   const F eye = identity_colfrag<IO>(lane);
   wy_ops<IO, D> op;
-  wy_operands<IO, D, C>(sm, r, gl, I, lane, eye, blk + L::KB, op);
+  wy_operands<IO, D, C, LP>(sm, r, gl, I, lane, eye, blk + L::KB, op);
   F ucol[NB][CTW];
-  wy_values<IO, NB, CTW>(rv, rw, eye, ucol);
+  wy_values<IO, NB, CTW, LP>(rv, rw, eye, ucol);
   __syncthreads();
   F af[NB];
   wy_products<IO, D, C>(sm, op, I, lane, af);
@@ -495,9 +497,15 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------- launchers --
 template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st) {
-  if (a.num_slots > 0)
-    hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C>), dim3(a.num_slots * a.H), dim3(64 * (C / 16)),
-                       0, st, a);
+  if (a.num_slots > 0) {
+    const dim3 grid(a.num_slots * a.H), block(64 * (C / 16));
+    if (a.gates & GATE_LAYER_PREP)
+      hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_LAYER>), grid, block, 0, st, a);
+    else if (a.gates)
+      hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_GATES>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_PLAIN>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ template <typename IO, int D, int C, int NG> struct fused_cfg {
 
 // grid: units_pad * NG workgroups (units_pad = N*H rounded up to 8; all
 // column groups of a head share an XCD); block: 64 * C/16 threads.
-template <typename IO, int D, int C, int NG>
+template <typename IO, int D, int C, int NG, int GM>
 __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a) {
   typedef fused_cfg<IO, D, C, NG> K;
   constexpr int NB = K::NB, NK = K::NK, CTK = K::CTK, NVW = K::NVW;
@@ -69,12 +69,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
   IO *out = static_cast<IO *>(a.o);
   const F eye = identity_colfrag<IO>(lane);
 
-  wy_rows<IO, D> r;
+  constexpr bool LP = GM == GM_LAYER;
+  wy_rows<IO, D, LP> r;
   raw4<IO> rv[NB][NVW], rw[NB][NVW];
   if (nchunks > 0) {
     const int len0 = (tend - tstart) < C ? static_cast<int>(tend - tstart) : C;
-    wy_load_rows<IO, D>(a, tstart, len0, h, 16 * I + m, g, r);
-    wy_load_vw<IO, D, C, NVW>(a, tstart, len0, h, vt0, true, m, g, rv, rw);
+    wy_load_rows<IO, D, GM>(a, tstart, len0, h, 16 * I + m, g, r);
+    wy_load_vw<IO, D, C, NVW, GM>(a, tstart, len0, h, vt0, true, m, g, rv, rw);
   }
   // outputs of the previous chunk, stored once this chunk's inputs have been
   // consumed (so that waiting for the prefetched inputs never waits for them)
@@ -98,18 +99,18 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
     const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
 
     f32x4 gl[NK];
-    wy_decay<IO, D, C>(sm, r, gl, I, tid, reinterpret_cast<float *>(tiles + L::GAM));
+    wy_decay<IO, D, C, LP>(sm, r, gl, I, tid, reinterpret_cast<float *>(tiles + L::GAM));
     wy_ops<IO, D> op;
-    wy_operands<IO, D, C>(sm, r, gl, I, lane, eye, tiles + L::KB, op);
+    wy_operands<IO, D, C, LP>(sm, r, gl, I, lane, eye, tiles + L::KB, op);
     F ucol[NB][NVW];
-    wy_values<IO, NB, NVW>(rv, rw, eye, ucol);
+    wy_values<IO, NB, NVW, LP>(rv, rw, eye, ucol);
     if (c > 0)
       store_prev();
     if (c + 1 < nchunks) {  // inputs of the next chunk, while this one computes
       const long tn = t0 + C;
       const int lenn = (tend - tn) < C ? static_cast<int>(tend - tn) : C;
-      wy_load_rows<IO, D>(a, tn, lenn, h, 16 * I + m, g, r);
-      wy_load_vw<IO, D, C, NVW>(a, tn, lenn, h, vt0, true, m, g, rv, rw);
+      wy_load_rows<IO, D, GM>(a, tn, lenn, h, 16 * I + m, g, r);
+      wy_load_vw<IO, D, C, NVW, GM>(a, tn, lenn, h, vt0, true, m, g, rv, rw);
     }
     __syncthreads();
     F af[NB];
@@ -240,8 +241,13 @@ template <typename IO, int D, int C, int NG> hipError_t launch_fused(const chunk
   if constexpr (fused_cfg<IO, D, C, NG>::OK) {
     const int units = a.num_seqs * a.H;
     const int units_pad = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG>), dim3(units_pad * NG), dim3(64 * (C / 16)), 0,
-                       st, a);
+    const dim3 grid(units_pad * NG), block(64 * (C / 16));
+    if (a.gates & GATE_LAYER_PREP)
+      hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_LAYER>), grid, block, 0, st, a);
+    else if (a.gates)
+      hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_GATES>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_PLAIN>), grid, block, 0, st, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidConfiguration;

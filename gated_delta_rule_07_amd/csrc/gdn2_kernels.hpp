@@ -29,7 +29,10 @@ struct chunk_args {
 
 // chunk_args::gates: b, w or alpha is one value per (token, head), laid out
 // [B, T, H] (or [1, T_total, H] packed), shared by all of its channels.
-constexpr uint32_t GATE_SCALAR_B = 1u, GATE_SCALAR_W = 2u, GATE_SCALAR_ALPHA = 4u;
+// GATE_LAYER_PREP: the inputs are the raw layer inputs (q, k not normalised,
+// b and w logits, alpha a float32 natural-log decay); the kernels apply the
+// L2 norm, the sigmoid and exp themselves.
+constexpr uint32_t GATE_SCALAR_B = 1u, GATE_SCALAR_W = 2u, GATE_SCALAR_ALPHA = 4u, GATE_LAYER_PREP = 8u;
 
 template <typename IO, int D, int C> size_t chunk_block_bytes();
 template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st);

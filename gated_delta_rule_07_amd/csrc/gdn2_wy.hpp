@@ -186,68 +186,135 @@ __device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (
 __device__ __forceinline__ constexpr int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // Per-wave registers of one chunk's row phases.
-template <typename IO, int D> struct wy_rows {
+// Rows of q, k, b, alpha held by one lane.  With layer prep (LP) alpha is
+// kept as log2 of the decay in float32 (lg), and qs / ks are the lane's row
+// scales 1 / ||q_t||, 1 / ||k_t|| (the raw rows stay in q, k).
+template <typename IO, int D, bool LP = false> struct wy_rows {
   static constexpr int NK = D / 16;
-  raw4<IO> q[NK], k[NK], b[NK], al[NK];
+  raw4<IO> q[NK], k[NK], b[NK];
+  raw4<IO> al[LP ? 1 : NK];
+  f32x4 lg[LP ? NK : 1];
+  float qs, ks;
 };
+
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + fast_exp2(-1.4426950408889634f * x));
+}
 
 // Loads row t (of the chunk starting at token t0) of q, k, b, alpha: this
 // lane's four channels 16kk + 4g .. +3 of every 16-channel tile.  Rows past
 // the valid length read as zeros (alpha as one, i.e. no decay).  With
 // GATE_SCALAR_B / GATE_SCALAR_ALPHA, b / alpha are one element per (token,
 // head), repeated over the channels.
-template <typename IO, int D>
+// Input modes of the loaders (compile-time): GM_PLAIN, every gate per
+// channel; GM_GATES, b / w / alpha may each be per (token, head) (the
+// GATE_SCALAR_* bits of chunk_args::gates); GM_LAYER, layer prep (raw q, k,
+// gate logits, float32 log decay) with the same per-(token, head) options.
+constexpr int GM_PLAIN = 0, GM_GATES = 1, GM_LAYER = 2;
+
+template <typename IO, int D, int GM = GM_PLAIN>
 __device__ __forceinline__ void wy_load_rows(const chunk_args &a, long t0, int len, int h, int t, int g,
-                                             wy_rows<IO, D> &r) {
+                                             wy_rows<IO, D, GM == GM_LAYER> &r) {
   constexpr int NK = D / 16;
+  constexpr bool LP = GM == GM_LAYER;
   const bool valid = t < len;
   const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
-  // per-(token, head) gates: one element for all channels of the row
-  IO bs = io<IO>::from_f(0.f), as = io<IO>::from_f(1.f);
-  if (valid && (a.gates & GATE_SCALAR_B))
-    bs = static_cast<const IO *>(a.b)[row];
-  if (valid && (a.gates & GATE_SCALAR_ALPHA))
-    as = static_cast<const IO *>(a.al)[row];
+  if constexpr (GM == GM_PLAIN) {
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const int c0 = 16 * kk + 4 * g;
-    if (valid) {
-      r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
-      r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
-      r.b[kk] = (a.gates & GATE_SCALAR_B) ? raw4<IO>::splat(bs)
-                                          : raw4<IO>::ld(static_cast<const IO *>(a.b) + row * D + c0);
-      r.al[kk] = (a.gates & GATE_SCALAR_ALPHA) ? raw4<IO>::splat(as)
-                                               : raw4<IO>::ld(static_cast<const IO *>(a.al) + row * D + c0);
-    } else {
-      r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
-      r.al[kk] = raw4<IO>::fill(1.f);
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c0 = 16 * kk + 4 * g;
+      if (valid) {
+        r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
+        r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
+        r.b[kk] = raw4<IO>::ld(static_cast<const IO *>(a.b) + row * D + c0);
+        r.al[kk] = raw4<IO>::ld(static_cast<const IO *>(a.al) + row * D + c0);
+      } else {
+        r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
+        r.al[kk] = raw4<IO>::fill(1.f);
+      }
     }
+  } else {
+    // per-(token, head) b and / or alpha: one element for all channels of the row
+    const IO *bp = static_cast<const IO *>(a.b);
+    const IO *ap = static_cast<const IO *>(a.al);
+    const bool sb = a.gates & GATE_SCALAR_B, sa = a.gates & GATE_SCALAR_ALPHA;
+    const raw4<IO> bs = raw4<IO>::splat((valid && sb) ? bp[row] : io<IO>::from_f(0.f));
+    raw4<IO> as = raw4<IO>::fill(1.f);
+    if constexpr (!LP)
+      as = raw4<IO>::splat((valid && sa) ? ap[row] : io<IO>::from_f(1.f));
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c0 = 16 * kk + 4 * g;
+      if (valid) {
+        r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
+        r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
+        r.b[kk] = sb ? bs : raw4<IO>::ld(bp + row * D + c0);
+        if constexpr (!LP)
+          r.al[kk] = sa ? as : raw4<IO>::ld(ap + row * D + c0);
+      } else {
+        r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
+        if constexpr (!LP)
+          r.al[kk] = raw4<IO>::fill(1.f);
+      }
+    }
+  }
+  r.qs = r.ks = 1.f;
+  if constexpr (LP) {
+    // float32 natural-log decay -> log2; rows past the end decay by 1
+    constexpr float LOG2E = 1.4426950408889634f;
+    const float *ga = static_cast<const float *>(a.al);
+    const float gs = (valid && (a.gates & GATE_SCALAR_ALPHA)) ? ga[row] * LOG2E : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      if (!valid || (a.gates & GATE_SCALAR_ALPHA))
+        r.lg[kk] = f32x4{gs, gs, gs, gs};
+      else
+        r.lg[kk] = *reinterpret_cast<const f32x4 *>(ga + row * D + 16 * kk + 4 * g) * LOG2E;
+    }
+    // row norms: this lane holds 4 of every 16 channels; the lanes m, m+16,
+    // m+32, m+48 together hold the whole row
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const f32x4 x = r.q[kk].f(), y = r.k[kk].f();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sq += x[i] * x[i];
+        sk += y[i] * y[i];
+      }
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sk += __shfl_xor(sk, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    sk += __shfl_xor(sk, 32, 64);
+    r.qs = sq > 0.f ? __frsqrt_rn(sq) : 0.f;
+    r.ks = sk > 0.f ? __frsqrt_rn(sk) : 0.f;
   }
 }
 
 // Loads v and w of all C tokens for NVW column tiles starting at vt0
 // (RowFrag layout: lane (m, g) holds row 16J + m, columns 16vt + 4g .. +3).
 // With GATE_SCALAR_W, w is one element per (token, head).
-template <typename IO, int D, int C, int NVW>
+template <typename IO, int D, int C, int NVW, int GM = GM_PLAIN>
 __device__ __forceinline__ void wy_load_vw(const chunk_args &a, long t0, int len, int h, int vt0,
                                            bool owner, int m, int g, raw4<IO> (&v)[C / 16][NVW],
                                            raw4<IO> (&w)[C / 16][NVW]) {
   constexpr int NB = C / 16;
+  const bool sw = GM != GM_PLAIN && (a.gates & GATE_SCALAR_W);
 #pragma unroll
   for (int J = 0; J < NB; ++J) {
     const int tj = 16 * J + m;
     const bool vj = owner && tj < len;
     const size_t row = static_cast<size_t>(t0 + (vj ? tj : 0)) * a.H + h;
-    IO ws = io<IO>::from_f(0.f);
-    if (vj && (a.gates & GATE_SCALAR_W))
-      ws = static_cast<const IO *>(a.w)[row];
+    raw4<IO> ws = raw4<IO>::fill(0.f);
+    if constexpr (GM != GM_PLAIN)
+      ws = raw4<IO>::splat((vj && sw) ? static_cast<const IO *>(a.w)[row] : io<IO>::from_f(0.f));
 #pragma unroll
     for (int j = 0; j < NVW; ++j) {
       const int c0 = 16 * (vt0 + j) + 4 * g;
       if (vj) {
         v[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.v) + row * D + c0);
-        w[J][j] = (a.gates & GATE_SCALAR_W) ? raw4<IO>::splat(ws)
-                                            : raw4<IO>::ld(static_cast<const IO *>(a.w) + row * D + c0);
+        w[J][j] = sw ? ws : raw4<IO>::ld(static_cast<const IO *>(a.w) + row * D + c0);
       } else {
         v[J][j] = w[J][j] = raw4<IO>::fill(0.f);
       }
@@ -259,17 +326,23 @@ __device__ __forceinline__ void wy_load_vw(const chunk_args &a, long t0, int len
 // per-channel factors between sub-block boundaries.  On return gl holds the
 // in-sub-block prefix sums g_t - rho_I.  gam_out[c] = gamma_C (may be LDS or
 // global memory).  Contains two workgroup barriers.
-template <typename IO, int D, int C>
-__device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO, D> &r, f32x4 (&gl)[D / 16],
+template <typename IO, int D, int C, bool LP = false>
+__device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO, D, LP> &r, f32x4 (&gl)[D / 16],
                                          int I, int tid, float *gam_out) {
   constexpr int NB = C / 16, NK = D / 16;
   const int lane = tid & 63, m = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    const f32x4 al = r.al[kk].f();
+    if constexpr (LP) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      gl[kk][i] = row16_inclusive_scan(fast_log2(al[i]));
+      for (int i = 0; i < 4; ++i)
+        gl[kk][i] = row16_inclusive_scan(r.lg[kk][i]);
+    } else {
+      const f32x4 al = r.al[kk].f();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        gl[kk][i] = row16_inclusive_scan(fast_log2(al[i]));
+    }
   }
   if (m == 15) {
 #pragma unroll
@@ -313,8 +386,8 @@ template <typename IO, int D> struct wy_ops {
 // Phase 1b: decayed, gated operands of sub-block I.  Writes the rescaled keys
 // for later sub-blocks and ColFrag(E) to LDS, and RowFrag(Kbar^T) tiles to
 // kb_out (the KB region of a block layout, LDS or global).
-template <typename IO, int D, int C>
-__device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows<IO, D> &r,
+template <typename IO, int D, int C, bool LP = false>
+__device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows<IO, D, LP> &r,
                                             const f32x4 (&gl)[D / 16], int I, int lane,
                                             const frag<IO> &eye, unsigned char *kb_out,
                                             wy_ops<IO, D> &op) {
@@ -332,9 +405,16 @@ __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows
       f[i] = fast_exp2(gl[kk][i]);    // e^{g_t - rho_I} <= 1
       fi[i] = fast_exp2(-gl[kk][i]);  // e^{rho_I - g_t} >= 1
     }
-    const f32x4 kf = r.k[kk].f();
-    const f32x4 er = r.b[kk].f() * kf * f;
-    const f32x4 qr = r.q[kk].f() * f;
+    f32x4 kf = r.k[kk].f(), bf = r.b[kk].f(), qf = r.q[kk].f();
+    if constexpr (LP) {
+      kf *= r.ks;
+      qf *= r.qs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bf[i] = fast_sigmoid(bf[i]);
+    }
+    const f32x4 er = bf * kf * f;
+    const f32x4 qr = qf * f;
     const f32x4 kh = kf * fi;
     op.ef[kk] = F::from(er);
     op.qf[kk] = F::from(qr);
@@ -354,14 +434,21 @@ __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows
 }
 
 // ColFrag(U_J) = ColFrag(w (.) v) for NVW column tiles and every sub-block.
-template <typename IO, int NB, int NVW>
+template <typename IO, int NB, int NVW, bool LP = false>
 __device__ __forceinline__ void wy_values(const raw4<IO> (&v)[NB][NVW], const raw4<IO> (&w)[NB][NVW],
                                           const frag<IO> &eye, frag<IO> (&ucol)[NB][NVW]) {
 #pragma unroll
   for (int J = 0; J < NB; ++J)
 #pragma unroll
-    for (int j = 0; j < NVW; ++j)
-      ucol[J][j] = frag<IO>::from(transpose_frag(frag<IO>::from(w[J][j].f() * v[J][j].f()), eye));
+    for (int j = 0; j < NVW; ++j) {
+      f32x4 wf = w[J][j].f();
+      if constexpr (LP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          wf[i] = fast_sigmoid(wf[i]);
+      }
+      ucol[J][j] = frag<IO>::from(transpose_frag(frag<IO>::from(wf * v[J][j].f()), eye));
+    }
 }
 
 // Phase 2: A and P rows of sub-block I.  RowFrag(A_IK) stays in registers

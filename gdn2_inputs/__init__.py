@@ -100,6 +100,38 @@ def make_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed
     return out
 
 
+def make_layer_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                      s0: str | None = None, scalar_beta: bool = False) -> dict:
+    """Raw layer inputs of one chunked-forward call in layer-prep mode: q and
+    k not normalised (N(0,1) times a per-row scale in [0.5, 4]), v ~ N(0,1),
+    gate logits b, w ~ N(0,1) (one shared logit per (batch, token, head) with
+    ``scalar_beta``, then shaped [B, T, H]), and the natural-log decay
+    log(sigmoid(N(3,1))) per key channel, always float32.  The recurrence
+    inputs these stand for have the same distributions as make_chunk_inputs.
+    """
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, dk)) * rng.uniform(0.5, 4.0, (B, T, H, 1))
+    k = rng.standard_normal((B, T, H, dk)) * rng.uniform(0.5, 4.0, (B, T, H, 1))
+    v = rng.standard_normal((B, T, H, dv))
+    log_alpha = np.log(_sigmoid(rng.normal(3.0, 1.0, (B, T, H, dk))))
+    if scalar_beta:
+        b = w = rng.standard_normal((B, T, H))
+    else:
+        b = rng.standard_normal((B, T, H, dk))
+        w = rng.standard_normal((B, T, H, dv))
+    out = {
+        "q": _cast(q, dtype), "k": _cast(k, dtype), "v": _cast(v, dtype),
+        "alpha": _cast(log_alpha, "f32"), "b": _cast(b, dtype), "w": _cast(w, dtype),
+    }
+    if s0 is None:
+        out["S0"] = None
+    elif s0 == "normal":
+        out["S0"] = torch.from_numpy(rng.normal(0.0, 0.1, (B, H, dk, dv))).float().contiguous()
+    else:
+        raise ValueError(f"unknown s0 mode {s0!r}")
+    return out
+
+
 def make_decode_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
                        steps: int) -> dict:
     """``steps`` distinct single-token inputs ``[steps, N, H, d]`` plus a state

@@ -89,6 +89,17 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
 #define GDN2_FLAG_SCALAR_B (1u << 4)     /* b is [B, T, H] */
 #define GDN2_FLAG_SCALAR_W (1u << 5)     /* w is [B, T, H] */
 #define GDN2_FLAG_SCALAR_ALPHA (1u << 6) /* alpha is [B, T, H] */
+/* Layer prep (chunked paths only; GDN2_ERR_UNSUPPORTED with
+ * GDN2_FLAG_RECURRENT).  The inputs are the layer's raw projections as the
+ * aixai.ru blog describes them (section on how the method is implemented in
+ * practice): q and k not yet L2-normalised, the gates b and w as logits
+ * (the kernel applies the logistic sigmoid, giving the [0, 1] gates of
+ * aiexpert.news/pt), and alpha as the float32 natural-log decay
+ * g = ln(alpha) <= 0, computed outside the kernel: alpha then points to
+ * float32 data whatever dt is ([B, T, H, dk], or [B, T, H] with
+ * GDN2_FLAG_SCALAR_ALPHA).  The kernels L2-normalise q and k per (token,
+ * head) in float32 (a zero row stays zero). */
+#define GDN2_FLAG_LAYER_PREP (1u << 0)
 
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and

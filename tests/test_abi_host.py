@@ -61,6 +61,7 @@ def test_fwd_rejects_before_launch(L):
     assert call_fwd(L, flags=(1 << 2) | (1 << 3)) == 1         # two paths at once
     assert call_fwd(L, flags=(1 << 1) | (1 << 4)) == 2         # token-by-token path with a per-(token, head) gate
     assert call_fwd(L, flags=(1 << 1) | (1 << 6)) == 2
+    assert call_fwd(L, flags=(1 << 1) | (1 << 0)) == 2         # token-by-token path with layer prep
     assert call_fwd(L, ptr=0) == 1
     assert call_fwd(L, q=FAKE + 4) == 1                       # misaligned
     assert call_fwd(L, N=3) == 1                              # num_seqs without cu_seqlens

@@ -38,11 +38,11 @@ def to_dev(inp):
     return {kk: (vv.cuda() if isinstance(vv, torch.Tensor) else vv) for kk, vv in inp.items()}
 
 
-def gpu_fwd(g, inp, chunk, cu=None, recurrent=False, S0=None, path="auto"):
+def gpu_fwd(g, inp, chunk, cu=None, recurrent=False, S0=None, path="auto", layer_prep=False):
     d = to_dev(inp)
     o, Sf = g.chunk_fwd(*(d[n] for n in NAMES), S0=(S0.cuda() if S0 is not None else d.get("S0")),
                         cu_seqlens=None if cu is None else cu.cuda(), chunk=chunk, recurrent=recurrent,
-                        path=path)
+                        path=path, layer_prep=layer_prep)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), Sf.cpu().numpy()
 
@@ -154,6 +154,29 @@ def test_per_token_gates_rejected_on_recurrent_path(g):
     inp["b"] = inp["b"][..., 0].contiguous()
     with pytest.raises(g.Gdn2Error):
         gpu_fwd(g, inp, 16, recurrent=True)
+
+
+# Layer prep: raw q, k (not normalised), gate logits and the float32
+# natural-log decay go in; the oracle applies the float64 layer prep
+# (oracle/layer_prep.py) to the same stored values and runs the recurrence.
+@pytest.mark.parametrize("path", ["two_pass", "fused"])
+@pytest.mark.parametrize("dtype,d,chunk,T", [("f32", 64, 64, 190), ("bf16", 128, 64, 200), ("bf16", 64, 16, 77)])
+@pytest.mark.parametrize("scalar", [False, True])
+def test_layer_prep(g, dtype, d, chunk, T, path, scalar):
+    from oracle import layer_prep as lp
+    raw = gi.make_layer_inputs(2, T, 3, d, d, dtype, seed=500 + T, s0="normal", scalar_beta=scalar)
+    prep = lp.layer_prep(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"])
+    full = {x: (prep[x][..., None] * np.ones(d) if prep[x].ndim == 3 else prep[x])
+            for x in ("q", "k", "alpha", "b", "w")}
+    o_ref, S_ref = oracle.fwd(full["q"], full["k"], raw["v"], full["alpha"], full["b"], full["w"], S0=raw["S0"])
+    o, Sf = gpu_fwd(g, raw, chunk, path=path, layer_prep=True)
+    check(o, Sf, o_ref, S_ref, TOL[dtype], f"layer prep {path} {dtype} d={d} C={chunk} scalar={scalar}")
+
+
+def test_layer_prep_rejected_on_recurrent_path(g):
+    raw = gi.make_layer_inputs(1, 32, 1, 16, 16, "f32", seed=6)
+    with pytest.raises(g.Gdn2Error):
+        gpu_fwd(g, raw, 16, recurrent=True, layer_prep=True)
 
 
 def test_chunk_size_invariance(g):

@@ -286,3 +286,58 @@ def _pin_suite_passes(mutation):
 def test_pins_catch_planted_mistakes(mutation):
     assert _pin_suite_passes(None)
     assert not _pin_suite_passes(mutation)
+
+
+# ------------------------------------------------------------ layer prep
+# Pins of the float64 layer prep (oracle/layer_prep.py) by properties its
+# definitions fix, not by re-evaluating them.
+def test_layer_prep_l2_normalise_properties():
+    from oracle import layer_prep as lp
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=(3, 5, 7, 32)) * rng.uniform(0.1, 10.0, size=(3, 5, 7, 1))
+    y = lp.l2_normalise(x)
+    assert np.allclose(np.sum(y * y, axis=-1), 1.0, atol=1e-13)          # unit length
+    assert np.allclose(lp.l2_normalise(4.5 * x), y, atol=1e-15)          # scale invariant
+    assert np.all(np.sum(y * x, axis=-1) > 0)                            # same direction
+    e = np.zeros(8); e[3] = -2.0
+    assert np.array_equal(lp.l2_normalise(e), -np.eye(8)[3])            # a basis vector
+    assert np.array_equal(lp.l2_normalise(np.zeros(8)), np.zeros(8))    # zero stays zero
+
+
+def test_layer_prep_sigmoid_properties():
+    from oracle import layer_prep as lp
+    x = np.linspace(-30, 30, 601)
+    s = lp.sigmoid(x)
+    assert lp.sigmoid(0.0) == 0.5
+    assert np.allclose(s + lp.sigmoid(-x), 1.0, atol=1e-15)              # symmetry
+    assert np.all(np.diff(s) > 0) and s.min() > 0 and s.max() < 1       # monotone into (0, 1)
+    p = np.array([0.1, 0.25, 0.9])
+    assert np.allclose(lp.sigmoid(np.log(p / (1 - p))), p, atol=1e-15)  # inverse of the logit
+    # derivative s(1 - s) against a central difference
+    h = 1e-6
+    d = (lp.sigmoid(x + h) - lp.sigmoid(x - h)) / (2 * h)
+    assert np.allclose(d, s * (1 - s), atol=1e-9)
+
+
+def test_layer_prep_decay_properties():
+    from oracle import layer_prep as lp
+    g = -np.array([0.0, 0.01, 0.5, 3.0])
+    a = lp.decay_from_log(g)
+    assert a[0] == 1.0
+    assert np.allclose(np.log(a), g, atol=1e-15)
+    # products of decays are sums of their logs
+    assert np.isclose(lp.decay_from_log(g[1] + g[2]), a[1] * a[2], rtol=1e-15)
+
+
+def test_layer_prep_feeds_the_recurrence():
+    """Raw inputs that are already normalised (to float32 rounding), with
+    gate logits and log decay of known values, reproduce the recurrence on
+    the plain inputs (to that rounding)."""
+    from oracle import layer_prep as lp
+    inp = gi.make_chunk_inputs(1, 40, 2, 16, 16, "f32", seed=12, s0="normal")
+    b = inp["b"].double().numpy(); w = inp["w"].double().numpy(); al = inp["alpha"].double().numpy()
+    raw = lp.layer_prep(inp["q"], inp["k"], np.log(al), np.log(b / (1 - b)), np.log(w / (1 - w)))
+    o1, S1 = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], S0=inp["S0"])
+    o2, S2 = oracle.fwd(raw["q"], raw["k"], inp["v"], raw["alpha"], raw["b"], raw["w"], S0=inp["S0"])
+    assert np.abs(o1 - o2).max() <= 1e-6 * np.abs(o1).max()
+    assert np.abs(S1 - S2).max() <= 1e-6 * np.abs(S1).max()
