@@ -46,9 +46,8 @@ gdn2_chunk_prep_kernel(chunk_args a) {
 
   constexpr bool LP = GM == GM_LAYER;
   wy_rows<IO, D, LP> r;
-  wy_load_rows<IO, D, GM>(a, t0, len, h, 16 * I + m, g, r);
   raw4<IO> rv[NB][CTW], rw[NB][CTW];
-  wy_load_vw<IO, D, C, CTW, GM>(a, t0, len, h, ct0, owner, m, g, rv, rw);
+  wy_load_chunk<IO, D, C, CTW, GM>(a, t0, len, h, I, ct0, owner, m, g, r, rv, rw);
   f32x4 gl[NK];
   wy_decay<IO, D, C, LP>(sm, r, gl, I, tid, reinterpret_cast<float *>(blk + L::GAM));
   const F eye = identity_colfrag<IO>(lane);
@@ -499,8 +498,13 @@ __global__ void __launch_bounds__(256)
 template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st) {
   if (a.num_slots > 0) {
     const dim3 grid(a.num_slots * a.H), block(64 * (C / 16));
+    const uint32_t kda = GATE_SCALAR_B | GATE_SCALAR_W;
     if (a.gates & GATE_LAYER_PREP)
       hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_LAYER>), grid, block, 0, st, a);
+    else if (a.gates == kda)
+      hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_KDA>), grid, block, 0, st, a);
+    else if (a.gates == (kda | GATE_SCALAR_ALPHA))
+      hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_GDN>), grid, block, 0, st, a);
     else if (a.gates)
       hipLaunchKernelGGL((gdn2_chunk_prep_kernel<IO, D, C, GM_GATES>), grid, block, 0, st, a);
     else

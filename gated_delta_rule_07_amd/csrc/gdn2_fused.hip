@@ -74,8 +74,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
   raw4<IO> rv[NB][NVW], rw[NB][NVW];
   if (nchunks > 0) {
     const int len0 = (tend - tstart) < C ? static_cast<int>(tend - tstart) : C;
-    wy_load_rows<IO, D, GM>(a, tstart, len0, h, 16 * I + m, g, r);
-    wy_load_vw<IO, D, C, NVW, GM>(a, tstart, len0, h, vt0, true, m, g, rv, rw);
+    wy_load_chunk<IO, D, C, NVW, GM>(a, tstart, len0, h, I, vt0, true, m, g, r, rv, rw);
   }
   // outputs of the previous chunk, stored once this chunk's inputs have been
   // consumed (so that waiting for the prefetched inputs never waits for them)
@@ -109,8 +108,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
     if (c + 1 < nchunks) {  // inputs of the next chunk, while this one computes
       const long tn = t0 + C;
       const int lenn = (tend - tn) < C ? static_cast<int>(tend - tn) : C;
-      wy_load_rows<IO, D, GM>(a, tn, lenn, h, 16 * I + m, g, r);
-      wy_load_vw<IO, D, C, NVW, GM>(a, tn, lenn, h, vt0, true, m, g, rv, rw);
+      wy_load_chunk<IO, D, C, NVW, GM>(a, tn, lenn, h, I, vt0, true, m, g, r, rv, rw);
     }
     __syncthreads();
     F af[NB];
@@ -242,8 +240,13 @@ template <typename IO, int D, int C, int NG> hipError_t launch_fused(const chunk
     const int units = a.num_seqs * a.H;
     const int units_pad = (units + 7) / 8 * 8;
     const dim3 grid(units_pad * NG), block(64 * (C / 16));
+    const uint32_t kda = GATE_SCALAR_B | GATE_SCALAR_W;
     if (a.gates & GATE_LAYER_PREP)
       hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_LAYER>), grid, block, 0, st, a);
+    else if (a.gates == kda)
+      hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_KDA>), grid, block, 0, st, a);
+    else if (a.gates == (kda | GATE_SCALAR_ALPHA))
+      hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_GDN>), grid, block, 0, st, a);
     else if (a.gates)
       hipLaunchKernelGGL((gdn2_fused_kernel<IO, D, C, NG, GM_GATES>), grid, block, 0, st, a);
     else

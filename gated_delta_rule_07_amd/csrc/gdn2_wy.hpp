@@ -66,6 +66,17 @@ template <> struct raw4<float> {
     return r;
   }
   __device__ static __forceinline__ raw4 splat(float e) { return fill(e); }
+  // one element parked in slot 0 (the others unspecified) and read back
+  __device__ static __forceinline__ raw4 first(float e) {
+    raw4 r;
+    r.x[0] = e;
+    return r;
+  }
+  __device__ __forceinline__ float first() const { return x[0]; }
+  // x where keep, else four copies of e
+  __device__ static __forceinline__ raw4 select(bool keep, const raw4 &x, float e) {
+    return keep ? x : fill(e);
+  }
   __device__ __forceinline__ f32x4 f() const { return x; }
 };
 template <> struct raw4<bf16_t> {
@@ -81,6 +92,19 @@ template <> struct raw4<bf16_t> {
     raw4 r;
     r.x.x = static_cast<uint32_t>(e) | (static_cast<uint32_t>(e) << 16);
     r.x.y = r.x.x;
+    return r;
+  }
+  __device__ static __forceinline__ raw4 first(bf16_t e) {
+    raw4 r;
+    r.x.x = e;
+    return r;
+  }
+  __device__ __forceinline__ bf16_t first() const { return static_cast<bf16_t>(x.x & 0xffffu); }
+  __device__ static __forceinline__ raw4 select(bool keep, const raw4 &x, float e) {
+    const raw4 f = fill(e);
+    raw4 r;
+    r.x.x = keep ? x.x.x : f.x.x;
+    r.x.y = keep ? x.x.y : f.x.y;
     return r;
   }
   __device__ __forceinline__ f32x4 f() const {
@@ -187,14 +211,12 @@ __device__ __forceinline__ constexpr int tri_index(int I, int J) { return I * (I
 
 // Per-wave registers of one chunk's row phases.
 // Rows of q, k, b, alpha held by one lane.  With layer prep (LP) alpha is
-// kept as log2 of the decay in float32 (lg), and qs / ks are the lane's row
-// scales 1 / ||q_t||, 1 / ||k_t|| (the raw rows stay in q, k).
+// kept as log2 of the decay in float32 (lg), and q, k are the raw rows.
 template <typename IO, int D, bool LP = false> struct wy_rows {
   static constexpr int NK = D / 16;
   raw4<IO> q[NK], k[NK], b[NK];
   raw4<IO> al[LP ? 1 : NK];
   f32x4 lg[LP ? NK : 1];
-  float qs, ks;
 };
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
@@ -207,119 +229,158 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
 // GATE_SCALAR_B / GATE_SCALAR_ALPHA, b / alpha are one element per (token,
 // head), repeated over the channels.
 // Input modes of the loaders (compile-time): GM_PLAIN, every gate per
-// channel; GM_GATES, b / w / alpha may each be per (token, head) (the
-// GATE_SCALAR_* bits of chunk_args::gates); GM_LAYER, layer prep (raw q, k,
-// gate logits, float32 log decay) with the same per-(token, head) options.
-constexpr int GM_PLAIN = 0, GM_GATES = 1, GM_LAYER = 2;
+// channel; GM_KDA, b and w per (token, head); GM_GDN, b, w and alpha per
+// (token, head); GM_GATES, any of them per (token, head), read from the
+// GATE_SCALAR_* bits of chunk_args::gates at run time; GM_LAYER, layer prep
+// (raw q, k, gate logits, float32 log decay) with the same run-time bits.
+constexpr int GM_PLAIN = 0, GM_GATES = 1, GM_LAYER = 2, GM_KDA = 3, GM_GDN = 4;
 
-template <typename IO, int D, int GM = GM_PLAIN>
-__device__ __forceinline__ void wy_load_rows(const chunk_args &a, long t0, int len, int h, int t, int g,
-                                             wy_rows<IO, D, GM == GM_LAYER> &r) {
-  constexpr int NK = D / 16;
-  constexpr bool LP = GM == GM_LAYER;
+// Loads the inputs of one chunk, with the gate layouts fixed at compile time
+// (SB, SW, SA: b, w, alpha one element per (token, head)):
+//  - rows of q, k, b, alpha for token t = 16 I + m of the lane (wy_rows);
+//  - v and w of all C tokens for NVW column tiles starting at vt0 (RowFrag
+//    layout: lane (m, g) holds row 16J + m, columns 16vt + 4g .. +3).
+// Rows past the end must act as absent: k = 0, v = 0 and alpha = 1 (no
+// decay).  Their loads read the chunk's first row instead (always in the
+// sequence; element `row` exists in either gate layout), unconditionally, and
+// the masks are applied only after every load has issued: no branch and no
+// consumer sits between the loads, so no memory round trip is paid before
+// the others start.  k = 0 and v = 0 remove b and w of those rows, and q only
+// reaches their own (unstored) outputs, so b, w and q need no mask.  With
+// layer prep (LP) alpha is the float32 natural-log decay, kept as log2 in lg.
+template <typename IO, int D, int C, int NVW, bool LP, bool SB, bool SW, bool SA>
+__device__ __forceinline__ void wy_load_chunk_t(const chunk_args &a, long t0, int len, int h, int I, int vt0,
+                                                bool owner, int m, int g, wy_rows<IO, D, LP> &r,
+                                                raw4<IO> (&v)[C / 16][NVW], raw4<IO> (&w)[C / 16][NVW]) {
+  constexpr int NK = D / 16, NB = C / 16;
+  constexpr float LOG2E = 1.4426950408889634f;
+  // waves whose column tiles lie past dv load no v, w (uniform per wave)
+  constexpr bool ALL_OWNERS = (NB - 1) * NVW < NK;
+  const int t = 16 * I + m;
   const bool valid = t < len;
   const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
-  if constexpr (GM == GM_PLAIN) {
+  const IO *bp = static_cast<const IO *>(a.b);
+  const IO *ap = static_cast<const IO *>(a.al);
+  const float *ga = static_cast<const float *>(a.al);
+  if constexpr (SB)
+    r.b[0] = raw4<IO>::first(bp[row]);
+  if constexpr (SA && !LP)
+    r.al[0] = raw4<IO>::first(ap[row]);
+  if constexpr (SA && LP)
+    r.lg[0][0] = ga[row];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const int c0 = 16 * kk + 4 * g;
-      if (valid) {
-        r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
-        r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
-        r.b[kk] = raw4<IO>::ld(static_cast<const IO *>(a.b) + row * D + c0);
-        r.al[kk] = raw4<IO>::ld(static_cast<const IO *>(a.al) + row * D + c0);
-      } else {
-        r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
-        r.al[kk] = raw4<IO>::fill(1.f);
+  for (int kk = 0; kk < NK; ++kk) {
+    const int c0 = 16 * kk + 4 * g;
+    r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
+    r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
+    if constexpr (!SB)
+      r.b[kk] = raw4<IO>::ld(bp + row * D + c0);
+    if constexpr (!SA && !LP)
+      r.al[kk] = raw4<IO>::ld(ap + row * D + c0);
+    if constexpr (!SA && LP)
+      r.lg[kk] = *reinterpret_cast<const f32x4 *>(ga + row * D + c0);
+  }
+  bool vjs[NB];
+  if (ALL_OWNERS || owner) {
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      const int tj = 16 * J + m;
+      vjs[J] = tj < len;
+      const size_t vrow = static_cast<size_t>(t0 + (vjs[J] ? tj : 0)) * a.H + h;
+      if constexpr (SW)
+        w[J][0] = raw4<IO>::first(static_cast<const IO *>(a.w)[vrow]);
+#pragma unroll
+      for (int j = 0; j < NVW; ++j) {
+        const int c0 = 16 * (vt0 + j) + 4 * g;
+        v[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.v) + vrow * D + c0);
+        if constexpr (!SW)
+          w[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.w) + vrow * D + c0);
       }
     }
   } else {
-    // per-(token, head) b and / or alpha: one element for all channels of the row
-    const IO *bp = static_cast<const IO *>(a.b);
-    const IO *ap = static_cast<const IO *>(a.al);
-    const bool sb = a.gates & GATE_SCALAR_B, sa = a.gates & GATE_SCALAR_ALPHA;
-    const raw4<IO> bs = raw4<IO>::splat((valid && sb) ? bp[row] : io<IO>::from_f(0.f));
-    raw4<IO> as = raw4<IO>::fill(1.f);
-    if constexpr (!LP)
-      as = raw4<IO>::splat((valid && sa) ? ap[row] : io<IO>::from_f(1.f));
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const int c0 = 16 * kk + 4 * g;
-      if (valid) {
-        r.q[kk] = raw4<IO>::ld(static_cast<const IO *>(a.q) + row * D + c0);
-        r.k[kk] = raw4<IO>::ld(static_cast<const IO *>(a.k) + row * D + c0);
-        r.b[kk] = sb ? bs : raw4<IO>::ld(bp + row * D + c0);
-        if constexpr (!LP)
-          r.al[kk] = sa ? as : raw4<IO>::ld(ap + row * D + c0);
-      } else {
-        r.q[kk] = r.k[kk] = r.b[kk] = raw4<IO>::fill(0.f);
-        if constexpr (!LP)
-          r.al[kk] = raw4<IO>::fill(1.f);
-      }
+    for (int J = 0; J < NB; ++J) {
+      vjs[J] = false;
+#pragma unroll
+      for (int j = 0; j < NVW; ++j)
+        v[J][j] = w[J][j] = raw4<IO>::fill(0.f);
     }
   }
-  r.qs = r.ks = 1.f;
-  if constexpr (LP) {
-    // float32 natural-log decay -> log2; rows past the end decay by 1
-    constexpr float LOG2E = 1.4426950408889634f;
-    const float *ga = static_cast<const float *>(a.al);
-    const float gs = (valid && (a.gates & GATE_SCALAR_ALPHA)) ? ga[row] * LOG2E : 0.f;
+  // every load has issued; now the masks and splats
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      if (!valid || (a.gates & GATE_SCALAR_ALPHA))
+  for (int kk = 0; kk < NK; ++kk)
+    r.k[kk] = raw4<IO>::select(valid, r.k[kk], 0.f);
+  if constexpr (SB) {
+    const raw4<IO> bs = raw4<IO>::splat(r.b[0].first());
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      r.b[kk] = bs;
+  }
+  if constexpr (!LP) {
+    if constexpr (SA) {
+      const raw4<IO> as = raw4<IO>::splat(valid ? r.al[0].first() : io<IO>::from_f(1.f));
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        r.al[kk] = as;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        r.al[kk] = raw4<IO>::select(valid, r.al[kk], 1.f);
+    }
+  } else {
+    if constexpr (SA) {
+      const float gs = valid ? r.lg[0][0] * LOG2E : 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
         r.lg[kk] = f32x4{gs, gs, gs, gs};
-      else
-        r.lg[kk] = *reinterpret_cast<const f32x4 *>(ga + row * D + 16 * kk + 4 * g) * LOG2E;
-    }
-    // row norms: this lane holds 4 of every 16 channels; the lanes m, m+16,
-    // m+32, m+48 together hold the whole row
-    float sq = 0.f, sk = 0.f;
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const f32x4 x = r.q[kk].f(), y = r.k[kk].f();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sq += x[i] * x[i];
-        sk += y[i] * y[i];
-      }
+      for (int kk = 0; kk < NK; ++kk)
+        r.lg[kk] = valid ? r.lg[kk] * LOG2E : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    sq += __shfl_xor(sq, 16, 64);
-    sk += __shfl_xor(sk, 16, 64);
-    sq += __shfl_xor(sq, 32, 64);
-    sk += __shfl_xor(sk, 32, 64);
-    r.qs = sq > 0.f ? __frsqrt_rn(sq) : 0.f;
-    r.ks = sk > 0.f ? __frsqrt_rn(sk) : 0.f;
+  }
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    if constexpr (SW) {
+      const raw4<IO> s = raw4<IO>::splat(w[J][0].first());
+#pragma unroll
+      for (int j = 0; j < NVW; ++j)
+        w[J][j] = s;
+    }
+#pragma unroll
+    for (int j = 0; j < NVW; ++j)
+      v[J][j] = raw4<IO>::select(vjs[J], v[J][j], 0.f);
   }
 }
 
-// Loads v and w of all C tokens for NVW column tiles starting at vt0
-// (RowFrag layout: lane (m, g) holds row 16J + m, columns 16vt + 4g .. +3).
-// With GATE_SCALAR_W, w is one element per (token, head).
-template <typename IO, int D, int C, int NVW, int GM = GM_PLAIN>
-__device__ __forceinline__ void wy_load_vw(const chunk_args &a, long t0, int len, int h, int vt0,
-                                           bool owner, int m, int g, raw4<IO> (&v)[C / 16][NVW],
-                                           raw4<IO> (&w)[C / 16][NVW]) {
-  constexpr int NB = C / 16;
-  const bool sw = GM != GM_PLAIN && (a.gates & GATE_SCALAR_W);
-#pragma unroll
-  for (int J = 0; J < NB; ++J) {
-    const int tj = 16 * J + m;
-    const bool vj = owner && tj < len;
-    const size_t row = static_cast<size_t>(t0 + (vj ? tj : 0)) * a.H + h;
-    raw4<IO> ws = raw4<IO>::fill(0.f);
-    if constexpr (GM != GM_PLAIN)
-      ws = raw4<IO>::splat((vj && sw) ? static_cast<const IO *>(a.w)[row] : io<IO>::from_f(0.f));
-#pragma unroll
-    for (int j = 0; j < NVW; ++j) {
-      const int c0 = 16 * (vt0 + j) + 4 * g;
-      if (vj) {
-        v[J][j] = raw4<IO>::ld(static_cast<const IO *>(a.v) + row * D + c0);
-        w[J][j] = sw ? ws : raw4<IO>::ld(static_cast<const IO *>(a.w) + row * D + c0);
-      } else {
-        v[J][j] = w[J][j] = raw4<IO>::fill(0.f);
-      }
+// Inputs of one chunk in input mode GM.  The modes that read the layouts at
+// run time branch once, uniformly, into the straight-line variants.
+template <typename IO, int D, int C, int NVW, int GM>
+__device__ __forceinline__ void wy_load_chunk(const chunk_args &a, long t0, int len, int h, int I, int vt0,
+                                              bool owner, int m, int g, wy_rows<IO, D, GM == GM_LAYER> &r,
+                                              raw4<IO> (&v)[C / 16][NVW], raw4<IO> (&w)[C / 16][NVW]) {
+  constexpr bool LP = GM == GM_LAYER;
+#define GDN2_LOAD(SB, SW, SA) \
+  wy_load_chunk_t<IO, D, C, NVW, LP, SB, SW, SA>(a, t0, len, h, I, vt0, owner, m, g, r, v, w)
+  if constexpr (GM == GM_PLAIN) {
+    GDN2_LOAD(false, false, false);
+  } else if constexpr (GM == GM_KDA) {
+    GDN2_LOAD(true, true, false);
+  } else if constexpr (GM == GM_GDN) {
+    GDN2_LOAD(true, true, true);
+  } else {
+    switch (a.gates & (GATE_SCALAR_B | GATE_SCALAR_W | GATE_SCALAR_ALPHA)) {
+      case 0: GDN2_LOAD(false, false, false); break;
+      case GATE_SCALAR_B: GDN2_LOAD(true, false, false); break;
+      case GATE_SCALAR_W: GDN2_LOAD(false, true, false); break;
+      case GATE_SCALAR_B | GATE_SCALAR_W: GDN2_LOAD(true, true, false); break;
+      case GATE_SCALAR_ALPHA: GDN2_LOAD(false, false, true); break;
+      case GATE_SCALAR_B | GATE_SCALAR_ALPHA: GDN2_LOAD(true, false, true); break;
+      case GATE_SCALAR_W | GATE_SCALAR_ALPHA: GDN2_LOAD(false, true, true); break;
+      default: GDN2_LOAD(true, true, true); break;
     }
   }
+#undef GDN2_LOAD
 }
 
 // Phase 1: log2(alpha), prefix sums over the tokens of each sub-block, and the
@@ -383,6 +444,31 @@ template <typename IO, int D> struct wy_ops {
   frag<IO> ef[NK], qf[NK], khf[NK], qcf[NK];
 };
 
+// Layer prep: 1 / ||q_t|| and 1 / ||k_t|| of this lane's row (zero rows keep
+// zero).  The lane holds 4 of every 16 channels; lanes m, m+16, m+32, m+48
+// together hold the whole row.  Kept apart from the loads so that waiting for
+// q and k does not hold back the loads issued after them.
+template <typename IO, int D>
+__device__ __forceinline__ void wy_row_scales(const wy_rows<IO, D, true> &r, float &qs, float &ks) {
+  constexpr int NK = D / 16;
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const f32x4 x = r.q[kk].f(), y = r.k[kk].f();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sq += x[i] * x[i];
+      sk += y[i] * y[i];
+    }
+  }
+  sq += __shfl_xor(sq, 16, 64);
+  sk += __shfl_xor(sk, 16, 64);
+  sq += __shfl_xor(sq, 32, 64);
+  sk += __shfl_xor(sk, 32, 64);
+  qs = sq > 0.f ? __frsqrt_rn(sq) : 0.f;
+  ks = sk > 0.f ? __frsqrt_rn(sk) : 0.f;
+}
+
 // Phase 1b: decayed, gated operands of sub-block I.  Writes the rescaled keys
 // for later sub-blocks and ColFrag(E) to LDS, and RowFrag(Kbar^T) tiles to
 // kb_out (the KB region of a block layout, LDS or global).
@@ -394,6 +480,9 @@ __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows
   constexpr int NB = C / 16, NK = D / 16;
   typedef frag<IO> F;
   const int g = lane >> 4;
+  float qs = 1.f, ks = 1.f;
+  if constexpr (LP)
+    wy_row_scales<IO, D>(r, qs, ks);
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const int c0 = 16 * kk + 4 * g;
@@ -407,8 +496,8 @@ __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows
     }
     f32x4 kf = r.k[kk].f(), bf = r.b[kk].f(), qf = r.q[kk].f();
     if constexpr (LP) {
-      kf *= r.ks;
-      qf *= r.qs;
+      kf *= ks;
+      qf *= qs;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         bf[i] = fast_sigmoid(bf[i]);
