@@ -5,7 +5,8 @@ leg may import this package.  It shares no code with the GPU library and the
 GPU library never imports it.
 
 ``fwd`` and ``decode`` run the plain float64 token-by-token recurrence written
-in C (``gdn2_oracle.c``).  Inputs are the stored tensors (float32 or bf16),
+in C (``gdn2_oracle.c``); ``bwd`` runs its hand-derived reverse-mode
+derivative, token by token from the last.  Inputs are the stored tensors (float32 or bf16),
 upcast to float64 exactly; outputs are float64 NumPy arrays.
 """
 from __future__ import annotations
@@ -46,6 +47,8 @@ def _load():
         lib.gdn2_oracle_fwd.argtypes = [dp] * 7 + [ip] + [ctypes.c_int] * 7 + [dp, dp]
         lib.gdn2_oracle_decode.restype = ctypes.c_int
         lib.gdn2_oracle_decode.argtypes = [dp] * 7 + [ctypes.c_int] * 5 + [dp]
+        lib.gdn2_oracle_bwd.restype = ctypes.c_int
+        lib.gdn2_oracle_bwd.argtypes = ([dp] * 7 + [ip] + [ctypes.c_int] * 6 + [dp] * 9)
         lib.gdn2_oracle_max_threads.restype = ctypes.c_int
         lib.gdn2_oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -114,3 +117,30 @@ def decode(q, k, v, alpha, b, w, S, rule: str = "R5"):
     if rc != 0:
         raise RuntimeError(f"gdn2_oracle_decode failed with code {rc}")
     return o, Sn
+
+
+def bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None):
+    """Gradients of the rule-0 forward: given dL/do [B,T,H,dv] and dL/dS_final
+    [N,H,dk,dv] (None = zero), returns a dict of float64 arrays dq, dk, dv,
+    dalpha, db, dw (each its input's shape) and dS0 [N,H,dk,dv]."""
+    q, k, v, alpha, b, w, do = (_f64(x) for x in (q, k, v, alpha, b, w, dout))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.numpy() if hasattr(cu_seqlens, "numpy") else cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        cu, N, cu_p = None, B, None
+    S0a, dSf = _f64(S0), _f64(dS_final)
+    g = {name: np.zeros(x.shape, dtype=np.float64)
+         for name, x in (("dq", q), ("dk", k), ("dv", v), ("dalpha", alpha), ("db", b), ("dw", w))}
+    g["dS0"] = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = _load().gdn2_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                 _ptr(S0a), cu_p, B, T, H, dk, dv, N, _ptr(do), _ptr(dSf),
+                                 _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
+                                 _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]))
+    if rc != 0:
+        raise RuntimeError(f"gdn2_oracle_bwd failed with code {rc}")
+    return g
