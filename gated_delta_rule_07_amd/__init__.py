@@ -7,6 +7,7 @@ PyTorch provides device memory and the current HIP stream.  There is no CPU
 fallback: without the library or a GPU these functions raise.
 
     o, S_final = chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk=64)
+    grads = chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, ...)
     o = decode_step(q, k, v, alpha, b, w, S)      # S updated in place
 
 Shapes: q, k, alpha, b [B, T, H, dk]; v, w [B, T, H, dv] (packed sequences:
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
         L.gdn2_chunk_fwd.restype = i
         L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
+        L.gdn2_chunk_bwd_workspace_bytes.restype = sz
+        L.gdn2_chunk_bwd_workspace_bytes.argtypes = [i] * 7 + [i]
+        L.gdn2_chunk_bwd.restype = i
+        L.gdn2_chunk_bwd.argtypes = [vp] * 8 + [i] * 8 + [u32] + [vp] * 9 + [vp, sz, vp]
         L.gdn2_decode_step.restype = i
         L.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
         L.gdn2_status_string.restype = ctypes.c_char_p
@@ -159,6 +164,59 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
         B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, dt, flags,
         _ptr(o), _ptr(Sf), _ptr(workspace), ws_bytes, _stream()))
     return o, Sf
+
+
+def bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chunk: int,
+                        dtype: torch.dtype) -> int:
+    code = GDN2_BF16 if dtype == torch.bfloat16 else GDN2_F32
+    return int(lib().gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, chunk, code))
+
+
+def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
+              chunk: int = 64, workspace=None, out=None, want_dS0: bool = True):
+    """Chunked backward of ``chunk_fwd`` (per-channel gates, prepared inputs).
+    Given dL/do (``dout``, like o) and dL/dS_final (or None for zero), returns
+    a dict with dq, dk, dv, dalpha, db, dw (each like its input) and dS0
+    ([N, H, dk, dv] float32, or None when ``want_dS0`` is False).  ``out``
+    may hold preallocated tensors under those names."""
+    _require_device(q, k, v, alpha, b, w, dout, S0, dS_final, cu_seqlens)
+    dt = _dtype_code(q)
+    for t in (k, v, alpha, b, w, dout):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, alpha, b, w, dout must share one dtype")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, name, full in ((alpha, "alpha", dk), (b, "b", dk), (k, "k", dk), (v, "v", dv), (w, "w", dv),
+                          (dout, "dout", dv)):
+        if tuple(t.shape) != (B, T, H, full):
+            raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}]")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for t, name in ((S0, "S0"), (dS_final, "dS_final")):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv)):
+            raise ValueError(f"{name} must be float32 [{N}, {H}, {dk}, {dv}]")
+    out = dict(out or {})
+    src = {"dq": q, "dk": k, "dv": v, "dalpha": alpha, "db": b, "dw": w}
+    for name, like in src.items():
+        if name not in out:
+            out[name] = torch.empty_like(like)
+    if want_dS0 and "dS0" not in out:
+        out["dS0"] = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    ns = N if cu_seqlens is not None else 0
+    ws_bytes = bwd_workspace_bytes(B, T, H, dk, dv, ns, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().gdn2_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, dk, dv, ns, chunk, dt, 0, _ptr(dout), _ptr(dS_final),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]),
+        _ptr(out["dw"]), _ptr(out.get("dS0")), _ptr(workspace), workspace.numel(), _stream()))
+    out.setdefault("dS0", None)
+    return out
 
 
 def decode_step(q, k, v, alpha, b, w, S, out=None):

@@ -221,6 +221,96 @@ int num_slots_for(int B, int T, int num_seqs, int chunk, bool packed) {
   return B * ((T + chunk - 1) / chunk);
 }
 
+// ---------------------------------------------------------------- backward --
+size_t bwd_scratch_floats_rt(int d, int c) {
+#define GDN2_BS(D, C) \
+  if (d == D && c == C) \
+    return gdn2::bwd_scratch_floats<D, C>();
+  GDN2_BS(16, 16) GDN2_BS(32, 16) GDN2_BS(64, 16) GDN2_BS(128, 16)
+  GDN2_BS(16, 64) GDN2_BS(32, 64) GDN2_BS(64, 64) GDN2_BS(128, 64)
+#undef GDN2_BS
+  return 0;
+}
+
+// Workgroups of the gradient kernel (each with its own scratch slot): enough
+// to fill the chip, and never more than there are chunk-heads.
+int bwd_grad_wgs(long chunk_heads) { return static_cast<int>(chunk_heads < 512 ? chunk_heads : 512); }
+
+template <typename IO, int D, int C> hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  gdn2::chunk_args &a = ba.f;
+  if (a.cu) {
+    prof_scope p("chunk_table", st);
+    e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  if (a.num_slots > 0) {
+    {
+      prof_scope p("chunk_prep", st);
+      e = gdn2::launch_chunk_prep<IO, D, C>(a, st);
+      if (e != hipSuccess)
+        return e;
+    }
+    {
+      prof_scope p("chunk_states", st);
+      e = gdn2::launch_chunk_states<IO, D, C>(a, st);
+      if (e != hipSuccess)
+        return e;
+    }
+  }
+  {
+    prof_scope p("bwd_dstate", st);
+    e = gdn2::launch_bwd_dstate<IO, D, C>(ba, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  if (a.num_slots > 0 && ba.grad_wgs > 0) {
+    prof_scope p("bwd_grad", st);
+    e = gdn2::launch_bwd_grad<IO, D, C>(ba, st);
+  }
+  return e;
+}
+
+hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, hipStream_t st) {
+#define GDN2_RB(IO, D, C) \
+  if (d == D && c == C)   \
+    return run_bwd<IO, D, C>(ba, C, st);
+  if (dt == GDN2_F32) {
+    GDN2_RB(float, 16, 16) GDN2_RB(float, 32, 16) GDN2_RB(float, 64, 16) GDN2_RB(float, 128, 16)
+    GDN2_RB(float, 16, 64) GDN2_RB(float, 32, 64) GDN2_RB(float, 64, 64) GDN2_RB(float, 128, 64)
+  } else {
+    GDN2_RB(gdn2::bf16_t, 16, 16) GDN2_RB(gdn2::bf16_t, 32, 16) GDN2_RB(gdn2::bf16_t, 64, 16)
+    GDN2_RB(gdn2::bf16_t, 128, 16) GDN2_RB(gdn2::bf16_t, 16, 64) GDN2_RB(gdn2::bf16_t, 32, 64)
+    GDN2_RB(gdn2::bf16_t, 64, 64) GDN2_RB(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_RB
+  return hipErrorInvalidValue;
+}
+
+// Byte layout of the backward's workspace: chunk table (packed input), the
+// forward's per-chunk blocks, entering states, leaving-state gradients, and
+// the gradient kernel's scratch slots.
+struct bwd_plan {
+  size_t table, blocks, states, dstates, scratch, total;
+  int wgs;
+};
+
+bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk, bool packed) {
+  bwd_plan p{};
+  const size_t slots = static_cast<size_t>(num_slots_for(B, T, N, chunk, packed));
+  const size_t sq = static_cast<size_t>(d) * d * sizeof(float);
+  p.table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
+  p.blocks = slots * H * chunk_block_bytes_rt(dt, d, chunk);
+  p.states = align256(slots * H * sq);
+  p.dstates = p.states;
+  p.wgs = bwd_grad_wgs(static_cast<long>(slots) * H);
+  p.scratch = static_cast<size_t>(p.wgs) * bwd_scratch_floats_rt(d, chunk) * sizeof(float);
+  p.total = p.table + p.blocks + p.states + p.dstates + p.scratch;
+  return p;
+}
+
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -353,6 +443,111 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   const hipError_t e = dispatch_chunk(dt, dk, chunk, a, flags, st);
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
+                                      gdn2_dtype_t dt) {
+  if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
+    return 0;
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return 0;
+  const int n = num_seqs > 0 ? num_seqs : B;
+  const bwd_plan pf = plan_bwd(dt, B, T, H, dk, B, chunk, false);
+  const bwd_plan pp = plan_bwd(dt, B, T, H, dk, n, chunk, true);
+  return pf.total > pp.total ? pf.total : pp.total;
+}
+
+gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *alpha,
+                             const void *b, const void *w, const float *S0,
+                             const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                             int num_seqs, int chunk, gdn2_dtype_t dt, uint32_t flags,
+                             const void *dout, const float *dS_final, void *dq, void *dk_out,
+                             void *dv_out, void *dalpha, void *db, void *dw, float *dS0,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: unknown dtype %d", static_cast<int>(dt));
+  if (flags != 0)
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_bwd: flags 0x%x: the backward takes per-channel gates and prepared inputs only",
+                flags);
+  if (B <= 0 || T < 0 || H <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: bad sizes B=%d T=%d H=%d", B, T, H);
+  if (dk != dv || !supported_dim(dk))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_bwd: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
+                dk, dv);
+  if (!supported_chunk(chunk))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: unsupported chunk %d (need 16 or 64)", chunk);
+  const bool packed = cu_seqlens != nullptr;
+  int N;
+  if (packed) {
+    if (B != 1)
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: packed input needs B == 1 (got %d)", B);
+    if (num_seqs <= 0)
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: packed input needs num_seqs > 0");
+    N = num_seqs;
+  } else {
+    if (num_seqs != 0 && num_seqs != B)
+      return fail(GDN2_ERR_INVALID_ARGUMENT,
+                  "gdn2_chunk_bwd: num_seqs=%d must be 0 or B=%d without cu_seqlens", num_seqs, B);
+    N = B;
+  }
+  if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !dout || !dq || !dk_out || !dv_out || !dalpha ||
+                !db || !dw))
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: null input or gradient pointer");
+  const void *ptrs[] = {q, k, v, alpha, b, w, S0, dout, dS_final, dq, dk_out, dv_out, dalpha, db, dw, dS0,
+                        workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p))
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: pointers must be 16-byte aligned");
+  const long long elems = static_cast<long long>(B) * T * H * dk;
+  if (elems > (1LL << 40))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: problem too large");
+  const bwd_plan plan = plan_bwd(dt, B, T, H, dk, N, chunk, packed);
+  if (workspace_bytes < plan.total || !workspace)
+    return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                "gdn2_chunk_bwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                plan.total);
+
+  gdn2::bwd_args ba{};
+  gdn2::chunk_args &a = ba.f;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.al = alpha;
+  a.b = b;
+  a.w = w;
+  a.S0 = S0;
+  a.cu = cu_seqlens;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.num_seqs = N;
+  a.num_slots = T == 0 ? 0 : num_slots_for(B, T, N, chunk, packed);
+  a.o = nullptr;
+  a.S_final = nullptr;
+  a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
+  a.gates = 0;
+  char *ws = static_cast<char *>(workspace);
+  a.offsets = packed ? reinterpret_cast<int32_t *>(ws) : nullptr;
+  a.blocks = ws + plan.table;
+  a.states = reinterpret_cast<float *>(ws + plan.table + plan.blocks);
+  ba.dstates = reinterpret_cast<float *>(ws + plan.table + plan.blocks + plan.states);
+  ba.scratch = reinterpret_cast<float *>(ws + plan.table + plan.blocks + plan.states + plan.dstates);
+  ba.grad_wgs = plan.wgs;
+  ba.dout = dout;
+  ba.dSf = dS_final;
+  ba.dS0 = dS0;
+  ba.dq = dq;
+  ba.dk = dk_out;
+  ba.dv = dv_out;
+  ba.dal = dalpha;
+  ba.db = db;
+  ba.dw = dw;
+  const hipError_t e = dispatch_bwd(dt, dk, chunk, ba, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -147,7 +147,10 @@ template <typename IO, int D, int C, int NT> struct scan_cfg {
 // Grid: units_pad * NGRP workgroups, units_pad = N*H rounded up to 8;
 // consecutive ids go to the 8 XCDs round-robin and all workgroups of one head
 // share an XCD (and its L2).
-template <typename IO, int D, int C, int NT>
+// With ST (states mode, used by the backward) the kernel writes, instead of
+// o, the float32 state entering every chunk to a.states (chunk slot order,
+// [slot * H + h][dk][dv]).
+template <typename IO, int D, int C, int NT, bool ST = false>
 __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<IO, D, C, NT>::NLW))
     gdn2_chunk_scan_kernel(chunk_args a) {
   typedef scan_cfg<IO, D, C, NT> K;
@@ -318,8 +321,18 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
 
   // One chunk: products, o stores (rows < len unless FULL) and state update.
   auto chunk_step = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], const F(&ocur)[NB][CPW], long t0,
-                        int len, auto full) {
+                        int len, int c, auto full) {
     constexpr bool FULL = decltype(full)::value;
+    if constexpr (ST) {
+      float *sp = a.states + (static_cast<size_t>(c_begin + c) * a.H + h) * D * D;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sp[(16 * kk + 4 * g + i) * D + 16 * (vt0 + j) + m] = S[kk][j][i];
+    }
     // o goes through a global-address-space pointer so that the compiler
     // knows these stores never alias the LDS operands it wants to hoist
     typedef __attribute__((address_space(1))) typename io<IO>::elem gelem;
@@ -392,7 +405,7 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
 #pragma unroll
       for (int j = 0; j < CPW; ++j) {
         zf[tt][j] = F::from(z[j]);
-        if (FULL || t < len)
+        if (!ST && (FULL || t < len))
           store4_global(gout + (static_cast<size_t>(t0 + t) * a.H + h) * D + 16 * (vt0 + j) + 4 * g, ot[j]);
       }
     }
@@ -435,9 +448,9 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
       if constexpr (!K::UO_LDS)
         tload(c + 1, unxt, onxt);
       if (len == C)
-        chunk_step(sb, ucur, ocur, t0, len, std::true_type{});
+        chunk_step(sb, ucur, ocur, t0, len, c, std::true_type{});
       else
-        chunk_step(sb, ucur, ocur, t0, len, std::false_type{});
+        chunk_step(sb, ucur, ocur, t0, len, c, std::false_type{});
       if constexpr (NBUF == 1)
         lds_barrier();  // done with the only buffer
       lds_barrier();    // chunk c + 1 is in LDS
@@ -513,11 +526,12 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
   return hipGetLastError();
 }
 
-template <typename IO, int D, int C, int NT> hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
+template <typename IO, int D, int C, int NT, bool ST>
+hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
   typedef scan_cfg<IO, D, C, NT> K;
   const int units = a.num_seqs * a.H;
   const int units_pad = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT>), dim3(units_pad * K::NGRP),
+  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT, ST>), dim3(units_pad * K::NGRP),
                      dim3(64 * (K::NCW + K::NLW)), 0, st, a);
   return hipGetLastError();
 }
@@ -528,22 +542,30 @@ template <typename IO, int D, int C, int NT> hipError_t launch_scan_nt(const chu
 // sequential per-chunk path; many units get 4 tiles per workgroup.
 // float32 inputs with d = 128, C = 64 keep one tile per workgroup: their
 // wider fragments would not fit in the registers of the larger workgroups.
-template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st) {
+template <typename IO, int D, int C, bool ST> hipError_t launch_scan_any(const chunk_args &a, hipStream_t st) {
   constexpr int NK = D / 16;
   const long units = static_cast<long>(a.num_seqs) * a.H;
   if constexpr (sizeof(IO) == 4 && D * C >= 128 * 64) {
-    return launch_scan_nt<IO, D, C, 1>(a, st);
+    return launch_scan_nt<IO, D, C, 1, ST>(a, st);
   } else {
     if (units * NK <= 256)
-      return launch_scan_nt<IO, D, C, 1>(a, st);
+      return launch_scan_nt<IO, D, C, 1, ST>(a, st);
     if constexpr (NK >= 2) {
       if (NK < 4 || units * (NK / 2) <= 256)
-        return launch_scan_nt<IO, D, C, 2>(a, st);
+        return launch_scan_nt<IO, D, C, 2, ST>(a, st);
     }
     if constexpr (NK >= 4)
-      return launch_scan_nt<IO, D, C, 4>(a, st);
-    return launch_scan_nt<IO, D, C, 1>(a, st);
+      return launch_scan_nt<IO, D, C, 4, ST>(a, st);
+    return launch_scan_nt<IO, D, C, 1, ST>(a, st);
   }
+}
+
+template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st) {
+  return launch_scan_any<IO, D, C, false>(a, st);
+}
+
+template <typename IO, int D, int C> hipError_t launch_chunk_states(const chunk_args &a, hipStream_t st) {
+  return launch_scan_any<IO, D, C, true>(a, st);
 }
 
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st) {
@@ -554,7 +576,8 @@ hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets,
 #define GDN2_INST_CHUNK(IO, D, C)                                                           \
   template size_t chunk_block_bytes<IO, D, C>();                                            \
   template hipError_t launch_chunk_prep<IO, D, C>(const chunk_args &, hipStream_t);         \
-  template hipError_t launch_chunk_scan<IO, D, C>(const chunk_args &, hipStream_t);
+  template hipError_t launch_chunk_scan<IO, D, C>(const chunk_args &, hipStream_t);        \
+  template hipError_t launch_chunk_states<IO, D, C>(const chunk_args &, hipStream_t);
 
 GDN2_INST_CHUNK(float, 16, 16)
 GDN2_INST_CHUNK(float, 32, 16)

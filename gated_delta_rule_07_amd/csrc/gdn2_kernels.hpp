@@ -25,6 +25,7 @@ struct chunk_args {
   char *blocks;      // num_slots * H blocks of blk_bytes each
   size_t blk_bytes;
   uint32_t gates;    // GATE_* bits: inputs given per (token, head) instead of per channel
+  float *states;     // backward only: state entering every chunk, [slot * H + h][dk][dv]
 };
 
 // chunk_args::gates: b, w or alpha is one value per (token, head), laid out
@@ -37,9 +38,29 @@ constexpr uint32_t GATE_SCALAR_B = 1u, GATE_SCALAR_W = 2u, GATE_SCALAR_ALPHA = 4
 template <typename IO, int D, int C> size_t chunk_block_bytes();
 template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_args &a, hipStream_t st);
 template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st);
+// the state scan in states mode: a.states instead of o (o is not written)
+template <typename IO, int D, int C> hipError_t launch_chunk_states(const chunk_args &a, hipStream_t st);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st);
 template <typename IO, int D, int C, int NG> bool fused_supported();
 template <typename IO, int D, int C, int NG> hipError_t launch_fused(const chunk_args &a, hipStream_t st);
+
+// Everything the chunked backward's own kernels need on top of the forward's
+// arguments (inputs, chunk table, per-chunk blocks and entering states).
+struct bwd_args {
+  chunk_args f;
+  const void *dout;      // dL/do [B, T, H, dv], element type IO
+  const float *dSf;      // dL/dS_final [N, H, dk, dv] or nullptr (zero)
+  float *dstates;        // dL/d(state leaving each chunk), [slot * H + h][dk][dv]
+  float *dS0;            // dL/dS0 [N, H, dk, dv] or nullptr
+  void *dq, *dk, *dv, *dal, *db, *dw;  // gradients, element type IO, input layouts
+  float *scratch;        // per-workgroup scratch of the gradient kernel
+  int grad_wgs;          // workgroups (scratch slots) of the gradient kernel
+};
+
+// float32 scratch elements per workgroup of the gradient kernel
+template <int D, int C> size_t bwd_scratch_floats();
+template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args &a, hipStream_t st);
+template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st);
 
 template <typename IO, int D>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,

@@ -100,6 +100,17 @@ def make_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed
     return out
 
 
+def make_bwd_grads(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                   num_seqs: int | None = None, with_dS: bool = True) -> dict:
+    """Incoming gradients of one backward call: dL/do ~ N(0, 1) [B, T, H, dv]
+    in ``dtype`` and dL/dS_final ~ N(0, 1) [N, H, dk, dv] float32 (None when
+    ``with_dS`` is False)."""
+    rng = np.random.default_rng(seed + 7919)
+    n = B if num_seqs is None else num_seqs
+    dS = torch.from_numpy(rng.standard_normal((n, H, dk, dv))).float().contiguous() if with_dS else None
+    return {"dout": _cast(rng.standard_normal((B, T, H, dv)), dtype), "dS_final": dS}
+
+
 def make_layer_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
                       s0: str | None = None, scalar_beta: bool = False) -> dict:
     """Raw layer inputs of one chunked-forward call in layer-prep mode: q and

@@ -138,6 +138,41 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
                              float *S_final, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Bytes of device workspace gdn2_chunk_bwd needs for these sizes (0 when
+ * the sizes are unsupported); num_seqs as for gdn2_chunk_fwd_workspace_bytes. */
+size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk, gdn2_dtype_t dt);
+
+/* Chunked backward: the gradients of a scalar loss L through the forward
+ * above (the same recurrence, inputs and sizes as gdn2_chunk_fwd), with both
+ * gates differentiated inside the chunked products (aiexpert.news/pt, method
+ * paragraph: the gate-aware backward; aixai.ru blog, section on how the
+ * method is implemented in practice).
+ *   q .. cu_seqlens, B .. dt : the forward's inputs and sizes.
+ *   flags     : must be 0 (per-channel gates and prepared inputs only; the
+ *               gate layout, layer prep and path flags of the forward return
+ *               GDN2_ERR_UNSUPPORTED).
+ *   dout      : dL/do [B, T, H, dv], element type dt.
+ *   dS_final  : dL/dS_final [N, H, dk, dv] float32, or NULL for zero.
+ *   dq, dk_out, dv_out, dalpha, db, dw : outputs (the gradients of q, k,
+ *               v, alpha, b, w), each with its input's layout and
+ *               element type dt (bfloat16 rounded to nearest even).  dalpha is
+ *               the gradient with respect to alpha itself.
+ *   dS0       : dL/dS0 [N, H, dk, dv] float32, or NULL.
+ *   workspace : device scratch of at least gdn2_chunk_bwd_workspace_bytes(...)
+ *               bytes; its contents on entry are irrelevant.
+ * The kernels recompute the forward's per-chunk quantities and the state
+ * entering every chunk; no forward output needs to be kept.  The numerical
+ * domain is the chunked forward's (see the conventions above); alpha must be
+ * nonzero. */
+gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *alpha,
+                             const void *b, const void *w, const float *S0,
+                             const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                             int num_seqs, int chunk, gdn2_dtype_t dt, uint32_t flags,
+                             const void *dout, const float *dS_final, void *dq, void *dk_out,
+                             void *dv_out, void *dalpha, void *db, void *dw, float *dS0,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* One recurrent decode step for N sequences x H heads at constant memory
  * (aixai.ru blog: constant-memory decoding; needhelp.icu/de, section on the
  * attention bottleneck).  q, k, alpha, b are [N, H, dk]; v, w, o are

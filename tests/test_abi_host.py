@@ -102,3 +102,38 @@ def test_header_compiles_as_c(tmp_path):
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def call_bwd(L, *, ptr=FAKE, B=1, T=64, H=1, dk=16, dv=16, N=0, chunk=16, dt=F32, flags=0,
+             cu=None, ws=FAKE, ws_bytes=1 << 40, dout=None, dq=None):
+    p = ptr
+    return L.gdn2_chunk_bwd(p, p, p, p, p, p, None, cu, B, T, H, dk, dv, N, chunk, dt, flags,
+                            dout if dout is not None else p, None, dq if dq is not None else p,
+                            p, p, p, p, p, None, ws, ws_bytes, None)
+
+
+def test_bwd_rejects_before_launch(L):
+    assert call_bwd(L, dk=24, dv=24) == 2
+    assert call_bwd(L, dk=64, dv=32) == 2
+    assert call_bwd(L, chunk=32) == 2
+    assert call_bwd(L, dt=7) == 2
+    assert call_bwd(L, B=0) == 1
+    assert call_bwd(L, T=-1) == 1
+    # the backward takes no forward path, gate layout or layer-prep flag
+    for flag in (1 << 0, 1 << 1, 1 << 2, 1 << 3, 1 << 4, 1 << 5, 1 << 6):
+        assert call_bwd(L, flags=flag) == 2
+    assert call_bwd(L, dout=0x10008) == 1      # misaligned
+    assert call_bwd(L, ws_bytes=16) == 3
+    assert call_bwd(L, B=2, N=1) == 1          # num_seqs without cu_seqlens
+    assert call_bwd(L, B=2, N=2, cu=FAKE) == 1  # packed needs B == 1
+    assert L.gdn2_last_error() != b""
+
+
+def test_bwd_workspace_bytes(L):
+    n = L.gdn2_chunk_bwd_workspace_bytes(2, 200, 3, 64, 64, 0, 64, BF16)
+    fwd = L.gdn2_chunk_fwd_workspace_bytes(2, 200, 3, 64, 64, 0, 64, BF16)
+    # at least the forward's blocks plus two float32 states per chunk-head
+    assert n >= fwd + 2 * (2 * 4 * 3) * 64 * 64 * 4
+    assert L.gdn2_chunk_bwd_workspace_bytes(2, 200, 3, 48, 48, 0, 64, BF16) == 0
+    assert L.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 32, 32, 3, 16, F32) >= \
+        L.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 32, 32, 0, 16, F32)

@@ -1,0 +1,124 @@
+"""GPU parity of the chunked backward (gdn2_chunk_bwd) against the float64
+oracle backward (MI355X only).  Every gradient tensor is compared element by
+element: max |x - ref| / max |ref| <= 1e-4 for float32 inputs and 2e-2 for
+bfloat16 inputs (the forward's bars), on the same stored inputs and incoming
+gradients."""
+import numpy as np
+import pytest
+import torch
+
+import gdn2_inputs as gi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("q", "k", "v", "alpha", "b", "w")
+GRADS = ("dq", "dk", "dv", "dalpha", "db", "dw")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_07_amd as mod
+    mod.lib()
+    return mod
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def gpu_bwd(g, inp, grads, chunk, cu=None):
+    d = {n: inp[n].cuda() for n in NAMES}
+    S0 = inp.get("S0")
+    dSf = grads["dS_final"]
+    out = g.chunk_bwd(*(d[n] for n in NAMES), grads["dout"].cuda(),
+                      S0=None if S0 is None else S0.cuda(), dS_final=None if dSf is None else dSf.cuda(),
+                      cu_seqlens=None if cu is None else cu.cuda(), chunk=chunk)
+    torch.cuda.synchronize()
+    return {k: v.float().cpu().numpy() for k, v in out.items() if v is not None}
+
+
+def check(got, ref, tol, label, sel=None):
+    for name in GRADS + ("dS0",):
+        x = got[name] if sel is None else sel(name, got[name])
+        e = rel_err(x, ref[name])
+        print(f"{label} {name} err={e:.3e}", flush=True)
+        assert e <= tol, f"{label}: {name} error {e:.3e} > {tol}"
+
+
+CASES = [  # dtype, d, chunk, B, T, H, s0, dS_final
+    ("f32", 32, 16, 2, 77, 2, "normal", True),
+    ("f32", 64, 64, 1, 190, 2, "normal", True),
+    ("f32", 128, 64, 1, 130, 1, None, False),
+    ("f32", 16, 64, 2, 64, 1, None, True),
+    ("bf16", 128, 64, 1, 200, 2, "normal", True),
+    ("bf16", 16, 64, 2, 100, 1, None, True),
+    ("bf16", 64, 16, 1, 77, 2, "normal", False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,B,T,H,s0,with_dS", CASES)
+def test_bwd_small(g, dtype, d, chunk, B, T, H, s0, with_dS):
+    seed = 100 + d + T
+    inp = gi.make_chunk_inputs(B, T, H, d, d, dtype, seed, s0=s0)
+    grads = gi.make_bwd_grads(B, T, H, d, d, dtype, seed, with_dS=with_dS)
+    print(f"case {dtype} d={d} C={chunk} B={B} T={T} H={H}", flush=True)
+    got = gpu_bwd(g, inp, grads, chunk)
+    ref = oracle.bwd(*(inp[n] for n in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"])
+    check(got, ref, TOL[dtype], f"{dtype} d={d} C={chunk} T={T}")
+
+
+def test_bwd_packed_with_empty_sequences(g):
+    lens = [70, 0, 1, 64, 130, 0, 15]
+    cu = gi.cu_seqlens_from(lens)
+    T = int(cu[-1])
+    inp = gi.make_chunk_inputs(1, T, 2, 64, 64, "f32", seed=19, s0="normal", num_seqs=len(lens))
+    grads = gi.make_bwd_grads(1, T, 2, 64, 64, "f32", seed=19, num_seqs=len(lens))
+    ref = oracle.bwd(*(inp[n] for n in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"],
+                     cu_seqlens=cu)
+    for chunk in (16, 64):
+        print(f"case packed C={chunk}", flush=True)
+        got = gpu_bwd(g, inp, grads, chunk, cu=cu)
+        check(got, ref, TOL["f32"], f"packed C={chunk}")
+
+
+def test_bwd_zero_length(g):
+    inp = gi.make_chunk_inputs(2, 0, 2, 32, 32, "f32", seed=3, s0="normal")
+    grads = gi.make_bwd_grads(2, 0, 2, 32, 32, "f32", seed=3)
+    print("case T=0", flush=True)
+    got = gpu_bwd(g, inp, grads, 64)
+    np.testing.assert_array_equal(got["dS0"], grads["dS_final"].numpy())
+
+
+def test_bwd_deterministic(g):
+    inp = gi.make_chunk_inputs(1, 300, 2, 128, 128, "bf16", seed=21, s0="normal")
+    grads = gi.make_bwd_grads(1, 300, 2, 128, 128, "bf16", seed=21)
+    print("case deterministic", flush=True)
+    a = gpu_bwd(g, inp, grads, 64)
+    b = gpu_bwd(g, inp, grads, 64)
+    for name in a:
+        np.testing.assert_array_equal(a[name], b[name])
+
+
+def test_bwd_config2_sampled_units(g):
+    """Full headline size (B=8, T=4096, H=16, d=128, bf16); the oracle
+    recomputes the gradients of two (batch, head) units end to end."""
+    c = gi.CONFIGS[2]
+    inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], s0=c["s0"])
+    grads = gi.make_bwd_grads(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"])
+    print("case config2 backward", flush=True)
+    got = gpu_bwd(g, inp, grads, 64)
+    for name in got:
+        assert np.isfinite(got[name]).all(), name
+    for (bb, hh) in ((0, 0), (6, 11)):
+        sub = {x: inp[x][bb:bb + 1, :, hh:hh + 1].contiguous() for x in NAMES}
+        S0 = None if inp["S0"] is None else inp["S0"][bb:bb + 1, hh:hh + 1].contiguous()
+        ref = oracle.bwd(*(sub[x] for x in NAMES), grads["dout"][bb:bb + 1, :, hh:hh + 1].contiguous(),
+                         S0=S0, dS_final=grads["dS_final"][bb:bb + 1, hh:hh + 1].contiguous())
+        sel = lambda name, x: x[bb:bb + 1, hh:hh + 1] if name == "dS0" else x[bb:bb + 1, :, hh:hh + 1]
+        check(got, ref, TOL["bf16"], f"cfg2 b={bb} h={hh}", sel=sel)
