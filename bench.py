@@ -18,6 +18,8 @@ In the same run (reported next to the headline, not in `value`):
     the 256 MB last-level cache);
   * the same layer as KDA (b = w = beta per token and head) and as Gated
     DeltaNet (also a per-(token, head) decay), and GDN-2's time over KDA's;
+  * the chunked backward (gdn2_chunk_bwd) on the same layer: its time per
+    step, per-kernel durations and the roofline of its dominant kernel;
   * the CPU oracle timed on a bounded sample of the same workload.
 Prints one JSON line.
 """
@@ -63,6 +65,24 @@ def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
         "chunk_fused": 6 * d * elem + d * elem,
         "chunk_prep": 6 * d * elem + 5 * d * elem + gam,
         "chunk_scan": 5 * d * elem + gam + d * elem,
+    }
+
+
+# Algorithmic HBM bytes per token and head of the backward's kernels (bf16
+# elements, float32 states of d*d per chunk):
+#   path         : read q, k, v, alpha, b, w and dL/do once, write six gradients
+#   chunk_states : read -W, Q', Kbar^T, Ut and gamma_C, write the entering state
+#   bwd_dstate   : read -W, Q', Kbar^T, gamma_C and dL/do, write the leaving-state gradient
+#   bwd_grad     : read the six inputs, dL/do, the state and its gradient, write six gradients
+def bwd_bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
+    gam = d * 4 / C
+    st = d * d * 4 / C
+    return {
+        "path": 7 * d * elem + 6 * d * elem,
+        "chunk_prep": 6 * d * elem + 5 * d * elem + gam,
+        "chunk_states": 4 * d * elem + gam + st,
+        "bwd_dstate": 4 * d * elem + gam + st,
+        "bwd_grad": 7 * d * elem + 2 * st + 6 * d * elem,
     }
 
 
@@ -296,6 +316,44 @@ def main() -> int:
                                   "GBps": round(step_bytes / (dkc_us * 1e-6) / 1e9, 1),
                                   "hbm_frac": round(step_bytes / (dkc_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         }
+
+        # the chunked backward of the same layer (dL/do ~ N(0,1), dL/dS_final = 0)
+        grads = gi.make_bwd_grads(B, T, H, d, d, "bf16", seed=2, with_dS=False)
+        dout = grads["dout"].cuda()
+        wsb = torch.empty(g.bwd_workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8,
+                          device="cuda")
+        gout = {n: torch.empty_like(dev[x]) for n, x in zip(("dq", "dk", "dv", "dalpha", "db", "dw"), NAMES)}
+        gout["dS0"] = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+
+        def bstep():
+            g.chunk_bwd(*(dev[x] for x in NAMES), dout, chunk=C, workspace=wsb, out=gout)
+
+        del ws
+        bstep()
+        torch.cuda.synchronize()
+        g.profile_enable(True)
+        g.profile_read(reset=True)
+        bsteps = max(3, args.steps // 5)
+        sec_b = timed_steps(bstep, bsteps, 2)
+        bprof = g.profile_read(reset=True)
+        g.profile_enable(False)
+        bkern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in bprof.items()}
+        bbyt = bwd_bytes_per_token_head(d, C)
+        bdom = max(bkern, key=lambda k: bkern[k]["avg_us"])
+        bach = bbyt[bdom] * tok_heads / (bkern[bdom]["avg_us"] * 1e-6) / 1e9
+        out["backward"] = {
+            "workload": "gdn2_chunk_bwd of the same layer: dq, dk, dv, dalpha, db, dw, dS0",
+            "steps": bsteps, "ms_per_step": round(sec_b * 1e3, 4),
+            "tokens_per_s": round(B * T / sec_b, 1),
+            "time_over_forward": round(sec_b / sec, 3),
+            "path_algorithmic_bytes": int(bbyt["path"] * tok_heads),
+            "path_hbm_frac": round(bbyt["path"] * tok_heads / sec_b / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels": bkern,
+            "roofline": {"bound": "hbm", "kernel": bdom, "achieved": round(bach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(bach / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": int(bbyt[bdom] * tok_heads)},
+        }
+        del wsb
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, H, args.cpu_budget)

@@ -222,20 +222,6 @@ int num_slots_for(int B, int T, int num_seqs, int chunk, bool packed) {
 }
 
 // ---------------------------------------------------------------- backward --
-size_t bwd_scratch_floats_rt(int d, int c) {
-#define GDN2_BS(D, C) \
-  if (d == D && c == C) \
-    return gdn2::bwd_scratch_floats<D, C>();
-  GDN2_BS(16, 16) GDN2_BS(32, 16) GDN2_BS(64, 16) GDN2_BS(128, 16)
-  GDN2_BS(16, 64) GDN2_BS(32, 64) GDN2_BS(64, 64) GDN2_BS(128, 64)
-#undef GDN2_BS
-  return 0;
-}
-
-// Workgroups of the gradient kernel (each with its own scratch slot): enough
-// to fill the chip, and never more than there are chunk-heads.
-int bwd_grad_wgs(long chunk_heads) { return static_cast<int>(chunk_heads < 512 ? chunk_heads : 512); }
-
 template <typename IO, int D, int C> hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, hipStream_t st) {
   hipError_t e = hipSuccess;
   gdn2::chunk_args &a = ba.f;
@@ -265,7 +251,7 @@ template <typename IO, int D, int C> hipError_t run_bwd(gdn2::bwd_args &ba, int 
     if (e != hipSuccess)
       return e;
   }
-  if (a.num_slots > 0 && ba.grad_wgs > 0) {
+  if (a.num_slots > 0) {
     prof_scope p("bwd_grad", st);
     e = gdn2::launch_bwd_grad<IO, D, C>(ba, st);
   }
@@ -289,11 +275,9 @@ hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, hipSt
 }
 
 // Byte layout of the backward's workspace: chunk table (packed input), the
-// forward's per-chunk blocks, entering states, leaving-state gradients, and
-// the gradient kernel's scratch slots.
+// forward's per-chunk blocks, entering states and leaving-state gradients.
 struct bwd_plan {
-  size_t table, blocks, states, dstates, scratch, total;
-  int wgs;
+  size_t table, blocks, states, dstates, total;
 };
 
 bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk, bool packed) {
@@ -304,9 +288,7 @@ bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk,
   p.blocks = slots * H * chunk_block_bytes_rt(dt, d, chunk);
   p.states = align256(slots * H * sq);
   p.dstates = p.states;
-  p.wgs = bwd_grad_wgs(static_cast<long>(slots) * H);
-  p.scratch = static_cast<size_t>(p.wgs) * bwd_scratch_floats_rt(d, chunk) * sizeof(float);
-  p.total = p.table + p.blocks + p.states + p.dstates + p.scratch;
+  p.total = p.table + p.blocks + p.states + p.dstates;
   return p;
 }
 
@@ -534,8 +516,6 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   a.blocks = ws + plan.table;
   a.states = reinterpret_cast<float *>(ws + plan.table + plan.blocks);
   ba.dstates = reinterpret_cast<float *>(ws + plan.table + plan.blocks + plan.states);
-  ba.scratch = reinterpret_cast<float *>(ws + plan.table + plan.blocks + plan.states + plan.dstates);
-  ba.grad_wgs = plan.wgs;
   ba.dout = dout;
   ba.dSf = dS_final;
   ba.dS0 = dS0;

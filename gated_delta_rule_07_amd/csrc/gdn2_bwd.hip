@@ -39,6 +39,56 @@
 
 namespace gdn2 {
 
+// acc (ColFrag) += a (RowFrag) * b (ColFrag), operands rounded to CT.  The
+// bfloat16 product is one 16x16x16 instruction accumulating in place.  The
+// float32 one is four 16x16x4 instructions; each starts from zero and the
+// four are summed on the vector ALU, so that no product reads another's
+// result as its accumulator (chained float32 accumulators whose destination
+// differs from their source were measured to read stale values here).
+template <typename CT> __device__ __forceinline__ void mm(f32x4 &acc, f32x4 a, f32x4 b) {
+  if constexpr (sizeof(CT) == 2) {
+    mma16(acc, frag<CT>::from(a), frag<CT>::from(b));
+  } else {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], z, 0, 0, 0);
+    const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], z, 0, 0, 0);
+    const f32x4 p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], z, 0, 0, 0);
+    const f32x4 p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], z, 0, 0, 0);
+    acc += (p0 + p1) + (p2 + p3);
+  }
+}
+
+// RowFrag <-> ColFrag of one tile, exactly (a float32 identity product)
+__device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane);
+
+// acc += a * b for fragments of the I/O type (the float32 form of mm)
+template <typename T> __device__ __forceinline__ void mm_io(f32x4 &acc, const frag<T> &a, const frag<T> &b) {
+  if constexpr (sizeof(T) == 2)
+    mma16(acc, a, b);
+  else
+    mm<float>(acc, a.v, b.v);
+}
+
+// The same for a fragment of the I/O type (one bfloat16 product, or the
+// float32 form above)
+template <typename T> __device__ __forceinline__ f32x4 transpose_io(const frag<T> &x, const frag<T> &eye, int lane) {
+  if constexpr (sizeof(T) == 2)
+    return transpose_frag(x, eye);
+  else
+    return transpose_f32(x.v, lane);
+}
+
+__device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  f32x4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    e[i] = (4 * g + i == c) ? 1.f : 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mm<float>(acc, x, e);
+  return acc;
+}
+
 // ------------------------------------------------------- reverse dH scan --
 // One workgroup per (sequence, head), one wave per 16-column slice of dH
 // (dk x 16 float32 in matrix-core accumulators).  Per chunk, from the last:
@@ -98,11 +148,11 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
       if (which == 0) {
         const int tt = r / NK, kk = r - tt * NK;
         const F x = F::ld_at(blk + L::KB + tile_off<IO, NB>(kk, tt, lane));
-        F::from(transpose_frag(x, eye)).st(sm + static_cast<size_t>(p) * TB, lane);
+        F::from(transpose_io(x, eye, lane)).st(sm + static_cast<size_t>(p) * TB, lane);
       } else {
         const int kk = r / NB, tt = r - kk * NB;
         const F x = F::ld_at(blk + (which == 1 ? L::QP : L::WN) + tile_off<IO, NK>(tt, kk, lane));
-        F::from(transpose_frag(x, eye)).st(sm + static_cast<size_t>(p) * TB, lane);
+        F::from(transpose_io(x, eye, lane)).st(sm + static_cast<size_t>(p) * TB, lane);
       }
     }
     for (int i = threadIdx.x; i < D; i += 64 * NW)
@@ -136,7 +186,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        mma16(x, F::ld(sm + static_cast<size_t>(tt * NK + kk) * TB, lane), dhf[kk]);
+        mm_io(x, F::ld(sm + static_cast<size_t>(tt * NK + kk) * TB, lane), dhf[kk]);
       xf[tt] = F::from(x);
     }
 #pragma unroll
@@ -145,8 +195,8 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
       dh[kk] *= gm;
 #pragma unroll
       for (int tt = 0; tt < NB; ++tt) {
-        mma16(dh[kk], F::ld(sm + static_cast<size_t>(NT + kk * NB + tt) * TB, lane), dof[tt]);
-        mma16(dh[kk], F::ld(sm + static_cast<size_t>(2 * NT + kk * NB + tt) * TB, lane), xf[tt]);
+        mm_io(dh[kk], F::ld(sm + static_cast<size_t>(NT + kk * NB + tt) * TB, lane), dof[tt]);
+        mm_io(dh[kk], F::ld(sm + static_cast<size_t>(2 * NT + kk * NB + tt) * TB, lane), xf[tt]);
       }
     }
     __syncthreads();
@@ -161,316 +211,431 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
 }
 
 // --------------------------------------------------- per-chunk gradients --
-// float32 scratch of one gradient workgroup: C x D matrices, then C x C.
-template <int D, int C> struct bwd_ws {
-  static constexpr int NB = C / 16;
-  static constexpr size_t MD = static_cast<size_t>(C) * D, MC = static_cast<size_t>(C) * C;
-  static constexpr size_t G = 0, DO = G + MD, QS = DO + MD, ES = QS + MD, KB = ES + MD, QR = KB + MD,
-                          ER = QR + MD, KR = ER + MD, Y = KR + NB * MD, Z = Y + MD, DZ = Z + MD,
-                          DY = DZ + MD, DQS = DY + MD, DES = DQS + MD, DKB = DES + MD, DQR = DKB + MD,
-                          DER = DQR + MD, DKR = DER + MD, T = DKR + NB * MD, P = T + MC, DA = P + MC,
-                          DP = DA + MC, FLOATS = DP + MC;
+// LDS of one gradient workgroup, in floats: row-major float32 matrices with
+// padded pitches PD = D + 4 and PC = C + 4.
+//   KT  : the scaled keys K~ (C x D)
+//   ST  : T (C x C);  SP: P (C x C)
+//   YZ  : Y, then Z, then the dK~ accumulators (fragment order)
+//   DOZ : A (until T is done), then dO, then dZ (sized for both)
+template <int D, int C> struct bwd_lds {
+  static constexpr int NB = C / 16, PD = D + 4, PC = C + 4;
+  // DOZ also holds A (C x C, pitch PC) early on, so it spans the larger of the two
+  static constexpr int DOZ_FLOATS = (C * PD > C * PC) ? C * PD : C * PC;
+  static constexpr int KT = 0, ST = KT + C * PD, SP = ST + C * PC, YZ = SP + C * PC, DOZ = YZ + C * PD,
+                       BTOT = DOZ + DOZ_FLOATS, GTOT = BTOT + NB * D, KBS = GTOT + NB * D, DGAM = KBS + NB * D,
+                       FLOATS = DGAM + D;
 };
 
-template <int D, int C> size_t bwd_scratch_floats() { return bwd_ws<D, C>::FLOATS; }
-
-// One 16 x 16 tile of op(A) op(B) over k in [k0, k1) (multiples of 16), all
-// operands float32 row-major in memory, the product in the matrix-core type
-// CT.  !TA: A[m][k] at A + m lda + k; TA: A is stored transposed, A[m][k] at
-// A + k lda + m.  !TB: B[k][n] at B + k ldb + n; TB: B[k][n] at B + n ldb + k.
-// Returns ColFrag(out tile): lane (c, g) holds rows m0 + 4g + i, column n0 + c.
-template <typename CT, bool TA, bool TB>
-__device__ __forceinline__ f32x4 tile_mm(const float *__restrict__ A, int lda, const float *__restrict__ B,
-                                         int ldb, int m0, int n0, int k0, int k1, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k = k0; k < k1; k += 16) {
-    f32x4 av, bv;
-    if constexpr (!TA) {
-      av = *reinterpret_cast<const f32x4 *>(A + static_cast<size_t>(m0 + r) * lda + k + 4 * g);
-    } else {
+// Fragments of a 16 x 16 tile at (r0, c0) of a row-major float32 matrix with
+// row pitch `pitch` (LDS or global): RowFrag (lane (m, g) holds row r0 + m,
+// columns c0 + 4g .. +3) and ColFrag (lane (c, g) holds rows r0 + 4g .. +3 of
+// column c0 + c).
+__device__ __forceinline__ f32x4 ld_rowf(const float *M, int pitch, int r0, int c0, int lane) {
+  return *reinterpret_cast<const f32x4 *>(M + static_cast<size_t>(r0 + (lane & 15)) * pitch + c0 + 4 * (lane >> 4));
+}
+__device__ __forceinline__ f32x4 ld_colf(const float *M, int pitch, int r0, int c0, int lane) {
+  const float *p = M + static_cast<size_t>(r0 + 4 * (lane >> 4)) * pitch + c0 + (lane & 15);
+  f32x4 x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[i] = A[static_cast<size_t>(k + 4 * g + i) * lda + m0 + r];
-    }
-    if constexpr (!TB) {
+  for (int i = 0; i < 4; ++i)
+    x[i] = p[static_cast<size_t>(i) * pitch];
+  return x;
+}
+__device__ __forceinline__ void st_rowf(float *M, int pitch, int r0, int c0, int lane, f32x4 x) {
+  *reinterpret_cast<f32x4 *>(M + static_cast<size_t>(r0 + (lane & 15)) * pitch + c0 + 4 * (lane >> 4)) = x;
+}
+__device__ __forceinline__ void st_colf(float *M, int pitch, int r0, int c0, int lane, f32x4 x) {
+  float *p = M + static_cast<size_t>(r0 + 4 * (lane >> 4)) * pitch + c0 + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bv[i] = B[static_cast<size_t>(k + 4 * g + i) * ldb + n0 + r];
-    } else {
-      bv = *reinterpret_cast<const f32x4 *>(B + static_cast<size_t>(n0 + r) * ldb + k + 4 * g);
-    }
-    mma16(acc, frag<CT>::from(av), frag<CT>::from(bv));
-  }
-  return acc;
+  for (int i = 0; i < 4; ++i)
+    p[static_cast<size_t>(i) * pitch] = x[i];
 }
 
-// Stores a ColFrag tile to a row-major float32 matrix.
-__device__ __forceinline__ void tile_st(float *__restrict__ out, int ld, int m0, int n0, int lane, f32x4 v) {
+// Keeps the lower triangle of a diagonal tile: ColFrag element (row 4g+i,
+// column c) or RowFrag element (row m, column 4g+i); strict drops the diagonal.
+__device__ __forceinline__ f32x4 tri_col(f32x4 v, int lane, bool strict) {
   const int c = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    out[static_cast<size_t>(m0 + 4 * g + i) * ld + n0 + c] = v[i];
-}
-
-// Lower-triangular masks of a diagonal-block tile (row 4g+i, column c).
-__device__ __forceinline__ f32x4 mask_lower(f32x4 v, int lane, bool strict) {
-  const int c = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;
-    if (strict ? (r <= c) : (r < c))
+    if (strict ? (4 * g + i <= c) : (4 * g + i < c))
       v[i] = 0.f;
-  }
+  return v;
+}
+__device__ __forceinline__ f32x4 tri_row(f32x4 v, int lane, bool strict) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (strict ? (r <= 4 * g + i) : (r < 4 * g + i))
+      v[i] = 0.f;
   return v;
 }
 
-// Persistent grid: workgroup w takes chunk-heads w, w + grid, ... and uses
-// scratch slot w.  Four waves; products are split over the waves by output
-// tile, with a workgroup barrier between dependent phases (all waves of a
-// workgroup share one compute unit and its caches, so the scratch written in
-// one phase is visible to every wave after the barrier).
+// One workgroup per chunk-head, one wave per 16-token sub-block: wave I keeps
+// the rows of sub-block I (q, k, e, g, dO, Z, dY and the gradient
+// accumulators) as RowFrag slabs in registers and computes every product
+// whose result lives on those rows.  A product X_I M with X_I its own rows is
+// taken as M^T X_I^T (operands swapped), which leaves the result in the same
+// RowFrag layout.  What other waves need goes through LDS.  Decay factors
+// e^{g_t - g_s} are split at rho_J, the cumulative log decay at the end of
+// the key's sub-block J: K~_s = k_s e^{rho_J - g_s} <= 1 is stored once per
+// row, and the query/erase side of row t takes e^{g_t - rho_J} (<= 1 for
+// J < I, bounded by one sub-block's decay for J = I).
 template <typename IO, int D, int C, typename CT>
-__global__ void __launch_bounds__(256) gdn2_bwd_grad_kernel(bwd_args ba) {
+__global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args ba) {
   const chunk_args &a = ba.f;
-  typedef bwd_ws<D, C> W;
-  constexpr int NB = C / 16, NK = D / 16, NWV = 4;
-  __shared__ float rho[NB][D];
-  __shared__ float gcs[D];
-  __shared__ float sA[C][C + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float *ws = ba.scratch + static_cast<size_t>(blockIdx.x) * W::FLOATS;
-  const IO *q = static_cast<const IO *>(a.q), *k = static_cast<const IO *>(a.k);
-  const IO *v = static_cast<const IO *>(a.v), *al = static_cast<const IO *>(a.al);
-  const IO *b = static_cast<const IO *>(a.b), *w = static_cast<const IO *>(a.w);
-  const IO *dout = static_cast<const IO *>(ba.dout);
-  const long total = static_cast<long>(a.num_slots) * a.H;
+  typedef bwd_lds<D, C> L;
+  constexpr int NB = C / 16, NK = D / 16, PD = L::PD, PC = L::PC;
+  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
+  float *KT = sm + L::KT, *sT = sm + L::ST, *sP = sm + L::SP, *YZ = sm + L::YZ, *DOZ = sm + L::DOZ;
+  float *btot = sm + L::BTOT, *gtot = sm + L::GTOT, *kbs = sm + L::KBS, *dgam = sm + L::DGAM;
+  float *sA = DOZ;
 
-  for (long chh = blockIdx.x; chh < total; chh += gridDim.x) {
-    const int slot = static_cast<int>(chh / a.H), h = static_cast<int>(chh - static_cast<long>(slot) * a.H);
-    int seq, len;
-    long t0;
-    if (!locate_chunk<C>(slot, a, seq, t0, len))
-      continue;  // the whole workgroup
-    (void)seq;
-    const float *S = a.states + (static_cast<size_t>(slot) * a.H + h) * D * D;
-    const float *dH = ba.dstates + (static_cast<size_t>(slot) * a.H + h) * D * D;
-    auto rowi = [&](int t) { return (static_cast<size_t>(t0 + t) * a.H + h) * D; };
-
-    // ---- phase 0: cumulative log decay per channel, masked dO
-    if (tid < D) {
-      float gs = 0.f;
-      for (int t = 0; t < C; ++t) {
-        if ((t & 15) == 0)
-          rho[t >> 4][tid] = gs;
-        if (t < len)
-          gs += __logf(io<IO>::to_f(al[rowi(t) + tid]));
-        ws[W::G + t * D + tid] = gs;
-      }
-      gcs[tid] = gs;
-    }
-    for (int e = tid; e < C * D; e += 256) {
-      const int t = e / D, j = e - t * D;
-      ws[W::DO + e] = t < len ? io<IO>::to_f(dout[rowi(t) + j]) : 0.f;
-    }
-    __syncthreads();
-    // scaled copies
-    for (int e = tid; e < C * D; e += 256) {
-      const int t = e / D, i = e - t * D, I = t >> 4;
-      float qv = 0.f, kv = 0.f, bv = 0.f;
-      if (t < len) {
-        qv = io<IO>::to_f(q[rowi(t) + i]);
-        kv = io<IO>::to_f(k[rowi(t) + i]);
-        bv = io<IO>::to_f(b[rowi(t) + i]);
-      }
-      const float gt = ws[W::G + e];
-      const float eg = __expf(gt), er = __expf(gt - rho[I][i]);
-      ws[W::QS + e] = qv * eg;
-      ws[W::ES + e] = bv * kv * eg;
-      ws[W::KB + e] = kv * __expf(gcs[i] - gt);
-      ws[W::QR + e] = qv * er;
-      ws[W::ER + e] = bv * kv * er;
+  const int slot = static_cast<int>(blockIdx.x / a.H), h = static_cast<int>(blockIdx.x - slot * a.H);
+  int seq, len;
+  long t0;
+  if (!locate_chunk<C>(slot, a, seq, t0, len))
+    return;  // the whole workgroup
+  (void)seq;
+  const int I = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const int t = 16 * I + m;
+  const bool valid = t < len;
+  const size_t row = (static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h) * D;
+  const float *__restrict__ S = a.states + (static_cast<size_t>(slot) * a.H + h) * D * D;
+  const float *__restrict__ dH = ba.dstates + (static_cast<size_t>(slot) * a.H + h) * D * D;
+  const IO *__restrict__ q = static_cast<const IO *>(a.q);
+  const IO *__restrict__ k = static_cast<const IO *>(a.k);
+  const IO *__restrict__ v = static_cast<const IO *>(a.v);
+  const IO *__restrict__ al = static_cast<const IO *>(a.al);
+  const IO *__restrict__ b = static_cast<const IO *>(a.b);
+  const IO *__restrict__ w = static_cast<const IO *>(a.w);
+  const IO *__restrict__ dout = static_cast<const IO *>(ba.dout);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // cumulative log decay at the end of sub-block J, for this lane's RowFrag columns of tile kk
+  auto rho_end = [&](int J, int kk) {
+    f32x4 r = zero4;
+    for (int J2 = 0; J2 <= J; ++J2)
+      r += *reinterpret_cast<const f32x4 *>(btot + J2 * D + 16 * kk + 4 * g);
+    return r;
+  };
+  auto ex4 = [](f32x4 x) {
+    f32x4 y;
 #pragma unroll
-      for (int I2 = 0; I2 < NB; ++I2)
-        ws[W::KR + I2 * W::MD + e] = I2 >= I ? kv * __expf(rho[I2][i] - gt) : 0.f;
+    for (int i = 0; i < 4; ++i)
+      y[i] = __expf(x[i]);
+    return y;
+  };
+
+  // ---- rows of the sub-block; g = cumulative ln(alpha) within the chunk
+  f32x4 qv[NK], kv[NK], ev[NK], gv[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const int c0 = 16 * kk + 4 * g;
+    f32x4 qq = io<IO>::load4(q + row + c0), kq = io<IO>::load4(k + row + c0);
+    f32x4 bq = io<IO>::load4(b + row + c0), aq = io<IO>::load4(al + row + c0);
+    if (!valid) {
+      qq = kq = bq = zero4;
+      aq = f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+    qv[kk] = qq;
+    kv[kk] = kq;
+    ev[kk] = bq * kq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      gv[kk][i] = row16_inclusive_scan(__logf(aq[i]));
+  }
+  if (m == 15) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      *reinterpret_cast<f32x4 *>(btot + I * D + 16 * kk + 4 * g) = gv[kk];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    if (I > 0)
+      gv[kk] += rho_end(I - 1, kk);
+
+  // ---- K~ rows to LDS, then A and P tiles (I, J <= I)
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    st_rowf(KT, PD, 16 * I, 16 * kk, lane, kv[kk] * ex4(rho_end(I, kk) - gv[kk]));
+  __syncthreads();
+  for (int J = 0; J <= I; ++J) {
+    f32x4 aa = zero4, pp = zero4;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
+      const f32x4 kt = ld_rowf(KT, PD, 16 * J, 16 * kk, lane);
+      mm<CT>(aa, ev[kk] * sc, kt);
+      mm<CT>(pp, qv[kk] * sc, kt);
+    }
+    if (J == I) {
+      aa = tri_col(aa, lane, true);
+      pp = tri_col(pp, lane, false);
+    }
+    st_colf(sA, PC, 16 * I, 16 * J, lane, aa);
+    st_colf(sP, PC, 16 * I, 16 * J, lane, pp);
+  }
+  __syncthreads();
+
+  // ---- diagonal blocks of T = (I + A)^{-1} (lane c < 16: column c), Y_I = U_I - ES_I S
+  if (lane < 16) {
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < r; ++s2)
+        acc -= sA[(16 * I + r) * PC + 16 * I + s2] * x[s2];
+      x[r] = acc;
+      sT[(16 * I + r) * PC + 16 * I + lane] = acc;
+    }
+  }
+  f32x4 zv[NK];  // Y, then Z
+  {
+    f32x4 es[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      es[kk] = ev[kk] * ex4(gv[kk]);
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      f32x4 acc = zero4;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        mm<CT>(acc, ld_colf(S, D, 16 * kk, 16 * n, lane), es[kk]);
+      f32x4 u = io<IO>::load4(w + row + 16 * n + 4 * g) * io<IO>::load4(v + row + 16 * n + 4 * g);
+      zv[n] = (valid ? u : zero4) - acc;
+      st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
+    }
+  }
+  __syncthreads();
+  // off-diagonal blocks of T, one block diagonal per round:
+  // T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
+  for (int d = 1; d < NB; ++d) {
+    if (I >= d) {
+      const int J = I - d;
+      f32x4 mk = zero4;
+      for (int K = J; K < I; ++K)
+        mm<float>(mk, ld_rowf(sA, PC, 16 * I, 16 * K, lane), ld_colf(sT, PC, 16 * K, 16 * J, lane));
+      f32x4 tij = zero4;
+      mm<float>(tij, ld_rowf(sT, PC, 16 * I, 16 * I, lane), mk);
+      st_colf(sT, PC, 16 * I, 16 * J, lane, -tij);
     }
     __syncthreads();
+  }
 
-    // ---- phase 1: A (to LDS) and P, block row I with the keys of KR_I
-    for (int p = wave; p < 2 * NB * NB; p += NWV) {
-      const int which = p / (NB * NB), r = p - which * (NB * NB), I = r / NB, J = r - I * NB;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+  // ---- Z_I = sum_{J <= I} T_IJ Y_J
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    f32x4 acc = zero4;
+    for (int J = 0; J <= I; ++J)
+      mm<CT>(acc, ld_colf(YZ, PD, 16 * J, 16 * n, lane), ld_rowf(sT, PC, 16 * I, 16 * J, lane));
+    zv[n] = acc;
+  }
+  f32x4 dov[NK];
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    const f32x4 x = io<IO>::load4(dout + row + 16 * n + 4 * g);
+    dov[n] = valid ? x : zero4;
+  }
+  __syncthreads();  // Y and A are no longer read
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
+    st_rowf(DOZ, PD, 16 * I, 16 * n, lane, dov[n]);
+  }
+  __syncthreads();
+
+  // ---- dZ_I = sum_{J >= I} P_JI^T dO_J + KB_I dH
+  f32x4 dyv[NK];  // dZ, then dY
+  {
+    f32x4 kb[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      kb[kk] = kv[kk] * ex4(rho_end(NB - 1, kk) - gv[kk]);
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      f32x4 acc = zero4;
+      for (int J = I; J < NB; ++J)
+        mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sP, PC, 16 * J, 16 * I, lane));
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        mm<CT>(acc, ld_colf(dH, D, 16 * kk, 16 * n, lane), kb[kk]);
+      dyv[n] = acc;
+    }
+  }
+  __syncthreads();  // dO of the other sub-blocks is no longer read
+#pragma unroll
+  for (int n = 0; n < NK; ++n)
+    st_rowf(DOZ, PD, 16 * I, 16 * n, lane, dyv[n]);
+  __syncthreads();
+  // dY_I = sum_{J >= I} T_JI^T dZ_J;  dv = dY (.) w, dw = dY (.) v
+  IO *dq = static_cast<IO *>(ba.dq), *dk = static_cast<IO *>(ba.dk), *db = static_cast<IO *>(ba.db);
+  IO *dal = static_cast<IO *>(ba.dal), *dvo = static_cast<IO *>(ba.dv), *dwo = static_cast<IO *>(ba.dw);
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    f32x4 acc = zero4;
+    for (int J = I; J < NB; ++J)
+      mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sT, PC, 16 * J, 16 * I, lane));
+    dyv[n] = acc;
+    if (valid) {
+      io<IO>::store4(dvo + row + 16 * n + 4 * g, acc * io<IO>::load4(w + row + 16 * n + 4 * g));
+      io<IO>::store4(dwo + row + 16 * n + 4 * g, acc * io<IO>::load4(v + row + 16 * n + 4 * g));
+    }
+  }
+
+  // ---- dA_IJ = -dY_I Z_J^T, dP_IJ = dO_I Z_J^T (J <= I), as ColFrag (c) and RowFrag (r)
+  f32x4 dAc[NB], dAr[NB], dPc[NB], dPr[NB];
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    dAc[J] = dAr[J] = dPc[J] = dPr[J] = zero4;
+    if (J <= I) {
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        const f32x4 zr = ld_rowf(YZ, PD, 16 * J, 16 * n, lane);
+        mm<CT>(dAc[J], dyv[n], zr);
+        mm<CT>(dAr[J], zr, dyv[n]);
+        mm<CT>(dPc[J], dov[n], zr);
+        mm<CT>(dPr[J], zr, dov[n]);
+      }
+      dAc[J] = -dAc[J];
+      dAr[J] = -dAr[J];
+      if (J == I) {
+        dAc[J] = tri_col(dAc[J], lane, true);
+        dPc[J] = tri_col(dPc[J], lane, false);
+        dAr[J] = tri_row(dAr[J], lane, true);
+        dPr[J] = tri_row(dPr[J], lane, false);
+      }
+    }
+  }
+
+  // ---- contributions to dq (cq), de (ce), dk (ck) and d g_C (kb term)
+  f32x4 cq[NK], ce[NK], ck[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    f32x4 a1 = zero4, a2 = zero4, a3 = zero4;
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      const f32x4 sr = ld_rowf(S, D, 16 * kk, 16 * n, lane);
+      mm<CT>(a1, sr, dov[n]);
+      mm<CT>(a2, sr, dyv[n]);
+      mm<CT>(a3, ld_rowf(dH, D, 16 * kk, 16 * n, lane), zv[n]);
+    }
+    const f32x4 eg = ex4(gv[kk]);
+    cq[kk] = a1 * eg;
+    ce[kk] = -(a2 * eg);
+    ck[kk] = a3 * ex4(rho_end(NB - 1, kk) - gv[kk]);  // dKB e^{g_C - g}
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
       if (J <= I) {
-        x = tile_mm<CT, false, true>(ws + (which ? W::QR : W::ER), D, ws + W::KR + I * W::MD, D, 16 * I,
-                                     16 * J, 0, D, lane);
-        if (J == I)
-          x = mask_lower(x, lane, which == 0);
+        const f32x4 ktc = ld_colf(KT, PD, 16 * J, 16 * kk, lane);
+        f32x4 aq = zero4, ae = zero4;
+        mm<CT>(aq, ktc, dPr[J]);
+        mm<CT>(ae, ktc, dAr[J]);
+        const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
+        cq[kk] += aq * sc;
+        ce[kk] += ae * sc;
       }
-      if (which == 0) {
-        const int c = lane & 15, g = lane >> 4;
+    }
+  }
+
+  // ---- dK~_J contributions of this sub-block's rows, accumulated in LDS in a
+  // fixed order (own rows first, then one block diagonal per round)
+  f32x4 qrc[NK], erc[NK];  // ColFrag of q e^{g - rho_I} and e e^{g - rho_I}
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sA[16 * I + 4 * g + i][16 * J + c] = x[i];
-      } else {
-        tile_st(ws + W::P, C, 16 * I, 16 * J, lane, x);
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 2: T = (I + A)^{-1} by forward substitution (wave 0, lane =
-    // column); Y = U - ES S (the other waves)
-    if (wave == 0) {
-      if (lane < C) {
-        float x[C];
+  for (int kk = 0; kk < NK; ++kk) {
+    const f32x4 sc = ex4(gv[kk] - rho_end(I, kk));
+    qrc[kk] = transpose_f32(qv[kk] * sc, lane);
+    erc[kk] = transpose_f32(ev[kk] * sc, lane);
+  }
+  // column scale e^{rho_I - rho_J} of ColFrag element (lane column c)
+  auto colscale = [&](int J, int kk) {
+    float r = 0.f;
+    for (int J2 = J + 1; J2 <= I; ++J2)
+      r += btot[J2 * D + 16 * kk + m];
+    return __expf(r);
+  };
+  __syncthreads();  // Z in YZ is no longer read
+  float *dKacc = YZ;
+  for (int d = 0; d < NB; ++d) {
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-          float acc = (r == lane) ? 1.f : 0.f;
+    for (int J = 0; J < NB; ++J) {
+      if (I - J == d) {
 #pragma unroll
-          for (int s2 = 0; s2 < r; ++s2)
-            acc -= sA[r][s2] * x[s2];
-          x[r] = acc;
-          ws[W::T + r * C + lane] = acc;
+        for (int kk = 0; kk < NK; ++kk) {
+          const float f = colscale(J, kk);
+          f32x4 acc = zero4;
+          mm<CT>(acc, qrc[kk] * f, dPc[J]);
+          mm<CT>(acc, erc[kk] * f, dAc[J]);
+          f32x4 *p = reinterpret_cast<f32x4 *>(dKacc) + (J * NK + kk) * 64 + lane;
+          *p = (d == 0) ? acc : (*p + acc);
         }
       }
-    } else {
-      for (int p = wave - 1; p < NB * NK; p += NWV - 1) {
-        const int tt = p / NK, j = p - tt * NK;
-        const f32x4 x = tile_mm<CT, false, false>(ws + W::ES, D, S, D, 16 * tt, 16 * j, 0, D, lane);
-        const int c = lane & 15, g = lane >> 4;
-        f32x4 y;
+    }
+    __syncthreads();
+  }
+
+  // ---- map to the inputs
+  // d gamma_C = rowsum(dH (.) S), one channel per thread
+  for (int i = threadIdx.x; i < D; i += 64 * NB) {
+    float s = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < D; j += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(dH + static_cast<size_t>(i) * D + j);
+      const f32x4 y = *reinterpret_cast<const f32x4 *>(S + static_cast<size_t>(i) * D + j);
+      s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+    }
+    dgam[i] = s;
+  }
+  f32x4 dg[NK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * tt + 4 * g + i, col = 16 * j + c;
-          const float u = t < len ? io<IO>::to_f(w[rowi(t) + col]) * io<IO>::to_f(v[rowi(t) + col]) : 0.f;
-          y[i] = u - x[i];
-        }
-        tile_st(ws + W::Y, D, 16 * tt, 16 * j, lane, y);
-      }
+  for (int kk = 0; kk < NK; ++kk) {
+    const f32x4 dkt = reinterpret_cast<const f32x4 *>(dKacc)[(I * NK + kk) * 64 + lane];
+    const f32x4 ckt = dkt * ex4(rho_end(I, kk) - gv[kk]);
+    const int c0 = 16 * kk + 4 * g;
+    const f32x4 bq = valid ? io<IO>::load4(b + row + c0) : zero4;
+    const f32x4 kbt = kv[kk] * ck[kk];  // k (.) dKB-contribution, part of d g_C
+    dg[kk] = qv[kk] * cq[kk] + ev[kk] * ce[kk] - kv[kk] * (ck[kk] + ckt);
+    if (valid) {
+      io<IO>::store4(dq + row + c0, cq[kk]);
+      io<IO>::store4(dk + row + c0, ck[kk] + ckt + bq * ce[kk]);
+      io<IO>::store4(db + row + c0, kv[kk] * ce[kk]);
     }
-    __syncthreads();
-
-    // ---- phase 3: Z = T Y;  dZ = P^T dO + KB dH
-    for (int p = wave; p < 2 * NB * NK; p += NWV) {
-      const int which = p / (NB * NK), r = p - which * (NB * NK), tt = r / NK, j = r - tt * NK;
-      if (which == 0) {
-        const f32x4 x = tile_mm<CT, false, false>(ws + W::T, C, ws + W::Y, D, 16 * tt, 16 * j, 0, 16 * (tt + 1), lane);
-        tile_st(ws + W::Z, D, 16 * tt, 16 * j, lane, x);
-      } else {
-        f32x4 x = tile_mm<CT, true, false>(ws + W::P, C, ws + W::DO, D, 16 * tt, 16 * j, 16 * tt, C, lane);
-        x += tile_mm<CT, false, false>(ws + W::KB, D, dH, D, 16 * tt, 16 * j, 0, D, lane);
-        tile_st(ws + W::DZ, D, 16 * tt, 16 * j, lane, x);
+    // sub-block sums over the 16 rows: kb terms and dg
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ks = row16_inclusive_scan(kbt[i]);
+      const float gs = row16_inclusive_scan(dg[kk][i]);
+      if (m == 15) {
+        kbs[I * D + c0 + i] = ks;
+        gtot[I * D + c0 + i] = gs;
       }
+      dg[kk][i] = gs;  // in-block inclusive prefix of dg
     }
-    __syncthreads();
-
-    // ---- phase 4: dY = T^T dZ;  dP = lower(dO Z^T);  dQS = dO S^T;  dKB = Z dH^T
-    for (int p = wave; p < 3 * NB * NK + NB * NB; p += NWV) {
-      if (p < NB * NK) {
-        const int tt = p / NK, j = p - tt * NK;
-        const f32x4 x = tile_mm<CT, true, false>(ws + W::T, C, ws + W::DZ, D, 16 * tt, 16 * j, 16 * tt, C, lane);
-        tile_st(ws + W::DY, D, 16 * tt, 16 * j, lane, x);
-      } else if (p < 3 * NB * NK) {
-        const int r = p - NB * NK, which = r / (NB * NK), r2 = r - which * (NB * NK), tt = r2 / NK,
-                  kk = r2 - tt * NK;
-        const f32x4 x = which == 0
-                            ? tile_mm<CT, false, true>(ws + W::DO, D, S, D, 16 * tt, 16 * kk, 0, D, lane)
-                            : tile_mm<CT, false, true>(ws + W::Z, D, dH, D, 16 * tt, 16 * kk, 0, D, lane);
-        tile_st(ws + (which == 0 ? W::DQS : W::DKB), D, 16 * tt, 16 * kk, lane, x);
-      } else {
-        const int r = p - 3 * NB * NK, I = r / NB, J = r - I * NB;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (J <= I) {
-          x = tile_mm<CT, false, true>(ws + W::DO, D, ws + W::Z, D, 16 * I, 16 * J, 0, D, lane);
-          if (J == I)
-            x = mask_lower(x, lane, false);
-        }
-        tile_st(ws + W::DP, C, 16 * I, 16 * J, lane, x);
-      }
+  }
+  __syncthreads();
+  // d ln(alpha_t) = sum_{s >= t} dg_s + d g_C, d g_C = gamma dgamma + sum of the kb terms
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const int c0 = 16 * kk + 4 * g;
+    const f32x4 gc = rho_end(NB - 1, kk);
+    const f32x4 own = *reinterpret_cast<const f32x4 *>(gtot + I * D + c0);
+    f32x4 tail = zero4, kbsum = zero4;
+    for (int J = 0; J < NB; ++J) {
+      kbsum += *reinterpret_cast<const f32x4 *>(kbs + J * D + c0);
+      if (J > I)
+        tail += *reinterpret_cast<const f32x4 *>(gtot + J * D + c0);
     }
-    __syncthreads();
-
-    // ---- phase 5: dA = -strict-lower(dY Z^T);  dES = -dY S^T
-    for (int p = wave; p < NB * NB + NB * NK; p += NWV) {
-      if (p < NB * NB) {
-        const int I = p / NB, J = p - I * NB;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (J <= I) {
-          x = -tile_mm<CT, false, true>(ws + W::DY, D, ws + W::Z, D, 16 * I, 16 * J, 0, D, lane);
-          if (J == I)
-            x = mask_lower(x, lane, true);
-        }
-        tile_st(ws + W::DA, C, 16 * I, 16 * J, lane, x);
-      } else {
-        const int r = p - NB * NB, tt = r / NK, kk = r - tt * NK;
-        const f32x4 x = -tile_mm<CT, false, true>(ws + W::DY, D, S, D, 16 * tt, 16 * kk, 0, D, lane);
-        tile_st(ws + W::DES, D, 16 * tt, 16 * kk, lane, x);
-      }
+    const f32x4 dgc = ex4(gc) * *reinterpret_cast<const f32x4 *>(dgam + c0) + kbsum;
+    // suffix within the sub-block: total - inclusive prefix + own element
+    f32x4 mine;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float prev = __shfl_up(dg[kk][i], 1, 16);
+      mine[i] = dg[kk][i] - (m == 0 ? 0.f : prev);
     }
-    __syncthreads();
-
-    // ---- phase 6: dQR_I = dP_I KR_I, dER_I = dA_I KR_I (rows of sub-block I);
-    // dKR_I (rows of sub-blocks J <= I) = dP_IJ^T QR_I + dA_IJ^T ER_I
-    for (int p = wave; p < 2 * NB * NK + NB * NB * NK; p += NWV) {
-      if (p < 2 * NB * NK) {
-        const int which = p / (NB * NK), r = p - which * (NB * NK), I = r / NK, kk = r - I * NK;
-        const f32x4 x = tile_mm<CT, false, false>(ws + (which ? W::DA : W::DP), C, ws + W::KR + I * W::MD, D,
-                                                  16 * I, 16 * kk, 0, 16 * (I + 1), lane);
-        tile_st(ws + (which ? W::DER : W::DQR), D, 16 * I, 16 * kk, lane, x);
-      } else {
-        const int r = p - 2 * NB * NK, I = r / (NB * NK), r2 = r - I * (NB * NK), J = r2 / NK, kk = r2 - J * NK;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (J <= I) {
-          x = tile_mm<CT, true, false>(ws + W::DP, C, ws + W::QR, D, 16 * J, 16 * kk, 16 * I, 16 * I + 16, lane);
-          x += tile_mm<CT, true, false>(ws + W::DA, C, ws + W::ER, D, 16 * J, 16 * kk, 16 * I, 16 * I + 16, lane);
-        }
-        tile_st(ws + W::DKR + I * W::MD, D, 16 * J, 16 * kk, lane, x);
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 7: map to the inputs.  Thread i < D owns key channel i.
-    IO *dq = static_cast<IO *>(ba.dq), *dk = static_cast<IO *>(ba.dk), *db = static_cast<IO *>(ba.db);
-    IO *dal = static_cast<IO *>(ba.dal), *dv = static_cast<IO *>(ba.dv), *dw = static_cast<IO *>(ba.dw);
-    if (tid < D) {
-      const int i = tid;
-      float dgam = 0.f;
-      for (int j = 0; j < D; ++j)
-        dgam += dH[i * D + j] * S[i * D + j];
-      float dgc = __expf(gcs[i]) * dgam;  // d g_C: gamma dgamma + sum_s k (.) dKB-contribution
-      for (int t = 0; t < len; ++t) {
-        const size_t e = static_cast<size_t>(t) * D + i;
-        const int I = t >> 4;
-        const float qv = io<IO>::to_f(q[rowi(t) + i]), kv = io<IO>::to_f(k[rowi(t) + i]);
-        const float bv = io<IO>::to_f(b[rowi(t) + i]);
-        const float gt = ws[W::G + e];
-        const float eg = __expf(gt), er = __expf(gt - rho[I][i]);
-        const float cq = ws[W::DQS + e] * eg + ws[W::DQR + e] * er;
-        const float ce = ws[W::DES + e] * eg + ws[W::DER + e] * er;
-        const float ckb = ws[W::DKB + e] * __expf(gcs[i] - gt);
-        float ckr = 0.f;
-        for (int I2 = I; I2 < NB; ++I2)
-          ckr += ws[W::DKR + I2 * W::MD + e] * __expf(rho[I2][i] - gt);
-        dq[rowi(t) + i] = io<IO>::from_f(cq);
-        dk[rowi(t) + i] = io<IO>::from_f(ckb + ckr + bv * ce);
-        db[rowi(t) + i] = io<IO>::from_f(kv * ce);
-        dgc += kv * ckb;
-        ws[W::DQS + e] = qv * cq + bv * kv * ce - kv * (ckb + ckr);  // dg_t
-      }
-      float acc = dgc;
-      for (int t = len - 1; t >= 0; --t) {
-        const size_t e = static_cast<size_t>(t) * D + i;
-        acc += ws[W::DQS + e];
-        dal[rowi(t) + i] = io<IO>::from_f(acc / io<IO>::to_f(al[rowi(t) + i]));
-      }
-    }
-    for (int e = tid; e < len * D; e += 256) {
-      const int t = e / D, j = e - t * D;
-      const float dy = ws[W::DY + e];
-      dv[rowi(t) + j] = io<IO>::from_f(dy * io<IO>::to_f(w[rowi(t) + j]));
-      dw[rowi(t) + j] = io<IO>::from_f(dy * io<IO>::to_f(v[rowi(t) + j]));
-    }
-    __syncthreads();  // scratch and LDS are reused by the next chunk-head
+    const f32x4 dl = own - dg[kk] + mine + tail + dgc;
+    if (valid)
+      io<IO>::store4(dal + row + c0, dl / io<IO>::load4(al + row + c0));
   }
 }
 
@@ -481,22 +646,15 @@ template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args
 }
 
 template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st) {
-  hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, float>), dim3(a.grad_wgs), dim3(256), 0, st, a);
+  const long n = static_cast<long>(a.f.num_slots) * a.f.H;
+  hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO>), dim3(static_cast<unsigned>(n)), dim3(64 * (C / 16)),
+                     0, st, a);
   return hipGetLastError();
 }
 
 #define GDN2_INST_BWD(IO, D, C)                                                    \
   template hipError_t launch_bwd_dstate<IO, D, C>(const bwd_args &, hipStream_t); \
   template hipError_t launch_bwd_grad<IO, D, C>(const bwd_args &, hipStream_t);
-
-template size_t bwd_scratch_floats<16, 16>();
-template size_t bwd_scratch_floats<32, 16>();
-template size_t bwd_scratch_floats<64, 16>();
-template size_t bwd_scratch_floats<128, 16>();
-template size_t bwd_scratch_floats<16, 64>();
-template size_t bwd_scratch_floats<32, 64>();
-template size_t bwd_scratch_floats<64, 64>();
-template size_t bwd_scratch_floats<128, 64>();
 
 GDN2_INST_BWD(float, 16, 16)
 GDN2_INST_BWD(float, 32, 16)

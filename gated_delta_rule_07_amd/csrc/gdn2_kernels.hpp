@@ -53,12 +53,8 @@ struct bwd_args {
   float *dstates;        // dL/d(state leaving each chunk), [slot * H + h][dk][dv]
   float *dS0;            // dL/dS0 [N, H, dk, dv] or nullptr
   void *dq, *dk, *dv, *dal, *db, *dw;  // gradients, element type IO, input layouts
-  float *scratch;        // per-workgroup scratch of the gradient kernel
-  int grad_wgs;          // workgroups (scratch slots) of the gradient kernel
 };
 
-// float32 scratch elements per workgroup of the gradient kernel
-template <int D, int C> size_t bwd_scratch_floats();
 template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args &a, hipStream_t st);
 template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st);
 
