@@ -283,7 +283,8 @@ struct bwd_plan {
 bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk, bool packed) {
   bwd_plan p{};
   const size_t slots = static_cast<size_t>(num_slots_for(B, T, N, chunk, packed));
-  const size_t sq = static_cast<size_t>(d) * d * sizeof(float);
+  // a state as two sets of (d/16)^2 fragment tiles of the I/O type
+  const size_t sq = 2 * static_cast<size_t>(d) * d * (dt == GDN2_BF16 ? 2 : 4);
   p.table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
   p.blocks = slots * H * chunk_block_bytes_rt(dt, d, chunk);
   p.states = align256(slots * H * sq);
@@ -514,8 +515,8 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   char *ws = static_cast<char *>(workspace);
   a.offsets = packed ? reinterpret_cast<int32_t *>(ws) : nullptr;
   a.blocks = ws + plan.table;
-  a.states = reinterpret_cast<float *>(ws + plan.table + plan.blocks);
-  ba.dstates = reinterpret_cast<float *>(ws + plan.table + plan.blocks + plan.states);
+  a.states = ws + plan.table + plan.blocks;
+  ba.dstates = ws + plan.table + plan.blocks + plan.states;
   ba.dout = dout;
   ba.dSf = dS_final;
   ba.dS0 = dS0;

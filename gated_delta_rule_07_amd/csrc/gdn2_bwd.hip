@@ -39,63 +39,13 @@
 
 namespace gdn2 {
 
-// acc (ColFrag) += a (RowFrag) * b (ColFrag), operands rounded to CT.  The
-// bfloat16 product is one 16x16x16 instruction accumulating in place.  The
-// float32 one is four 16x16x4 instructions; each starts from zero and the
-// four are summed on the vector ALU, so that no product reads another's
-// result as its accumulator (chained float32 accumulators whose destination
-// differs from their source were measured to read stale values here).
-template <typename CT> __device__ __forceinline__ void mm(f32x4 &acc, f32x4 a, f32x4 b) {
-  if constexpr (sizeof(CT) == 2) {
-    mma16(acc, frag<CT>::from(a), frag<CT>::from(b));
-  } else {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], z, 0, 0, 0);
-    const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], z, 0, 0, 0);
-    const f32x4 p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], z, 0, 0, 0);
-    const f32x4 p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], z, 0, 0, 0);
-    acc += (p0 + p1) + (p2 + p3);
-  }
-}
-
-// RowFrag <-> ColFrag of one tile, exactly (a float32 identity product)
-__device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane);
-
-// acc += a * b for fragments of the I/O type (the float32 form of mm)
-template <typename T> __device__ __forceinline__ void mm_io(f32x4 &acc, const frag<T> &a, const frag<T> &b) {
-  if constexpr (sizeof(T) == 2)
-    mma16(acc, a, b);
-  else
-    mm<float>(acc, a.v, b.v);
-}
-
-// The same for a fragment of the I/O type (one bfloat16 product, or the
-// float32 form above)
-template <typename T> __device__ __forceinline__ f32x4 transpose_io(const frag<T> &x, const frag<T> &eye, int lane) {
-  if constexpr (sizeof(T) == 2)
-    return transpose_frag(x, eye);
-  else
-    return transpose_f32(x.v, lane);
-}
-
-__device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane) {
-  const int c = lane & 15, g = lane >> 4;
-  f32x4 e;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    e[i] = (4 * g + i == c) ? 1.f : 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  mm<float>(acc, x, e);
-  return acc;
-}
-
 // ------------------------------------------------------- reverse dH scan --
 // One workgroup per (sequence, head), one wave per 16-column slice of dH
 // (dk x 16 float32 in matrix-core accumulators).  Per chunk, from the last:
 // the waves re-lay the chunk's Kbar, Q'^T and -W^T tiles (stored by the prep
 // as RowFrag(Kbar^T), RowFrag(Q'), RowFrag(-W)) into LDS with one identity
 // product each, then every wave stores its slice of dH (the gradient of the
-// state leaving the chunk) and updates it.
+// state leaving the chunk, as state_tiles fragments) and updates it.
 template <typename IO, int D, int C>
 __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args ba) {
   const chunk_args &a = ba.f;
@@ -169,17 +119,16 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
       }
       dof[tt] = F::from(x);
     }
-    float *dp = ba.dstates + (slot * a.H + h) * D * D;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dp[(16 * kk + 4 * g + i) * D + 16 * j + m] = dh[kk][i];
-    __syncthreads();
+    typedef state_tiles<IO, D> ST_;
+    unsigned char *dp = reinterpret_cast<unsigned char *>(ba.dstates) + (slot * a.H + h) * ST_::BYTES;
     F dhf[NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      dhf[kk] = F::from(dh[kk]);
+    for (int kk = 0; kk < NK; ++kk) {
+      dhf[kk] = F::from(dh[kk]);  // ColFrag(dH tile (kk, j))
+      dhf[kk].st(dp + ST_::COL + ST_::off(kk, j), lane);
+      F::from(transpose_io(dhf[kk], eye, lane)).st(dp + ST_::ROW + ST_::off(kk, j), lane);
+    }
+    __syncthreads();
     F xf[NB];  // Kbar dH, ColFrag tiles (tt, j)
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
@@ -300,8 +249,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   const int t = 16 * I + m;
   const bool valid = t < len;
   const size_t row = (static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h) * D;
-  const float *__restrict__ S = a.states + (static_cast<size_t>(slot) * a.H + h) * D * D;
-  const float *__restrict__ dH = ba.dstates + (static_cast<size_t>(slot) * a.H + h) * D * D;
+  typedef frag<IO> F;
+  typedef state_tiles<IO, D> ST_;
+  // S and dH of this chunk as fragment tiles: ColFrag at ST_::COL, RowFrag at ST_::ROW
+  const unsigned char *__restrict__ St =
+      reinterpret_cast<const unsigned char *>(a.states) + (static_cast<size_t>(slot) * a.H + h) * ST_::BYTES;
+  const unsigned char *__restrict__ Ht =
+      reinterpret_cast<const unsigned char *>(ba.dstates) + (static_cast<size_t>(slot) * a.H + h) * ST_::BYTES;
   const IO *__restrict__ q = static_cast<const IO *>(a.q);
   const IO *__restrict__ k = static_cast<const IO *>(a.k);
   const IO *__restrict__ v = static_cast<const IO *>(a.v);
@@ -323,6 +277,17 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     for (int i = 0; i < 4; ++i)
       y[i] = __expf(x[i]);
     return y;
+  };
+
+  // q, k, b of this lane's row for tile kk (zero past the end); reloaded in
+  // the late phases rather than kept in registers through the kernel
+  auto rowvals = [&](int kk, f32x4 &qq, f32x4 &kq, f32x4 &bq) {
+    const int c0 = 16 * kk + 4 * g;
+    qq = io<IO>::load4(q + row + c0);
+    kq = io<IO>::load4(k + row + c0);
+    bq = io<IO>::load4(b + row + c0);
+    if (!valid)
+      qq = kq = bq = zero4;
   };
 
   // ---- rows of the sub-block; g = cumulative ln(alpha) within the chunk
@@ -392,16 +357,16 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   }
   f32x4 zv[NK];  // Y, then Z
   {
-    f32x4 es[NK];
+    F esf[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      es[kk] = ev[kk] * ex4(gv[kk]);
+      esf[kk] = F::from(ev[kk] * ex4(gv[kk]));
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
       f32x4 acc = zero4;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        mm<CT>(acc, ld_colf(S, D, 16 * kk, 16 * n, lane), es[kk]);
+        mm_io(acc, F::ld(St + ST_::COL + ST_::off(kk, n), lane), esf[kk]);
       f32x4 u = io<IO>::load4(w + row + 16 * n + 4 * g) * io<IO>::load4(v + row + 16 * n + 4 * g);
       zv[n] = (valid ? u : zero4) - acc;
       st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
@@ -448,10 +413,10 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   // ---- dZ_I = sum_{J >= I} P_JI^T dO_J + KB_I dH
   f32x4 dyv[NK];  // dZ, then dY
   {
-    f32x4 kb[NK];
+    F kbf[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      kb[kk] = kv[kk] * ex4(rho_end(NB - 1, kk) - gv[kk]);
+      kbf[kk] = F::from(kv[kk] * ex4(rho_end(NB - 1, kk) - gv[kk]));
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
       f32x4 acc = zero4;
@@ -459,7 +424,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
         mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sP, PC, 16 * J, 16 * I, lane));
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        mm<CT>(acc, ld_colf(dH, D, 16 * kk, 16 * n, lane), kb[kk]);
+        mm_io(acc, F::ld(Ht + ST_::COL + ST_::off(kk, n), lane), kbf[kk]);
       dyv[n] = acc;
     }
   }
@@ -510,15 +475,22 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 
   // ---- contributions to dq (cq), de (ce), dk (ck) and d g_C (kb term)
   f32x4 cq[NK], ce[NK], ck[NK];
+  F dof[NK], dyf[NK], zf[NK];
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    dof[n] = F::from(dov[n]);
+    dyf[n] = F::from(dyv[n]);
+    zf[n] = F::from(zv[n]);
+  }
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     f32x4 a1 = zero4, a2 = zero4, a3 = zero4;
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
-      const f32x4 sr = ld_rowf(S, D, 16 * kk, 16 * n, lane);
-      mm<CT>(a1, sr, dov[n]);
-      mm<CT>(a2, sr, dyv[n]);
-      mm<CT>(a3, ld_rowf(dH, D, 16 * kk, 16 * n, lane), zv[n]);
+      const F sr = F::ld(St + ST_::ROW + ST_::off(kk, n), lane);
+      mm_io(a1, sr, dof[n]);
+      mm_io(a2, sr, dyf[n]);
+      mm_io(a3, F::ld(Ht + ST_::ROW + ST_::off(kk, n), lane), zf[n]);
     }
     const f32x4 eg = ex4(gv[kk]);
     cq[kk] = a1 * eg;
@@ -543,9 +515,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   f32x4 qrc[NK], erc[NK];  // ColFrag of q e^{g - rho_I} and e e^{g - rho_I}
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
+    f32x4 qq, kq, bq;
+    rowvals(kk, qq, kq, bq);
     const f32x4 sc = ex4(gv[kk] - rho_end(I, kk));
-    qrc[kk] = transpose_f32(qv[kk] * sc, lane);
-    erc[kk] = transpose_f32(ev[kk] * sc, lane);
+    qrc[kk] = transpose_f32(qq * sc, lane);
+    erc[kk] = transpose_f32(bq * kq * sc, lane);
   }
   // column scale e^{rho_I - rho_J} of ColFrag element (lane column c)
   auto colscale = [&](int J, int kk) {
@@ -575,16 +549,25 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   }
 
   // ---- map to the inputs
-  // d gamma_C = rowsum(dH (.) S), one channel per thread
-  for (int i = threadIdx.x; i < D; i += 64 * NB) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < D; j += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(dH + static_cast<size_t>(i) * D + j);
-      const f32x4 y = *reinterpret_cast<const f32x4 *>(S + static_cast<size_t>(i) * D + j);
-      s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+  // d gamma_C = rowsum(dH (.) S): wave I takes row tiles kk = I, I + NB, ..;
+  // lane (c, g) of ColFrag tile (kk, n) holds rows 16kk + 4g .. +3 of column 16n + c
+  for (int kk = I; kk < NK; kk += NB) {
+    f32x4 acc = zero4;
+#pragma unroll
+    for (int n = 0; n < NK; ++n)
+      acc += F::ld(St + ST_::COL + ST_::off(kk, n), lane).to_f32() *
+             F::ld(Ht + ST_::COL + ST_::off(kk, n), lane).to_f32();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = acc[i];
+      x += __shfl_xor(x, 1, 16);
+      x += __shfl_xor(x, 2, 16);
+      x += __shfl_xor(x, 4, 16);
+      x += __shfl_xor(x, 8, 16);
+      acc[i] = x;
     }
-    dgam[i] = s;
+    if (m == 0)
+      *reinterpret_cast<f32x4 *>(dgam + 16 * kk + 4 * g) = acc;
   }
   f32x4 dg[NK];
 #pragma unroll
@@ -592,13 +575,14 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     const f32x4 dkt = reinterpret_cast<const f32x4 *>(dKacc)[(I * NK + kk) * 64 + lane];
     const f32x4 ckt = dkt * ex4(rho_end(I, kk) - gv[kk]);
     const int c0 = 16 * kk + 4 * g;
-    const f32x4 bq = valid ? io<IO>::load4(b + row + c0) : zero4;
-    const f32x4 kbt = kv[kk] * ck[kk];  // k (.) dKB-contribution, part of d g_C
-    dg[kk] = qv[kk] * cq[kk] + ev[kk] * ce[kk] - kv[kk] * (ck[kk] + ckt);
+    f32x4 qq, kq, bq;
+    rowvals(kk, qq, kq, bq);
+    const f32x4 kbt = kq * ck[kk];  // k (.) dKB-contribution, part of d g_C
+    dg[kk] = qq * cq[kk] + bq * kq * ce[kk] - kq * (ck[kk] + ckt);
     if (valid) {
       io<IO>::store4(dq + row + c0, cq[kk]);
       io<IO>::store4(dk + row + c0, ck[kk] + ckt + bq * ce[kk]);
-      io<IO>::store4(db + row + c0, kv[kk] * ce[kk]);
+      io<IO>::store4(db + row + c0, kq * ce[kk]);
     }
     // sub-block sums over the 16 rows: kb terms and dg
 #pragma unroll

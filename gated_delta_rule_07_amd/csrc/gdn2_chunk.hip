@@ -148,8 +148,8 @@ template <typename IO, int D, int C, int NT> struct scan_cfg {
 // consecutive ids go to the 8 XCDs round-robin and all workgroups of one head
 // share an XCD (and its L2).
 // With ST (states mode, used by the backward) the kernel writes, instead of
-// o, the float32 state entering every chunk to a.states (chunk slot order,
-// [slot * H + h][dk][dv]).
+// o, the state entering every chunk to a.states (chunk slot order, one
+// state_tiles block per chunk-head: fragment tiles of the I/O type).
 template <typename IO, int D, int C, int NT, bool ST = false>
 __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<IO, D, C, NT>::NLW))
     gdn2_chunk_scan_kernel(chunk_args a) {
@@ -324,14 +324,17 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
                         int len, int c, auto full) {
     constexpr bool FULL = decltype(full)::value;
     if constexpr (ST) {
-      float *sp = a.states + (static_cast<size_t>(c_begin + c) * a.H + h) * D * D;
+      typedef state_tiles<IO, D> ST_;
+      unsigned char *sp =
+          reinterpret_cast<unsigned char *>(a.states) + (static_cast<size_t>(c_begin + c) * a.H + h) * ST_::BYTES;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-        for (int j = 0; j < CPW; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sp[(16 * kk + 4 * g + i) * D + 16 * (vt0 + j) + m] = S[kk][j][i];
+        for (int j = 0; j < CPW; ++j) {
+          const F sc = F::from(S[kk][j]);  // ColFrag(S tile (kk, vt0 + j))
+          sc.st(sp + ST_::COL + ST_::off(kk, vt0 + j), lane);
+          F::from(transpose_io(sc, eye, lane)).st(sp + ST_::ROW + ST_::off(kk, vt0 + j), lane);
+        }
     }
     // o goes through a global-address-space pointer so that the compiler
     // knows these stores never alias the LDS operands it wants to hoist

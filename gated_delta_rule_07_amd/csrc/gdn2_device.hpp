@@ -264,6 +264,66 @@ __device__ __forceinline__ f32x4 transpose_frag(const frag<T> &x, const frag<T> 
   return acc;
 }
 
+// acc (ColFrag) += a (RowFrag) * b (ColFrag), operands rounded to CT.  The
+// bfloat16 product is one 16x16x16 instruction accumulating in place.  The
+// float32 one is four 16x16x4 instructions; each starts from zero and the
+// four are summed on the vector ALU, so that no product reads another's
+// result as its accumulator (chained float32 accumulators whose destination
+// differs from their source were measured to read stale values here).
+template <typename CT> __device__ __forceinline__ void mm(f32x4 &acc, f32x4 a, f32x4 b) {
+  if constexpr (sizeof(CT) == 2) {
+    mma16(acc, frag<CT>::from(a), frag<CT>::from(b));
+  } else {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], z, 0, 0, 0);
+    const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], z, 0, 0, 0);
+    const f32x4 p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], z, 0, 0, 0);
+    const f32x4 p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], z, 0, 0, 0);
+    acc += (p0 + p1) + (p2 + p3);
+  }
+}
+
+// RowFrag <-> ColFrag of one tile, exactly (a float32 identity product)
+__device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane);
+
+// acc += a * b for fragments of the I/O type (the float32 form of mm)
+template <typename T> __device__ __forceinline__ void mm_io(f32x4 &acc, const frag<T> &a, const frag<T> &b) {
+  if constexpr (sizeof(T) == 2)
+    mma16(acc, a, b);
+  else
+    mm<float>(acc, a.v, b.v);
+}
+
+// The same for a fragment of the I/O type (one bfloat16 product, or the
+// float32 form above)
+template <typename T> __device__ __forceinline__ f32x4 transpose_io(const frag<T> &x, const frag<T> &eye, int lane) {
+  if constexpr (sizeof(T) == 2)
+    return transpose_frag(x, eye);
+  else
+    return transpose_f32(x.v, lane);
+}
+
+__device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  f32x4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    e[i] = (4 * g + i == c) ? 1.f : 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mm<float>(acc, x, e);
+  return acc;
+}
+
+// A dk x dv float32 state handed between the backward's kernels as fragment
+// tiles of the I/O type: the NK x NK tiles (kk, n) (rows 16kk.., columns
+// 16n..) as ColFrag, then the same tiles as RowFrag.  BYTES per chunk-head.
+template <typename IO, int D> struct state_tiles {
+  static constexpr int NK = D / 16;
+  static constexpr size_t TB = frag<IO>::TILE_BYTES;
+  static constexpr size_t COL = 0, ROW = static_cast<size_t>(NK) * NK * TB, BYTES = 2 * ROW;
+  __host__ __device__ static constexpr size_t off(int kk, int n) { return static_cast<size_t>(kk * NK + n) * TB; }
+};
+
 // ------------------------------------------------------------- barriers --
 // Workgroup barrier that orders LDS accesses only: LDS writes issued before it
 // are complete and visible after it, but outstanding global loads and stores

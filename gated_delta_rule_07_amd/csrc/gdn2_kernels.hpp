@@ -25,7 +25,7 @@ struct chunk_args {
   char *blocks;      // num_slots * H blocks of blk_bytes each
   size_t blk_bytes;
   uint32_t gates;    // GATE_* bits: inputs given per (token, head) instead of per channel
-  float *states;     // backward only: state entering every chunk, [slot * H + h][dk][dv]
+  void *states;      // backward only: state entering every chunk (state_tiles blocks, slot * H + h)
 };
 
 // chunk_args::gates: b, w or alpha is one value per (token, head), laid out
@@ -50,7 +50,7 @@ struct bwd_args {
   chunk_args f;
   const void *dout;      // dL/do [B, T, H, dv], element type IO
   const float *dSf;      // dL/dS_final [N, H, dk, dv] or nullptr (zero)
-  float *dstates;        // dL/d(state leaving each chunk), [slot * H + h][dk][dv]
+  void *dstates;         // dL/d(state leaving each chunk), state_tiles blocks like states
   float *dS0;            // dL/dS0 [N, H, dk, dv] or nullptr
   void *dq, *dk, *dv, *dal, *db, *dw;  // gradients, element type IO, input layouts
 };
