@@ -88,37 +88,74 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
   const F eye = identity_colfrag<IO>(lane);
   const IO *dout = static_cast<const IO *>(ba.dout);
 
-  for (int c = nchunks - 1; c >= 0; --c) {
+  // software pipeline: chunk c - 1's operand tiles, gamma and dO are loaded
+  // into registers while chunk c is computed, and laid into LDS after it
+  constexpr int PPW = (3 * NT + NW - 1) / NW;  // tiles per wave
+  F raw[PPW], dof[NB];
+  IO dor[NB][4];  // raw dO elements of the next chunk (rows past its end: masked at commit)
+  int lenn = 0;
+  float gamv = 0.f;
+  auto issue = [&](int c) {
     const size_t slot = static_cast<size_t>(c_begin + c);
     const unsigned char *blk = reinterpret_cast<const unsigned char *>(a.blocks) + (slot * a.H + h) * a.blk_bytes;
     const long t0 = tstart + static_cast<long>(c) * C;
     const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
-    for (int p = wave; p < 3 * NT; p += NW) {
-      const int which = p / NT, r = p - which * NT;
-      if (which == 0) {
-        const int tt = r / NK, kk = r - tt * NK;
-        const F x = F::ld_at(blk + L::KB + tile_off<IO, NB>(kk, tt, lane));
-        F::from(transpose_io(x, eye, lane)).st(sm + static_cast<size_t>(p) * TB, lane);
-      } else {
-        const int kk = r / NB, tt = r - kk * NB;
-        const F x = F::ld_at(blk + (which == 1 ? L::QP : L::WN) + tile_off<IO, NK>(tt, kk, lane));
-        F::from(transpose_io(x, eye, lane)).st(sm + static_cast<size_t>(p) * TB, lane);
+#pragma unroll
+    for (int r = 0; r < PPW; ++r) {
+      const int p = wave + r * NW;
+      if (p < 3 * NT) {
+        const int which = p / NT, q2 = p - which * NT;
+        if (which == 0) {
+          const int tt = q2 / NK, kk = q2 - tt * NK;
+          raw[r] = F::ld_at(blk + L::KB + tile_off<IO, NB>(kk, tt, lane));
+        } else {
+          const int kk = q2 / NB, tt = q2 - kk * NB;
+          raw[r] = F::ld_at(blk + (which == 1 ? L::QP : L::WN) + tile_off<IO, NK>(tt, kk, lane));
+        }
       }
     }
-    for (int i = threadIdx.x; i < D; i += 64 * NW)
-      gam[i] = reinterpret_cast<const float *>(blk + L::GAM)[i];
-    // ColFrag(dO tile (tt, j)): rows 16 tt + 4 g + i, column 16 j + m
-    F dof[NB];
+    if (threadIdx.x < D)
+      gamv = reinterpret_cast<const float *>(blk + L::GAM)[threadIdx.x];
+    // ColFrag(dO tile (tt, j)): rows 16 tt + 4 g + i, column 16 j + m.
+    // Rows past the end read the chunk's first row (every load unconditional,
+    // so none waits for another); they are zeroed at commit.
+    lenn = len;
+    const IO *dbase = dout + (static_cast<size_t>(t0) * a.H + h) * D + 16 * j;  // uniform
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tt + 4 * g + i;
+        const unsigned off = static_cast<unsigned>((t < len ? t : 0) * a.H * D + m);
+        dor[tt][i] = dbase[off];
+      }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int r = 0; r < PPW; ++r) {
+      const int p = wave + r * NW;
+      if (p < 3 * NT)
+        F::from(transpose_io(raw[r], eye, lane)).st(sm + static_cast<size_t>(p) * TB, lane);
+    }
+    if (threadIdx.x < D)
+      gam[threadIdx.x] = gamv;
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
       f32x4 x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tt + 4 * g + i;
-        x[i] = t < len ? io<IO>::to_f(dout[(static_cast<size_t>(t0 + t) * a.H + h) * D + 16 * j + m]) : 0.f;
-      }
+      for (int i = 0; i < 4; ++i)
+        x[i] = (16 * tt + 4 * g + i < lenn) ? io<IO>::to_f(dor[tt][i]) : 0.f;
       dof[tt] = F::from(x);
     }
+  };
+  if (nchunks > 0) {
+    issue(nchunks - 1);
+    commit();
+  }
+  lds_barrier();
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const size_t slot = static_cast<size_t>(c_begin + c);
+    issue(c > 0 ? c - 1 : 0);  // on the last step a harmless re-read, so no branch
     typedef state_tiles<IO, D> ST_;
     unsigned char *dp = reinterpret_cast<unsigned char *>(ba.dstates) + (slot * a.H + h) * ST_::BYTES;
     F dhf[NK];
@@ -128,7 +165,6 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
       dhf[kk].st(dp + ST_::COL + ST_::off(kk, j), lane);
       F::from(transpose_io(dhf[kk], eye, lane)).st(dp + ST_::ROW + ST_::off(kk, j), lane);
     }
-    __syncthreads();
     F xf[NB];  // Kbar dH, ColFrag tiles (tt, j)
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
@@ -148,7 +184,10 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
         mm_io(dh[kk], F::ld(sm + static_cast<size_t>(2 * NT + kk * NB + tt) * TB, lane), xf[tt]);
       }
     }
-    __syncthreads();
+    lds_barrier();  // LDS of chunk c is no longer read
+    if (c > 0)
+      commit();
+    lds_barrier();  // chunk c - 1 is in LDS
   }
   if (ba.dS0) {
 #pragma unroll
@@ -313,7 +352,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     for (int kk = 0; kk < NK; ++kk)
       *reinterpret_cast<f32x4 *>(btot + I * D + 16 * kk + 4 * g) = gv[kk];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
     if (I > 0)
@@ -323,7 +362,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
     st_rowf(KT, PD, 16 * I, 16 * kk, lane, kv[kk] * ex4(rho_end(I, kk) - gv[kk]));
-  __syncthreads();
+  lds_barrier();
   for (int J = 0; J <= I; ++J) {
     f32x4 aa = zero4, pp = zero4;
 #pragma unroll
@@ -340,7 +379,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     st_colf(sA, PC, 16 * I, 16 * J, lane, aa);
     st_colf(sP, PC, 16 * I, 16 * J, lane, pp);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- diagonal blocks of T = (I + A)^{-1} (lane c < 16: column c), Y_I = U_I - ES_I S
   if (lane < 16) {
@@ -372,7 +411,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // off-diagonal blocks of T, one block diagonal per round:
   // T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
   for (int d = 1; d < NB; ++d) {
@@ -385,7 +424,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       mm<float>(tij, ld_rowf(sT, PC, 16 * I, 16 * I, lane), mk);
       st_colf(sT, PC, 16 * I, 16 * J, lane, -tij);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- Z_I = sum_{J <= I} T_IJ Y_J
@@ -402,13 +441,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     const f32x4 x = io<IO>::load4(dout + row + 16 * n + 4 * g);
     dov[n] = valid ? x : zero4;
   }
-  __syncthreads();  // Y and A are no longer read
+  lds_barrier();  // Y and A are no longer read
 #pragma unroll
   for (int n = 0; n < NK; ++n) {
     st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
     st_rowf(DOZ, PD, 16 * I, 16 * n, lane, dov[n]);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- dZ_I = sum_{J >= I} P_JI^T dO_J + KB_I dH
   f32x4 dyv[NK];  // dZ, then dY
@@ -428,11 +467,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       dyv[n] = acc;
     }
   }
-  __syncthreads();  // dO of the other sub-blocks is no longer read
+  lds_barrier();  // dO of the other sub-blocks is no longer read
 #pragma unroll
   for (int n = 0; n < NK; ++n)
     st_rowf(DOZ, PD, 16 * I, 16 * n, lane, dyv[n]);
-  __syncthreads();
+  lds_barrier();
   // dY_I = sum_{J >= I} T_JI^T dZ_J;  dv = dY (.) w, dw = dY (.) v
   IO *dq = static_cast<IO *>(ba.dq), *dk = static_cast<IO *>(ba.dk), *db = static_cast<IO *>(ba.db);
   IO *dal = static_cast<IO *>(ba.dal), *dvo = static_cast<IO *>(ba.dv), *dwo = static_cast<IO *>(ba.dw);
@@ -528,7 +567,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       r += btot[J2 * D + 16 * kk + m];
     return __expf(r);
   };
-  __syncthreads();  // Z in YZ is no longer read
+  lds_barrier();  // Z in YZ is no longer read
   float *dKacc = YZ;
   for (int d = 0; d < NB; ++d) {
 #pragma unroll
@@ -545,7 +584,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- map to the inputs
@@ -596,7 +635,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       dg[kk][i] = gs;  // in-block inclusive prefix of dg
     }
   }
-  __syncthreads();
+  lds_barrier();
   // d ln(alpha_t) = sum_{s >= t} dg_s + d g_C, d g_C = gamma dgamma + sum of the kb terms
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
