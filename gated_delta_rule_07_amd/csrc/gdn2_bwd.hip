@@ -318,34 +318,33 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     return y;
   };
 
-  // q, k, b of this lane's row for tile kk (zero past the end); reloaded in
-  // the late phases rather than kept in registers through the kernel
-  auto rowvals = [&](int kk, f32x4 &qq, f32x4 &kq, f32x4 &bq) {
-    const int c0 = 16 * kk + 4 * g;
-    qq = io<IO>::load4(q + row + c0);
-    kq = io<IO>::load4(k + row + c0);
-    bq = io<IO>::load4(b + row + c0);
-    if (!valid)
-      qq = kq = bq = zero4;
-  };
-
   // ---- rows of the sub-block; g = cumulative ln(alpha) within the chunk
   f32x4 qv[NK], kv[NK], ev[NK], gv[NK];
+  {
+    // every row load first, then the arithmetic
+    raw4<IO> rq[NK], rk[NK], rb[NK], ra[NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const int c0 = 16 * kk + 4 * g;
-    f32x4 qq = io<IO>::load4(q + row + c0), kq = io<IO>::load4(k + row + c0);
-    f32x4 bq = io<IO>::load4(b + row + c0), aq = io<IO>::load4(al + row + c0);
-    if (!valid) {
-      qq = kq = bq = zero4;
-      aq = f32x4{1.f, 1.f, 1.f, 1.f};
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c0 = 16 * kk + 4 * g;
+      rq[kk] = raw4<IO>::ld(q + row + c0);
+      rk[kk] = raw4<IO>::ld(k + row + c0);
+      rb[kk] = raw4<IO>::ld(b + row + c0);
+      ra[kk] = raw4<IO>::ld(al + row + c0);
     }
-    qv[kk] = qq;
-    kv[kk] = kq;
-    ev[kk] = bq * kq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      gv[kk][i] = row16_inclusive_scan(__logf(aq[i]));
+    for (int kk = 0; kk < NK; ++kk) {
+      f32x4 qq = rq[kk].f(), kq = rk[kk].f(), bq = rb[kk].f(), aq = ra[kk].f();
+      if (!valid) {
+        qq = kq = bq = zero4;
+        aq = f32x4{1.f, 1.f, 1.f, 1.f};
+      }
+      qv[kk] = qq;
+      kv[kk] = kq;
+      ev[kk] = bq * kq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        gv[kk][i] = row16_inclusive_scan(__logf(aq[i]));
+    }
   }
   if (m == 15) {
 #pragma unroll
@@ -400,12 +399,25 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
       esf[kk] = F::from(ev[kk] * ex4(gv[kk]));
+    // S tiles of column n + 1 are loaded while column n is multiplied
+    F cur[NK], nxt[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      cur[kk] = F::ld(St + ST_::COL + ST_::off(kk, 0), lane);
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
+      if (n + 1 < NK) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          nxt[kk] = F::ld(St + ST_::COL + ST_::off(kk, n + 1), lane);
+      }
       f32x4 acc = zero4;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        mm_io(acc, F::ld(St + ST_::COL + ST_::off(kk, n), lane), esf[kk]);
+        mm_io(acc, cur[kk], esf[kk]);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        cur[kk] = nxt[kk];
       f32x4 u = io<IO>::load4(w + row + 16 * n + 4 * g) * io<IO>::load4(v + row + 16 * n + 4 * g);
       zv[n] = (valid ? u : zero4) - acc;
       st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
@@ -456,14 +468,26 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
       kbf[kk] = F::from(kv[kk] * ex4(rho_end(NB - 1, kk) - gv[kk]));
+    F cur[NK], nxt[NK];  // dH tiles, column n + 1 in flight during column n
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      cur[kk] = F::ld(Ht + ST_::COL + ST_::off(kk, 0), lane);
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
+      if (n + 1 < NK) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          nxt[kk] = F::ld(Ht + ST_::COL + ST_::off(kk, n + 1), lane);
+      }
       f32x4 acc = zero4;
       for (int J = I; J < NB; ++J)
         mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sP, PC, 16 * J, 16 * I, lane));
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        mm_io(acc, F::ld(Ht + ST_::COL + ST_::off(kk, n), lane), kbf[kk]);
+        mm_io(acc, cur[kk], kbf[kk]);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        cur[kk] = nxt[kk];
       dyv[n] = acc;
     }
   }
@@ -521,15 +545,33 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     dyf[n] = F::from(dyv[n]);
     zf[n] = F::from(zv[n]);
   }
+  // S and dH tiles of row tile kk + 1 are loaded while row tile kk is multiplied
+  F scur[NK], hcur[NK], snxt[NK], hnxt[NK];
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    scur[n] = F::ld(St + ST_::ROW + ST_::off(0, n), lane);
+    hcur[n] = F::ld(Ht + ST_::ROW + ST_::off(0, n), lane);
+  }
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
+    if (kk + 1 < NK) {
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        snxt[n] = F::ld(St + ST_::ROW + ST_::off(kk + 1, n), lane);
+        hnxt[n] = F::ld(Ht + ST_::ROW + ST_::off(kk + 1, n), lane);
+      }
+    }
     f32x4 a1 = zero4, a2 = zero4, a3 = zero4;
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
-      const F sr = F::ld(St + ST_::ROW + ST_::off(kk, n), lane);
-      mm_io(a1, sr, dof[n]);
-      mm_io(a2, sr, dyf[n]);
-      mm_io(a3, F::ld(Ht + ST_::ROW + ST_::off(kk, n), lane), zf[n]);
+      mm_io(a1, scur[n], dof[n]);
+      mm_io(a2, scur[n], dyf[n]);
+      mm_io(a3, hcur[n], zf[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      scur[n] = snxt[n];
+      hcur[n] = hnxt[n];
     }
     const f32x4 eg = ex4(gv[kk]);
     cq[kk] = a1 * eg;
@@ -552,13 +594,21 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   // ---- dK~_J contributions of this sub-block's rows, accumulated in LDS in a
   // fixed order (own rows first, then one block diagonal per round)
   f32x4 qrc[NK], erc[NK];  // ColFrag of q e^{g - rho_I} and e e^{g - rho_I}
+  {
+    raw4<IO> rq[NK], rk[NK], rb[NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    f32x4 qq, kq, bq;
-    rowvals(kk, qq, kq, bq);
-    const f32x4 sc = ex4(gv[kk] - rho_end(I, kk));
-    qrc[kk] = transpose_f32(qq * sc, lane);
-    erc[kk] = transpose_f32(bq * kq * sc, lane);
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c0 = 16 * kk + 4 * g;
+      rq[kk] = raw4<IO>::ld(q + row + c0);
+      rk[kk] = raw4<IO>::ld(k + row + c0);
+      rb[kk] = raw4<IO>::ld(b + row + c0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const f32x4 sc = valid ? ex4(gv[kk] - rho_end(I, kk)) : zero4;
+      qrc[kk] = transpose_f32(rq[kk].f() * sc, lane);
+      erc[kk] = transpose_f32(rb[kk].f() * rk[kk].f() * sc, lane);
+    }
   }
   // column scale e^{rho_I - rho_J} of ColFrag element (lane column c)
   auto colscale = [&](int J, int kk) {
@@ -609,13 +659,26 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       *reinterpret_cast<f32x4 *>(dgam + 16 * kk + 4 * g) = acc;
   }
   f32x4 dg[NK];
+  raw4<IO> ral[NK];  // alpha of the rows, for d alpha at the end
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    ral[kk] = raw4<IO>::ld(al + row + 16 * kk + 4 * g);
+  // q, k, b of row tile kk + 1 are loaded while tile kk is mapped
+  raw4<IO> nq = raw4<IO>::ld(q + row + 4 * g), nk = raw4<IO>::ld(k + row + 4 * g),
+           nb = raw4<IO>::ld(b + row + 4 * g);
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const f32x4 dkt = reinterpret_cast<const f32x4 *>(dKacc)[(I * NK + kk) * 64 + lane];
     const f32x4 ckt = dkt * ex4(rho_end(I, kk) - gv[kk]);
     const int c0 = 16 * kk + 4 * g;
-    f32x4 qq, kq, bq;
-    rowvals(kk, qq, kq, bq);
+    f32x4 qq = nq.f(), kq = nk.f(), bq = nb.f();
+    if (!valid)
+      qq = kq = bq = zero4;
+    if (kk + 1 < NK) {
+      nq = raw4<IO>::ld(q + row + c0 + 16);
+      nk = raw4<IO>::ld(k + row + c0 + 16);
+      nb = raw4<IO>::ld(b + row + c0 + 16);
+    }
     const f32x4 kbt = kq * ck[kk];  // k (.) dKB-contribution, part of d g_C
     dg[kk] = qq * cq[kk] + bq * kq * ce[kk] - kq * (ck[kk] + ckt);
     if (valid) {
@@ -658,7 +721,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     }
     const f32x4 dl = own - dg[kk] + mine + tail + dgc;
     if (valid)
-      io<IO>::store4(dal + row + c0, dl / io<IO>::load4(al + row + c0));
+      io<IO>::store4(dal + row + c0, dl / ral[kk].f());
   }
 }
 
