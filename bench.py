@@ -69,7 +69,8 @@ def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
 
 
 # Algorithmic HBM bytes per token and head of the backward's kernels (bf16
-# elements, float32 states of d*d per chunk):
+# elements; a state crosses HBM as two fragment-tile copies of d*d elements
+# per chunk, the same bytes as one float32 copy):
 #   path         : read q, k, v, alpha, b, w and dL/do once, write six gradients
 #   chunk_states : read -W, Q', Kbar^T, Ut and gamma_C, write the entering state
 #   bwd_dstate   : read -W, Q', Kbar^T, gamma_C and dL/do, write the leaving-state gradient
