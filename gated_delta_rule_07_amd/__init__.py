@@ -1,5 +1,5 @@
-"""Python binding of libgdn2, the MI355X (gfx950) forward hot path of the
-Gated DeltaNet-2 recurrence.
+"""Python binding of libgdn2, the MI355X (gfx950) hot path (forward, backward,
+decode) of the Gated DeltaNet-2 recurrence.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libgdn2.so`` (built in-tree by ``gated_delta_rule_07_amd.build``).
@@ -37,6 +37,7 @@ FLAG_SCALAR_B = 1 << 4
 FLAG_SCALAR_W = 1 << 5
 FLAG_SCALAR_ALPHA = 1 << 6
 FLAG_LAYER_PREP = 1 << 0
+FLAG_RULE_R1 = 1 << 7
 PATHS = {"auto": 0, "recurrent": FLAG_RECURRENT, "two_pass": FLAG_TWO_PASS, "fused": FLAG_FUSED}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
@@ -117,10 +118,12 @@ def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chu
 
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
               recurrent: bool = False, out=None, S_final=None, workspace=None,
-              want_final: bool = True, path: str = "auto", layer_prep: bool = False):
+              want_final: bool = True, path: str = "auto", layer_prep: bool = False,
+              rule: str = "R5"):
     """Chunked forward.  ``path`` selects the kernels: "auto" (the library
     chooses), "fused" (single pass), "two_pass", or "recurrent" (token by
-    token; also selected by ``recurrent=True``).  Returns (o, S_final);
+    token; also selected by ``recurrent=True``).  ``rule="R1"`` runs the
+    alternative reading R1 (token-by-token path only).  Returns (o, S_final);
     S_final is None when ``want_final`` is False."""
     if recurrent:
         path = "recurrent"
@@ -152,7 +155,9 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
     Sf = S_final
     if Sf is None and want_final:
         Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    flags = PATHS[path] | gate_flags | (FLAG_LAYER_PREP if layer_prep else 0)
+    if rule not in ("R5", "R1"):
+        raise ValueError(f"unknown rule {rule!r}")
+    flags = PATHS[path] | gate_flags | (FLAG_LAYER_PREP if layer_prep else 0) | (FLAG_RULE_R1 if rule == "R1" else 0)
     ws_bytes = 0
     if path != "recurrent":
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)

@@ -182,12 +182,12 @@ bool fused_available(gdn2_dtype_t dt, int d, int c) {
 
 hipError_t dispatch_recurrent(gdn2_dtype_t dt, int d, const void *q, const void *k, const void *v,
                               const void *al, const void *b, const void *w, const float *S0,
-                              const int32_t *cu, int T, int H, int N, void *o, float *Sf,
+                              const int32_t *cu, int T, int H, int N, void *o, float *Sf, bool r1,
                               hipStream_t st) {
   prof_scope p("recurrent", st);
 #define GDN2_RR(IO, D) \
   if (d == D)          \
-    return gdn2::launch_recurrent<IO, D>(q, k, v, al, b, w, S0, cu, T, H, N, o, Sf, st);
+    return gdn2::launch_recurrent<IO, D>(q, k, v, al, b, w, S0, cu, T, H, N, o, Sf, r1, st);
   if (dt == GDN2_F32) {
     GDN2_RR(float, 16) GDN2_RR(float, 32) GDN2_RR(float, 64) GDN2_RR(float, 128)
   } else {
@@ -326,8 +326,10 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unknown dtype %d", static_cast<int>(dt));
   const uint32_t path_flags = GDN2_FLAG_RECURRENT | GDN2_FLAG_TWO_PASS | GDN2_FLAG_FUSED;
   const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
-  if (flags & ~(path_flags | gate_flags))
+  if (flags & ~(path_flags | gate_flags | GDN2_FLAG_RULE_R1))
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: unknown flags 0x%x", flags);
+  if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: rule R1 runs on the token-by-token path only");
   {
     const uint32_t paths = flags & path_flags;
     if (paths & (paths - 1))
@@ -371,7 +373,7 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
 
   if (flags & GDN2_FLAG_RECURRENT) {
     const hipError_t e = dispatch_recurrent(dt, dk, q, k, v, alpha, b, w, S0, cu_seqlens, T, H, N,
-                                            o, S_final, st);
+                                            o, S_final, (flags & GDN2_FLAG_RULE_R1) != 0, st);
     if (e != hipSuccess)
       return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -65,6 +65,7 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const void
 template <typename IO, int D>
 hipError_t launch_recurrent(const void *q, const void *k, const void *v, const void *al,
                             const void *b, const void *w, const float *S0, const int32_t *cu,
-                            int T, int H, int num_seqs, void *o, float *S_final, hipStream_t st);
+                            int T, int H, int num_seqs, void *o, float *S_final, bool r1,
+                            hipStream_t st);
 
 }  // namespace gdn2

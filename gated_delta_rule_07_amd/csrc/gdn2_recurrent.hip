@@ -13,6 +13,12 @@
 // which is D = Diag(alpha) S, z = w (.) v - D^T (b (.) k), S = D + k z^T,
 // o = S^T q (aixai.ru blog, formal paragraph of the gate section).
 //
+// The recurrent kernel also runs the alternative reading R1, in which b only
+// places the erase and the read uses the plain key:
+//   r = D^T k;  S = D - (b (.) k) r^T + k (w (.) v)^T;  o = S^T q
+// (the "location-gated erase": the same pages, read with the erase gate on
+// the erased direction instead of on the read).
+//
 // Work split: one workgroup per (sequence, head).  A thread owns 4
 // consecutive value columns in DK / ROWS_PER_PASS rows, so every state load
 // and store is a 16-byte vector and a row of 4*DV/4 threads reads one
@@ -56,19 +62,20 @@ __device__ __forceinline__ void rec_stage_token(rec_smem<DK, DV> &sm, const IO *
 
 // One token update of the thread's state slice s[p] (rows tr + RPP*p,
 // columns 4*tc .. 4*tc+3).  Writes o (DV values, element type IO) if o != 0.
-template <typename IO, int DK, int DV>
+// R1 selects the alternative reading above.
+template <typename IO, int DK, int DV, bool R1 = false>
 __device__ __forceinline__ void rec_token_update(rec_smem<DK, DV> &sm,
                                                  f32x4 (&s)[rec_shape<DK, DV>::PASSES], IO *o,
                                                  int tid) {
   typedef rec_shape<DK, DV> R;
   const int tc = tid % R::TPR, tr = tid / R::TPR;
-  // read with the erase-gated key, from the decayed state
+  // read with the erase-gated key (R1: the plain key), from the decayed state
   f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < R::PASSES; ++p) {
     const int i = tr + R::RPP * p;
     s[p] *= sm.a[i];
-    r += sm.e[i] * s[p];
+    r += (R1 ? sm.k[i] : sm.e[i]) * s[p];
   }
   *reinterpret_cast<f32x4 *>(&sm.red[tr][4 * tc]) = r;
   __syncthreads();
@@ -77,15 +84,19 @@ __device__ __forceinline__ void rec_token_update(rec_smem<DK, DV> &sm,
 #pragma unroll
     for (int t = 0; t < R::RPP; ++t)
       acc += sm.red[t][j];
-    sm.z[j] = sm.u[j] - acc;
+    sm.z[j] = R1 ? acc : sm.u[j] - acc;  // R1 keeps the read r itself
   }
   __syncthreads();
   const f32x4 z = *reinterpret_cast<const f32x4 *>(&sm.z[4 * tc]);
+  const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&sm.u[4 * tc]);
   f32x4 oq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < R::PASSES; ++p) {
     const int i = tr + R::RPP * p;
-    s[p] += sm.k[i] * z;
+    if constexpr (R1)
+      s[p] += sm.k[i] * u4 - sm.e[i] * z;  // erase along b (.) k, write along k
+    else
+      s[p] += sm.k[i] * z;
     oq += sm.q[i] * s[p];
   }
   *reinterpret_cast<f32x4 *>(&sm.red[tr][4 * tc]) = oq;
@@ -133,7 +144,7 @@ __global__ void __launch_bounds__((rec_shape<DK, DV>::NT))
 
 // grid: N*H workgroups (unit = n*H + h); block: rec_shape::NT threads.
 // Fixed length when cu == nullptr (sequence n = batch row n of length T).
-template <typename IO, int DK, int DV>
+template <typename IO, int DK, int DV, bool R1>
 __global__ void __launch_bounds__((rec_shape<DK, DV>::NT))
     gdn2_recurrent_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
                           const IO *__restrict__ v, const IO *__restrict__ al,
@@ -172,7 +183,7 @@ __global__ void __launch_bounds__((rec_shape<DK, DV>::NT))
     rec_stage_token<IO, DK, DV>(sm, q + row * DK, k + row * DK, v + row * DV, al + row * DK,
                                 b + row * DK, w + row * DV, tid);
     __syncthreads();
-    rec_token_update<IO, DK, DV>(sm, s, o + row * DV, tid);
+    rec_token_update<IO, DK, DV, R1>(sm, s, o + row * DV, tid);
   }
   if (S_final) {
     float *Su = S_final + static_cast<size_t>(u) * DK * DV;
@@ -200,14 +211,21 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const void
 template <typename IO, int D>
 hipError_t launch_recurrent(const void *q, const void *k, const void *v, const void *al,
                             const void *b, const void *w, const float *S0, const int32_t *cu,
-                            int T, int H, int num_seqs, void *o, float *S_final,
+                            int T, int H, int num_seqs, void *o, float *S_final, bool r1,
                             hipStream_t st) {
   typedef rec_shape<D, D> R;
-  hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, D, D>), dim3(num_seqs * H), dim3(R::NT), 0, st,
-                     static_cast<const IO *>(q), static_cast<const IO *>(k),
-                     static_cast<const IO *>(v), static_cast<const IO *>(al),
-                     static_cast<const IO *>(b), static_cast<const IO *>(w), S0, cu, T, H,
-                     num_seqs, static_cast<IO *>(o), S_final);
+  if (r1)
+    hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, D, D, true>), dim3(num_seqs * H), dim3(R::NT), 0, st,
+                       static_cast<const IO *>(q), static_cast<const IO *>(k),
+                       static_cast<const IO *>(v), static_cast<const IO *>(al),
+                       static_cast<const IO *>(b), static_cast<const IO *>(w), S0, cu, T, H,
+                       num_seqs, static_cast<IO *>(o), S_final);
+  else
+    hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, D, D, false>), dim3(num_seqs * H), dim3(R::NT), 0, st,
+                       static_cast<const IO *>(q), static_cast<const IO *>(k),
+                       static_cast<const IO *>(v), static_cast<const IO *>(al),
+                       static_cast<const IO *>(b), static_cast<const IO *>(w), S0, cu, T, H,
+                       num_seqs, static_cast<IO *>(o), S_final);
   return hipGetLastError();
 }
 
@@ -217,7 +235,7 @@ hipError_t launch_recurrent(const void *q, const void *k, const void *v, const v
                                            void *, int, int, hipStream_t);                    \
   template hipError_t launch_recurrent<IO, D>(                                                \
       const void *, const void *, const void *, const void *, const void *, const void *,     \
-      const float *, const int32_t *, int, int, int, void *, float *, hipStream_t);
+      const float *, const int32_t *, int, int, int, void *, float *, bool, hipStream_t);
 
 GDN2_INST_REC(float, 16)
 GDN2_INST_REC(float, 32)

@@ -1,6 +1,6 @@
 /*
- * gdn2.h -- C ABI of libgdn2, the MI355X (gfx950) forward hot path of the
- * Gated DeltaNet-2 (GDN-2) sequence-mixing recurrence.
+ * gdn2.h -- C ABI of libgdn2, the MI355X (gfx950) hot path (forward, backward
+ * and decode) of the Gated DeltaNet-2 (GDN-2) sequence-mixing recurrence.
  *
  * The operation (one head; state S is dk x dv float32, row i = key channel,
  * column j = value channel).  For every token t, in order:
@@ -100,6 +100,15 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
  * GDN2_FLAG_SCALAR_ALPHA).  The kernels L2-normalise q and k per (token,
  * head) in float32 (a zero row stays zero). */
 #define GDN2_FLAG_LAYER_PREP (1u << 0)
+/* Rule R1 (token-by-token path only: with GDN2_FLAG_RECURRENT, else
+ * GDN2_ERR_UNSUPPORTED).  The alternative reading of the pages' formal
+ * paragraph (aixai.ru blog, gate section) in which the erase gate places the
+ * erased direction instead of weighting the read:
+ *   D = Diag(alpha) S;  r = D^T k;  S = D - (b (.) k) r^T + k (w (.) v)^T;
+ *   o = S^T q.
+ * It reduces to KDA, Gated DeltaNet and DeltaNet as the default rule does;
+ * the pages do not settle which of the two they mean. */
+#define GDN2_FLAG_RULE_R1 (1u << 7)
 
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and

@@ -374,3 +374,46 @@ def test_decode_steps_equal_chunk_forward(g):
     torch.cuda.synchronize()
     assert rel_err(torch.stack(outs, 1).cpu().numpy(), o.cpu().numpy()) < 1e-4
     assert rel_err(S.cpu().numpy(), Sf.cpu().numpy()) < 1e-4
+
+
+# -------------------------------------------------------------- rule R1
+@pytest.mark.parametrize("dtype,d,T", [("f32", 64, 150), ("bf16", 128, 200)])
+def test_rule_r1_recurrent(g, dtype, d, T):
+    """The alternative reading R1 on the token-by-token kernel against the
+    oracle's R1, fixed-length with S0 and packed with an empty sequence."""
+    inp = gi.make_chunk_inputs(2, T, 2, d, d, dtype, seed=31 + d, s0="normal")
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], rule="R1")
+    d_ = to_dev(inp)
+    o, Sf = g.chunk_fwd(*(d_[n] for n in NAMES), S0=d_["S0"], recurrent=True, rule="R1")
+    torch.cuda.synchronize()
+    check(o.float().cpu().numpy(), Sf.cpu().numpy(), o_ref, S_ref, TOL[dtype], f"R1 {dtype} d={d}")
+    # R1 and R5 differ for generic gates
+    o5, _ = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], rule="R5")
+    assert rel_err(o5, o_ref) > 2 * TOL[dtype]
+    lens = [90, 0, T - 90]
+    cu = gi.cu_seqlens_from(lens)
+    pk = gi.make_chunk_inputs(1, T, 2, d, d, dtype, seed=32 + d, s0="normal", num_seqs=3)
+    o_ref, S_ref = oracle.fwd(*(pk[n] for n in NAMES), S0=pk["S0"], cu_seqlens=cu, rule="R1")
+    d_ = to_dev(pk)
+    o, Sf = g.chunk_fwd(*(d_[n] for n in NAMES), S0=d_["S0"], cu_seqlens=cu.cuda(), recurrent=True, rule="R1")
+    torch.cuda.synchronize()
+    check(o.float().cpu().numpy(), Sf.cpu().numpy(), o_ref, S_ref, TOL[dtype], f"R1 packed {dtype}")
+
+
+def test_rule_r1_equals_r5_when_gates_collapse(g):
+    """With b = w = beta both readings are KDA: the GPU's R1 and R5 agree."""
+    inp = gi.make_chunk_inputs(1, 130, 2, 64, 64, "f32", seed=33, s0="normal", scalar_beta=True)
+    d_ = to_dev(inp)
+    o1, S1 = g.chunk_fwd(*(d_[n] for n in NAMES), S0=d_["S0"], recurrent=True, rule="R1")
+    o5, S5 = g.chunk_fwd(*(d_[n] for n in NAMES), S0=d_["S0"], recurrent=True, rule="R5")
+    torch.cuda.synchronize()
+    assert rel_err(o1.cpu().numpy(), o5.cpu().numpy()) < 1e-5
+    assert rel_err(S1.cpu().numpy(), S5.cpu().numpy()) < 1e-5
+
+
+def test_rule_r1_rejected_on_chunked_paths(g):
+    inp = to_dev(gi.make_chunk_inputs(1, 64, 1, 32, 32, "f32", seed=34))
+    for path in ("auto", "two_pass", "fused"):
+        with pytest.raises(g.Gdn2Error) as e:
+            g.chunk_fwd(*(inp[n] for n in NAMES), path=path, rule="R1")
+        assert e.value.status == 2
