@@ -9,6 +9,8 @@ fallback: without the library or a GPU these functions raise.
     o, S_final = chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk=64)
     grads = chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, ...)
     o = decode_step(q, k, v, alpha, b, w, S)      # S updated in place
+    Phi, Psi = segment_map(q, k, v, alpha, b, w)  # per-sequence state maps
+    S_in, S_final = segment_combine(Phi, Psi, S0) # entering state of each segment
 
 Shapes: q, k, alpha, b [B, T, H, dk]; v, w [B, T, H, dv] (packed sequences:
 B = 1 and ``cu_seqlens`` int32 [N + 1] on the device); states [N, H, dk, dv]
@@ -66,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.gdn2_chunk_bwd_workspace_bytes.argtypes = [i] * 7 + [i]
         L.gdn2_chunk_bwd.restype = i
         L.gdn2_chunk_bwd.argtypes = [vp] * 8 + [i] * 8 + [u32] + [vp] * 9 + [vp, sz, vp]
+        L.gdn2_chunk_segment_map.restype = i
+        L.gdn2_chunk_segment_map.argtypes = [vp] * 7 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
+        L.gdn2_segment_combine.restype = i
+        L.gdn2_segment_combine.argtypes = [vp] * 3 + [i] * 4 + [vp, vp, vp]
         L.gdn2_decode_step.restype = i
         L.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
         L.gdn2_status_string.restype = ctypes.c_char_p
@@ -110,6 +116,19 @@ def _require_device(*ts) -> None:
             raise ValueError("libgdn2 takes contiguous device tensors")
 
 
+def _gate_flags(q, v, alpha, b, w) -> int:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    flags = 0
+    for t, flag, name, full in ((b, FLAG_SCALAR_B, "b", dk), (w, FLAG_SCALAR_W, "w", dv),
+                                (alpha, FLAG_SCALAR_ALPHA, "alpha", dk)):
+        if tuple(t.shape) == (B, T, H):
+            flags |= flag
+        elif tuple(t.shape) != (B, T, H, full):
+            raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}] or [{B}, {T}, {H}]")
+    return flags
+
+
 def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chunk: int,
                     dtype: torch.dtype) -> int:
     code = GDN2_BF16 if dtype == torch.bfloat16 else GDN2_F32
@@ -136,13 +155,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
         raise TypeError("with layer_prep, alpha is the float32 log-decay")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    gate_flags = 0
-    for t, flag, name, full in ((b, FLAG_SCALAR_B, "b", dk), (w, FLAG_SCALAR_W, "w", dv),
-                                (alpha, FLAG_SCALAR_ALPHA, "alpha", dk)):
-        if tuple(t.shape) == (B, T, H):
-            gate_flags |= flag
-        elif tuple(t.shape) != (B, T, H, full):
-            raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}] or [{B}, {T}, {H}]")
+    gate_flags = _gate_flags(q, v, alpha, b, w)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
@@ -222,6 +235,67 @@ def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=Non
         _ptr(out["dw"]), _ptr(out.get("dS0")), _ptr(workspace), workspace.numel(), _stream()))
     out.setdefault("dS0", None)
     return out
+
+
+def segment_map(q, k, v, alpha, b, w, cu_seqlens=None, chunk: int = 64, layer_prep: bool = False,
+                workspace=None, out=None):
+    """Affine state map of every sequence of the call (each taken as one
+    segment of a longer sequence): returns (Phi [N, H, dk, dk], Psi
+    [N, H, dk, dv]) float32 with S_out = Phi S_in + Psi.  Inputs as for
+    ``chunk_fwd`` (gate layouts and ``layer_prep`` included).  ``out`` may
+    be a preallocated (Phi, Psi) pair."""
+    _require_device(q, k, v, alpha, b, w, cu_seqlens)
+    dt = _dtype_code(q)
+    for t in (k, v, b, w) + (() if layer_prep else (alpha,)):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, alpha, b, w must share one dtype")
+    if layer_prep and alpha.dtype != torch.float32:
+        raise TypeError("with layer_prep, alpha is the float32 log-decay")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    flags = _gate_flags(q, v, alpha, b, w) | (FLAG_LAYER_PREP if layer_prep else 0)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if out is not None:
+        Phi, Psi = out
+    else:
+        Phi = torch.empty((N, H, dk, dk), dtype=torch.float32, device=q.device)
+        Psi = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _require_device(Phi, Psi)
+    if tuple(Phi.shape) != (N, H, dk, dk) or tuple(Psi.shape) != (N, H, dk, dv) or \
+            Phi.dtype != torch.float32 or Psi.dtype != torch.float32:
+        raise ValueError(f"Phi, Psi must be float32 [{N}, {H}, {dk}, {dk}] and [{N}, {H}, {dk}, {dv}]")
+    ns = N if cu_seqlens is not None else 0
+    ws_bytes = workspace_bytes(B, T, H, dk, dv, ns, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().gdn2_chunk_segment_map(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens),
+        B, T, H, dk, dv, ns, chunk, dt, flags, _ptr(Phi), _ptr(Psi), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return Phi, Psi
+
+
+def segment_combine(Phi, Psi, S0=None, want_final: bool = True, out=None):
+    """Exclusive scan of the maps of G consecutive segments of one sequence
+    (Phi [G, H, dk, dk], Psi [G, H, dk, dv]) from S0 [H, dk, dv] (None: zero).
+    Returns (S_in [G, H, dk, dv], S_final [H, dk, dv] or None)."""
+    _require_device(Phi, Psi, S0)
+    G, H, dk, _ = Phi.shape
+    dv = Psi.shape[-1]
+    if Phi.dtype != torch.float32 or Psi.dtype != torch.float32 or tuple(Psi.shape) != (G, H, dk, dv):
+        raise ValueError("Phi, Psi must be float32 [G, H, dk, dk] and [G, H, dk, dv]")
+    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (H, dk, dv)):
+        raise ValueError(f"S0 must be float32 [{H}, {dk}, {dv}]")
+    S_in = out if out is not None else torch.empty((G, H, dk, dv), dtype=torch.float32, device=Phi.device)
+    Sf = torch.empty((H, dk, dv), dtype=torch.float32, device=Phi.device) if want_final else None
+    _check(lib().gdn2_segment_combine(_ptr(Phi), _ptr(Psi), _ptr(S0), G, H, dk, dv, _ptr(S_in), _ptr(Sf),
+                                      _stream()))
+    return S_in, Sf
 
 
 def decode_step(q, k, v, alpha, b, w, S, out=None):

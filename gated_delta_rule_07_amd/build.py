@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libgdn2.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("GDN2_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gdn2_api.cpp", "gdn2_recurrent.hip", "gdn2_chunk.hip", "gdn2_fused.hip", "gdn2_bwd.hip"]
+SOURCES = ["gdn2_api.cpp", "gdn2_recurrent.hip", "gdn2_chunk.hip", "gdn2_fused.hip", "gdn2_bwd.hip", "gdn2_segment.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument"]

@@ -296,6 +296,43 @@ bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk,
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ------------------------------------------------------------ segment maps --
+template <typename IO, int D, int C>
+hipError_t run_segmap(const gdn2::chunk_args &a, int C_rt, float *Phi, float *Psi, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (a.cu) {
+    prof_scope p("chunk_table", st);
+    e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  if (a.num_slots > 0) {
+    prof_scope p("chunk_prep", st);
+    e = gdn2::launch_chunk_prep<IO, D, C>(a, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  prof_scope p("segment_map", st);
+  return gdn2::launch_segmap<IO, D, C>(a, Phi, Psi, st);
+}
+
+hipError_t dispatch_segmap(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, float *Phi, float *Psi,
+                           hipStream_t st) {
+#define GDN2_RS(IO, D, C) \
+  if (d == D && c == C)   \
+    return run_segmap<IO, D, C>(a, C, Phi, Psi, st);
+  if (dt == GDN2_F32) {
+    GDN2_RS(float, 16, 16) GDN2_RS(float, 32, 16) GDN2_RS(float, 64, 16) GDN2_RS(float, 128, 16)
+    GDN2_RS(float, 16, 64) GDN2_RS(float, 32, 64) GDN2_RS(float, 64, 64) GDN2_RS(float, 128, 64)
+  } else {
+    GDN2_RS(gdn2::bf16_t, 16, 16) GDN2_RS(gdn2::bf16_t, 32, 16) GDN2_RS(gdn2::bf16_t, 64, 16)
+    GDN2_RS(gdn2::bf16_t, 128, 16) GDN2_RS(gdn2::bf16_t, 16, 64) GDN2_RS(gdn2::bf16_t, 32, 64)
+    GDN2_RS(gdn2::bf16_t, 64, 64) GDN2_RS(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_RS
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 extern "C" {
@@ -531,6 +568,116 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   const hipError_t e = dispatch_bwd(dt, dk, chunk, ba, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gdn2_status_t gdn2_chunk_segment_map(const void *q, const void *k, const void *v, const void *alpha,
+                                     const void *b, const void *w, const int32_t *cu_seqlens, int B, int T,
+                                     int H, int dk, int dv, int num_seqs, int chunk, gdn2_dtype_t dt,
+                                     uint32_t flags, float *Phi, float *Psi, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_segment_map: unknown dtype %d", static_cast<int>(dt));
+  const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
+  if (flags & ~gate_flags)
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_segment_map: flags 0x%x: only the gate layout and layer prep flags apply", flags);
+  if (B <= 0 || T < 0 || H <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: bad sizes B=%d T=%d H=%d", B, T, H);
+  if (dk != dv || !supported_dim(dk))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_segment_map: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
+                dk, dv);
+  if (!supported_chunk(chunk))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_segment_map: unsupported chunk %d (need 16 or 64)", chunk);
+  const bool packed = cu_seqlens != nullptr;
+  int N;
+  if (packed) {
+    if (B != 1)
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: packed input needs B == 1 (got %d)", B);
+    if (num_seqs <= 0)
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: packed input needs num_seqs > 0");
+    N = num_seqs;
+  } else {
+    if (num_seqs != 0 && num_seqs != B)
+      return fail(GDN2_ERR_INVALID_ARGUMENT,
+                  "gdn2_chunk_segment_map: num_seqs=%d must be 0 or B=%d without cu_seqlens", num_seqs, B);
+    N = B;
+  }
+  if (!Phi || !Psi)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: null Phi or Psi");
+  if (T > 0 && (!q || !k || !v || !alpha || !b || !w))
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: null input pointer");
+  const void *ptrs[] = {q, k, v, alpha, b, w, Phi, Psi, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p))
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: pointers must be 16-byte aligned");
+  const long long elems = static_cast<long long>(B) * T * H * dk;
+  if (elems > (1LL << 40))
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_segment_map: problem too large");
+  const size_t table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
+  const size_t need = table + static_cast<size_t>(num_slots_for(B, T, N, chunk, packed)) * H *
+                                  chunk_block_bytes_rt(dt, dk, chunk);
+  if (workspace_bytes < need || !workspace)
+    return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                "gdn2_chunk_segment_map: workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need);
+  gdn2::chunk_args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.al = alpha;
+  a.b = b;
+  a.w = w;
+  a.cu = cu_seqlens;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.num_seqs = N;
+  a.num_slots = T == 0 ? 0 : num_slots_for(B, T, N, chunk, packed);
+  a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
+  a.gates = ((flags & GDN2_FLAG_SCALAR_B) ? gdn2::GATE_SCALAR_B : 0u) |
+            ((flags & GDN2_FLAG_SCALAR_W) ? gdn2::GATE_SCALAR_W : 0u) |
+            ((flags & GDN2_FLAG_SCALAR_ALPHA) ? gdn2::GATE_SCALAR_ALPHA : 0u) |
+            ((flags & GDN2_FLAG_LAYER_PREP) ? gdn2::GATE_LAYER_PREP : 0u);
+  char *ws = static_cast<char *>(workspace);
+  a.offsets = packed ? reinterpret_cast<int32_t *>(ws) : nullptr;
+  a.blocks = ws + table;
+  const hipError_t e = dispatch_segmap(dt, dk, chunk, a, Phi, Psi, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(GDN2_ERR_HIP, "gdn2_chunk_segment_map: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gdn2_status_t gdn2_segment_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int dk,
+                                   int dv, float *S_in, float *S_final, void *stream) {
+  if (G < 0 || H <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_segment_combine: bad sizes G=%d H=%d", G, H);
+  if (dk != dv || !supported_dim(dk))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_segment_combine: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
+                dk, dv);
+  if (G > 0 && (!Phi || !Psi || !S_in))
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_segment_combine: null Phi, Psi or S_in");
+  const void *ptrs[] = {Phi, Psi, S0, S_in, S_final};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p))
+      return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_segment_combine: pointers must be 16-byte aligned");
+  if (G == 0 && !S_final)
+    return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipErrorInvalidValue;
+  {
+    prof_scope p("segment_combine", st);
+    switch (dk) {
+      case 16: e = gdn2::launch_seg_combine<16>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
+      case 32: e = gdn2::launch_seg_combine<32>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
+      case 64: e = gdn2::launch_seg_combine<64>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
+      case 128: e = gdn2::launch_seg_combine<128>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
+    }
+  }
+  if (e != hipSuccess)
+    return fail(GDN2_ERR_HIP, "gdn2_segment_combine: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -58,6 +58,14 @@ struct bwd_args {
 template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args &a, hipStream_t st);
 template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st);
 
+// Affine state map of every sequence taken as one segment: Phi [N, H, D, D]
+// and Psi [N, H, D, D] float32, row-major, from the prepared blocks.
+template <typename IO, int D, int C> hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_t st);
+// Exclusive scan of G segment maps [G, H, D, D] from S0 [H, D, D] (nullptr: zero).
+template <int D>
+hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, float *S_in,
+                              float *S_final, hipStream_t st);
+
 template <typename IO, int D>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,
                          const void *b, const void *w, float *S, void *o, int N, int H,

@@ -63,20 +63,23 @@ def cu_seqlens_from(lengths: list[int]) -> torch.Tensor:
 
 def make_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
                       s0: str | None = None, num_seqs: int | None = None,
-                      scalar_beta: bool = False) -> dict:
+                      scalar_beta: bool = False, alpha_mean: float = 3.0) -> dict:
     """Inputs of one chunked-forward call.
 
     ``s0``: None (no initial state), "zero" (explicit zeros) or "normal"
     (N(0, 0.1^2)).  ``num_seqs`` is the number of state slots (B for fixed
     length, the sequence count for packed input).  ``scalar_beta`` replaces
     b and w by one shared scalar beta = sigmoid(N(0,1)) per (batch, token,
-    head), broadcast over channels (the collapsed-gate case).
+    head), broadcast over channels (the collapsed-gate case).  ``alpha_mean``
+    is the mean of the decay logit: 3 (the default) forgets within a few
+    hundred tokens, 8 decays a channel by about e^-2.3 over 4096 tokens
+    (a long-memory head).
     """
     rng = np.random.default_rng(seed)
     q = _l2norm(rng.standard_normal((B, T, H, dk)))
     k = _l2norm(rng.standard_normal((B, T, H, dk)))
     v = rng.standard_normal((B, T, H, dv))
-    alpha = _sigmoid(rng.normal(3.0, 1.0, (B, T, H, dk)))
+    alpha = _sigmoid(rng.normal(alpha_mean, 1.0, (B, T, H, dk)))
     if scalar_beta:
         beta = _sigmoid(rng.standard_normal((B, T, H, 1)))
         b = np.broadcast_to(beta, (B, T, H, dk))

@@ -182,6 +182,45 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
                              void *dv_out, void *dalpha, void *db, void *dw, float *dS0,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* Affine state map of sequence segments (context parallelism along T: a
+ * long sequence cut into segments that run side by side).  Over any run of
+ * tokens the recurrence above is affine in the state it starts from,
+ *   S_out = Phi S_in + Psi,
+ * because every token's update is (Diag(alpha) - k (b (.) k)^T Diag(alpha)) S
+ * plus a term free of S.  Phi (dk x dk) is the product of the tokens' linear
+ * parts, last first; Psi (dk x dv) is S_out for S_in = 0.  This follows from
+ * the rule itself and the chunkwise form the aixai.ru blog names (section on
+ * how the method is implemented in practice); the pages describe no
+ * sequence-parallel split.
+ * Every sequence of the call (B rows, or num_seqs packed sequences) is one
+ * segment:
+ *   q .. w, cu_seqlens, B .. dt : as for gdn2_chunk_fwd (the gate layout and
+ *               layer prep flags apply; no S0: a segment's map does not
+ *               depend on it).
+ *   flags     : GDN2_FLAG_SCALAR_B / _W / _ALPHA and GDN2_FLAG_LAYER_PREP
+ *               only (others return GDN2_ERR_UNSUPPORTED).
+ *   Phi, Psi  : outputs, [N, H, dk, dk] and [N, H, dk, dv] float32, row-major
+ *               per head.  An empty segment gives Phi = I, Psi = 0.
+ *   workspace : at least gdn2_chunk_fwd_workspace_bytes(...) bytes.
+ * The maps use the chunked path's arithmetic (the state rounded to dt for
+ * the matrix products, as in gdn2_chunk_fwd) and its numerical domain. */
+gdn2_status_t gdn2_chunk_segment_map(const void *q, const void *k, const void *v, const void *alpha,
+                                     const void *b, const void *w, const int32_t *cu_seqlens, int B, int T,
+                                     int H, int dk, int dv, int num_seqs, int chunk, gdn2_dtype_t dt,
+                                     uint32_t flags, float *Phi, float *Psi, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/* The exclusive scan of G consecutive segments' maps of one sequence (H
+ * heads): S_in[0] = S0, S_in[g+1] = Phi[g] S_in[g] + Psi[g], in float32.
+ *   Phi, Psi  : [G, H, dk, dk] and [G, H, dk, dv] float32 (gdn2_chunk_segment_map).
+ *   S0        : [H, dk, dv] float32 state entering segment 0, or NULL for zero.
+ *   S_in      : output [G, H, dk, dv], the state entering every segment.
+ *   S_final   : output [H, dk, dv], the state after segment G-1, or NULL.
+ * Running gdn2_chunk_fwd on each segment from its S_in then gives the
+ * outputs of the whole sequence.  G = 0 is allowed (S_final = S0). */
+gdn2_status_t gdn2_segment_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int dk,
+                                   int dv, float *S_in, float *S_final, void *stream);
+
 /* One recurrent decode step for N sequences x H heads at constant memory
  * (aixai.ru blog: constant-memory decoding; needhelp.icu/de, section on the
  * attention bottleneck).  q, k, alpha, b are [N, H, dk]; v, w, o are

@@ -6,8 +6,11 @@ GPU library never imports it.
 
 ``fwd`` and ``decode`` run the plain float64 token-by-token recurrence written
 in C (``gdn2_oracle.c``); ``bwd`` runs its hand-derived reverse-mode
-derivative, token by token from the last.  Inputs are the stored tensors (float32 or bf16),
-upcast to float64 exactly; outputs are float64 NumPy arrays.
+derivative, token by token from the last.  ``segment_map`` and
+``segment_combine`` (NumPy, float64) give the affine state map of a run of
+tokens and the exclusive scan that chains such maps.  Inputs are the stored
+tensors (float32 or bf16), upcast to float64 exactly; outputs are float64
+NumPy arrays.
 """
 from __future__ import annotations
 
@@ -144,3 +147,55 @@ def bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None):
     if rc != 0:
         raise RuntimeError(f"gdn2_oracle_bwd failed with code {rc}")
     return g
+
+
+def _sequences(B, T, cu_seqlens):
+    """(row, start, end) of every sequence: B rows of T tokens, or packed."""
+    if cu_seqlens is None:
+        return [(n, 0, T) for n in range(B)]
+    cu = np.asarray(cu_seqlens.numpy() if hasattr(cu_seqlens, "numpy") else cu_seqlens, dtype=np.int64)
+    return [(0, int(cu[i]), int(cu[i + 1])) for i in range(cu.shape[0] - 1)]
+
+
+def segment_map(q, k, v, alpha, b, w, cu_seqlens=None):
+    """Affine state map S_out = Phi S_in + Psi of every sequence (rule R5).
+
+    Putting D = Diag(alpha) S and z = w (.) v - D^T (b (.) k) into
+    S' = D + k z^T (the formal paragraph of the aixai.ru Gated DeltaNet-2
+    blog, in this library's reading) gives, per token,
+        S' = A S + k (w (.) v)^T,   A = (I - k (b (.) k)^T) Diag(alpha),
+    so over a run of tokens Phi = A_last ... A_first and Psi is the state
+    reached from zero.  Both are accumulated token by token in float64:
+    Phi <- A Phi, Psi <- A Psi + k (w (.) v)^T, with A applied as its two
+    factors.  Returns (Phi [N,H,dk,dk], Psi [N,H,dk,dv])."""
+    q, k, v, alpha, b, w = (_f64(x) for x in (q, k, v, alpha, b, w))
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    seqs = _sequences(B, T, cu_seqlens)
+    Phi = np.zeros((len(seqs), H, dk, dk))
+    Psi = np.zeros((len(seqs), H, dk, dv))
+    for i, (n, s, e) in enumerate(seqs):
+        P = np.broadcast_to(np.eye(dk), (H, dk, dk)).copy()
+        Q = np.zeros((H, dk, dv))
+        for t in range(s, e):
+            kt, bt, at = k[n, t], b[n, t], alpha[n, t]           # [H, dk]
+            for M in (P, Q):
+                M *= at[:, :, None]                              # Diag(alpha) M
+                M -= kt[:, :, None] * np.einsum("hi,hij->hj", bt * kt, M)[:, None, :]
+            Q += kt[:, :, None] * (w[n, t] * v[n, t])[:, None, :]
+        Phi[i], Psi[i] = P, Q
+    return Phi, Psi
+
+
+def segment_combine(Phi, Psi, S0=None):
+    """Exclusive scan of consecutive segments' maps [G,H,..]: the state
+    entering segment g, S_in[0] = S0 (zero if None), S_in[g+1] =
+    Phi[g] S_in[g] + Psi[g].  Returns (S_in [G,H,dk,dv], S_final [H,dk,dv])."""
+    Phi, Psi = _f64(Phi), _f64(Psi)
+    G, H, dk, dv = Psi.shape
+    S = np.zeros((H, dk, dv)) if S0 is None else _f64(S0).copy()
+    S_in = np.zeros((G, H, dk, dv))
+    for g in range(G):
+        S_in[g] = S
+        S = Phi[g] @ S + Psi[g]
+    return S_in, S

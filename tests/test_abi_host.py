@@ -139,3 +139,41 @@ def test_bwd_workspace_bytes(L):
     assert L.gdn2_chunk_bwd_workspace_bytes(2, 200, 3, 48, 48, 0, 64, BF16) == 0
     assert L.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 32, 32, 3, 16, F32) >= \
         L.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 32, 32, 0, 16, F32)
+
+
+def call_segmap(L, *, ptr=FAKE, B=1, T=64, H=1, dk=16, dv=16, N=0, chunk=16, dt=F32, flags=0,
+                cu=None, ws=FAKE, ws_bytes=1 << 40, phi=FAKE, psi=FAKE):
+    p = ptr
+    return L.gdn2_chunk_segment_map(p, p, p, p, p, p, cu, B, T, H, dk, dv, N, chunk, dt, flags,
+                                    phi, psi, ws, ws_bytes, None)
+
+
+def test_segment_map_rejects_before_launch(L):
+    assert call_segmap(L, dk=24, dv=24) == 2
+    assert call_segmap(L, dk=64, dv=32) == 2
+    assert call_segmap(L, chunk=32) == 2
+    assert call_segmap(L, dt=7) == 2
+    assert call_segmap(L, B=0) == 1
+    assert call_segmap(L, T=-1) == 1
+    # path and rule flags do not apply to the map
+    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 8):
+        assert call_segmap(L, flags=flag) == 2
+    assert call_segmap(L, phi=None) == 1
+    assert call_segmap(L, psi=0x10004) == 1      # misaligned
+    assert call_segmap(L, ws_bytes=16) == 3
+    assert call_segmap(L, B=2, N=1) == 1         # num_seqs without cu_seqlens
+    assert call_segmap(L, B=2, N=2, cu=FAKE) == 1
+    assert L.gdn2_last_error() != b""
+
+
+def test_segment_combine_rejects_before_launch(L):
+    p = FAKE
+    assert L.gdn2_segment_combine(p, p, None, -1, 1, 16, 16, p, None, None) == 1
+    assert L.gdn2_segment_combine(p, p, None, 2, 0, 16, 16, p, None, None) == 1
+    assert L.gdn2_segment_combine(p, p, None, 2, 1, 48, 48, p, None, None) == 2
+    assert L.gdn2_segment_combine(p, p, None, 2, 1, 32, 16, p, None, None) == 2
+    assert L.gdn2_segment_combine(None, p, None, 2, 1, 16, 16, p, None, None) == 1
+    assert L.gdn2_segment_combine(p, p, None, 2, 1, 16, 16, None, None, None) == 1
+    assert L.gdn2_segment_combine(p, p, 0x10008, 2, 1, 16, 16, p, None, None) == 1
+    # nothing to do: no segment and no final state asked for
+    assert L.gdn2_segment_combine(None, None, None, 0, 1, 16, 16, None, None, None) == 0
