@@ -20,6 +20,9 @@ In the same run (reported next to the headline, not in `value`):
     DeltaNet (also a per-(token, head) decay), and GDN-2's time over KDA's;
   * the chunked backward (gdn2_chunk_bwd) on the same layer: its time per
     step, per-kernel durations and the roofline of its dominant kernel;
+  * a context-parallel split of one 32768-token sequence into 8 segments:
+    the per-rank segment map and re-run against the serial forward, and all
+    eight on this GPU with the scan of the maps;
   * the CPU oracle timed on a bounded sample of the same workload.
 Prints one JSON line.
 """
@@ -144,6 +147,107 @@ def load_traffic(kernel: str) -> dict | None:
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec
+
+
+# Algorithmic HBM bytes of the segment-map kernel per token and head: read
+# -W, Kbar^T and Ut (bf16) and gamma_C (fp32 per chunk); the two maps it
+# writes (2 d^2 fp32 per segment and head) are added per launch.  FLOPs: the
+# products Z = Ut - W S and S <- gamma S + Kbar^T Z, 4 d^2 per token for each
+# of Phi and Psi.
+def segmap_bytes_per_token_head(d: int, C: int, elem: int = 2) -> float:
+    return 3 * d * elem + d * 4 / C
+
+
+def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
+    """The 32768-token stream of the packed workload as ONE sequence cut
+    into 8 segments of 4096 tokens (an 8-way context-parallel split).  Per
+    rank: the segment's map (prep + segment-map kernel) and its re-run from
+    the true entering state (gdn2_chunk_fwd), against the serial forward of
+    the same 4096 x 16 share.  On one GPU: all 8 maps in one call, the scan
+    of the maps, the 8 re-runs in one packed call, against the forward of the
+    whole 32768-token sequence."""
+    G, L = 8, 4096
+    res = {"workload": "one 32768-token sequence, H=16, d=128, bf16, cut into 8 segments of 4096",
+           "per_rank_shape": {"T": L, "H": H}}
+    rank = {x: dev[x][0:1] for x in NAMES}                    # [1, 4096, H, d]
+    ws1 = torch.empty(g.workspace_bytes(1, L, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    Phi1 = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+    Psi1 = torch.empty_like(Phi1)
+    o1 = torch.empty((1, L, H, d), dtype=torch.bfloat16, device="cuda")
+    Sf1 = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+    S_in1 = torch.zeros((1, H, d, d), dtype=torch.float32, device="cuda")
+
+    def rank_map():
+        g.segment_map(*(rank[x] for x in NAMES), chunk=C, workspace=ws1, out=(Phi1, Psi1))
+
+    def rank_fwd(S0):
+        g.chunk_fwd(*(rank[x] for x in NAMES), S0=S0, chunk=C, out=o1, S_final=Sf1, workspace=ws1, path=path)
+
+    g.profile_enable(True)
+    g.profile_read(reset=True)
+    sec_map = timed_steps(rank_map, 20, 3)
+    prof = g.profile_read(reset=True)
+    g.profile_enable(False)
+    kern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in prof.items()}
+    sec_rerun = timed_steps(lambda: rank_fwd(S_in1), 20, 3)
+    sec_serial = timed_steps(lambda: rank_fwd(None), 20, 3)
+    sm_us = kern["segment_map"]["avg_us"]
+    tok_heads = L * H
+    sm_bytes = segmap_bytes_per_token_head(d, C) * tok_heads + 2 * H * d * d * 4
+    sm_flops = 8.0 * d * d * tok_heads
+    res["per_rank"] = {
+        "map_ms": round(sec_map * 1e3, 4), "rerun_ms": round(sec_rerun * 1e3, 4),
+        "serial_forward_ms": round(sec_serial * 1e3, 4),
+        "map_plus_rerun_over_serial": round((sec_map + sec_rerun) / sec_serial, 3),
+        "kernels": kern,
+        "segment_map_roofline": {"bound": "hbm", "achieved": round(sm_bytes / (sm_us * 1e-6) / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(sm_bytes / (sm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "algorithmic_bytes_per_launch": int(sm_bytes),
+                                 "tflops": round(sm_flops / (sm_us * 1e-6) / 1e12, 2)},
+    }
+    del ws1
+
+    # all eight segments on this one GPU
+    cu = gi.cu_seqlens_from([L] * G).cuda()
+    full = {x: dev[x].view(1, G * L, H, d) for x in NAMES}
+    wsG = torch.empty(g.workspace_bytes(1, G * L, H, d, d, G, C, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    PhiG = torch.empty((G, H, d, d), dtype=torch.float32, device="cuda")
+    PsiG = torch.empty_like(PhiG)
+    S_inG = torch.empty_like(PhiG)
+    oG = torch.empty((1, G * L, H, d), dtype=torch.bfloat16, device="cuda")
+    SfG = torch.empty_like(PhiG)
+    ws_seq = torch.empty(g.workspace_bytes(1, G * L, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8,
+                         device="cuda")
+    Sf_seq = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+
+    def all_maps():
+        g.segment_map(*(full[x] for x in NAMES), cu_seqlens=cu, chunk=C, workspace=wsG, out=(PhiG, PsiG))
+
+    def combine():
+        g.segment_combine(PhiG, PsiG, None, want_final=False, out=S_inG)
+
+    def reruns():
+        g.chunk_fwd(*(full[x] for x in NAMES), S0=S_inG, cu_seqlens=cu, chunk=C, out=oG, S_final=SfG,
+                    workspace=wsG, path=path)
+
+    def whole():
+        g.chunk_fwd(*(full[x] for x in NAMES), chunk=C, out=oG, S_final=Sf_seq, workspace=ws_seq, path=path)
+
+    g.profile_enable(True)
+    g.profile_read(reset=True)
+    sec_comb = timed_steps(combine, 20, 3)
+    cprof = g.profile_read(reset=True)
+    g.profile_enable(False)
+    sec_all = timed_steps(lambda: (all_maps(), combine(), reruns()), 10, 2)
+    sec_whole = timed_steps(whole, 10, 2)
+    res["one_gpu"] = {
+        "maps_combine_reruns_ms": round(sec_all * 1e3, 4), "whole_sequence_forward_ms": round(sec_whole * 1e3, 4),
+        "ratio": round(sec_all / sec_whole, 3),
+        "combine_kernel_us": round(1e3 * cprof["segment_combine"][0] / cprof["segment_combine"][1], 2),
+        "exchange_bytes_per_rank": 2 * H * d * d * 4,
+    }
+    return res
 
 
 def main() -> int:
@@ -355,6 +459,8 @@ def main() -> int:
                          "algorithmic_bytes_per_launch": int(bbyt[bdom] * tok_heads)},
         }
         del wsb
+
+        out["context_parallel"] = context_parallel(g, dev, H, d, C, args.path)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, H, args.cpu_budget)

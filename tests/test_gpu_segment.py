@@ -57,6 +57,8 @@ CASES = [  # dtype, d, chunk, B, T, H
     ("bf16", 64, 16, 2, 77, 2),
     ("bf16", 128, 64, 2, 300, 2),
     ("bf16", 16, 64, 1, 64, 3),
+    ("bf16", 16, 16, 2, 50, 2),
+    ("bf16", 32, 64, 1, 130, 2),
 ]
 
 
