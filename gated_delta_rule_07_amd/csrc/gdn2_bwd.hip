@@ -367,9 +367,9 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
-      const f32x4 kt = ld_rowf(KT, PD, 16 * J, 16 * kk, lane);
-      mm<CT>(aa, ev[kk] * sc, kt);
-      mm<CT>(pp, qv[kk] * sc, kt);
+      const F kt = F::from(ld_rowf(KT, PD, 16 * J, 16 * kk, lane));
+      mm_io(aa, F::from(ev[kk] * sc), kt);
+      mm_io(pp, F::from(qv[kk] * sc), kt);
     }
     if (J == I) {
       aa = tri_col(aa, lane, true);
@@ -511,33 +511,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     }
   }
 
-  // ---- dA_IJ = -dY_I Z_J^T, dP_IJ = dO_I Z_J^T (J <= I), as ColFrag (c) and RowFrag (r)
-  f32x4 dAc[NB], dAr[NB], dPc[NB], dPr[NB];
-#pragma unroll
-  for (int J = 0; J < NB; ++J) {
-    dAc[J] = dAr[J] = dPc[J] = dPr[J] = zero4;
-    if (J <= I) {
-#pragma unroll
-      for (int n = 0; n < NK; ++n) {
-        const f32x4 zr = ld_rowf(YZ, PD, 16 * J, 16 * n, lane);
-        mm<CT>(dAc[J], dyv[n], zr);
-        mm<CT>(dAr[J], zr, dyv[n]);
-        mm<CT>(dPc[J], dov[n], zr);
-        mm<CT>(dPr[J], zr, dov[n]);
-      }
-      dAc[J] = -dAc[J];
-      dAr[J] = -dAr[J];
-      if (J == I) {
-        dAc[J] = tri_col(dAc[J], lane, true);
-        dPc[J] = tri_col(dPc[J], lane, false);
-        dAr[J] = tri_row(dAr[J], lane, true);
-        dPr[J] = tri_row(dPr[J], lane, false);
-      }
-    }
-  }
-
-  // ---- contributions to dq (cq), de (ce), dk (ck) and d g_C (kb term)
-  f32x4 cq[NK], ce[NK], ck[NK];
+  // ---- dA_IJ = -dY_I Z_J^T, dP_IJ = dO_I Z_J^T (J <= I), as ColFrag (c) and RowFrag (r),
+  // kept as operand fragments (every later use is a product operand)
   F dof[NK], dyf[NK], zf[NK];
 #pragma unroll
   for (int n = 0; n < NK; ++n) {
@@ -545,6 +520,36 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     dyf[n] = F::from(dyv[n]);
     zf[n] = F::from(zv[n]);
   }
+  F dAc[NB], dAr[NB], dPc[NB], dPr[NB];
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    f32x4 ac = zero4, ar = zero4, pc = zero4, pr = zero4;
+    if (J <= I) {
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        const F zr = F::from(ld_rowf(YZ, PD, 16 * J, 16 * n, lane));
+        mm_io(ac, dyf[n], zr);
+        mm_io(ar, zr, dyf[n]);
+        mm_io(pc, dof[n], zr);
+        mm_io(pr, zr, dof[n]);
+      }
+      ac = -ac;
+      ar = -ar;
+      if (J == I) {
+        ac = tri_col(ac, lane, true);
+        pc = tri_col(pc, lane, false);
+        ar = tri_row(ar, lane, true);
+        pr = tri_row(pr, lane, false);
+      }
+    }
+    dAc[J] = F::from(ac);
+    dAr[J] = F::from(ar);
+    dPc[J] = F::from(pc);
+    dPr[J] = F::from(pr);
+  }
+
+  // ---- contributions to dq (cq), de (ce), dk (ck) and d g_C (kb term)
+  f32x4 cq[NK], ce[NK], ck[NK];
   // S and dH tiles of row tile kk + 1 are loaded while row tile kk is multiplied
   F scur[NK], hcur[NK], snxt[NK], hnxt[NK];
 #pragma unroll
@@ -580,10 +585,10 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
       if (J <= I) {
-        const f32x4 ktc = ld_colf(KT, PD, 16 * J, 16 * kk, lane);
+        const F ktc = F::from(ld_colf(KT, PD, 16 * J, 16 * kk, lane));
         f32x4 aq = zero4, ae = zero4;
-        mm<CT>(aq, ktc, dPr[J]);
-        mm<CT>(ae, ktc, dAr[J]);
+        mm_io(aq, ktc, dPr[J]);
+        mm_io(ae, ktc, dAr[J]);
         const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
         cq[kk] += aq * sc;
         ce[kk] += ae * sc;
@@ -627,8 +632,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
         for (int kk = 0; kk < NK; ++kk) {
           const float f = colscale(J, kk);
           f32x4 acc = zero4;
-          mm<CT>(acc, qrc[kk] * f, dPc[J]);
-          mm<CT>(acc, erc[kk] * f, dAc[J]);
+          mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
+          mm_io(acc, F::from(erc[kk] * f), dAc[J]);
           f32x4 *p = reinterpret_cast<f32x4 *>(dKacc) + (J * NK + kk) * 64 + lane;
           *p = (d == 0) ? acc : (*p + acc);
         }
