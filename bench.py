@@ -443,6 +443,11 @@ def main() -> int:
         bprof = g.profile_read(reset=True)
         g.profile_enable(False)
         bkern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in bprof.items()}
+        # the same backward for KDA inputs (b = w = beta per (token, head))
+        kin = dict(dev, b=dev["b"][..., 0].contiguous(), w=dev["b"][..., 0].contiguous())
+        kout = dict(gout, db=torch.empty_like(kin["b"]), dw=torch.empty_like(kin["w"]))
+        sec_bk = timed_steps(lambda: g.chunk_bwd(*(kin[x] for x in NAMES), dout, chunk=C, workspace=wsb, out=kout),
+                             bsteps, 2)
         bbyt = bwd_bytes_per_token_head(d, C)
         bdom = max(bkern, key=lambda k: bkern[k]["avg_us"])
         bach = bbyt[bdom] * tok_heads / (bkern[bdom]["avg_us"] * 1e-6) / 1e9
@@ -451,6 +456,8 @@ def main() -> int:
             "steps": bsteps, "ms_per_step": round(sec_b * 1e3, 4),
             "tokens_per_s": round(B * T / sec_b, 1),
             "time_over_forward": round(sec_b / sec, 3),
+            "kda_ms_per_step": round(sec_bk * 1e3, 4),
+            "gdn2_over_kda_time": round(sec_b / sec_bk, 4),
             "path_algorithmic_bytes": int(bbyt["path"] * tok_heads),
             "path_hbm_frac": round(bbyt["path"] * tok_heads / sec_b / 1e9 / HBM_PEAK_GBS, 4),
             "kernels": bkern,

@@ -191,23 +191,28 @@ def bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int,
 
 
 def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
-              chunk: int = 64, workspace=None, out=None, want_dS0: bool = True):
-    """Chunked backward of ``chunk_fwd`` (per-channel gates, prepared inputs).
-    Given dL/do (``dout``, like o) and dL/dS_final (or None for zero), returns
-    a dict with dq, dk, dv, dalpha, db, dw (each like its input) and dS0
+              chunk: int = 64, workspace=None, out=None, want_dS0: bool = True,
+              layer_prep: bool = False):
+    """Chunked backward of ``chunk_fwd``, for the same input modes (b, w,
+    alpha per channel or [B, T, H]; ``layer_prep`` for the raw layer
+    inputs).  Given dL/do (``dout``, like o) and dL/dS_final (or None for
+    zero), returns a dict with dq, dk, dv, dalpha, db, dw (each like its
+    input: the gradient with respect to the input as given) and dS0
     ([N, H, dk, dv] float32, or None when ``want_dS0`` is False).  ``out``
     may hold preallocated tensors under those names."""
     _require_device(q, k, v, alpha, b, w, dout, S0, dS_final, cu_seqlens)
     dt = _dtype_code(q)
-    for t in (k, v, alpha, b, w, dout):
+    for t in (k, v, b, w, dout) + (() if layer_prep else (alpha,)):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, alpha, b, w, dout must share one dtype")
+    if layer_prep and alpha.dtype != torch.float32:
+        raise TypeError("with layer_prep, alpha is the float32 log-decay")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    for t, name, full in ((alpha, "alpha", dk), (b, "b", dk), (k, "k", dk), (v, "v", dv), (w, "w", dv),
-                          (dout, "dout", dv)):
+    for t, name, full in ((k, "k", dk), (v, "v", dv), (dout, "dout", dv)):
         if tuple(t.shape) != (B, T, H, full):
             raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}]")
+    flags = _gate_flags(q, v, alpha, b, w) | (FLAG_LAYER_PREP if layer_prep else 0)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
@@ -230,7 +235,7 @@ def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=Non
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     _check(lib().gdn2_chunk_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(cu_seqlens),
-        B, T, H, dk, dv, ns, chunk, dt, 0, _ptr(dout), _ptr(dS_final),
+        B, T, H, dk, dv, ns, chunk, dt, flags, _ptr(dout), _ptr(dS_final),
         _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]),
         _ptr(out["dw"]), _ptr(out.get("dS0")), _ptr(workspace), workspace.numel(), _stream()))
     out.setdefault("dS0", None)

@@ -489,10 +489,10 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
                              void *workspace, size_t workspace_bytes, void *stream) {
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: unknown dtype %d", static_cast<int>(dt));
-  if (flags != 0)
+  const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
+  if (flags & ~gate_flags)
     return fail(GDN2_ERR_UNSUPPORTED,
-                "gdn2_chunk_bwd: flags 0x%x: the backward takes per-channel gates and prepared inputs only",
-                flags);
+                "gdn2_chunk_bwd: flags 0x%x: only the gate layout and layer prep flags apply to the backward", flags);
   if (B <= 0 || T < 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: bad sizes B=%d T=%d H=%d", B, T, H);
   if (dk != dv || !supported_dim(dk))
@@ -550,7 +550,10 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   a.o = nullptr;
   a.S_final = nullptr;
   a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
-  a.gates = 0;
+  a.gates = ((flags & GDN2_FLAG_SCALAR_B) ? gdn2::GATE_SCALAR_B : 0u) |
+            ((flags & GDN2_FLAG_SCALAR_W) ? gdn2::GATE_SCALAR_W : 0u) |
+            ((flags & GDN2_FLAG_SCALAR_ALPHA) ? gdn2::GATE_SCALAR_ALPHA : 0u) |
+            ((flags & GDN2_FLAG_LAYER_PREP) ? gdn2::GATE_LAYER_PREP : 0u);
   char *ws = static_cast<char *>(workspace);
   a.offsets = packed ? reinterpret_cast<int32_t *>(ws) : nullptr;
   a.blocks = ws + plan.table;

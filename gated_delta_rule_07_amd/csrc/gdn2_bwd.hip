@@ -268,8 +268,14 @@ __device__ __forceinline__ f32x4 tri_row(f32x4 v, int lane, bool strict) {
 // the key's sub-block J: K~_s = k_s e^{rho_J - g_s} <= 1 is stored once per
 // row, and the query/erase side of row t takes e^{g_t - rho_J} (<= 1 for
 // J < I, bounded by one sub-block's decay for J = I).
-template <typename IO, int D, int C, typename CT>
+// Input modes of the gradient kernel: per-channel inputs, KDA (b and w per
+// (token, head)), Gated DeltaNet (also alpha), and any other combination of
+// the gate layouts and layer prep read from chunk_args::gates at run time.
+enum { BG_PLAIN = 0, BG_KDA = 1, BG_GDN = 2, BG_FLAGS = 3 };
+
+template <typename IO, int D, int C, typename CT, int GM>
 __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args ba) {
+  constexpr bool GN = GM != BG_PLAIN;
   const chunk_args &a = ba.f;
   typedef bwd_lds<D, C> L;
   constexpr int NB = C / 16, NK = D / 16, PD = L::PD, PC = L::PC;
@@ -317,33 +323,131 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       y[i] = __expf(x[i]);
     return y;
   };
+  // Input modes (GN): b, w or alpha given per (token, head) ([B, T, H], one
+  // value broadcast over the channels), and layer prep (q, k raw, b and w
+  // logits, alpha as the float32 natural-log decay).  Every read of an input
+  // goes through these, which give the recurrence's inputs; without GN they
+  // are the plain per-channel loads.
+  const uint32_t gates = GM == BG_FLAGS ? a.gates
+                        : GM == BG_KDA  ? (GATE_SCALAR_B | GATE_SCALAR_W)
+                        : GM == BG_GDN  ? (GATE_SCALAR_B | GATE_SCALAR_W | GATE_SCALAR_ALPHA)
+                                        : 0u;
+  const bool LPm = (gates & GATE_LAYER_PREP) != 0, SBm = (gates & GATE_SCALAR_B) != 0,
+             SWm = (gates & GATE_SCALAR_W) != 0, SAm = (gates & GATE_SCALAR_ALPHA) != 0;
+  const size_t srow = row / D;  // index of this row in a [B, T, H] input
+  const float *__restrict__ lga = static_cast<const float *>(a.al);
+  float qs = 1.f, ks = 1.f;  // 1 / |q|, 1 / |k| of this row (layer prep)
+  auto sig4 = [](f32x4 x) {
+    f32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      y[i] = 1.f / (1.f + __expf(-x[i]));
+    return y;
+  };
+  auto ld_gate = [&](const IO *p, bool scalar, int c0) -> f32x4 {
+    f32x4 x;
+    if (GN && scalar) {
+      const float e = io<IO>::to_f(p[srow]);
+      x = f32x4{e, e, e, e};
+    } else {
+      x = io<IO>::load4(p + row + c0);
+    }
+    return (GN && LPm) ? sig4(x) : x;
+  };
+  auto ld_b = [&](int c0) { return ld_gate(b, SBm, c0); };
+  auto ld_w = [&](int c0) { return ld_gate(w, SWm, c0); };
+  // alpha itself (not under layer prep)
+  auto ld_alpha = [&](int c0) -> f32x4 {
+    if (GN && SAm) {
+      const float e = io<IO>::to_f(al[srow]);
+      return f32x4{e, e, e, e};
+    }
+    return io<IO>::load4(al + row + c0);
+  };
+  // ln(alpha)
+  auto ld_logalpha = [&](int c0) -> f32x4 {
+    if (GN && LPm) {
+      if (SAm) {
+        const float e = lga[srow];
+        return f32x4{e, e, e, e};
+      }
+      return *reinterpret_cast<const f32x4 *>(lga + row + c0);
+    }
+    f32x4 x = ld_alpha(c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = __logf(x[i]);
+    return x;
+  };
+  // sum over the row's D channels: this lane's four of tile kk and the three
+  // other lanes of the row (lanes m + 16 g)
+  auto row_sum = [](float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+  };
 
   // ---- rows of the sub-block; g = cumulative ln(alpha) within the chunk
   f32x4 qv[NK], kv[NK], ev[NK], gv[NK];
   {
     // every row load first, then the arithmetic
     raw4<IO> rq[NK], rk[NK], rb[NK], ra[NK];
+    if constexpr (!GN) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const int c0 = 16 * kk + 4 * g;
-      rq[kk] = raw4<IO>::ld(q + row + c0);
-      rk[kk] = raw4<IO>::ld(k + row + c0);
-      rb[kk] = raw4<IO>::ld(b + row + c0);
-      ra[kk] = raw4<IO>::ld(al + row + c0);
+      for (int kk = 0; kk < NK; ++kk) {
+        const int c0 = 16 * kk + 4 * g;
+        rq[kk] = raw4<IO>::ld(q + row + c0);
+        rk[kk] = raw4<IO>::ld(k + row + c0);
+        rb[kk] = raw4<IO>::ld(b + row + c0);
+        ra[kk] = raw4<IO>::ld(al + row + c0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const int c0 = 16 * kk + 4 * g;
+        rq[kk] = raw4<IO>::ld(q + row + c0);
+        rk[kk] = raw4<IO>::ld(k + row + c0);
+      }
+      if (LPm) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const f32x4 x = rq[kk].f(), y = rk[kk].f();
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sq += x[i] * x[i];
+            sk += y[i] * y[i];
+          }
+        }
+        sq = row_sum(sq);
+        sk = row_sum(sk);
+        qs = sq > 0.f ? __frsqrt_rn(sq) : 0.f;
+        ks = sk > 0.f ? __frsqrt_rn(sk) : 0.f;
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      f32x4 qq = rq[kk].f(), kq = rk[kk].f(), bq = rb[kk].f(), aq = ra[kk].f();
+      const int c0 = 16 * kk + 4 * g;
+      f32x4 qq = rq[kk].f() * qs, kq = rk[kk].f() * ks, bq, lq;
+      if constexpr (!GN) {
+        bq = rb[kk].f();
+        lq = ra[kk].f();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lq[i] = __logf(lq[i]);
+      } else {
+        bq = ld_b(c0);
+        lq = ld_logalpha(c0);
+      }
       if (!valid) {
-        qq = kq = bq = zero4;
-        aq = f32x4{1.f, 1.f, 1.f, 1.f};
+        qq = kq = bq = lq = zero4;
       }
       qv[kk] = qq;
       kv[kk] = kq;
       ev[kk] = bq * kq;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        gv[kk][i] = row16_inclusive_scan(__logf(aq[i]));
+        gv[kk][i] = row16_inclusive_scan(lq[i]);
     }
   }
   if (m == 15) {
@@ -418,7 +522,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         cur[kk] = nxt[kk];
-      f32x4 u = io<IO>::load4(w + row + 16 * n + 4 * g) * io<IO>::load4(v + row + 16 * n + 4 * g);
+      f32x4 u = ld_w(16 * n + 4 * g) * io<IO>::load4(v + row + 16 * n + 4 * g);
       zv[n] = (valid ? u : zero4) - acc;
       st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
     }
@@ -499,16 +603,36 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   // dY_I = sum_{J >= I} T_JI^T dZ_J;  dv = dY (.) w, dw = dY (.) v
   IO *dq = static_cast<IO *>(ba.dq), *dk = static_cast<IO *>(ba.dk), *db = static_cast<IO *>(ba.db);
   IO *dal = static_cast<IO *>(ba.dal), *dvo = static_cast<IO *>(ba.dv), *dwo = static_cast<IO *>(ba.dw);
+  float dws = 0.f;  // dw summed over the channels (w per (token, head))
 #pragma unroll
   for (int n = 0; n < NK; ++n) {
     f32x4 acc = zero4;
     for (int J = I; J < NB; ++J)
       mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sT, PC, 16 * J, 16 * I, lane));
     dyv[n] = acc;
-    if (valid) {
-      io<IO>::store4(dvo + row + 16 * n + 4 * g, acc * io<IO>::load4(w + row + 16 * n + 4 * g));
-      io<IO>::store4(dwo + row + 16 * n + 4 * g, acc * io<IO>::load4(v + row + 16 * n + 4 * g));
+    const int c0 = 16 * n + 4 * g;
+    if constexpr (!GN) {
+      if (valid) {
+        io<IO>::store4(dvo + row + c0, acc * io<IO>::load4(w + row + c0));
+        io<IO>::store4(dwo + row + c0, acc * io<IO>::load4(v + row + c0));
+      }
+    } else {
+      const f32x4 wq = ld_w(c0);
+      f32x4 dwq = acc * io<IO>::load4(v + row + c0);
+      if (LPm)
+        dwq *= wq * (f32x4{1.f, 1.f, 1.f, 1.f} - wq);  // through the sigmoid
+      if (valid) {
+        io<IO>::store4(dvo + row + c0, acc * wq);
+        if (!SWm)
+          io<IO>::store4(dwo + row + c0, dwq);
+      }
+      dws += (dwq[0] + dwq[1]) + (dwq[2] + dwq[3]);
     }
+  }
+  if constexpr (GN) {
+    dws = row_sum(dws);
+    if (SWm && valid && g == 0)
+      dwo[srow] = io<IO>::from_f(dws);
   }
 
   // ---- dA_IJ = -dY_I Z_J^T, dP_IJ = dO_I Z_J^T (J <= I), as ColFrag (c) and RowFrag (r),
@@ -606,13 +730,15 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       const int c0 = 16 * kk + 4 * g;
       rq[kk] = raw4<IO>::ld(q + row + c0);
       rk[kk] = raw4<IO>::ld(k + row + c0);
-      rb[kk] = raw4<IO>::ld(b + row + c0);
+      if constexpr (!GN)
+        rb[kk] = raw4<IO>::ld(b + row + c0);
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const f32x4 sc = valid ? ex4(gv[kk] - rho_end(I, kk)) : zero4;
-      qrc[kk] = transpose_f32(rq[kk].f() * sc, lane);
-      erc[kk] = transpose_f32(rb[kk].f() * rk[kk].f() * sc, lane);
+      const f32x4 bq = GN ? ld_b(16 * kk + 4 * g) : rb[kk].f();
+      qrc[kk] = transpose_f32(rq[kk].f() * (qs * sc), lane);
+      erc[kk] = transpose_f32(bq * rk[kk].f() * (ks * sc), lane);
     }
   }
   // column scale e^{rho_I - rho_J} of ColFrag element (lane column c)
@@ -665,46 +791,92 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   }
   f32x4 dg[NK];
   raw4<IO> ral[NK];  // alpha of the rows, for d alpha at the end
+  if constexpr (!GN) {
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-    ral[kk] = raw4<IO>::ld(al + row + 16 * kk + 4 * g);
+    for (int kk = 0; kk < NK; ++kk)
+      ral[kk] = raw4<IO>::ld(al + row + 16 * kk + 4 * g);
+  }
   // q, k, b of row tile kk + 1 are loaded while tile kk is mapped
-  raw4<IO> nq = raw4<IO>::ld(q + row + 4 * g), nk = raw4<IO>::ld(k + row + 4 * g),
-           nb = raw4<IO>::ld(b + row + 4 * g);
+  raw4<IO> nq = raw4<IO>::ld(q + row + 4 * g), nk = raw4<IO>::ld(k + row + 4 * g), nb;
+  if constexpr (!GN)
+    nb = raw4<IO>::ld(b + row + 4 * g);
+  float dotq = 0.f, dotk = 0.f, dbs = 0.f;  // GN: row sums for layer prep and per-(token, head) b
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const f32x4 dkt = reinterpret_cast<const f32x4 *>(dKacc)[(I * NK + kk) * 64 + lane];
     const f32x4 ckt = dkt * ex4(rho_end(I, kk) - gv[kk]);
     const int c0 = 16 * kk + 4 * g;
-    f32x4 qq = nq.f(), kq = nk.f(), bq = nb.f();
+    f32x4 qq = nq.f() * qs, kq = nk.f() * ks, bq = GN ? ld_b(c0) : nb.f();
     if (!valid)
       qq = kq = bq = zero4;
     if (kk + 1 < NK) {
       nq = raw4<IO>::ld(q + row + c0 + 16);
       nk = raw4<IO>::ld(k + row + c0 + 16);
-      nb = raw4<IO>::ld(b + row + c0 + 16);
+      if constexpr (!GN)
+        nb = raw4<IO>::ld(b + row + c0 + 16);
     }
     const f32x4 kbt = kq * ck[kk];  // k (.) dKB-contribution, part of d g_C
     dg[kk] = qq * cq[kk] + bq * kq * ce[kk] - kq * (ck[kk] + ckt);
-    if (valid) {
-      io<IO>::store4(dq + row + c0, cq[kk]);
-      io<IO>::store4(dk + row + c0, ck[kk] + ckt + bq * ce[kk]);
-      io<IO>::store4(db + row + c0, kq * ce[kk]);
+    if constexpr (!GN) {
+      if (valid) {
+        io<IO>::store4(dq + row + c0, cq[kk]);
+        io<IO>::store4(dk + row + c0, ck[kk] + ckt + bq * ce[kk]);
+        io<IO>::store4(db + row + c0, kq * ce[kk]);
+      }
+    } else {
+      // gradients with respect to the recurrence's k and b, kept for the
+      // second pass (ck, ce are not read again otherwise)
+      ck[kk] = ck[kk] + ckt + bq * ce[kk];
+      ce[kk] = kq * ce[kk];
+      if (LPm)
+        ce[kk] *= bq * (f32x4{1.f, 1.f, 1.f, 1.f} - bq);  // through the sigmoid
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dotq += qq[i] * cq[kk][i];
+        dotk += kq[i] * ck[kk][i];
+        dbs += ce[kk][i];
+      }
     }
     // sub-block sums over the 16 rows: kb terms and dg
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float ks = row16_inclusive_scan(kbt[i]);
+      const float kbsc = row16_inclusive_scan(kbt[i]);
       const float gs = row16_inclusive_scan(dg[kk][i]);
       if (m == 15) {
-        kbs[I * D + c0 + i] = ks;
+        kbs[I * D + c0 + i] = kbsc;
         gtot[I * D + c0 + i] = gs;
       }
       dg[kk][i] = gs;  // in-block inclusive prefix of dg
     }
   }
+  if constexpr (GN) {
+    // second pass: through the L2 normalisation (layer prep),
+    // dx = (dq - q (q . dq)) / |x|, and the stores
+    dotq = row_sum(dotq);
+    dotk = row_sum(dotk);
+    dbs = row_sum(dbs);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c0 = 16 * kk + 4 * g;
+      f32x4 dqv = cq[kk], dkv = ck[kk];
+      if (LPm) {
+        const f32x4 qh = raw4<IO>::ld(q + row + c0).f() * qs, kh = raw4<IO>::ld(k + row + c0).f() * ks;
+        dqv = (dqv - qh * dotq) * qs;
+        dkv = (dkv - kh * dotk) * ks;
+      }
+      if (valid) {
+        io<IO>::store4(dq + row + c0, dqv);
+        io<IO>::store4(dk + row + c0, dkv);
+        if (!SBm)
+          io<IO>::store4(db + row + c0, ce[kk]);
+      }
+    }
+    if (SBm && valid && g == 0)
+      db[srow] = io<IO>::from_f(dbs);
+  }
   lds_barrier();
   // d ln(alpha_t) = sum_{s >= t} dg_s + d g_C, d g_C = gamma dgamma + sum of the kb terms
+  float das = 0.f;  // GN: d alpha summed over the channels
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const int c0 = 16 * kk + 4 * g;
@@ -725,8 +897,29 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       mine[i] = dg[kk][i] - (m == 0 ? 0.f : prev);
     }
     const f32x4 dl = own - dg[kk] + mine + tail + dgc;
-    if (valid)
-      io<IO>::store4(dal + row + c0, dl / ral[kk].f());
+    if constexpr (!GN) {
+      if (valid)
+        io<IO>::store4(dal + row + c0, dl / ral[kk].f());
+    } else {
+      // layer prep: the input is ln(alpha) (float32), whose gradient is dl
+      const f32x4 da = LPm ? dl : dl / ld_alpha(c0);
+      if (valid && !SAm) {
+        if (LPm)
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(ba.dal) + row + c0) = da;
+        else
+          io<IO>::store4(dal + row + c0, da);
+      }
+      das += (da[0] + da[1]) + (da[2] + da[3]);
+    }
+  }
+  if constexpr (GN) {
+    das = row_sum(das);
+    if (SAm && valid && g == 0) {
+      if (LPm)
+        static_cast<float *>(ba.dal)[srow] = das;
+      else
+        dal[srow] = io<IO>::from_f(das);
+    }
   }
 }
 
@@ -738,8 +931,16 @@ template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args
 
 template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st) {
   const long n = static_cast<long>(a.f.num_slots) * a.f.H;
-  hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO>), dim3(static_cast<unsigned>(n)), dim3(64 * (C / 16)),
-                     0, st, a);
+  const dim3 grid(static_cast<unsigned>(n)), block(64 * (C / 16));
+  const uint32_t kda = GATE_SCALAR_B | GATE_SCALAR_W, gdn = kda | GATE_SCALAR_ALPHA;
+  if (a.f.gates == 0)
+    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_PLAIN>), grid, block, 0, st, a);
+  else if (a.f.gates == kda)
+    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_KDA>), grid, block, 0, st, a);
+  else if (a.f.gates == gdn)
+    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_GDN>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_FLAGS>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -158,15 +158,22 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * paragraph: the gate-aware backward; aixai.ru blog, section on how the
  * method is implemented in practice).
  *   q .. cu_seqlens, B .. dt : the forward's inputs and sizes.
- *   flags     : must be 0 (per-channel gates and prepared inputs only; the
- *               gate layout, layer prep and path flags of the forward return
- *               GDN2_ERR_UNSUPPORTED).
+ *   flags     : GDN2_FLAG_SCALAR_B / _W / _ALPHA and GDN2_FLAG_LAYER_PREP,
+ *               with the forward's meaning (inputs given per (token, head),
+ *               or the raw layer inputs); the path and rule flags return
+ *               GDN2_ERR_UNSUPPORTED.
  *   dout      : dL/do [B, T, H, dv], element type dt.
  *   dS_final  : dL/dS_final [N, H, dk, dv] float32, or NULL for zero.
- *   dq, dk_out, dv_out, dalpha, db, dw : outputs (the gradients of q, k,
- *               v, alpha, b, w), each with its input's layout and
- *               element type dt (bfloat16 rounded to nearest even).  dalpha is
- *               the gradient with respect to alpha itself.
+ *   dq, dk_out, dv_out, dalpha, db, dw : outputs, the gradients with respect
+ *               to the inputs as given: each has its input's layout and
+ *               element type (dt; under layer prep dalpha is float32 like
+ *               the log-decay input), bfloat16 rounded to nearest even.
+ *               Without layer prep dalpha is the gradient with respect to
+ *               alpha itself; with it, with respect to ln(alpha), and dq,
+ *               dk, db, dw are taken through the L2 normalisation and the
+ *               sigmoids (a zero q or k row gets a zero gradient).  An input
+ *               given per (token, head) gets the sum of its channels'
+ *               gradients.
  *   dS0       : dL/dS0 [N, H, dk, dv] float32, or NULL.
  *   workspace : device scratch of at least gdn2_chunk_bwd_workspace_bytes(...)
  *               bytes; its contents on entry are irrelevant.

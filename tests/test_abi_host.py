@@ -120,8 +120,8 @@ def test_bwd_rejects_before_launch(L):
     assert call_bwd(L, dt=7) == 2
     assert call_bwd(L, B=0) == 1
     assert call_bwd(L, T=-1) == 1
-    # the backward takes no forward path, gate layout or layer-prep flag
-    for flag in (1 << 0, 1 << 1, 1 << 2, 1 << 3, 1 << 4, 1 << 5, 1 << 6):
+    # the backward takes no forward path or rule flag
+    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 8):
         assert call_bwd(L, flags=flag) == 2
     assert call_bwd(L, dout=0x10008) == 1      # misaligned
     assert call_bwd(L, ws_bytes=16) == 3

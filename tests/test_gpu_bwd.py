@@ -122,3 +122,77 @@ def test_bwd_config2_sampled_units(g):
                          S0=S0, dS_final=grads["dS_final"][bb:bb + 1, hh:hh + 1].contiguous())
         sel = lambda name, x: x[bb:bb + 1, hh:hh + 1] if name == "dS0" else x[bb:bb + 1, :, hh:hh + 1]
         check(got, ref, TOL["bf16"], f"cfg2 b={bb} h={hh}", sel=sel)
+
+
+def gpu_bwd_raw(g, inp, grads, chunk, layer_prep=False):
+    d = {n: inp[n].cuda() for n in NAMES}
+    S0 = inp.get("S0")
+    dSf = grads["dS_final"]
+    out = g.chunk_bwd(*(d[n] for n in NAMES), grads["dout"].cuda(),
+                      S0=None if S0 is None else S0.cuda(), dS_final=None if dSf is None else dSf.cuda(),
+                      chunk=chunk, layer_prep=layer_prep)
+    torch.cuda.synchronize()
+    for name, x in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dalpha", "alpha"), ("db", "b"), ("dw", "w")):
+        assert tuple(out[name].shape) == tuple(inp[x].shape) and out[name].dtype == inp[x].dtype, name
+    return {k: v.float().cpu().numpy() for k, v in out.items() if v is not None}
+
+
+# Gates per (token, head): the GPU reads the compact [B, T, H] tensors; the
+# oracle gets the same values repeated over the channels and its per-channel
+# gradients are summed over them (oracle/layer_prep.py sum_to_layout).
+GATE_CASES = {"kda": ("b", "w"), "gdn": ("b", "w", "alpha"), "b_only": ("b",), "w_only": ("w",)}
+
+
+@pytest.mark.parametrize("dtype,d,T,chunk", [("f32", 64, 190, 64), ("bf16", 128, 200, 64), ("bf16", 32, 77, 16)])
+@pytest.mark.parametrize("case", list(GATE_CASES))
+def test_bwd_per_token_gates(g, case, dtype, d, T, chunk):
+    from oracle import layer_prep as lp
+    inp = gi.make_chunk_inputs(2, T, 3, d, d, dtype, seed=900 + T, s0="normal",
+                               scalar_beta=(case in ("kda", "gdn")))
+    grads = gi.make_bwd_grads(2, T, 3, d, d, dtype, seed=900 + T)
+    full, compact = dict(inp), dict(inp)
+    for x in GATE_CASES[case]:
+        s = inp[x][..., 0].contiguous()
+        compact[x] = s
+        full[x] = s[..., None].expand_as(inp[x]).contiguous()
+    print(f"case bwd gates {case} {dtype} d={d} C={chunk}", flush=True)
+    got = gpu_bwd_raw(g, compact, grads, chunk)
+    ref = oracle.bwd(*(full[n] for n in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"])
+    for name, x in (("db", "b"), ("dw", "w"), ("dalpha", "alpha")):
+        ref[name] = lp.sum_to_layout(ref[name], compact[x].float().numpy())
+    check(got, ref, TOL[dtype], f"bwd gates {case} {dtype} d={d}")
+
+
+# Layer prep: raw q, k, gate logits and the float32 log-decay go in; the
+# oracle prepares them in float64, takes the recurrence's gradients and
+# carries them back through the prep (oracle/layer_prep.py layer_prep_bwd).
+@pytest.mark.parametrize("dtype,d,T,chunk", [("f32", 64, 150, 64), ("bf16", 128, 200, 64), ("bf16", 64, 77, 16)])
+@pytest.mark.parametrize("scalar", [False, True])
+def test_bwd_layer_prep(g, dtype, d, T, chunk, scalar):
+    from oracle import layer_prep as lp
+    raw = gi.make_layer_inputs(2, T, 3, d, d, dtype, seed=950 + T, s0="normal", scalar_beta=scalar)
+    grads = gi.make_bwd_grads(2, T, 3, d, d, dtype, seed=950 + T)
+    prep = lp.layer_prep(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"])
+    full = {x: (prep[x][..., None] * np.ones(d) if prep[x].ndim == 3 else prep[x])
+            for x in ("q", "k", "alpha", "b", "w")}
+    print(f"case bwd layer prep {dtype} d={d} C={chunk} scalar={scalar}", flush=True)
+    got = gpu_bwd_raw(g, raw, grads, chunk, layer_prep=True)
+    gp = oracle.bwd(full["q"], full["k"], raw["v"], full["alpha"], full["b"], full["w"], grads["dout"],
+                    S0=raw["S0"], dS_final=grads["dS_final"])
+    ref = lp.layer_prep_bwd(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"], gp)
+    ref["dS0"] = gp["dS0"]
+    check(got, ref, TOL[dtype], f"bwd layer prep {dtype} d={d} scalar={scalar}")
+
+
+def test_bwd_rejects_path_and_rule_flags(g):
+    inp = gi.make_chunk_inputs(1, 32, 1, 16, 16, "f32", seed=5)
+    grads = gi.make_bwd_grads(1, 32, 1, 16, 16, "f32", seed=5)
+    d = {n: inp[n].cuda() for n in NAMES}
+    lib = g.lib()
+    ws = torch.empty(g.bwd_workspace_bytes(1, 32, 1, 16, 16, 0, 16, torch.float32), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(d[n]) for n in NAMES]
+    for flag in (g.FLAG_RECURRENT, g.FLAG_FUSED, g.FLAG_RULE_R1):
+        st = lib.gdn2_chunk_bwd(*(d[n].data_ptr() for n in NAMES), None, None, 1, 32, 1, 16, 16, 0, 16, 0, flag,
+                                grads["dout"].cuda().data_ptr(), None, *(o.data_ptr() for o in outs), None,
+                                ws.data_ptr(), ws.numel(), None)
+        assert st == 2

@@ -129,3 +129,102 @@ def test_bwd_zero_incoming_gradient_gives_zero():
     g = oracle.bwd(*(x[n] for n in NAMES), np.zeros((1, 9, 2, 3)))
     for key, val in g.items():
         assert np.all(val == 0.0), key
+
+
+def test_layer_prep_bwd_matches_finite_differences():
+    """The chain rule of oracle/layer_prep.py against central differences of
+    the loss through layer_prep and the forward oracle, for per-channel and
+    per-(token, head) gate layouts."""
+    from oracle import layer_prep as lp
+    rng = np.random.default_rng(15)
+    B, T, H, dk, dv = 1, 6, 1, 3, 2
+    for scalar in (False, True):
+        gshape = (B, T, H) if scalar else None
+        raw = {
+            "q": rng.standard_normal((B, T, H, dk)) * 2.0,
+            "k": rng.standard_normal((B, T, H, dk)) * 0.7,
+            "v": rng.standard_normal((B, T, H, dv)),
+            "alpha": np.log(1.0 / (1.0 + np.exp(-rng.normal(2.0, 1.0, gshape or (B, T, H, dk))))),
+            "b": rng.standard_normal(gshape or (B, T, H, dk)),
+            "w": rng.standard_normal(gshape or (B, T, H, dv)),
+        }
+        raw["q"][0, 2, 0] = 0.0  # a zero row stays zero, and so does its gradient
+        S0 = rng.normal(0.0, 0.3, (B, H, dk, dv))
+        do = rng.standard_normal((B, T, H, dv))
+        dSf = rng.standard_normal((B, H, dk, dv))
+
+        def prepared(r):
+            p = lp.layer_prep(r["q"], r["k"], r["alpha"], r["b"], r["w"])
+            full = {x: (p[x][..., None] * np.ones(dk if x in ("alpha", "b") else dv) if p[x].ndim == 3 else p[x])
+                    for x in ("q", "k", "alpha", "b", "w")}
+            full["v"] = r["v"]
+            return full
+
+        def L(r):
+            p = prepared(r)
+            o, Sf = oracle.fwd(*(p[n] for n in NAMES), S0=S0)
+            return float(np.sum(do * o) + np.sum(dSf * Sf))
+
+        p = prepared(raw)
+        gp = oracle.bwd(*(p[n] for n in NAMES), do, S0=S0, dS_final=dSf)
+        g = lp.layer_prep_bwd(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"], gp)
+        h = 1e-6
+        for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("alpha", "dalpha"), ("b", "db"), ("w", "dw")):
+            arr = raw[name]
+            fd = np.zeros_like(arr)
+            skip = np.zeros(arr.shape, dtype=bool)
+            if name == "q":  # normalisation is not differentiable at the zero row
+                skip[0, 2, 0] = True
+            for idx in np.ndindex(arr.shape):
+                if skip[idx]:
+                    continue
+                keep = arr[idx]
+                arr[idx] = keep + h
+                lp_ = L(raw)
+                arr[idx] = keep - h
+                lm = L(raw)
+                arr[idx] = keep
+                fd[idx] = (lp_ - lm) / (2 * h)
+            assert g[gname].shape == arr.shape, name
+            err = np.max(np.abs(np.where(skip, 0.0, fd - g[gname]))) / np.max(np.abs(fd))
+            assert err < 1e-7, (scalar, name, err)
+        assert np.all(g["dq"][0, 2, 0] == 0.0)
+
+
+def test_per_token_gate_gradients_are_channel_sums():
+    """Gates given per (token, head) and broadcast over the channels: their
+    gradient (oracle.bwd per channel, summed by sum_to_layout) against
+    central differences of the loss in the compact gate."""
+    from oracle import layer_prep as lp
+    rng = np.random.default_rng(16)
+    B, T, H, dk, dv = 1, 7, 2, 3, 4
+    x = rand_inputs(rng, B, T, H, dk, dv)
+    compact = {"b": rng.uniform(0.1, 0.9, (B, T, H)), "w": rng.uniform(0.1, 0.9, (B, T, H)),
+               "alpha": rng.uniform(0.5, 0.99, (B, T, H))}
+    do = rng.standard_normal((B, T, H, dv))
+
+    def full(c):
+        f = dict(x)
+        f["b"] = np.repeat(c["b"][..., None], dk, -1)
+        f["w"] = np.repeat(c["w"][..., None], dv, -1)
+        f["alpha"] = np.repeat(c["alpha"][..., None], dk, -1)
+        return f
+
+    f = full(compact)
+    gfull = oracle.bwd(*(f[n] for n in NAMES), do)
+    h = 1e-6
+    for name in ("b", "w", "alpha"):
+        got = lp.sum_to_layout(gfull["d" + name], compact[name])
+        assert got.shape == compact[name].shape
+        fd = np.zeros_like(compact[name])
+        for idx in np.ndindex(fd.shape):
+            keep = compact[name][idx]
+            compact[name][idx] = keep + h
+            fp = full(compact)
+            lpl = float(np.sum(do * oracle.fwd(*(fp[n] for n in NAMES))[0]))
+            compact[name][idx] = keep - h
+            fm = full(compact)
+            lmi = float(np.sum(do * oracle.fwd(*(fm[n] for n in NAMES))[0]))
+            compact[name][idx] = keep
+            fd[idx] = (lpl - lmi) / (2 * h)
+        assert np.max(np.abs(fd - got)) / np.max(np.abs(fd)) < 1e-7, name
