@@ -466,25 +466,36 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   for (int kk = 0; kk < NK; ++kk)
     st_rowf(KT, PD, 16 * I, 16 * kk, lane, kv[kk] * ex4(rho_end(I, kk) - gv[kk]));
   lds_barrier();
-  for (int J = 0; J <= I; ++J) {
-    f32x4 aa = zero4, pp = zero4;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
-      const F kt = F::from(ld_rowf(KT, PD, 16 * J, 16 * kk, lane));
-      mm_io(aa, F::from(ev[kk] * sc), kt);
-      mm_io(pp, F::from(qv[kk] * sc), kt);
+  for (int J = 0; J < NB; ++J) {
+    if (J <= I) {  // J unrolled: the decay sums of rho_end become independent reads
+      f32x4 aa = zero4, pp = zero4;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
+        const F kt = F::from(ld_rowf(KT, PD, 16 * J, 16 * kk, lane));
+        mm_io(aa, F::from(ev[kk] * sc), kt);
+        mm_io(pp, F::from(qv[kk] * sc), kt);
+      }
+      if (J == I) {
+        aa = tri_col(aa, lane, true);
+        pp = tri_col(pp, lane, false);
+      }
+      st_colf(sA, PC, 16 * I, 16 * J, lane, aa);
+      st_colf(sP, PC, 16 * I, 16 * J, lane, pp);
     }
-    if (J == I) {
-      aa = tri_col(aa, lane, true);
-      pp = tri_col(pp, lane, false);
-    }
-    st_colf(sA, PC, 16 * I, 16 * J, lane, aa);
-    st_colf(sP, PC, 16 * I, 16 * J, lane, pp);
   }
   lds_barrier();
 
   // ---- diagonal blocks of T = (I + A)^{-1} (lane c < 16: column c), Y_I = U_I - ES_I S
+  // w and v of every column are loaded first: they arrive during the solve
+  raw4<IO> rw[NK], rv[NK];
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    const int c0 = 16 * n + 4 * g;
+    rw[n] = (GN && SWm) ? raw4<IO>::splat(w[srow]) : raw4<IO>::ld(w + row + c0);
+    rv[n] = raw4<IO>::ld(v + row + c0);
+  }
   if (lane < 16) {
     float x[16];
 #pragma unroll
@@ -522,7 +533,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         cur[kk] = nxt[kk];
-      f32x4 u = ld_w(16 * n + 4 * g) * io<IO>::load4(v + row + 16 * n + 4 * g);
+      f32x4 u = ((GN && LPm) ? sig4(rw[n].f()) : rw[n].f()) * rv[n].f();
       zv[n] = (valid ? u : zero4) - acc;
       st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
     }
@@ -606,6 +617,12 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   float dws = 0.f;  // dw summed over the channels (w per (token, head))
 #pragma unroll
   for (int n = 0; n < NK; ++n) {
+    const int c0 = 16 * n + 4 * g;
+    rw[n] = (GN && SWm) ? raw4<IO>::splat(w[srow]) : raw4<IO>::ld(w + row + c0);
+    rv[n] = raw4<IO>::ld(v + row + c0);
+  }
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
     f32x4 acc = zero4;
     for (int J = I; J < NB; ++J)
       mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sT, PC, 16 * J, 16 * I, lane));
@@ -613,12 +630,12 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     const int c0 = 16 * n + 4 * g;
     if constexpr (!GN) {
       if (valid) {
-        io<IO>::store4(dvo + row + c0, acc * io<IO>::load4(w + row + c0));
-        io<IO>::store4(dwo + row + c0, acc * io<IO>::load4(v + row + c0));
+        io<IO>::store4(dvo + row + c0, acc * rw[n].f());
+        io<IO>::store4(dwo + row + c0, acc * rv[n].f());
       }
     } else {
-      const f32x4 wq = ld_w(c0);
-      f32x4 dwq = acc * io<IO>::load4(v + row + c0);
+      const f32x4 wq = LPm ? sig4(rw[n].f()) : rw[n].f();
+      f32x4 dwq = acc * rv[n].f();
       if (LPm)
         dwq *= wq * (f32x4{1.f, 1.f, 1.f, 1.f} - wq);  // through the sigmoid
       if (valid) {
