@@ -737,8 +737,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     }
   }
 
-  // ---- dK~_J contributions of this sub-block's rows, accumulated in LDS in a
-  // fixed order (own rows first, then one block diagonal per round)
+  // ---- dK~_J contributions of this sub-block's rows, one LDS slot per
+  // (I, J <= I); the owner of J sums its slots in ascending I (a fixed order)
   f32x4 qrc[NK], erc[NK];  // ColFrag of q e^{g - rho_I} and e e^{g - rho_I}
   {
     raw4<IO> rq[NK], rk[NK], rb[NK];
@@ -758,32 +758,35 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       erc[kk] = transpose_f32(bq * rk[kk].f() * (ks * sc), lane);
     }
   }
-  // column scale e^{rho_I - rho_J} of ColFrag element (lane column c)
-  auto colscale = [&](int J, int kk) {
-    float r = 0.f;
-    for (int J2 = J + 1; J2 <= I; ++J2)
-      r += btot[J2 * D + 16 * kk + m];
-    return __expf(r);
+  lds_barrier();  // K~, T, P, Y/Z and dZ are no longer read: LDS from 0 holds the slots
+  static_assert((NB * (NB + 1) / 2) * NK * 256 <= L::BTOT, "dK~ slots fit below the sub-block sums");
+  auto dk_slot = [&](int I2, int J2, int kk) {
+    return reinterpret_cast<f32x4 *>(sm) + ((I2 * (I2 + 1) / 2 + J2) * NK + kk) * 64;
   };
-  lds_barrier();  // Z in YZ is no longer read
-  float *dKacc = YZ;
-  for (int d = 0; d < NB; ++d) {
+  {
+    // column scale e^{rho_I - rho_J} of ColFrag element (lane column c),
+    // summed up while J descends from I
+    float rs[NK];
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      if (I - J == d) {
+    for (int kk = 0; kk < NK; ++kk)
+      rs[kk] = 0.f;
+#pragma unroll
+    for (int J = NB - 1; J >= 0; --J) {
+      if (J <= I) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          const float f = colscale(J, kk);
+          if (J < I)
+            rs[kk] += btot[(J + 1) * D + 16 * kk + m];
+          const float f = __expf(rs[kk]);
           f32x4 acc = zero4;
           mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
           mm_io(acc, F::from(erc[kk] * f), dAc[J]);
-          f32x4 *p = reinterpret_cast<f32x4 *>(dKacc) + (J * NK + kk) * 64 + lane;
-          *p = (d == 0) ? acc : (*p + acc);
+          dk_slot(I, J, kk)[lane] = acc;
         }
       }
     }
-    lds_barrier();
   }
+  lds_barrier();
 
   // ---- map to the inputs
   // d gamma_C = rowsum(dH (.) S): wave I takes row tiles kk = I, I + NB, ..;
@@ -820,7 +823,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   float dotq = 0.f, dotk = 0.f, dbs = 0.f;  // GN: row sums for layer prep and per-(token, head) b
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    const f32x4 dkt = reinterpret_cast<const f32x4 *>(dKacc)[(I * NK + kk) * 64 + lane];
+    f32x4 dkt = zero4;
+#pragma unroll
+    for (int I2 = 0; I2 < NB; ++I2)
+      if (I2 >= I)
+        dkt += dk_slot(I2, I, kk)[lane];
     const f32x4 ckt = dkt * ex4(rho_end(I, kk) - gv[kk]);
     const int c0 = 16 * kk + 4 * g;
     f32x4 qq = nq.f() * qs, kq = nk.f() * ks, bq = GN ? ld_b(c0) : nb.f();
