@@ -347,94 +347,228 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
       for (int j = 0; j < CPW; ++j)
         sf[kk][j] = F::from(S[kk][j]);
     F zf[NB][CPW];
+    if constexpr (NK % 2 == 0 && NB % 2 == 0 && CPW == 1) {
+      // (one column tile per wave: with two, these registers would spill)
+      // Every product chain is short (NK / 2 steps for Z and O, NB / 2 for
+      // the update) and a dependent step costs several times an issue slot,
+      // so the loops run the k-pairs outermost: each step advances the
+      // chains of all row tiles (Z and O) or of a group of GK row tiles (the
+      // update), whose products are independent and fill each other's wait.
+      f32x4 z[NB][CPW], ot[NB][CPW];
 #pragma unroll
-    for (int tt = 0; tt < NB; ++tt) {
-      f32x4 z[CPW], ot[CPW];
-      F ut[CPW], oi[CPW];
-      if constexpr (K::UO_LDS) {
-        uo_row_lds(sb, tt, ut, oi);
-      } else {
+      for (int tt = 0; tt < NB; ++tt) {
+        F ut[CPW], oi[CPW];
+        if constexpr (K::UO_LDS) {
+          uo_row_lds(sb, tt, ut, oi);
+        } else {
+#pragma unroll
+          for (int j = 0; j < CPW; ++j) {
+            ut[j] = ucur[tt][j];
+            oi[j] = ocur[tt][j];
+          }
+        }
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-          ut[j] = ucur[tt][j];
-          oi[j] = ocur[tt][j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        if constexpr (sizeof(IO) == 2) {
-          // start from Ut and O_intra^T with an identity product instead of
-          // unpacking bf16 on the vector ALU (which the products wait for);
-          // same product shape as the rest of the chain (see mma32)
-          z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          ot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (NK % 2 == 0) {
-            mma32(z[j], F2::make(eye, F::zero()), F2::make(ut[j], ut[j]));
-            mma32(ot[j], F2::make(eye, F::zero()), F2::make(oi[j], oi[j]));
+          if constexpr (sizeof(IO) == 2) {
+            // start from Ut and O_intra^T with an identity product instead of
+            // unpacking bf16 on the vector ALU (which the products wait for);
+            // same product shape as the rest of the chain (see mma32)
+            z[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ot[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma32(z[tt][j], F2::make(eye, F::zero()), F2::make(ut[j], ut[j]));
+            mma32(ot[tt][j], F2::make(eye, F::zero()), F2::make(oi[j], oi[j]));
           } else {
-            mma16(z[j], eye, ut[j]);
-            mma16(ot[j], eye, oi[j]);
+            z[tt][j] = ut[j].to_f32();
+            ot[tt][j] = oi[j].to_f32();
           }
-        } else {
-          z[j] = ut[j].to_f32();
-          ot[j] = oi[j].to_f32();
         }
       }
-      if constexpr (NK % 2 == 0) {
+      // -W and Q' pairs of k-pair k2 for every row tile, two register
+      // buffers: pair k2 + 1 is read while k2 is multiplied
+      F2 w2[2][NB], q2[2][NB];
+      auto wq_pair = [&](int k2, int b) {
 #pragma unroll
-        for (int k2 = 0; k2 < NK / 2; ++k2) {
-          const F2 w2 = F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
-          const F2 q2 = F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+        for (int tt = 0; tt < NB; ++tt) {
+          w2[b][tt] = F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+          q2[b][tt] = F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+        }
+      };
+      wq_pair(0, 0);
+#pragma unroll
+      for (int k2 = 0; k2 < NK / 2; ++k2) {
+        if (k2 + 1 < NK / 2)
+          wq_pair(k2 + 1, (k2 + 1) % 2);
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
           for (int j = 0; j < CPW; ++j) {
             const F2 s2 = F2::make(sf[2 * k2][j], sf[2 * k2 + 1][j]);
-            mma32(z[j], w2, s2);
-            mma32(ot[j], s2, q2);
+            mma32(z[tt][j], w2[k2 % 2][tt], s2);
+            mma32(ot[tt][j], s2, q2[k2 % 2][tt]);
+          }
+      }
+#pragma unroll
+      for (int tt = 0; tt < NB; ++tt) {
+        const int t = 16 * tt + m;  // this lane's row of the O tile
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          zf[tt][j] = F::from(z[tt][j]);
+          if (!ST && (FULL || t < len))
+            store4_global(gout + (static_cast<size_t>(t0 + t) * a.H + h) * D + 16 * (vt0 + j) + 4 * g, ot[tt][j]);
+        }
+      }
+      // S <- Diag(gamma_C) S + Kbar^T Z, GK row tiles at a time
+      constexpr int GK = NK;
+#pragma unroll
+      for (int k0 = 0; k0 < NK; k0 += GK) {
+        f32x4 gamv[GK];
+        F2 kbp[GK][NB / 2];
+#pragma unroll
+        for (int u = 0; u < GK; ++u) {
+          gamv[u] = *reinterpret_cast<const f32x4 *>(sb + L::GAM + (16 * (k0 + u) + 4 * g) * sizeof(float));
+#pragma unroll
+          for (int t2 = 0; t2 < NB / 2; ++t2)
+            kbp[u][t2] = F2::ld(sb + L::KB + tile_off<IO, NB>(k0 + u, 2 * t2, 0), lane);
+        }
+#pragma unroll
+        for (int u = 0; u < GK; ++u)
+#pragma unroll
+          for (int j = 0; j < CPW; ++j)
+            S[k0 + u][j] *= gamv[u];
+#pragma unroll
+        for (int t2 = 0; t2 < NB / 2; ++t2)
+#pragma unroll
+          for (int u = 0; u < GK; ++u)
+#pragma unroll
+            for (int j = 0; j < CPW; ++j)
+              mma32(S[k0 + u][j], kbp[u][t2], F2::make(zf[2 * t2][j], zf[2 * t2 + 1][j]));
+      }
+    } else {
+      // LDS operands of the state update (gamma_C and the Kbar^T pairs of row
+      // tile kk), in two register buffers: row tile kk + 1 is read while kk is
+      // multiplied, and row tile 0 during the products above (read at their
+      // use, each row tile waited a full LDS round trip)
+      constexpr int NKB = NB % 2 == 0 ? NB / 2 : 1;
+      f32x4 gamv[2];
+      F2 kbp[2][NKB];
+      auto su_load = [&](int kk, int b) {
+        gamv[b] = *reinterpret_cast<const f32x4 *>(sb + L::GAM + (16 * kk + 4 * g) * sizeof(float));
+        if constexpr (NB % 2 == 0) {
+  #pragma unroll
+          for (int t2 = 0; t2 < NKB; ++t2)
+            kbp[b][t2] = F2::ld(sb + L::KB + tile_off<IO, NB>(kk, 2 * t2, 0), lane);
+        }
+      };
+      // -W and Q' pairs of row tile tt, two register buffers: tile tt + 1 is
+      // read while tile tt is multiplied (one column tile per wave; with two,
+      // the extra registers would spill and the pairs are read at their use)
+      constexpr bool WQ_PF = CPW == 1;
+      constexpr int NKP = NK % 2 == 0 ? NK / 2 : 1;
+      F2 wq_w[WQ_PF ? 2 : 1][NKP], wq_q[WQ_PF ? 2 : 1][NKP];
+      auto wq_load = [&](int tt, F2(&w)[NKP], F2(&q)[NKP]) {
+        if constexpr (NK % 2 == 0 && WQ_PF) {
+  #pragma unroll
+          for (int k2 = 0; k2 < NKP; ++k2) {
+            w[k2] = F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+            q[k2] = F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
           }
         }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          const F w1 = F::ld(sb + L::WN + tile_off<IO, NK>(tt, kk, 0), lane);
-          const F q1 = F::ld(sb + L::QP + tile_off<IO, NK>(tt, kk, 0), lane);
-#pragma unroll
+      };
+      wq_load(0, wq_w[0], wq_q[0]);
+  #pragma unroll
+      for (int tt = 0; tt < NB; ++tt) {
+        if (tt + 1 < NB)
+          wq_load(tt + 1, wq_w[WQ_PF ? (tt + 1) % 2 : 0], wq_q[WQ_PF ? (tt + 1) % 2 : 0]);
+        else
+          su_load(0, 0);
+        f32x4 z[CPW], ot[CPW];
+        F ut[CPW], oi[CPW];
+        if constexpr (K::UO_LDS) {
+          uo_row_lds(sb, tt, ut, oi);
+        } else {
+  #pragma unroll
           for (int j = 0; j < CPW; ++j) {
-            mma16(z[j], w1, sf[kk][j]);
-            mma16(ot[j], sf[kk][j], q1);
+            ut[j] = ucur[tt][j];
+            oi[j] = ocur[tt][j];
           }
         }
+  #pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          if constexpr (sizeof(IO) == 2) {
+            // start from Ut and O_intra^T with an identity product instead of
+            // unpacking bf16 on the vector ALU (which the products wait for);
+            // same product shape as the rest of the chain (see mma32)
+            z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (NK % 2 == 0) {
+              mma32(z[j], F2::make(eye, F::zero()), F2::make(ut[j], ut[j]));
+              mma32(ot[j], F2::make(eye, F::zero()), F2::make(oi[j], oi[j]));
+            } else {
+              mma16(z[j], eye, ut[j]);
+              mma16(ot[j], eye, oi[j]);
+            }
+          } else {
+            z[j] = ut[j].to_f32();
+            ot[j] = oi[j].to_f32();
+          }
+        }
+        if constexpr (NK % 2 == 0) {
+  #pragma unroll
+          for (int k2 = 0; k2 < NK / 2; ++k2) {
+            const F2 w2 = WQ_PF ? wq_w[tt % 2][k2] : F2::ld(sb + L::WN + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+            const F2 q2 = WQ_PF ? wq_q[tt % 2][k2] : F2::ld(sb + L::QP + tile_off<IO, NK>(tt, 2 * k2, 0), lane);
+  #pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+              const F2 s2 = F2::make(sf[2 * k2][j], sf[2 * k2 + 1][j]);
+              mma32(z[j], w2, s2);
+              mma32(ot[j], s2, q2);
+            }
+          }
+        } else {
+  #pragma unroll
+          for (int kk = 0; kk < NK; ++kk) {
+            const F w1 = F::ld(sb + L::WN + tile_off<IO, NK>(tt, kk, 0), lane);
+            const F q1 = F::ld(sb + L::QP + tile_off<IO, NK>(tt, kk, 0), lane);
+  #pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+              mma16(z[j], w1, sf[kk][j]);
+              mma16(ot[j], sf[kk][j], q1);
+            }
+          }
+        }
+        const int t = 16 * tt + m;  // this lane's row of the O tile
+  #pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          zf[tt][j] = F::from(z[j]);
+          if (!ST && (FULL || t < len))
+            store4_global(gout + (static_cast<size_t>(t0 + t) * a.H + h) * D + 16 * (vt0 + j) + 4 * g, ot[j]);
+        }
       }
-      const int t = 16 * tt + m;  // this lane's row of the O tile
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        zf[tt][j] = F::from(z[j]);
-        if (!ST && (FULL || t < len))
-          store4_global(gout + (static_cast<size_t>(t0 + t) * a.H + h) * D + 16 * (vt0 + j) + 4 * g, ot[j]);
-      }
+  #pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk + 1 < NK)
+          su_load(kk + 1, (kk + 1) % 2);
+  #pragma unroll
+        for (int j = 0; j < CPW; ++j)
+          S[kk][j] *= gamv[kk % 2];
+        if constexpr (NB % 2 == 0) {
+  #pragma unroll
+          for (int t2 = 0; t2 < NB / 2; ++t2) {
+  #pragma unroll
+            for (int j = 0; j < CPW; ++j)
+              mma32(S[kk][j], kbp[kk % 2][t2], F2::make(zf[2 * t2][j], zf[2 * t2 + 1][j]));
+          }
+        } else {
+  #pragma unroll
+          for (int tt = 0; tt < NB; ++tt) {
+            const F kb1 = F::ld(sb + L::KB + tile_off<IO, NB>(kk, tt, 0), lane);
+  #pragma unroll
+            for (int j = 0; j < CPW; ++j)
+              mma16(S[kk][j], kb1, zf[tt][j]);
+          }
+        }
+
     }
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const f32x4 gam = *reinterpret_cast<const f32x4 *>(sb + L::GAM + (16 * kk + 4 * g) * sizeof(float));
-#pragma unroll
-      for (int j = 0; j < CPW; ++j)
-        S[kk][j] *= gam;
-      if constexpr (NB % 2 == 0) {
-#pragma unroll
-        for (int t2 = 0; t2 < NB / 2; ++t2) {
-          const F2 kb2 = F2::ld(sb + L::KB + tile_off<IO, NB>(kk, 2 * t2, 0), lane);
-#pragma unroll
-          for (int j = 0; j < CPW; ++j)
-            mma32(S[kk][j], kb2, F2::make(zf[2 * t2][j], zf[2 * t2 + 1][j]));
-        }
-      } else {
-#pragma unroll
-        for (int tt = 0; tt < NB; ++tt) {
-          const F kb1 = F::ld(sb + L::KB + tile_off<IO, NB>(kk, tt, 0), lane);
-#pragma unroll
-          for (int j = 0; j < CPW; ++j)
-            mma16(S[kk][j], kb1, zf[tt][j]);
-        }
-      }
     }
   };
 
