@@ -360,21 +360,43 @@ def main() -> int:
         # timed interleaved, 3 rounds of 20 steps, and the medians reported;
         # GDN-2's time over KDA's is the measured cost of its two per-channel
         # gates.
+        # A fourth entry, layer_prep, takes the raw layer inputs (q, k before
+        # the L2 norm, b and w as logits, alpha as the float32 log-decay).
         beta = dev["b"][..., 0].contiguous()
         alpha_s = dev["alpha"][..., 0].contiguous()
         vins = {"gdn2": dev, "kda": dict(dev, b=beta, w=beta),
-                "gated_deltanet": dict(dev, b=beta, w=beta, alpha=alpha_s)}
+                "gated_deltanet": dict(dev, b=beta, w=beta, alpha=alpha_s),
+                "layer_prep": dict(dev, alpha=torch.log(dev["alpha"].float()))}
         secs = {name: [] for name in vins}
         for _ in range(3):
             for name, vin in vins.items():
                 secs[name].append(timed_steps(
                     lambda: g.chunk_fwd(*(vin[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws,
-                                        path=args.path), 20, 3))
+                                        path=args.path, layer_prep=(name == "layer_prep")), 20, 3))
         med = {name: float(np.median(v)) for name, v in secs.items()}
         variants = {name: {"tokens_per_s": round(B * T / t, 1), "ms": round(t * 1e3, 4)} for name, t in med.items()}
         variants["gdn2_over_kda_time"] = round(med["gdn2"] / med["kda"], 4)
         variants["gdn2_throughput_vs_gated_deltanet"] = round(med["gated_deltanet"] / med["gdn2"], 4)
+        variants["layer_prep_over_gdn2_time"] = round(med["layer_prep"] / med["gdn2"], 4)
         out["gate_variants"] = variants
+        del vins
+
+        # token-by-token path (the cross-check and the R1 rule's GPU path) on
+        # the first 1024 tokens of the same layer: rule R5 against rule R1
+        Tr = 1024
+        rin = {x: dev[x][:, :Tr].contiguous() for x in NAMES}
+        orr = torch.empty((B, Tr, H, d), dtype=torch.bfloat16, device="cuda")
+        rsec = {}
+        for rule in ("R5", "R1"):
+            rsec[rule] = timed_steps(lambda: g.chunk_fwd(*(rin[x] for x in NAMES), out=orr, S_final=Sf,
+                                                         path="recurrent", rule=rule), 5, 1)
+        out["token_recurrent"] = {
+            "workload": f"B={B} T={Tr} H={H} d={d} bf16, token by token",
+            "r5_tokens_per_s": round(B * Tr / rsec["R5"], 1), "r5_ms": round(rsec["R5"] * 1e3, 4),
+            "r1_tokens_per_s": round(B * Tr / rsec["R1"], 1), "r1_ms": round(rsec["R1"] * 1e3, 4),
+            "r1_over_r5_time": round(rsec["R1"] / rsec["R5"], 4),
+        }
+        del rin, orr
 
         lens = gi.packed_lengths(3)
         cu = gi.cu_seqlens_from(lens).cuda()
