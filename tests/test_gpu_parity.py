@@ -245,6 +245,27 @@ def test_varlen_equals_separate_runs(g):
         np.testing.assert_array_equal(Sf[n:n + 1], S1)
 
 
+@pytest.mark.parametrize("path", ["two_pass", "fused", "recurrent"])
+def test_chunk_aligned_slices_chain_exactly(g, path):
+    """Cutting every sequence at chunk boundaries and running the pieces in
+    order, each from the state the previous piece left, reproduces the
+    whole-sequence outputs and final state bit for bit: the kernels carry
+    the state from chunk to chunk in float32, as S0 is read and S_final
+    written.  The last piece ends in a ragged chunk."""
+    B, T, H, d, C = 2, 450, 3, 128, 64
+    inp = gi.make_chunk_inputs(B, T, H, d, d, "bf16", seed=23, s0="normal")
+    print(f"case path={path} B={B} T={T} H={H} d={d}", flush=True)
+    o, Sf = gpu_fwd(g, inp, C, path=path)
+    S = inp["S0"]
+    cuts = [0, 128, 192, T]
+    for a, bnd in zip(cuts[:-1], cuts[1:]):
+        sub = {x: inp[x][:, a:bnd].contiguous() for x in NAMES}
+        o1, S1 = gpu_fwd(g, sub, C, S0=S, path=path)
+        np.testing.assert_array_equal(o[:, a:bnd], o1)
+        S = torch.from_numpy(S1)
+    np.testing.assert_array_equal(Sf, S.numpy())
+
+
 # -------------------------------------------------------- headline config
 @pytest.mark.parametrize("path", ["auto", "two_pass"])
 def test_config2_sampled_units(g, path):
