@@ -162,8 +162,9 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     """The 32768-token stream of the packed workload as ONE sequence cut
     into 8 segments of 4096 tokens (an 8-way context-parallel split).  Per
     rank: the segment's map (prep + segment-map kernel) and its re-run from
-    the true entering state (gdn2_chunk_fwd), against the serial forward of
-    the same 4096 x 16 share.  On one GPU: all 8 maps in one call, the scan
+    the true entering state (gdn2_chunk_fwd, in full, and on the workspace
+    the map left: the scan alone), against the serial forward of the same
+    4096 x 16 share.  On one GPU: all 8 maps in one call, the scan
     of the maps, the 8 re-runs in one packed call, against the forward of the
     whole 32768-token sequence."""
     G, L = 8, 4096
@@ -190,6 +191,10 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     g.profile_enable(False)
     kern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in prof.items()}
     sec_rerun = timed_steps(lambda: rank_fwd(S_in1), 20, 3)
+    # the re-run on the workspace the map left (GDN2_FLAG_PREPARED): scan only
+    rank_map()
+    sec_rerun_p = timed_steps(lambda: g.chunk_fwd(*(rank[x] for x in NAMES), S0=S_in1, chunk=C, out=o1,
+                                                  S_final=Sf1, workspace=ws1, prepared=True), 20, 3)
     sec_serial = timed_steps(lambda: rank_fwd(None), 20, 3)
     sm_us = kern["segment_map"]["avg_us"]
     tok_heads = L * H
@@ -199,6 +204,8 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
         "map_ms": round(sec_map * 1e3, 4), "rerun_ms": round(sec_rerun * 1e3, 4),
         "serial_forward_ms": round(sec_serial * 1e3, 4),
         "map_plus_rerun_over_serial": round((sec_map + sec_rerun) / sec_serial, 3),
+        "prepared_rerun_ms": round(sec_rerun_p * 1e3, 4),
+        "map_plus_prepared_rerun_over_serial": round((sec_map + sec_rerun_p) / sec_serial, 3),
         "kernels": kern,
         "segment_map_roofline": {"bound": "hbm", "achieved": round(sm_bytes / (sm_us * 1e-6) / 1e9, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -239,11 +246,18 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     sec_comb = timed_steps(combine, 20, 3)
     cprof = g.profile_read(reset=True)
     g.profile_enable(False)
+    def reruns_prepared():
+        g.chunk_fwd(*(full[x] for x in NAMES), S0=S_inG, cu_seqlens=cu, chunk=C, out=oG, S_final=SfG,
+                    workspace=wsG, prepared=True)
+
     sec_all = timed_steps(lambda: (all_maps(), combine(), reruns()), 10, 2)
+    sec_all_p = timed_steps(lambda: (all_maps(), combine(), reruns_prepared()), 10, 2)
     sec_whole = timed_steps(whole, 10, 2)
     res["one_gpu"] = {
         "maps_combine_reruns_ms": round(sec_all * 1e3, 4), "whole_sequence_forward_ms": round(sec_whole * 1e3, 4),
         "ratio": round(sec_all / sec_whole, 3),
+        "maps_combine_prepared_reruns_ms": round(sec_all_p * 1e3, 4),
+        "prepared_ratio": round(sec_all_p / sec_whole, 3),
         "combine_kernel_us": round(1e3 * cprof["segment_combine"][0] / cprof["segment_combine"][1], 2),
         "exchange_bytes_per_rank": 2 * H * d * d * 4,
     }

@@ -40,6 +40,7 @@ FLAG_SCALAR_W = 1 << 5
 FLAG_SCALAR_ALPHA = 1 << 6
 FLAG_LAYER_PREP = 1 << 0
 FLAG_RULE_R1 = 1 << 7
+FLAG_PREPARED = 1 << 8
 PATHS = {"auto": 0, "recurrent": FLAG_RECURRENT, "two_pass": FLAG_TWO_PASS, "fused": FLAG_FUSED}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
@@ -138,12 +139,14 @@ def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chu
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
               recurrent: bool = False, out=None, S_final=None, workspace=None,
               want_final: bool = True, path: str = "auto", layer_prep: bool = False,
-              rule: str = "R5"):
+              rule: str = "R5", prepared: bool = False):
     """Chunked forward.  ``path`` selects the kernels: "auto" (the library
     chooses), "fused" (single pass), "two_pass", or "recurrent" (token by
     token; also selected by ``recurrent=True``).  ``rule="R1"`` runs the
-    alternative reading R1 (token-by-token path only).  Returns (o, S_final);
-    S_final is None when ``want_final`` is False."""
+    alternative reading R1 (token-by-token path only).  ``prepared=True``
+    runs the state scan alone on a ``workspace`` that ``segment_map`` (or a
+    two-pass ``chunk_fwd``) filled for the same inputs.  Returns (o,
+    S_final); S_final is None when ``want_final`` is False."""
     if recurrent:
         path = "recurrent"
     _require_device(q, k, v, alpha, b, w, S0, cu_seqlens)
@@ -170,7 +173,10 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
         Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     if rule not in ("R5", "R1"):
         raise ValueError(f"unknown rule {rule!r}")
-    flags = PATHS[path] | gate_flags | (FLAG_LAYER_PREP if layer_prep else 0) | (FLAG_RULE_R1 if rule == "R1" else 0)
+    if prepared and workspace is None:
+        raise ValueError("prepared=True reads the given workspace")
+    flags = (PATHS[path] | gate_flags | (FLAG_LAYER_PREP if layer_prep else 0) | (FLAG_RULE_R1 if rule == "R1" else 0)
+             | (FLAG_PREPARED if prepared else 0))
     ws_bytes = 0
     if path != "recurrent":
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)

@@ -134,7 +134,7 @@ hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, uint32_t flags, hipStr
     prof_scope p("chunk_fused", st);
     return ng == 1 ? gdn2::launch_fused<IO, D, C, 1>(a, st) : gdn2::launch_fused<IO, D, C, 2>(a, st);
   }
-  {
+  if (!(flags & GDN2_FLAG_PREPARED)) {
     prof_scope p("chunk_prep", st);
     e = gdn2::launch_chunk_prep<IO, D, C>(a, st);
     if (e != hipSuccess)
@@ -363,8 +363,13 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unknown dtype %d", static_cast<int>(dt));
   const uint32_t path_flags = GDN2_FLAG_RECURRENT | GDN2_FLAG_TWO_PASS | GDN2_FLAG_FUSED;
   const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
-  if (flags & ~(path_flags | gate_flags | GDN2_FLAG_RULE_R1))
+  if (flags & ~(path_flags | gate_flags | GDN2_FLAG_RULE_R1 | GDN2_FLAG_PREPARED))
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: unknown flags 0x%x", flags);
+  if (flags & GDN2_FLAG_PREPARED) {
+    if (flags & (GDN2_FLAG_RECURRENT | GDN2_FLAG_FUSED))
+      return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: a prepared workspace is read by the two-pass path only");
+    flags |= GDN2_FLAG_TWO_PASS;
+  }
   if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT))
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: rule R1 runs on the token-by-token path only");
   {

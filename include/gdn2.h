@@ -109,6 +109,17 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
  * It reduces to KDA, Gated DeltaNet and DeltaNet as the default rule does;
  * the pages do not settle which of the two they mean. */
 #define GDN2_FLAG_RULE_R1 (1u << 7)
+/* Prepared workspace (two-pass path only; GDN2_ERR_UNSUPPORTED with
+ * GDN2_FLAG_RECURRENT or GDN2_FLAG_FUSED).  For the caller that has just run
+ * gdn2_chunk_segment_map on the same inputs, sizes, gate flags and workspace:
+ * a context-parallel rank that computes its segment's map, exchanges the
+ * maps, and then runs its segment from the true entering state.  The
+ * workspace already holds every chunk's intermediates (they do not depend
+ * on S0), so gdn2_chunk_fwd skips the per-chunk kernel and runs the state
+ * scan alone; q .. w are checked but not read.  A workspace filled by
+ * gdn2_chunk_fwd on the two-pass path serves the same way.  Any other
+ * contents give undefined outputs. */
+#define GDN2_FLAG_PREPARED (1u << 8)
 
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and
@@ -128,7 +139,8 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               sequence boundary.
  *   B, T, H, dk, dv, num_seqs, chunk, dt : sizes; chunk is the chunk length.
  *   flags     : at most one of GDN2_FLAG_RECURRENT, GDN2_FLAG_TWO_PASS,
- *               GDN2_FLAG_FUSED, plus any of the gate layout flags.  With no
+ *               GDN2_FLAG_FUSED, plus any of the gate layout flags, and
+ *               GDN2_FLAG_PREPARED (two-pass path implied).  With no
  *               path flag the library runs the two-pass chunked kernels (all
  *               chunks in parallel, then the state scan); GDN2_FLAG_FUSED
  *               runs the single-pass kernel (one workgroup per head walks its
@@ -138,7 +150,9 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *   S_final   : final states [N, H, dk, dv] float32, or NULL.  May alias S0.
  *   workspace : device scratch of at least
  *               gdn2_chunk_fwd_workspace_bytes(...) bytes (NULL allowed when
- *               that is 0).  Its contents on entry are irrelevant.
+ *               that is 0).  Its contents on entry are irrelevant, except
+ *               with GDN2_FLAG_PREPARED.  On return (two-pass path) it holds
+ *               the chunks' intermediates.
  * T == 0 is allowed: nothing but S_final = S0 (or zeros) is written. */
 gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
                              const void *b, const void *w, const float *S0,
@@ -208,7 +222,9 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
  *               only (others return GDN2_ERR_UNSUPPORTED).
  *   Phi, Psi  : outputs, [N, H, dk, dk] and [N, H, dk, dv] float32, row-major
  *               per head.  An empty segment gives Phi = I, Psi = 0.
- *   workspace : at least gdn2_chunk_fwd_workspace_bytes(...) bytes.
+ *   workspace : at least gdn2_chunk_fwd_workspace_bytes(...) bytes.  On
+ *               return it holds the chunks' intermediates, which
+ *               gdn2_chunk_fwd with GDN2_FLAG_PREPARED reads.
  * The maps use the chunked path's arithmetic (the state rounded to dt for
  * the matrix products, as in gdn2_chunk_fwd) and its numerical domain. */
 gdn2_status_t gdn2_chunk_segment_map(const void *q, const void *k, const void *v, const void *alpha,

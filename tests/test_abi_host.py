@@ -57,7 +57,10 @@ def test_fwd_rejects_before_launch(L):
     assert call_fwd(L, dt=7) == 2
     assert call_fwd(L, B=0) == 1
     assert call_fwd(L, T=-1) == 1
-    assert call_fwd(L, flags=1 << 8) == 1          # unknown flag
+    assert call_fwd(L, flags=1 << 9) == 1          # unknown flag
+    assert call_fwd(L, flags=(1 << 8) | (1 << 1)) == 2         # prepared workspace on the token-by-token path
+    assert call_fwd(L, flags=(1 << 8) | (1 << 3)) == 2         # prepared workspace on the single-pass path
+    assert call_fwd(L, flags=1 << 8, ws_bytes=100) == 3        # a prepared workspace is still size-checked
     assert call_fwd(L, flags=1 << 7) == 2          # rule R1 needs the token-by-token path
     assert call_fwd(L, flags=(1 << 2) | (1 << 3)) == 1         # two paths at once
     assert call_fwd(L, flags=(1 << 1) | (1 << 4)) == 2         # token-by-token path with a per-(token, head) gate

@@ -178,6 +178,50 @@ def test_segments_reproduce_the_sequence(g, dtype, d, chunk, lens):
     assert max(e_o, e_f, e_l) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d,chunk,lens", [
+    ("f32", 64, 64, [250, 0, 333, 64, 353]),
+    ("bf16", 128, 64, [512, 300, 700, 8]),
+    ("bf16", 32, 16, [100, 1, 99]),
+])
+def test_prepared_rerun_equals_full_rerun(g, dtype, d, chunk, lens):
+    """gdn2_chunk_fwd with GDN2_FLAG_PREPARED on the workspace that the
+    segment maps left runs the state scan alone; outputs and final states
+    equal those of the full forward from the same entering states bit for
+    bit (the same per-chunk kernel wrote the workspace)."""
+    T, H = sum(lens), 2
+    inp = gi.make_chunk_inputs(1, T, H, d, d, dtype, seed=900 + T, s0="normal", alpha_mean=8.0)
+    print(f"case prepared rerun {dtype} d={d} C={chunk} lens={lens}", flush=True)
+    cu = gi.cu_seqlens_from(lens).cuda()
+    dd = {n: inp[n].cuda() for n in NAMES}
+    ws = torch.empty(g.workspace_bytes(1, T, H, d, d, len(lens), chunk, dd["q"].dtype), dtype=torch.uint8,
+                     device="cuda")
+    Phi, Psi = g.segment_map(*(dd[n] for n in NAMES), cu_seqlens=cu, chunk=chunk, workspace=ws)
+    S_in, _ = g.segment_combine(Phi, Psi, inp["S0"][0].cuda())
+    o_p, Sf_p = g.chunk_fwd(*(dd[n] for n in NAMES), S0=S_in, cu_seqlens=cu, chunk=chunk, workspace=ws,
+                            prepared=True)
+    o_f, Sf_f = g.chunk_fwd(*(dd[n] for n in NAMES), S0=S_in, cu_seqlens=cu, chunk=chunk, path="two_pass")
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_f)
+    assert torch.equal(Sf_p, Sf_f)
+
+
+def test_prepared_workspace_of_a_forward_call(g):
+    """A workspace filled by a two-pass forward serves a prepared call from
+    another initial state (fixed-length batch, ragged last chunk)."""
+    B, T, H, d, C = 3, 200, 2, 64, 64
+    inp = gi.make_chunk_inputs(B, T, H, d, d, "bf16", seed=77, s0="normal")
+    print(f"case prepared forward workspace B={B} T={T}", flush=True)
+    dd = {n: inp[n].cuda() for n in NAMES}
+    ws = torch.empty(g.workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    g.chunk_fwd(*(dd[n] for n in NAMES), chunk=C, workspace=ws, path="two_pass")
+    S1 = inp["S0"].cuda()
+    o_p, Sf_p = g.chunk_fwd(*(dd[n] for n in NAMES), S0=S1, chunk=C, workspace=ws, prepared=True)
+    o_f, Sf_f = g.chunk_fwd(*(dd[n] for n in NAMES), S0=S1, chunk=C, path="two_pass")
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_f)
+    assert torch.equal(Sf_p, Sf_f)
+
+
 def test_segments_per_rank_shape(g):
     """Config 3's 32768-token stream (H=16, d=128, bf16) as one sequence cut
     into 8 segments of 4096 tokens, the per-rank share of an 8-way
