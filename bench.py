@@ -241,6 +241,9 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     def whole():
         g.chunk_fwd(*(full[x] for x in NAMES), chunk=C, out=oG, S_final=Sf_seq, workspace=ws_seq, path=path)
 
+    def whole_serial():
+        g.chunk_fwd(*(full[x] for x in NAMES), chunk=C, out=oG, S_final=Sf_seq, workspace=ws_seq, path="two_pass")
+
     g.profile_enable(True)
     g.profile_read(reset=True)
     sec_comb = timed_steps(combine, 20, 3)
@@ -253,11 +256,13 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     sec_all = timed_steps(lambda: (all_maps(), combine(), reruns()), 10, 2)
     sec_all_p = timed_steps(lambda: (all_maps(), combine(), reruns_prepared()), 10, 2)
     sec_whole = timed_steps(whole, 10, 2)
+    sec_serial_w = timed_steps(whole_serial, 10, 2)
     res["one_gpu"] = {
-        "maps_combine_reruns_ms": round(sec_all * 1e3, 4), "whole_sequence_forward_ms": round(sec_whole * 1e3, 4),
-        "ratio": round(sec_all / sec_whole, 3),
+        "maps_combine_reruns_ms": round(sec_all * 1e3, 4),
         "maps_combine_prepared_reruns_ms": round(sec_all_p * 1e3, 4),
-        "prepared_ratio": round(sec_all_p / sec_whole, 3),
+        "whole_sequence_serial_scan_ms": round(sec_serial_w * 1e3, 4),
+        "whole_sequence_default_path_ms": round(sec_whole * 1e3, 4),
+        "prepared_over_serial": round(sec_all_p / sec_serial_w, 3),
         "combine_kernel_us": round(1e3 * cprof["segment_combine"][0] / cprof["segment_combine"][1], 2),
         "exchange_bytes_per_rank": 2 * H * d * d * 4,
     }
@@ -297,8 +302,11 @@ def main() -> int:
     dev = {x: inp[x].cuda() for x in NAMES}
     o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
     Sf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(g.workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8,
-                     device="cuda")
+    # one workspace for the headline and every T of the sweep (a single long
+    # sequence also takes the segment schedule's maps)
+    ws = torch.empty(max([g.workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16)] +
+                         [g.workspace_bytes(32768 // Ts, Ts, H, d, d, 0, C, torch.bfloat16) for Ts in gi.SWEEP_T]),
+                     dtype=torch.uint8, device="cuda")
 
     def step():
         g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws,

@@ -340,6 +340,23 @@ hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S
   return hipGetLastError();
 }
 
+// Bounds of G segments of one sequence of T tokens, L tokens each (the last
+// shorter): cu[i] = min(i L, T), i = 0 .. G.
+__global__ void gdn2_seg_bounds_kernel(int32_t *cu, int G, int L, int T) {
+  const int i = static_cast<int>(threadIdx.x);
+  if (i <= G) {
+    const long x = static_cast<long>(i) * L;
+    cu[i] = static_cast<int32_t>(x < T ? x : T);
+  }
+}
+
+hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, hipStream_t st) {
+  if (G < 1 || G > 255)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gdn2_seg_bounds_kernel, dim3(1), dim3(256), 0, st, cu, G, L, T);
+  return hipGetLastError();
+}
+
 #define GDN2_INST_SEG(IO, D, C) \
   template hipError_t launch_segmap<IO, D, C>(const chunk_args &, float *, float *, hipStream_t);
 

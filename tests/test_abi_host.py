@@ -85,6 +85,37 @@ def test_workspace_bytes(L):
     assert f(1, 100, 2, 64, 64, 5, 16, F32) >= f(1, 100, 2, 64, 64, 0, 16, F32)
 
 
+def test_workspace_bytes_long_sequence(L):
+    # One sequence of 512 chunks or more with at most 16 heads also reserves
+    # the segment schedule (8 segments: their bounds, chunk table, blocks of
+    # the packed layout, and Phi, Psi, S_in); shorter sequences, more heads,
+    # batches and packed input get the plain size.
+    d, C = 128, 64
+
+    def ws(B, T, H, n=0):
+        return L.gdn2_chunk_fwd_workspace_bytes(B, T, H, d, d, n, C, BF16)
+
+    blk = (ws(1, C, 1) - 256) // 2          # one chunk slot of one head (B = 1 reserves nc + 1 slots)
+    assert blk > 0 and ws(1, C, 1) == 256 + 2 * blk
+
+    def plain(B, T, H):
+        nc = -(-T // C)
+        return 256 * (-(-(B + 1) * 4 // 256)) + max(B * nc, nc + B) * H * blk
+
+    def seg(T, H):
+        nc = -(-T // C)
+        blocks = (nc + 8) * H * blk
+        return 256 + 256 + -(-blocks // 256) * 256 + 3 * 8 * H * d * d * 4
+
+    assert ws(1, 32768, 16) == max(plain(1, 32768, 16), seg(32768, 16))
+    assert ws(1, 32768, 16) > plain(1, 32768, 16)
+    assert ws(1, 40000, 3) == max(plain(1, 40000, 3), seg(40000, 3))
+    assert ws(1, 511 * C, 16) == plain(1, 511 * C, 16)       # 511 chunks
+    assert ws(2, 32768, 16) == plain(2, 32768, 16)           # two sequences
+    assert ws(1, 32768, 17) == plain(1, 32768, 17)           # 17 heads
+    assert ws(1, 32768, 16, 1) == plain(1, 32768, 16)        # packed
+
+
 def test_decode_rejects_before_launch(L):
     p = FAKE
     assert L.gdn2_decode_step(p, p, p, p, p, p, p, p, 4, 2, 16, 16, 5, None) == 2

@@ -295,6 +295,40 @@ def test_sweep_endpoints_sampled(g):
               f"sweep T={T}")
 
 
+@pytest.mark.parametrize("dtype,d,H,T", [("f32", 64, 2, 512 * 64 + 100), ("bf16", 128, 4, 512 * 64 + 37)])
+def test_long_sequence_segment_schedule(g, dtype, d, H, T):
+    """One sequence of more than 512 chunks on the default path: the
+    library cuts it into 8 segments (maps, their scan, every segment's scan
+    from its entering state).  Checked against the oracle with an initial
+    state, a ragged last segment, and S_final written over S0."""
+    inp = gi.make_chunk_inputs(1, T, H, d, d, dtype, seed=41 + d, s0="normal", alpha_mean=8.0)
+    print(f"case segment schedule {dtype} d={d} H={H} T={T}", flush=True)
+    dd = to_dev(inp)
+    S = dd["S0"].clone()
+    o, _ = g.chunk_fwd(*(dd[n] for n in NAMES), S0=S, S_final=S, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    check(o.float().cpu().numpy(), S.cpu().numpy(), o_ref, S_ref, TOL[dtype], f"segments {dtype} d={d}")
+
+
+def test_long_sequence_small_workspace_runs_the_serial_scan(g):
+    """With a workspace sized for the plain two-pass path only, the default
+    path runs it: the result equals the forced two-pass call bit for bit."""
+    T, H, d, C = 512 * 64, 2, 64, 64
+    inp = gi.make_chunk_inputs(1, T, H, d, d, "bf16", seed=43, s0="normal")
+    print(f"case small workspace T={T}", flush=True)
+    dd = to_dev(inp)
+    o_t, S_t = g.chunk_fwd(*(dd[n] for n in NAMES), S0=dd["S0"], chunk=C, path="two_pass")
+    # twice the (unsegmented) half-length size: the plain size of T plus one table
+    ws_small = 2 * g.workspace_bytes(1, T // 2, H, d, d, 0, C, torch.bfloat16)
+    assert ws_small < g.workspace_bytes(1, T, H, d, d, 0, C, torch.bfloat16)
+    ws = torch.empty(ws_small, dtype=torch.uint8, device="cuda")
+    o_a, S_a = g.chunk_fwd(*(dd[n] for n in NAMES), S0=dd["S0"], chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_t)
+    assert torch.equal(S_a, S_t)
+
+
 # ------------------------------------------------------------- properties
 def test_state_aliasing_and_split_resume(g):
     inp = gi.make_chunk_inputs(2, 192, 2, 64, 64, "f32", seed=11, s0="normal")
