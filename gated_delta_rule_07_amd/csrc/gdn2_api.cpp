@@ -336,33 +336,44 @@ hipError_t dispatch_segmap(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args
 // Segment-parallel schedule of the default forward for one long sequence.
 // With few (sequence, head) units the state scan, whose chunks run in
 // order, occupies a fraction of the compute units.  The sequence is then
-// cut into SEG_G segments of whole chunks: their affine state maps (segment
-// map kernel, on the prep's blocks), the exclusive scan of the maps from S0
+// cut into G segments of whole chunks: their affine state maps (segment map
+// kernel, on the prep's blocks), the exclusive scan of the maps from S0
 // (which also gives S_final), and the state scan of every segment from its
-// entering state on the same blocks.  Measured on MI355X for one
-// 32768-token sequence of 16 heads (d = 128, bf16): 0.71 ms against 0.89 ms
-// for the serial scan; with two sequences of 16384 the serial scan is
-// faster (0.63 against 0.72 ms), hence the bounds below.
-constexpr int SEG_G = 8;
+// entering state on the same blocks.  G = min(16, 128 / H, chunks / 16) puts
+// about 128 (segment, head) units on the GPU with segments of 16 chunks or
+// more.  Measured on MI355X (bf16, d = 128, one sequence): 16 heads x 32768
+// tokens 0.71 ms against 0.89 ms for the serial scan, 16 x 16384 0.38
+// against 0.47, 8 x 16384 0.23 against 0.34, 4 x 8192 0.10 against 0.16,
+// 4 x 65536 0.43 against 1.25; with 32 heads, or two sequences of 16 heads,
+// the serial scan is as fast or faster, hence the bounds below.
+int seg_count(int T, int H, int chunk) {
+  const int nc = (T + chunk - 1) / chunk;
+  int g = 16;
+  while (g > 1 && (g * H > 128 || 16 * g > nc))
+    g /= 2;
+  return g;
+}
 
 bool use_segments(int B, int T, int H, int chunk, bool packed) {
-  return !packed && B == 1 && H <= 16 && (T + chunk - 1) / chunk >= 512;
+  return !packed && B == 1 && H <= 16 && (T + chunk - 1) / chunk >= 128 && seg_count(T, H, chunk) >= 2;
 }
 
 struct seg_plan {
   size_t cu, table, blocks, map_bytes, total;
+  int G;           // segments
   int seg_tokens;  // L: tokens per segment (whole chunks; the last segment shorter)
 };
 
 seg_plan plan_segments(gdn2_dtype_t dt, int T, int H, int d, int chunk) {
   seg_plan p{};
   const int nc = (T + chunk - 1) / chunk;
-  p.seg_tokens = (nc + SEG_G - 1) / SEG_G * chunk;
-  p.cu = align256(static_cast<size_t>(SEG_G + 1) * sizeof(int32_t));
+  p.G = seg_count(T, H, chunk);
+  p.seg_tokens = (nc + p.G - 1) / p.G * chunk;
+  p.cu = align256(static_cast<size_t>(p.G + 1) * sizeof(int32_t));
   p.table = p.cu;
-  p.blocks = align256(static_cast<size_t>(num_slots_for(1, T, SEG_G, chunk, true)) * H *
+  p.blocks = align256(static_cast<size_t>(num_slots_for(1, T, p.G, chunk, true)) * H *
                       chunk_block_bytes_rt(dt, d, chunk));
-  p.map_bytes = static_cast<size_t>(SEG_G) * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
+  p.map_bytes = static_cast<size_t>(p.G) * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
   p.total = p.cu + p.table + p.blocks + 3 * p.map_bytes;
   return p;
 }
@@ -386,14 +397,14 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   float *Phi = reinterpret_cast<float *>(ws + pl.cu + pl.table + pl.blocks);
   float *Psi = Phi + pl.map_bytes / sizeof(float);
   float *S_in = Psi + pl.map_bytes / sizeof(float);
-  hipError_t e = gdn2::launch_seg_bounds(cu, SEG_G, pl.seg_tokens, a.T, st);
+  hipError_t e = gdn2::launch_seg_bounds(cu, pl.G, pl.seg_tokens, a.T, st);
   if (e != hipSuccess)
     return e;
   gdn2::chunk_args s = a;
   s.cu = cu;
   s.offsets = reinterpret_cast<int32_t *>(ws + pl.cu);
-  s.num_seqs = SEG_G;
-  s.num_slots = num_slots_for(1, a.T, SEG_G, chunk, true);
+  s.num_seqs = pl.G;
+  s.num_slots = num_slots_for(1, a.T, pl.G, chunk, true);
   s.blocks = ws + pl.cu + pl.table;
   s.S0 = nullptr;
   s.o = nullptr;
@@ -401,7 +412,7 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   e = dispatch_segmap(dt, d, chunk, s, Phi, Psi, st);
   if (e != hipSuccess)
     return e;
-  e = dispatch_combine(d, Phi, Psi, a.S0, SEG_G, a.H, S_in, a.S_final, st);
+  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, S_in, a.S_final, st);
   if (e != hipSuccess)
     return e;
   s.S0 = S_in;

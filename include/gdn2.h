@@ -145,10 +145,11 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               GDN2_FLAG_PREPARED (two-pass path implied).  With no
  *               path flag the library runs the two-pass chunked kernels (all
  *               chunks in parallel, then the state scan).  For one
- *               fixed-length sequence (B = 1, no cu_seqlens) of at least 512
+ *               fixed-length sequence (B = 1, no cu_seqlens) of at least 128
  *               chunks and at most 16 heads, given the workspace
  *               gdn2_chunk_fwd_workspace_bytes reports for it, the default
- *               path cuts the sequence into 8 segments of whole chunks: the
+ *               path cuts the sequence into G = min(16, 128 / H, chunks / 16)
+ *               segments of whole chunks (8 or 16): the
  *               segments' state maps (as gdn2_chunk_segment_map), their scan
  *               from S0 (as gdn2_segment_combine, which also gives S_final),
  *               and every segment's state scan from its entering state, so

@@ -295,12 +295,14 @@ def test_sweep_endpoints_sampled(g):
               f"sweep T={T}")
 
 
-@pytest.mark.parametrize("dtype,d,H,T", [("f32", 64, 2, 512 * 64 + 100), ("bf16", 128, 4, 512 * 64 + 37)])
+@pytest.mark.parametrize("dtype,d,H,T", [("f32", 64, 2, 512 * 64 + 100), ("bf16", 128, 4, 512 * 64 + 37),
+                                         ("bf16", 64, 16, 130 * 64 + 5)])
 def test_long_sequence_segment_schedule(g, dtype, d, H, T):
-    """One sequence of more than 512 chunks on the default path: the
-    library cuts it into 8 segments (maps, their scan, every segment's scan
-    from its entering state).  Checked against the oracle with an initial
-    state, a ragged last segment, and S_final written over S0."""
+    """One sequence of 128 chunks or more on the default path: the library
+    cuts it into 16 segments (2 and 4 heads) or 8 (16 heads): maps, their
+    scan, every segment's scan from its entering state.  Checked against
+    the oracle with an initial state, a ragged last segment, and S_final
+    written over S0."""
     inp = gi.make_chunk_inputs(1, T, H, d, d, dtype, seed=41 + d, s0="normal", alpha_mean=8.0)
     print(f"case segment schedule {dtype} d={d} H={H} T={T}", flush=True)
     dd = to_dev(inp)
@@ -319,8 +321,8 @@ def test_long_sequence_small_workspace_runs_the_serial_scan(g):
     print(f"case small workspace T={T}", flush=True)
     dd = to_dev(inp)
     o_t, S_t = g.chunk_fwd(*(dd[n] for n in NAMES), S0=dd["S0"], chunk=C, path="two_pass")
-    # twice the (unsegmented) half-length size: the plain size of T plus one table
-    ws_small = 2 * g.workspace_bytes(1, T // 2, H, d, d, 0, C, torch.bfloat16)
+    # the packed layout's size never includes the segment schedule
+    ws_small = g.workspace_bytes(1, T, H, d, d, 1, C, torch.bfloat16)
     assert ws_small < g.workspace_bytes(1, T, H, d, d, 0, C, torch.bfloat16)
     ws = torch.empty(ws_small, dtype=torch.uint8, device="cuda")
     o_a, S_a = g.chunk_fwd(*(dd[n] for n in NAMES), S0=dd["S0"], chunk=C, workspace=ws)
