@@ -90,9 +90,15 @@ def bwd_bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
     }
 
 
+# The sources that define the chunked forward's kernels (prep and scan):
+# their file, the per-chunk phases, the device helpers and the argument
+# block.  A counter record stays valid while these are unchanged.
+KERNEL_SOURCES = ("gdn2_chunk.hip", "gdn2_wy.hpp", "gdn2_device.hpp", "gdn2_kernels.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "gated_delta_rule_07_amd", "csrc"))):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "gated_delta_rule_07_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
