@@ -333,29 +333,31 @@ hipError_t dispatch_segmap(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args
   return hipErrorInvalidValue;
 }
 
-// Segment-parallel schedule of the default forward for one long sequence.
-// With few (sequence, head) units the state scan, whose chunks run in
-// order, occupies a fraction of the compute units.  The sequence is then
-// cut into G segments of whole chunks: their affine state maps (segment map
-// kernel, on the prep's blocks), the exclusive scan of the maps from S0
-// (which also gives S_final), and the state scan of every segment from its
-// entering state on the same blocks.  G = min(16, 128 / H, chunks / 16) puts
-// about 128 (segment, head) units on the GPU with segments of 16 chunks or
-// more.  Measured on MI355X (bf16, d = 128, one sequence): 16 heads x 32768
+// Segment-parallel schedule of the default forward for a few long
+// sequences.  With few (sequence, head) units the state scan, whose chunks
+// run in order, occupies a fraction of the compute units.  Every sequence is
+// then cut into G segments of whole chunks: their affine state maps
+// (segment map kernel, on the prep's blocks), the exclusive scan of each
+// sequence's maps from its S0 (which also gives S_final), and the state scan
+// of every segment from its entering state on the same blocks.
+// G = min(16, 128 / (B H), chunks / 16) puts about 128 (segment, head)
+// units on the GPU with segments of 16 chunks or more.  Measured on MI355X (bf16, d = 128, one sequence): 16 heads x 32768
 // tokens 0.71 ms against 0.89 ms for the serial scan, 16 x 16384 0.38
 // against 0.47, 8 x 16384 0.23 against 0.34, 4 x 8192 0.10 against 0.16,
-// 4 x 65536 0.43 against 1.25; with 32 heads, or two sequences of 16 heads,
-// the serial scan is as fast or faster, hence the bounds below.
-int seg_count(int T, int H, int chunk) {
+// 4 x 65536 0.43 against 1.25; with 32 (sequence, head) units (32 heads,
+// or two sequences of 16 heads) the serial scan is as fast or faster, hence
+// the bounds below.
+int seg_count(int T, int units, int chunk) {
   const int nc = (T + chunk - 1) / chunk;
   int g = 16;
-  while (g > 1 && (g * H > 128 || 16 * g > nc))
+  while (g > 1 && (g * units > 128 || 16 * g > nc))
     g /= 2;
   return g;
 }
 
 bool use_segments(int B, int T, int H, int chunk, bool packed) {
-  return !packed && B == 1 && H <= 16 && (T + chunk - 1) / chunk >= 128 && seg_count(T, H, chunk) >= 2;
+  return !packed && static_cast<long>(B) * H <= 16 && (T + chunk - 1) / chunk >= 128 &&
+         static_cast<long>(B) * T <= 0x7fffffffL && seg_count(T, B * H, chunk) >= 2;
 }
 
 struct seg_plan {
@@ -364,47 +366,51 @@ struct seg_plan {
   int seg_tokens;  // L: tokens per segment (whole chunks; the last segment shorter)
 };
 
-seg_plan plan_segments(gdn2_dtype_t dt, int T, int H, int d, int chunk) {
+seg_plan plan_segments(gdn2_dtype_t dt, int B, int T, int H, int d, int chunk) {
   seg_plan p{};
   const int nc = (T + chunk - 1) / chunk;
-  p.G = seg_count(T, H, chunk);
+  p.G = seg_count(T, B * H, chunk);
   p.seg_tokens = (nc + p.G - 1) / p.G * chunk;
-  p.cu = align256(static_cast<size_t>(p.G + 1) * sizeof(int32_t));
+  p.cu = align256(static_cast<size_t>(B * p.G + 1) * sizeof(int32_t));
   p.table = p.cu;
-  p.blocks = align256(static_cast<size_t>(num_slots_for(1, T, p.G, chunk, true)) * H *
+  p.blocks = align256(static_cast<size_t>(num_slots_for(1, B * T, B * p.G, chunk, true)) * H *
                       chunk_block_bytes_rt(dt, d, chunk));
-  p.map_bytes = static_cast<size_t>(p.G) * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
+  p.map_bytes = static_cast<size_t>(B) * p.G * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
   p.total = p.cu + p.table + p.blocks + 3 * p.map_bytes;
   return p;
 }
 
-hipError_t dispatch_combine(int d, const float *Phi, const float *Psi, const float *S0, int G, int H, float *S_in,
-                            float *S_final, hipStream_t st) {
+hipError_t dispatch_combine(int d, const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
+                            float *S_in, float *S_final, hipStream_t st) {
   prof_scope p("segment_combine", st);
   switch (d) {
-    case 16: return gdn2::launch_seg_combine<16>(Phi, Psi, S0, G, H, S_in, S_final, st);
-    case 32: return gdn2::launch_seg_combine<32>(Phi, Psi, S0, G, H, S_in, S_final, st);
-    case 64: return gdn2::launch_seg_combine<64>(Phi, Psi, S0, G, H, S_in, S_final, st);
-    case 128: return gdn2::launch_seg_combine<128>(Phi, Psi, S0, G, H, S_in, S_final, st);
+    case 16: return gdn2::launch_seg_combine<16>(Phi, Psi, S0, G, H, B, S_in, S_final, st);
+    case 32: return gdn2::launch_seg_combine<32>(Phi, Psi, S0, G, H, B, S_in, S_final, st);
+    case 64: return gdn2::launch_seg_combine<64>(Phi, Psi, S0, G, H, B, S_in, S_final, st);
+    case 128: return gdn2::launch_seg_combine<128>(Phi, Psi, S0, G, H, B, S_in, S_final, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// The schedule above; `a` is the call's fixed-length argument block (B = 1).
+// The schedule above; `a` is the call's fixed-length argument block.  The B
+// sequences of T tokens are read as one packed stretch of B T tokens cut
+// into B G segments.
 hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_args &a, char *ws, hipStream_t st) {
-  const seg_plan pl = plan_segments(dt, a.T, a.H, d, chunk);
+  const seg_plan pl = plan_segments(dt, a.B, a.T, a.H, d, chunk);
   int32_t *cu = reinterpret_cast<int32_t *>(ws);
   float *Phi = reinterpret_cast<float *>(ws + pl.cu + pl.table + pl.blocks);
   float *Psi = Phi + pl.map_bytes / sizeof(float);
   float *S_in = Psi + pl.map_bytes / sizeof(float);
-  hipError_t e = gdn2::launch_seg_bounds(cu, pl.G, pl.seg_tokens, a.T, st);
+  hipError_t e = gdn2::launch_seg_bounds(cu, pl.G, pl.seg_tokens, a.T, a.B, st);
   if (e != hipSuccess)
     return e;
   gdn2::chunk_args s = a;
   s.cu = cu;
   s.offsets = reinterpret_cast<int32_t *>(ws + pl.cu);
-  s.num_seqs = pl.G;
-  s.num_slots = num_slots_for(1, a.T, pl.G, chunk, true);
+  s.B = 1;
+  s.T = a.B * a.T;
+  s.num_seqs = a.B * pl.G;
+  s.num_slots = num_slots_for(1, s.T, s.num_seqs, chunk, true);
   s.blocks = ws + pl.cu + pl.table;
   s.S0 = nullptr;
   s.o = nullptr;
@@ -412,7 +418,7 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   e = dispatch_segmap(dt, d, chunk, s, Phi, Psi, st);
   if (e != hipSuccess)
     return e;
-  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, S_in, a.S_final, st);
+  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, a.B, S_in, a.S_final, st);
   if (e != hipSuccess)
     return e;
   s.S0 = S_in;
@@ -439,7 +445,7 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   const size_t table = align256(static_cast<size_t>(n + 1) * sizeof(int32_t));
   const size_t plain = table + slots * static_cast<size_t>(H) * chunk_block_bytes_rt(dt, dk, chunk);
   if (num_seqs <= 0 && use_segments(B, T, H, chunk, false)) {
-    const size_t seg = plan_segments(dt, T, H, dk, chunk).total;
+    const size_t seg = plan_segments(dt, B, T, H, dk, chunk).total;
     return seg > plain ? seg : plain;
   }
   return plain;
@@ -560,7 +566,7 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: no single-pass kernel for dtype %d, dk=%d, chunk=%d",
                 static_cast<int>(dt), dk, chunk);
   if ((flags & (path_flags | GDN2_FLAG_PREPARED)) == 0 && use_segments(B, T, H, chunk, packed) &&
-      workspace_bytes >= plan_segments(dt, T, H, dk, chunk).total) {
+      workspace_bytes >= plan_segments(dt, B, T, H, dk, chunk).total) {
     const hipError_t e = run_segments(dt, dk, chunk, a, ws, st);
     if (e != hipSuccess)
       return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
@@ -777,10 +783,10 @@ gdn2_status_t gdn2_segment_combine(const float *Phi, const float *Psi, const flo
   {
     prof_scope p("segment_combine", st);
     switch (dk) {
-      case 16: e = gdn2::launch_seg_combine<16>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
-      case 32: e = gdn2::launch_seg_combine<32>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
-      case 64: e = gdn2::launch_seg_combine<64>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
-      case 128: e = gdn2::launch_seg_combine<128>(Phi, Psi, S0, G, H, S_in, S_final, st); break;
+      case 16: e = gdn2::launch_seg_combine<16>(Phi, Psi, S0, G, H, 1, S_in, S_final, st); break;
+      case 32: e = gdn2::launch_seg_combine<32>(Phi, Psi, S0, G, H, 1, S_in, S_final, st); break;
+      case 64: e = gdn2::launch_seg_combine<64>(Phi, Psi, S0, G, H, 1, S_in, S_final, st); break;
+      case 128: e = gdn2::launch_seg_combine<128>(Phi, Psi, S0, G, H, 1, S_in, S_final, st); break;
     }
   }
   if (e != hipSuccess)

@@ -61,12 +61,14 @@ template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &
 // Affine state map of every sequence taken as one segment: Phi [N, H, D, D]
 // and Psi [N, H, D, D] float32, row-major, from the prepared blocks.
 template <typename IO, int D, int C> hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_t st);
-// cu[0 .. G] = the bounds of G segments of L tokens of one T-token sequence.
-hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, hipStream_t st);
-// Exclusive scan of G segment maps [G, H, D, D] from S0 [H, D, D] (nullptr: zero).
+// cu[0 .. B G] = the bounds of G segments of L tokens of each of B sequences
+// of T tokens laid end to end.
+hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, int B, hipStream_t st);
+// Exclusive scan of the G segment maps of each of B sequences, [B, G, H, D, D],
+// from S0 [B, H, D, D] (nullptr: zero).
 template <int D>
-hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, float *S_in,
-                              float *S_final, hipStream_t st);
+hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
+                              float *S_in, float *S_final, hipStream_t st);
 
 template <typename IO, int D>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,

@@ -260,10 +260,11 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
       out[(16 * kk + 4 * g + i) * D + 16 * j + m] = s[kk][i];
 }
 
-// One workgroup per (head, 16-column tile j of the state), one wave per
-// 16-row tile kk.  Segments g = 0 .. G-1 of one sequence, maps [G][H][D][D]:
-// writes the state entering every segment to S_in [G][H][D][D] and, if
-// S_final is given, the state after the last one.  Per segment the column
+// One workgroup per (sequence, head, 16-column tile j of the state), one
+// wave per 16-row tile kk.  B sequences of G segments each, maps
+// [B][G][H][D][D] (segment g of sequence b at b G + g), S0 [B][H][D][D]:
+// writes the state entering every segment to S_in [B][G][H][D][D] and, if
+// S_final is given, the state after the last one, [B][H][D][D].  Per segment the column
 // of state tiles (., j) sits in LDS and wave kk forms its tile of
 // Psi_g + Phi_g S from row tile kk of Phi_g, loaded one segment ahead.
 // float32 throughout (products as in mm<float>).
@@ -271,20 +272,27 @@ template <int D>
 __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const float *__restrict__ Phi,
                                                                          const float *__restrict__ Psi,
                                                                          const float *__restrict__ S0, int G, int H,
-                                                                         float *__restrict__ S_in,
+                                                                         int B, float *__restrict__ S_in,
                                                                          float *__restrict__ S_final) {
   constexpr int NK = D / 16;
   __shared__ f32x4 col[NK][64];  // ColFrag of the state tiles (k2, j)
-  const int h = static_cast<int>(blockIdx.x) / NK, j = static_cast<int>(blockIdx.x) % NK;
-  if (h >= H)
+  const int bh = static_cast<int>(blockIdx.x) / NK, j = static_cast<int>(blockIdx.x) % NK;
+  if (bh >= B * H)
     return;
+  const int b = bh / H, h = bh - b * H;
+  // maps and entering states of sequence b: segment g is row b G + g; its
+  // head h is then at ((b G + g) H + h), i.e. at (g H' + h) from Phi_b
+  // with H' = H
+  Phi += static_cast<size_t>(b) * G * H * D * D;
+  Psi += static_cast<size_t>(b) * G * H * D * D;
+  S_in += static_cast<size_t>(b) * G * H * D * D;
   const int kk = static_cast<int>(threadIdx.x) >> 6, lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   // element i of this lane's ColFrag of tile (kk, j) within one D x D matrix
   auto at = [&](int i) { return static_cast<size_t>(16 * kk + 4 * g + i) * D + 16 * j + m; };
   f32x4 s;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    s[i] = S0 ? S0[static_cast<size_t>(h) * D * D + at(i)] : 0.f;
+    s[i] = S0 ? S0[static_cast<size_t>(bh) * D * D + at(i)] : 0.f;
   f32x4 ph[NK], ps;  // RowFrag of Phi tiles (kk, k2); ColFrag of Psi tile (kk, j)
   auto load = [&](int seg) {
     const size_t base = (static_cast<size_t>(seg) * H + h) * D * D;
@@ -319,7 +327,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
   if (S_final) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      S_final[static_cast<size_t>(h) * D * D + at(i)] = s[i];
+      S_final[static_cast<size_t>(bh) * D * D + at(i)] = s[i];
   }
 }
 
@@ -333,27 +341,29 @@ hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_
 }
 
 template <int D>
-hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, float *S_in,
-                              float *S_final, hipStream_t st) {
-  hipLaunchKernelGGL((gdn2_seg_combine_kernel<D>), dim3(H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi, Psi, S0, G,
-                     H, S_in, S_final);
+hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
+                              float *S_in, float *S_final, hipStream_t st) {
+  hipLaunchKernelGGL((gdn2_seg_combine_kernel<D>), dim3(B * H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi, Psi, S0,
+                     G, H, B, S_in, S_final);
   return hipGetLastError();
 }
 
-// Bounds of G segments of one sequence of T tokens, L tokens each (the last
-// shorter): cu[i] = min(i L, T), i = 0 .. G.
-__global__ void gdn2_seg_bounds_kernel(int32_t *cu, int G, int L, int T) {
+// Bounds of G segments of each of B sequences of T tokens laid end to end,
+// L tokens per segment (the last of a sequence shorter): segment g of
+// sequence b starts at b T + min(g L, T); cu[B G] = B T.
+__global__ void gdn2_seg_bounds_kernel(int32_t *cu, int G, int L, int T, int B) {
   const int i = static_cast<int>(threadIdx.x);
-  if (i <= G) {
-    const long x = static_cast<long>(i) * L;
-    cu[i] = static_cast<int32_t>(x < T ? x : T);
+  if (i <= B * G) {
+    const int b = i / G, g = i - b * G;
+    const long x = static_cast<long>(g) * L;
+    cu[i] = static_cast<int32_t>(static_cast<long>(b) * T + (x < T ? x : T));
   }
 }
 
-hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, hipStream_t st) {
-  if (G < 1 || G > 255)
+hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, int B, hipStream_t st) {
+  if (G < 1 || B < 1 || B * G > 255 || static_cast<long>(B) * T > 0x7fffffffL)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gdn2_seg_bounds_kernel, dim3(1), dim3(256), 0, st, cu, G, L, T);
+  hipLaunchKernelGGL(gdn2_seg_bounds_kernel, dim3(1), dim3(256), 0, st, cu, G, L, T, B);
   return hipGetLastError();
 }
 
@@ -377,13 +387,13 @@ GDN2_INST_SEG(bf16_t, 32, 64)
 GDN2_INST_SEG(bf16_t, 64, 64)
 GDN2_INST_SEG(bf16_t, 128, 64)
 
-template hipError_t launch_seg_combine<16>(const float *, const float *, const float *, int, int, float *, float *,
+template hipError_t launch_seg_combine<16>(const float *, const float *, const float *, int, int, int, float *, float *,
                                            hipStream_t);
-template hipError_t launch_seg_combine<32>(const float *, const float *, const float *, int, int, float *, float *,
+template hipError_t launch_seg_combine<32>(const float *, const float *, const float *, int, int, int, float *, float *,
                                            hipStream_t);
-template hipError_t launch_seg_combine<64>(const float *, const float *, const float *, int, int, float *, float *,
+template hipError_t launch_seg_combine<64>(const float *, const float *, const float *, int, int, int, float *, float *,
                                            hipStream_t);
-template hipError_t launch_seg_combine<128>(const float *, const float *, const float *, int, int, float *, float *,
+template hipError_t launch_seg_combine<128>(const float *, const float *, const float *, int, int, int, float *, float *,
                                             hipStream_t);
 
 }  // namespace gdn2

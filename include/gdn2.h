@@ -124,7 +124,7 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and
  * the sequence count num_seqs; without, num_seqs is ignored (it is B).  For
- * one long sequence the figure includes the segment schedule's maps (see
+ * a few long sequences the figure includes the segment schedule's maps (see
  * gdn2_chunk_fwd, flags). */
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk, gdn2_dtype_t dt);
@@ -144,12 +144,12 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               GDN2_FLAG_FUSED, plus any of the gate layout flags, and
  *               GDN2_FLAG_PREPARED (two-pass path implied).  With no
  *               path flag the library runs the two-pass chunked kernels (all
- *               chunks in parallel, then the state scan).  For one
- *               fixed-length sequence (B = 1, no cu_seqlens) of at least 128
- *               chunks and at most 16 heads, given the workspace
- *               gdn2_chunk_fwd_workspace_bytes reports for it, the default
- *               path cuts the sequence into G = min(16, 128 / H, chunks / 16)
- *               segments of whole chunks (8 or 16): the
+ *               chunks in parallel, then the state scan).  For
+ *               fixed-length sequences (no cu_seqlens) of at least 128
+ *               chunks with B H <= 16, given the workspace
+ *               gdn2_chunk_fwd_workspace_bytes reports for them, the default
+ *               path cuts every sequence into G = min(16, 128 / (B H),
+ *               chunks / 16) segments of whole chunks (8 or 16): the
  *               segments' state maps (as gdn2_chunk_segment_map), their scan
  *               from S0 (as gdn2_segment_combine, which also gives S_final),
  *               and every segment's state scan from its entering state, so

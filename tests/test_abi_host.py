@@ -86,11 +86,11 @@ def test_workspace_bytes(L):
 
 
 def test_workspace_bytes_long_sequence(L):
-    # One sequence of 128 chunks or more with at most 16 heads also reserves
-    # the segment schedule: G = min(16, 128 / H, chunks / 16) segments, their
-    # bounds, chunk table, blocks of the packed layout, and Phi, Psi, S_in.
-    # Shorter sequences, more heads, batches and packed input get the plain
-    # size.
+    # B sequences of 128 chunks or more with at most 16 (sequence, head)
+    # units also reserve the segment schedule: G = min(16, 128 / (B H),
+    # chunks / 16) segments per sequence, their bounds, chunk table, blocks of
+    # the packed layout, and Phi, Psi, S_in.  Shorter sequences, more units
+    # and packed input get the plain size.
     d, C = 128, 64
 
     def ws(B, T, H, n=0):
@@ -103,18 +103,20 @@ def test_workspace_bytes_long_sequence(L):
         nc = -(-T // C)
         return 256 * (-(-(B + 1) * 4 // 256)) + max(B * nc, nc + B) * H * blk
 
-    def seg(T, H, G):
-        nc = -(-T // C)
-        blocks = (nc + G) * H * blk
-        return 2 * 256 * (-(-(G + 1) * 4 // 256)) + -(-blocks // 256) * 256 + 3 * G * H * d * d * 4
+    def seg(B, T, H, G):
+        nt = -(-(B * T) // C)
+        blocks = (nt + B * G) * H * blk
+        return 2 * 256 * (-(-(B * G + 1) * 4 // 256)) + -(-blocks // 256) * 256 + 3 * B * G * H * d * d * 4
 
-    assert ws(1, 32768, 16) == max(plain(1, 32768, 16), seg(32768, 16, 8))
+    assert ws(1, 32768, 16) == max(plain(1, 32768, 16), seg(1, 32768, 16, 8))
     assert ws(1, 32768, 16) > plain(1, 32768, 16)
-    assert ws(1, 40000, 3) == max(plain(1, 40000, 3), seg(40000, 3, 16))      # 625 chunks, 3 heads
-    assert ws(1, 128 * C, 16) == max(plain(1, 128 * C, 16), seg(128 * C, 16, 8))
-    assert ws(1, 256 * C, 8) == max(plain(1, 256 * C, 8), seg(256 * C, 8, 16))
+    assert ws(1, 40000, 3) == max(plain(1, 40000, 3), seg(1, 40000, 3, 16))      # 625 chunks, 3 heads
+    assert ws(1, 128 * C, 16) == max(plain(1, 128 * C, 16), seg(1, 128 * C, 16, 8))
+    assert ws(1, 256 * C, 8) == max(plain(1, 256 * C, 8), seg(1, 256 * C, 8, 16))
+    assert ws(2, 256 * C, 8) == max(plain(2, 256 * C, 8), seg(2, 256 * C, 8, 8))  # 16 (sequence, head) units
+    assert ws(4, 200 * C, 2) == max(plain(4, 200 * C, 2), seg(4, 200 * C, 2, 8))
     assert ws(1, 127 * C, 16) == plain(1, 127 * C, 16)       # 127 chunks
-    assert ws(2, 32768, 16) == plain(2, 32768, 16)           # two sequences
+    assert ws(2, 32768, 16) == plain(2, 32768, 16)           # 32 units
     assert ws(1, 32768, 17) == plain(1, 32768, 17)           # 17 heads
     assert ws(1, 32768, 16, 1) == plain(1, 32768, 16)        # packed
 

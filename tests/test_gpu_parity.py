@@ -295,16 +295,17 @@ def test_sweep_endpoints_sampled(g):
               f"sweep T={T}")
 
 
-@pytest.mark.parametrize("dtype,d,H,T", [("f32", 64, 2, 512 * 64 + 100), ("bf16", 128, 4, 512 * 64 + 37),
-                                         ("bf16", 64, 16, 130 * 64 + 5)])
-def test_long_sequence_segment_schedule(g, dtype, d, H, T):
-    """One sequence of 128 chunks or more on the default path: the library
-    cuts it into 16 segments (2 and 4 heads) or 8 (16 heads): maps, their
-    scan, every segment's scan from its entering state.  Checked against
-    the oracle with an initial state, a ragged last segment, and S_final
-    written over S0."""
-    inp = gi.make_chunk_inputs(1, T, H, d, d, dtype, seed=41 + d, s0="normal", alpha_mean=8.0)
-    print(f"case segment schedule {dtype} d={d} H={H} T={T}", flush=True)
+@pytest.mark.parametrize("dtype,d,B,H,T", [("f32", 64, 1, 2, 512 * 64 + 100), ("bf16", 128, 1, 4, 512 * 64 + 37),
+                                           ("bf16", 64, 1, 16, 130 * 64 + 5), ("bf16", 64, 2, 4, 130 * 64 + 5),
+                                           ("f32", 32, 4, 2, 160 * 64 - 3)])
+def test_long_sequence_segment_schedule(g, dtype, d, B, H, T):
+    """Sequences of 128 chunks or more with at most 16 (sequence, head)
+    units on the default path: the library cuts every sequence into 8 or
+    16 segments (maps, the scan of each sequence's maps, every segment's
+    scan from its entering state).  Checked against the oracle with initial
+    states, ragged last segments, and S_final written over S0."""
+    inp = gi.make_chunk_inputs(B, T, H, d, d, dtype, seed=41 + d + B, s0="normal", alpha_mean=8.0)
+    print(f"case segment schedule {dtype} d={d} B={B} H={H} T={T}", flush=True)
     dd = to_dev(inp)
     S = dd["S0"].clone()
     o, _ = g.chunk_fwd(*(dd[n] for n in NAMES), S0=S, S_final=S, chunk=64)
