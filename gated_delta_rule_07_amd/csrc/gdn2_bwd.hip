@@ -355,7 +355,6 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     return (GN && LPm) ? sig4(x) : x;
   };
   auto ld_b = [&](int c0) { return ld_gate(b, SBm, c0); };
-  auto ld_w = [&](int c0) { return ld_gate(w, SWm, c0); };
   // alpha itself (not under layer prep)
   auto ld_alpha = [&](int c0) -> f32x4 {
     if (GN && SAm) {

@@ -198,12 +198,14 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
       return;  // the compute waves take no barrier either
     const int lw = wave - NCW;
     // byte offset in the block of LDS piece p (SHARED, then Ut rows, then O_intra rows)
+    // (Ut / O_intra pieces exist only when UO_LDS, i.e. RPP >= 1)
     auto piece_src = [&](int p) -> size_t {
+      constexpr int R = RPP > 0 ? RPP : 1;
       if (p < NPS)
         return static_cast<size_t>(p) * 1024;
       const int q = p - NPS;
-      const int region = q / (NB * RPP), rem = q % (NB * RPP);
-      return (region ? L::OI : L::UT) + tile_off<IO, NK>(rem / RPP, vtf, 0) + static_cast<size_t>(rem % RPP) * 1024;
+      const int region = q / (NB * R), rem = q % (NB * R);
+      return (region ? L::OI : L::UT) + tile_off<IO, NK>(rem / R, vtf, 0) + static_cast<size_t>(rem % R) * 1024;
     };
     int src_off[PPW];
 #pragma unroll
