@@ -334,48 +334,61 @@ hipError_t dispatch_segmap(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args
 }
 
 // Segment-parallel schedule of the default forward for a few long
-// sequences.  With few (sequence, head) units the state scan, whose chunks
-// run in order, occupies a fraction of the compute units.  Every sequence is
-// then cut into G segments of whole chunks: their affine state maps
-// (segment map kernel, on the prep's blocks), the exclusive scan of each
-// sequence's maps from its S0 (which also gives S_final), and the state scan
-// of every segment from its entering state on the same blocks.
-// G = min(16, 128 / (B H), chunks / 16) puts about 128 (segment, head)
-// units on the GPU with segments of 16 chunks or more.  Measured on MI355X (bf16, d = 128, one sequence): 16 heads x 32768
+// sequences (fixed-length or packed).  With few (sequence, head) units the
+// state scan, whose chunks run in order, occupies a fraction of the compute
+// units.  Every sequence is then cut into G segments of whole chunks: their
+// affine state maps (segment map kernel, on the prep's blocks), the
+// exclusive scan of each sequence's maps from its S0 (which also gives
+// S_final), and the state scan of every segment from its entering state on
+// the same blocks.  G = min(16, 128 / (N H), chunks / 16), with N sequences
+// of (on average) `chunks` chunks, puts about 128 (segment, head) units on
+// the GPU with segments of 16 chunks or more.  Measured on MI355X (bf16,
+// d = 128, one sequence): 16 heads x 32768
 // tokens 0.71 ms against 0.89 ms for the serial scan, 16 x 16384 0.38
 // against 0.47, 8 x 16384 0.23 against 0.34, 4 x 8192 0.10 against 0.16,
 // 4 x 65536 0.43 against 1.25; with 32 (sequence, head) units (32 heads,
 // or two sequences of 16 heads) the serial scan is as fast or faster, hence
 // the bounds below.
-int seg_count(int T, int units, int chunk) {
-  const int nc = (T + chunk - 1) / chunk;
+int seg_count(int nc, int units) {
   int g = 16;
   while (g > 1 && (g * units > 128 || 16 * g > nc))
     g /= 2;
   return g;
 }
 
-bool use_segments(int B, int T, int H, int chunk, bool packed) {
-  return !packed && static_cast<long>(B) * H <= 16 && (T + chunk - 1) / chunk >= 128 &&
-         static_cast<long>(B) * T <= 0x7fffffffL && seg_count(T, B * H, chunk) >= 2;
+// Sizes of a call as the schedule sees them: N sequences, T_total tokens in
+// all, nc chunks per sequence (packed: the mean).
+struct seg_shape {
+  int N, T_total, nc;
+};
+
+seg_shape seg_shape_of(int B, int T, int num_seqs, int chunk, bool packed) {
+  seg_shape x{};
+  x.N = packed ? num_seqs : B;
+  const long tt = packed ? static_cast<long>(T) : static_cast<long>(B) * T;
+  x.T_total = tt > 0x7fffffffL ? -1 : static_cast<int>(tt);
+  x.nc = x.N > 0 ? (packed ? static_cast<int>((tt + chunk - 1) / chunk / x.N) : (T + chunk - 1) / chunk) : 0;
+  return x;
+}
+
+bool use_segments(const seg_shape &x, int H) {
+  return x.N > 0 && x.T_total > 0 && static_cast<long>(x.N) * H <= 16 && x.nc >= 128 && seg_count(x.nc, x.N * H) >= 2;
 }
 
 struct seg_plan {
   size_t cu, table, blocks, map_bytes, total;
-  int G;           // segments
-  int seg_tokens;  // L: tokens per segment (whole chunks; the last segment shorter)
+  int G;  // segments per sequence
 };
 
-seg_plan plan_segments(gdn2_dtype_t dt, int B, int T, int H, int d, int chunk) {
+seg_plan plan_segments(gdn2_dtype_t dt, const seg_shape &x, int H, int d, int chunk) {
   seg_plan p{};
-  const int nc = (T + chunk - 1) / chunk;
-  p.G = seg_count(T, B * H, chunk);
-  p.seg_tokens = (nc + p.G - 1) / p.G * chunk;
-  p.cu = align256(static_cast<size_t>(B * p.G + 1) * sizeof(int32_t));
+  p.G = seg_count(x.nc, x.N * H);
+  const int nseg = x.N * p.G;
+  p.cu = align256(static_cast<size_t>(nseg + 1) * sizeof(int32_t));
   p.table = p.cu;
-  p.blocks = align256(static_cast<size_t>(num_slots_for(1, B * T, B * p.G, chunk, true)) * H *
+  p.blocks = align256(static_cast<size_t>(num_slots_for(1, x.T_total, nseg, chunk, true)) * H *
                       chunk_block_bytes_rt(dt, d, chunk));
-  p.map_bytes = static_cast<size_t>(B) * p.G * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
+  p.map_bytes = static_cast<size_t>(nseg) * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
   p.total = p.cu + p.table + p.blocks + 3 * p.map_bytes;
   return p;
 }
@@ -392,24 +405,25 @@ hipError_t dispatch_combine(int d, const float *Phi, const float *Psi, const flo
   }
 }
 
-// The schedule above; `a` is the call's fixed-length argument block.  The B
-// sequences of T tokens are read as one packed stretch of B T tokens cut
-// into B G segments.
-hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_args &a, char *ws, hipStream_t st) {
-  const seg_plan pl = plan_segments(dt, a.B, a.T, a.H, d, chunk);
+// The schedule above; `a` is the call's argument block (fixed-length or
+// packed).  The N sequences are read as one packed stretch of tokens cut
+// into N G segments, whose bounds a small kernel derives on the device.
+hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_args &a, const seg_shape &x, char *ws,
+                        hipStream_t st) {
+  const seg_plan pl = plan_segments(dt, x, a.H, d, chunk);
   int32_t *cu = reinterpret_cast<int32_t *>(ws);
   float *Phi = reinterpret_cast<float *>(ws + pl.cu + pl.table + pl.blocks);
   float *Psi = Phi + pl.map_bytes / sizeof(float);
   float *S_in = Psi + pl.map_bytes / sizeof(float);
-  hipError_t e = gdn2::launch_seg_bounds(cu, pl.G, pl.seg_tokens, a.T, a.B, st);
+  hipError_t e = gdn2::launch_seg_bounds(a.cu, cu, pl.G, a.T, x.N, chunk, st);
   if (e != hipSuccess)
     return e;
   gdn2::chunk_args s = a;
   s.cu = cu;
   s.offsets = reinterpret_cast<int32_t *>(ws + pl.cu);
   s.B = 1;
-  s.T = a.B * a.T;
-  s.num_seqs = a.B * pl.G;
+  s.T = x.T_total;
+  s.num_seqs = x.N * pl.G;
   s.num_slots = num_slots_for(1, s.T, s.num_seqs, chunk, true);
   s.blocks = ws + pl.cu + pl.table;
   s.S0 = nullptr;
@@ -418,7 +432,7 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   e = dispatch_segmap(dt, d, chunk, s, Phi, Psi, st);
   if (e != hipSuccess)
     return e;
-  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, a.B, S_in, a.S_final, st);
+  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, x.N, S_in, a.S_final, st);
   if (e != hipSuccess)
     return e;
   s.S0 = S_in;
@@ -444,8 +458,9 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   const size_t slots = slots_packed > slots_fixed ? slots_packed : slots_fixed;
   const size_t table = align256(static_cast<size_t>(n + 1) * sizeof(int32_t));
   const size_t plain = table + slots * static_cast<size_t>(H) * chunk_block_bytes_rt(dt, dk, chunk);
-  if (num_seqs <= 0 && use_segments(B, T, H, chunk, false)) {
-    const size_t seg = plan_segments(dt, B, T, H, dk, chunk).total;
+  const seg_shape x = seg_shape_of(B, T, num_seqs, chunk, num_seqs > 0);
+  if (use_segments(x, H)) {
+    const size_t seg = plan_segments(dt, x, H, dk, chunk).total;
     return seg > plain ? seg : plain;
   }
   return plain;
@@ -565,9 +580,10 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   if ((flags & GDN2_FLAG_FUSED) && !fused_available(dt, dk, chunk))
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: no single-pass kernel for dtype %d, dk=%d, chunk=%d",
                 static_cast<int>(dt), dk, chunk);
-  if ((flags & (path_flags | GDN2_FLAG_PREPARED)) == 0 && use_segments(B, T, H, chunk, packed) &&
-      workspace_bytes >= plan_segments(dt, B, T, H, dk, chunk).total) {
-    const hipError_t e = run_segments(dt, dk, chunk, a, ws, st);
+  const seg_shape sx = seg_shape_of(B, T, N, chunk, packed);
+  if ((flags & (path_flags | GDN2_FLAG_PREPARED)) == 0 && use_segments(sx, H) &&
+      workspace_bytes >= plan_segments(dt, sx, H, dk, chunk).total) {
+    const hipError_t e = run_segments(dt, dk, chunk, a, sx, ws, st);
     if (e != hipSuccess)
       return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -61,9 +61,10 @@ template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &
 // Affine state map of every sequence taken as one segment: Phi [N, H, D, D]
 // and Psi [N, H, D, D] float32, row-major, from the prepared blocks.
 template <typename IO, int D, int C> hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_t st);
-// cu[0 .. B G] = the bounds of G segments of L tokens of each of B sequences
-// of T tokens laid end to end.
-hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, int B, hipStream_t st);
+// seg_cu[0 .. B G] = the bounds of G segments of whole chunks (C tokens) of
+// each of B sequences laid end to end: packed ones given by cu, else B
+// sequences of T tokens (cu == nullptr).
+hipError_t launch_seg_bounds(const int32_t *cu, int32_t *seg_cu, int G, int T, int B, int C, hipStream_t st);
 // Exclusive scan of the G segment maps of each of B sequences, [B, G, H, D, D],
 // from S0 [B, H, D, D] (nullptr: zero).
 template <int D>

@@ -348,22 +348,28 @@ hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S
   return hipGetLastError();
 }
 
-// Bounds of G segments of each of B sequences of T tokens laid end to end,
-// L tokens per segment (the last of a sequence shorter): segment g of
-// sequence b starts at b T + min(g L, T); cu[B G] = B T.
-__global__ void gdn2_seg_bounds_kernel(int32_t *cu, int G, int L, int T, int B) {
-  const int i = static_cast<int>(threadIdx.x);
-  if (i <= B * G) {
-    const int b = i / G, g = i - b * G;
+// Bounds of G segments of each of B sequences laid end to end: sequence b
+// spans [cu[b], cu[b+1]) when cu is given (packed input), else [b T, b T + T).
+// Its segments hold ceil(chunks / G) chunks each, the last ones shorter or
+// empty: segment g starts at start_b + min(g L_b, len_b).  seg_cu[B G] is the
+// end of the last sequence.
+__global__ void gdn2_seg_bounds_kernel(const int32_t *__restrict__ cu, int32_t *__restrict__ seg_cu, int G, int T,
+                                       int B, int C) {
+  for (int i = static_cast<int>(threadIdx.x); i <= B * G; i += static_cast<int>(blockDim.x)) {
+    const int b = i < B * G ? i / G : B - 1, g = i < B * G ? i - b * G : G;
+    const long start = cu ? static_cast<long>(cu[b]) : static_cast<long>(b) * T;
+    const long len = cu ? static_cast<long>(cu[b + 1]) - cu[b] : static_cast<long>(T);
+    const long nc = (len + C - 1) / C;
+    const long L = (nc + G - 1) / G * C;
     const long x = static_cast<long>(g) * L;
-    cu[i] = static_cast<int32_t>(static_cast<long>(b) * T + (x < T ? x : T));
+    seg_cu[i] = static_cast<int32_t>(start + (x < len ? x : len));
   }
 }
 
-hipError_t launch_seg_bounds(int32_t *cu, int G, int L, int T, int B, hipStream_t st) {
-  if (G < 1 || B < 1 || B * G > 255 || static_cast<long>(B) * T > 0x7fffffffL)
+hipError_t launch_seg_bounds(const int32_t *cu, int32_t *seg_cu, int G, int T, int B, int C, hipStream_t st) {
+  if (G < 1 || B < 1 || C < 1)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gdn2_seg_bounds_kernel, dim3(1), dim3(256), 0, st, cu, G, L, T, B);
+  hipLaunchKernelGGL(gdn2_seg_bounds_kernel, dim3(1), dim3(256), 0, st, cu, seg_cu, G, T, B, C);
   return hipGetLastError();
 }
 

@@ -144,12 +144,13 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               GDN2_FLAG_FUSED, plus any of the gate layout flags, and
  *               GDN2_FLAG_PREPARED (two-pass path implied).  With no
  *               path flag the library runs the two-pass chunked kernels (all
- *               chunks in parallel, then the state scan).  For
- *               fixed-length sequences (no cu_seqlens) of at least 128
- *               chunks with B H <= 16, given the workspace
+ *               chunks in parallel, then the state scan).  For N
+ *               sequences (B, or num_seqs packed) of at least 128 chunks (on
+ *               average, packed) with N H <= 16, given the workspace
  *               gdn2_chunk_fwd_workspace_bytes reports for them, the default
- *               path cuts every sequence into G = min(16, 128 / (B H),
- *               chunks / 16) segments of whole chunks (8 or 16): the
+ *               path cuts every sequence into G = min(16, 128 / (N H),
+ *               chunks / 16) segments of whole chunks (8 or 16; bounds
+ *               computed on the device from cu_seqlens when packed): the
  *               segments' state maps (as gdn2_chunk_segment_map), their scan
  *               from S0 (as gdn2_segment_combine, which also gives S_final),
  *               and every segment's state scan from its entering state, so

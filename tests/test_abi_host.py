@@ -88,9 +88,9 @@ def test_workspace_bytes(L):
 def test_workspace_bytes_long_sequence(L):
     # B sequences of 128 chunks or more with at most 16 (sequence, head)
     # units also reserve the segment schedule: G = min(16, 128 / (B H),
-    # chunks / 16) segments per sequence, their bounds, chunk table, blocks of
-    # the packed layout, and Phi, Psi, S_in.  Shorter sequences, more units
-    # and packed input get the plain size.
+    # chunks / 16) segments per sequence (packed: the mean length), their
+    # bounds, chunk table, blocks of the packed layout, and Phi, Psi, S_in.
+    # Shorter sequences and more units get the plain size.
     d, C = 128, 64
 
     def ws(B, T, H, n=0):
@@ -99,12 +99,14 @@ def test_workspace_bytes_long_sequence(L):
     blk = (ws(1, C, 1) - 256) // 2          # one chunk slot of one head (B = 1 reserves nc + 1 slots)
     assert blk > 0 and ws(1, C, 1) == 256 + 2 * blk
 
-    def plain(B, T, H):
+    def plain(B, T, H, n=0):
         nc = -(-T // C)
-        return 256 * (-(-(B + 1) * 4 // 256)) + max(B * nc, nc + B) * H * blk
+        m = n if n > 0 else B
+        return 256 * (-(-(m + 1) * 4 // 256)) + max(B * nc, nc + m) * H * blk
 
-    def seg(B, T, H, G):
-        nt = -(-(B * T) // C)
+    def seg(B, T, H, G, total=None):
+        # B sequences of T tokens (or `total` tokens in all, packed), G segments each
+        nt = -(-(total if total is not None else B * T) // C)
         blocks = (nt + B * G) * H * blk
         return 2 * 256 * (-(-(B * G + 1) * 4 // 256)) + -(-blocks // 256) * 256 + 3 * B * G * H * d * d * 4
 
@@ -118,7 +120,10 @@ def test_workspace_bytes_long_sequence(L):
     assert ws(1, 127 * C, 16) == plain(1, 127 * C, 16)       # 127 chunks
     assert ws(2, 32768, 16) == plain(2, 32768, 16)           # 32 units
     assert ws(1, 32768, 17) == plain(1, 32768, 17)           # 17 heads
-    assert ws(1, 32768, 16, 1) == plain(1, 32768, 16)        # packed
+    assert ws(1, 32768, 16, 1) == max(plain(1, 32768, 16), seg(1, 32768, 16, 8))   # one packed sequence
+    assert ws(1, 32768, 8, 2) == max(plain(1, 32768, 8, 2), seg(2, 16384, 8, 8))   # two, 256 chunks on average
+    assert ws(1, 32768, 16, 2) == plain(1, 32768, 16, 2)     # 32 units
+    assert ws(1, 32768, 4, 3) == max(plain(1, 32768, 4, 3), seg(3, 0, 4, 8, total=32768))
 
 
 def test_decode_rejects_before_launch(L):

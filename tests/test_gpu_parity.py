@@ -314,6 +314,23 @@ def test_long_sequence_segment_schedule(g, dtype, d, B, H, T):
     check(o.float().cpu().numpy(), S.cpu().numpy(), o_ref, S_ref, TOL[dtype], f"segments {dtype} d={d}")
 
 
+@pytest.mark.parametrize("dtype,d,H,lens", [("bf16", 64, 8, [512 * 64 + 21]),
+                                            ("f32", 64, 4, [30000, 0, 37, 5000])])
+def test_long_packed_segment_schedule(g, dtype, d, H, lens):
+    """Packed input of at most 16 (sequence, head) units averaging 128
+    chunks or more: the segment bounds come from cu_seqlens on the device
+    (G segments per sequence; short sequences leave empty segments, an empty
+    sequence only empty ones).  Checked against the oracle."""
+    cu = gi.cu_seqlens_from(lens)
+    T = int(cu[-1])
+    inp = gi.make_chunk_inputs(1, T, H, d, d, dtype, seed=47 + d, s0="normal", num_seqs=len(lens),
+                               alpha_mean=8.0)
+    print(f"case packed segment schedule {dtype} d={d} H={H} lens={lens}", flush=True)
+    o, Sf = gpu_fwd(g, inp, 64, cu=cu)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], cu_seqlens=cu)
+    check(o, Sf, o_ref, S_ref, TOL[dtype], f"packed segments {dtype} d={d}")
+
+
 def test_long_sequence_small_workspace_runs_the_serial_scan(g):
     """With a workspace sized for the plain two-pass path only, the default
     path runs it: the result equals the forced two-pass call bit for bit."""
@@ -322,8 +339,9 @@ def test_long_sequence_small_workspace_runs_the_serial_scan(g):
     print(f"case small workspace T={T}", flush=True)
     dd = to_dev(inp)
     o_t, S_t = g.chunk_fwd(*(dd[n] for n in NAMES), S0=dd["S0"], chunk=C, path="two_pass")
-    # the packed layout's size never includes the segment schedule
-    ws_small = g.workspace_bytes(1, T, H, d, d, 1, C, torch.bfloat16)
+    # the plain two-pass size: a table and nc + 1 chunk slots of H heads
+    slot_h = (g.workspace_bytes(1, C, H, d, d, 0, C, torch.bfloat16) - 256) // 2
+    ws_small = 256 + (T // C + 1) * slot_h
     assert ws_small < g.workspace_bytes(1, T, H, d, d, 0, C, torch.bfloat16)
     ws = torch.empty(ws_small, dtype=torch.uint8, device="cuda")
     o_a, S_a = g.chunk_fwd(*(dd[n] for n in NAMES), S0=dd["S0"], chunk=C, workspace=ws)
