@@ -331,6 +331,22 @@ def test_long_packed_segment_schedule(g, dtype, d, H, lens):
     check(o, Sf, o_ref, S_ref, TOL[dtype], f"packed segments {dtype} d={d}")
 
 
+def test_long_sequence_segment_schedule_chunk16_no_states(g):
+    """The segment schedule with chunk 16 (3000 tokens = 188 chunks, G = 8),
+    no initial state and no final state wanted."""
+    B, T, H, d, C = 1, 3000, 2, 32, 16
+    inp = gi.make_chunk_inputs(B, T, H, d, d, "f32", seed=53, s0=None, alpha_mean=8.0)
+    print(f"case segment schedule chunk 16 T={T}", flush=True)
+    dd = to_dev(inp)
+    o, Sf = g.chunk_fwd(*(dd[n] for n in NAMES), chunk=C, want_final=False)
+    torch.cuda.synchronize()
+    assert Sf is None
+    o_ref, _ = oracle.fwd(*(inp[n] for n in NAMES))
+    e = rel_err(o.cpu().numpy(), o_ref)
+    print(f"segments chunk 16 err_o={e:.3e}", flush=True)
+    assert e <= TOL["f32"]
+
+
 def test_long_sequence_small_workspace_runs_the_serial_scan(g):
     """With a workspace sized for the plain two-pass path only, the default
     path runs it: the result equals the forced two-pass call bit for bit."""
