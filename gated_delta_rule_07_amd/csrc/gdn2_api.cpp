@@ -222,7 +222,96 @@ int num_slots_for(int B, int T, int num_seqs, int chunk, bool packed) {
 }
 
 // ---------------------------------------------------------------- backward --
-template <typename IO, int D, int C> hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, hipStream_t st) {
+// The backward's share of the segment schedule (see run_segments): N
+// sequences of T_total tokens in all, G segments each, and its workspace
+// (bounds, chunk table, then Phi, Psi, S_in, Psi', X: [N, G, H, D, D]
+// float32 each).
+struct seg_run {
+  char *ws;
+  size_t cu_bytes;
+  int N, G, T_total;
+};
+
+// Segment schedule of the backward.  The segments are whole chunks in
+// order, so their chunk slots are numbered as the call's own: the blocks,
+// states and state gradients land where the plain backward puts them.
+//   states: the segment maps from the prep's blocks, their scan from S0,
+//     and the states-mode scan of every segment from its entering state;
+//   state gradients: the reverse scan of every segment from zero gives
+//     Psi'_g, the gradient of the state before segment g from g's own
+//     outputs; the adjoint scan X(g - 1) = Phi_g^T X(g) + Psi'_g from
+//     dL/dS_final gives the gradient after every segment (and dL/dS0); the
+//     reverse scan of every segment from X(g) writes the final gradients.
+template <typename IO, int D, int C>
+hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  const gdn2::chunk_args &a = ba.f;
+  const int nseg = sg.N * sg.G;
+  const size_t mb = static_cast<size_t>(nseg) * a.H * D * D;
+  int32_t *scu = reinterpret_cast<int32_t *>(sg.ws);
+  int32_t *stab = reinterpret_cast<int32_t *>(sg.ws + sg.cu_bytes);
+  float *Phi = reinterpret_cast<float *>(sg.ws + 2 * sg.cu_bytes);
+  float *Psi = Phi + mb, *S_in = Psi + mb, *Psi2 = S_in + mb, *X = Psi2 + mb;
+  gdn2::chunk_args s = a;
+  s.cu = scu;
+  s.offsets = stab;
+  s.B = 1;
+  s.T = sg.T_total;
+  s.num_seqs = nseg;
+  s.num_slots = num_slots_for(1, sg.T_total, nseg, C_rt, true);
+  s.S0 = nullptr;
+  s.S_final = nullptr;
+  s.o = nullptr;
+  if ((e = gdn2::launch_seg_bounds(a.cu, scu, sg.G, a.T, sg.N, C_rt, st)) != hipSuccess)
+    return e;
+  {
+    prof_scope p("chunk_table", st);
+    if ((e = gdn2::launch_chunk_table(scu, nseg, C_rt, stab, st)) != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("chunk_prep", st);
+    if ((e = gdn2::launch_chunk_prep<IO, D, C>(s, st)) != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("segment_map", st);
+    if ((e = gdn2::launch_segmap<IO, D, C>(s, Phi, Psi, st)) != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("segment_combine", st);
+    if ((e = gdn2::launch_seg_combine<D>(Phi, Psi, a.S0, sg.G, a.H, sg.N, S_in, nullptr, st, false)) != hipSuccess)
+      return e;
+  }
+  s.S0 = S_in;
+  {
+    prof_scope p("chunk_states", st);
+    if ((e = gdn2::launch_chunk_states<IO, D, C>(s, st)) != hipSuccess)
+      return e;
+  }
+  gdn2::bwd_args bs = ba;
+  bs.f = s;
+  bs.dSf = nullptr;
+  bs.dS0 = Psi2;
+  {
+    prof_scope p("bwd_dstate", st);
+    if ((e = gdn2::launch_bwd_dstate<IO, D, C>(bs, st)) != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("segment_combine", st);
+    if ((e = gdn2::launch_seg_combine<D>(Phi, Psi2, ba.dSf, sg.G, a.H, sg.N, X, ba.dS0, st, true)) != hipSuccess)
+      return e;
+  }
+  bs.dSf = X;
+  bs.dS0 = nullptr;
+  prof_scope p("bwd_dstate", st);
+  return gdn2::launch_bwd_dstate<IO, D, C>(bs, st);
+}
+
+template <typename IO, int D, int C>
+hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, hipStream_t st) {
   hipError_t e = hipSuccess;
   gdn2::chunk_args &a = ba.f;
   if (a.cu) {
@@ -230,6 +319,12 @@ template <typename IO, int D, int C> hipError_t run_bwd(gdn2::bwd_args &ba, int 
     e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
     if (e != hipSuccess)
       return e;
+  }
+  if (sg) {
+    if ((e = run_bwd_segments<IO, D, C>(ba, C_rt, *sg, st)) != hipSuccess)
+      return e;
+    prof_scope p("bwd_grad", st);
+    return gdn2::launch_bwd_grad<IO, D, C>(ba, st);
   }
   if (a.num_slots > 0) {
     {
@@ -258,10 +353,10 @@ template <typename IO, int D, int C> hipError_t run_bwd(gdn2::bwd_args &ba, int 
   return e;
 }
 
-hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, hipStream_t st) {
+hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, const seg_run *sg, hipStream_t st) {
 #define GDN2_RB(IO, D, C) \
   if (d == D && c == C)   \
-    return run_bwd<IO, D, C>(ba, C, st);
+    return run_bwd<IO, D, C>(ba, C, sg, st);
   if (dt == GDN2_F32) {
     GDN2_RB(float, 16, 16) GDN2_RB(float, 32, 16) GDN2_RB(float, 64, 16) GDN2_RB(float, 128, 16)
     GDN2_RB(float, 16, 64) GDN2_RB(float, 32, 64) GDN2_RB(float, 64, 64) GDN2_RB(float, 128, 64)
@@ -391,6 +486,19 @@ seg_plan plan_segments(gdn2_dtype_t dt, const seg_shape &x, int H, int d, int ch
   p.map_bytes = static_cast<size_t>(nseg) * H * d * d * sizeof(float);  // one of Phi, Psi, S_in
   p.total = p.cu + p.table + p.blocks + 3 * p.map_bytes;
   return p;
+}
+
+// Bytes the backward's segment schedule adds after the backward's own
+// workspace: bounds and chunk table of N G segments, then Phi, Psi, S_in,
+// Psi' and X.
+size_t seg_bwd_extra(const seg_shape &x, int H, int d, size_t *cu_bytes = nullptr, int *G = nullptr) {
+  const int g = seg_count(x.nc, x.N * H);
+  const size_t cb = align256(static_cast<size_t>(x.N * g + 1) * sizeof(int32_t));
+  if (cu_bytes)
+    *cu_bytes = cb;
+  if (G)
+    *G = g;
+  return 2 * cb + 5 * static_cast<size_t>(x.N) * g * H * d * d * sizeof(float);
 }
 
 hipError_t dispatch_combine(int d, const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
@@ -603,7 +711,10 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   const int n = num_seqs > 0 ? num_seqs : B;
   const bwd_plan pf = plan_bwd(dt, B, T, H, dk, B, chunk, false);
   const bwd_plan pp = plan_bwd(dt, B, T, H, dk, n, chunk, true);
-  return pf.total > pp.total ? pf.total : pp.total;
+  const size_t plain = pf.total > pp.total ? pf.total : pp.total;
+  // a few long sequences also take the segment schedule
+  const seg_shape x = seg_shape_of(B, T, num_seqs, chunk, num_seqs > 0);
+  return use_segments(x, H) ? align256(plain) + seg_bwd_extra(x, H, dk) : plain;
 }
 
 gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *alpha,
@@ -694,7 +805,24 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   ba.dal = dalpha;
   ba.db = db;
   ba.dw = dw;
-  const hipError_t e = dispatch_bwd(dt, dk, chunk, ba, static_cast<hipStream_t>(stream));
+  // a few long sequences: the segment schedule, when the workspace holds it
+  seg_run sr{};
+  const seg_run *sgp = nullptr;
+  const seg_shape sx = seg_shape_of(B, T, N, chunk, packed);
+  if (use_segments(sx, H)) {
+    size_t cb = 0;
+    int G = 0;
+    const size_t extra = seg_bwd_extra(sx, H, dk, &cb, &G);
+    if (workspace_bytes >= align256(plan.total) + extra) {
+      sr.ws = ws + align256(plan.total);
+      sr.cu_bytes = cb;
+      sr.N = sx.N;
+      sr.G = G;
+      sr.T_total = sx.T_total;
+      sgp = &sr;
+    }
+  }
+  const hipError_t e = dispatch_bwd(dt, dk, chunk, ba, sgp, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -66,10 +66,11 @@ template <typename IO, int D, int C> hipError_t launch_segmap(const chunk_args &
 // sequences of T tokens (cu == nullptr).
 hipError_t launch_seg_bounds(const int32_t *cu, int32_t *seg_cu, int G, int T, int B, int C, hipStream_t st);
 // Exclusive scan of the G segment maps of each of B sequences, [B, G, H, D, D],
-// from S0 [B, H, D, D] (nullptr: zero).
+// from S0 [B, H, D, D] (nullptr: zero).  reverse: the backward's adjoint
+// scan (Phi transposed, segments from the last; see the kernel).
 template <int D>
 hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
-                              float *S_in, float *S_final, hipStream_t st);
+                              float *S_in, float *S_final, hipStream_t st, bool reverse = false);
 
 template <typename IO, int D>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,

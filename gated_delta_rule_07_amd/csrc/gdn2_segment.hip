@@ -268,7 +268,13 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
 // of state tiles (., j) sits in LDS and wave kk forms its tile of
 // Psi_g + Phi_g S from row tile kk of Phi_g, loaded one segment ahead.
 // float32 throughout (products as in mm<float>).
-template <int D>
+// REV: the adjoint scan of the backward, segments from the last: the input
+// in S0's place is the gradient of the state after the last segment; then
+// per segment g (descending) S_in[g] is the gradient of the state after g and
+// the next one is Phi_g^T S_in[g] + Psi_g, with Psi_g the gradient of the
+// state before g from g's own outputs; S_final receives the gradient of the
+// state before the first segment.
+template <int D, bool REV = false>
 __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const float *__restrict__ Phi,
                                                                          const float *__restrict__ Psi,
                                                                          const float *__restrict__ S0, int G, int H,
@@ -293,19 +299,28 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     s[i] = S0 ? S0[static_cast<size_t>(bh) * D * D + at(i)] : 0.f;
-  f32x4 ph[NK], ps;  // RowFrag of Phi tiles (kk, k2); ColFrag of Psi tile (kk, j)
+  f32x4 ph[NK], ps;  // RowFrag of Phi (REV: Phi^T) tiles (kk, k2); ColFrag of Psi tile (kk, j)
   auto load = [&](int seg) {
     const size_t base = (static_cast<size_t>(seg) * H + h) * D * D;
 #pragma unroll
-    for (int k2 = 0; k2 < NK; ++k2)
-      ph[k2] = *reinterpret_cast<const f32x4 *>(Phi + base + static_cast<size_t>(16 * kk + m) * D + 16 * k2 + 4 * g);
+    for (int k2 = 0; k2 < NK; ++k2) {
+      if constexpr (REV) {
+        // Phi^T[16 kk + m][16 k2 + 4 g + i] = Phi[16 k2 + 4 g + i][16 kk + m]
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ph[k2][i] = Phi[base + static_cast<size_t>(16 * k2 + 4 * g + i) * D + 16 * kk + m];
+      } else {
+        ph[k2] = *reinterpret_cast<const f32x4 *>(Phi + base + static_cast<size_t>(16 * kk + m) * D + 16 * k2 + 4 * g);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       ps[i] = Psi[base + at(i)];
   };
   if (G > 0)
-    load(0);
-  for (int seg = 0; seg < G; ++seg) {
+    load(REV ? G - 1 : 0);
+  for (int step = 0; step < G; ++step) {
+    const int seg = REV ? G - 1 - step : step;
     const size_t base = (static_cast<size_t>(seg) * H + h) * D * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -317,7 +332,10 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
     for (int k2 = 0; k2 < NK; ++k2)
       cph[k2] = ph[k2];
     f32x4 nw = ps;
-    load(seg + 1 < G ? seg + 1 : seg);  // the last step re-reads its own maps: no branch
+    if constexpr (REV)
+      load(seg > 0 ? seg - 1 : seg);  // the last step re-reads its own maps: no branch
+    else
+      load(seg + 1 < G ? seg + 1 : seg);
 #pragma unroll
     for (int k2 = 0; k2 < NK; ++k2)
       mm<float>(nw, cph[k2], col[k2][lane]);
@@ -342,9 +360,13 @@ hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_
 
 template <int D>
 hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
-                              float *S_in, float *S_final, hipStream_t st) {
-  hipLaunchKernelGGL((gdn2_seg_combine_kernel<D>), dim3(B * H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi, Psi, S0,
-                     G, H, B, S_in, S_final);
+                              float *S_in, float *S_final, hipStream_t st, bool reverse) {
+  if (reverse)
+    hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, true>), dim3(B * H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi,
+                       Psi, S0, G, H, B, S_in, S_final);
+  else
+    hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false>), dim3(B * H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi,
+                       Psi, S0, G, H, B, S_in, S_final);
   return hipGetLastError();
 }
 
@@ -393,13 +415,13 @@ GDN2_INST_SEG(bf16_t, 32, 64)
 GDN2_INST_SEG(bf16_t, 64, 64)
 GDN2_INST_SEG(bf16_t, 128, 64)
 
-template hipError_t launch_seg_combine<16>(const float *, const float *, const float *, int, int, int, float *, float *,
-                                           hipStream_t);
-template hipError_t launch_seg_combine<32>(const float *, const float *, const float *, int, int, int, float *, float *,
-                                           hipStream_t);
-template hipError_t launch_seg_combine<64>(const float *, const float *, const float *, int, int, int, float *, float *,
-                                           hipStream_t);
-template hipError_t launch_seg_combine<128>(const float *, const float *, const float *, int, int, int, float *, float *,
-                                            hipStream_t);
+template hipError_t launch_seg_combine<16>(const float *, const float *, const float *, int, int, int, float *,
+                                           float *, hipStream_t, bool);
+template hipError_t launch_seg_combine<32>(const float *, const float *, const float *, int, int, int, float *,
+                                           float *, hipStream_t, bool);
+template hipError_t launch_seg_combine<64>(const float *, const float *, const float *, int, int, int, float *,
+                                           float *, hipStream_t, bool);
+template hipError_t launch_seg_combine<128>(const float *, const float *, const float *, int, int, int, float *,
+                                           float *, hipStream_t, bool);
 
 }  // namespace gdn2

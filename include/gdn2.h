@@ -176,7 +176,9 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
                              void *stream);
 
 /* Bytes of device workspace gdn2_chunk_bwd needs for these sizes (0 when
- * the sizes are unsupported); num_seqs as for gdn2_chunk_fwd_workspace_bytes. */
+ * the sizes are unsupported); num_seqs as for gdn2_chunk_fwd_workspace_bytes.
+ * For a few long sequences the figure includes the segment schedule's maps
+ * (see gdn2_chunk_bwd). */
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk, gdn2_dtype_t dt);
 
@@ -206,7 +208,12 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *   workspace : device scratch of at least gdn2_chunk_bwd_workspace_bytes(...)
  *               bytes; its contents on entry are irrelevant.
  * The kernels recompute the forward's per-chunk quantities and the state
- * entering every chunk; no forward output needs to be kept.  The numerical
+ * entering every chunk; no forward output needs to be kept.  For the shapes
+ * where gdn2_chunk_fwd takes its segment schedule (a few long sequences),
+ * given the workspace gdn2_chunk_bwd_workspace_bytes reports, both of the
+ * backward's scans take it too: the states from the segment maps and their
+ * scan, the state gradients from per-segment reverse scans and the adjoint
+ * scan of the maps (Phi transposed, from the last segment).  The numerical
  * domain is the chunked forward's (see the conventions above); alpha must be
  * nonzero. */
 gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *alpha,

@@ -95,6 +95,33 @@ def test_bwd_zero_length(g):
     np.testing.assert_array_equal(got["dS0"], grads["dS_final"].numpy())
 
 
+@pytest.mark.parametrize("dtype,d,chunk,B,T,H,lens", [
+    ("f32", 32, 64, 1, 130 * 64 + 5, 2, None),
+    ("f32", 32, 16, 1, 3000, 2, None),
+    ("bf16", 64, 64, 2, 140 * 64 - 7, 4, None),
+    ("f32", 32, 64, 1, None, 4, [30000, 0, 37, 5000]),
+])
+def test_bwd_segment_schedule(g, dtype, d, chunk, B, T, H, lens):
+    """Sequences of 128 chunks or more with at most 16 (sequence, head)
+    units: both scans of the backward take the segment schedule (the
+    forward maps and their scan for the states; per-segment reverse scans
+    from zero, the adjoint scan of the maps and the final reverse scans for
+    the state gradients).  Every gradient, and dS0, against the oracle's;
+    fixed-length and packed (empty and sub-chunk sequences), chunks 64 and
+    16."""
+    cu = None if lens is None else gi.cu_seqlens_from(lens)
+    if cu is not None:
+        T = int(cu[-1])
+    n = None if lens is None else len(lens)
+    inp = gi.make_chunk_inputs(B, T, H, d, d, dtype, seed=61 + d, s0="normal", num_seqs=n, alpha_mean=8.0)
+    grads = gi.make_bwd_grads(B, T, H, d, d, dtype, seed=61 + d, num_seqs=n)
+    print(f"case bwd segment schedule {dtype} d={d} C={chunk} B={B} T={T} H={H} lens={lens}", flush=True)
+    got = gpu_bwd(g, inp, grads, chunk, cu=cu)
+    ref = oracle.bwd(*(inp[x] for x in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"],
+                     cu_seqlens=cu)
+    check(got, ref, TOL[dtype], f"bwd segments {dtype} d={d} C={chunk}")
+
+
 def test_bwd_deterministic(g):
     inp = gi.make_chunk_inputs(1, 300, 2, 128, 128, "bf16", seed=21, s0="normal")
     grads = gi.make_bwd_grads(1, 300, 2, 128, 128, "bf16", seed=21)
