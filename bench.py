@@ -263,11 +263,21 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     sec_all_p = timed_steps(lambda: (all_maps(), combine(), reruns_prepared()), 10, 2)
     sec_whole = timed_steps(whole, 10, 2)
     sec_serial_w = timed_steps(whole_serial, 10, 2)
+    # the backward of the same sequence (its scans take the segment schedule too)
+    grads = gi.make_bwd_grads(1, G * L, H, d, d, "bf16", seed=5, with_dS=False)
+    dout = grads["dout"].cuda()
+    wsb = torch.empty(g.bwd_workspace_bytes(1, G * L, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8,
+                      device="cuda")
+    gout = {n: torch.empty_like(full[x]) for n, x in zip(("dq", "dk", "dv", "dalpha", "db", "dw"), NAMES)}
+    gout["dS0"] = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+    sec_bwd = timed_steps(lambda: g.chunk_bwd(*(full[x] for x in NAMES), dout, chunk=C, workspace=wsb, out=gout), 5, 2)
+    del wsb, gout, dout
     res["one_gpu"] = {
         "maps_combine_reruns_ms": round(sec_all * 1e3, 4),
         "maps_combine_prepared_reruns_ms": round(sec_all_p * 1e3, 4),
         "whole_sequence_serial_scan_ms": round(sec_serial_w * 1e3, 4),
         "whole_sequence_default_path_ms": round(sec_whole * 1e3, 4),
+        "whole_sequence_backward_ms": round(sec_bwd * 1e3, 4),
         "prepared_over_serial": round(sec_all_p / sec_serial_w, 3),
         "combine_kernel_us": round(1e3 * cprof["segment_combine"][0] / cprof["segment_combine"][1], 2),
         "exchange_bytes_per_rank": 2 * H * d * d * 4,
