@@ -40,16 +40,25 @@
 namespace gdn2 {
 
 // ------------------------------------------------------- reverse dH scan --
-// One workgroup per (sequence, head), one wave per 16-column slice of dH
-// (dk x 16 float32 in matrix-core accumulators).  Per chunk, from the last:
+// NSPL workgroups per (sequence, head), placed on one XCD (their common tile
+// reads hit its L2), each with one wave per 16-column slice of dH of its
+// share (dk x 16 float32 in matrix-core accumulators): with two, a batch of
+// 128 (sequence, head) units fills the 256 compute units.  Per chunk, from the last:
 // the waves re-lay the chunk's Kbar, Q'^T and -W^T tiles (stored by the prep
 // as RowFrag(Kbar^T), RowFrag(Q'), RowFrag(-W)) into LDS with one identity
 // product each, then every wave stores its slice of dH (the gradient of the
 // state leaving the chunk, as state_tiles fragments) and updates it.
+template <int D> struct dstate_cfg {
+  static constexpr int NK = D / 16;
+  static constexpr int NSPL = NK >= 2 ? 2 : 1;  // workgroups per (sequence, head)
+  static constexpr int NW = NK / NSPL;          // waves (dv tiles) per workgroup
+};
+
 template <typename IO, int D, int C>
-__global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args ba) {
+__global__ void __launch_bounds__(64 * dstate_cfg<D>::NW) gdn2_bwd_dstate_kernel(bwd_args ba) {
   const chunk_args &a = ba.f;
-  constexpr int NB = C / 16, NK = D / 16, NW = NK, NT = NB * NK;
+  constexpr int NB = C / 16, NK = D / 16, NSPL = dstate_cfg<D>::NSPL, NW = dstate_cfg<D>::NW, NT = NB * NK;
+  static_assert(64 * NW >= D, "gamma_C is loaded one channel per thread");
   typedef frag<IO> F;
   typedef blk_layout<IO, D, C> L;
   constexpr size_t TB = F::TILE_BYTES;
@@ -58,13 +67,14 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_bwd_dstate_kernel(bwd_args
   __shared__ __attribute__((aligned(16))) unsigned char sm[3 * NT * TB + D * sizeof(float)];
   float *gam = reinterpret_cast<float *>(sm + 3 * NT * TB);
 
-  const int unit = blockIdx.x;
+  const int x = static_cast<int>(blockIdx.x), xcd = x & 7, s8 = x >> 3;
+  const int unit = (s8 / NSPL) * 8 + xcd, grp = s8 % NSPL;
   if (unit >= a.num_seqs * a.H)
-    return;
+    return;  // the whole workgroup
   const int n = unit / a.H, h = unit - n * a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int j = wave;  // dv tile of this wave
+  const int j = grp * NW + wave;  // dv tile of this wave
   int c_begin, nchunks;
   long tstart, tend;
   if (a.cu) {
@@ -947,8 +957,9 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 }
 
 template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args &a, hipStream_t st) {
-  const int units = a.f.num_seqs * a.f.H;
-  hipLaunchKernelGGL((gdn2_bwd_dstate_kernel<IO, D, C>), dim3(units), dim3(64 * (D / 16)), 0, st, a);
+  const long units_pad = (static_cast<long>(a.f.num_seqs) * a.f.H + 7) / 8 * 8;
+  hipLaunchKernelGGL((gdn2_bwd_dstate_kernel<IO, D, C>), dim3(static_cast<unsigned>(units_pad * dstate_cfg<D>::NSPL)),
+                     dim3(64 * dstate_cfg<D>::NW), 0, st, a);
   return hipGetLastError();
 }
 
