@@ -145,7 +145,7 @@ def cpu_baseline(inp: dict, H: int, budget_s: float) -> dict:
 def load_traffic(kernel: str) -> dict | None:
     """HBM bytes per launch measured with rocprofv3 counters, if they were taken
     on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_config2.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_layer_8x4096x16_d128.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -303,8 +303,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every (sequence, head) is independent; see the sharding notes in DESIGN.md)",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(every (sequence, head) is independent, and a long sequence splits through its segment maps)",
               file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
@@ -449,7 +449,7 @@ def main() -> int:
                          "ms": round(sec_p * 1e3, 4)}
 
         # decode: 256 sequences x 16 heads, 16 distinct step inputs cycled
-        c4 = gi.CONFIGS[4]
+        c4 = gi.WORKLOADS["decode_256x16_d128"]
         dd = gi.make_decode_inputs(c4["N"], c4["H"], d, d, "bf16", c4["seed"], steps=c4["steps"])
         ddev = {x: dd[x].cuda() for x in NAMES}
         S_a = dd["S"].cuda()

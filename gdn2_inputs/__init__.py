@@ -165,16 +165,18 @@ def make_decode_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
     }
 
 
-# The five workloads (shapes, dtypes, seeds).  Config 3's packed lengths come
-# from ``packed_lengths(3)``; its sweep uses fixed-length batches with
-# B * T = 32768.
-CONFIGS = {
-    0: dict(B=1, H=1, T=64, dk=16, dv=16, chunk=16, dtype="f32", seed=0, s0="zero"),
-    1: dict(B=2, H=4, T=512, dk=64, dv=64, chunk=64, dtype="f32", seed=1, s0="normal"),
-    2: dict(B=8, H=16, T=4096, dk=128, dv=128, chunk=64, dtype="bf16", seed=2, s0=None),
-    3: dict(B=1, H=16, T=32768, dk=128, dv=128, chunk=64, dtype="bf16", seed=3, s0=None,
-            packed=True),
-    4: dict(N=256, H=16, dk=128, dv=128, dtype="bf16", seed=4, steps=16),
+# The five workloads (shapes, dtypes, seeds), named by what they are: a tiny
+# and a small float32 case the oracle finishes in seconds, the 1.3B-scale
+# layer (8 x 4096 tokens x 16 heads, d = 128, bf16), 32768 packed tokens of
+# mixed lengths (from ``packed_lengths(3)``; its sweep uses fixed-length
+# batches with B * T = 32768), and a decode step of 256 sequences x 16 heads.
+WORKLOADS = {
+    "tiny_1x64x1_d16": dict(B=1, H=1, T=64, dk=16, dv=16, chunk=16, dtype="f32", seed=0, s0="zero"),
+    "small_2x512x4_d64": dict(B=2, H=4, T=512, dk=64, dv=64, chunk=64, dtype="f32", seed=1, s0="normal"),
+    "layer_8x4096x16_d128": dict(B=8, H=16, T=4096, dk=128, dv=128, chunk=64, dtype="bf16", seed=2, s0=None),
+    "packed_32768x16_d128": dict(B=1, H=16, T=32768, dk=128, dv=128, chunk=64, dtype="bf16", seed=3, s0=None,
+                                 packed=True),
+    "decode_256x16_d128": dict(N=256, H=16, dk=128, dv=128, dtype="bf16", seed=4, steps=16),
 }
 
 SWEEP_T = (2048, 4096, 8192, 16384, 32768)

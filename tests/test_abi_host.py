@@ -78,7 +78,7 @@ def test_fwd_rejects_before_launch(L):
 
 def test_workspace_bytes(L):
     f = L.gdn2_chunk_fwd_workspace_bytes
-    # config 2: 8 x 64 chunks x 16 heads of bf16 intermediates, plus the table
+    # the layer workload: 8 x 64 chunks x 16 heads of bf16 intermediates, plus the table
     w = f(8, 4096, 16, 128, 128, 0, 64, BF16)
     assert 8 * 64 * 16 * 80 * 1024 <= w <= 8 * 64 * 16 * 82 * 1024 + 4096
     assert f(8, 4096, 16, 128, 64, 0, 64, BF16) == 0

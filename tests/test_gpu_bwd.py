@@ -132,13 +132,13 @@ def test_bwd_deterministic(g):
         np.testing.assert_array_equal(a[name], b[name])
 
 
-def test_bwd_config2_sampled_units(g):
+def test_bwd_layer_8x4096x16_sampled_units(g):
     """Full headline size (B=8, T=4096, H=16, d=128, bf16); the oracle
     recomputes the gradients of two (batch, head) units end to end."""
-    c = gi.CONFIGS[2]
+    c = gi.WORKLOADS["layer_8x4096x16_d128"]
     inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], s0=c["s0"])
     grads = gi.make_bwd_grads(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"])
-    print("case config2 backward", flush=True)
+    print("case layer backward", flush=True)
     got = gpu_bwd(g, inp, grads, 64)
     for name in got:
         assert np.isfinite(got[name]).all(), name
@@ -148,7 +148,7 @@ def test_bwd_config2_sampled_units(g):
         ref = oracle.bwd(*(sub[x] for x in NAMES), grads["dout"][bb:bb + 1, :, hh:hh + 1].contiguous(),
                          S0=S0, dS_final=grads["dS_final"][bb:bb + 1, hh:hh + 1].contiguous())
         sel = lambda name, x: x[bb:bb + 1, hh:hh + 1] if name == "dS0" else x[bb:bb + 1, :, hh:hh + 1]
-        check(got, ref, TOL["bf16"], f"cfg2 b={bb} h={hh}", sel=sel)
+        check(got, ref, TOL["bf16"], f"layer b={bb} h={hh}", sel=sel)
 
 
 def gpu_bwd_raw(g, inp, grads, chunk, layer_prep=False):

@@ -54,41 +54,41 @@ def check(o, Sf, o_ref, S_ref, tol, label=""):
     assert es <= tol, f"{label}: S_final error {es:.3e} > {tol}"
 
 
-def make(cfg, **over):
-    c = dict(gi.CONFIGS[cfg])
+def make(name, **over):
+    c = dict(gi.WORKLOADS[name])
     c.update(over)
     return c, gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"], c["seed"],
                                    s0=c["s0"])
 
 
-# ------------------------------------------------------------ small configs
+# ---------------------------------------------------------- small workloads
 @pytest.mark.parametrize("recurrent", [False, True])
-def test_config0(g, recurrent):
-    c, inp = make(0)
+def test_tiny_1x64x1(g, recurrent):
+    c, inp = make("tiny_1x64x1_d16")
     o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
     for s0 in (inp["S0"], None):  # explicit zeros and NULL
         inp2 = dict(inp, S0=s0)
         o, Sf = gpu_fwd(g, inp2, c["chunk"], recurrent=recurrent)
-        check(o, Sf, o_ref, S_ref, TOL["f32"], f"cfg0 rec={recurrent} s0={'zeros' if s0 is not None else 'NULL'}")
+        check(o, Sf, o_ref, S_ref, TOL["f32"], f"tiny rec={recurrent} s0={'zeros' if s0 is not None else 'NULL'}")
 
 
 @pytest.mark.parametrize("path", ["auto", "recurrent", "two_pass", "fused"])
-def test_config1(g, path):
-    c, inp = make(1)
+def test_small_2x512x4(g, path):
+    c, inp = make("small_2x512x4_d64")
     o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
     o, Sf = gpu_fwd(g, inp, c["chunk"], path=path)
-    check(o, Sf, o_ref, S_ref, TOL["f32"], f"cfg1 {path}")
+    check(o, Sf, o_ref, S_ref, TOL["f32"], f"small {path}")
 
 
-def test_config1b_collapsed_gates(g):
+def test_small_collapsed_gates(g):
     """b = w = beta (KDA case): the GPU matches the oracle, which is pinned to
     textbook KDA on the CPU."""
-    c = gi.CONFIGS[1]
+    c = gi.WORKLOADS["small_2x512x4_d64"]
     inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], "f32", c["seed"],
                                s0="normal", scalar_beta=True)
     o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
     o, Sf = gpu_fwd(g, inp, 64)
-    check(o, Sf, o_ref, S_ref, TOL["f32"], "cfg1b")
+    check(o, Sf, o_ref, S_ref, TOL["f32"], "small collapsed gates")
 
 
 RAGGED = [("bf16", 128, 64, 200), ("bf16", 64, 16, 77), ("f32", 128, 64, 130), ("f32", 32, 64, 64),
@@ -213,12 +213,12 @@ def test_packed_small_with_empty_sequences(g):
     check(o, Sf, o_ref, S_ref, TOL["f32"], "packed rec")
 
 
-def test_config3_packed_sampled(g):
-    """Config 3: 32768 packed tokens, H=16, d=128, bf16.  The oracle checks
+def test_packed_32768_sampled(g):
+    """32768 packed tokens, H=16, d=128, bf16.  The oracle checks
     every head of two sequences (the shortest and the last one)."""
     lens = gi.packed_lengths(3)
     cu = gi.cu_seqlens_from(lens)
-    c = gi.CONFIGS[3]
+    c = gi.WORKLOADS["packed_32768x16_d128"]
     inp = gi.make_chunk_inputs(1, c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], s0=None,
                                num_seqs=len(lens))
     o, Sf = gpu_fwd(g, inp, 64, cu=cu)
@@ -227,7 +227,7 @@ def test_config3_packed_sampled(g):
         a, bnd = int(cu[n]), int(cu[n + 1])
         sub = {x: inp[x][:, a:bnd] for x in NAMES}
         o_ref, S_ref = oracle.fwd(*(sub[x] for x in NAMES))
-        check(o[:, a:bnd], Sf[n:n + 1], o_ref, S_ref, TOL["bf16"], f"cfg3 seq{n} len={bnd - a}")
+        check(o[:, a:bnd], Sf[n:n + 1], o_ref, S_ref, TOL["bf16"], f"packed seq{n} len={bnd - a}")
 
 
 def test_varlen_equals_separate_runs(g):
@@ -268,18 +268,18 @@ def test_chunk_aligned_slices_chain_exactly(g, path):
 
 # -------------------------------------------------------- headline config
 @pytest.mark.parametrize("path", ["auto", "two_pass"])
-def test_config2_sampled_units(g, path):
-    """Config 2 at full size (B=8, T=4096, H=16, d=128, bf16) in the launch
+def test_layer_8x4096x16_sampled_units(g, path):
+    """The layer workload at full size (B=8, T=4096, H=16, d=128, bf16) in the launch
     configuration the benchmark times ("auto"); the oracle recomputes four
     (batch, head) units end to end."""
-    c, inp = make(2)
+    c, inp = make("layer_8x4096x16_d128")
     o, Sf = gpu_fwd(g, inp, 64, path=path)
     assert np.isfinite(o).all() and np.isfinite(Sf).all()
     for (bb, hh) in ((0, 0), (3, 7), (5, 15), (7, 9)):
         sub = {x: inp[x][bb:bb + 1, :, hh:hh + 1].contiguous() for x in NAMES}
         o_ref, S_ref = oracle.fwd(*(sub[x] for x in NAMES))
         check(o[bb:bb + 1, :, hh:hh + 1], Sf[bb:bb + 1, hh:hh + 1], o_ref, S_ref, TOL["bf16"],
-              f"cfg2 b={bb} h={hh}")
+              f"layer b={bb} h={hh}")
 
 
 def test_sweep_endpoints_sampled(g):
@@ -405,7 +405,7 @@ def test_nan_propagates_within_unit(g):
 
 @pytest.mark.parametrize("path", ["two_pass", "fused"])
 def test_deterministic(g, path):
-    c, inp = make(1)
+    c, inp = make("small_2x512x4_d64")
     o1, S1 = gpu_fwd(g, inp, 64, path=path)
     o2, S2 = gpu_fwd(g, inp, 64, path=path)
     np.testing.assert_array_equal(o1, o2)
@@ -437,8 +437,8 @@ def test_decode_small(g, dtype, d):
         check(o.float().cpu().numpy(), S_gpu.cpu().numpy(), o_ref, S_ref, tol, f"decode {dtype} d={d} t={t}")
 
 
-def test_decode_config4_16_steps(g):
-    c = gi.CONFIGS[4]
+def test_decode_256x16_16_steps(g):
+    c = gi.WORKLOADS["decode_256x16_d128"]
     dd = gi.make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], steps=c["steps"])
     S_gpu = dd["S"].cuda()
     S_ref = dd["S"].double().numpy()
@@ -452,7 +452,7 @@ def test_decode_config4_16_steps(g):
         eo = rel_err(outs[t].float().cpu().numpy(), o_ref)
         assert eo <= TOL["bf16"], f"step {t}: o error {eo:.3e}"
     es = rel_err(S_gpu.cpu().numpy(), S_ref)
-    print(f"cfg4 16 steps err_S={es:.3e}", flush=True)
+    print(f"decode 16 steps err_S={es:.3e}", flush=True)
     assert es <= TOL["bf16"]
 
 

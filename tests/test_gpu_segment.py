@@ -223,7 +223,7 @@ def test_prepared_workspace_of_a_forward_call(g):
 
 
 def test_segments_per_rank_shape(g):
-    """Config 3's 32768-token stream (H=16, d=128, bf16) as one sequence cut
+    """The packed workload's 32768-token stream (H=16, d=128, bf16) as one sequence cut
     into 8 segments of 4096 tokens, the per-rank share of an 8-way
     context-parallel split, with long-memory decay so the state crosses
     every boundary.  The oracle recomputes two heads end to end: their

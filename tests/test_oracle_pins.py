@@ -218,9 +218,9 @@ def test_P9_decode_steps_equal_forward():
     np.testing.assert_array_equal(S, Sf)
 
 
-def test_c_oracle_matches_numpy_transcription_configs_0_1():
-    for cfg in (0, 1):
-        c = gi.CONFIGS[cfg]
+def test_c_oracle_matches_numpy_transcription_small_workloads():
+    for name in ("tiny_1x64x1_d16", "small_2x512x4_d64"):
+        c = gi.WORKLOADS[name]
         inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"],
                                    c["seed"], s0=c["s0"])
         args = [inp[x].double().numpy() for x in ("q", "k", "v", "alpha", "b", "w")]
@@ -230,10 +230,10 @@ def test_c_oracle_matches_numpy_transcription_configs_0_1():
         assert rel(o, o2) < 1e-12 and rel(Sf, Sf2) < 1e-12
 
 
-def test_kda_reduction_on_config_1b():
-    """Config 1 with b = w = beta (scalar per batch, token, head): the GDN-2
+def test_kda_reduction_on_small_workload():
+    """The small workload with b = w = beta (scalar per batch, token, head): the GDN-2
     oracle equals textbook KDA on every head."""
-    c = gi.CONFIGS[1]
+    c = gi.WORKLOADS["small_2x512x4_d64"]
     inp = gi.make_chunk_inputs(c["B"], 128, c["H"], c["dk"], c["dv"], "f32", c["seed"],
                                s0="normal", scalar_beta=True)
     A = {x: inp[x].double().numpy() for x in ("q", "k", "v", "alpha", "b", "w")}
