@@ -170,7 +170,8 @@ def gpu_bwd_raw(g, inp, grads, chunk, layer_prep=False):
 GATE_CASES = {"kda": ("b", "w"), "gdn": ("b", "w", "alpha"), "b_only": ("b",), "w_only": ("w",)}
 
 
-@pytest.mark.parametrize("dtype,d,T,chunk", [("f32", 64, 190, 64), ("bf16", 128, 200, 64), ("bf16", 32, 77, 16)])
+@pytest.mark.parametrize("dtype,d,T,chunk", [("f32", 64, 190, 64), ("bf16", 128, 200, 64), ("bf16", 32, 77, 16),
+                                             ("f32", 32, 130 * 64, 64)])  # the last: segment schedule
 @pytest.mark.parametrize("case", list(GATE_CASES))
 def test_bwd_per_token_gates(g, case, dtype, d, T, chunk):
     from oracle import layer_prep as lp

@@ -149,6 +149,25 @@ def test_per_token_gates(g, case, dtype, d, T, path):
     check(o, Sf, o_ref, S_ref, TOL[dtype], f"gates {case} {path} {dtype} d={d}")
 
 
+@pytest.mark.parametrize("case", list(GATE_CASES))
+def test_per_token_gates_segment_schedule(g, case):
+    """Per-(token, head) gates on the default path of two sequences of 130
+    chunks and 3 heads, which takes the segment schedule (the gate layouts
+    reach the maps and the re-runs)."""
+    B, T, H, d = 2, 130 * 64 + 9, 3, 32
+    inp = gi.make_chunk_inputs(B, T, H, d, d, "f32", seed=71, s0="normal", alpha_mean=8.0,
+                               scalar_beta=(case in ("kda", "gdn")))
+    full, compact = dict(inp), dict(inp)
+    for x in GATE_CASES[case]:
+        s = inp[x][..., 0].contiguous()
+        compact[x] = s
+        full[x] = s[..., None].expand_as(inp[x]).contiguous()
+    print(f"case gates {case} segment schedule T={T}", flush=True)
+    o_ref, S_ref = oracle.fwd(*(full[n] for n in NAMES), S0=inp["S0"])
+    o, Sf = gpu_fwd(g, compact, 64)
+    check(o, Sf, o_ref, S_ref, TOL["f32"], f"gates {case} segment schedule")
+
+
 def test_per_token_gates_rejected_on_recurrent_path(g):
     inp = gi.make_chunk_inputs(1, 32, 1, 16, 16, "f32", seed=5)
     inp["b"] = inp["b"][..., 0].contiguous()
