@@ -137,15 +137,23 @@ def cpu_baseline(inp: dict, H: int, budget_s: float) -> dict:
     while total < budget_s and reps < 64:      # repeat the sample until the budget is spent
         total += run(Tp)
         reps += 1
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": B * Tp * reps / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu,
             "sample": f"float64 token-by-token oracle on all {B}x{H} (batch, head) units of the "
                       f"workload, first {Tp} of {T} tokens each, {reps} run(s), {total:.1f} s"}
 
 
-def load_traffic(kernel: str) -> dict | None:
-    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
-    on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_layer_8x4096x16_d128.json")
+def load_traffic() -> dict | None:
+    """HBM bytes per launch of the forward's kernels measured with rocprofv3
+    counters (FETCH_SIZE and WRITE_SIZE, scaled by a device copy of known
+    size), if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_layer_8x4096x16_d128.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -153,6 +161,28 @@ def load_traffic(kernel: str) -> dict | None:
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec
+
+
+def host_info() -> dict:
+    """CPU model and core count of the host, GPU name and architecture."""
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    p = torch.cuda.get_device_properties(0)
+    return {"cpu_model": cpu, "host_cpus": os.cpu_count(), "gpu_name": p.name,
+            "gpu_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "gpu_memory_gib": round(p.total_memory / 2**30, 1)}
+
+
+def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
+    """max |x - ref| / max |ref| over the whole tensor."""
+    return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
 
 
 # Algorithmic HBM bytes of the segment-map kernel per token and head: read
@@ -335,28 +365,43 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    g.profile_enable(True)
-    step()
-    torch.cuda.synchronize()
-    g.profile_read(reset=True)
+    # the headline: K timed steps with the library's timing hooks off
     sec = timed_steps(step, args.steps, args.warmup)
+    # the timed output against the oracle (every element of o and S_final)
+    o_gpu = o.float().cpu().numpy()
+    S_gpu = Sf.cpu().numpy()
+    # per-kernel durations in a separate pass: HIP events on the launch stream
+    g.profile_enable(True)
+    g.profile_read(reset=True)
+    sec_hooks = timed_steps(step, args.steps, 3)
     prof = g.profile_read(reset=True)
     g.profile_enable(False)
-    launches = args.steps + args.warmup
     kern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in prof.items()}
 
     tok_heads = B * T * H
     fl = flops_per_token_head(d, C) * tok_heads
     byt = bytes_per_token_head(d, C)
+    path_bytes = byt["path"] * tok_heads
     dominant = max(kern, key=lambda k: kern[k]["avg_us"])
     dom_us = kern[dominant]["avg_us"]
-    dom_bytes = byt[dominant] * tok_heads
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    tr = load_traffic(dominant)
+    achieved = path_bytes / (dom_us * 1e-6) / 1e9
+    own_bytes = byt[dominant] * tok_heads
+    own_achieved = own_bytes / (dom_us * 1e-6) / 1e9
+    tr = load_traffic()
+    traffic = tr["kernels"][dominant]["bytes_per_launch"] if tr and dominant in tr["kernels"] else None
+    step_traffic = (sum(tr["kernels"][k]["bytes_per_launch"] for k in kern if k in tr["kernels"])
+                    if tr and all(k in tr["kernels"] for k in kern) else None)
+    # roofline of the dominant kernel: the path's algorithmic bytes (1792 B
+    # per token-head: six bf16 inputs read once, o written once) over that
+    # kernel's average launch time; the kernel's own bytes (its inputs and
+    # outputs, workspace included) are reported beside it
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": (tr["bytes_per_launch"] if tr else None),
-                "kernel": dominant, "algorithmic_bytes_per_launch": int(dom_bytes)}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dominant, "algorithmic_bytes_per_launch": int(path_bytes),
+                "algorithmic_bytes_per_token_head": byt["path"], "token_heads_per_launch": tok_heads,
+                "kernel_own": {"bytes_per_launch": int(own_bytes), "achieved": round(own_achieved, 1),
+                               "frac": round(own_achieved / HBM_PEAK_GBS, 4)},
+                "traffic_over_algorithmic": (round(step_traffic / path_bytes, 3) if step_traffic else None)}
 
     out = {
         "metric": "GDN-2 chunk fwd tokens/s + % bf16 MFMA peak (H16 d128 T4K); decode % HBM",
@@ -372,11 +417,28 @@ def main() -> int:
         "roofline": roofline,
         "path": {"tflops": round(fl / sec / 1e12, 2),
                  "mfma_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
-                 "algorithmic_bytes": int(byt["path"] * tok_heads),
-                 "hbm_frac": round(byt["path"] * tok_heads / sec / 1e9 / HBM_PEAK_GBS, 4),
-                 "flops_per_token_head": flops_per_token_head(d, C)},
+                 "algorithmic_bytes": int(path_bytes),
+                 "hbm_frac": round(path_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                 "flops_per_token_head": flops_per_token_head(d, C),
+                 "step_traffic_bytes": step_traffic},
         "kernels": kern,
+        "ms_per_step_with_timing_hooks": round(sec_hooks * 1e3, 4),
+        "host": host_info(),
     }
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        o_ref, S_ref = oracle.fwd(*(inp[x] for x in NAMES))
+        eo, es = rel_err(o_gpu, o_ref), rel_err(S_gpu, S_ref)
+        out["max_err_o"] = eo
+        out["max_err_S"] = es
+        out["parity"] = {"max_err_o": eo, "max_err_S": es, "tol": 2e-2,
+                         "metric": "max |gpu - oracle| / max |oracle| over every element of the timed step's "
+                                   "o and S_final",
+                         "oracle": "float64 token-by-token recurrence, all 128 (batch, head) units",
+                         "oracle_s": round(time.perf_counter() - t0, 2)}
+        del o_ref, S_ref
+    del o_gpu, S_gpu
 
     if not args.no_extras:
         # T sweep at B*T = 32768 and the packed workload reuse the same tokens
@@ -479,10 +541,23 @@ def main() -> int:
             "algorithmic_bytes_per_step": step_bytes,
             "GBps": round(step_bytes / (dk_us * 1e-6) / 1e9, 1),
             "hbm_frac": round(step_bytes / (dk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "oracle_ms_per_step": None,
             "two_state_buffers": {"kernel_us": round(dkc_us, 2),
                                   "GBps": round(step_bytes / (dkc_us * 1e-6) / 1e9, 1),
                                   "hbm_frac": round(step_bytes / (dkc_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         }
+
+        if not args.no_cpu:
+            # the oracle's decode step on the same state and inputs, all host
+            # threads over the 4096 (sequence, head) units, 20 steps
+            import oracle
+            S_host = dd["S"].double().numpy()
+            t0 = time.perf_counter()
+            for i in range(20):
+                _, S_host = oracle.decode(*(dd[x][i % c4["steps"]] for x in NAMES), S_host)
+            out["decode"]["oracle_ms_per_step"] = round((time.perf_counter() - t0) / 20 * 1e3, 2)
+            out["decode"]["oracle_cores"] = oracle.max_threads()
+            del S_host
 
         # the chunked backward of the same layer (dL/do ~ N(0,1), dL/dS_final = 0)
         grads = gi.make_bwd_grads(B, T, H, d, d, "bf16", seed=2, with_dS=False)

@@ -132,23 +132,17 @@ def test_bwd_deterministic(g):
         np.testing.assert_array_equal(a[name], b[name])
 
 
-def test_bwd_layer_8x4096x16_sampled_units(g):
-    """Full headline size (B=8, T=4096, H=16, d=128, bf16); the oracle
-    recomputes the gradients of two (batch, head) units end to end."""
+def test_bwd_layer_8x4096x16_all_units(g):
+    """Full headline size (B=8, T=4096, H=16, d=128, bf16) with dL/dS_final:
+    every element of every gradient and of dS0 against the oracle's backward
+    of the whole layer (all 128 (batch, head) units)."""
     c = gi.WORKLOADS["layer_8x4096x16_d128"]
     inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], s0=c["s0"])
     grads = gi.make_bwd_grads(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", c["seed"])
     print("case layer backward", flush=True)
     got = gpu_bwd(g, inp, grads, 64)
-    for name in got:
-        assert np.isfinite(got[name]).all(), name
-    for (bb, hh) in ((0, 0), (6, 11)):
-        sub = {x: inp[x][bb:bb + 1, :, hh:hh + 1].contiguous() for x in NAMES}
-        S0 = None if inp["S0"] is None else inp["S0"][bb:bb + 1, hh:hh + 1].contiguous()
-        ref = oracle.bwd(*(sub[x] for x in NAMES), grads["dout"][bb:bb + 1, :, hh:hh + 1].contiguous(),
-                         S0=S0, dS_final=grads["dS_final"][bb:bb + 1, hh:hh + 1].contiguous())
-        sel = lambda name, x: x[bb:bb + 1, hh:hh + 1] if name == "dS0" else x[bb:bb + 1, :, hh:hh + 1]
-        check(got, ref, TOL["bf16"], f"layer b={bb} h={hh}", sel=sel)
+    ref = oracle.bwd(*(inp[x] for x in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"])
+    check(got, ref, TOL["bf16"], "layer backward")
 
 
 def gpu_bwd_raw(g, inp, grads, chunk, layer_prep=False):
