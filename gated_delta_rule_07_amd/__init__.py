@@ -117,6 +117,28 @@ def _require_device(*ts) -> None:
             raise ValueError("libgdn2 takes contiguous device tensors")
 
 
+def _require(t, name: str, shape: tuple, dtype) -> None:
+    """A caller-provided tensor: on the device, contiguous, of this shape and dtype."""
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, not {list(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+
+
+def _require_workspace(ws, need: int) -> int:
+    """Bytes of a caller-provided workspace (a contiguous device tensor)."""
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, {need} are needed")
+    return nbytes
+
+
 def _gate_flags(q, v, alpha, b, w) -> int:
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -156,17 +178,23 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
             raise TypeError("q, k, v, alpha, b, w must share one dtype")
     if layer_prep and alpha.dtype != torch.float32:
         raise TypeError("with layer_prep, alpha is the float32 log-decay")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, T, H, d]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    _require(k, "k", (B, T, H, dk), q.dtype)
+    _require(v, "v", (B, T, H, dv), q.dtype)
     gate_flags = _gate_flags(q, v, alpha, b, w)
     if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
         N = cu_seqlens.numel() - 1
     else:
         N = B
     if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (N, H, dk, dv)):
         raise ValueError(f"S0 must be float32 [{N}, {H}, {dk}, {dv}]")
+    _require(out, "out", (B, T, H, dv), q.dtype)
+    _require(S_final, "S_final", (N, H, dk, dv), torch.float32)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     Sf = S_final
     if Sf is None and want_final:
@@ -182,7 +210,10 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-        ws_bytes = workspace.numel()
+            ws_bytes = workspace.numel()
+        else:
+            # a smaller workspace is allowed (the plain two-pass size): the library checks it
+            ws_bytes = _require_workspace(workspace, 0)
     _check(lib().gdn2_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, dt, flags,
@@ -239,11 +270,14 @@ def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=Non
     ws_bytes = bwd_workspace_bytes(B, T, H, dk, dv, ns, chunk, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    for name, like in src.items():
+        _require(out[name], name, tuple(like.shape), like.dtype)
+    _require(out.get("dS0"), "dS0", (N, H, dk, dv), torch.float32)
     _check(lib().gdn2_chunk_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, dk, dv, ns, chunk, dt, flags, _ptr(dout), _ptr(dS_final),
         _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]),
-        _ptr(out["dw"]), _ptr(out.get("dS0")), _ptr(workspace), workspace.numel(), _stream()))
+        _ptr(out["dw"]), _ptr(out.get("dS0")), _ptr(workspace), _require_workspace(workspace, 0), _stream()))
     out.setdefault("dS0", None)
     return out
 
@@ -287,7 +321,7 @@ def segment_map(q, k, v, alpha, b, w, cu_seqlens=None, chunk: int = 64, layer_pr
     _check(lib().gdn2_chunk_segment_map(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens),
         B, T, H, dk, dv, ns, chunk, dt, flags, _ptr(Phi), _ptr(Psi), _ptr(workspace),
-        workspace.numel(), _stream()))
+        _require_workspace(workspace, 0), _stream()))
     return Phi, Psi
 
 
@@ -313,10 +347,15 @@ def decode_step(q, k, v, alpha, b, w, S, out=None):
     """One decode step: inputs [N, H, d]; S [N, H, dk, dv] float32, updated in place."""
     _require_device(q, k, v, alpha, b, w, S)
     dt = _dtype_code(q)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [N, H, d]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    for t, name, d in ((k, "k", dk), (alpha, "alpha", dk), (b, "b", dk), (v, "v", dv), (w, "w", dv)):
+        _require(t, name, (N, H, d), q.dtype)
     if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
         raise ValueError(f"S must be float32 [{N}, {H}, {dk}, {dv}]")
+    _require(out, "out", (N, H, dv), q.dtype)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _check(lib().gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                   _ptr(S), _ptr(o), N, H, dk, dv, dt, _stream()))

@@ -370,9 +370,10 @@ hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, const
 }
 
 // Byte layout of the backward's workspace: chunk table (packed input), the
-// forward's per-chunk blocks, entering states and leaving-state gradients.
+// forward's per-chunk blocks, entering states, leaving-state gradients and
+// one flag byte per chunk-head (strong decay: see gdn2_bwd_grad_kernel).
 struct bwd_plan {
-  size_t table, blocks, states, dstates, total;
+  size_t table, blocks, states, dstates, flags, total;
 };
 
 bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk, bool packed) {
@@ -384,7 +385,8 @@ bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk,
   p.blocks = slots * H * chunk_block_bytes_rt(dt, d, chunk);
   p.states = align256(slots * H * sq);
   p.dstates = p.states;
-  p.total = p.table + p.blocks + p.states + p.dstates;
+  p.flags = align256(slots * H);  // one byte per chunk-head: the gradient kernel's strong-decay path
+  p.total = p.table + p.blocks + p.states + p.dstates + p.flags;
   return p;
 }
 
@@ -796,6 +798,7 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   a.blocks = ws + plan.table;
   a.states = ws + plan.table + plan.blocks;
   ba.dstates = ws + plan.table + plan.blocks + plan.states;
+  ba.pwflag = reinterpret_cast<unsigned char *>(ws + plan.table + plan.blocks + plan.states + plan.dstates);
   ba.dout = dout;
   ba.dSf = dS_final;
   ba.dS0 = dS0;

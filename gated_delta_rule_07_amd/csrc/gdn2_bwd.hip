@@ -20,9 +20,17 @@
 // channel; rho_I = g before 16-token sub-block I; e = b (.) k; u = w (.) v):
 //   QS = q e^{g}, ES = e e^{g}, KB = k e^{g_C - g}        (chunk-start scale)
 //   QR = q e^{g - rho_I(t)}, ER = e e^{g - rho_I(t)}       (own sub-block)
-//   KR_I = k e^{rho_I - g}  for rows in sub-blocks <= I
-//   A = strict-lower(ER KR^T), P = lower(QR KR^T), per sub-block row I with
-//       KR_I, so every factor e^{g_t - g_s} is a product of two bounded ones
+//   K~ = k e^{rho_{J+1} - g}  (key s of sub-block J, to the end of J)
+//   A = strict-lower(ER X K~^T), P = lower(QR X K~^T) with X the factor
+//       e^{rho_I - rho_{J+1}} between the pair's sub-blocks: every factor
+//       e^{g_t - g_s} is a product of bounded ones.  Each factor is a sum of
+//       log decays taken directly (never the difference of two prefix
+//       sums), so alpha = 0 (ln = -inf) gives exact zeros, not NaN.  A
+//       diagonal pair (I = J) takes X = e^{-(sub-block's log decay)}, bounded
+//       while that decay is above e^-DIAG_LIM_LN; a chunk with a stronger one
+//       (or alpha = 0) is left to the kernel's PW variant, which forms the
+//       diagonal blocks and their gradients pair by pair with running
+//       products of the alphas
 //   T = (I + A)^{-1},  Y = U - ES S,  Z = T Y
 //   O = QS S + P Z,  S_C = Diag(e^{g_C}) S + KB^T Z.
 // Reverse mode: dZ = P^T dO + KB dH, dY = T^T dZ, dA = -strict-lower(dY Z^T),
@@ -215,13 +223,15 @@ __global__ void __launch_bounds__(64 * dstate_cfg<D>::NW) gdn2_bwd_dstate_kernel
 //   ST  : T (C x C);  SP: P (C x C)
 //   YZ  : Y, then Z, then the dK~ accumulators (fragment order)
 //   DOZ : A (until T is done), then dO, then dZ (sized for both)
-template <int D, int C> struct bwd_lds {
+template <int D, int C, bool PW = false> struct bwd_lds {
   static constexpr int NB = C / 16, PD = D + 4, PC = C + 4;
   // DOZ also holds A (C x C, pitch PC) early on, so it spans the larger of the two
   static constexpr int DOZ_FLOATS = (C * PD > C * PC) ? C * PD : C * PC;
   static constexpr int KT = 0, ST = KT + C * PD, SP = ST + C * PC, YZ = SP + C * PC, DOZ = YZ + C * PD,
                        BTOT = DOZ + DOZ_FLOATS, GTOT = BTOT + NB * D, KBS = GTOT + NB * D, DGAM = KBS + NB * D,
-                       FLOATS = DGAM + D;
+                       PWF = DGAM + D,                // one flag per sub-block (strong decay)
+                       DIAG = PWF + NB,               // PW: dA_II, dP_II (16 x 16 each) per sub-block
+                       FLOATS = DIAG + (PW ? NB * 512 : 0);
 };
 
 // Fragments of a 16 x 16 tile at (r0, c0) of a row-major float32 matrix with
@@ -283,11 +293,19 @@ __device__ __forceinline__ f32x4 tri_row(f32x4 v, int lane, bool strict) {
 // the gate layouts and layer prep read from chunk_args::gates at run time.
 enum { BG_PLAIN = 0, BG_KDA = 1, BG_GDN = 2, BG_FLAGS = 3 };
 
-template <typename IO, int D, int C, typename CT, int GM>
+// Decay over a sub-block below e^-DIAG_LIM_LN (= 2^-64) in some channel: the
+// chunk goes to the PW variant.
+constexpr float DIAG_LIM_LN = 44.3614195558365f;
+
+// PW = false: every chunk whose sub-blocks all decay less than that; it
+// records for each chunk-head whether it left it (ba.pwflag).  PW = true:
+// launched after it, the chunks it left (every diagonal pair formed pairwise
+// from the chunk's inputs); the others exit at once.
+template <typename IO, int D, int C, typename CT, int GM, bool PW = false>
 __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args ba) {
   constexpr bool GN = GM != BG_PLAIN;
   const chunk_args &a = ba.f;
-  typedef bwd_lds<D, C> L;
+  typedef bwd_lds<D, C, PW> L;
   constexpr int NB = C / 16, NK = D / 16, PD = L::PD, PC = L::PC;
   __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *KT = sm + L::KT, *sT = sm + L::ST, *sP = sm + L::SP, *YZ = sm + L::YZ, *DOZ = sm + L::DOZ;
@@ -295,6 +313,10 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   float *sA = DOZ;
 
   const int slot = static_cast<int>(blockIdx.x / a.H), h = static_cast<int>(blockIdx.x - slot * a.H);
+  if constexpr (PW) {
+    if (!ba.pwflag[blockIdx.x])
+      return;  // the whole workgroup: this chunk-head is done
+  }
   int seq, len;
   long t0;
   if (!locate_chunk<C>(slot, a, seq, t0, len))
@@ -319,13 +341,17 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   const IO *__restrict__ w = static_cast<const IO *>(a.w);
   const IO *__restrict__ dout = static_cast<const IO *>(ba.dout);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  // cumulative log decay at the end of sub-block J, for this lane's RowFrag columns of tile kk
-  auto rho_end = [&](int J, int kk) {
+  // sums of whole sub-blocks' log decays (btot), for this lane's RowFrag
+  // columns of tile kk: sub-blocks lo .. hi - 1 (never a difference, so
+  // -inf stays -inf)
+  auto tot_sum = [&](int lo, int hi, int kk) {
     f32x4 r = zero4;
-    for (int J2 = 0; J2 <= J; ++J2)
+    for (int J2 = lo; J2 < hi; ++J2)
       r += *reinterpret_cast<const f32x4 *>(btot + J2 * D + 16 * kk + 4 * g);
     return r;
   };
+  // cumulative log decay at the end of sub-block J (finite without PW)
+  auto rho_end = [&](int J, int kk) { return tot_sum(0, J + 1, kk); };
   auto ex4 = [](f32x4 x) {
     f32x4 y;
 #pragma unroll
@@ -396,8 +422,10 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     return x;
   };
 
-  // ---- rows of the sub-block; g = cumulative ln(alpha) within the chunk
-  f32x4 qv[NK], kv[NK], ev[NK], gv[NK];
+  // ---- rows of the sub-block; gv = cumulative ln(alpha) within the
+  // sub-block (g_t - rho_I); PW: kfac = e^{rho_{I+1} - g_t} (the key's
+  // factor, from the suffix sums; otherwise key_fac forms it on use)
+  f32x4 qv[NK], kv[NK], ev[NK], gv[NK], kfac[PW ? NK : 1];
   {
     // every row load first, then the arithmetic
     raw4<IO> rq[NK], rk[NK], rb[NK], ra[NK];
@@ -455,9 +483,23 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       kv[kk] = kq;
       ev[kk] = bq * kq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gv[kk][i] = row16_inclusive_scan(lq[i]);
+      for (int i = 0; i < 4; ++i) {
+        gv[kk][i] = row16_inclusive_scan(lq[i]);  // g_t - rho_I
+        if constexpr (PW)
+          kfac[PW ? kk : 0][i] = __expf(row16_exclusive_suffix(lq[i]));  // e^{rho_{I+1} - g_t}
+      }
     }
+  }
+  {
+    float mn = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mn = fminf(mn, gv[kk][i]);
+    const bool pw_wave = __ballot(m == 15 && mn < -DIAG_LIM_LN) != 0;
+    if (lane == 0)
+      sm[L::PWF + I] = pw_wave ? 1.f : 0.f;
   }
   if (m == 15) {
 #pragma unroll
@@ -465,23 +507,67 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       *reinterpret_cast<f32x4 *>(btot + I * D + 16 * kk + 4 * g) = gv[kk];
   }
   lds_barrier();
+  if constexpr (!PW) {
+    bool any_pw = false;
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-    if (I > 0)
-      gv[kk] += rho_end(I - 1, kk);
+    for (int J = 0; J < NB; ++J)
+      any_pw = any_pw || sm[L::PWF + J] != 0.f;
+    if (threadIdx.x == 0)
+      ba.pwflag[blockIdx.x] = any_pw ? 1 : 0;
+    if (any_pw)
+      return;  // the whole workgroup (the flags are uniform): the PW variant takes it
+  }
+  // Without PW every sub-block decays by at most e^-DIAG_LIM_LN, so every
+  // cumulative log decay is finite and bounded (|g| <= C DIAG_LIM_LN / 16):
+  // gv becomes the chunk's cumulative g_t and the factors are differences
+  // of it.  With PW gv stays relative to the sub-block and every factor is
+  // a sum (any decay, -inf included).
+  if constexpr (!PW) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      if (I > 0)
+        gv[kk] += rho_end(I - 1, kk);
+  }
+  // e^{rho_{I+1} - g_t}, the key's factor
+  auto key_fac = [&](int kk) -> f32x4 {
+    if constexpr (PW)
+      return kfac[PW ? kk : 0];
+    else
+      return ex4(rho_end(I, kk) - gv[kk]);
+  };
+  // e^{g_t - rho_{J+1}} for J <= I (the row's side of pair (I, J))
+  auto row_fac = [&](int J, int kk) -> f32x4 {
+    if constexpr (PW)
+      return ex4(J < I ? gv[kk] + tot_sum(J + 1, I, kk) : gv[kk] - tot_sum(I, I + 1, kk));
+    else
+      return ex4(gv[kk] - rho_end(J, kk));
+  };
+  // e^{g_t} and e^{g_C - g_t}
+  auto start_fac = [&](int kk) -> f32x4 {
+    if constexpr (PW)
+      return ex4(gv[kk] + tot_sum(0, I, kk));
+    else
+      return ex4(gv[kk]);
+  };
+  auto end_fac = [&](int kk) -> f32x4 {
+    if constexpr (PW)
+      return kfac[PW ? kk : 0] * ex4(tot_sum(I + 1, NB, kk));
+    else
+      return ex4(rho_end(NB - 1, kk) - gv[kk]);
+  };
 
   // ---- K~ rows to LDS, then A and P tiles (I, J <= I)
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
-    st_rowf(KT, PD, 16 * I, 16 * kk, lane, kv[kk] * ex4(rho_end(I, kk) - gv[kk]));
+    st_rowf(KT, PD, 16 * I, 16 * kk, lane, kv[kk] * key_fac(kk));
   lds_barrier();
 #pragma unroll
   for (int J = 0; J < NB; ++J) {
-    if (J <= I) {  // J unrolled: the decay sums of rho_end become independent reads
+    if (J < I || (J == I && !PW)) {  // J unrolled: the decay sums become independent reads
       f32x4 aa = zero4, pp = zero4;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
+        const f32x4 sc = row_fac(J, kk);
         const F kt = F::from(ld_rowf(KT, PD, 16 * J, 16 * kk, lane));
         mm_io(aa, F::from(ev[kk] * sc), kt);
         mm_io(pp, F::from(qv[kk] * sc), kt);
@@ -493,6 +579,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       st_colf(sA, PC, 16 * I, 16 * J, lane, aa);
       st_colf(sP, PC, 16 * I, 16 * J, lane, pp);
     }
+  }
+  if constexpr (PW) {
+    // the diagonal pair, token by token (any decay, alpha = 0 included)
+    f32x4 da, dp;
+    wy_diag_pairwise<IO, D>(a, t0, len, h, I, lane, qs, ks, da, dp);
+    st_rowf(sA, PC, 16 * I, 16 * I, lane, da);
+    st_rowf(sP, PC, 16 * I, 16 * I, lane, dp);
   }
   lds_barrier();
 
@@ -522,7 +615,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     F esf[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      esf[kk] = F::from(ev[kk] * ex4(gv[kk]));
+      esf[kk] = F::from(ev[kk] * start_fac(kk));  // e e^{g_t}
     // S tiles of column n + 1 are loaded while column n is multiplied
     F cur[NK], nxt[NK];
 #pragma unroll
@@ -591,7 +684,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     F kbf[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      kbf[kk] = F::from(kv[kk] * ex4(rho_end(NB - 1, kk) - gv[kk]));
+      kbf[kk] = F::from(kv[kk] * end_fac(kk));  // k e^{g_C - g_t}
     F cur[NK], nxt[NK];  // dH tiles, column n + 1 in flight during column n
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
@@ -697,6 +790,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     dPc[J] = F::from(pc);
     dPr[J] = F::from(pr);
   }
+  if constexpr (PW) {
+    // this sub-block's diagonal dA, dP (row t = m, columns 4g .. 4g+3), for
+    // the pairwise gradients below (read by this wave only)
+    float *dA_I = sm + L::DIAG + I * 512, *dP_I = dA_I + 256;
+    *reinterpret_cast<f32x4 *>(dA_I + m * 16 + 4 * g) = dAr[I].to_f32();
+    *reinterpret_cast<f32x4 *>(dP_I + m * 16 + 4 * g) = dPr[I].to_f32();
+  }
 
   // ---- contributions to dq (cq), de (ce), dk (ck) and d g_C (kb term)
   f32x4 cq[NK], ce[NK], ck[NK];
@@ -728,21 +828,47 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       scur[n] = snxt[n];
       hcur[n] = hnxt[n];
     }
-    const f32x4 eg = ex4(gv[kk]);
+    const f32x4 eg = start_fac(kk);  // e^{g_t}
     cq[kk] = a1 * eg;
     ce[kk] = -(a2 * eg);
-    ck[kk] = a3 * ex4(rho_end(NB - 1, kk) - gv[kk]);  // dKB e^{g_C - g}
+    ck[kk] = a3 * end_fac(kk);  // dKB e^{g_C - g}
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
-      if (J <= I) {
+      if (J < I || (J == I && !PW)) {
         const F ktc = F::from(ld_colf(KT, PD, 16 * J, 16 * kk, lane));
         f32x4 aq = zero4, ae = zero4;
         mm_io(aq, ktc, dPr[J]);
         mm_io(ae, ktc, dAr[J]);
-        const f32x4 sc = ex4(gv[kk] - rho_end(J, kk));
+        const f32x4 sc = row_fac(J, kk);
         cq[kk] += aq * sc;
         ce[kk] += ae * sc;
       }
+    }
+    if constexpr (PW) {
+      // the diagonal pair: dq_t += sum_s dP_ts k_s F_ts, de_t += sum_s dA_ts k_s F_ts
+      // over s = t - j of this sub-block, F_ts = alpha_t .. alpha_{s+1}
+      f32x4 q4, k4, e4, a4;
+      wy_row4<IO, D>(a, srow, valid, 16 * kk + 4 * g, qs, ks, q4, k4, e4, a4);
+      const float *dA_I = sm + L::DIAG + I * 512, *dP_I = dA_I + 256;
+      f32x4 Fp = {1.f, 1.f, 1.f, 1.f}, xq = zero4, xe = zero4;
+#pragma unroll 1
+      for (int j = 0; j < 16; ++j) {
+        const int src = m >= j ? lane - j : lane, srca = m >= j ? lane - j + 1 : lane;
+        f32x4 kf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (j > 0)
+            Fp[i] *= __shfl(a4[i], srca, 64);
+          kf[i] = __shfl(k4[i], src, 64) * Fp[i];
+        }
+        if (m >= j) {
+          xq += kf * dP_I[m * 16 + (m - j)];
+          if (j > 0)
+            xe += kf * dA_I[m * 16 + (m - j)];
+        }
+      }
+      cq[kk] += xq;
+      ce[kk] += xe;
     }
   }
 
@@ -761,7 +887,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const f32x4 sc = valid ? ex4(gv[kk] - rho_end(I, kk)) : zero4;
+      // PW: e^{g_t - rho_I} (column factors from rho_I); else e^{g_t - rho_{I+1}}
+      const f32x4 sc = valid ? (PW ? ex4(gv[kk]) : ex4(gv[kk] - rho_end(I, kk))) : zero4;
       const f32x4 bq = GN ? ld_b(16 * kk + 4 * g) : rb[kk].f();
       qrc[kk] = transpose_f32(rq[kk].f() * (qs * sc), lane);
       erc[kk] = transpose_f32(bq * rk[kk].f() * (ks * sc), lane);
@@ -773,8 +900,9 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     return reinterpret_cast<f32x4 *>(sm) + ((I2 * (I2 + 1) / 2 + J2) * NK + kk) * 64;
   };
   {
-    // column scale e^{rho_I - rho_J} of ColFrag element (lane column c),
-    // summed up while J descends from I
+    // column scale of ColFrag element (lane column c): e^{rho_I - rho_{J+1}}
+    // (the sub-blocks between J and I, summed up while J descends), and
+    // e^{-(sub-block I's log decay)} for the diagonal pair
     float rs[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
@@ -784,12 +912,24 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       if (J <= I) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          if (J < I)
-            rs[kk] += btot[(J + 1) * D + 16 * kk + m];
-          const float f = __expf(rs[kk]);
           f32x4 acc = zero4;
-          mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
-          mm_io(acc, F::from(erc[kk] * f), dAc[J]);
+          if constexpr (PW) {
+            // e^{rho_I - rho_{J+1}} for J < I; the diagonal pair is added below
+            if (J < I - 1)
+              rs[kk] += btot[(J + 1) * D + 16 * kk + m];
+            if (J < I) {
+              const float f = __expf(rs[kk]);
+              mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
+              mm_io(acc, F::from(erc[kk] * f), dAc[J]);
+            }
+          } else {
+            // e^{rho_{I+1} - rho_{J+1}}
+            if (J < I)
+              rs[kk] += btot[(J + 1) * D + 16 * kk + m];
+            const float f = __expf(rs[kk]);
+            mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
+            mm_io(acc, F::from(erc[kk] * f), dAc[J]);
+          }
           dk_slot(I, J, kk)[lane] = acc;
         }
       }
@@ -837,7 +977,31 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     for (int I2 = 0; I2 < NB; ++I2)
       if (I2 >= I)
         dkt += dk_slot(I2, I, kk)[lane];
-    const f32x4 ckt = dkt * ex4(rho_end(I, kk) - gv[kk]);
+    f32x4 ckt = dkt * key_fac(kk);
+    if constexpr (PW) {
+      // the diagonal pair: dk_s += sum_t (dP_ts q_t + dA_ts e_t) F_ts over
+      // t = s + j of this sub-block, F_ts = alpha_{s+1} .. alpha_t
+      f32x4 q4, k4, e4, a4;
+      wy_row4<IO, D>(a, srow, valid, 16 * kk + 4 * g, qs, ks, q4, k4, e4, a4);
+      const float *dA_I = sm + L::DIAG + I * 512, *dP_I = dA_I + 256;
+      f32x4 Fk = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+      for (int j = 0; j < 16; ++j) {
+        const int src = m + j <= 15 ? lane + j : lane;
+        f32x4 qt, et;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (j > 0)
+            Fk[i] *= __shfl(a4[i], src, 64);
+          qt[i] = __shfl(q4[i], src, 64);
+          et[i] = __shfl(e4[i], src, 64);
+        }
+        if (m + j <= 15) {
+          const int tt = m + j;
+          ckt += (qt * dP_I[tt * 16 + m] + (j > 0 ? et * dA_I[tt * 16 + m] : zero4)) * Fk;
+        }
+      }
+    }
     const int c0 = 16 * kk + 4 * g;
     f32x4 qq = nq.f() * qs, kq = nk.f() * ks, bq = GN ? ld_b(c0) : nb.f();
     if (!valid)
@@ -963,19 +1127,35 @@ template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args
   return hipGetLastError();
 }
 
-template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st) {
+// Two launches: every chunk-head whose decays allow the matrix-core
+// diagonal, then the PW variant on the rest (flags from the first).
+template <typename IO, int D, int C, bool PW> hipError_t launch_bwd_grad_pass(const bwd_args &a, hipStream_t st) {
   const long n = static_cast<long>(a.f.num_slots) * a.f.H;
   const dim3 grid(static_cast<unsigned>(n)), block(64 * (C / 16));
   const uint32_t kda = GATE_SCALAR_B | GATE_SCALAR_W, gdn = kda | GATE_SCALAR_ALPHA;
-  if (a.f.gates == 0)
-    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_PLAIN>), grid, block, 0, st, a);
-  else if (a.f.gates == kda)
-    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_KDA>), grid, block, 0, st, a);
-  else if (a.f.gates == gdn)
-    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_GDN>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_FLAGS>), grid, block, 0, st, a);
+  if constexpr (PW) {
+    // the rare path: one variant that reads every input layout from the flags
+    (void)kda;
+    (void)gdn;
+    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_FLAGS, true>), grid, block, 0, st, a);
+  } else {
+    if (a.f.gates == 0)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_PLAIN, false>), grid, block, 0, st, a);
+    else if (a.f.gates == kda)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_KDA, false>), grid, block, 0, st, a);
+    else if (a.f.gates == gdn)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_GDN, false>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<IO, D, C, IO, BG_FLAGS, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
+}
+
+template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st) {
+  const hipError_t e = launch_bwd_grad_pass<IO, D, C, false>(a, st);
+  if (e != hipSuccess)
+    return e;
+  return launch_bwd_grad_pass<IO, D, C, true>(a, st);
 }
 
 #define GDN2_INST_BWD(IO, D, C)                                                    \

@@ -49,10 +49,11 @@ gdn2_chunk_prep_kernel(chunk_args a) {
   raw4<IO> rv[NB][CTW], rw[NB][CTW];
   wy_load_chunk<IO, D, C, CTW, GM>(a, t0, len, h, I, ct0, owner, m, g, r, rv, rw);
   f32x4 gl[NK];
-  wy_decay<IO, D, C, LP>(sm, r, gl, I, tid, reinterpret_cast<float *>(blk + L::GAM));
+  bool pw;
+  wy_decay<IO, D, C, LP>(sm, r, gl, pw, a, t0, len, h, I, tid, reinterpret_cast<float *>(blk + L::GAM));
   const F eye = identity_colfrag<IO>(lane);
   wy_ops<IO, D> op;
-  wy_operands<IO, D, C, LP>(sm, r, gl, I, lane, eye, blk + L::KB, op);
+  wy_operands<IO, D, C, LP>(sm, r, gl, pw, a, t0, len, h, I, lane, eye, blk + L::KB, op);
   F ucol[NB][CTW];
   wy_values<IO, NB, CTW, LP>(rv, rw, eye, ucol);
   __syncthreads();

@@ -165,11 +165,17 @@ template <> struct frag<float> {
 __device__ __forceinline__ void mma16(f32x4 &acc, const frag<bf16_t> &a, const frag<bf16_t> &b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, acc, 0, 0, 0);
 }
+// The float32 product is four 16x16x4 instructions, each from a zero
+// accumulator, summed on the vector ALU: no product reads another's result
+// as its accumulator (chained float32 accumulators whose destination
+// differs from their source were measured to read stale values here).
 __device__ __forceinline__ void mma16(f32x4 &acc, const frag<float> &a, const frag<float> &b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc, 0, 0, 0);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], z, 0, 0, 0);
+  const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], z, 0, 0, 0);
+  const f32x4 p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], z, 0, 0, 0);
+  const f32x4 p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], z, 0, 0, 0);
+  acc += (p0 + p1) + (p2 + p3);
 }
 
 // Product shapes and accumulators.  On gfx950 an accumulator written by a
@@ -264,22 +270,14 @@ __device__ __forceinline__ f32x4 transpose_frag(const frag<T> &x, const frag<T> 
   return acc;
 }
 
-// acc (ColFrag) += a (RowFrag) * b (ColFrag), operands rounded to CT.  The
-// bfloat16 product is one 16x16x16 instruction accumulating in place.  The
-// float32 one is four 16x16x4 instructions; each starts from zero and the
-// four are summed on the vector ALU, so that no product reads another's
-// result as its accumulator (chained float32 accumulators whose destination
-// differs from their source were measured to read stale values here).
+// acc (ColFrag) += a (RowFrag) * b (ColFrag), operands rounded to CT: one
+// 16x16x16 bfloat16 instruction accumulating in place, or the float32 form
+// of mma16 above.
 template <typename CT> __device__ __forceinline__ void mm(f32x4 &acc, f32x4 a, f32x4 b) {
   if constexpr (sizeof(CT) == 2) {
     mma16(acc, frag<CT>::from(a), frag<CT>::from(b));
   } else {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], z, 0, 0, 0);
-    const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], z, 0, 0, 0);
-    const f32x4 p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], z, 0, 0, 0);
-    const f32x4 p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], z, 0, 0, 0);
-    acc += (p0 + p1) + (p2 + p3);
+    mma16(acc, frag<float>::from(a), frag<float>::from(b));
   }
 }
 

@@ -98,9 +98,10 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
     const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
 
     f32x4 gl[NK];
-    wy_decay<IO, D, C, LP>(sm, r, gl, I, tid, reinterpret_cast<float *>(tiles + L::GAM));
+    bool pw;
+    wy_decay<IO, D, C, LP>(sm, r, gl, pw, a, t0, len, h, I, tid, reinterpret_cast<float *>(tiles + L::GAM));
     wy_ops<IO, D> op;
-    wy_operands<IO, D, C, LP>(sm, r, gl, I, lane, eye, tiles + L::KB, op);
+    wy_operands<IO, D, C, LP>(sm, r, gl, pw, a, t0, len, h, I, lane, eye, tiles + L::KB, op);
     F ucol[NB][NVW];
     wy_values<IO, NB, NVW, LP>(rv, rw, eye, ucol);
     if (c > 0)

@@ -53,6 +53,7 @@ struct bwd_args {
   void *dstates;         // dL/d(state leaving each chunk), state_tiles blocks like states
   float *dS0;            // dL/dS0 [N, H, dk, dv] or nullptr
   void *dq, *dk, *dv, *dal, *db, *dw;  // gradients, element type IO, input layouts
+  unsigned char *pwflag;  // [num_slots * H]: chunk-heads whose gradients need the pairwise diagonal path
 };
 
 template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args &a, hipStream_t st);

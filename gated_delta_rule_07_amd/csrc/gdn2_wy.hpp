@@ -23,16 +23,27 @@
 // the entering state only enters through three state-sized products.
 //
 // Numerics of the decay factorisation: every factor exp(g_t - g_s) with s <= t
-// is at most 1, but splitting it as gamma_t / gamma_s can overflow.  A and P
-// are therefore built per 16-token sub-block with the reference point at the
-// start of the row's own sub-block I:
-//   A[t][s] = sum_c (b k_t e^{g_t - rho_I}) (k_s e^{rho_J - g_s}) e^{rho_I - rho_J}
-// for s in sub-block J <= I, rho_J = g just before sub-block J; the last
-// factor is applied to the keys of sub-block J (one rescaled copy per later
-// sub-block, shared by A and P).  The first and last factors are <= 1; the
-// middle one is bounded by the decay over one 16-token sub-block.  E, Qchk
-// and Kbar use the chunk start / chunk end and are <= 1.
-//
+// is at most 1, but splitting it as gamma_t / gamma_s can overflow, and with
+// alpha = 0 (log -inf) a difference of two prefix sums is -inf - (-inf).
+// Every factor below is therefore a sum of log decays taken directly (a
+// prefix or suffix scan, or a sum of whole sub-blocks), never a difference,
+// and is at most 1, except on the diagonal blocks.  Per 16-token sub-block
+// I (rho_I = g just before it):
+//   rows     e^{g_t - rho_I}  (prefix within the sub-block)
+//   keys     e^{rho_{I+1} - g_s} (suffix within the sub-block: the key
+//            referenced to the END of its own sub-block)
+//   between  e^{rho_I - rho_{J+1}} (whole sub-blocks J+1 .. I-1), folded into
+//            the keys of sub-block J for row sub-block I > J
+//   A[t][s] = sum_c (b k_t e^{g_t - rho_I}) (k_s e^{rho_{J+1} - g_s}) e^{rho_I - rho_{J+1}}
+// E, Qchk use the chunk start (e^{g_t} = e^{rho_I} e^{g_t - rho_I}) and Kbar
+// the chunk end (e^{g_C - g_s} = e^{rho_{J+1} - g_s} e^{g_C - rho_{J+1}}).
+// The diagonal blocks (s, t in one sub-block) take the key factor
+// e^{rho_I - g_s} <= e^{-(sub-block's log decay)}: while every channel's
+// decay over the sub-block is above 2^-64 that is bounded and the block is
+// one matrix-core product; otherwise (very strong decay, alpha = 0) the
+// sub-block's wave forms the block pairwise, token by token, with running
+// products of the alphas themselves (wy_diag_pairwise).
+
 // Work split inside a workgroup of C/16 waves (the "wy" phases below):
 //   rows     wave I owns the 16-token sub-block I: loads of q, k, alpha, b,
 //            log2(alpha) and its prefix sum over tokens (DPP row scan), the
@@ -194,10 +205,11 @@ template <typename IO, int D, int C> struct wy_smem {
   static constexpr int TB = frag<IO>::TILE_BYTES;
   float tot[NB][D];                  // per-sub-block sum of log2(alpha)
   float f1[NB][D];                   // exp2(rho_I): decay from chunk start to sub-block I
-  float f2[NB][D];                   // exp2(g_C - rho_I): decay from sub-block I to chunk end
-  float sig[NP > 0 ? NP : 1][D];     // exp2(rho_I - rho_J) <= 1 for the pair (I, J), J < I
+  float f2[NB][D];                   // exp2(g_C - rho_{I+1}): decay after sub-block I to chunk end
+  float sig[NP > 0 ? NP : 1][D];     // exp2(rho_I - rho_{J+1}) <= 1 for the pair (I, J), J < I
   float ad[NB][16][16];              // diagonal blocks of A, row-major
-  // RowFrag(Khat_J * sig_IJ) for each pair (I, J), k tiles paired; after the
+  // RowFrag(k_s e^{rho_I - g_s}) (keys of sub-block J for rows of sub-block
+  // I, J < I) for each pair (I, J), k tiles paired; after the
   // A/P products the same bytes hold RowFrag(Qchk) tiles [NB][NK]
   alignas(16) unsigned char khs[NKS][NK][TB];
   alignas(16) unsigned char ec[NB][NK][TB];  // ColFrag(E_J), one tile per 16 channels
@@ -383,66 +395,154 @@ __device__ __forceinline__ void wy_load_chunk(const chunk_args &a, long t0, int 
 #undef GDN2_LOAD
 }
 
-// Phase 1: log2(alpha), prefix sums over the tokens of each sub-block, and the
-// per-channel factors between sub-block boundaries.  On return gl holds the
-// in-sub-block prefix sums g_t - rho_I.  gam_out[c] = gamma_C (may be LDS or
-// global memory).  Contains two workgroup barriers.
-template <typename IO, int D, int C, bool LP = false>
-__device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO, D, LP> &r, f32x4 (&gl)[D / 16],
-                                         int I, int tid, float *gam_out) {
-  constexpr int NB = C / 16, NK = D / 16;
-  const int lane = tid & 63, m = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    if constexpr (LP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gl[kk][i] = row16_inclusive_scan(r.lg[kk][i]);
-    } else {
-      const f32x4 al = r.al[kk].f();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gl[kk][i] = row16_inclusive_scan(fast_log2(al[i]));
-    }
-  }
-  if (m == 15) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      *reinterpret_cast<f32x4 *>(&sm.tot[I][16 * kk + 4 * g]) = gl[kk];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < NB * D; idx += 64 * NB) {
-    const int J = idx / D, c = idx - J * D;
-    float rho = 0.f, suf = 0.f;
-#pragma unroll
-    for (int K = 0; K < NB; ++K) {
-      const float x = sm.tot[K][c];
-      if (K < J)
-        rho += x;
-      else
-        suf += x;
-    }
-    sm.f1[J][c] = fast_exp2(rho);
-    sm.f2[J][c] = fast_exp2(suf);
-    float part = 0.f;  // sum of tot over sub-blocks J .. I2-1
-#pragma unroll
-    for (int I2 = 1; I2 < NB; ++I2) {
-      if (I2 > J) {
-        part += sm.tot[I2 - 1][c];
-        sm.sig[pair_index(I2, J)][c] = fast_exp2(part);
-      }
-    }
-    if (J == 0)
-      gam_out[c] = fast_exp2(suf);
-  }
-  __syncthreads();
+// Decay over a sub-block below 2^-DIAG_LIM (in some channel) sends that
+// sub-block's diagonal A and P blocks to the pairwise path.
+constexpr float DIAG_LIM = 64.f;
+
+// Value of lane m - J of this lane's DPP row (lanes 16g .. 16g+15), zero for
+// m < J (row_shr:J).
+template <int J> __device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + J, 0xF, 0xF, false));
+}
+// Value of lane m + J of this lane's DPP row, zero for m + J > 15 (row_shl:J).
+template <int J> __device__ __forceinline__ float row_shl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + J, 0xF, 0xF, false));
+}
+// Sum of x over the lanes after this one in its DPP row (an exclusive
+// suffix scan over the 16 tokens of a sub-block).
+__device__ __forceinline__ float row16_exclusive_suffix(float x) {
+  x = row_shl<1>(x);
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
+  return x;
 }
 
-// Register operands of the A and P products for sub-block I.
-template <typename IO, int D> struct wy_ops {
-  static constexpr int NK = D / 16;
-  frag<IO> ef[NK], qf[NK], khf[NK], qcf[NK];
-};
+__device__ __forceinline__ float dot4(f32x4 x, f32x4 y) { return (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]); }
+
+// Row `row` ((token, head) index) of the inputs, this lane's channels
+// c0 .. c0+3, as the recurrence's float32 values: q and k (times the row
+// scales qs, ks: the L2 normalisation under layer prep, else 1), e = b (.) k
+// and alpha itself.  Gate layouts and layer prep are read from a.gates.  An
+// invalid row gives k = 0 and alpha = 1.
+template <typename IO, int D>
+__device__ __forceinline__ void wy_row4(const chunk_args &a, size_t row, bool valid, int c0, float qs, float ks,
+                                        f32x4 &q4, f32x4 &k4, f32x4 &e4, f32x4 &a4) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  const IO *bp = static_cast<const IO *>(a.b);
+  const bool lp = (a.gates & GATE_LAYER_PREP) != 0, sa = (a.gates & GATE_SCALAR_ALPHA) != 0;
+  q4 = io<IO>::load4(static_cast<const IO *>(a.q) + row * D + c0) * qs;
+  k4 = io<IO>::load4(static_cast<const IO *>(a.k) + row * D + c0) * ks;
+  f32x4 b4;
+  if (a.gates & GATE_SCALAR_B) {
+    const float x = io<IO>::to_f(bp[row]);
+    b4 = f32x4{x, x, x, x};
+  } else {
+    b4 = io<IO>::load4(bp + row * D + c0);
+  }
+  if (lp) {
+    const float *lg = static_cast<const float *>(a.al);
+    const f32x4 l = sa ? f32x4{lg[row], lg[row], lg[row], lg[row]} : *reinterpret_cast<const f32x4 *>(lg + row * D + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b4[i] = fast_sigmoid(b4[i]);
+      a4[i] = fast_exp2(l[i] * LOG2E);
+    }
+  } else if (sa) {
+    const float x = io<IO>::to_f(static_cast<const IO *>(a.al)[row]);
+    a4 = f32x4{x, x, x, x};
+  } else {
+    a4 = io<IO>::load4(static_cast<const IO *>(a.al) + row * D + c0);
+  }
+  if (!valid) {
+    k4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    a4 = f32x4{1.f, 1.f, 1.f, 1.f};
+  }
+  e4 = b4 * k4;
+}
+
+// log2(alpha) of this lane's row (token 16 I + m of the chunk at t0, head h)
+// for channels c0 .. c0+3, read again from global memory (layouts and layer
+// prep from a.gates); rows past the end give 0.
+template <typename IO, int D>
+__device__ __forceinline__ f32x4 wy_log_decay4(const chunk_args &a, long t0, int len, int h, int I, int lane,
+                                               int c0) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  const int t = 16 * I + (lane & 15);
+  const bool valid = t < len;
+  const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
+  const bool sa = (a.gates & GATE_SCALAR_ALPHA) != 0;
+  f32x4 x;
+  if (a.gates & GATE_LAYER_PREP) {
+    const float *lg = static_cast<const float *>(a.al);
+    x = sa ? f32x4{lg[row], lg[row], lg[row], lg[row]} : *reinterpret_cast<const f32x4 *>(lg + row * D + c0);
+    x *= LOG2E;
+  } else {
+    const IO *ap = static_cast<const IO *>(a.al);
+    const f32x4 al = sa ? f32x4{io<IO>::to_f(ap[row]), io<IO>::to_f(ap[row]), io<IO>::to_f(ap[row]),
+                                io<IO>::to_f(ap[row])}
+                        : io<IO>::load4(ap + row * D + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = fast_log2(al[i]);
+  }
+  return valid ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// The diagonal A and P blocks of sub-block I, pair by pair:
+//   A[t][s] = sum_c e_tc k_sc prod_{u=s+1..t} alpha_uc  (s < t),
+//   P[t][s] = sum_c q_tc k_sc prod_{u=s+1..t} alpha_uc  (s <= t),
+// with the decay a running product of the alphas, so that any decay (alpha
+// = 0 included) is exact to rounding.  The inputs are read again from
+// global memory, one tile of 16 channels at a time; lane (t, g) walks the
+// distances J = t - s in a loop, taking row t - J's values from the lane
+// J below it in its 16-lane row.  Returns the blocks in the accumulator
+// layout of the matrix-core product (lane (t, g) holds columns
+// s = 4g .. 4g+3 of row t), zero outside the triangles.  A slow path: the
+// loops are kept rolled so that it adds few registers to its kernel.
+template <typename IO, int D>
+__device__ __forceinline__ void wy_diag_pairwise(const chunk_args &a, long t0, int len, int h, int I, int lane,
+                                                 float qs, float ks, f32x4 &dA, f32x4 &dP) {
+  constexpr int NK = D / 16;
+  const int m = lane & 15, g = lane >> 4, t = 16 * I + m;
+  const bool valid = t < len;
+  const size_t row = static_cast<size_t>(t0 + (valid ? t : 0)) * a.H + h;
+  dA = dP = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int kk = 0; kk < NK; ++kk) {
+    f32x4 q4, k4, e4, a4;
+    wy_row4<IO, D>(a, row, valid, 16 * kk + 4 * g, qs, ks, q4, k4, e4, a4);
+    f32x4 F = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+    for (int J = 0; J < 16; ++J) {
+      // F = alpha_t .. alpha_{t-J+1}; the key of row t - J
+      const int src = m >= J ? lane - J : lane;
+      const int srca = m >= J ? lane - J + 1 : lane;
+      f32x4 kf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (J > 0)
+          F[i] *= __shfl(a4[i], srca, 64);
+        kf[i] = __shfl(k4[i], src, 64) * F[i];
+      }
+      float xa = m >= J ? dot4(e4, kf) : 0.f;
+      float xp = m >= J ? dot4(q4, kf) : 0.f;
+      xa += __shfl_xor(xa, 16, 64);
+      xp += __shfl_xor(xp, 16, 64);
+      xa += __shfl_xor(xa, 32, 64);
+      xp += __shfl_xor(xp, 32, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (m - (4 * g + i) == J) {
+          if (J > 0)
+            dA[i] += xa;
+          dP[i] += xp;
+        }
+      }
+    }
+  }
+}
 
 // Layer prep: 1 / ||q_t|| and 1 / ||k_t|| of this lane's row (zero rows keep
 // zero).  The lane holds 4 of every 16 channels; lanes m, m+16, m+32, m+48
@@ -469,14 +569,102 @@ __device__ __forceinline__ void wy_row_scales(const wy_rows<IO, D, true> &r, flo
   ks = sk > 0.f ? __frsqrt_rn(sk) : 0.f;
 }
 
+// Phase 1: log2(alpha), prefix sums over the tokens of each sub-block, and the
+// per-channel factors between sub-block boundaries.  On return gl holds the
+// in-sub-block prefix sums g_t - rho_I, and pw is true (the same on every
+// lane of the wave) when sub-block I's decay in some channel is below
+// 2^-DIAG_LIM: its diagonal blocks then take the pairwise path
+// (wy_diag_pairwise, on the inputs of the chunk at t0, len, head h, read
+// again from a), which writes them to LDS where wy_products would.  gam_out[c] = gamma_C (may be LDS or
+// global memory).  Contains two workgroup barriers.
+template <typename IO, int D, int C, bool LP = false>
+__device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO, D, LP> &r, f32x4 (&gl)[D / 16],
+                                         bool &pw, const chunk_args &a, long t0, int len, int h, int I, int tid,
+                                         float *gam_out) {
+  constexpr int NB = C / 16, NK = D / 16;
+  const int lane = tid & 63, m = lane & 15, g = lane >> 4;
+  float mn = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    f32x4 x;
+    if constexpr (LP) {
+      x = r.lg[kk];
+    } else {
+      const f32x4 al = r.al[kk].f();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[i] = fast_log2(al[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gl[kk][i] = row16_inclusive_scan(x[i]);
+      mn = fminf(mn, gl[kk][i]);
+    }
+  }
+  pw = __ballot(m == 15 && mn < -DIAG_LIM) != 0;
+  if (pw) {
+    // the diagonal A and P blocks go straight to where the products would
+    // put them (wy_products skips them)
+    float qs = 1.f, ks = 1.f;
+    if constexpr (LP)
+      wy_row_scales<IO, D>(r, qs, ks);
+    f32x4 da, dp;
+    wy_diag_pairwise<IO, D>(a, t0, len, h, I, lane, qs, ks, da, dp);
+    *reinterpret_cast<f32x4 *>(&sm.ad[I][m][4 * g]) = da;
+    frag<IO>::from(dp).st(sm.pr[tri_index(I, I)], lane);
+  }
+  if (m == 15) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      *reinterpret_cast<f32x4 *>(&sm.tot[I][16 * kk + 4 * g]) = gl[kk];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NB * D; idx += 64 * NB) {
+    const int J = idx / D, c = idx - J * D;
+    float rho = 0.f, suf = 0.f, all = 0.f;
+#pragma unroll
+    for (int K = 0; K < NB; ++K) {
+      const float x = sm.tot[K][c];
+      all += x;
+      if (K < J)
+        rho += x;
+      else if (K > J)
+        suf += x;
+    }
+    sm.f1[J][c] = fast_exp2(rho);
+    sm.f2[J][c] = fast_exp2(suf);
+    float part = 0.f;  // sum of tot over sub-blocks J+1 .. I2-1
+#pragma unroll
+    for (int I2 = 1; I2 < NB; ++I2) {
+      if (I2 > J) {
+        sm.sig[pair_index(I2, J)][c] = fast_exp2(part);
+        part += sm.tot[I2][c];
+      }
+    }
+    if (J == 0)
+      gam_out[c] = fast_exp2(all);
+  }
+  __syncthreads();
+}
+
+// Register operands of the A and P products for sub-block I.  With pw the
+// diagonal blocks are already in LDS (wy_decay).
+template <typename IO, int D> struct wy_ops {
+  static constexpr int NK = D / 16;
+  frag<IO> ef[NK], qf[NK], khf[NK], qcf[NK];
+  bool pw;
+};
+
 // Phase 1b: decayed, gated operands of sub-block I.  Writes the rescaled keys
 // for later sub-blocks and ColFrag(E) to LDS, and RowFrag(Kbar^T) tiles to
-// kb_out (the KB region of a block layout, LDS or global).
+// kb_out (the KB region of a block layout, LDS or global).  With pw (from
+// wy_decay) the key suffixes are read again from the chunk's inputs (chunk
+// t0, len, head h of a).
 template <typename IO, int D, int C, bool LP = false>
 __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows<IO, D, LP> &r,
-                                            const f32x4 (&gl)[D / 16], int I, int lane,
-                                            const frag<IO> &eye, unsigned char *kb_out,
-                                            wy_ops<IO, D> &op) {
+                                            const f32x4 (&gl)[D / 16], bool pw, const chunk_args &a, long t0,
+                                            int len, int h, int I, int lane,
+                                            const frag<IO> &eye, unsigned char *kb_out, wy_ops<IO, D> &op) {
   constexpr int NB = C / 16, NK = D / 16;
   typedef frag<IO> F;
   const int g = lane >> 4;
@@ -488,11 +676,24 @@ __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows
     const int c0 = 16 * kk + 4 * g;
     const f32x4 f1v = *reinterpret_cast<const f32x4 *>(&sm.f1[I][c0]);
     const f32x4 f2v = *reinterpret_cast<const f32x4 *>(&sm.f2[I][c0]);
-    f32x4 f, fi;
+    // suffix rho_{I+1} - g_t of the log decay within the sub-block: the
+    // sub-block's total minus the prefix while both are bounded, else the
+    // suffix scan of the log decays themselves (read again)
+    f32x4 sfx;
+    if (!pw) {
+      sfx = *reinterpret_cast<const f32x4 *>(&sm.tot[I][c0]) - gl[kk];
+    } else {
+      const f32x4 x = wy_log_decay4<IO, D>(a, t0, len, h, I, lane, c0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sfx[i] = row16_exclusive_suffix(x[i]);
+    }
+    f32x4 f, fk, fi;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[i] = fast_exp2(gl[kk][i]);    // e^{g_t - rho_I} <= 1
-      fi[i] = fast_exp2(-gl[kk][i]);  // e^{rho_I - g_t} >= 1
+      f[i] = fast_exp2(gl[kk][i]);                  // e^{g_t - rho_I} <= 1
+      fk[i] = fast_exp2(sfx[i]);                    // e^{rho_{I+1} - g_t} <= 1
+      fi[i] = pw ? 0.f : fast_exp2(-gl[kk][i]);     // e^{rho_I - g_t} <= 2^64 (diagonal product only)
     }
     f32x4 kf = r.k[kk].f(), bf = r.b[kk].f(), qf = r.q[kk].f();
     if constexpr (LP) {
@@ -504,22 +705,23 @@ __device__ __forceinline__ void wy_operands(wy_smem<IO, D, C> &sm, const wy_rows
     }
     const f32x4 er = bf * kf * f;
     const f32x4 qr = qf * f;
-    const f32x4 kh = kf * fi;
+    const f32x4 kt = kf * fk;
     op.ef[kk] = F::from(er);
     op.qf[kk] = F::from(qr);
-    op.khf[kk] = F::from(kh);
+    op.khf[kk] = F::from(kf * fi);
     op.qcf[kk] = F::from(qr * f1v);
-    // keys of this sub-block rescaled to the reference point of each later one
+    // keys of this sub-block referenced to the start of each later one
 #pragma unroll
     for (int I2 = 1; I2 < NB; ++I2) {
       if (I2 > I) {
         const f32x4 s = *reinterpret_cast<const f32x4 *>(&sm.sig[pair_index(I2, I)][c0]);
-        F::from(kh * s).st(&sm.khs[pair_index(I2, I)][0][0] + tile_off<IO, NK>(0, kk, lane), 0);
+        F::from(kt * s).st(&sm.khs[pair_index(I2, I)][0][0] + tile_off<IO, NK>(0, kk, lane), 0);
       }
     }
     F::from(transpose_frag(F::from(er * f1v), eye)).st(sm.ec[I][kk], lane);
-    F::from(transpose_frag(F::from(kh * f2v), eye)).st(kb_out + tile_off<IO, NB>(kk, I, lane), 0);
+    F::from(transpose_frag(F::from(kt * f2v), eye)).st(kb_out + tile_off<IO, NB>(kk, I, lane), 0);
   }
+  op.pw = pw;
 }
 
 // ColFrag(U_J) = ColFrag(w (.) v) for NVW column tiles and every sub-block.
@@ -572,7 +774,7 @@ __device__ __forceinline__ void wy_products(wy_smem<IO, D, C> &sm, const wy_ops<
           mma16(accP[J], a1, op.qf[kk]);
         }
       }
-    } else if (J == I) {
+    } else if (J == I && !op.pw) {
       if constexpr (NK % 2 == 0) {
 #pragma unroll
         for (int kp = 0; kp < NK / 2; ++kp) {
@@ -597,7 +799,7 @@ __device__ __forceinline__ void wy_products(wy_smem<IO, D, C> &sm, const wy_ops<
       }
       *reinterpret_cast<f32x4 *>(&sm.ad[I][m][4 * g]) = accA[J];
     }
-    if (J <= I)
+    if (J < I || (J == I && !op.pw))
       F::from(accP[J]).st(sm.pr[tri_index(I, J)], lane);
   }
 #pragma unroll

@@ -103,6 +103,27 @@ def make_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed
     return out
 
 
+def make_strong_decay_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                             s0: str | None = None, num_seqs: int | None = None,
+                             logit_mean: float = -2.0, logit_std: float = 2.0,
+                             tiny_frac: float = 0.01, tiny: float = 1e-4, zero_frac: float = 0.01,
+                             alpha_min: float = 0.0) -> dict:
+    """Inputs of one chunked-forward call with strong and degenerate decay:
+    as make_chunk_inputs, but alpha = sigmoid(N(logit_mean, logit_std^2))
+    per key channel, then a fraction ``tiny_frac`` of the (token, head,
+    channel) entries set to ``tiny`` and a fraction ``zero_frac`` set to 0
+    exactly (drawn after everything else, from the same generator), and
+    alpha raised to at least ``alpha_min``."""
+    out = make_chunk_inputs(B, T, H, dk, dv, dtype, seed, s0=s0, num_seqs=num_seqs)
+    rng = np.random.default_rng(seed + 104729)
+    alpha = _sigmoid(rng.normal(logit_mean, logit_std, (B, T, H, dk)))
+    u = rng.random((B, T, H, dk))
+    alpha = np.where(u < tiny_frac, tiny, alpha)
+    alpha = np.where((u >= tiny_frac) & (u < tiny_frac + zero_frac), 0.0, alpha)
+    out["alpha"] = _cast(np.maximum(alpha, alpha_min), dtype)
+    return out
+
+
 def make_bwd_grads(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
                    num_seqs: int | None = None, with_dS: bool = True) -> dict:
     """Incoming gradients of one backward call: dL/do ~ N(0, 1) [B, T, H, dv]
@@ -115,13 +136,18 @@ def make_bwd_grads(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: i
 
 
 def make_layer_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed: int,
-                      s0: str | None = None, scalar_beta: bool = False) -> dict:
+                      s0: str | None = None, scalar_beta: bool = False, strong_decay: bool = False,
+                      neg_inf_frac: float = 0.0) -> dict:
     """Raw layer inputs of one chunked-forward call in layer-prep mode: q and
     k not normalised (N(0,1) times a per-row scale in [0.5, 4]), v ~ N(0,1),
     gate logits b, w ~ N(0,1) (one shared logit per (batch, token, head) with
     ``scalar_beta``, then shaped [B, T, H]), and the natural-log decay
     log(sigmoid(N(3,1))) per key channel, always float32.  The recurrence
     inputs these stand for have the same distributions as make_chunk_inputs.
+    With ``strong_decay`` the log-decay is log(sigmoid(N(-2, 2^2))) floored
+    at -20, with 1% of the entries at -20 exactly, and a fraction
+    ``neg_inf_frac`` at -inf (alpha = 0); these are drawn after everything
+    else.
     """
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, T, H, dk)) * rng.uniform(0.5, 4.0, (B, T, H, 1))
@@ -143,6 +169,13 @@ def make_layer_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str, seed
         out["S0"] = torch.from_numpy(rng.normal(0.0, 0.1, (B, H, dk, dv))).float().contiguous()
     else:
         raise ValueError(f"unknown s0 mode {s0!r}")
+    if strong_decay:
+        r2 = np.random.default_rng(seed + 104729)
+        la = np.maximum(np.log(_sigmoid(r2.normal(-2.0, 2.0, (B, T, H, dk)))), -20.0)
+        u = r2.random((B, T, H, dk))
+        la = np.where(u < 0.01, -20.0, la)
+        la = np.where((u >= 0.01) & (u < 0.01 + neg_inf_frac), -np.inf, la)
+        out["alpha"] = _cast(la, "f32")
     return out
 
 

@@ -11,9 +11,9 @@
  *   o_t = S^T q_t                  (read after the update, no 1/sqrt(dk))
  *
  * Sources: the formal paragraph of the aixai.ru blog ("Gated DeltaNet-2",
- * section on why one scalar cannot serve both decisions: decay first, the
- * erase gate b weights the key coordinates used for the read, the write gate
- * w weights the candidate value); aiexpert.news/pt (method paragraph: b_t in
+ * section on why one scalar cannot serve both decisions: the decay is
+ * applied first, b enters the read of the state, w gates the value
+ * written); aiexpert.news/pt (method paragraph: b_t in
  * [0,1]^dk on the key axis, w_t in [0,1]^dv on the value axis, per-channel
  * decay kept from KDA, exact reduction to KDA when b and w collapse to one
  * scalar); aixai.ru, implementation section (chunkwise parallel form, q and k
@@ -41,11 +41,18 @@
  *     cu_seqlens, NaN/Inf inputs) are not detected: NaN propagates to the
  *     outputs of its sequence and head.
  *   - Supported sizes: dk == dv in {16, 32, 64, 128}; chunk in {16, 64}.
- *   - Numerical domain of the chunked path: the per-channel decay accumulated
- *     over any 16 consecutive tokens (aligned to 16 within a chunk) must stay
- *     above about 2^-120, i.e. the product of those 16 alphas; beyond that the
- *     factorised decay overflows float32.  The recurrent path has no such
- *     limit.
+ *   - Decay range: any alpha in [0, 1], alpha = 0 (a full erase of that
+ *     channel) included, on every path.  The chunked kernels build every
+ *     decay factor from sums of log decays (never the difference of two
+ *     prefix sums) and form the diagonal 16-token blocks pair by pair, from
+ *     running products of the alphas, wherever a 16-token stretch decays by
+ *     more than 2^-64 (the pages keep the log-decay in float32 because the
+ *     in-chunk cumulative sum is precision-sensitive: aixai.ru blog, section
+ *     on how the method is implemented in practice).  The backward's
+ *     gradient with respect to alpha itself is d(ln alpha) / alpha: its
+ *     error grows as 1 / alpha and alpha = 0 gives no finite value; the
+ *     log-decay input (GDN2_FLAG_LAYER_PREP) returns d(ln alpha) directly
+ *     for every decay.
  */
 #ifndef GDN2_H
 #define GDN2_H
@@ -213,9 +220,9 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * given the workspace gdn2_chunk_bwd_workspace_bytes reports, both of the
  * backward's scans take it too: the states from the segment maps and their
  * scan, the state gradients from per-segment reverse scans and the adjoint
- * scan of the maps (Phi transposed, from the last segment).  The numerical
- * domain is the chunked forward's (see the conventions above); alpha must be
- * nonzero. */
+ * scan of the maps (Phi transposed, from the last segment).  Decay range:
+ * see the conventions above (dalpha with respect to alpha itself needs
+ * alpha > 0; under layer prep every decay, -inf log included, works). */
 gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *alpha,
                              const void *b, const void *w, const float *S0,
                              const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
@@ -247,7 +254,7 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
  *               return it holds the chunks' intermediates, which
  *               gdn2_chunk_fwd with GDN2_FLAG_PREPARED reads.
  * The maps use the chunked path's arithmetic (the state rounded to dt for
- * the matrix products, as in gdn2_chunk_fwd) and its numerical domain. */
+ * the matrix products, as in gdn2_chunk_fwd) and accept any decay. */
 gdn2_status_t gdn2_chunk_segment_map(const void *q, const void *k, const void *v, const void *alpha,
                                      const void *b, const void *w, const int32_t *cu_seqlens, int B, int T,
                                      int H, int dk, int dv, int num_seqs, int chunk, gdn2_dtype_t dt,

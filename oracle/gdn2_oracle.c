@@ -13,8 +13,8 @@
  *      inherited from KDA ("Gated DeltaNet-2", aixai.ru blog, section "One
  *      scalar cannot decide two different questions", formal paragraph; the
  *      gate tables on needhelp.icu/fa and needhelp.icu/de).
- *   2. read with the erase-gated key: r = D^T (b_t (.) k_t); the erase gate
- *      weights the key coordinates used for the read (same paragraph).
+ *   2. read with the erase-gated key: r = D^T (b_t (.) k_t); in this reading
+ *      b enters the read of the state (same paragraph).
  *   3. delta value with the write-gated candidate: z = w_t (.) v_t - r; the
  *      write gate sits on the value side (aiexpert.news/pt, method paragraph:
  *      b_t in [0,1]^dk on the key axis, w_t in [0,1]^dv on the value axis).

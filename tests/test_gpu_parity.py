@@ -539,3 +539,36 @@ def test_rule_r1_rejected_on_chunked_paths(g):
         with pytest.raises(g.Gdn2Error) as e:
             g.chunk_fwd(*(inp[n] for n in NAMES), path=path, rule="R1")
         assert e.value.status == 2
+
+
+def test_binding_rejects_wrong_tensors(g):
+    """The binding checks every tensor's shape, dtype, device and layout
+    before it calls the library (no launch happens for these)."""
+    inp = to_dev(gi.make_chunk_inputs(2, 64, 2, 32, 32, "bf16", seed=90))
+    args = [inp[n] for n in NAMES]
+    bad = [
+        dict(k=inp["k"][:, :32].contiguous()),                       # k shorter than q
+        dict(v=inp["v"].float()),                                    # dtype
+        dict(k=inp["k"].cpu()),                                      # device
+        dict(v=inp["v"].transpose(0, 1)),                            # not contiguous
+    ]
+    for over in bad:
+        a = [over.get(n, inp[n]) for n in NAMES]
+        with pytest.raises((ValueError, TypeError)):
+            g.chunk_fwd(*a, chunk=16)
+    for kw in (dict(out=torch.empty((2, 64, 2, 16), dtype=torch.bfloat16, device="cuda")),
+               dict(out=torch.empty((2, 64, 2, 32), dtype=torch.float32, device="cuda")),
+               dict(S_final=torch.empty((2, 2, 32, 32), dtype=torch.bfloat16, device="cuda")),
+               dict(S_final=torch.empty((3, 2, 32, 32), dtype=torch.float32, device="cuda")),
+               dict(workspace=torch.empty(64, dtype=torch.uint8))):
+        with pytest.raises((ValueError, TypeError)):
+            g.chunk_fwd(*args, chunk=16, **kw)
+    d = gi.make_decode_inputs(4, 2, 32, 32, "bf16", seed=91, steps=1)
+    dd = {n: d[n][0].cuda() for n in NAMES}
+    S = d["S"].cuda()
+    for name, t in (("k", dd["k"][:3].contiguous()), ("w", dd["w"].float()), ("alpha", dd["alpha"][..., :16].contiguous())):
+        a = [t if n == name else dd[n] for n in NAMES]
+        with pytest.raises((ValueError, TypeError)):
+            g.decode_step(*a, S)
+    with pytest.raises((ValueError, TypeError)):
+        g.decode_step(*(dd[n] for n in NAMES), S, out=torch.empty((4, 2, 16), dtype=torch.bfloat16, device="cuda"))
