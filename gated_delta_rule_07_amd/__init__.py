@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
         L.gdn2_chunk_fwd.restype = i
         L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
+        L.gdn2_chunk_fwd_noalloc.restype = i
+        L.gdn2_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp]
         L.gdn2_chunk_bwd_workspace_bytes.restype = sz
         L.gdn2_chunk_bwd_workspace_bytes.argtypes = [i] * 7 + [i]
         L.gdn2_chunk_bwd.restype = i

@@ -550,6 +550,44 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   return dispatch_chunk(dt, d, chunk, s, GDN2_FLAG_TWO_PASS | GDN2_FLAG_PREPARED, st);
 }
 
+// ------------------------------------------------------- no-alloc scratch --
+// Device scratch of the allocation-free forward (gdn2_chunk_fwd_noalloc):
+// one copy per GPU, reserved with the library's code object and held until
+// the process ends.  In host code `scratch` is a host-side stand-in, not a
+// device address: its address on a device comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[GDN2_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (nullptr and a HIP error
+// on failure).
+void *device_scratch(hipError_t *err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess)
+    return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !ptr) {
+      if (*err == hipSuccess)
+        *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -964,6 +1002,100 @@ gdn2_status_t gdn2_decode_step(const void *q, const void *k, const void *v, cons
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_decode_step: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gdn2_status_t gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *alpha,
+                                     const void *b, const void *w, const float *S0,
+                                     const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                                     int num_seqs, int chunk, gdn2_dtype_t dt, uint32_t flags, void *o,
+                                     float *S_final, void *stream) {
+  const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
+  if (flags & ~(gate_flags | GDN2_FLAG_TWO_PASS))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd_noalloc: flags 0x%x: only the gate layout and layer prep flags apply "
+                "(it runs the two-pass kernels)", flags);
+  if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd_noalloc: unknown dtype %d", static_cast<int>(dt));
+  if (B <= 0 || T < 0 || H <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd_noalloc: bad sizes B=%d T=%d H=%d", B, T, H);
+  if (dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd_noalloc: unsupported dk=%d dv=%d chunk=%d (need dk == dv in {16,32,64,128}, "
+                "chunk 16 or 64)", dk, dv, chunk);
+  if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !o))
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd_noalloc: null input or output pointer");
+  flags |= GDN2_FLAG_TWO_PASS;
+  const size_t cap = GDN2_NOALLOC_SCRATCH_BYTES;
+  const bool packed = cu_seqlens != nullptr;
+  if (packed && num_seqs <= 0)
+    return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd_noalloc: packed input needs num_seqs > 0");
+  // the plain two-pass workspace of the whole call, as gdn2_chunk_fwd checks it
+  const size_t whole_plain = (packed ? align256(static_cast<size_t>(num_seqs + 1) * sizeof(int32_t)) : 0) +
+                             static_cast<size_t>(num_slots_for(B, T, packed ? num_seqs : B, chunk, packed)) * H *
+                                 chunk_block_bytes_rt(dt, dk, chunk);
+  if (packed && whole_plain > cap)
+    return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                "gdn2_chunk_fwd_noalloc: packed input needs %zu bytes of scratch, more than the %zu the "
+                "library holds; split the call", whole_plain, cap);
+  hipError_t herr = hipSuccess;
+  if (whole_plain <= cap) {
+    char *ws = static_cast<char *>(device_scratch(&herr));
+    if (!ws)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd_noalloc: scratch address: %s", hipGetErrorString(herr));
+    return gdn2_chunk_fwd(q, k, v, alpha, b, w, S0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk, dt, flags, o,
+                          S_final, ws, cap, stream);
+  }
+  // Fixed-length input too large for the scratch in one call: every
+  // sequence in pieces of whole chunks, run in order, each from the state
+  // the previous piece left (in S_final, or in the scratch's first bytes).
+  // Pieces of whole chunks reproduce the single call's results exactly.
+  if (num_seqs != 0 && num_seqs != B)
+    return fail(GDN2_ERR_INVALID_ARGUMENT,
+                "gdn2_chunk_fwd_noalloc: num_seqs=%d must be 0 or B=%d without cu_seqlens", num_seqs, B);
+  const size_t carry = S_final ? 0 : align256(static_cast<size_t>(H) * dk * dv * sizeof(float));
+  const size_t per_chunk = static_cast<size_t>(H) * chunk_block_bytes_rt(dt, dk, chunk);
+  const long max_chunks = cap > carry ? static_cast<long>((cap - carry) / per_chunk) : 0;
+  if (max_chunks < 1)
+    return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                "gdn2_chunk_fwd_noalloc: one chunk of %d heads needs %zu bytes of scratch, more than the %zu "
+                "the library holds", H, per_chunk + carry, cap);
+  const int Tp = static_cast<int>(max_chunks > T / chunk + 1 ? T / chunk + 1 : max_chunks) * chunk;
+  const size_t el = dt == GDN2_BF16 ? 2 : 4;
+  // bytes per token of each tensor: [.., H, width] rows of its element type
+  const size_t row_q = static_cast<size_t>(H) * dk * el, row_v = static_cast<size_t>(H) * dv * el;
+  const size_t row_a = static_cast<size_t>(H) * ((flags & GDN2_FLAG_SCALAR_ALPHA) ? 1 : dk) *
+                       ((flags & GDN2_FLAG_LAYER_PREP) ? 4 : el);
+  const size_t row_b = static_cast<size_t>(H) * ((flags & GDN2_FLAG_SCALAR_B) ? 1 : dk) * el;
+  const size_t row_w = static_cast<size_t>(H) * ((flags & GDN2_FLAG_SCALAR_W) ? 1 : dv) * el;
+  const size_t st = static_cast<size_t>(H) * dk * dv;  // floats per sequence state
+  char *ws = static_cast<char *>(device_scratch(&herr));
+  if (!ws)
+    return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd_noalloc: scratch address: %s", hipGetErrorString(herr));
+  float *carry_p = reinterpret_cast<float *>(ws);
+  for (int n = 0; n < B; ++n) {
+    for (int t0 = 0; t0 < T; t0 += Tp) {
+      const int len = T - t0 < Tp ? T - t0 : Tp;
+      const size_t tok = static_cast<size_t>(n) * T + t0;
+      auto at = [&](const void *p, size_t row) {
+        return p ? static_cast<const void *>(static_cast<const char *>(p) + tok * row) : nullptr;
+      };
+      const void *pa = at(alpha, row_a), *pb = at(b, row_b), *pw = at(w, row_w);
+      for (const void *p : {pa, pb, pw})
+        if (p && !aligned16(p))
+          return fail(GDN2_ERR_UNSUPPORTED,
+                      "gdn2_chunk_fwd_noalloc: the call needs %zu bytes of scratch (more than %zu) and its "
+                      "pieces of %d tokens would leave a per-(token, head) gate 16-byte misaligned",
+                      whole_plain, cap, Tp);
+      const float *s_in = t0 == 0 ? (S0 ? S0 + n * st : nullptr) : (S_final ? S_final + n * st : carry_p);
+      float *s_out = S_final ? S_final + n * st : (t0 + len < T ? carry_p : nullptr);
+      const gdn2_status_t r = gdn2_chunk_fwd(
+          at(q, row_q), at(k, row_q), at(v, row_v), pa, pb, pw, s_in, nullptr, 1, len, H, dk, dv, 0, chunk, dt,
+          flags, static_cast<char *>(o) + tok * row_v, s_out, ws + carry, cap - carry, stream);
+      if (r != GDN2_OK)
+        return r;
+    }
+  }
   return ok();
 }
 

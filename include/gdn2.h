@@ -182,6 +182,37 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
                              float *S_final, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gdn2_chunk_fwd on the two-pass kernels without a workspace
+ * argument.  The per-chunk intermediates go to a scratch array the library
+ * holds in device memory, GDN2_NOALLOC_SCRATCH_BYTES on every GPU it runs
+ * on, kept until the process ends; no memory is allocated per call.
+ *   Arguments: as gdn2_chunk_fwd, minus the workspace.  flags: the gate
+ *   layout and layer prep flags (GDN2_FLAG_TWO_PASS is accepted and
+ *   implied); the path, rule and prepared-workspace flags return
+ *   GDN2_ERR_UNSUPPORTED.
+ *   Sizes: a call whose two-pass workspace (gdn2_chunk_fwd_workspace_bytes
+ *   without the segment schedule) fits the scratch runs as one
+ *   gdn2_chunk_fwd call.  A larger fixed-length call (cu_seqlens == NULL)
+ *   runs every sequence in pieces of whole chunks, in order, each piece
+ *   starting from the state the previous one left (kept in S_final, or in
+ *   the scratch when S_final is NULL); the results equal gdn2_chunk_fwd's
+ *   on the two-pass path exactly.  Larger packed input, one chunk of H heads
+ *   that does not fit, or pieces that would misalign a per-(token, head)
+ *   gate tensor return GDN2_ERR_WORKSPACE_TOO_SMALL or GDN2_ERR_UNSUPPORTED
+ *   before any launch.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (several host threads, or several streams without
+ *   ordering between them) race and give undefined outputs.  Nothing in the
+ *   scratch needs to start at zero. */
+#define GDN2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn2_status_t gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *alpha,
+                                     const void *b, const void *w, const float *S0,
+                                     const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                                     int num_seqs, int chunk, gdn2_dtype_t dt, uint32_t flags, void *o,
+                                     float *S_final, void *stream);
+
 /* Bytes of device workspace gdn2_chunk_bwd needs for these sizes (0 when
  * the sizes are unsupported); num_seqs as for gdn2_chunk_fwd_workspace_bytes.
  * For a few long sequences the figure includes the segment schedule's maps

@@ -221,3 +221,25 @@ def test_segment_combine_rejects_before_launch(L):
     assert L.gdn2_segment_combine(p, p, 0x10008, 2, 1, 16, 16, p, None, None) == 1
     # nothing to do: no segment and no final state asked for
     assert L.gdn2_segment_combine(None, None, None, 0, 1, 16, 16, None, None, None) == 0
+
+
+def call_noalloc(L, *, ptr=FAKE, B=1, T=64, H=1, dk=16, dv=16, N=0, chunk=16, dt=F32, flags=0, cu=None):
+    p = ptr
+    return L.gdn2_chunk_fwd_noalloc(p, p, p, p, p, p, None, cu, B, T, H, dk, dv, N, chunk, dt, flags, p, None, None)
+
+
+def test_noalloc_rejects_before_launch(L):
+    """The allocation-free forward checks its arguments before it touches the
+    device: path, rule and prepared-workspace flags, sizes, null pointers,
+    and packed input larger than its scratch."""
+    for flag in (1 << 1, 1 << 3, 1 << 7, 1 << 8, 1 << 9):
+        assert call_noalloc(L, flags=flag) == 2
+    assert call_noalloc(L, dk=24, dv=24) == 2
+    assert call_noalloc(L, chunk=32) == 2
+    assert call_noalloc(L, dt=7) == 2
+    assert call_noalloc(L, B=0) == 1
+    assert call_noalloc(L, ptr=0) == 1
+    assert call_noalloc(L, cu=FAKE, N=0) == 1
+    # 1 x 65536 packed tokens x 16 heads, d = 128: far more than the scratch
+    assert call_noalloc(L, cu=FAKE, N=4, T=65536, H=16, dk=128, dv=128, chunk=64, dt=BF16) == 3
+    assert b"scratch" in L.gdn2_last_error()
