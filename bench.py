@@ -18,6 +18,7 @@ In the same run (reported next to the headline, not in `value`):
     the 256 MB last-level cache);
   * the same layer as KDA (b = w = beta per token and head) and as Gated
     DeltaNet (also a per-(token, head) decay), and GDN-2's time over KDA's;
+  * the same layer under the alternative reading R1 (chunked two-pass path);
   * the chunked backward (gdn2_chunk_bwd) on the same layer: its time per
     step, per-kernel durations and the roofline of its dominant kernel;
   * a context-parallel split of one 32768-token sequence into 8 segments:
@@ -497,6 +498,23 @@ def main() -> int:
             "r1_over_r5_time": round(rsec["R1"] / rsec["R5"], 4),
         }
         del rin, orr
+
+        # rule R1 on the chunked two-pass path, the same layer
+        ws_r1 = torch.empty(g.workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16, g.FLAG_RULE_R1),
+                            dtype=torch.uint8, device="cuda")
+        g.profile_enable(True)
+        g.profile_read(reset=True)
+        sec_r1 = timed_steps(lambda: g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o, S_final=Sf,
+                                                 workspace=ws_r1, rule="R1"), 20, 5)
+        r1prof = g.profile_read(reset=True)
+        g.profile_enable(False)
+        out["rule_r1_chunked"] = {
+            "workload": "the same layer (8 x 4096 x 16 heads, d=128, bf16), rule R1, two-pass kernels",
+            "tokens_per_s": round(B * T / sec_r1, 1), "ms": round(sec_r1 * 1e3, 4),
+            "r1_over_r5_time": round(sec_r1 / sec, 4),
+            "kernels": {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in r1prof.items()},
+        }
+        del ws_r1
 
         lens = gi.packed_lengths(3)
         cu = gi.cu_seqlens_from(lens).cuda()

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         vp, i, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
         L.gdn2_chunk_fwd_workspace_bytes.restype = sz
         L.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
+        L.gdn2_chunk_fwd_workspace_bytes_flags.restype = sz
+        L.gdn2_chunk_fwd_workspace_bytes_flags.argtypes = [i] * 7 + [i, u32]
         L.gdn2_chunk_fwd.restype = i
         L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
         L.gdn2_chunk_fwd_noalloc.restype = i
@@ -155,9 +157,9 @@ def _gate_flags(q, v, alpha, b, w) -> int:
 
 
 def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chunk: int,
-                    dtype: torch.dtype) -> int:
+                    dtype: torch.dtype, flags: int = 0) -> int:
     code = GDN2_BF16 if dtype == torch.bfloat16 else GDN2_F32
-    return int(lib().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, chunk, code))
+    return int(lib().gdn2_chunk_fwd_workspace_bytes_flags(B, T, H, dk, dv, num_seqs, chunk, code, flags))
 
 
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
@@ -167,7 +169,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
     """Chunked forward.  ``path`` selects the kernels: "auto" (the library
     chooses), "fused" (single pass), "two_pass", or "recurrent" (token by
     token; also selected by ``recurrent=True``).  ``rule="R1"`` runs the
-    alternative reading R1 (token-by-token path only).  ``prepared=True``
+    alternative reading R1 (two-pass or token-by-token path).  ``prepared=True``
     runs the state scan alone on a ``workspace`` that ``segment_map`` (or a
     two-pass ``chunk_fwd``) filled for the same inputs.  Returns (o,
     S_final); S_final is None when ``want_final`` is False."""
@@ -209,7 +211,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
              | (FLAG_PREPARED if prepared else 0))
     ws_bytes = 0
     if path != "recurrent":
-        ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype)
+        ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype, flags)
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
             ws_bytes = workspace.numel()

@@ -101,6 +101,59 @@ size_t chunk_block_bytes_rt(gdn2_dtype_t dt, int d, int c) {
   return 0;
 }
 
+size_t r1_block_bytes_rt(gdn2_dtype_t dt, int d, int c) {
+#define GDN2_RB1(IO, D, C) \
+  if (d == D && c == C)    \
+    return gdn2::r1_block_bytes<IO, D, C>();
+  if (dt == GDN2_F32) {
+    GDN2_RB1(float, 16, 16) GDN2_RB1(float, 32, 16) GDN2_RB1(float, 64, 16) GDN2_RB1(float, 128, 16)
+    GDN2_RB1(float, 16, 64) GDN2_RB1(float, 32, 64) GDN2_RB1(float, 64, 64)
+  } else {
+    GDN2_RB1(gdn2::bf16_t, 16, 16) GDN2_RB1(gdn2::bf16_t, 32, 16) GDN2_RB1(gdn2::bf16_t, 64, 16)
+    GDN2_RB1(gdn2::bf16_t, 128, 16) GDN2_RB1(gdn2::bf16_t, 16, 64) GDN2_RB1(gdn2::bf16_t, 32, 64)
+    GDN2_RB1(gdn2::bf16_t, 64, 64) GDN2_RB1(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_RB1
+  return 0;  // float32 with d = 128 and chunk 64: not built (its LDS does not fit)
+}
+
+// Rule R1 on the two-pass path: chunk table (packed input), its per-chunk
+// kernel, its state scan.
+template <typename IO, int D, int C>
+hipError_t run_chunk_r1(const gdn2::chunk_args &a, int C_rt, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (a.cu) {
+    prof_scope p("chunk_table", st);
+    e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  {
+    prof_scope p("r1_prep", st);
+    e = gdn2::launch_r1_prep<IO, D, C>(a, st);
+    if (e != hipSuccess)
+      return e;
+  }
+  prof_scope p("r1_scan", st);
+  return gdn2::launch_r1_scan<IO, D, C>(a, st);
+}
+
+hipError_t dispatch_chunk_r1(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, hipStream_t st) {
+#define GDN2_RR1(IO, D, C) \
+  if (d == D && c == C)    \
+    return run_chunk_r1<IO, D, C>(a, C, st);
+  if (dt == GDN2_F32) {
+    GDN2_RR1(float, 16, 16) GDN2_RR1(float, 32, 16) GDN2_RR1(float, 64, 16) GDN2_RR1(float, 128, 16)
+    GDN2_RR1(float, 16, 64) GDN2_RR1(float, 32, 64) GDN2_RR1(float, 64, 64)
+  } else {
+    GDN2_RR1(gdn2::bf16_t, 16, 16) GDN2_RR1(gdn2::bf16_t, 32, 16) GDN2_RR1(gdn2::bf16_t, 64, 16)
+    GDN2_RR1(gdn2::bf16_t, 128, 16) GDN2_RR1(gdn2::bf16_t, 16, 64) GDN2_RR1(gdn2::bf16_t, 32, 64)
+    GDN2_RR1(gdn2::bf16_t, 64, 64) GDN2_RR1(gdn2::bf16_t, 128, 64)
+  }
+#undef GDN2_RR1
+  return hipErrorInvalidValue;
+}
+
 // Path choice for the chunked forward.  0 = two-pass, otherwise the column
 // group count NG of the single-pass kernel.
 template <typename IO, int D, int C> int choose_fused(long units, uint32_t flags) {
@@ -614,6 +667,25 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   return plain;
 }
 
+size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
+                                            gdn2_dtype_t dt, uint32_t flags) {
+  if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT)) {
+    if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
+      return 0;
+    if (dt != GDN2_F32 && dt != GDN2_BF16)
+      return 0;
+    const size_t blk = r1_block_bytes_rt(dt, dk, chunk);
+    if (blk == 0)
+      return 0;
+    const int n = num_seqs > 0 ? num_seqs : B;
+    const size_t slots_fixed = static_cast<size_t>(num_slots_for(B, T, B, chunk, false));
+    const size_t slots_packed = static_cast<size_t>(num_slots_for(B, T, n, chunk, true));
+    const size_t slots = slots_packed > slots_fixed ? slots_packed : slots_fixed;
+    return align256(static_cast<size_t>(n + 1) * sizeof(int32_t)) + slots * static_cast<size_t>(H) * blk;
+  }
+  return gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, chunk, dt);
+}
+
 gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
                              const void *b, const void *w, const float *S0,
                              const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
@@ -631,8 +703,11 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
       return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: a prepared workspace is read by the two-pass path only");
     flags |= GDN2_FLAG_TWO_PASS;
   }
-  if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT))
-    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: rule R1 runs on the token-by-token path only");
+  const bool r1_chunked = (flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT);
+  if (r1_chunked && (flags & (GDN2_FLAG_FUSED | GDN2_FLAG_PREPARED)))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd: rule R1 runs on the two-pass and token-by-token paths (no single-pass kernel, "
+                "no prepared workspace)");
   {
     const uint32_t paths = flags & path_flags;
     if (paths & (paths - 1))
@@ -682,10 +757,13 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     return ok();
   }
 
+  const size_t blk_bytes = r1_chunked ? r1_block_bytes_rt(dt, dk, chunk) : chunk_block_bytes_rt(dt, dk, chunk);
+  if (blk_bytes == 0)
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd: rule R1 on the chunked path needs bfloat16 or chunk 16 with dk = 128");
   const size_t need_exact = [&] {
     const size_t table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
-    return table + static_cast<size_t>(num_slots_for(B, T, N, chunk, packed)) * H *
-                       chunk_block_bytes_rt(dt, dk, chunk);
+    return table + static_cast<size_t>(num_slots_for(B, T, N, chunk, packed)) * H * blk_bytes;
   }();
   if (workspace_bytes < need_exact || (need_exact > 0 && !workspace))
     return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
@@ -708,7 +786,7 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   a.num_slots = num_slots_for(B, T, N, chunk, packed);
   a.o = o;
   a.S_final = S_final;
-  a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
+  a.blk_bytes = blk_bytes;
   a.gates = ((flags & GDN2_FLAG_SCALAR_B) ? gdn2::GATE_SCALAR_B : 0u) |
             ((flags & GDN2_FLAG_SCALAR_W) ? gdn2::GATE_SCALAR_W : 0u) |
             ((flags & GDN2_FLAG_SCALAR_ALPHA) ? gdn2::GATE_SCALAR_ALPHA : 0u) |
@@ -728,6 +806,12 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   if ((flags & GDN2_FLAG_FUSED) && !fused_available(dt, dk, chunk))
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: no single-pass kernel for dtype %d, dk=%d, chunk=%d",
                 static_cast<int>(dt), dk, chunk);
+  if (r1_chunked) {
+    const hipError_t e = dispatch_chunk_r1(dt, dk, chunk, a, st);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   const seg_shape sx = seg_shape_of(B, T, N, chunk, packed);
   if ((flags & (path_flags | GDN2_FLAG_PREPARED)) == 0 && use_segments(sx, H) &&
       workspace_bytes >= plan_segments(dt, sx, H, dk, chunk).total) {

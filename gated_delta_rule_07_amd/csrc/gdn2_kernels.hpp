@@ -56,6 +56,12 @@ struct bwd_args {
   unsigned char *pwflag;  // [num_slots * H]: chunk-heads whose gradients need the pairwise diagonal path
 };
 
+// Rule R1 on the two-pass path: its own per-chunk kernel and state scan, on
+// blocks of r1_block_bytes (not instantiated for float32, D = 128, C = 64).
+template <typename IO, int D, int C> size_t r1_block_bytes();
+template <typename IO, int D, int C> hipError_t launch_r1_prep(const chunk_args &a, hipStream_t st);
+template <typename IO, int D, int C> hipError_t launch_r1_scan(const chunk_args &a, hipStream_t st);
+
 template <typename IO, int D, int C> hipError_t launch_bwd_dstate(const bwd_args &a, hipStream_t st);
 template <typename IO, int D, int C> hipError_t launch_bwd_grad(const bwd_args &a, hipStream_t st);
 

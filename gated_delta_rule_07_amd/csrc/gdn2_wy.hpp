@@ -491,8 +491,10 @@ __device__ __forceinline__ f32x4 wy_log_decay4(const chunk_args &a, long t0, int
 }
 
 // The diagonal A and P blocks of sub-block I, pair by pair:
-//   A[t][s] = sum_c e_tc k_sc prod_{u=s+1..t} alpha_uc  (s < t),
-//   P[t][s] = sum_c q_tc k_sc prod_{u=s+1..t} alpha_uc  (s <= t),
+//   A[t][s] = sum_c x_tc y_sc prod_{u=s+1..t} alpha_uc  (s < t),
+//   P[t][s] = sum_c q_tc y_sc prod_{u=s+1..t} alpha_uc  (s <= t),
+// with (x, y) = (e, k) for the default rule (SEL 0), (k, e) for the rule-R1
+// erase products (SEL 1) and (k, k) for its write products (SEL 2),
 // with the decay a running product of the alphas, so that any decay (alpha
 // = 0 included) is exact to rounding.  The inputs are read again from
 // global memory, one tile of 16 channels at a time; lane (t, g) walks the
@@ -501,7 +503,7 @@ __device__ __forceinline__ f32x4 wy_log_decay4(const chunk_args &a, long t0, int
 // layout of the matrix-core product (lane (t, g) holds columns
 // s = 4g .. 4g+3 of row t), zero outside the triangles.  A slow path: the
 // loops are kept rolled so that it adds few registers to its kernel.
-template <typename IO, int D>
+template <typename IO, int D, int SEL = 0>
 __device__ __forceinline__ void wy_diag_pairwise(const chunk_args &a, long t0, int len, int h, int I, int lane,
                                                  float qs, float ks, f32x4 &dA, f32x4 &dP) {
   constexpr int NK = D / 16;
@@ -513,6 +515,7 @@ __device__ __forceinline__ void wy_diag_pairwise(const chunk_args &a, long t0, i
   for (int kk = 0; kk < NK; ++kk) {
     f32x4 q4, k4, e4, a4;
     wy_row4<IO, D>(a, row, valid, 16 * kk + 4 * g, qs, ks, q4, k4, e4, a4);
+    const f32x4 x4 = SEL == 0 ? e4 : k4, y4 = SEL == 1 ? e4 : k4;
     f32x4 F = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll 1
     for (int J = 0; J < 16; ++J) {
@@ -524,9 +527,9 @@ __device__ __forceinline__ void wy_diag_pairwise(const chunk_args &a, long t0, i
       for (int i = 0; i < 4; ++i) {
         if (J > 0)
           F[i] *= __shfl(a4[i], srca, 64);
-        kf[i] = __shfl(k4[i], src, 64) * F[i];
+        kf[i] = __shfl(y4[i], src, 64) * F[i];
       }
-      float xa = m >= J ? dot4(e4, kf) : 0.f;
+      float xa = m >= J ? dot4(x4, kf) : 0.f;
       float xp = m >= J ? dot4(q4, kf) : 0.f;
       xa += __shfl_xor(xa, 16, 64);
       xp += __shfl_xor(xp, 16, 64);
@@ -577,7 +580,7 @@ __device__ __forceinline__ void wy_row_scales(const wy_rows<IO, D, true> &r, flo
 // (wy_diag_pairwise, on the inputs of the chunk at t0, len, head h, read
 // again from a), which writes them to LDS where wy_products would.  gam_out[c] = gamma_C (may be LDS or
 // global memory).  Contains two workgroup barriers.
-template <typename IO, int D, int C, bool LP = false>
+template <typename IO, int D, int C, bool LP = false, int SEL = 0>
 __device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO, D, LP> &r, f32x4 (&gl)[D / 16],
                                          bool &pw, const chunk_args &a, long t0, int len, int h, int I, int tid,
                                          float *gam_out) {
@@ -609,7 +612,7 @@ __device__ __forceinline__ void wy_decay(wy_smem<IO, D, C> &sm, const wy_rows<IO
     if constexpr (LP)
       wy_row_scales<IO, D>(r, qs, ks);
     f32x4 da, dp;
-    wy_diag_pairwise<IO, D>(a, t0, len, h, I, lane, qs, ks, da, dp);
+    wy_diag_pairwise<IO, D, SEL>(a, t0, len, h, I, lane, qs, ks, da, dp);
     *reinterpret_cast<f32x4 *>(&sm.ad[I][m][4 * g]) = da;
     frag<IO>::from(dp).st(sm.pr[tri_index(I, I)], lane);
   }

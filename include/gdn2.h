@@ -107,14 +107,20 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
  * GDN2_FLAG_SCALAR_ALPHA).  The kernels L2-normalise q and k per (token,
  * head) in float32 (a zero row stays zero). */
 #define GDN2_FLAG_LAYER_PREP (1u << 0)
-/* Rule R1 (token-by-token path only: with GDN2_FLAG_RECURRENT, else
- * GDN2_ERR_UNSUPPORTED).  The alternative reading of the pages' formal
- * paragraph (aixai.ru blog, gate section) in which the erase gate places the
- * erased direction instead of weighting the read:
+/* Rule R1.  The alternative reading of the pages' formal paragraph
+ * (aixai.ru blog, gate section) in which the erase gate places the erased
+ * direction instead of weighting the read:
  *   D = Diag(alpha) S;  r = D^T k;  S = D - (b (.) k) r^T + k (w (.) v)^T;
  *   o = S^T q.
  * It reduces to KDA, Gated DeltaNet and DeltaNet as the default rule does;
- * the pages do not settle which of the two they mean. */
+ * the pages do not settle which of the two they mean.  It runs on the
+ * token-by-token path (with GDN2_FLAG_RECURRENT) and on the chunked two-pass
+ * path (the default path or GDN2_FLAG_TWO_PASS; never the segment schedule),
+ * with any gate layout and layer prep; with GDN2_FLAG_FUSED or
+ * GDN2_FLAG_PREPARED it returns GDN2_ERR_UNSUPPORTED, and so it does for
+ * float32 with dk = 128 and chunk 64.  Its chunked path needs the workspace
+ * gdn2_chunk_fwd_workspace_bytes_flags reports for this flag (larger
+ * per-chunk blocks). */
 #define GDN2_FLAG_RULE_R1 (1u << 7)
 /* Prepared workspace (two-pass path only; GDN2_ERR_UNSUPPORTED with
  * GDN2_FLAG_RECURRENT or GDN2_FLAG_FUSED).  For the caller that has just run
@@ -135,6 +141,12 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
  * gdn2_chunk_fwd, flags). */
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk, gdn2_dtype_t dt);
+
+/* The same for a given set of gdn2_chunk_fwd flags: with GDN2_FLAG_RULE_R1
+ * on the chunked path the per-chunk blocks are larger; for every other set
+ * of flags it equals gdn2_chunk_fwd_workspace_bytes. */
+size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv, int num_seqs,
+                                            int chunk, gdn2_dtype_t dt, uint32_t flags);
 
 /* Chunkwise-parallel forward over whole sequences (aixai.ru blog, section on
  * how it is implemented in practice: chunks with matrix products inside,

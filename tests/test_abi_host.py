@@ -61,7 +61,10 @@ def test_fwd_rejects_before_launch(L):
     assert call_fwd(L, flags=(1 << 8) | (1 << 1)) == 2         # prepared workspace on the token-by-token path
     assert call_fwd(L, flags=(1 << 8) | (1 << 3)) == 2         # prepared workspace on the single-pass path
     assert call_fwd(L, flags=1 << 8, ws_bytes=100) == 3        # a prepared workspace is still size-checked
-    assert call_fwd(L, flags=1 << 7) == 2          # rule R1 needs the token-by-token path
+    assert call_fwd(L, flags=(1 << 7) | (1 << 3)) == 2         # rule R1 has no single-pass kernel
+    assert call_fwd(L, flags=(1 << 7) | (1 << 8)) == 2         # nor a prepared workspace
+    assert call_fwd(L, flags=1 << 7, dk=128, dv=128, chunk=64) == 2   # float32, d = 128, chunk 64: not built
+    assert call_fwd(L, flags=1 << 7, ws_bytes=100) == 3        # its larger blocks are size-checked
     assert call_fwd(L, flags=(1 << 2) | (1 << 3)) == 1         # two paths at once
     assert call_fwd(L, flags=(1 << 1) | (1 << 4)) == 2         # token-by-token path with a per-(token, head) gate
     assert call_fwd(L, flags=(1 << 1) | (1 << 6)) == 2
@@ -243,3 +246,16 @@ def test_noalloc_rejects_before_launch(L):
     # 1 x 65536 packed tokens x 16 heads, d = 128: far more than the scratch
     assert call_noalloc(L, cu=FAKE, N=4, T=65536, H=16, dk=128, dv=128, chunk=64, dt=BF16) == 3
     assert b"scratch" in L.gdn2_last_error()
+
+
+def test_workspace_bytes_rule_r1(L):
+    f = L.gdn2_chunk_fwd_workspace_bytes
+    fl = L.gdn2_chunk_fwd_workspace_bytes_flags
+    L.gdn2_chunk_fwd_workspace_bytes_flags.argtypes = [ctypes.c_int] * 8 + [ctypes.c_uint32]
+    L.gdn2_chunk_fwd_workspace_bytes_flags.restype = ctypes.c_size_t
+    assert fl(8, 4096, 16, 128, 128, 0, 64, BF16, 0) == f(8, 4096, 16, 128, 128, 0, 64, BF16)
+    # rule R1: per chunk-head the default block plus N (dk x dv, bf16): 32 KiB more
+    r1 = fl(8, 4096, 16, 128, 128, 0, 64, BF16, 1 << 7)
+    assert r1 >= f(8, 4096, 16, 128, 128, 0, 64, BF16) + 8 * 64 * 16 * 32 * 1024 - 4096
+    assert fl(1, 100, 2, 128, 128, 0, 64, F32, 1 << 7) == 0      # not built
+    assert fl(1, 100, 2, 128, 128, 0, 16, F32, 1 << 7) > 0

@@ -213,3 +213,48 @@ def test_chunk_backward_equals_oracle_backward(C):
         for name in got:
             assert rel(got[name], ref[name][0, :, hh]) < 1e-10, name
         assert rel(dS0, ref["dS0"][0, hh]) < 1e-10
+
+
+def chunk_forward_r1(q, k, v, al, b, w, S, C):
+    """Chunk form of reading R1 (erase along b (.) k, read with k) for one
+    sequence and head.  With R = [r_t] the reads D_t^T k_t of the chunk:
+      (I + A') R = Kchk S0 + B' U,  A' = strict_lower(Kchk Ehat^T),
+      B' = strict_lower(Kchk Khat^T),  R = W' S0 + Ut',  W' = T' Kchk,
+      Ut' = T' B' U,  T' = (I + A')^-1,
+      O = (Qchk - P_e W') S0 + (P_k U - P_e Ut'),  P_e = lower(Qchk Ehat^T),
+      P_k = lower(Qchk Khat^T),
+      S_C = Diag(gamma_C) S0 + Kbar^T U - Ebar^T R
+    (Kchk = k e^g, Ehat = e e^-g, Khat = k e^-g, Qchk = q e^g, Kbar =
+    k e^{g_C - g}, Ebar = e e^{g_C - g})."""
+    T = q.shape[0]
+    o = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, C):
+        sl = slice(c0, min(c0 + C, T))
+        qc, kc, vc, ac, bc, wc = q[sl], k[sl], v[sl], al[sl], b[sl], w[sl]
+        n = qc.shape[0]
+        g = np.cumsum(np.log(ac), axis=0)
+        gam, gC = np.exp(g), np.exp(g[-1])
+        e = bc * kc
+        U = wc * vc
+        Kc, Eh, Kh, Qc = kc * gam, e / gam, kc / gam, qc * gam
+        Ap = (Kc @ Eh.T) * np.tri(n, k=-1)
+        Bp = (Kc @ Kh.T) * np.tri(n, k=-1)
+        Pe = (Qc @ Eh.T) * np.tri(n)
+        Pk = (Qc @ Kh.T) * np.tri(n)
+        Tp = np.linalg.inv(np.eye(n) + Ap)
+        Wp = Tp @ Kc
+        Utp = Tp @ (Bp @ U)
+        o[sl] = (Qc - Pe @ Wp) @ S + (Pk @ U - Pe @ Utp)
+        R = Wp @ S + Utp
+        S = gC[:, None] * S + (kc * gC / gam).T @ U - (e * gC / gam).T @ R
+    return o, S
+
+
+@pytest.mark.parametrize("C", [8, 16, 64])
+def test_r1_chunk_form_equals_token_recurrence(C):
+    inp = gi.make_chunk_inputs(1, 150, 2, 16, 16, "f32", seed=11, s0="normal")
+    x = f64(inp)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], rule="R1")
+    for hh in range(2):
+        o, S = chunk_forward_r1(*(x[n][0, :, hh] for n in NAMES), inp["S0"][0, hh].double().numpy(), C)
+        assert rel(o, o_ref[0, :, hh]) < 1e-12 and rel(S, S_ref[0, hh]) < 1e-12

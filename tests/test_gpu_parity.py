@@ -533,12 +533,83 @@ def test_rule_r1_equals_r5_when_gates_collapse(g):
     assert rel_err(S1.cpu().numpy(), S5.cpu().numpy()) < 1e-5
 
 
-def test_rule_r1_rejected_on_chunked_paths(g):
+def test_rule_r1_rejected_on_single_pass_path(g):
     inp = to_dev(gi.make_chunk_inputs(1, 64, 1, 32, 32, "f32", seed=34))
-    for path in ("auto", "two_pass", "fused"):
-        with pytest.raises(g.Gdn2Error) as e:
-            g.chunk_fwd(*(inp[n] for n in NAMES), path=path, rule="R1")
-        assert e.value.status == 2
+    with pytest.raises(g.Gdn2Error) as e:
+        g.chunk_fwd(*(inp[n] for n in NAMES), path="fused", rule="R1")
+    assert e.value.status == 2
+
+
+def gpu_fwd_r1(g, inp, chunk, cu=None, path="auto", layer_prep=False):
+    d = to_dev(inp)
+    o, Sf = g.chunk_fwd(*(d[n] for n in NAMES), S0=d.get("S0"), cu_seqlens=None if cu is None else cu.cuda(),
+                        chunk=chunk, path=path, rule="R1", layer_prep=layer_prep)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), Sf.cpu().numpy()
+
+
+# Rule R1 on the chunked two-pass path (its own per-chunk kernel and scan)
+R1_CASES = [("f32", 16, 16, 1, 64, 1), ("f32", 64, 64, 2, 512, 4), ("f32", 128, 16, 2, 40, 2),
+            ("f32", 32, 64, 2, 130, 3), ("bf16", 128, 64, 2, 200, 3), ("bf16", 64, 16, 2, 77, 3),
+            ("bf16", 16, 64, 1, 90, 2)]
+
+
+@pytest.mark.parametrize("path", ["auto", "two_pass"])
+@pytest.mark.parametrize("dtype,d,chunk,B,T,H", R1_CASES)
+def test_rule_r1_chunked(g, dtype, d, chunk, B, T, H, path):
+    inp = gi.make_chunk_inputs(B, T, H, d, d, dtype, seed=120 + d + T, s0="normal")
+    print(f"case R1 chunked {dtype} d={d} C={chunk} B={B} T={T} H={H} {path}", flush=True)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], rule="R1")
+    o, Sf = gpu_fwd_r1(g, inp, chunk, path=path)
+    check(o, Sf, o_ref, S_ref, TOL[dtype], f"R1 chunked {dtype} d={d} C={chunk} {path}")
+
+
+def test_rule_r1_chunked_packed_and_extreme_decay(g):
+    """Packed input with empty and one-token sequences; then decays down to
+    1e-4 and zero (the pairwise diagonal blocks of both product families)."""
+    lens = [70, 0, 1, 64, 130, 0, 15]
+    cu = gi.cu_seqlens_from(lens)
+    inp = gi.make_chunk_inputs(1, int(cu[-1]), 2, 64, 64, "f32", seed=131, s0="normal", num_seqs=len(lens))
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], cu_seqlens=cu, rule="R1")
+    for chunk in (16, 64):
+        print(f"case R1 packed C={chunk}", flush=True)
+        o, Sf = gpu_fwd_r1(g, inp, chunk, cu=cu)
+        check(o, Sf, o_ref, S_ref, TOL["f32"], f"R1 packed C={chunk}")
+    for dtype, d, chunk in (("f32", 64, 64), ("bf16", 128, 64), ("f32", 32, 16)):
+        inp = gi.make_strong_decay_inputs(2, 150, 2, d, d, dtype, seed=132 + d, s0="normal")
+        print(f"case R1 strong decay {dtype} d={d} C={chunk}", flush=True)
+        o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], rule="R1")
+        o, Sf = gpu_fwd_r1(g, inp, chunk)
+        check(o, Sf, o_ref, S_ref, TOL[dtype], f"R1 strong decay {dtype} d={d} C={chunk}")
+
+
+def test_rule_r1_chunked_gate_layouts(g):
+    """Per-(token, head) gates (b = w = beta: both readings are KDA, so R1
+    equals R5) and layer prep, against the oracle."""
+    from oracle import layer_prep as lp
+    inp = gi.make_chunk_inputs(2, 190, 3, 64, 64, "f32", seed=133, s0="normal", scalar_beta=True)
+    compact = dict(inp, b=inp["b"][..., 0].contiguous(), w=inp["w"][..., 0].contiguous())
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], rule="R1")
+    print("case R1 KDA gates", flush=True)
+    o, Sf = gpu_fwd_r1(g, compact, 64)
+    check(o, Sf, o_ref, S_ref, TOL["f32"], "R1 KDA gates")
+    raw = gi.make_layer_inputs(2, 200, 3, 128, 128, "bf16", seed=134, s0="normal")
+    prep = lp.layer_prep(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"])
+    o_ref, S_ref = oracle.fwd(prep["q"], prep["k"], raw["v"], prep["alpha"], prep["b"], prep["w"], S0=raw["S0"],
+                              rule="R1")
+    print("case R1 layer prep", flush=True)
+    o, Sf = gpu_fwd_r1(g, raw, 64, layer_prep=True)
+    check(o, Sf, o_ref, S_ref, TOL["bf16"], "R1 layer prep")
+
+
+def test_rule_r1_chunked_layer_8x4096x16(g):
+    """Rule R1 on the layer workload (B=8, T=4096, H=16, d=128, bf16): every
+    element against the oracle's R1."""
+    c, inp = make("layer_8x4096x16_d128")
+    print("case R1 layer 8x4096x16", flush=True)
+    o, Sf = gpu_fwd_r1(g, inp, 64)
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), rule="R1")
+    check(o, Sf, o_ref, S_ref, TOL["bf16"], "R1 layer")
 
 
 def test_binding_rejects_wrong_tensors(g):
