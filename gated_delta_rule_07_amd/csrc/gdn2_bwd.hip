@@ -45,6 +45,8 @@
 #include "gdn2_kernels.hpp"
 #include "gdn2_wy.hpp"
 
+#include <type_traits>
+
 namespace gdn2 {
 
 // ------------------------------------------------------- reverse dH scan --
@@ -217,21 +219,34 @@ __global__ void __launch_bounds__(64 * dstate_cfg<D>::NW) gdn2_bwd_dstate_kernel
 }
 
 // --------------------------------------------------- per-chunk gradients --
-// LDS of one gradient workgroup, in floats: row-major float32 matrices with
-// padded pitches PD = D + 4 and PC = C + 4.
+// LDS of one gradient workgroup, byte offsets.  Row-major matrices with
+// padded pitches:
 //   KT  : the scaled keys K~ (C x D)
-//   ST  : T (C x C);  SP: P (C x C)
-//   YZ  : Y, then Z, then the dK~ accumulators (fragment order)
-//   DOZ : A (until T is done), then dO, then dZ (sized for both)
-template <int D, int C, bool PW = false> struct bwd_lds {
-  static constexpr int NB = C / 16, PD = D + 4, PC = C + 4;
-  // DOZ also holds A (C x C, pitch PC) early on, so it spans the larger of the two
-  static constexpr int DOZ_FLOATS = (C * PD > C * PC) ? C * PD : C * PC;
-  static constexpr int KT = 0, ST = KT + C * PD, SP = ST + C * PC, YZ = SP + C * PC, DOZ = YZ + C * PD,
-                       BTOT = DOZ + DOZ_FLOATS, GTOT = BTOT + NB * D, KBS = GTOT + NB * D, DGAM = KBS + NB * D,
-                       PWF = DGAM + D,                // one flag per sub-block (strong decay)
-                       DIAG = PWF + NB,               // PW: dA_II, dP_II (16 x 16 each) per sub-block
-                       FLOATS = DIAG + (PW ? NB * 512 : 0);
+//   YZ  : Y, then Z (C x D)
+//   ST  : T (C x C), float32
+//   DOZ : A (C x C, float32) until Z is formed, then dO, then dZ (C x D)
+//   SP  : P (C x C)
+// K~, Y/Z, dO/dZ and P are only ever read as matrix-core operands, so they
+// are kept in LT, the operand type (bfloat16 for bfloat16 inputs: the stored
+// value is the one the product rounds to), with pitches PDL = D + 4 and
+// PCL = C + 4 elements; A and T, which the triangular solve reads, stay
+// float32 with pitch PC = C + 4.  Above them: BTOT (the NB sub-blocks' log
+// decays), DGAM, one strong-decay flag per sub-block and, in the PW variant,
+// DIAG (dA_II and dP_II, 16 x 16 floats each, per sub-block).  Once the
+// products are done the bottom of the LDS is reused for the dK~ sums of the
+// NB sub-blocks (DKS, NK tiles of 256 floats each) and the per-sub-block sums
+// GTOT and KBS.  For bfloat16 with D = 128, C = 64 this is under 80 KB, so
+// two workgroups share a compute unit.
+template <typename LT, int D, int C, bool PW = false> struct bwd_lds {
+  static constexpr int NB = C / 16, NK = D / 16, PC = C + 4, PDL = D + 4, PCL = C + 4;
+  static constexpr size_t SZ_CD = sizeof(LT) * C * PDL, SZ_CC = sizeof(float) * C * PC;
+  static constexpr size_t KT = 0, YZ = KT + SZ_CD, ST = YZ + SZ_CD, DOZ = ST + SZ_CC,
+                          SP = DOZ + (SZ_CD > SZ_CC ? SZ_CD : SZ_CC), BTOT = SP + sizeof(LT) * C * PCL,
+                          DGAM = BTOT + sizeof(float) * NB * D, PWF = DGAM + sizeof(float) * D,
+                          DIAG = PWF + sizeof(float) * NB, BYTES = DIAG + (PW ? sizeof(float) * NB * 512 : 0);
+  static constexpr size_t DKS = 0, GTOT = DKS + sizeof(float) * NB * NK * 256, KBS = GTOT + sizeof(float) * NB * D;
+  static_assert(KBS + sizeof(float) * NB * D <= BTOT, "the dK~ and sub-block sums fit below BTOT");
+  static_assert(SZ_CD % 16 == 0 && SZ_CC % 16 == 0 && (sizeof(LT) * C * PCL) % 16 == 0, "16-byte aligned regions");
 };
 
 // Fragments of a 16 x 16 tile at (r0, c0) of a row-major float32 matrix with
@@ -278,6 +293,40 @@ __device__ __forceinline__ f32x4 tri_row(f32x4 v, int lane, bool strict) {
   return v;
 }
 
+// The same tiles of a row-major LDS matrix of element type T (pitch in
+// elements) as operand fragments of type T, and RowFrag / ColFrag stores
+// rounded to T.  For T = bfloat16 a RowFrag is one 8-byte access per lane
+// and a ColFrag four 2-byte ones.
+template <typename T> __device__ __forceinline__ frag<T> ldm_row(const T *M, int pitch, int r0, int c0, int lane) {
+  return frag<T>::ld_at(M + static_cast<size_t>(r0 + (lane & 15)) * pitch + c0 + 4 * (lane >> 4));
+}
+template <typename T> __device__ __forceinline__ frag<T> ldm_col(const T *M, int pitch, int r0, int c0, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    return frag<T>::from(ld_colf(M, pitch, r0, c0, lane));
+  } else {
+    const T *p = M + static_cast<size_t>(r0 + 4 * (lane >> 4)) * pitch + c0 + (lane & 15);
+    frag<T> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.v[i] = static_cast<short>(p[static_cast<size_t>(i) * pitch]);
+    return f;
+  }
+}
+template <typename T> __device__ __forceinline__ void stm_row(T *M, int pitch, int r0, int c0, int lane, f32x4 x) {
+  frag<T>::from(x).st_at(M + static_cast<size_t>(r0 + (lane & 15)) * pitch + c0 + 4 * (lane >> 4));
+}
+template <typename T> __device__ __forceinline__ void stm_col(T *M, int pitch, int r0, int c0, int lane, f32x4 x) {
+  if constexpr (sizeof(T) == 4) {
+    st_colf(M, pitch, r0, c0, lane, x);
+  } else {
+    const frag<T> f = frag<T>::from(x);
+    T *p = M + static_cast<size_t>(r0 + 4 * (lane >> 4)) * pitch + c0 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      p[static_cast<size_t>(i) * pitch] = static_cast<T>(f.v[i]);
+  }
+}
+
 // One workgroup per chunk-head, one wave per 16-token sub-block: wave I keeps
 // the rows of sub-block I (q, k, e, g, dO, Z, dY and the gradient
 // accumulators) as RowFrag slabs in registers and computes every product
@@ -305,12 +354,17 @@ template <typename IO, int D, int C, typename CT, int GM, bool PW = false>
 __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args ba) {
   constexpr bool GN = GM != BG_PLAIN;
   const chunk_args &a = ba.f;
-  typedef bwd_lds<D, C, PW> L;
-  constexpr int NB = C / 16, NK = D / 16, PD = L::PD, PC = L::PC;
-  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
-  float *KT = sm + L::KT, *sT = sm + L::ST, *sP = sm + L::SP, *YZ = sm + L::YZ, *DOZ = sm + L::DOZ;
-  float *btot = sm + L::BTOT, *gtot = sm + L::GTOT, *kbs = sm + L::KBS, *dgam = sm + L::DGAM;
-  float *sA = DOZ;
+  static_assert(std::is_same<CT, IO>::value, "LDS operands are kept in the I/O type");
+  typedef CT LT;
+  typedef bwd_lds<LT, D, C, PW> L;
+  constexpr int NB = C / 16, NK = D / 16, PC = L::PC, PDL = L::PDL, PCL = L::PCL;
+  __shared__ __attribute__((aligned(16))) unsigned char smb[L::BYTES];
+  LT *KT = reinterpret_cast<LT *>(smb + L::KT), *YZ = reinterpret_cast<LT *>(smb + L::YZ);
+  LT *DOZ = reinterpret_cast<LT *>(smb + L::DOZ), *sP = reinterpret_cast<LT *>(smb + L::SP);
+  float *sT = reinterpret_cast<float *>(smb + L::ST), *sA = reinterpret_cast<float *>(smb + L::DOZ);
+  float *btot = reinterpret_cast<float *>(smb + L::BTOT), *gtot = reinterpret_cast<float *>(smb + L::GTOT);
+  float *kbs = reinterpret_cast<float *>(smb + L::KBS), *dgam = reinterpret_cast<float *>(smb + L::DGAM);
+  float *pwf = reinterpret_cast<float *>(smb + L::PWF), *diag = reinterpret_cast<float *>(smb + L::DIAG);
 
   const int slot = static_cast<int>(blockIdx.x / a.H), h = static_cast<int>(blockIdx.x - slot * a.H);
   if constexpr (PW) {
@@ -499,7 +553,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
         mn = fminf(mn, gv[kk][i]);
     const bool pw_wave = __ballot(m == 15 && mn < -DIAG_LIM_LN) != 0;
     if (lane == 0)
-      sm[L::PWF + I] = pw_wave ? 1.f : 0.f;
+      pwf[I] = pw_wave ? 1.f : 0.f;
   }
   if (m == 15) {
 #pragma unroll
@@ -511,7 +565,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     bool any_pw = false;
 #pragma unroll
     for (int J = 0; J < NB; ++J)
-      any_pw = any_pw || sm[L::PWF + J] != 0.f;
+      any_pw = any_pw || pwf[J] != 0.f;
     if (threadIdx.x == 0)
       ba.pwflag[blockIdx.x] = any_pw ? 1 : 0;
     if (any_pw)
@@ -559,7 +613,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   // ---- K~ rows to LDS, then A and P tiles (I, J <= I)
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
-    st_rowf(KT, PD, 16 * I, 16 * kk, lane, kv[kk] * key_fac(kk));
+    stm_row(KT, PDL, 16 * I, 16 * kk, lane, kv[kk] * key_fac(kk));
   lds_barrier();
 #pragma unroll
   for (int J = 0; J < NB; ++J) {
@@ -568,7 +622,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const f32x4 sc = row_fac(J, kk);
-        const F kt = F::from(ld_rowf(KT, PD, 16 * J, 16 * kk, lane));
+        const F kt = ldm_row(KT, PDL, 16 * J, 16 * kk, lane);
         mm_io(aa, F::from(ev[kk] * sc), kt);
         mm_io(pp, F::from(qv[kk] * sc), kt);
       }
@@ -577,7 +631,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
         pp = tri_col(pp, lane, false);
       }
       st_colf(sA, PC, 16 * I, 16 * J, lane, aa);
-      st_colf(sP, PC, 16 * I, 16 * J, lane, pp);
+      stm_col(sP, PCL, 16 * I, 16 * J, lane, pp);
     }
   }
   if constexpr (PW) {
@@ -585,7 +639,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     f32x4 da, dp;
     wy_diag_pairwise<IO, D>(a, t0, len, h, I, lane, qs, ks, da, dp);
     st_rowf(sA, PC, 16 * I, 16 * I, lane, da);
-    st_rowf(sP, PC, 16 * I, 16 * I, lane, dp);
+    stm_row(sP, PCL, 16 * I, 16 * I, lane, dp);
   }
   lds_barrier();
 
@@ -637,7 +691,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
         cur[kk] = nxt[kk];
       f32x4 u = ((GN && LPm) ? sig4(rw[n].f()) : rw[n].f()) * rv[n].f();
       zv[n] = (valid ? u : zero4) - acc;
-      st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
+      stm_row(YZ, PDL, 16 * I, 16 * n, lane, zv[n]);
     }
   }
   lds_barrier();
@@ -661,7 +715,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   for (int n = 0; n < NK; ++n) {
     f32x4 acc = zero4;
     for (int J = 0; J <= I; ++J)
-      mm<CT>(acc, ld_colf(YZ, PD, 16 * J, 16 * n, lane), ld_rowf(sT, PC, 16 * I, 16 * J, lane));
+      mm_io(acc, ldm_col(YZ, PDL, 16 * J, 16 * n, lane), F::from(ld_rowf(sT, PC, 16 * I, 16 * J, lane)));
     zv[n] = acc;
   }
   f32x4 dov[NK];
@@ -673,8 +727,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   lds_barrier();  // Y and A are no longer read
 #pragma unroll
   for (int n = 0; n < NK; ++n) {
-    st_rowf(YZ, PD, 16 * I, 16 * n, lane, zv[n]);
-    st_rowf(DOZ, PD, 16 * I, 16 * n, lane, dov[n]);
+    stm_row(YZ, PDL, 16 * I, 16 * n, lane, zv[n]);
+    stm_row(DOZ, PDL, 16 * I, 16 * n, lane, dov[n]);
   }
   lds_barrier();
 
@@ -698,7 +752,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       }
       f32x4 acc = zero4;
       for (int J = I; J < NB; ++J)
-        mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sP, PC, 16 * J, 16 * I, lane));
+        mm_io(acc, ldm_col(DOZ, PDL, 16 * J, 16 * n, lane), ldm_col(sP, PCL, 16 * J, 16 * I, lane));
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         mm_io(acc, cur[kk], kbf[kk]);
@@ -711,7 +765,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   lds_barrier();  // dO of the other sub-blocks is no longer read
 #pragma unroll
   for (int n = 0; n < NK; ++n)
-    st_rowf(DOZ, PD, 16 * I, 16 * n, lane, dyv[n]);
+    stm_row(DOZ, PDL, 16 * I, 16 * n, lane, dyv[n]);
   lds_barrier();
   // dY_I = sum_{J >= I} T_JI^T dZ_J;  dv = dY (.) w, dw = dY (.) v
   IO *dq = static_cast<IO *>(ba.dq), *dk = static_cast<IO *>(ba.dk), *db = static_cast<IO *>(ba.db);
@@ -727,7 +781,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   for (int n = 0; n < NK; ++n) {
     f32x4 acc = zero4;
     for (int J = I; J < NB; ++J)
-      mm<CT>(acc, ld_colf(DOZ, PD, 16 * J, 16 * n, lane), ld_colf(sT, PC, 16 * J, 16 * I, lane));
+      mm_io(acc, ldm_col(DOZ, PDL, 16 * J, 16 * n, lane), F::from(ld_colf(sT, PC, 16 * J, 16 * I, lane)));
     dyv[n] = acc;
     const int c0 = 16 * n + 4 * g;
     if constexpr (!GN) {
@@ -770,7 +824,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     if (J <= I) {
 #pragma unroll
       for (int n = 0; n < NK; ++n) {
-        const F zr = F::from(ld_rowf(YZ, PD, 16 * J, 16 * n, lane));
+        const F zr = ldm_row(YZ, PDL, 16 * J, 16 * n, lane);
         mm_io(ac, dyf[n], zr);
         mm_io(ar, zr, dyf[n]);
         mm_io(pc, dof[n], zr);
@@ -793,7 +847,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   if constexpr (PW) {
     // this sub-block's diagonal dA, dP (row t = m, columns 4g .. 4g+3), for
     // the pairwise gradients below (read by this wave only)
-    float *dA_I = sm + L::DIAG + I * 512, *dP_I = dA_I + 256;
+    float *dA_I = diag + I * 512, *dP_I = dA_I + 256;
     *reinterpret_cast<f32x4 *>(dA_I + m * 16 + 4 * g) = dAr[I].to_f32();
     *reinterpret_cast<f32x4 *>(dP_I + m * 16 + 4 * g) = dPr[I].to_f32();
   }
@@ -835,7 +889,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
       if (J < I || (J == I && !PW)) {
-        const F ktc = F::from(ld_colf(KT, PD, 16 * J, 16 * kk, lane));
+        const F ktc = ldm_col(KT, PDL, 16 * J, 16 * kk, lane);
         f32x4 aq = zero4, ae = zero4;
         mm_io(aq, ktc, dPr[J]);
         mm_io(ae, ktc, dAr[J]);
@@ -849,7 +903,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       // over s = t - j of this sub-block, F_ts = alpha_t .. alpha_{s+1}
       f32x4 q4, k4, e4, a4;
       wy_row4<IO, D>(a, srow, valid, 16 * kk + 4 * g, qs, ks, q4, k4, e4, a4);
-      const float *dA_I = sm + L::DIAG + I * 512, *dP_I = dA_I + 256;
+      const float *dA_I = diag + I * 512, *dP_I = dA_I + 256;
       f32x4 Fp = {1.f, 1.f, 1.f, 1.f}, xq = zero4, xe = zero4;
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
@@ -894,11 +948,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       erc[kk] = transpose_f32(bq * rk[kk].f() * (ks * sc), lane);
     }
   }
-  lds_barrier();  // K~, T, P, Y/Z and dZ are no longer read: LDS from 0 holds the slots
-  static_assert((NB * (NB + 1) / 2) * NK * 256 <= L::BTOT, "dK~ slots fit below the sub-block sums");
-  auto dk_slot = [&](int I2, int J2, int kk) {
-    return reinterpret_cast<f32x4 *>(sm) + ((I2 * (I2 + 1) / 2 + J2) * NK + kk) * 64;
-  };
+  lds_barrier();  // K~, T, P, Y/Z and dZ are no longer read: the dK~ sums take the bottom of the LDS
+  // dK~_J = sum over the sub-blocks I >= J of their rows' terms, added in
+  // ascending I: in round r wave I adds its term for J = I - r (round 0
+  // writes it), so every sum is formed in the same order on every run.
+  auto dk_sum = [&](int J2, int kk) { return reinterpret_cast<f32x4 *>(smb + L::DKS) + (J2 * NK + kk) * 64; };
   {
     // column scale of ColFrag element (lane column c): e^{rho_I - rho_{J+1}}
     // (the sub-blocks between J and I, summed up while J descends), and
@@ -908,8 +962,16 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     for (int kk = 0; kk < NK; ++kk)
       rs[kk] = 0.f;
 #pragma unroll
-    for (int J = NB - 1; J >= 0; --J) {
-      if (J <= I) {
+    for (int r = 0; r < NB; ++r) {
+      const int J = I - r;
+      if (J >= 0) {
+        F dpj = dPc[0], daj = dAc[0];  // dP_IJ, dA_IJ (selected, not indexed: they stay in registers)
+#pragma unroll
+        for (int J2 = 1; J2 < NB; ++J2)
+          if (J2 == J) {
+            dpj = dPc[J2];
+            daj = dAc[J2];
+          }
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
           f32x4 acc = zero4;
@@ -919,23 +981,24 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
               rs[kk] += btot[(J + 1) * D + 16 * kk + m];
             if (J < I) {
               const float f = __expf(rs[kk]);
-              mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
-              mm_io(acc, F::from(erc[kk] * f), dAc[J]);
+              mm_io(acc, F::from(qrc[kk] * f), dpj);
+              mm_io(acc, F::from(erc[kk] * f), daj);
             }
           } else {
             // e^{rho_{I+1} - rho_{J+1}}
             if (J < I)
               rs[kk] += btot[(J + 1) * D + 16 * kk + m];
             const float f = __expf(rs[kk]);
-            mm_io(acc, F::from(qrc[kk] * f), dPc[J]);
-            mm_io(acc, F::from(erc[kk] * f), dAc[J]);
+            mm_io(acc, F::from(qrc[kk] * f), dpj);
+            mm_io(acc, F::from(erc[kk] * f), daj);
           }
-          dk_slot(I, J, kk)[lane] = acc;
+          f32x4 *ps = dk_sum(J, kk) + lane;
+          *ps = (r == 0) ? acc : *ps + acc;
         }
       }
+      lds_barrier();
     }
   }
-  lds_barrier();
 
   // ---- map to the inputs
   // d gamma_C = rowsum(dH (.) S): wave I takes row tiles kk = I, I + NB, ..;
@@ -972,18 +1035,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   float dotq = 0.f, dotk = 0.f, dbs = 0.f;  // GN: row sums for layer prep and per-(token, head) b
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    f32x4 dkt = zero4;
-#pragma unroll
-    for (int I2 = 0; I2 < NB; ++I2)
-      if (I2 >= I)
-        dkt += dk_slot(I2, I, kk)[lane];
-    f32x4 ckt = dkt * key_fac(kk);
+    f32x4 ckt = dk_sum(I, kk)[lane] * key_fac(kk);
     if constexpr (PW) {
       // the diagonal pair: dk_s += sum_t (dP_ts q_t + dA_ts e_t) F_ts over
       // t = s + j of this sub-block, F_ts = alpha_{s+1} .. alpha_t
       f32x4 q4, k4, e4, a4;
       wy_row4<IO, D>(a, srow, valid, 16 * kk + 4 * g, qs, ks, q4, k4, e4, a4);
-      const float *dA_I = sm + L::DIAG + I * 512, *dP_I = dA_I + 256;
+      const float *dA_I = diag + I * 512, *dP_I = dA_I + 256;
       f32x4 Fk = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
