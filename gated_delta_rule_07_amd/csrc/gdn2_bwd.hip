@@ -235,15 +235,21 @@ __global__ void __launch_bounds__(64 * dstate_cfg<D>::NW) gdn2_bwd_dstate_kernel
 // DIAG (dA_II and dP_II, 16 x 16 floats each, per sub-block).  Once the
 // products are done the bottom of the LDS is reused for the dK~ sums of the
 // NB sub-blocks (DKS, NK tiles of 256 floats each) and the per-sub-block sums
-// GTOT and KBS.  For bfloat16 with D = 128, C = 64 this is under 80 KB, so
-// two workgroups share a compute unit.
+// GTOT and KBS.  For bfloat16 the chunk's S and dH tiles are staged at the
+// top (STG, below).
 template <typename LT, int D, int C, bool PW = false> struct bwd_lds {
   static constexpr int NB = C / 16, NK = D / 16, PC = C + 4, PDL = D + 4, PCL = C + 4;
   static constexpr size_t SZ_CD = sizeof(LT) * C * PDL, SZ_CC = sizeof(float) * C * PC;
   static constexpr size_t KT = 0, YZ = KT + SZ_CD, ST = YZ + SZ_CD, DOZ = ST + SZ_CC,
                           SP = DOZ + (SZ_CD > SZ_CC ? SZ_CD : SZ_CC), BTOT = SP + sizeof(LT) * C * PCL,
                           DGAM = BTOT + sizeof(float) * NB * D, PWF = DGAM + sizeof(float) * D,
-                          DIAG = PWF + sizeof(float) * NB, BYTES = DIAG + (PW ? sizeof(float) * NB * 512 : 0);
+                          DIAG = PWF + sizeof(float) * NB, STG = DIAG + (PW ? sizeof(float) * NB * 512 : 0);
+  // STAGE: the chunk's entering state S and leaving-state gradient dH are
+  // copied into LDS (STG: S then dH, one fragment layout at a time) instead
+  // of every wave reading them from global memory
+  static constexpr size_t STB = static_cast<size_t>(NK) * NK * frag<LT>::TILE_BYTES;
+  static constexpr bool STAGE = sizeof(LT) == 2 && STG + 2 * STB <= 160 * 1024;
+  static constexpr size_t BYTES = STG + (STAGE ? 2 * STB : 0);
   static constexpr size_t DKS = 0, GTOT = DKS + sizeof(float) * NB * NK * 256, KBS = GTOT + sizeof(float) * NB * D;
   static_assert(KBS + sizeof(float) * NB * D <= BTOT, "the dK~ and sub-block sums fit below BTOT");
   static_assert(SZ_CD % 16 == 0 && SZ_CC % 16 == 0 && (sizeof(LT) * C * PCL) % 16 == 0, "16-byte aligned regions");
@@ -571,6 +577,34 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     if (any_pw)
       return;  // the whole workgroup (the flags are uniform): the PW variant takes it
   }
+  // S and dH in fragment layout `layout` (ST_::COL or ST_::ROW) to LDS: a
+  // direct global -> LDS copy in 1 KB pieces (16 bytes a lane), the pieces
+  // dealt to the waves in turn; waited for (vmcnt) and published by a
+  // barrier before the first read
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  auto stage_states = [&](size_t layout) {
+    if constexpr (L::STAGE) {
+      constexpr int PIECES = static_cast<int>((2 * L::STB + 1023) / 1024);
+#pragma unroll
+      for (int i = 0; i < (PIECES + NB - 1) / NB; ++i) {
+        const int pc = wv + NB * i;
+        if (pc < PIECES) {
+          const size_t o = static_cast<size_t>(pc) * 1024 + 16 * static_cast<size_t>(lane);
+          const unsigned char *src = o < L::STB ? St + layout + o : Ht + layout + (o - L::STB);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void *)src,
+              (__attribute__((address_space(3))) void *)(smb + L::STG + static_cast<size_t>(pc) * 1024), 16, 0, 0);
+        }
+      }
+    }
+  };
+  auto staged_wait = [&]() {
+    if constexpr (L::STAGE)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  const unsigned char *sS = smb + L::STG, *sH = smb + L::STG + L::STB;  // staged S, dH tiles
+  stage_states(ST_::COL);
+
   // Without PW every sub-block decays by at most e^-DIAG_LIM_LN, so every
   // cumulative log decay is finite and bounded (|g| <= C DIAG_LIM_LN / 16):
   // gv becomes the chunk's cumulative g_t and the factors are differences
@@ -641,6 +675,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     st_rowf(sA, PC, 16 * I, 16 * I, lane, da);
     stm_row(sP, PCL, 16 * I, 16 * I, lane, dp);
   }
+  staged_wait();  // S, dH (column layout) are in LDS after the barrier
   lds_barrier();
 
   // ---- diagonal blocks of T = (I + A)^{-1} (lane c < 16: column c), Y_I = U_I - ES_I S
@@ -670,14 +705,21 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
       esf[kk] = F::from(ev[kk] * start_fac(kk));  // e e^{g_t}
-    // S tiles of column n + 1 are loaded while column n is multiplied
+    // S tiles from LDS (staged), or from global memory with the tiles of
+    // column n + 1 loaded while column n is multiplied
     F cur[NK], nxt[NK];
+    if constexpr (!L::STAGE) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      cur[kk] = F::ld(St + ST_::COL + ST_::off(kk, 0), lane);
+      for (int kk = 0; kk < NK; ++kk)
+        cur[kk] = F::ld(St + ST_::COL + ST_::off(kk, 0), lane);
+    }
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
-      if (n + 1 < NK) {
+      if constexpr (L::STAGE) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          cur[kk] = F::ld(sS + ST_::off(kk, n), lane);
+      } else if (n + 1 < NK) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
           nxt[kk] = F::ld(St + ST_::COL + ST_::off(kk, n + 1), lane);
@@ -686,9 +728,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         mm_io(acc, cur[kk], esf[kk]);
+      if constexpr (!L::STAGE) {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        cur[kk] = nxt[kk];
+        for (int kk = 0; kk < NK; ++kk)
+          cur[kk] = nxt[kk];
+      }
       f32x4 u = ((GN && LPm) ? sig4(rw[n].f()) : rw[n].f()) * rv[n].f();
       zv[n] = (valid ? u : zero4) - acc;
       stm_row(YZ, PDL, 16 * I, 16 * n, lane, zv[n]);
@@ -739,13 +783,21 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
       kbf[kk] = F::from(kv[kk] * end_fac(kk));  // k e^{g_C - g_t}
-    F cur[NK], nxt[NK];  // dH tiles, column n + 1 in flight during column n
+    // dH tiles from LDS (staged), or from global memory with column n + 1 in
+    // flight during column n
+    F cur[NK], nxt[NK];
+    if constexpr (!L::STAGE) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      cur[kk] = F::ld(Ht + ST_::COL + ST_::off(kk, 0), lane);
+      for (int kk = 0; kk < NK; ++kk)
+        cur[kk] = F::ld(Ht + ST_::COL + ST_::off(kk, 0), lane);
+    }
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
-      if (n + 1 < NK) {
+      if constexpr (L::STAGE) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          cur[kk] = F::ld(sH + ST_::off(kk, n), lane);
+      } else if (n + 1 < NK) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
           nxt[kk] = F::ld(Ht + ST_::COL + ST_::off(kk, n + 1), lane);
@@ -756,13 +808,16 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         mm_io(acc, cur[kk], kbf[kk]);
+      if constexpr (!L::STAGE) {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        cur[kk] = nxt[kk];
+        for (int kk = 0; kk < NK; ++kk)
+          cur[kk] = nxt[kk];
+      }
       dyv[n] = acc;
     }
   }
-  lds_barrier();  // dO of the other sub-blocks is no longer read
+  lds_barrier();  // dO of the other sub-blocks (and the staged column layouts) are no longer read
+  stage_states(ST_::ROW);  // row layouts of S and dH, for dq, de, dk and d gamma_C
 #pragma unroll
   for (int n = 0; n < NK; ++n)
     stm_row(DOZ, PDL, 16 * I, 16 * n, lane, dyv[n]);
@@ -854,16 +909,28 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
 
   // ---- contributions to dq (cq), de (ce), dk (ck) and d g_C (kb term)
   f32x4 cq[NK], ce[NK], ck[NK];
-  // S and dH tiles of row tile kk + 1 are loaded while row tile kk is multiplied
+  // S and dH tiles in row layout: from LDS (staged; waited for here), or from
+  // global memory with row tile kk + 1 loaded while row tile kk is multiplied
   F scur[NK], hcur[NK], snxt[NK], hnxt[NK];
+  if constexpr (L::STAGE) {
+    staged_wait();
+    lds_barrier();
+  } else {
 #pragma unroll
-  for (int n = 0; n < NK; ++n) {
-    scur[n] = F::ld(St + ST_::ROW + ST_::off(0, n), lane);
-    hcur[n] = F::ld(Ht + ST_::ROW + ST_::off(0, n), lane);
+    for (int n = 0; n < NK; ++n) {
+      scur[n] = F::ld(St + ST_::ROW + ST_::off(0, n), lane);
+      hcur[n] = F::ld(Ht + ST_::ROW + ST_::off(0, n), lane);
+    }
   }
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    if (kk + 1 < NK) {
+    if constexpr (L::STAGE) {
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        scur[n] = F::ld(sS + ST_::off(kk, n), lane);
+        hcur[n] = F::ld(sH + ST_::off(kk, n), lane);
+      }
+    } else if (kk + 1 < NK) {
 #pragma unroll
       for (int n = 0; n < NK; ++n) {
         snxt[n] = F::ld(St + ST_::ROW + ST_::off(kk + 1, n), lane);
@@ -877,10 +944,12 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
       mm_io(a2, scur[n], dyf[n]);
       mm_io(a3, hcur[n], zf[n]);
     }
+    if constexpr (!L::STAGE) {
 #pragma unroll
-    for (int n = 0; n < NK; ++n) {
-      scur[n] = snxt[n];
-      hcur[n] = hnxt[n];
+      for (int n = 0; n < NK; ++n) {
+        scur[n] = snxt[n];
+        hcur[n] = hnxt[n];
+      }
     }
     const f32x4 eg = start_fac(kk);  // e^{g_t}
     cq[kk] = a1 * eg;
@@ -1001,25 +1070,42 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
   }
 
   // ---- map to the inputs
-  // d gamma_C = rowsum(dH (.) S): wave I takes row tiles kk = I, I + NB, ..;
-  // lane (c, g) of ColFrag tile (kk, n) holds rows 16kk + 4g .. +3 of column 16n + c
-  for (int kk = I; kk < NK; kk += NB) {
-    f32x4 acc = zero4;
+  // d gamma_C = rowsum(dH (.) S): wave I takes row tiles kk = I, I + NB, ..
+  if constexpr (L::STAGE) {
+    // staged row layout: lane (m, g) of RowFrag tile (kk, n) holds row
+    // 16kk + m, columns 16n + 4g .. +3
+    for (int kk = I; kk < NK; kk += NB) {
+      float x = 0.f;
 #pragma unroll
-    for (int n = 0; n < NK; ++n)
-      acc += F::ld(St + ST_::COL + ST_::off(kk, n), lane).to_f32() *
-             F::ld(Ht + ST_::COL + ST_::off(kk, n), lane).to_f32();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = acc[i];
-      x += __shfl_xor(x, 1, 16);
-      x += __shfl_xor(x, 2, 16);
-      x += __shfl_xor(x, 4, 16);
-      x += __shfl_xor(x, 8, 16);
-      acc[i] = x;
+      for (int n = 0; n < NK; ++n) {
+        const f32x4 p = F::ld(sS + ST_::off(kk, n), lane).to_f32() * F::ld(sH + ST_::off(kk, n), lane).to_f32();
+        x += (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      if (g == 0)
+        dgam[16 * kk + m] = x;
     }
-    if (m == 0)
-      *reinterpret_cast<f32x4 *>(dgam + 16 * kk + 4 * g) = acc;
+  } else {
+    // lane (c, g) of ColFrag tile (kk, n) holds rows 16kk + 4g .. +3 of column 16n + c
+    for (int kk = I; kk < NK; kk += NB) {
+      f32x4 acc = zero4;
+#pragma unroll
+      for (int n = 0; n < NK; ++n)
+        acc += F::ld(St + ST_::COL + ST_::off(kk, n), lane).to_f32() *
+               F::ld(Ht + ST_::COL + ST_::off(kk, n), lane).to_f32();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[i];
+        x += __shfl_xor(x, 1, 16);
+        x += __shfl_xor(x, 2, 16);
+        x += __shfl_xor(x, 4, 16);
+        x += __shfl_xor(x, 8, 16);
+        acc[i] = x;
+      }
+      if (m == 0)
+        *reinterpret_cast<f32x4 *>(dgam + 16 * kk + 4 * g) = acc;
+    }
   }
   f32x4 dg[NK];
   raw4<IO> ral[NK];  // alpha of the rows, for d alpha at the end
