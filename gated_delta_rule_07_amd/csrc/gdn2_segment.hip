@@ -22,30 +22,35 @@
 
 namespace gdn2 {
 
-// Workgroups per (segment, head) and map: NSPL, each with NW = NK / NSPL
-// compute waves, one per 16-column tile of the map; part 0 computes Psi,
-// part 1 Phi.  Per chunk every compute wave takes
+// Per chunk every compute wave takes
 //   Z = [Ut] - W S,   S <- Diag(gamma_C) S + Kbar^T Z
-// on its columns (Ut only for Psi) from the chunk's -W and Kbar^T tiles,
-// its Ut tiles and gamma_C, staged in LDS: the -W and Kbar^T regions of the
-// prep's block are copied byte for byte (16 or 8 bytes a lane), so
-// they keep the block's tile order, with 16-wide k tiles paired; bfloat16
-// products then take two k tiles per 16x16x32 instruction.
-// bfloat16: NL loader waves stage the chunks into two LDS buffers, chunk k
-// by loader (k - 1) mod NL, which issues its loads NL chunks before they
-// are due, so the compute waves never wait on global memory (one barrier
-// per chunk).  float32: the compute waves stage the tiles themselves, one
-// chunk ahead (the loaders' registers would not hold float32 chunks).  More
-// workgroups with fewer compute waves spread a few long segments over more
-// compute units (the per-rank shape of a context-parallel split has only H
-// units); every workgroup of one (segment, head) sits on the same XCD,
+// on its CPW 16-column tiles of one map (Ut only for Psi; Phi starts from
+// the identity) from the chunk's -W and Kbar^T tiles, its Ut tiles and
+// gamma_C, staged in LDS: the -W and Kbar^T regions of the prep's block are
+// copied byte for byte (16 or 8 bytes a lane), so they keep the block's
+// tile order, with 16-wide k tiles paired; bfloat16 products then take two
+// k tiles per 16x16x32 instruction.
+// bfloat16 (MERGED): NSPL = NK / CPW workgroups per (segment, head), each
+// with two compute waves on the same CPW = 2 column tiles, wave 0 of Psi
+// and wave 1 of Phi, so both maps share one staged copy of each chunk and
+// every -W and Kbar^T fragment read from LDS serves two column tiles; NL
+// loader waves stage the chunks into two LDS buffers, chunk k by loader
+// (k - 1) mod NL, which issues its loads NL chunks before they are due, so
+// the compute waves never wait on global memory (one barrier per chunk).
+// float32: two workgroups per (segment, head), part 0 of Psi and part 1 of
+// Phi, each with one compute wave per column tile, which stage the tiles
+// themselves one chunk ahead (loader registers would not hold float32
+// chunks).  Every workgroup of one (segment, head) sits on the same XCD,
 // whose L2 serves their common reads.
-// Grid: units_pad * 2 * NSPL workgroups, units_pad = N*H rounded up to 8.
+// Grid: units_pad * NPART * NSPL workgroups, units_pad = N*H rounded up to 8.
 template <typename IO, int D, int C> struct segmap_cfg {
   static constexpr int NK = D / 16, NB = C / 16;
   static constexpr bool PIPE = sizeof(IO) == 2;
-  static constexpr int NSPL = (PIPE && NK >= 4) ? NK / 2 : 1;
-  static constexpr int NW = NK / NSPL;  // compute waves
+  static constexpr bool MERGED = PIPE;                          // both maps in one workgroup
+  static constexpr int CPW = (MERGED && NK % 2 == 0) ? 2 : 1;   // column tiles per compute wave
+  static constexpr int NSPL = MERGED ? NK / CPW : 1;            // workgroups per (segment, head) and part
+  static constexpr int NPART = MERGED ? 1 : 2;                  // parts (maps) in the grid
+  static constexpr int NW = MERGED ? 2 : NK;                    // compute waves
   static constexpr int NL = PIPE ? 2 : 0;
   static constexpr int NBUF = PIPE ? 2 : 1;
   static constexpr size_t TB = frag<IO>::TILE_BYTES;
@@ -53,7 +58,8 @@ template <typename IO, int D, int C> struct segmap_cfg {
   static constexpr int PW = RB % 1024 == 0 ? 16 : 8;                // bytes a lane copies per piece
   static constexpr size_t PB = 64 * PW;                              // bytes of one piece
   static constexpr int NRP = static_cast<int>(2 * RB / PB);          // pieces of the two regions
-  static constexpr size_t UTO = 2 * RB, GMO = 2 * RB + NW * NB * TB;  // Ut tiles, gamma_C
+  static constexpr int NUT = MERGED ? CPW * NB : NW * NB;           // staged Ut tiles
+  static constexpr size_t UTO = 2 * RB, GMO = 2 * RB + NUT * TB;     // Ut tiles, gamma_C
   static constexpr size_t BUF = GMO + D * sizeof(float);
 };
 
@@ -61,7 +67,8 @@ template <typename IO, int D, int C>
 __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<IO, D, C>::NL)))
     gdn2_segmap_kernel(chunk_args a, float *Phi, float *Psi) {
   typedef segmap_cfg<IO, D, C> K;
-  constexpr int NB = C / 16, NK = D / 16, NW = K::NW, NSPL = K::NSPL, NL = K::NL, NRP = K::NRP;
+  constexpr int NB = C / 16, NK = D / 16, NW = K::NW, NSPL = K::NSPL, NL = K::NL, NRP = K::NRP, CPW = K::CPW,
+                NPART = K::NPART, NUT = K::NUT;
   typedef frag<IO> F;
   typedef frag2<IO> F2;
   typedef blk_layout<IO, D, C> L;
@@ -73,8 +80,8 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
 
   const int x = blockIdx.x;
   const int xcd = x & 7, s8 = x >> 3;
-  const int unit = (s8 / (2 * NSPL)) * 8 + xcd;
-  const int part = (s8 % (2 * NSPL)) / NSPL, grp = s8 % NSPL;
+  const int unit = (s8 / (NPART * NSPL)) * 8 + xcd;
+  const int gpart = (s8 % (NPART * NSPL)) / NSPL, grp = s8 % NSPL;
   if (unit >= a.num_seqs * a.H)
     return;  // whole workgroup
   const int n = unit / a.H, h = unit - n * a.H;
@@ -99,8 +106,12 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
     return (q < NRP / 2 ? L::WN + static_cast<size_t>(q) * PB : L::KB + static_cast<size_t>(q - NRP / 2) * PB) +
            static_cast<size_t>(lane) * PW;
   };
-  // this lane's fragment of Ut tile tt of compute wave w, in the block
-  auto ut_src = [&](int w, int tt) -> size_t { return L::UT + tile_off<IO, NK>(tt, grp * NW + w, lane); };
+  // this lane's fragment of staged Ut tile i (column tile i / NB of the
+  // workgroup, row tile i % NB), in the block
+  auto ut_src = [&](int i) -> size_t {
+    const int col = K::MERGED ? CPW * grp + i / NB : grp * NW + i / NB;
+    return L::UT + tile_off<IO, NK>(i % NB, col, lane);
+  };
 
   if constexpr (NL > 0) {
     if (wave >= NW) {
@@ -110,7 +121,7 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
       const int l = wave - NW;
       constexpr int GPL = (D + 63) / 64;  // gamma entries per lane
       PV r[NRP];
-      F u[NW * NB];
+      F u[NUT];
       float gv[GPL];
       auto gload = [&](int c) {
         const unsigned char *blk = blk_of(c);
@@ -118,10 +129,8 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
         for (int q = 0; q < NRP; ++q)
           r[q] = *reinterpret_cast<const PV *>(blk + piece_src(q));
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-#pragma unroll
-          for (int tt = 0; tt < NB; ++tt)
-            u[w * NB + tt] = F::ld_at(blk + ut_src(w, tt));
+        for (int i = 0; i < NUT; ++i)
+          u[i] = F::ld_at(blk + ut_src(i));
 #pragma unroll
         for (int q = 0; q < GPL; ++q)
           gv[q] = reinterpret_cast<const float *>(blk + L::GAM)[lane + 64 * q < D ? lane + 64 * q : D - 1];
@@ -131,7 +140,7 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
         for (int q = 0; q < NRP; ++q)
           *reinterpret_cast<PV *>(&sbuf[b][q * PB + lane * PW]) = r[q];
 #pragma unroll
-        for (int i = 0; i < NW * NB; ++i)
+        for (int i = 0; i < NUT; ++i)
           u[i].st(&sbuf[b][K::UTO + i * TB], lane);
 #pragma unroll
         for (int q = 0; q < GPL; ++q)
@@ -155,49 +164,80 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
     }
   }
 
-  // ---- compute wave: column tile j of the map
-  const int j = grp * NW + wave;
-  f32x4 s[NK];
+  // ---- compute wave: column tiles jb .. jb + CPW - 1 of one map
+  const int part = K::MERGED ? wave : gpart;  // 0: Psi, 1: Phi
+  const int jb = K::MERGED ? CPW * grp : grp * NW + wave;
+  const int ub = K::MERGED ? 0 : wave * NB;  // first staged Ut tile of this wave
+  f32x4 s[NK][CPW];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s[kk][i] = (part == 1 && kk == j && 4 * g + i == m) ? 1.f : 0.f;
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[kk][c][i] = (part == 1 && kk == jb + c && 4 * g + i == m) ? 1.f : 0.f;
 
-  // the products of one chunk from its staged buffer
+  // the products of one chunk from its staged buffer (each -W and Kbar^T
+  // fragment read once for the wave's CPW column tiles)
   constexpr bool PAIR_K = sizeof(IO) == 2 && NK % 2 == 0, PAIR_T = sizeof(IO) == 2 && NB % 2 == 0;
   auto step = [&](const unsigned char *sb) {
-    F sf[NK];
+    F sf[NK][CPW];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      sf[kk] = F::from(s[kk]);
-    F zf[NB];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        sf[kk][c] = F::from(s[kk][c]);
+    F zf[NB][CPW];
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
-      f32x4 z = (part == 0) ? F::ld(sb + K::UTO + (wave * NB + tt) * TB, lane).to_f32() : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 z[CPW];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        z[c] = (part == 0) ? F::ld(sb + K::UTO + (ub + c * NB + tt) * TB, lane).to_f32() : f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (PAIR_K) {
 #pragma unroll
-        for (int kp = 0; kp < NK / 2; ++kp)
-          mma32(z, F2::ld(sb + tile_off<IO, NK>(tt, 2 * kp, 0), lane), F2::make(sf[2 * kp], sf[2 * kp + 1]));
+        for (int kp = 0; kp < NK / 2; ++kp) {
+          const F2 w2 = F2::ld(sb + tile_off<IO, NK>(tt, 2 * kp, 0), lane);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            mma32(z[c], w2, F2::make(sf[2 * kp][c], sf[2 * kp + 1][c]));
+        }
       } else {
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-          mm_io(z, F::ld_at(sb + tile_off<IO, NK>(tt, kk, lane)), sf[kk]);
+        for (int kk = 0; kk < NK; ++kk) {
+          const F w1 = F::ld_at(sb + tile_off<IO, NK>(tt, kk, lane));
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            mm_io(z[c], w1, sf[kk][c]);
+        }
       }
-      zf[tt] = F::from(z);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        zf[tt][c] = F::from(z[c]);
     }
     const float *gam = reinterpret_cast<const float *>(sb + K::GMO);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      s[kk] *= *reinterpret_cast<const f32x4 *>(gam + 16 * kk + 4 * g);
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + 16 * kk + 4 * g);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        s[kk][c] *= gm;
       if constexpr (PAIR_T) {
 #pragma unroll
-        for (int tp = 0; tp < NB / 2; ++tp)
-          mma32(s[kk], F2::ld(sb + RB + tile_off<IO, NB>(kk, 2 * tp, 0), lane), F2::make(zf[2 * tp], zf[2 * tp + 1]));
+        for (int tp = 0; tp < NB / 2; ++tp) {
+          const F2 kb = F2::ld(sb + RB + tile_off<IO, NB>(kk, 2 * tp, 0), lane);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            mma32(s[kk][c], kb, F2::make(zf[2 * tp][c], zf[2 * tp + 1][c]));
+        }
       } else {
 #pragma unroll
-        for (int tt = 0; tt < NB; ++tt)
-          mm_io(s[kk], F::ld_at(sb + RB + tile_off<IO, NB>(kk, tt, lane)), zf[tt]);
+        for (int tt = 0; tt < NB; ++tt) {
+          const F kb = F::ld_at(sb + RB + tile_off<IO, NB>(kk, tt, lane));
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            mm_io(s[kk][c], kb, zf[tt][c]);
+        }
       }
     }
   };
@@ -225,7 +265,7 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
         }
 #pragma unroll
         for (int tt = 0; tt < NB; ++tt)
-          u[tt] = F::ld_at(blk + ut_src(wave, tt));
+          u[tt] = F::ld_at(blk + ut_src(wave * NB + tt));
         gv = reinterpret_cast<const float *>(blk + L::GAM)[threadIdx.x < D ? threadIdx.x : D - 1];
       };
       auto commit = [&]() {
@@ -256,8 +296,10 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out[(16 * kk + 4 * g + i) * D + 16 * j + m] = s[kk][i];
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[(16 * kk + 4 * g + i) * D + 16 * (jb + c) + m] = s[kk][c][i];
 }
 
 // One workgroup per (sequence, head, 16-column tile j of the state), one
@@ -353,7 +395,7 @@ template <typename IO, int D, int C>
 hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_t st) {
   typedef segmap_cfg<IO, D, C> K;
   const long units_pad = (static_cast<long>(a.num_seqs) * a.H + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_segmap_kernel<IO, D, C>), dim3(static_cast<unsigned>(units_pad * 2 * K::NSPL)),
+  hipLaunchKernelGGL((gdn2_segmap_kernel<IO, D, C>), dim3(static_cast<unsigned>(units_pad * K::NPART * K::NSPL)),
                      dim3(64 * (K::NW + K::NL)), 0, st, a, Phi, Psi);
   return hipGetLastError();
 }
