@@ -115,49 +115,45 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
 
   if constexpr (NL > 0) {
     if (wave >= NW) {
-      // ---- loader wave: chunks 1 + l, 1 + l + NL, ...
+      // ---- loader wave (bfloat16, MERGED): chunk c + 1 is copied into LDS
+      // buffer (c + 1) % 2 by loader (c + 1) mod NL while the compute waves
+      // take chunk c, with direct global -> LDS loads (16 bytes a lane; 4
+      // for a tail under 1 KB): the block's -W and Kbar^T regions byte for
+      // byte, the workgroup's Ut tiles of each row tile (one stored pair,
+      // or one tile when NK is odd), and gamma_C.  No registers hold the
+      // data, and the copy is waited for (vmcnt) before the barrier that
+      // hands the buffer over.
       if (nchunks == 0)
         return;  // no barrier is taken
       const int l = wave - NW;
-      constexpr int GPL = (D + 63) / 64;  // gamma entries per lane
-      PV r[NRP];
-      F u[NUT];
-      float gv[GPL];
-      auto gload = [&](int c) {
+      auto dma = [&](const unsigned char *src, unsigned char *dst, int n) {
+        int o = 0;
+        for (; o + 1024 <= n; o += 1024)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + o + 16 * lane),
+                                           (__attribute__((address_space(3))) void *)(dst + o), 16, 0, 0);
+        for (; o < n; o += 256)
+          if (o + 4 * lane < n)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + o + 4 * lane),
+                                             (__attribute__((address_space(3))) void *)(dst + o), 4, 0, 0);
+      };
+      auto stage = [&](int c, int bsel) {
         const unsigned char *blk = blk_of(c);
+        unsigned char *dst = &sbuf[bsel][0];
+        dma(blk + L::WN, dst, static_cast<int>(RB));
+        dma(blk + L::KB, dst + RB, static_cast<int>(RB));
 #pragma unroll
-        for (int q = 0; q < NRP; ++q)
-          r[q] = *reinterpret_cast<const PV *>(blk + piece_src(q));
-#pragma unroll
-        for (int i = 0; i < NUT; ++i)
-          u[i] = F::ld_at(blk + ut_src(i));
-#pragma unroll
-        for (int q = 0; q < GPL; ++q)
-          gv[q] = reinterpret_cast<const float *>(blk + L::GAM)[lane + 64 * q < D ? lane + 64 * q : D - 1];
+        for (int tt = 0; tt < NB; ++tt)
+          dma(blk + L::UT + tile_off<IO, NK>(tt, CPW * grp, 0), dst + K::UTO + static_cast<size_t>(tt) * CPW * TB,
+              static_cast<int>(CPW * TB));
+        dma(blk + L::GAM, dst + K::GMO, static_cast<int>(D * sizeof(float)));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       };
-      auto lstore = [&](int b) {
-#pragma unroll
-        for (int q = 0; q < NRP; ++q)
-          *reinterpret_cast<PV *>(&sbuf[b][q * PB + lane * PW]) = r[q];
-#pragma unroll
-        for (int i = 0; i < NUT; ++i)
-          u[i].st(&sbuf[b][K::UTO + i * TB], lane);
-#pragma unroll
-        for (int q = 0; q < GPL; ++q)
-          if (lane + 64 * q < D)
-            reinterpret_cast<float *>(&sbuf[b][K::GMO])[lane + 64 * q] = gv[q];
-      };
-      if (l == 0) {
-        gload(0);
-        lstore(0);
-      }
-      gload(l + 1 < last ? l + 1 : last);
-      lds_barrier();
+      if (l == 0)
+        stage(0, 0);
+      lds_barrier();  // chunk 0 is staged
       for (int i = 0; i < nchunks; ++i) {
-        if (i % NL == l && i + 1 < nchunks) {
-          lstore((i + 1) % 2);
-          gload(i + 1 + NL < last ? i + 1 + NL : last);
-        }
+        if (i + 1 < nchunks && (i + 1) % NL == l)
+          stage(i + 1, (i + 1) % 2);  // buffer (i + 1) % 2 was freed by the previous barrier
         lds_barrier();  // chunk i + 1 is staged, chunk i's buffer is free
       }
       return;
@@ -191,9 +187,20 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
       f32x4 z[CPW];
+      if (part != 0) {
 #pragma unroll
-      for (int c = 0; c < CPW; ++c)
-        z[c] = (part == 0) ? F::ld(sb + K::UTO + (ub + c * NB + tt) * TB, lane).to_f32() : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CPW; ++c)
+          z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else if constexpr (K::MERGED && CPW == 2) {
+        const F2 u2 = F2::ld(sb + K::UTO + static_cast<size_t>(tt) * 2 * TB, lane);  // row tile tt's stored pair
+        z[0] = u2.lo.to_f32();
+        z[1] = u2.hi.to_f32();
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+          z[c] = F::ld(sb + K::UTO + (K::MERGED ? static_cast<size_t>(tt) * CPW + c : static_cast<size_t>(ub + tt)) * TB,
+                       lane).to_f32();
+      }
       if constexpr (PAIR_K) {
 #pragma unroll
         for (int kp = 0; kp < NK / 2; ++kp) {
