@@ -176,8 +176,12 @@ def host_info() -> dict:
     except OSError:
         pass
     p = torch.cuda.get_device_properties(0)
-    return {"cpu_model": cpu, "host_cpus": os.cpu_count(), "gpu_name": p.name,
-            "gpu_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+    arch = getattr(p, "gcnArchName", "")
+    # the device name comes from libdrm's marketing-name table, which some
+    # hosts lack: then say so rather than print nothing
+    name = p.name or f"{arch.split(':')[0]} (no marketing-name table on this host)"
+    return {"cpu_model": cpu, "host_cpus": os.cpu_count(), "gpu_name": name,
+            "gpu_arch": arch, "compute_units": p.multi_processor_count,
             "gpu_memory_gib": round(p.total_memory / 2**30, 1)}
 
 

@@ -43,11 +43,17 @@ namespace gdn2 {
 // chunks).  Every workgroup of one (segment, head) sits on the same XCD,
 // whose L2 serves their common reads.
 // Grid: units_pad * NPART * NSPL workgroups, units_pad = N*H rounded up to 8.
-template <typename IO, int D, int C> struct segmap_cfg {
+// CW: column tiles per compute wave when merged (1 or 2; 2 needs NK even),
+// chosen at launch: two halve the workgroups, which pays once there are
+// enough of them to fill the compute units.
+template <typename IO, int D, int C, int CW> struct segmap_cfg {
   static constexpr int NK = D / 16, NB = C / 16;
   static constexpr bool PIPE = sizeof(IO) == 2;
-  static constexpr bool MERGED = PIPE;                          // both maps in one workgroup
-  static constexpr int CPW = (MERGED && NK % 2 == 0) ? 2 : 1;   // column tiles per compute wave
+  static constexpr bool MERGED = PIPE;                              // both maps in one workgroup
+  static constexpr int CPW = (MERGED && NK % 2 == 0 && CW == 2) ? 2 : 1;  // column tiles per compute wave
+  // staged Ut bytes per row tile (merged): the stored pair holding the
+  // wave's tiles, or the one tile when NK is odd (no pairs)
+  static constexpr size_t UTS = (NK % 2 == 0 ? 2 : 1) * frag<IO>::TILE_BYTES;
   static constexpr int NSPL = MERGED ? NK / CPW : 1;            // workgroups per (segment, head) and part
   static constexpr int NPART = MERGED ? 1 : 2;                  // parts (maps) in the grid
   static constexpr int NW = MERGED ? 2 : NK;                    // compute waves
@@ -58,15 +64,15 @@ template <typename IO, int D, int C> struct segmap_cfg {
   static constexpr int PW = RB % 1024 == 0 ? 16 : 8;                // bytes a lane copies per piece
   static constexpr size_t PB = 64 * PW;                              // bytes of one piece
   static constexpr int NRP = static_cast<int>(2 * RB / PB);          // pieces of the two regions
-  static constexpr int NUT = MERGED ? CPW * NB : NW * NB;           // staged Ut tiles
-  static constexpr size_t UTO = 2 * RB, GMO = 2 * RB + NUT * TB;     // Ut tiles, gamma_C
+  static constexpr int NUT = NW * NB;                               // staged Ut tiles (not merged)
+  static constexpr size_t UTO = 2 * RB, GMO = 2 * RB + (MERGED ? NB * UTS : NUT * TB);  // Ut tiles, gamma_C
   static constexpr size_t BUF = GMO + D * sizeof(float);
 };
 
-template <typename IO, int D, int C>
-__global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<IO, D, C>::NL)))
+template <typename IO, int D, int C, int CW>
+__global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C, CW>::NW + segmap_cfg<IO, D, C, CW>::NL)))
     gdn2_segmap_kernel(chunk_args a, float *Phi, float *Psi) {
-  typedef segmap_cfg<IO, D, C> K;
+  typedef segmap_cfg<IO, D, C, CW> K;
   constexpr int NB = C / 16, NK = D / 16, NW = K::NW, NSPL = K::NSPL, NL = K::NL, NRP = K::NRP, CPW = K::CPW,
                 NPART = K::NPART, NUT = K::NUT;
   typedef frag<IO> F;
@@ -141,10 +147,11 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
         unsigned char *dst = &sbuf[bsel][0];
         dma(blk + L::WN, dst, static_cast<int>(RB));
         dma(blk + L::KB, dst + RB, static_cast<int>(RB));
+        const int ucol = NK % 2 == 0 ? (CPW * grp) & ~1 : grp;  // first column tile of the staged Ut
 #pragma unroll
         for (int tt = 0; tt < NB; ++tt)
-          dma(blk + L::UT + tile_off<IO, NK>(tt, CPW * grp, 0), dst + K::UTO + static_cast<size_t>(tt) * CPW * TB,
-              static_cast<int>(CPW * TB));
+          dma(blk + L::UT + tile_off<IO, NK>(tt, ucol, 0), dst + K::UTO + static_cast<size_t>(tt) * K::UTS,
+              static_cast<int>(K::UTS));
         dma(blk + L::GAM, dst + K::GMO, static_cast<int>(D * sizeof(float)));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       };
@@ -191,14 +198,18 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C>::NW + segmap_cfg<I
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
           z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else if constexpr (K::MERGED && CPW == 2) {
-        const F2 u2 = F2::ld(sb + K::UTO + static_cast<size_t>(tt) * 2 * TB, lane);  // row tile tt's stored pair
-        z[0] = u2.lo.to_f32();
-        z[1] = u2.hi.to_f32();
+      } else if constexpr (K::MERGED && NK % 2 == 0) {
+        const F2 u2 = F2::ld(sb + K::UTO + static_cast<size_t>(tt) * K::UTS, lane);  // row tile tt's stored pair
+        if constexpr (CPW == 2) {
+          z[0] = u2.lo.to_f32();
+          z[1] = u2.hi.to_f32();
+        } else {
+          z[0] = ((grp & 1) ? u2.hi : u2.lo).to_f32();
+        }
       } else {
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
-          z[c] = F::ld(sb + K::UTO + (K::MERGED ? static_cast<size_t>(tt) * CPW + c : static_cast<size_t>(ub + tt)) * TB,
+          z[c] = F::ld(sb + K::UTO + (K::MERGED ? static_cast<size_t>(tt) : static_cast<size_t>(ub + tt)) * TB,
                        lane).to_f32();
       }
       if constexpr (PAIR_K) {
@@ -398,13 +409,26 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
   }
 }
 
-template <typename IO, int D, int C>
-hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_t st) {
-  typedef segmap_cfg<IO, D, C> K;
+template <typename IO, int D, int C, int CW>
+hipError_t launch_segmap_cw(const chunk_args &a, float *Phi, float *Psi, hipStream_t st) {
+  typedef segmap_cfg<IO, D, C, CW> K;
   const long units_pad = (static_cast<long>(a.num_seqs) * a.H + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_segmap_kernel<IO, D, C>), dim3(static_cast<unsigned>(units_pad * K::NPART * K::NSPL)),
+  hipLaunchKernelGGL((gdn2_segmap_kernel<IO, D, C, CW>), dim3(static_cast<unsigned>(units_pad * K::NPART * K::NSPL)),
                      dim3(64 * (K::NW + K::NL)), 0, st, a, Phi, Psi);
   return hipGetLastError();
+}
+
+// Two column tiles per wave once one tile per wave would need more than one
+// round of workgroups (two per compute unit); fewer units keep one tile per
+// wave and twice the workgroups.
+template <typename IO, int D, int C>
+hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_t st) {
+  constexpr int NK = D / 16;
+  if constexpr (sizeof(IO) == 2 && NK % 2 == 0) {
+    if (static_cast<long>(a.num_seqs) * a.H * NK > 512)
+      return launch_segmap_cw<IO, D, C, 2>(a, Phi, Psi, st);
+  }
+  return launch_segmap_cw<IO, D, C, 1>(a, Phi, Psi, st);
 }
 
 template <int D>
