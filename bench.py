@@ -320,6 +320,76 @@ def context_parallel(g, dev: dict, H: int, d: int, C: int, path: str) -> dict:
     return res
 
 
+def configs_table(g) -> dict:
+    """Every workload once (part of the oracle leg, ``--configs``): GPU time
+    (HIP-synchronised wall time per call after warm-up), parity against the
+    oracle (max |gpu - oracle| / max |oracle| of o and S_final, every
+    element) and the oracle's own time on the host's cores."""
+    import oracle
+    out = {}
+
+    def timed(fn, budget_s=0.3):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    fwd_cases = [("tiny_1x64x1_d16", None), ("small_2x512x4_d64", None), ("small_2x512x4_d64", "kda"),
+                 ("layer_8x4096x16_d128", None), ("packed_32768x16_d128", None)]
+    for name, variant in fwd_cases:
+        c = gi.WORKLOADS[name]
+        cu = None
+        if c.get("packed"):
+            lens = gi.packed_lengths(c["seed"])
+            cu = gi.cu_seqlens_from(lens)
+            inp = gi.make_chunk_inputs(1, c["T"], c["H"], c["dk"], c["dv"], c["dtype"], c["seed"], s0=c["s0"],
+                                       num_seqs=len(lens))
+        else:
+            inp = gi.make_chunk_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"], c["seed"], s0=c["s0"],
+                                       scalar_beta=(variant == "kda"))
+        dev = {x: inp[x].cuda() for x in NAMES}
+        if variant == "kda":  # b = w = beta per (token, head): the KDA input layout
+            dev = dict(dev, b=dev["b"][..., 0].contiguous(), w=dev["w"][..., 0].contiguous())
+        S0 = inp["S0"].cuda() if inp.get("S0") is not None else None
+        cud = cu.cuda() if cu is not None else None
+        fn = lambda: g.chunk_fwd(*(dev[x] for x in NAMES), S0=S0, cu_seqlens=cud, chunk=c["chunk"])
+        sec = timed(fn)
+        o, Sf = fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        o_ref, S_ref = oracle.fwd(*(inp[x] for x in NAMES), S0=inp.get("S0"), cu_seqlens=cu)
+        t_or = time.perf_counter() - t0
+        tok = int(o.shape[0] * o.shape[1])
+        key = name + ("_kda_gates" if variant else "")
+        out[key] = {"dtype": c["dtype"], "gpu_ms": round(sec * 1e3, 4), "tokens_per_s": round(tok / sec, 1),
+                    "tflops": round(flops_per_token_head(c["dk"], c["chunk"]) * tok * c["H"] / sec / 1e12, 3),
+                    "err_o": rel_err(o.float().cpu().numpy(), o_ref), "err_S": rel_err(Sf.cpu().numpy(), S_ref),
+                    "oracle_s": round(t_or, 3)}
+        del dev, o, Sf
+    c = gi.WORKLOADS["decode_256x16_d128"]
+    dd = gi.make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], "bf16", c["seed"], steps=c["steps"])
+    S_gpu = dd["S"].cuda()
+    ddev = {x: dd[x].cuda() for x in NAMES}
+    outs = [g.decode_step(*(ddev[x][t] for x in NAMES), S_gpu) for t in range(c["steps"])]
+    torch.cuda.synchronize()
+    S_ref = dd["S"].double().numpy()
+    eo, t0 = 0.0, time.perf_counter()
+    for t in range(c["steps"]):
+        o_ref, S_ref = oracle.decode(*(dd[x][t] for x in NAMES), S_ref)
+        eo = max(eo, rel_err(outs[t].float().cpu().numpy(), o_ref))
+    t_or = (time.perf_counter() - t0) / c["steps"]
+    out["decode_256x16_d128"] = {"dtype": "bf16", "steps": c["steps"], "err_o_max_over_steps": eo,
+                                 "err_S_after_steps": rel_err(S_gpu.cpu().numpy(), S_ref),
+                                 "oracle_ms_per_step": round(t_or * 1e3, 2)}
+    out["oracle_cores"] = oracle.max_threads()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +403,8 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "two_pass"],
                     help="chunked kernels to time (default: the library's own choice)")
+    ap.add_argument("--configs", action="store_true",
+                    help="also run every workload once against the oracle (GPU time, error, oracle time)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -638,6 +710,8 @@ def main() -> int:
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, H, args.cpu_budget)
+        if args.configs:
+            out["configs"] = configs_table(g)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
