@@ -58,17 +58,24 @@ def flops_per_token_head(d: int, C: int) -> float:
 
 # Algorithmic HBM bytes per token and head (bf16 elements, d = 128):
 #   path : read q, k, v, alpha, b, w once, write o once
-#   prep : read the six inputs, write -W, Q', Kbar^T, Ut, O_intra (bf16) and
+#   prep : read the six inputs, write -W, Q', Kbar^T, Ut (bf16), the lower
+#          triangle of P (C/16 (C/16 + 1) / 2 tiles of 16 x 16 per chunk) and
 #          gamma_C (fp32, one d-vector per chunk)
-#   scan : read -W, Q', Kbar^T, Ut, O_intra and gamma_C, write o
+#   scan : read -W, Q', Kbar^T, Ut, P and gamma_C, write o
 #   fused: the path itself (inputs once, o once)
+def p_bytes_per_token_head(C: int, elem: int = 2) -> float:
+    nb = C // 16
+    return nb * (nb + 1) / 2 * 256 * elem / C
+
+
 def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
     gam = d * 4 / C
+    pb = p_bytes_per_token_head(C, elem)
     return {
         "path": 6 * d * elem + d * elem,
         "chunk_fused": 6 * d * elem + d * elem,
-        "chunk_prep": 6 * d * elem + 5 * d * elem + gam,
-        "chunk_scan": 5 * d * elem + gam + d * elem,
+        "chunk_prep": 6 * d * elem + 4 * d * elem + pb + gam,
+        "chunk_scan": 4 * d * elem + pb + gam + d * elem,
     }
 
 
@@ -76,16 +83,17 @@ def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
 # elements; a state crosses HBM as two fragment-tile copies of d*d elements
 # per chunk, the same bytes as one float32 copy):
 #   path         : read q, k, v, alpha, b, w and dL/do once, write six gradients
-#   chunk_states : read -W, Q', Kbar^T, Ut and gamma_C, write the entering state
+#   chunk_states : read -W, Q', Kbar^T, P, Ut and gamma_C, write the entering state
 #   bwd_dstate   : read -W, Q', Kbar^T, gamma_C and dL/do, write the leaving-state gradient
 #   bwd_grad     : read the six inputs, dL/do, the state and its gradient, write six gradients
 def bwd_bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
     gam = d * 4 / C
     st = d * d * 4 / C
+    pb = p_bytes_per_token_head(C, elem)
     return {
         "path": 7 * d * elem + 6 * d * elem,
-        "chunk_prep": 6 * d * elem + 5 * d * elem + gam,
-        "chunk_states": 4 * d * elem + gam + st,
+        "chunk_prep": 6 * d * elem + 4 * d * elem + pb + gam,
+        "chunk_states": 4 * d * elem + pb + gam + st,
         "bwd_dstate": 4 * d * elem + gam + st,
         "bwd_grad": 7 * d * elem + 2 * st + 6 * d * elem,
     }

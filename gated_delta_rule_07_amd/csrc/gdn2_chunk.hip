@@ -60,10 +60,16 @@ gdn2_chunk_prep_kernel(chunk_args a) {
   F af[NB];
   wy_products<IO, D, C>(sm, op, I, lane, af);
   wy_inverse<IO, D, C>(sm, af, I, lane, eye);
+  // P's tiles of this wave's rows (complete in LDS since wy_inverse's
+  // barriers), for the scan to form O_intra = P Ut
+#pragma unroll
+  for (int J = 0; J < NB; ++J)
+    if (J <= I)
+      F::ld(sm.pr[tri_index(I, J)], lane).st(blk + L::P + static_cast<size_t>(tri_index(I, J)) * L::TB, lane);
   if (owner) {
     wy_tp<IO, C> tp;
     wy_load_tp<IO, D, C>(sm, lane, tp);
-    F ut[CTW][NB], oi[CTW][NB];
+    F ut[CTW][NB];
 #pragma unroll
     for (int j = 0; j < CTW; ++j) {
       const int ct = ct0 + j;
@@ -73,27 +79,21 @@ gdn2_chunk_prep_kernel(chunk_args a) {
       for (int J = 0; J < NB; ++J)
         uc_j[J] = ucol[J][j];
       f32x4 u4[NB], o4[NB];
-      wy_uo<IO, C, true>(tp, uc_j, u4, o4);
+      wy_uo<IO, C, true, false>(tp, uc_j, u4, o4);
 #pragma unroll
-      for (int I2 = 0; I2 < NB; ++I2) {
+      for (int I2 = 0; I2 < NB; ++I2)
         ut[j][I2] = F::from(u4[I2]);
-        oi[j][I2] = F::from(o4[I2]);
-      }
     }
 #pragma unroll
     for (int I2 = 0; I2 < NB; ++I2) {
       if constexpr (CTW % 2 == 0 && NK % 2 == 0) {
 #pragma unroll
-        for (int j = 0; j < CTW; j += 2) {  // ct0 is even: one 16-byte store per tile pair
+        for (int j = 0; j < CTW; j += 2)  // ct0 is even: one 16-byte store per tile pair
           frag2<IO>::make(ut[j][I2], ut[j + 1][I2]).st(blk + L::UT + tile_off<IO, NK>(I2, ct0 + j, 0), lane);
-          frag2<IO>::make(oi[j][I2], oi[j + 1][I2]).st(blk + L::OI + tile_off<IO, NK>(I2, ct0 + j, 0), lane);
-        }
       } else {
 #pragma unroll
-        for (int j = 0; j < CTW; ++j) {
+        for (int j = 0; j < CTW; ++j)
           ut[j][I2].st_at(blk + L::UT + tile_off<IO, NK>(I2, ct0 + j, lane));
-          oi[j][I2].st_at(blk + L::OI + tile_off<IO, NK>(I2, ct0 + j, lane));
-        }
       }
     }
   }
@@ -103,9 +103,9 @@ gdn2_chunk_prep_kernel(chunk_args a) {
 // NGRP = NK / NT workgroups of NT tiles each (NT is chosen at launch from the
 // number of units), each with NCW compute waves of CPW 16-column state slices
 // and NLW loader waves.  Each LDS buffer holds the SHARED part of one chunk's
-// block and, when a tile row of the workgroup's columns is a whole number of
-// KB (UO_LDS), the workgroup's Ut and O_intra tiles (rows tt, TF tiles each:
-// its NT tiles rounded out to whole stored pairs).
+// block (P's tiles included) and, when a tile row of the workgroup's columns
+// is a whole number of KB (UO_LDS), the workgroup's Ut tiles (rows tt, TF
+// tiles each: its NT tiles rounded out to whole stored pairs).
 template <typename IO, int D, int C, int NT> struct scan_cfg {
   typedef blk_layout<IO, D, C> L;
   static constexpr int NB = C / 16, NK = D / 16;
@@ -120,7 +120,7 @@ template <typename IO, int D, int C, int NT> struct scan_cfg {
   static constexpr size_t RB = TF * L::TB;           // one staged tile row of Ut
   static constexpr bool UO_LDS = RB % 1024 == 0;
   static constexpr int RPP = static_cast<int>(RB / 1024);
-  static constexpr size_t BUF = L::SHARED + (UO_LDS ? 2 * NB * RB : 0);
+  static constexpr size_t BUF = L::SHARED + (UO_LDS ? NB * RB : 0);
   static constexpr int NPS = static_cast<int>(L::SHARED / 1024);
   static constexpr int NPIECE = static_cast<int>(BUF / 1024);  // 1 KB per wave load
   static constexpr int NLW = NPIECE < 4 ? NPIECE : (NPIECE + 12) / 13 > 4 ? (NPIECE + 12) / 13 : 4;
@@ -198,15 +198,14 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
     if (nchunks == 0)
       return;  // the compute waves take no barrier either
     const int lw = wave - NCW;
-    // byte offset in the block of LDS piece p (SHARED, then Ut rows, then O_intra rows)
-    // (Ut / O_intra pieces exist only when UO_LDS, i.e. RPP >= 1)
+    // byte offset in the block of LDS piece p (SHARED, then Ut rows; the Ut
+    // pieces exist only when UO_LDS, i.e. RPP >= 1)
     auto piece_src = [&](int p) -> size_t {
       constexpr int R = RPP > 0 ? RPP : 1;
       if (p < NPS)
         return static_cast<size_t>(p) * 1024;
       const int q = p - NPS;
-      const int region = q / (NB * R), rem = q % (NB * R);
-      return (region ? L::OI : L::UT) + tile_off<IO, NK>(rem / R, vtf, 0) + static_cast<size_t>(rem % R) * 1024;
+      return L::UT + tile_off<IO, NK>(q / R, vtf, 0) + static_cast<size_t>(q % R) * 1024;
     };
     int src_off[PPW];
 #pragma unroll
@@ -287,44 +286,52 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
       for (int j = 0; j < CPW; ++j)
         S[kk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Ut and O_intra tiles of chunk c from global memory (when they are not
-  // staged in LDS; past the last chunk: the last again)
-  auto tload = [&](int c, F(&u)[NB][CPW], F(&o)[NB][CPW]) {
+  // Ut tiles of chunk c from global memory (when they are not staged in
+  // LDS; past the last chunk: the last again)
+  auto tload = [&](int c, F(&u)[NB][CPW]) {
     const unsigned char *blk = blk_of(c < nchunks ? c : nchunks - 1);
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
+      for (int j = 0; j < CPW; ++j)
         u[tt][j] = F::ld_at(blk + L::UT + tile_off<IO, NK>(tt, vt0 + j, lane));
-        o[tt][j] = F::ld_at(blk + L::OI + tile_off<IO, NK>(tt, vt0 + j, lane));
-      }
   };
-  // Ut and O_intra tiles of row tt from an LDS buffer
-  auto uo_row_lds = [&](const unsigned char *sb, int tt, F(&u)[CPW], F(&o)[CPW]) {
-    const unsigned char *ur = sb + L::SHARED + tt * RB;
-    const unsigned char *orow = sb + L::SHARED + (NB + tt) * RB;
-    if constexpr (CPW % 2 == 0) {  // vt0 - vtf is even
+  // Ut tile (row tile J, column slice j): from an LDS buffer (UO_LDS), read
+  // at its use, or from the registers tload filled
+  auto u_tile = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], int J, int j) -> F {
+    if constexpr (K::UO_LDS)
+      return F::ld_at(sb + L::SHARED + J * RB + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
+    else
+      return ucur[J][j];
+  };
+  // O_intra^T of row tile tt, column slice j: sum over J <= tt of
+  // Ut(J)^T P(tt, J)^T (operands swapped as in the prep: RowFrag(O_intra)),
+  // in the product shape of the rest of the output chain -- PAIR: 16x16x32
+  // over pairs of J (a missing partner is a zero tile), else single tiles.
+  auto o_intra = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], int tt, int j, auto pair) -> f32x4 {
+    constexpr bool PAIR = decltype(pair)::value;
+    auto ptile = [&](int J) { return F::ld(sb + L::P + static_cast<size_t>(tri_index(tt, J)) * L::TB, lane); };
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (PAIR) {
 #pragma unroll
-      for (int j = 0; j < CPW; j += 2) {
-        const F2 u2 = F2::ld(ur + tile_off<IO, TF>(0, vt0 + j - vtf, 0), lane);
-        const F2 o2 = F2::ld(orow + tile_off<IO, TF>(0, vt0 + j - vtf, 0), lane);
-        u[j] = u2.lo;
-        u[j + 1] = u2.hi;
-        o[j] = o2.lo;
-        o[j + 1] = o2.hi;
+      for (int J = 0; J < NB; J += 2) {
+        if (J <= tt) {
+          const bool two = J + 1 <= tt && J + 1 < NB;
+          mma32(o, F2::make(u_tile(sb, ucur, J, j), two ? u_tile(sb, ucur, J + 1, j) : F::zero()),
+                F2::make(ptile(J), two ? ptile(J + 1) : F::zero()));
+        }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        u[j] = F::ld_at(ur + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
-        o[j] = F::ld_at(orow + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
-      }
+      for (int J = 0; J < NB; ++J)
+        if (J <= tt)
+          mm_io(o, u_tile(sb, ucur, J, j), ptile(J));
     }
+    return o;
   };
 
   // One chunk: products, o stores (rows < len unless FULL) and state update.
-  auto chunk_step = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], const F(&ocur)[NB][CPW], long t0,
-                        int len, int c, auto full) {
+  auto chunk_step = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], long t0, int len, int c, auto full) {
     constexpr bool FULL = decltype(full)::value;
     if constexpr (ST) {
       typedef state_tiles<IO, D> ST_;
@@ -360,29 +367,19 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
       f32x4 z[NB][CPW], ot[NB][CPW];
 #pragma unroll
       for (int tt = 0; tt < NB; ++tt) {
-        F ut[CPW], oi[CPW];
-        if constexpr (K::UO_LDS) {
-          uo_row_lds(sb, tt, ut, oi);
-        } else {
-#pragma unroll
-          for (int j = 0; j < CPW; ++j) {
-            ut[j] = ucur[tt][j];
-            oi[j] = ocur[tt][j];
-          }
-        }
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
+          const F ut = u_tile(sb, ucur, tt, j);
           if constexpr (sizeof(IO) == 2) {
-            // start from Ut and O_intra^T with an identity product instead of
-            // unpacking bf16 on the vector ALU (which the products wait for);
-            // same product shape as the rest of the chain (see mma32)
+            // start from Ut with an identity product instead of unpacking
+            // bf16 on the vector ALU (which the products wait for); same
+            // product shape as the rest of the chain (see mma32)
             z[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ot[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            mma32(z[tt][j], F2::make(eye, F::zero()), F2::make(ut[j], ut[j]));
-            mma32(ot[tt][j], F2::make(eye, F::zero()), F2::make(oi[j], oi[j]));
+            mma32(z[tt][j], F2::make(eye, F::zero()), F2::make(ut, ut));
+            ot[tt][j] = o_intra(sb, ucur, tt, j, std::true_type{});
           } else {
-            z[tt][j] = ut[j].to_f32();
-            ot[tt][j] = oi[j].to_f32();
+            z[tt][j] = ut.to_f32();
+            ot[tt][j] = o_intra(sb, ucur, tt, j, std::false_type{});
           }
         }
       }
@@ -485,34 +482,24 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
         else
           su_load(0, 0);
         f32x4 z[CPW], ot[CPW];
-        F ut[CPW], oi[CPW];
-        if constexpr (K::UO_LDS) {
-          uo_row_lds(sb, tt, ut, oi);
-        } else {
-  #pragma unroll
-          for (int j = 0; j < CPW; ++j) {
-            ut[j] = ucur[tt][j];
-            oi[j] = ocur[tt][j];
-          }
-        }
   #pragma unroll
         for (int j = 0; j < CPW; ++j) {
+          const F ut = u_tile(sb, ucur, tt, j);
           if constexpr (sizeof(IO) == 2) {
-            // start from Ut and O_intra^T with an identity product instead of
-            // unpacking bf16 on the vector ALU (which the products wait for);
-            // same product shape as the rest of the chain (see mma32)
+            // start from Ut with an identity product instead of unpacking
+            // bf16 on the vector ALU (which the products wait for); same
+            // product shape as the rest of the chain (see mma32)
             z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (NK % 2 == 0) {
-              mma32(z[j], F2::make(eye, F::zero()), F2::make(ut[j], ut[j]));
-              mma32(ot[j], F2::make(eye, F::zero()), F2::make(oi[j], oi[j]));
+              mma32(z[j], F2::make(eye, F::zero()), F2::make(ut, ut));
+              ot[j] = o_intra(sb, ucur, tt, j, std::true_type{});
             } else {
-              mma16(z[j], eye, ut[j]);
-              mma16(ot[j], eye, oi[j]);
+              mma16(z[j], eye, ut);
+              ot[j] = o_intra(sb, ucur, tt, j, std::false_type{});
             }
           } else {
-            z[j] = ut[j].to_f32();
-            ot[j] = oi[j].to_f32();
+            z[j] = ut.to_f32();
+            ot[j] = o_intra(sb, ucur, tt, j, std::false_type{});
           }
         }
         if constexpr (NK % 2 == 0) {
@@ -576,21 +563,21 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
   };
 
   if (nchunks > 0) {
-    F ucur[NB][CPW], ocur[NB][CPW];
+    F ucur[NB][CPW];
     if constexpr (!K::UO_LDS)
-      tload(0, ucur, ocur);
+      tload(0, ucur);
     lds_barrier();  // chunk 0 is in buffer 0
     for (int c = 0; c < nchunks; ++c) {
       const unsigned char *sb = sbuf[c % NBUF];
       const long t0 = tstart + static_cast<long>(c) * C;
       const int len = (tend - t0) < C ? static_cast<int>(tend - t0) : C;
-      F unxt[NB][CPW], onxt[NB][CPW];
+      F unxt[NB][CPW];
       if constexpr (!K::UO_LDS)
-        tload(c + 1, unxt, onxt);
+        tload(c + 1, unxt);
       if (len == C)
-        chunk_step(sb, ucur, ocur, t0, len, c, std::true_type{});
+        chunk_step(sb, ucur, t0, len, c, std::true_type{});
       else
-        chunk_step(sb, ucur, ocur, t0, len, c, std::false_type{});
+        chunk_step(sb, ucur, t0, len, c, std::false_type{});
       if constexpr (NBUF == 1)
         lds_barrier();  // done with the only buffer
       lds_barrier();    // chunk c + 1 is in LDS
@@ -598,10 +585,8 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
 #pragma unroll
         for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
-          for (int j = 0; j < CPW; ++j) {
+          for (int j = 0; j < CPW; ++j)
             ucur[tt][j] = unxt[tt][j];
-            ocur[tt][j] = onxt[tt][j];
-          }
       }
     }
   }

@@ -23,7 +23,7 @@ template <typename IO, int D, int C, int NG> struct fused_cfg {
   static constexpr int NB = C / 16, NK = D / 16;
   static constexpr int CTK = NK / NB;         // dk tiles of W, Q' per wave
   static constexpr int NVW = NK / (NG * NB);  // dv tiles (state columns) per wave
-  static constexpr size_t LDS = sizeof(wy_smem<IO, D, C>) + blk_layout<IO, D, C>::SHARED;
+  static constexpr size_t LDS = sizeof(wy_smem<IO, D, C>) + blk_layout<IO, D, C>::SHARED0;
   static constexpr bool OK = NK % NB == 0 && NK % (NG * NB) == 0 && NVW >= 1 && LDS <= 160 * 1024;
 };
 
@@ -38,7 +38,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_fused_kernel(chunk_args a)
   typedef blk_layout<IO, D, C> L;
   __shared__ wy_smem<IO, D, C> sm;
   // -W, Q', Kbar^T and gamma_C of the current chunk, in the block layout
-  __shared__ __attribute__((aligned(16))) unsigned char tiles[L::SHARED];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[L::SHARED0];
 
   const int x = blockIdx.x;
   const int xcd = x & 7, s8 = x >> 3;

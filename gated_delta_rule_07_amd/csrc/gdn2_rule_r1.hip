@@ -28,11 +28,15 @@
 
 namespace gdn2 {
 
+// The R1 block: the default block's -W', Q'', Ebar^T and gamma_C slots (its
+// first SHARED0 bytes), then -Ut' (ColFrag), O'' (RowFrag) and N.
 template <typename IO, int D, int C> struct r1_layout {
   typedef blk_layout<IO, D, C> L;
   static constexpr int NB = C / 16, NK = D / 16;
   static constexpr size_t TB = L::TB;
-  static constexpr size_t NC = L::OI + NB * NK * TB;  // dk tiles x dv tiles: ColFrag(N)
+  static constexpr size_t UT = L::SHARED0;            // rows tt, dv tiles paired: ColFrag(-Ut')
+  static constexpr size_t OI = UT + NB * NK * TB;     // rows tt, dv tiles paired: RowFrag(O'')
+  static constexpr size_t NC = OI + NB * NK * TB;     // dk tiles x dv tiles: ColFrag(N)
   static constexpr size_t BYTES = align256(NC + NK * NK * TB);
 };
 
@@ -282,8 +286,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_r1_prep_kernel(chunk_args 
       r1_uo<IO, D, C>(tp, sx, lane, uc_j, utn, oi);
 #pragma unroll
       for (int I2 = 0; I2 < NB; ++I2) {
-        utn[I2].st_at(blk + L::UT + tile_off<IO, NK>(I2, ct, lane));
-        oi[I2].st_at(blk + L::OI + tile_off<IO, NK>(I2, ct, lane));
+        utn[I2].st_at(blk + R::UT + tile_off<IO, NK>(I2, ct, lane));
+        oi[I2].st_at(blk + R::OI + tile_off<IO, NK>(I2, ct, lane));
       }
       // N tile (kk, ct) = sum over the chunk's tokens of Kbar^T U
 #pragma unroll
@@ -344,8 +348,8 @@ __global__ void __launch_bounds__(64 * (r1_scan_cfg<IO, D, C>::WPG)) gdn2_r1_sca
     F zf[NB];
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
-      f32x4 z = F::ld_at(blk + L::UT + tile_off<IO, NK>(tt, j, lane)).to_f32();
-      f32x4 ot = F::ld_at(blk + L::OI + tile_off<IO, NK>(tt, j, lane)).to_f32();
+      f32x4 z = F::ld_at(blk + R::UT + tile_off<IO, NK>(tt, j, lane)).to_f32();
+      f32x4 ot = F::ld_at(blk + R::OI + tile_off<IO, NK>(tt, j, lane)).to_f32();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         mm_io(z, F::ld_at(blk + L::WN + tile_off<IO, NK>(tt, kk, lane)), sf[kk]);

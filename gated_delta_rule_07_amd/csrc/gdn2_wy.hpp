@@ -131,22 +131,26 @@ template <> struct raw4<bf16_t> {
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Per (chunk, head) block of intermediates, all tiles fragment-ordered.  The
-// first SHARED bytes (-W, Q', Kbar^T, gamma_C) are what every column slice of
-// the state scan needs; the scan copies them to LDS as one block.  A operands
-// of the scan are stored with their 16-wide k tiles paired (tile_off), so one
-// 16-byte load yields a 16x16x32 operand.  The fused kernel keeps the same
-// SHARED layout in LDS.
+// first SHARED bytes (-W, Q', Kbar^T, gamma_C and the lower-triangular tiles
+// of P) are what every column slice of the state scan needs; the scan copies
+// them to LDS as one block and forms O_intra = P Ut itself from P and the Ut
+// tiles it reads anyway (P's tiles are a third of O_intra's bytes, so the
+// block is 13 % smaller for bf16, d = 128, C = 64).  A operands of the scan
+// are stored with their 16-wide k tiles paired (tile_off), so one 16-byte
+// load yields a 16x16x32 operand.  The fused kernel keeps the first SHARED0
+// bytes in LDS.
 template <typename IO, int D, int C> struct blk_layout {
-  static constexpr int NB = C / 16, NK = D / 16;
+  static constexpr int NB = C / 16, NK = D / 16, NT = NB * (NB + 1) / 2;
   static constexpr size_t TB = frag<IO>::TILE_BYTES;
   static constexpr size_t WN = 0;                   // rows tt, k tiles over dk: RowFrag(-W)
   static constexpr size_t QP = WN + NB * NK * TB;   // rows tt, k tiles over dk: RowFrag(Q')
   static constexpr size_t KB = QP + NB * NK * TB;   // rows dk tile, k tiles over tokens: RowFrag(Kbar^T)
   static constexpr size_t GAM = KB + NK * NB * TB;  // [D] float gamma_C
-  static constexpr size_t SHARED = (GAM + D * sizeof(float) + 1023) & ~static_cast<size_t>(1023);
+  static constexpr size_t SHARED0 = (GAM + D * sizeof(float) + 1023) & ~static_cast<size_t>(1023);
+  static constexpr size_t P = SHARED0;              // NT tiles RowFrag(P_IJ), J <= I, at tri_index(I, J)
+  static constexpr size_t SHARED = (P + NT * TB + 1023) & ~static_cast<size_t>(1023);
   static constexpr size_t UT = SHARED;              // rows tt, dv tiles paired: ColFrag(Ut)
-  static constexpr size_t OI = UT + NB * NK * TB;   // rows tt, dv tiles paired: RowFrag(O_intra)
-  static constexpr size_t BYTES = align256(OI + NB * NK * TB);
+  static constexpr size_t BYTES = align256(UT + NB * NK * TB);
 };
 
 // chunk slot -> (sequence, first token (flat index), valid length)
@@ -927,8 +931,8 @@ __device__ __forceinline__ void wy_wq(const wy_smem<IO, D, C> &sm, const wy_tp<I
 // float accumulators (ut[I], oi[I] for the 16 rows of sub-block I).  ut is
 // ColFrag; oi is ColFrag, or RowFrag when OI_ROW (computed as O_intra^T =
 // Ut^T P^T by swapping the operands, which puts 4 consecutive columns of one
-// row in each lane).
-template <typename IO, int C, bool OI_ROW = false>
+// row in each lane).  Without WITH_O only Ut is formed (oi untouched).
+template <typename IO, int C, bool OI_ROW = false, bool WITH_O = true>
 __device__ __forceinline__ void wy_uo(const wy_tp<IO, C> &tp, const frag<IO> (&ucol)[C / 16],
                                       f32x4 (&ut)[C / 16], f32x4 (&oi)[C / 16]) {
   constexpr int NB = C / 16;
@@ -943,6 +947,8 @@ __device__ __forceinline__ void wy_uo(const wy_tp<IO, C> &tp, const frag<IO> (&u
     ut[I2] = u;
     uc[I2] = F::from(u);
   }
+  if constexpr (!WITH_O)
+    return;
 #pragma unroll
   for (int I2 = 0; I2 < NB; ++I2) {
     f32x4 o = {0.f, 0.f, 0.f, 0.f};

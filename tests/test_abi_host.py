@@ -81,9 +81,11 @@ def test_fwd_rejects_before_launch(L):
 
 def test_workspace_bytes(L):
     f = L.gdn2_chunk_fwd_workspace_bytes
-    # the layer workload: 8 x 64 chunks x 16 heads of bf16 intermediates, plus the table
+    # the layer workload: 8 x 64 chunks x 16 heads of bf16 intermediates, 70 KiB
+    # each: -W, Q', Kbar^T (16 KiB each), gamma_C and P's 10 tiles (to 54 KiB
+    # in whole KiB), Ut (16 KiB); in front of them the 256-byte chunk table
     w = f(8, 4096, 16, 128, 128, 0, 64, BF16)
-    assert 8 * 64 * 16 * 80 * 1024 <= w <= 8 * 64 * 16 * 82 * 1024 + 4096
+    assert w == 256 + 8 * 64 * 16 * 70 * 1024
     assert f(8, 4096, 16, 128, 64, 0, 64, BF16) == 0
     assert f(1, 100, 2, 64, 64, 5, 16, F32) >= f(1, 100, 2, 64, 64, 0, 16, F32)
 
@@ -254,7 +256,7 @@ def test_workspace_bytes_rule_r1(L):
     L.gdn2_chunk_fwd_workspace_bytes_flags.argtypes = [ctypes.c_int] * 8 + [ctypes.c_uint32]
     L.gdn2_chunk_fwd_workspace_bytes_flags.restype = ctypes.c_size_t
     assert fl(8, 4096, 16, 128, 128, 0, 64, BF16, 0) == f(8, 4096, 16, 128, 128, 0, 64, BF16)
-    # rule R1: per chunk-head the default block plus N (dk x dv, bf16): 32 KiB more
+    # rule R1: per chunk-head -W', Q'', Ebar^T, gamma_C, -Ut', O'' and N (dk x dv, bf16): over 32 KiB more
     r1 = fl(8, 4096, 16, 128, 128, 0, 64, BF16, 1 << 7)
     assert r1 >= f(8, 4096, 16, 128, 128, 0, 64, BF16) + 8 * 64 * 16 * 32 * 1024 - 4096
     assert fl(1, 100, 2, 128, 128, 0, 64, F32, 1 << 7) == 0      # not built
