@@ -105,12 +105,14 @@ gdn2_chunk_prep_kernel(chunk_args a) {
 // and NLW loader waves.  Each LDS buffer holds the SHARED part of one chunk's
 // block (P's tiles included) and, when a tile row of the workgroup's columns
 // is a whole number of KB (UO_LDS), the workgroup's Ut tiles (rows tt, TF
-// tiles each: its NT tiles rounded out to whole stored pairs).
-template <typename IO, int D, int C, int NT> struct scan_cfg {
+// tiles each: its NT tiles rounded out to whole stored pairs).  R1: the
+// block of rule R1, whose shared part ends at SHARED0 (no P) and whose -Ut'
+// and O'' rows are both staged; one column tile per compute wave.
+template <typename IO, int D, int C, int NT, bool R1 = false> struct scan_cfg {
   typedef blk_layout<IO, D, C> L;
   static constexpr int NB = C / 16, NK = D / 16;
   static_assert(NT >= 1 && NT <= NK && NK % NT == 0, "tiles per workgroup");
-  static constexpr int CPW = (sizeof(IO) == 2 && NT >= 2) ? 2 : 1;
+  static constexpr int CPW = (sizeof(IO) == 2 && NT >= 2 && !R1) ? 2 : 1;
   static constexpr int NCW = NT / CPW;
   static constexpr int NGRP = NK / NT;
   static constexpr int NTW = NT;                     // dv tiles per workgroup
@@ -120,8 +122,11 @@ template <typename IO, int D, int C, int NT> struct scan_cfg {
   static constexpr size_t RB = TF * L::TB;           // one staged tile row of Ut
   static constexpr bool UO_LDS = RB % 1024 == 0;
   static constexpr int RPP = static_cast<int>(RB / 1024);
-  static constexpr size_t BUF = L::SHARED + (UO_LDS ? NB * RB : 0);
-  static constexpr int NPS = static_cast<int>(L::SHARED / 1024);
+  static constexpr size_t SHR = R1 ? L::SHARED0 : L::SHARED;  // shared part of the block
+  static constexpr int NRW = R1 ? 2 : 1;                        // staged row regions: Ut (and O'')
+  static_assert(!R1 || UO_LDS, "rule R1 stages its -Ut' and O'' rows");
+  static constexpr size_t BUF = SHR + (UO_LDS ? NRW * NB * RB : 0);
+  static constexpr int NPS = static_cast<int>(SHR / 1024);
   static constexpr int NPIECE = static_cast<int>(BUF / 1024);  // 1 KB per wave load
   static constexpr int NLW = NPIECE < 4 ? NPIECE : (NPIECE + 12) / 13 > 4 ? (NPIECE + 12) / 13 : 4;
   static constexpr int PPW = (NPIECE + NLW - 1) / NLW;         // pieces per loader wave
@@ -151,10 +156,18 @@ template <typename IO, int D, int C, int NT> struct scan_cfg {
 // With ST (states mode, used by the backward) the kernel writes, instead of
 // o, the state entering every chunk to a.states (chunk slot order, one
 // state_tiles block per chunk-head: fragment tiles of the I/O type).
-template <typename IO, int D, int C, int NT, bool ST = false>
-__global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<IO, D, C, NT>::NLW))
+// With R1 it scans the blocks of rule R1 (r1_layout): O starts from the
+// stored O'' instead of P Ut, and the update adds the chunk's N tiles, which
+// each compute wave reads from the block at the start of the chunk:
+//   Z = -Ut' - W' S,  O = Q'' S + O'',  S <- Diag(gamma_C) S + Ebar^T Z + N.
+template <typename IO, int D, int C, int NT, bool ST = false, bool R1 = false>
+__global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1>::NCW + scan_cfg<IO, D, C, NT, R1>::NLW))
     gdn2_chunk_scan_kernel(chunk_args a) {
-  typedef scan_cfg<IO, D, C, NT> K;
+  typedef scan_cfg<IO, D, C, NT, R1> K;
+  typedef r1_layout<IO, D, C> R;
+  static_assert(!(ST && R1), "rule R1 has no states mode");
+  static_assert(!R1 || (sizeof(IO) == 2 && (D / 16) % 2 == 0 && (C / 16) % 2 == 0),
+                "rule R1 takes the bfloat16 paired-tile form");
   constexpr int NB = C / 16, NK = D / 16;
   constexpr int NCW = K::NCW, CPW = K::CPW, NGRP = K::NGRP, NLW = K::NLW, PPW = K::PPW, NTW = K::NTW,
                 TF = K::TF;
@@ -198,14 +211,20 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
     if (nchunks == 0)
       return;  // the compute waves take no barrier either
     const int lw = wave - NCW;
-    // byte offset in the block of LDS piece p (SHARED, then Ut rows; the Ut
-    // pieces exist only when UO_LDS, i.e. RPP >= 1)
+    // byte offset in the block of LDS piece p (the shared part, then Ut
+    // rows, then for R1 the O'' rows; the row pieces exist only when UO_LDS,
+    // i.e. RPP >= 1)
     auto piece_src = [&](int p) -> size_t {
-      constexpr int R = RPP > 0 ? RPP : 1;
+      constexpr int RP = RPP > 0 ? RPP : 1;
       if (p < NPS)
         return static_cast<size_t>(p) * 1024;
-      const int q = p - NPS;
-      return L::UT + tile_off<IO, NK>(q / R, vtf, 0) + static_cast<size_t>(q % R) * 1024;
+      int q = p - NPS;
+      size_t base = R1 ? R::UT : L::UT;
+      if (R1 && q >= NB * RP) {
+        q -= NB * RP;
+        base = R::OI;
+      }
+      return base + tile_off<IO, NK>(q / RP, vtf, 0) + static_cast<size_t>(q % RP) * 1024;
     };
     int src_off[PPW];
 #pragma unroll
@@ -300,7 +319,7 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
   // at its use, or from the registers tload filled
   auto u_tile = [&](const unsigned char *sb, const F(&ucur)[NB][CPW], int J, int j) -> F {
     if constexpr (K::UO_LDS)
-      return F::ld_at(sb + L::SHARED + J * RB + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
+      return F::ld_at(sb + K::SHR + J * RB + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
     else
       return ucur[J][j];
   };
@@ -365,6 +384,16 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
       // chains of all row tiles (Z and O) or of a group of GK row tiles (the
       // update), whose products are independent and fill each other's wait.
       f32x4 z[NB][CPW], ot[NB][CPW];
+      // R1: this wave's N tiles of the chunk, in flight during the products
+      F ntile[R1 ? NK : 1][CPW];
+      if constexpr (R1) {
+        const unsigned char *blk = blk_of(c);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+          for (int j = 0; j < CPW; ++j)
+            ntile[kk][j] = F::ld_at(blk + R::NC + tile_off<IO, NK>(kk, vt0 + j, lane));
+      }
 #pragma unroll
       for (int tt = 0; tt < NB; ++tt) {
 #pragma unroll
@@ -376,7 +405,14 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
             // product shape as the rest of the chain (see mma32)
             z[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             mma32(z[tt][j], F2::make(eye, F::zero()), F2::make(ut, ut));
-            ot[tt][j] = o_intra(sb, ucur, tt, j, std::true_type{});
+            if constexpr (R1) {
+              // O''^T of row tile tt from the staged rows after the Ut rows
+              const F oi = F::ld_at(sb + K::SHR + (NB + tt) * RB + tile_off<IO, TF>(0, vt0 + j - vtf, lane));
+              ot[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+              mma32(ot[tt][j], F2::make(eye, F::zero()), F2::make(oi, oi));
+            } else {
+              ot[tt][j] = o_intra(sb, ucur, tt, j, std::true_type{});
+            }
           } else {
             z[tt][j] = ut.to_f32();
             ot[tt][j] = o_intra(sb, ucur, tt, j, std::false_type{});
@@ -433,8 +469,11 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT>::NCW + scan_cfg<I
 #pragma unroll
         for (int u = 0; u < GK; ++u)
 #pragma unroll
-          for (int j = 0; j < CPW; ++j)
+          for (int j = 0; j < CPW; ++j) {
             S[k0 + u][j] *= gamv[u];
+            if constexpr (R1)  // + N, by an identity product (exact in float32)
+              mma32(S[k0 + u][j], F2::make(eye, F::zero()), F2::make(ntile[k0 + u][j], ntile[k0 + u][j]));
+          }
 #pragma unroll
         for (int t2 = 0; t2 < NB / 2; ++t2)
 #pragma unroll
@@ -651,12 +690,12 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
   return hipGetLastError();
 }
 
-template <typename IO, int D, int C, int NT, bool ST>
+template <typename IO, int D, int C, int NT, bool ST, bool R1 = false>
 hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
-  typedef scan_cfg<IO, D, C, NT> K;
+  typedef scan_cfg<IO, D, C, NT, R1> K;
   const int units = a.num_seqs * a.H;
   const int units_pad = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT, ST>), dim3(units_pad * K::NGRP),
+  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT, ST, R1>), dim3(units_pad * K::NGRP),
                      dim3(64 * (K::NCW + K::NLW)), 0, st, a);
   return hipGetLastError();
 }
@@ -667,21 +706,22 @@ hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
 // sequential per-chunk path; many units get 4 tiles per workgroup.
 // float32 inputs with d = 128, C = 64 keep one tile per workgroup: their
 // wider fragments would not fit in the registers of the larger workgroups.
-template <typename IO, int D, int C, bool ST> hipError_t launch_scan_any(const chunk_args &a, hipStream_t st) {
+template <typename IO, int D, int C, bool ST, bool R1 = false>
+hipError_t launch_scan_any(const chunk_args &a, hipStream_t st) {
   constexpr int NK = D / 16;
   const long units = static_cast<long>(a.num_seqs) * a.H;
   if constexpr (sizeof(IO) == 4 && D * C >= 128 * 64) {
-    return launch_scan_nt<IO, D, C, 1, ST>(a, st);
+    return launch_scan_nt<IO, D, C, 1, ST, R1>(a, st);
   } else {
     if (units * NK <= 256)
-      return launch_scan_nt<IO, D, C, 1, ST>(a, st);
+      return launch_scan_nt<IO, D, C, 1, ST, R1>(a, st);
     if constexpr (NK >= 2) {
       if (NK < 4 || units * (NK / 2) <= 256)
-        return launch_scan_nt<IO, D, C, 2, ST>(a, st);
+        return launch_scan_nt<IO, D, C, 2, ST, R1>(a, st);
     }
     if constexpr (NK >= 4)
-      return launch_scan_nt<IO, D, C, 4, ST>(a, st);
-    return launch_scan_nt<IO, D, C, 1, ST>(a, st);
+      return launch_scan_nt<IO, D, C, 4, ST, R1>(a, st);
+    return launch_scan_nt<IO, D, C, 1, ST, R1>(a, st);
   }
 }
 
@@ -693,6 +733,13 @@ template <typename IO, int D, int C> hipError_t launch_chunk_states(const chunk_
   return launch_scan_any<IO, D, C, true>(a, st);
 }
 
+template <typename IO, int D, int C> hipError_t launch_chunk_scan_r1(const chunk_args &a, hipStream_t st) {
+  if constexpr (scan_r1_supported<IO, D, C>())
+    return launch_scan_any<IO, D, C, false, true>(a, st);
+  else
+    return hipErrorNotSupported;
+}
+
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st) {
   hipLaunchKernelGGL(gdn2_chunk_table_kernel, dim3(1), dim3(256), 0, st, cu, N, C, offsets);
   return hipGetLastError();
@@ -702,7 +749,8 @@ hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets,
   template size_t chunk_block_bytes<IO, D, C>();                                            \
   template hipError_t launch_chunk_prep<IO, D, C>(const chunk_args &, hipStream_t);         \
   template hipError_t launch_chunk_scan<IO, D, C>(const chunk_args &, hipStream_t);        \
-  template hipError_t launch_chunk_states<IO, D, C>(const chunk_args &, hipStream_t);
+  template hipError_t launch_chunk_states<IO, D, C>(const chunk_args &, hipStream_t);       \
+  template hipError_t launch_chunk_scan_r1<IO, D, C>(const chunk_args &, hipStream_t);
 
 GDN2_INST_CHUNK(float, 16, 16)
 GDN2_INST_CHUNK(float, 32, 16)

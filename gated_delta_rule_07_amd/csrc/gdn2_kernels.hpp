@@ -40,6 +40,12 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
 template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st);
 // the state scan in states mode: a.states instead of o (o is not written)
 template <typename IO, int D, int C> hipError_t launch_chunk_states(const chunk_args &a, hipStream_t st);
+// rule R1's state scan on the scan kernel above (bfloat16, even numbers of
+// 16-wide tiles in D and C; otherwise hipErrorNotSupported)
+template <typename IO, int D, int C> constexpr bool scan_r1_supported() {
+  return sizeof(IO) == 2 && (D / 16) % 2 == 0 && (C / 16) % 2 == 0;
+}
+template <typename IO, int D, int C> hipError_t launch_chunk_scan_r1(const chunk_args &a, hipStream_t st);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st);
 template <typename IO, int D, int C, int NG> bool fused_supported();
 template <typename IO, int D, int C, int NG> hipError_t launch_fused(const chunk_args &a, hipStream_t st);

@@ -28,18 +28,6 @@
 
 namespace gdn2 {
 
-// The R1 block: the default block's -W', Q'', Ebar^T and gamma_C slots (its
-// first SHARED0 bytes), then -Ut' (ColFrag), O'' (RowFrag) and N.
-template <typename IO, int D, int C> struct r1_layout {
-  typedef blk_layout<IO, D, C> L;
-  static constexpr int NB = C / 16, NK = D / 16;
-  static constexpr size_t TB = L::TB;
-  static constexpr size_t UT = L::SHARED0;            // rows tt, dv tiles paired: ColFrag(-Ut')
-  static constexpr size_t OI = UT + NB * NK * TB;     // rows tt, dv tiles paired: RowFrag(O'')
-  static constexpr size_t NC = OI + NB * NK * TB;     // dk tiles x dv tiles: ColFrag(N)
-  static constexpr size_t BYTES = align256(NC + NK * NK * TB);
-};
-
 template <typename IO, int D, int C> size_t r1_block_bytes() { return r1_layout<IO, D, C>::BYTES; }
 
 // LDS of the rule-R1 products beyond wy_smem: the Khat keys of each later
@@ -302,9 +290,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_r1_prep_kernel(chunk_args 
   }
 }
 
-// Pass 2 of rule R1: the state scan.  One wave per 16-column tile of the
-// state (dk x 16 float32 in matrix-core accumulators), WPG waves per
-// workgroup, every operand read from the block in global memory.  For chunk
+// Pass 2 of rule R1 where the scan kernel of gdn2_chunk.hip does not take
+// it (float32, or an odd number of 16-wide tiles in D or C): the state scan
+// with one wave per 16-column tile of the state (dk x 16 float32 in
+// matrix-core accumulators), WPG waves per workgroup, every operand read
+// from the block in global memory.  For chunk
 // c: Z = -Ut' + (-W') S, O^T = S^T Q''^T + O''^T (stored as rows of four
 // consecutive columns), S <- Diag(gamma_C) S + Ebar^T Z + N.
 template <typename IO, int D, int C> struct r1_scan_cfg {
@@ -393,11 +383,15 @@ template <typename IO, int D, int C> hipError_t launch_r1_prep(const chunk_args 
 }
 
 template <typename IO, int D, int C> hipError_t launch_r1_scan(const chunk_args &a, hipStream_t st) {
-  typedef r1_scan_cfg<IO, D, C> K;
-  const long units = static_cast<long>(a.num_seqs) * a.H;
-  hipLaunchKernelGGL((gdn2_r1_scan_kernel<IO, D, C>), dim3(static_cast<unsigned>(units * K::NGRP)),
-                     dim3(64 * K::WPG), 0, st, a);
-  return hipGetLastError();
+  if constexpr (scan_r1_supported<IO, D, C>()) {
+    return launch_chunk_scan_r1<IO, D, C>(a, st);  // loader waves and LDS staging
+  } else {
+    typedef r1_scan_cfg<IO, D, C> K;
+    const long units = static_cast<long>(a.num_seqs) * a.H;
+    hipLaunchKernelGGL((gdn2_r1_scan_kernel<IO, D, C>), dim3(static_cast<unsigned>(units * K::NGRP)),
+                       dim3(64 * K::WPG), 0, st, a);
+    return hipGetLastError();
+  }
 }
 
 #define GDN2_INST_R1(IO, D, C)                                                   \

@@ -153,6 +153,19 @@ template <typename IO, int D, int C> struct blk_layout {
   static constexpr size_t BYTES = align256(UT + NB * NK * TB);
 };
 
+// The block of rule R1 (gdn2_rule_r1.hip): the default block's -W', Q'',
+// Ebar^T and gamma_C slots (its first SHARED0 bytes), then -Ut' (ColFrag),
+// O'' (RowFrag) and N = Kbar^T U (ColFrag tiles, dk tile x dv tile).
+template <typename IO, int D, int C> struct r1_layout {
+  typedef blk_layout<IO, D, C> L;
+  static constexpr int NB = C / 16, NK = D / 16;
+  static constexpr size_t TB = L::TB;
+  static constexpr size_t UT = L::SHARED0;            // rows tt, dv tiles paired: ColFrag(-Ut')
+  static constexpr size_t OI = UT + NB * NK * TB;     // rows tt, dv tiles paired: RowFrag(O'')
+  static constexpr size_t NC = OI + NB * NK * TB;     // dk tiles x dv tiles: ColFrag(N)
+  static constexpr size_t BYTES = align256(NC + NK * NK * TB);
+};
+
 // chunk slot -> (sequence, first token (flat index), valid length)
 template <int C>
 __device__ __forceinline__ bool locate_chunk(int slot, const chunk_args &a, int &seq, long &t0,
