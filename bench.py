@@ -83,7 +83,7 @@ def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
 # elements; a state crosses HBM as two fragment-tile copies of d*d elements
 # per chunk, the same bytes as one float32 copy):
 #   path         : read q, k, v, alpha, b, w and dL/do once, write six gradients
-#   chunk_states : read -W, Q', Kbar^T, P, Ut and gamma_C, write the entering state
+#   chunk_states : read -W, Kbar^T, Ut and gamma_C, write the entering state
 #   bwd_dstate   : read -W, Q', Kbar^T, gamma_C and dL/do, write the leaving-state gradient
 #   bwd_grad     : read the six inputs, dL/do, the state and its gradient, write six gradients
 def bwd_bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
@@ -93,7 +93,7 @@ def bwd_bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
     return {
         "path": 7 * d * elem + 6 * d * elem,
         "chunk_prep": 6 * d * elem + 4 * d * elem + pb + gam,
-        "chunk_states": 4 * d * elem + pb + gam + st,
+        "chunk_states": 3 * d * elem + gam + st,
         "bwd_dstate": 4 * d * elem + gam + st,
         "bwd_grad": 7 * d * elem + 2 * st + 6 * d * elem,
     }

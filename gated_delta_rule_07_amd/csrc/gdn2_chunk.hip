@@ -107,8 +107,10 @@ gdn2_chunk_prep_kernel(chunk_args a) {
 // is a whole number of KB (UO_LDS), the workgroup's Ut tiles (rows tt, TF
 // tiles each: its NT tiles rounded out to whole stored pairs).  R1: the
 // block of rule R1, whose shared part ends at SHARED0 (no P) and whose -Ut'
-// and O'' rows are both staged; one column tile per compute wave.
-template <typename IO, int D, int C, int NT, bool R1 = false> struct scan_cfg {
+// and O'' rows are both staged; one column tile per compute wave.  ST
+// (states mode): the output's operands Q' and P are not copied, only -W,
+// Kbar^T, gamma_C and the Ut rows (the LDS keeps the block's offsets).
+template <typename IO, int D, int C, int NT, bool R1 = false, bool ST = false> struct scan_cfg {
   typedef blk_layout<IO, D, C> L;
   static constexpr int NB = C / 16, NK = D / 16;
   static_assert(NT >= 1 && NT <= NK && NK % NT == 0, "tiles per workgroup");
@@ -127,7 +129,12 @@ template <typename IO, int D, int C, int NT, bool R1 = false> struct scan_cfg {
   static_assert(!R1 || UO_LDS, "rule R1 stages its -Ut' and O'' rows");
   static constexpr size_t BUF = SHR + (UO_LDS ? NRW * NB * RB : 0);
   static constexpr int NPS = static_cast<int>(SHR / 1024);
-  static constexpr int NPIECE = static_cast<int>(BUF / 1024);  // 1 KB per wave load
+  // states mode: the Q' pieces [QP, KB) are skipped when they are whole KB,
+  // and the P pieces [SHARED0, SHARED) always (SHARED0 is a whole KB)
+  static constexpr bool SKIPQ = ST && L::QP % 1024 == 0 && L::KB % 1024 == 0;
+  static constexpr int NQS = SKIPQ ? static_cast<int>((L::KB - L::QP) / 1024) : 0;
+  static constexpr int NPS_LD = ST ? static_cast<int>(L::SHARED0 / 1024) - NQS : NPS;  // shared pieces copied
+  static constexpr int NPIECE = NPS_LD + static_cast<int>((BUF - SHR) / 1024);         // 1 KB per wave load
   static constexpr int NLW = NPIECE < 4 ? NPIECE : (NPIECE + 12) / 13 > 4 ? (NPIECE + 12) / 13 : 4;
   static constexpr int PPW = (NPIECE + NLW - 1) / NLW;         // pieces per loader wave
   static constexpr int RSETS = PPW <= 16 ? 2 : 1;              // loader register buffers
@@ -161,9 +168,9 @@ template <typename IO, int D, int C, int NT, bool R1 = false> struct scan_cfg {
 // each compute wave reads from the block at the start of the chunk:
 //   Z = -Ut' - W' S,  O = Q'' S + O'',  S <- Diag(gamma_C) S + Ebar^T Z + N.
 template <typename IO, int D, int C, int NT, bool ST = false, bool R1 = false>
-__global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1>::NCW + scan_cfg<IO, D, C, NT, R1>::NLW))
+__global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1, ST>::NCW + scan_cfg<IO, D, C, NT, R1, ST>::NLW))
     gdn2_chunk_scan_kernel(chunk_args a) {
-  typedef scan_cfg<IO, D, C, NT, R1> K;
+  typedef scan_cfg<IO, D, C, NT, R1, ST> K;
   typedef r1_layout<IO, D, C> R;
   static_assert(!(ST && R1), "rule R1 has no states mode");
   static_assert(!R1 || (sizeof(IO) == 2 && (D / 16) % 2 == 0 && (C / 16) % 2 == 0),
@@ -171,7 +178,7 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1>::NCW + scan_c
   constexpr int NB = C / 16, NK = D / 16;
   constexpr int NCW = K::NCW, CPW = K::CPW, NGRP = K::NGRP, NLW = K::NLW, PPW = K::PPW, NTW = K::NTW,
                 TF = K::TF;
-  constexpr int NPIECE = K::NPIECE, NPS = K::NPS, RPP = K::RPP, NBUF = K::NBUF;
+  constexpr int NPIECE = K::NPIECE, NPS_LD = K::NPS_LD, RPP = K::RPP, NBUF = K::NBUF;
   constexpr size_t RB = K::RB;
   typedef frag<IO> F;
   typedef frag2<IO> F2;
@@ -213,12 +220,14 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1>::NCW + scan_c
     const int lw = wave - NCW;
     // byte offset in the block of LDS piece p (the shared part, then Ut
     // rows, then for R1 the O'' rows; the row pieces exist only when UO_LDS,
-    // i.e. RPP >= 1)
+    // i.e. RPP >= 1), and its offset in an LDS buffer: a shared piece keeps
+    // its block offset (states mode skips the Q' pieces), the row pieces
+    // follow the shared part
     auto piece_src = [&](int p) -> size_t {
       constexpr int RP = RPP > 0 ? RPP : 1;
-      if (p < NPS)
-        return static_cast<size_t>(p) * 1024;
-      int q = p - NPS;
+      if (p < NPS_LD)
+        return static_cast<size_t>(p >= static_cast<int>(L::QP / 1024) ? p + K::NQS : p) * 1024;
+      int q = p - NPS_LD;
       size_t base = R1 ? R::UT : L::UT;
       if (R1 && q >= NB * RP) {
         q -= NB * RP;
@@ -226,11 +235,17 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1>::NCW + scan_c
       }
       return base + tile_off<IO, NK>(q / RP, vtf, 0) + static_cast<size_t>(q % RP) * 1024;
     };
-    int src_off[PPW];
+    auto piece_dst = [&](int p) -> int {
+      if (p < NPS_LD)
+        return static_cast<int>(piece_src(p));
+      return static_cast<int>(K::SHR) + (p - NPS_LD) * 1024;
+    };
+    int src_off[PPW], dst_off[PPW];
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
       const int piece = lw + p * NLW;
       src_off[p] = piece < NPIECE ? static_cast<int>(piece_src(piece)) : 0;
+      dst_off[p] = piece < NPIECE ? piece_dst(piece) : 0;
     }
     u32x4 ra[PPW], rb[PPW];
     // Always issues PPW loads (past the last chunk: the first bytes of the
@@ -247,7 +262,7 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1>::NCW + scan_c
       for (int p = 0; p < PPW; ++p) {
         const int piece = lw + p * NLW;
         if (piece < NPIECE)
-          *reinterpret_cast<u32x4 *>(&sbuf[buf][piece * 1024 + lane * 16]) = r[p];
+          *reinterpret_cast<u32x4 *>(&sbuf[buf][dst_off[p] + lane * 16]) = r[p];
       }
     };
     gload(0, ra);
@@ -692,7 +707,7 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
 
 template <typename IO, int D, int C, int NT, bool ST, bool R1 = false>
 hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
-  typedef scan_cfg<IO, D, C, NT, R1> K;
+  typedef scan_cfg<IO, D, C, NT, R1, ST> K;
   const int units = a.num_seqs * a.H;
   const int units_pad = (units + 7) / 8 * 8;
   hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT, ST, R1>), dim3(units_pad * K::NGRP),
