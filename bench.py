@@ -113,6 +113,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def event_us(fn, steps: int, warmup: int) -> float:
+    """Average time of one call of fn in microseconds, from two HIP events
+    recorded on torch's current stream (the stream the library launches on)
+    around `steps` calls."""
+    for _ in range(warmup):
+        fn()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(steps):
+        fn()
+    t_end.record()
+    t_end.synchronize()
+    return t_start.elapsed_time(t_end) * 1e3 / steps
+
+
 def timed_steps(fn, steps: int, warmup: int) -> float:
     for _ in range(warmup):
         fn()
@@ -455,13 +470,30 @@ def main() -> int:
     # the timed output against the oracle (every element of o and S_final)
     o_gpu = o.float().cpu().numpy()
     S_gpu = Sf.cpu().numpy()
-    # per-kernel durations in a separate pass: HIP events on the launch stream
+    # per-kernel durations in a separate pass: the library's HIP events
+    # around every launch (an event between the two kernels delays the next
+    # launch, the prep's by about 15 %)
     g.profile_enable(True)
     g.profile_read(reset=True)
     sec_hooks = timed_steps(step, args.steps, 3)
     prof = g.profile_read(reset=True)
     g.profile_enable(False)
-    kern = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in prof.items()}
+    kern_hooked = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in prof.items()}
+    kern = kern_hooked
+    duration_method = "library HIP events around every launch"
+    if set(kern_hooked) == {"chunk_prep", "chunk_scan"}:
+        # without per-launch events: HIP events around K whole steps and
+        # around K runs of the scan alone on the workspace the last step
+        # filled (prepared mode, same blocks); the prep is the difference
+        def scan_only():
+            g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o, S_final=Sf, workspace=ws,
+                        path=args.path, prepared=True)
+        full_us = event_us(step, args.steps, 20)
+        scan_us = event_us(scan_only, args.steps, 20)
+        kern = {"chunk_prep": {"avg_us": full_us - scan_us, "launches": args.steps},
+                "chunk_scan": {"avg_us": scan_us, "launches": args.steps}}
+        duration_method = ("HIP events on the launch stream around K steps and around K scan-only "
+                           "runs on the filled workspace; prep = step - scan")
 
     tok_heads = B * T * H
     fl = flops_per_token_head(d, C) * tok_heads
@@ -482,7 +514,8 @@ def main() -> int:
     # outputs, workspace included) are reported beside it
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dominant, "algorithmic_bytes_per_launch": int(path_bytes),
+                "kernel": dominant, "duration_us": round(dom_us, 2), "duration_method": duration_method,
+                "algorithmic_bytes_per_launch": int(path_bytes),
                 "algorithmic_bytes_per_token_head": byt["path"], "token_heads_per_launch": tok_heads,
                 "kernel_own": {"bytes_per_launch": int(own_bytes), "achieved": round(own_achieved, 1),
                                "frac": round(own_achieved / HBM_PEAK_GBS, 4)},
@@ -507,6 +540,7 @@ def main() -> int:
                  "flops_per_token_head": flops_per_token_head(d, C),
                  "step_traffic_bytes": step_traffic},
         "kernels": kern,
+        "kernels_event_hooks": kern_hooked,
         "ms_per_step_with_timing_hooks": round(sec_hooks * 1e3, 4),
         "host": host_info(),
     }
