@@ -548,10 +548,14 @@ def gpu_fwd_r1(g, inp, chunk, cu=None, path="auto", layer_prep=False):
     return o.float().cpu().numpy(), Sf.cpu().numpy()
 
 
-# Rule R1 on the chunked two-pass path (its own per-chunk kernel and scan)
+# Rule R1 on the chunked two-pass path (its own per-chunk kernel; the state
+# scan's R1 mode for bf16 with d = 32, 64, 128 and chunk 64, at one (6 and
+# 10 units), two (48 units, d = 128) or, in the layer test, four column
+# tiles per workgroup; the one-wave-per-tile R1 scan otherwise)
 R1_CASES = [("f32", 16, 16, 1, 64, 1), ("f32", 64, 64, 2, 512, 4), ("f32", 128, 16, 2, 40, 2),
             ("f32", 32, 64, 2, 130, 3), ("bf16", 128, 64, 2, 200, 3), ("bf16", 64, 16, 2, 77, 3),
-            ("bf16", 16, 64, 1, 90, 2)]
+            ("bf16", 16, 64, 1, 90, 2), ("bf16", 128, 64, 4, 300, 12), ("bf16", 64, 64, 2, 333, 5),
+            ("bf16", 32, 64, 3, 150, 2)]
 
 
 @pytest.mark.parametrize("path", ["auto", "two_pass"])
@@ -575,6 +579,12 @@ def test_rule_r1_chunked_packed_and_extreme_decay(g):
         print(f"case R1 packed C={chunk}", flush=True)
         o, Sf = gpu_fwd_r1(g, inp, chunk, cu=cu)
         check(o, Sf, o_ref, S_ref, TOL["f32"], f"R1 packed C={chunk}")
+    # bf16, d = 128: the scan's R1 mode on packed sequences with ragged ends
+    inp = gi.make_chunk_inputs(1, int(cu[-1]), 3, 128, 128, "bf16", seed=135, s0="normal", num_seqs=len(lens))
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"], cu_seqlens=cu, rule="R1")
+    print("case R1 packed bf16 d=128 C=64", flush=True)
+    o, Sf = gpu_fwd_r1(g, inp, 64, cu=cu)
+    check(o, Sf, o_ref, S_ref, TOL["bf16"], "R1 packed bf16 d=128 C=64")
     for dtype, d, chunk in (("f32", 64, 64), ("bf16", 128, 64), ("f32", 32, 16)):
         inp = gi.make_strong_decay_inputs(2, 150, 2, d, d, dtype, seed=132 + d, s0="normal")
         print(f"case R1 strong decay {dtype} d={d} C={chunk}", flush=True)
