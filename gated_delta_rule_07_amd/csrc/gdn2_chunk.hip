@@ -114,7 +114,10 @@ template <typename IO, int D, int C, int NT, bool R1 = false, bool ST = false> s
   typedef blk_layout<IO, D, C> L;
   static constexpr int NB = C / 16, NK = D / 16;
   static_assert(NT >= 1 && NT <= NK && NK % NT == 0, "tiles per workgroup");
-  static constexpr int CPW = (sizeof(IO) == 2 && NT >= 2 && !R1) ? 2 : 1;
+  // two column tiles per compute wave at NT = 2 (one compute wave per
+  // workgroup); at NT = 4 two such waves would spill, four waves of one tile
+  // do not, and rule R1's N tiles need the room
+  static constexpr int CPW = (sizeof(IO) == 2 && NT == 2 && !R1) ? 2 : 1;
   static constexpr int NCW = NT / CPW;
   static constexpr int NGRP = NK / NT;
   static constexpr int NTW = NT;                     // dv tiles per workgroup
