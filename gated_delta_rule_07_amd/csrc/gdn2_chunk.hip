@@ -2,9 +2,10 @@
 //
 // Pass 1 (gdn2_chunk_prep_kernel) runs the per-chunk phases of gdn2_wy.hpp for
 // every (chunk, head) in parallel and writes the chunk's -W, Q', Kbar^T,
-// gamma_C, Ut and O_intra to the workspace in fragment order.  Pass 2
-// (gdn2_chunk_scan_kernel) walks the chunks of each sequence in order with
-// the state in matrix-core accumulators.  This path keeps the whole GPU busy
+// gamma_C, P's lower-triangular tiles and Ut to the workspace in fragment
+// order.  Pass 2 (gdn2_chunk_scan_kernel) walks the chunks of each sequence
+// in order with the state in matrix-core accumulators and forms
+// O_intra = P Ut on the way.  This path keeps the whole GPU busy
 // when there are few (sequence, head) units (long sequences, small batch);
 // gdn2_fused.hip does both passes in one workgroup per head and avoids the
 // workspace round trip when there are enough units.  gdn2_chunk_table_kernel
@@ -145,13 +146,14 @@ template <typename IO, int D, int C, int NT, bool R1 = false, bool ST = false> s
 };
 
 // Pass 2: sequential state scan + output.  For chunk c of a (sequence, head):
-//   Z = Ut - W S,  O = O_intra + Q' S  (written to o),  S <- Diag(gamma_C) S + Kbar^T Z.
+//   Z = Ut - W S,  O = P Ut + Q' S  (written to o),  S <- Diag(gamma_C) S + Kbar^T Z.
 // Every 16-column slice of S evolves on its own given the chunk's -W, Q',
-// Kbar^T and gamma_C (the SHARED part of the block), so the dv columns are
+// Kbar^T, gamma_C and P (the SHARED part of the block), so the dv columns are
 // split over NGRP workgroups x NCW compute waves, each keeping its CPW slices
 // of S (dk x 16, float32) in matrix-core accumulators for the whole sequence.
-// NLW loader waves move each chunk's operands (65 KB for bf16, d = 128,
-// C = 64) HBM -> registers -> LDS two chunks ahead of the compute waves (one
+// NLW loader waves move each chunk's operands (62 KB for a workgroup of four
+// column tiles, bf16, d = 128, C = 64: the 54 KB shared part and 8 KB of Ut)
+// HBM -> registers -> LDS two chunks ahead of the compute waves (one
 // LDS buffer ahead, one register set ahead), so that the wide loads are
 // spread over several waves and never stall the waves doing the products; a
 // compute wave issues no global load inside the loop.  O is accumulated
