@@ -53,44 +53,49 @@ class Gdn2Error(RuntimeError):
         self.status = status
 
 
+def configure(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Sets the argument and result types of every C-ABI entry point on a
+    loaded copy of the library and returns it."""
+    vp, i, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
+    L.gdn2_chunk_fwd_workspace_bytes.restype = sz
+    L.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
+    L.gdn2_chunk_fwd_workspace_bytes_flags.restype = sz
+    L.gdn2_chunk_fwd_workspace_bytes_flags.argtypes = [i] * 7 + [i, u32]
+    L.gdn2_chunk_fwd.restype = i
+    L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
+    L.gdn2_chunk_fwd_noalloc.restype = i
+    L.gdn2_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp]
+    L.gdn2_chunk_bwd_workspace_bytes.restype = sz
+    L.gdn2_chunk_bwd_workspace_bytes.argtypes = [i] * 7 + [i]
+    L.gdn2_chunk_bwd.restype = i
+    L.gdn2_chunk_bwd.argtypes = [vp] * 8 + [i] * 8 + [u32] + [vp] * 9 + [vp, sz, vp]
+    L.gdn2_chunk_segment_map.restype = i
+    L.gdn2_chunk_segment_map.argtypes = [vp] * 7 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
+    L.gdn2_segment_combine.restype = i
+    L.gdn2_segment_combine.argtypes = [vp] * 3 + [i] * 4 + [vp, vp, vp]
+    L.gdn2_decode_step.restype = i
+    L.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
+    L.gdn2_status_string.restype = ctypes.c_char_p
+    L.gdn2_status_string.argtypes = [i]
+    L.gdn2_last_error.restype = ctypes.c_char_p
+    L.gdn2_last_error.argtypes = []
+    L.gdn2_abi_version.restype = i
+    L.gdn2_profile_enable.restype = i
+    L.gdn2_profile_enable.argtypes = [i]
+    L.gdn2_profile_read.restype = i
+    L.gdn2_profile_read.argtypes = [i, ctypes.POINTER(ctypes.c_char_p),
+                                    ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), i]
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded ``libgdn2.so`` (raises if it has not been built)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing; run `python -m gated_delta_rule_07_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
-        L.gdn2_chunk_fwd_workspace_bytes.restype = sz
-        L.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
-        L.gdn2_chunk_fwd_workspace_bytes_flags.restype = sz
-        L.gdn2_chunk_fwd_workspace_bytes_flags.argtypes = [i] * 7 + [i, u32]
-        L.gdn2_chunk_fwd.restype = i
-        L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
-        L.gdn2_chunk_fwd_noalloc.restype = i
-        L.gdn2_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 8 + [u32, vp, vp, vp]
-        L.gdn2_chunk_bwd_workspace_bytes.restype = sz
-        L.gdn2_chunk_bwd_workspace_bytes.argtypes = [i] * 7 + [i]
-        L.gdn2_chunk_bwd.restype = i
-        L.gdn2_chunk_bwd.argtypes = [vp] * 8 + [i] * 8 + [u32] + [vp] * 9 + [vp, sz, vp]
-        L.gdn2_chunk_segment_map.restype = i
-        L.gdn2_chunk_segment_map.argtypes = [vp] * 7 + [i] * 8 + [u32, vp, vp, vp, sz, vp]
-        L.gdn2_segment_combine.restype = i
-        L.gdn2_segment_combine.argtypes = [vp] * 3 + [i] * 4 + [vp, vp, vp]
-        L.gdn2_decode_step.restype = i
-        L.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
-        L.gdn2_status_string.restype = ctypes.c_char_p
-        L.gdn2_status_string.argtypes = [i]
-        L.gdn2_last_error.restype = ctypes.c_char_p
-        L.gdn2_last_error.argtypes = []
-        L.gdn2_abi_version.restype = i
-        L.gdn2_profile_enable.restype = i
-        L.gdn2_profile_enable.argtypes = [i]
-        L.gdn2_profile_read.restype = i
-        L.gdn2_profile_read.argtypes = [i, ctypes.POINTER(ctypes.c_char_p),
-                                        ctypes.POINTER(ctypes.c_double),
-                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), i]
-        _lib = L
+        _lib = configure(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

@@ -5,6 +5,12 @@
 compiles every source under csrc/ with hipcc for gfx950 and links
 gated_delta_rule_07_amd/libgdn2.so.  Packed-FP32 instruction selection is
 switched off for device code (the flag is harmless for the host pass).
+
+It also links libgdn2_hostcheck.so: the same kernels with the host side of
+gdn2_api.cpp (argument checks, workspace planning, launch set-up) built with
+undefined-behaviour checks that trap (signed overflow, shifts, array bounds,
+misaligned or null accesses), for the host-side tests.  The product binding
+never loads it.
 """
 from __future__ import annotations
 
@@ -16,6 +22,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdn2.so")
+OUT_HOSTCHECK = os.path.join(HERE, "libgdn2_hostcheck.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("GDN2_OFFLOAD_ARCH", "gfx950")
 
@@ -29,6 +36,10 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
 # default the compiler keeps them in AGPRs and copies them to VGPRs and back
 # every chunk, which the VGPR form of the products avoids.
 EXTRA = {"gdn2_segment.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Host-only undefined-behaviour traps for the checked build of gdn2_api.cpp
+# (each flag after -Xarch_host: device code is compiled as in the product).
+HOSTCHECK = [f for x in ("-fsanitize=undefined", "-fsanitize-trap=undefined", "-fsanitize=bounds",
+                         "-fno-sanitize-recover=all") for f in ("-Xarch_host", x)]
 
 
 def _hipcc() -> str:
@@ -38,29 +49,38 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, hostcheck: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_hostcheck" if hostcheck else "") + ".o")
     cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc(), *COMMON, *(HOSTCHECK if hostcheck else []), "-x", "hip", "-c", os.path.join(CSRC, src),
+               "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     r = subprocess.run([_hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        futs = [ex.submit(_compile, src) for src in SOURCES]
+        checked_api = ex.submit(_compile, "gdn2_api.cpp", True)
+        objs = [f.result() for f in futs]
+        api_checked = checked_api.result()
+    _link(objs, OUT)
+    _link([api_checked if o.endswith("gdn2_api.o") else o for o in objs], OUT_HOSTCHECK)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {OUT_HOSTCHECK}")
     return OUT
 
 

@@ -268,10 +268,33 @@ hipError_t dispatch_decode(gdn2_dtype_t dt, int d, const void *q, const void *k,
   return hipErrorInvalidValue;
 }
 
-int num_slots_for(int B, int T, int num_seqs, int chunk, bool packed) {
-  if (packed)
-    return (T + chunk - 1) / chunk + num_seqs;  // upper bound: sum of ceil(len/C)
-  return B * ((T + chunk - 1) / chunk);
+// Chunk slots of a call: ceil(T / C) per sequence, or for packed input an
+// upper bound of the sum of ceil(len / C).  Formed in 64 bits; every entry
+// point checks sizes_supported first, so a call's count fits an int.
+long long num_slots_for(int B, int T, int num_seqs, int chunk, bool packed) {
+  const long long per = (static_cast<long long>(T) + chunk - 1) / chunk;
+  return packed ? per + num_seqs : static_cast<long long>(B) * per;
+}
+
+// The sizes the library serves.  A dispatch holds its grid size in 32-bit
+// work-item counts: the per-chunk kernels launch one workgroup of up to 256
+// threads per chunk-head, so chunk slots x heads stay below 2^24; the scans
+// launch up to two workgroups of up to 576 threads per (sequence, head), so
+// sequences x heads stay at or below 2^21.  The inputs hold at most 2^40
+// elements.
+constexpr long long kMaxChunkHeads = (1LL << 24) - 1;
+constexpr long long kMaxSeqHeads = 1LL << 21;
+
+bool sizes_supported(int B, int T, int H, int d, int num_seqs, int chunk, bool packed) {
+  if (B <= 0 || T < 0 || H <= 0 || d <= 0 || chunk <= 0 || num_seqs < 0 || (packed && num_seqs == 0))
+    return false;
+  const long long bt = static_cast<long long>(B) * T;
+  if (bt > (1LL << 40) / (static_cast<long long>(H) * d))
+    return false;
+  const long long n = packed ? num_seqs : B;
+  if (n > kMaxSeqHeads / H)
+    return false;
+  return num_slots_for(B, T, static_cast<int>(n), chunk, packed) <= kMaxChunkHeads / H;
 }
 
 // ---------------------------------------------------------------- backward --
@@ -311,7 +334,7 @@ hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, hip
   s.B = 1;
   s.T = sg.T_total;
   s.num_seqs = nseg;
-  s.num_slots = num_slots_for(1, sg.T_total, nseg, C_rt, true);
+  s.num_slots = static_cast<int>(num_slots_for(1, sg.T_total, nseg, C_rt, true));
   s.S0 = nullptr;
   s.S_final = nullptr;
   s.o = nullptr;
@@ -587,7 +610,7 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   s.B = 1;
   s.T = x.T_total;
   s.num_seqs = x.N * pl.G;
-  s.num_slots = num_slots_for(1, s.T, s.num_seqs, chunk, true);
+  s.num_slots = static_cast<int>(num_slots_for(1, s.T, s.num_seqs, chunk, true));
   s.blocks = ws + pl.cu + pl.table;
   s.S0 = nullptr;
   s.o = nullptr;
@@ -651,6 +674,9 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
     return 0;
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return 0;
+  if (!sizes_supported(B, T, H, dk, B, chunk, false) ||
+      (num_seqs > 0 && !sizes_supported(B, T, H, dk, num_seqs, chunk, true)))
+    return 0;
   // num_seqs > 0 asks for packed input (B must then be 1); the bound returned
   // covers both the packed and the fixed-length layout of these sizes.
   const int n = num_seqs > 0 ? num_seqs : B;
@@ -673,6 +699,9 @@ size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv,
     if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
       return 0;
     if (dt != GDN2_F32 && dt != GDN2_BF16)
+      return 0;
+    if (!sizes_supported(B, T, H, dk, B, chunk, false) ||
+        (num_seqs > 0 && !sizes_supported(B, T, H, dk, num_seqs, chunk, true)))
       return 0;
     const size_t blk = r1_block_bytes_rt(dt, dk, chunk);
     if (blk == 0)
@@ -744,9 +773,10 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   for (const void *p : ptrs)
     if (p && !aligned16(p))
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: pointers must be 16-byte aligned");
-  const long long elems = static_cast<long long>(B) * T * H * dk;
-  if (elems > (1LL << 40))
-    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: problem too large");
+  if (!sizes_supported(B, T, H, dk, N, chunk, packed))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd: sizes beyond the library's limits (at most 2^40 input elements, 2^24 chunk-heads, "
+                "2^21 sequence-heads)");
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (flags & GDN2_FLAG_RECURRENT) {
@@ -783,7 +813,7 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   a.T = T;
   a.H = H;
   a.num_seqs = N;
-  a.num_slots = num_slots_for(B, T, N, chunk, packed);
+  a.num_slots = static_cast<int>(num_slots_for(B, T, N, chunk, packed));
   a.o = o;
   a.S_final = S_final;
   a.blk_bytes = blk_bytes;
@@ -831,6 +861,9 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
     return 0;
   if (dt != GDN2_F32 && dt != GDN2_BF16)
+    return 0;
+  if (!sizes_supported(B, T, H, dk, B, chunk, false) ||
+      (num_seqs > 0 && !sizes_supported(B, T, H, dk, num_seqs, chunk, true)))
     return 0;
   const int n = num_seqs > 0 ? num_seqs : B;
   const bwd_plan pf = plan_bwd(dt, B, T, H, dk, B, chunk, false);
@@ -884,9 +917,10 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   for (const void *p : ptrs)
     if (p && !aligned16(p))
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: pointers must be 16-byte aligned");
-  const long long elems = static_cast<long long>(B) * T * H * dk;
-  if (elems > (1LL << 40))
-    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: problem too large");
+  if (!sizes_supported(B, T, H, dk, N, chunk, packed))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_bwd: sizes beyond the library's limits (at most 2^40 input elements, 2^24 chunk-heads, "
+                "2^21 sequence-heads)");
   const bwd_plan plan = plan_bwd(dt, B, T, H, dk, N, chunk, packed);
   if (workspace_bytes < plan.total || !workspace)
     return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
@@ -907,7 +941,7 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   a.T = T;
   a.H = H;
   a.num_seqs = N;
-  a.num_slots = T == 0 ? 0 : num_slots_for(B, T, N, chunk, packed);
+  a.num_slots = T == 0 ? 0 : static_cast<int>(num_slots_for(B, T, N, chunk, packed));
   a.o = nullptr;
   a.S_final = nullptr;
   a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
@@ -994,9 +1028,10 @@ gdn2_status_t gdn2_chunk_segment_map(const void *q, const void *k, const void *v
   for (const void *p : ptrs)
     if (p && !aligned16(p))
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_segment_map: pointers must be 16-byte aligned");
-  const long long elems = static_cast<long long>(B) * T * H * dk;
-  if (elems > (1LL << 40))
-    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_segment_map: problem too large");
+  if (!sizes_supported(B, T, H, dk, N, chunk, packed))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_segment_map: sizes beyond the library's limits (at most 2^40 input elements, 2^24 chunk-heads, "
+                "2^21 sequence-heads)");
   const size_t table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
   const size_t need = table + static_cast<size_t>(num_slots_for(B, T, N, chunk, packed)) * H *
                                   chunk_block_bytes_rt(dt, dk, chunk);
@@ -1016,7 +1051,7 @@ gdn2_status_t gdn2_chunk_segment_map(const void *q, const void *k, const void *v
   a.T = T;
   a.H = H;
   a.num_seqs = N;
-  a.num_slots = T == 0 ? 0 : num_slots_for(B, T, N, chunk, packed);
+  a.num_slots = T == 0 ? 0 : static_cast<int>(num_slots_for(B, T, N, chunk, packed));
   a.blk_bytes = chunk_block_bytes_rt(dt, dk, chunk);
   a.gates = ((flags & GDN2_FLAG_SCALAR_B) ? gdn2::GATE_SCALAR_B : 0u) |
             ((flags & GDN2_FLAG_SCALAR_W) ? gdn2::GATE_SCALAR_W : 0u) |
@@ -1080,8 +1115,8 @@ gdn2_status_t gdn2_decode_step(const void *q, const void *k, const void *v, cons
   for (const void *p : ptrs)
     if (!aligned16(p))
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: pointers must be 16-byte aligned");
-  if (static_cast<long long>(N) * H > (1LL << 31) - 1)
-    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_decode_step: too many sequence-heads");
+  if (static_cast<long long>(N) * H > (1LL << 24) - 1)  // one workgroup of 256 threads per sequence-head
+    return fail(GDN2_ERR_UNSUPPORTED, "gdn2_decode_step: too many sequence-heads (at most 2^24 - 1)");
   const hipError_t e = dispatch_decode(dt, dk, q, k, v, alpha, b, w, S, o, N, H,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
@@ -1114,6 +1149,10 @@ gdn2_status_t gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v
   const bool packed = cu_seqlens != nullptr;
   if (packed && num_seqs <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd_noalloc: packed input needs num_seqs > 0");
+  if (!sizes_supported(B, T, H, dk, packed ? num_seqs : B, chunk, packed))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_fwd_noalloc: sizes beyond the library's limits (at most 2^40 input elements, "
+                "2^24 chunk-heads, 2^21 sequence-heads)");
   // the plain two-pass workspace of the whole call, as gdn2_chunk_fwd checks it
   const size_t whole_plain = (packed ? align256(static_cast<size_t>(num_seqs + 1) * sizeof(int32_t)) : 0) +
                              static_cast<size_t>(num_slots_for(B, T, packed ? num_seqs : B, chunk, packed)) * H *
@@ -1195,6 +1234,8 @@ const char *gdn2_status_string(gdn2_status_t status) {
     return "workspace too small";
   case GDN2_ERR_HIP:
     return "HIP error";
+  default:
+    break;
   }
   return "unknown status";
 }

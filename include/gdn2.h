@@ -66,15 +66,20 @@ extern "C" {
 
 #define GDN2_ABI_VERSION 1
 
+/* The *_MAX_ENUM values are never returned or accepted: they give both
+ * enums the range of a non-negative int, so that any such value a caller
+ * passes (an unknown status or dtype) is a valid value of the type and is
+ * refused by the library, not undefined. */
 typedef enum {
     GDN2_OK = 0,
     GDN2_ERR_INVALID_ARGUMENT = 1,
     GDN2_ERR_UNSUPPORTED = 2,
     GDN2_ERR_WORKSPACE_TOO_SMALL = 3,
-    GDN2_ERR_HIP = 4
+    GDN2_ERR_HIP = 4,
+    GDN2_STATUS_MAX_ENUM = 0x7FFFFFFF
 } gdn2_status_t;
 
-typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1, GDN2_DTYPE_MAX_ENUM = 0x7FFFFFFF } gdn2_dtype_t;
 
 /* flags of gdn2_chunk_fwd */
 #define GDN2_FLAG_RECURRENT (1u << 1) /* token-by-token kernel instead of the
@@ -133,6 +138,15 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype_t;
  * gdn2_chunk_fwd on the two-pass path serves the same way.  Any other
  * contents give undefined outputs. */
 #define GDN2_FLAG_PREPARED (1u << 8)
+
+/* Size limits of every chunked entry point (gdn2_chunk_fwd, its
+ * allocation-free variant, gdn2_chunk_bwd, gdn2_chunk_segment_map): at most
+ * 2^40 input elements (B T H dk), fewer than 2^24 chunk-heads (chunk slots
+ * x H: one workgroup each, whose work-items a dispatch counts in 32 bits),
+ * at most 2^21 sequence-heads (sequences x H).  Larger calls return
+ * GDN2_ERR_UNSUPPORTED before any launch, and the workspace-size functions
+ * return 0 for them.  gdn2_decode_step takes fewer than 2^24
+ * sequence-heads. */
 
 /* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when
  * the sizes are unsupported).  With cu_seqlens, pass the packed total T and

@@ -11,12 +11,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn2.h")
 
 
-@pytest.fixture(scope="module")
-def L():
+# Every host-side check runs against the product library and against its
+# host-checked build (the C-ABI layer with undefined-behaviour checks that
+# trap: an overflow in the size arithmetic or an out-of-bounds host access
+# ends the test process instead of passing silently).
+@pytest.fixture(scope="module", params=["libgdn2.so", "libgdn2_hostcheck.so"])
+def L(request):
     import gated_delta_rule_07_amd as g
-    if not os.path.exists(g.LIB_PATH):
-        pytest.fail("libgdn2.so is not built (run __graft_entry__.build())")
-    return g.lib()
+    if request.param == "libgdn2.so":
+        if not os.path.exists(g.LIB_PATH):
+            pytest.fail("libgdn2.so is not built (run __graft_entry__.build())")
+        return g.lib()
+    path = os.path.join(os.path.dirname(g.LIB_PATH), request.param)
+    if not os.path.exists(path):
+        pytest.fail(f"{request.param} is not built (run __graft_entry__.build())")
+    return g.configure(ctypes.CDLL(path))
 
 
 def declared_functions():
@@ -261,3 +270,29 @@ def test_workspace_bytes_rule_r1(L):
     assert r1 >= f(8, 4096, 16, 128, 128, 0, 64, BF16) + 8 * 64 * 16 * 32 * 1024 - 4096
     assert fl(1, 100, 2, 128, 128, 0, 64, F32, 1 << 7) == 0      # not built
     assert fl(1, 100, 2, 128, 128, 0, 16, F32, 1 << 7) > 0
+
+
+def test_sizes_at_the_limits(L):
+    """Workspace sizes and argument checks with sizes near the int range:
+    every product is formed in size_t, so nothing overflows (the host-checked
+    build traps on a signed overflow), and calls the library cannot serve
+    are refused or sized as 0, never wrapped around."""
+    f, fb = L.gdn2_chunk_fwd_workspace_bytes, L.gdn2_chunk_bwd_workspace_bytes
+    big = 2 ** 31 - 1
+    for B, T, H in ((1, big, 1), (big, 64, 1), (1, 64, big), (2 ** 16, 2 ** 16, 16), (1, big, 64)):
+        for dt in (F32, BF16):
+            w = f(B, T, H, 128, 128, 0, 64, dt)
+            assert w == 0 or w >= B * H * ((T + 63) // 64) * 1024
+            wb = fb(B, T, H, 128, 128, 0, 64, dt)
+            assert wb == 0 or wb >= w
+    # the limits: chunk slots x heads below 2^24, sequences x heads at most
+    # 2^21, inputs at most 2^40 elements; past them the size is 0
+    assert f(1, 2 ** 24, 16, 64, 64, 2 ** 16, 64, BF16) > 0
+    assert f(1, 2 ** 24, 16, 64, 64, 2 ** 18, 64, BF16) == 0      # 2^22 sequence-heads
+    assert f(1, 2 ** 26, 16, 128, 128, 0, 64, BF16) == 0          # 2^24 chunk-heads
+    assert f(1, 2 ** 26 - 64, 16, 128, 128, 0, 64, BF16) > 0
+    assert f(1, 1, 1, 16, 16, big, 16, F32) == 0
+    # the entry points refuse such sizes before touching a pointer
+    assert call_fwd(L, B=big, T=big, H=big, ws_bytes=1 << 40) == 2
+    assert call_fwd(L, T=big, H=big, ws_bytes=1 << 40) == 2
+    assert call_fwd(L, B=1, T=2 ** 26, H=16, dk=128, dv=128, chunk=64, ws_bytes=1 << 50) == 2
