@@ -27,7 +27,7 @@ BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("GDN2_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["gdn2_api.cpp", "gdn2_recurrent.hip", "gdn2_chunk.hip", "gdn2_fused.hip", "gdn2_bwd.hip", "gdn2_segment.hip",
-           "gdn2_rule_r1.hip"]
+           "gdn2_rule_r1.hip", "gdn2_pad.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument"]

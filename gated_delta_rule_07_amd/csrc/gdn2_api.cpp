@@ -233,37 +233,41 @@ bool fused_available(gdn2_dtype_t dt, int d, int c) {
   return false;
 }
 
-hipError_t dispatch_recurrent(gdn2_dtype_t dt, int d, const void *q, const void *k, const void *v,
+hipError_t dispatch_recurrent(gdn2_dtype_t dt, int dk, int dv, const void *q, const void *k, const void *v,
                               const void *al, const void *b, const void *w, const float *S0,
                               const int32_t *cu, int T, int H, int N, void *o, float *Sf, bool r1,
                               hipStream_t st) {
   prof_scope p("recurrent", st);
-#define GDN2_RR(IO, D) \
-  if (d == D)          \
-    return gdn2::launch_recurrent<IO, D>(q, k, v, al, b, w, S0, cu, T, H, N, o, Sf, r1, st);
+#define GDN2_RR(IO, DK, DV) \
+  if (dk == DK && dv == DV) \
+    return gdn2::launch_recurrent<IO, DK, DV>(q, k, v, al, b, w, S0, cu, T, H, N, o, Sf, r1, st);
+#define GDN2_RR_DK(IO, DK) GDN2_RR(IO, DK, 16) GDN2_RR(IO, DK, 32) GDN2_RR(IO, DK, 64) GDN2_RR(IO, DK, 128)
   if (dt == GDN2_F32) {
-    GDN2_RR(float, 16) GDN2_RR(float, 32) GDN2_RR(float, 64) GDN2_RR(float, 128)
+    GDN2_RR_DK(float, 16) GDN2_RR_DK(float, 32) GDN2_RR_DK(float, 64) GDN2_RR_DK(float, 128)
   } else {
-    GDN2_RR(gdn2::bf16_t, 16) GDN2_RR(gdn2::bf16_t, 32) GDN2_RR(gdn2::bf16_t, 64)
-    GDN2_RR(gdn2::bf16_t, 128)
+    GDN2_RR_DK(gdn2::bf16_t, 16) GDN2_RR_DK(gdn2::bf16_t, 32) GDN2_RR_DK(gdn2::bf16_t, 64)
+    GDN2_RR_DK(gdn2::bf16_t, 128)
   }
+#undef GDN2_RR_DK
 #undef GDN2_RR
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_decode(gdn2_dtype_t dt, int d, const void *q, const void *k, const void *v,
+hipError_t dispatch_decode(gdn2_dtype_t dt, int dk, int dv, const void *q, const void *k, const void *v,
                            const void *al, const void *b, const void *w, float *S, void *o, int N,
                            int H, hipStream_t st) {
   prof_scope p("decode", st);
-#define GDN2_DD(IO, D) \
-  if (d == D)          \
-    return gdn2::launch_decode<IO, D>(q, k, v, al, b, w, S, o, N, H, st);
+#define GDN2_DD(IO, DK, DV) \
+  if (dk == DK && dv == DV) \
+    return gdn2::launch_decode<IO, DK, DV>(q, k, v, al, b, w, S, o, N, H, st);
+#define GDN2_DD_DK(IO, DK) GDN2_DD(IO, DK, 16) GDN2_DD(IO, DK, 32) GDN2_DD(IO, DK, 64) GDN2_DD(IO, DK, 128)
   if (dt == GDN2_F32) {
-    GDN2_DD(float, 16) GDN2_DD(float, 32) GDN2_DD(float, 64) GDN2_DD(float, 128)
+    GDN2_DD_DK(float, 16) GDN2_DD_DK(float, 32) GDN2_DD_DK(float, 64) GDN2_DD_DK(float, 128)
   } else {
-    GDN2_DD(gdn2::bf16_t, 16) GDN2_DD(gdn2::bf16_t, 32) GDN2_DD(gdn2::bf16_t, 64)
-    GDN2_DD(gdn2::bf16_t, 128)
+    GDN2_DD_DK(gdn2::bf16_t, 16) GDN2_DD_DK(gdn2::bf16_t, 32) GDN2_DD_DK(gdn2::bf16_t, 64)
+    GDN2_DD_DK(gdn2::bf16_t, 128)
   }
+#undef GDN2_DD_DK
 #undef GDN2_DD
   return hipErrorInvalidValue;
 }
@@ -295,6 +299,44 @@ bool sizes_supported(int B, int T, int H, int d, int num_seqs, int chunk, bool p
   if (n > kMaxSeqHeads / H)
     return false;
   return num_slots_for(B, T, static_cast<int>(n), chunk, packed) <= kMaxChunkHeads / H;
+}
+
+// Calls with dk != dv run the chunked kernels on d = max(dk, dv) with the
+// narrower side widened (gdn2_pad.hip says why that is exact).  In front of
+// the widened call's own workspace: widened copies of the narrower side's
+// inputs (q, k, alpha, b when dk < d; v, w and the widened o when dv < d),
+// each slot sized for 4-byte elements (float32 inputs, or layer prep's
+// float32 log-decay), and one d x d float32 state per (sequence, head) for
+// S0 and S_final.
+struct rect_plan {
+  int d;
+  size_t q, k, al, b, v, w, o, state, total;
+};
+
+rect_plan plan_rect(int B, int T, int H, int dk, int dv, int N) {
+  rect_plan p{};
+  p.d = dk > dv ? dk : dv;
+  const size_t slot = align256(static_cast<size_t>(B) * T * H * p.d * 4);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t at = off;
+    off += n;
+    return at;
+  };
+  if (dk < p.d) {
+    p.q = take(slot);
+    p.k = take(slot);
+    p.al = take(slot);
+    p.b = take(slot);
+  }
+  if (dv < p.d) {
+    p.v = take(slot);
+    p.w = take(slot);
+    p.o = take(slot);
+  }
+  p.state = take(align256(static_cast<size_t>(N) * H * p.d * p.d * sizeof(float)));
+  p.total = off;
+  return p;
 }
 
 // ---------------------------------------------------------------- backward --
@@ -670,8 +712,13 @@ extern "C" {
 
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
                                       gdn2_dtype_t dt) {
-  if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
+  if (B <= 0 || T < 0 || H <= 0 || !supported_dim(dk) || !supported_dim(dv) || !supported_chunk(chunk))
     return 0;
+  if (dk != dv) {
+    const int d = dk > dv ? dk : dv;
+    const size_t inner = gdn2_chunk_fwd_workspace_bytes(B, T, H, d, d, num_seqs, chunk, dt);
+    return inner == 0 ? 0 : plan_rect(B, T, H, dk, dv, num_seqs > 0 ? num_seqs : B).total + inner;
+  }
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return 0;
   if (!sizes_supported(B, T, H, dk, B, chunk, false) ||
@@ -695,6 +742,13 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
 
 size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
                                             gdn2_dtype_t dt, uint32_t flags) {
+  if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT) && dk != dv) {
+    if (!supported_dim(dk) || !supported_dim(dv))
+      return 0;
+    const int d = dk > dv ? dk : dv;
+    const size_t inner = gdn2_chunk_fwd_workspace_bytes_flags(B, T, H, d, d, num_seqs, chunk, dt, flags);
+    return inner == 0 ? 0 : plan_rect(B, T, H, dk, dv, num_seqs > 0 ? num_seqs : B).total + inner;
+  }
   if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT)) {
     if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
       return 0;
@@ -747,10 +801,9 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
                 "gdn2_chunk_fwd: the token-by-token path takes neither per-(token, head) gates nor layer prep");
   if (B <= 0 || T < 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: bad sizes B=%d T=%d H=%d", B, T, H);
-  if (dk != dv || !supported_dim(dk))
+  if (!supported_dim(dk) || !supported_dim(dv))
     return fail(GDN2_ERR_UNSUPPORTED,
-                "gdn2_chunk_fwd: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
-                dk, dv);
+                "gdn2_chunk_fwd: unsupported head dims dk=%d dv=%d (need dk, dv in {16,32,64,128})", dk, dv);
   if (!supported_chunk(chunk))
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unsupported chunk %d (need 16 or 64)", chunk);
   const bool packed = cu_seqlens != nullptr;
@@ -773,15 +826,69 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
   for (const void *p : ptrs)
     if (p && !aligned16(p))
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: pointers must be 16-byte aligned");
-  if (!sizes_supported(B, T, H, dk, N, chunk, packed))
+  if (!sizes_supported(B, T, H, dk > dv ? dk : dv, N, chunk, packed))
     return fail(GDN2_ERR_UNSUPPORTED,
                 "gdn2_chunk_fwd: sizes beyond the library's limits (at most 2^40 input elements, 2^24 chunk-heads, "
                 "2^21 sequence-heads)");
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (flags & GDN2_FLAG_RECURRENT) {
-    const hipError_t e = dispatch_recurrent(dt, dk, q, k, v, alpha, b, w, S0, cu_seqlens, T, H, N,
+    const hipError_t e = dispatch_recurrent(dt, dk, dv, q, k, v, alpha, b, w, S0, cu_seqlens, T, H, N,
                                             o, S_final, (flags & GDN2_FLAG_RULE_R1) != 0, st);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+
+  if (dk != dv) {
+    // the chunked kernels on d = max(dk, dv), the narrower side widened in
+    // the front of the workspace, o and S_final narrowed back afterwards
+    const rect_plan rp = plan_rect(B, T, H, dk, dv, N);
+    const int d = rp.d;
+    if (workspace_bytes < rp.total || !workspace)
+      return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                  "gdn2_chunk_fwd: workspace of %zu bytes is smaller than the %zu needed to widen dk=%d dv=%d to %d",
+                  workspace_bytes, rp.total, dk, dv, d);
+    char *wsr = static_cast<char *>(workspace);
+    const long long rows = static_cast<long long>(B) * T * H;
+    const int E = dt == GDN2_BF16 ? 2 : 4;
+    const uint32_t one_bits = dt == GDN2_BF16 ? 0x3F80u : 0x3F800000u;  // 1.0: no decay
+    hipError_t e = hipSuccess;
+    auto widen = [&](const void *src, size_t at, int width, int esz, uint32_t fill) -> const void * {
+      if (e == hipSuccess)
+        e = gdn2::launch_pad(src, wsr + at, rows, 1, width, 1, d, esz, fill, st);
+      return wsr + at;
+    };
+    const void *q2 = q, *k2 = k, *al2 = alpha, *b2 = b, *v2 = v, *w2 = w;
+    if (T > 0 && dk < d) {
+      q2 = widen(q, rp.q, dk, E, 0);
+      k2 = widen(k, rp.k, dk, E, 0);
+      if (!(flags & GDN2_FLAG_SCALAR_ALPHA))  // layer prep: float32 log-decay, 0 = no decay
+        al2 = (flags & GDN2_FLAG_LAYER_PREP) ? widen(alpha, rp.al, dk, 4, 0) : widen(alpha, rp.al, dk, E, one_bits);
+      if (!(flags & GDN2_FLAG_SCALAR_B))
+        b2 = widen(b, rp.b, dk, E, 0);
+    }
+    if (T > 0 && dv < d) {
+      v2 = widen(v, rp.v, dv, E, 0);
+      if (!(flags & GDN2_FLAG_SCALAR_W))
+        w2 = widen(w, rp.w, dv, E, 0);
+    }
+    float *st2 = reinterpret_cast<float *>(wsr + rp.state);
+    if (S0 && e == hipSuccess)
+      e = gdn2::launch_pad(S0, st2, static_cast<long long>(N) * H, dk, dv, d, d, 4, 0, st);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    void *o2 = dv < d ? static_cast<void *>(wsr + rp.o) : o;
+    const gdn2_status_t s = gdn2_chunk_fwd(q2, k2, v2, al2, b2, w2, S0 ? st2 : nullptr, cu_seqlens, B, T, H, d, d,
+                                           num_seqs, chunk, dt, flags, T > 0 ? o2 : o,
+                                           S_final ? st2 : nullptr, wsr + rp.total, workspace_bytes - rp.total,
+                                           stream);
+    if (s != GDN2_OK)
+      return s;  // the widened call's message stands
+    if (T > 0 && dv < d)
+      e = gdn2::launch_pad(o2, o, rows, 1, d, 1, dv, E, 0, st);
+    if (S_final && e == hipSuccess)
+      e = gdn2::launch_pad(st2, S_final, static_cast<long long>(N) * H, d, d, dk, dv, 4, 0, st);
     if (e != hipSuccess)
       return fail(GDN2_ERR_HIP, "gdn2_chunk_fwd: launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -1105,10 +1212,9 @@ gdn2_status_t gdn2_decode_step(const void *q, const void *k, const void *v, cons
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_decode_step: unknown dtype %d", static_cast<int>(dt));
   if (N <= 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: bad sizes N=%d H=%d", N, H);
-  if (dk != dv || !supported_dim(dk))
+  if (!supported_dim(dk) || !supported_dim(dv))
     return fail(GDN2_ERR_UNSUPPORTED,
-                "gdn2_decode_step: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
-                dk, dv);
+                "gdn2_decode_step: unsupported head dims dk=%d dv=%d (need dk, dv in {16,32,64,128})", dk, dv);
   if (!q || !k || !v || !alpha || !b || !w || !S || !o)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: null pointer");
   const void *ptrs[] = {q, k, v, alpha, b, w, S, o};
@@ -1117,7 +1223,7 @@ gdn2_status_t gdn2_decode_step(const void *q, const void *k, const void *v, cons
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_decode_step: pointers must be 16-byte aligned");
   if (static_cast<long long>(N) * H > (1LL << 24) - 1)  // one workgroup of 256 threads per sequence-head
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_decode_step: too many sequence-heads (at most 2^24 - 1)");
-  const hipError_t e = dispatch_decode(dt, dk, q, k, v, alpha, b, w, S, o, N, H,
+  const hipError_t e = dispatch_decode(dt, dk, dv, q, k, v, alpha, b, w, S, o, N, H,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_decode_step: launch failed: %s", hipGetErrorString(e));

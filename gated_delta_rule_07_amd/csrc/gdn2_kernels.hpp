@@ -47,6 +47,11 @@ template <typename IO, int D, int C> constexpr bool scan_r1_supported() {
 }
 template <typename IO, int D, int C> hipError_t launch_chunk_scan_r1(const chunk_args &a, hipStream_t st);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets, hipStream_t st);
+// dst[u][r][c] (Rd x Cd per u) = src[u][r][c] where r < Rs and c < Cs, else
+// the raw bits fill_bits; elements of elem_bytes (2 or 4) bytes
+// (gdn2_pad.hip: widening for calls with dk != dv).
+hipError_t launch_pad(const void *src, void *dst, long long U, int Rs, int Cs, int Rd, int Cd, int elem_bytes,
+                      uint32_t fill_bits, hipStream_t st);
 template <typename IO, int D, int C, int NG> bool fused_supported();
 template <typename IO, int D, int C, int NG> hipError_t launch_fused(const chunk_args &a, hipStream_t st);
 
@@ -85,11 +90,11 @@ template <int D>
 hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
                               float *S_in, float *S_final, hipStream_t st, bool reverse = false);
 
-template <typename IO, int D>
+template <typename IO, int DK, int DV>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,
                          const void *b, const void *w, float *S, void *o, int N, int H,
                          hipStream_t st);
-template <typename IO, int D>
+template <typename IO, int DK, int DV>
 hipError_t launch_recurrent(const void *q, const void *k, const void *v, const void *al,
                             const void *b, const void *w, const float *S0, const int32_t *cu,
                             int T, int H, int num_seqs, void *o, float *S_final, bool r1,

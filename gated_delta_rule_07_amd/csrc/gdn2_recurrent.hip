@@ -194,13 +194,13 @@ __global__ void __launch_bounds__((rec_shape<DK, DV>::NT))
 }
 
 // ------------------------------------------------------------- launchers --
-template <typename IO, int D>
+template <typename IO, int DK, int DV>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *al,
                          const void *b, const void *w, float *S, void *o, int N, int H,
                          hipStream_t st) {
-  typedef rec_shape<D, D> R;
+  typedef rec_shape<DK, DV> R;
   const int units = N * H;
-  hipLaunchKernelGGL((gdn2_decode_kernel<IO, D, D>), dim3(units), dim3(R::NT), 0, st,
+  hipLaunchKernelGGL((gdn2_decode_kernel<IO, DK, DV>), dim3(units), dim3(R::NT), 0, st,
                      static_cast<const IO *>(q), static_cast<const IO *>(k),
                      static_cast<const IO *>(v), static_cast<const IO *>(al),
                      static_cast<const IO *>(b), static_cast<const IO *>(w), S,
@@ -208,20 +208,20 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const void
   return hipGetLastError();
 }
 
-template <typename IO, int D>
+template <typename IO, int DK, int DV>
 hipError_t launch_recurrent(const void *q, const void *k, const void *v, const void *al,
                             const void *b, const void *w, const float *S0, const int32_t *cu,
                             int T, int H, int num_seqs, void *o, float *S_final, bool r1,
                             hipStream_t st) {
-  typedef rec_shape<D, D> R;
+  typedef rec_shape<DK, DV> R;
   if (r1)
-    hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, D, D, true>), dim3(num_seqs * H), dim3(R::NT), 0, st,
+    hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, DK, DV, true>), dim3(num_seqs * H), dim3(R::NT), 0, st,
                        static_cast<const IO *>(q), static_cast<const IO *>(k),
                        static_cast<const IO *>(v), static_cast<const IO *>(al),
                        static_cast<const IO *>(b), static_cast<const IO *>(w), S0, cu, T, H,
                        num_seqs, static_cast<IO *>(o), S_final);
   else
-    hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, D, D, false>), dim3(num_seqs * H), dim3(R::NT), 0, st,
+    hipLaunchKernelGGL((gdn2_recurrent_kernel<IO, DK, DV, false>), dim3(num_seqs * H), dim3(R::NT), 0, st,
                        static_cast<const IO *>(q), static_cast<const IO *>(k),
                        static_cast<const IO *>(v), static_cast<const IO *>(al),
                        static_cast<const IO *>(b), static_cast<const IO *>(w), S0, cu, T, H,
@@ -229,21 +229,24 @@ hipError_t launch_recurrent(const void *q, const void *k, const void *v, const v
   return hipGetLastError();
 }
 
-#define GDN2_INST_REC(IO, D)                                                                   \
-  template hipError_t launch_decode<IO, D>(const void *, const void *, const void *,         \
-                                           const void *, const void *, const void *, float *, \
-                                           void *, int, int, hipStream_t);                    \
-  template hipError_t launch_recurrent<IO, D>(                                                \
+// every (dk, dv) pair of {16, 32, 64, 128}: the state is dk x dv
+#define GDN2_INST_REC(IO, DK, DV)                                                              \
+  template hipError_t launch_decode<IO, DK, DV>(const void *, const void *, const void *,    \
+                                                const void *, const void *, const void *,     \
+                                                float *, void *, int, int, hipStream_t);       \
+  template hipError_t launch_recurrent<IO, DK, DV>(                                           \
       const void *, const void *, const void *, const void *, const void *, const void *,     \
       const float *, const int32_t *, int, int, int, void *, float *, bool, hipStream_t);
+#define GDN2_INST_REC_DK(IO, DK) \
+  GDN2_INST_REC(IO, DK, 16) GDN2_INST_REC(IO, DK, 32) GDN2_INST_REC(IO, DK, 64) GDN2_INST_REC(IO, DK, 128)
 
-GDN2_INST_REC(float, 16)
-GDN2_INST_REC(float, 32)
-GDN2_INST_REC(float, 64)
-GDN2_INST_REC(float, 128)
-GDN2_INST_REC(bf16_t, 16)
-GDN2_INST_REC(bf16_t, 32)
-GDN2_INST_REC(bf16_t, 64)
-GDN2_INST_REC(bf16_t, 128)
+GDN2_INST_REC_DK(float, 16)
+GDN2_INST_REC_DK(float, 32)
+GDN2_INST_REC_DK(float, 64)
+GDN2_INST_REC_DK(float, 128)
+GDN2_INST_REC_DK(bf16_t, 16)
+GDN2_INST_REC_DK(bf16_t, 32)
+GDN2_INST_REC_DK(bf16_t, 64)
+GDN2_INST_REC_DK(bf16_t, 128)
 
 }  // namespace gdn2

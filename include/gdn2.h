@@ -40,7 +40,17 @@
  *     GDN2_ERR_HIP.  Conditions only the device could see (a non-monotone
  *     cu_seqlens, NaN/Inf inputs) are not detected: NaN propagates to the
  *     outputs of its sequence and head.
- *   - Supported sizes: dk == dv in {16, 32, 64, 128}; chunk in {16, 64}.
+ *   - Supported sizes: dk and dv each in {16, 32, 64, 128}; chunk in
+ *     {16, 64}.  gdn2_chunk_fwd and gdn2_decode_step take dk != dv; the
+ *     backward, the segment maps and their combine, and the allocation-free
+ *     forward take dk == dv (GDN2_ERR_UNSUPPORTED otherwise).  The decode
+ *     step and the token-by-token path are built for every (dk, dv) pair.
+ *     The chunked paths run a call with dk != dv on d = max(dk, dv): the
+ *     narrower side's inputs are widened in the front of the workspace with
+ *     channels that cannot reach the result (extra key channels with
+ *     q = k = b = 0 and no decay, whose state rows stay zero; extra value
+ *     channels with v = w = 0, whose state columns stay zero), the d x d
+ *     call runs, and o and S_final are narrowed back.
  *   - Decay range: any alpha in [0, 1], alpha = 0 (a full erase of that
  *     channel) included, on every path.  The chunked kernels build every
  *     decay factor from sums of log decays (never the difference of two
@@ -199,7 +209,8 @@ size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv,
  *               gdn2_chunk_fwd_workspace_bytes(...) bytes (NULL allowed when
  *               that is 0).  Its contents on entry are irrelevant, except
  *               with GDN2_FLAG_PREPARED.  On return (two-pass path) it holds
- *               the chunks' intermediates.
+ *               the chunks' intermediates (with dk != dv: after the widened
+ *               copies of the inputs and one d x d state per sequence-head).
  * T == 0 is allowed: nothing but S_final = S0 (or zeros) is written. */
 gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
                              const void *b, const void *w, const float *S0,

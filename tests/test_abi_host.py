@@ -61,7 +61,8 @@ def call_fwd(L, *, ptr=FAKE, B=1, T=64, H=1, dk=16, dv=16, N=0, chunk=16, dt=F32
 
 def test_fwd_rejects_before_launch(L):
     assert call_fwd(L, dk=24, dv=24) == 2
-    assert call_fwd(L, dk=64, dv=32) == 2
+    assert call_fwd(L, dk=64, dv=48) == 2
+    assert call_fwd(L, dk=16, dv=64, ws_bytes=100) == 3   # dk != dv widens in the workspace: size-checked first
     assert call_fwd(L, chunk=32) == 2
     assert call_fwd(L, dt=7) == 2
     assert call_fwd(L, B=0) == 1
@@ -95,7 +96,7 @@ def test_workspace_bytes(L):
     # in whole KiB), Ut (16 KiB); in front of them the 256-byte chunk table
     w = f(8, 4096, 16, 128, 128, 0, 64, BF16)
     assert w == 256 + 8 * 64 * 16 * 70 * 1024
-    assert f(8, 4096, 16, 128, 64, 0, 64, BF16) == 0
+    assert f(8, 4096, 16, 128, 64, 0, 64, BF16) > w   # dk != dv: the square call plus the widened copies
     assert f(1, 100, 2, 64, 64, 5, 16, F32) >= f(1, 100, 2, 64, 64, 0, 16, F32)
 
 
@@ -296,3 +297,19 @@ def test_sizes_at_the_limits(L):
     assert call_fwd(L, B=big, T=big, H=big, ws_bytes=1 << 40) == 2
     assert call_fwd(L, T=big, H=big, ws_bytes=1 << 40) == 2
     assert call_fwd(L, B=1, T=2 ** 26, H=16, dk=128, dv=128, chunk=64, ws_bytes=1 << 50) == 2
+
+
+def test_workspace_bytes_rectangular_heads(L):
+    """dk != dv: the square call's workspace on d = max(dk, dv) plus the
+    widened copies of the narrower side and one d x d state per
+    (sequence, head), each rounded up to 256 bytes."""
+    f = L.gdn2_chunk_fwd_workspace_bytes
+    for dk, dv in ((16, 64), (64, 16), (128, 64), (32, 128)):
+        d = max(dk, dv)
+        for B, T, H, n, C, dt in ((2, 200, 3, 0, 64, BF16), (1, 300, 4, 3, 16, F32)):
+            sq = f(B, T, H, d, d, n, C, dt)
+            slot = -(-B * T * H * d * 4 // 256) * 256
+            N = n if n > 0 else B
+            state = -(-N * H * d * d * 4 // 256) * 256
+            assert f(B, T, H, dk, dv, n, C, dt) == sq + (4 if dk < d else 3) * slot + state
+    assert f(2, 64, 2, 16, 48, 0, 64, BF16) == 0

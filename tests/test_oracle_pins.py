@@ -341,3 +341,32 @@ def test_layer_prep_feeds_the_recurrence():
     o2, S2 = oracle.fwd(raw["q"], raw["k"], inp["v"], raw["alpha"], raw["b"], raw["w"], S0=inp["S0"])
     assert np.abs(o1 - o2).max() <= 1e-6 * np.abs(o1).max()
     assert np.abs(S1 - S2).max() <= 1e-6 * np.abs(S1).max()
+
+
+@pytest.mark.parametrize("dk,dv", [(3, 5), (6, 2)])
+@pytest.mark.parametrize("rule", ["R5", "R1"])
+def test_P9_rectangular_head_equals_widened_square(dk, dv, rule):
+    """A head with dk != dv gives what the square head of width
+    d = max(dk, dv) gives on widened inputs (extra key channels: q = k = b = 0,
+    alpha = 1; extra value channels: v = w = 0), on its dk x dv corner; the
+    widened rows and columns of the square state and the widened outputs stay
+    exactly zero.  A dk/dv index swapped anywhere in the oracle breaks it."""
+    inp = gi.make_chunk_inputs(2, 9, 2, dk, dv, "f32", seed=61 + dk, s0="normal")
+    d = max(dk, dv)
+
+    def widen(x, width, fill):
+        out = torch.full(x.shape[:-1] + (d,), fill, dtype=torch.float64)
+        out[..., :width] = x.double()
+        return out
+
+    wide = {"q": widen(inp["q"], dk, 0.0), "k": widen(inp["k"], dk, 0.0), "alpha": widen(inp["alpha"], dk, 1.0),
+            "b": widen(inp["b"], dk, 0.0), "v": widen(inp["v"], dv, 0.0), "w": widen(inp["w"], dv, 0.0)}
+    S0 = torch.zeros(inp["S0"].shape[:2] + (d, d), dtype=torch.float64)
+    S0[:, :, :dk, :dv] = inp["S0"].double()
+    names = ("q", "k", "v", "alpha", "b", "w")
+    o_r, S_r = oracle.fwd(*(inp[n] for n in names), S0=inp["S0"], rule=rule)
+    o_s, S_s = oracle.fwd(*(wide[n] for n in names), S0=S0, rule=rule)
+    assert o_r.shape[-1] == dv and S_r.shape[-2:] == (dk, dv)
+    np.testing.assert_allclose(o_r, o_s[..., :dv], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S_r, S_s[:, :, :dk, :dv], rtol=0, atol=1e-12)
+    assert np.all(o_s[..., dv:] == 0) and np.all(S_s[:, :, dk:, :] == 0) and np.all(S_s[:, :, :, dv:] == 0)
