@@ -339,6 +339,41 @@ rect_plan plan_rect(int B, int T, int H, int dk, int dv, int N) {
   return p;
 }
 
+// The backward's widened call (dk != dv): slots for the narrower side's
+// inputs and their gradients (q, k, alpha, b and dq, dk, dalpha, db when
+// dk < d; v, w, dout and dv, dw when dv < d), then three d x d float32
+// states per (sequence, head): S0, dL/dS_final and dL/dS0.
+struct rect_bwd_plan {
+  int d;
+  size_t in[6], grad[6], dout, s0, dsf, ds0, total;  // in/grad index: q, k, v, alpha, b, w
+};
+
+rect_bwd_plan plan_rect_bwd(int B, int T, int H, int dk, int dv, int N) {
+  rect_bwd_plan p{};
+  p.d = dk > dv ? dk : dv;
+  const size_t slot = align256(static_cast<size_t>(B) * T * H * p.d * 4);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t at = off;
+    off += n;
+    return at;
+  };
+  const bool key_side[6] = {true, true, false, true, true, false};
+  for (int i = 0; i < 6; ++i)
+    if ((key_side[i] && dk < p.d) || (!key_side[i] && dv < p.d)) {
+      p.in[i] = take(slot);
+      p.grad[i] = take(slot);
+    }
+  if (dv < p.d)
+    p.dout = take(slot);
+  const size_t st = align256(static_cast<size_t>(N) * H * p.d * p.d * sizeof(float));
+  p.s0 = take(st);
+  p.dsf = take(st);
+  p.ds0 = take(st);
+  p.total = off;
+  return p;
+}
+
 // ---------------------------------------------------------------- backward --
 // The backward's share of the segment schedule (see run_segments): N
 // sequences of T_total tokens in all, G segments each, and its workspace
@@ -965,8 +1000,13 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
 
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
                                       gdn2_dtype_t dt) {
-  if (B <= 0 || T < 0 || H <= 0 || dk != dv || !supported_dim(dk) || !supported_chunk(chunk))
+  if (B <= 0 || T < 0 || H <= 0 || !supported_dim(dk) || !supported_dim(dv) || !supported_chunk(chunk))
     return 0;
+  if (dk != dv) {
+    const int d = dk > dv ? dk : dv;
+    const size_t inner = gdn2_chunk_bwd_workspace_bytes(B, T, H, d, d, num_seqs, chunk, dt);
+    return inner == 0 ? 0 : plan_rect_bwd(B, T, H, dk, dv, num_seqs > 0 ? num_seqs : B).total + inner;
+  }
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return 0;
   if (!sizes_supported(B, T, H, dk, B, chunk, false) ||
@@ -996,10 +1036,9 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
                 "gdn2_chunk_bwd: flags 0x%x: only the gate layout and layer prep flags apply to the backward", flags);
   if (B <= 0 || T < 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: bad sizes B=%d T=%d H=%d", B, T, H);
-  if (dk != dv || !supported_dim(dk))
+  if (!supported_dim(dk) || !supported_dim(dv))
     return fail(GDN2_ERR_UNSUPPORTED,
-                "gdn2_chunk_bwd: unsupported head dims dk=%d dv=%d (need dk == dv in {16,32,64,128})",
-                dk, dv);
+                "gdn2_chunk_bwd: unsupported head dims dk=%d dv=%d (need dk, dv in {16,32,64,128})", dk, dv);
   if (!supported_chunk(chunk))
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: unsupported chunk %d (need 16 or 64)", chunk);
   const bool packed = cu_seqlens != nullptr;
@@ -1024,10 +1063,77 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   for (const void *p : ptrs)
     if (p && !aligned16(p))
       return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: pointers must be 16-byte aligned");
-  if (!sizes_supported(B, T, H, dk, N, chunk, packed))
+  if (!sizes_supported(B, T, H, dk > dv ? dk : dv, N, chunk, packed))
     return fail(GDN2_ERR_UNSUPPORTED,
                 "gdn2_chunk_bwd: sizes beyond the library's limits (at most 2^40 input elements, 2^24 chunk-heads, "
                 "2^21 sequence-heads)");
+  if (dk != dv) {
+    // the square backward on d = max(dk, dv) (see gdn2_chunk_fwd): the
+    // narrower side's inputs, dout and the states widened in the front of
+    // the workspace, its gradients and dL/dS0 narrowed back; gradients of
+    // the widened channels are dropped (those channels never reach o)
+    const rect_bwd_plan rp = plan_rect_bwd(B, T, H, dk, dv, N);
+    const int d = rp.d;
+    if (workspace_bytes < rp.total || !workspace)
+      return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                  "gdn2_chunk_bwd: workspace of %zu bytes is smaller than the %zu needed to widen dk=%d dv=%d to %d",
+                  workspace_bytes, rp.total, dk, dv, d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *wsr = static_cast<char *>(workspace);
+    const long long rows = static_cast<long long>(B) * T * H;
+    const long long units = static_cast<long long>(N) * H;
+    const int E = dt == GDN2_BF16 ? 2 : 4;
+    const bool lp = (flags & GDN2_FLAG_LAYER_PREP) != 0;
+    const uint32_t one_bits = dt == GDN2_BF16 ? 0x3F80u : 0x3F800000u;
+    const void *in[6] = {q, k, v, alpha, b, w};
+    void *grad[6] = {dq, dk_out, dv_out, dalpha, db, dw};
+    const int width[6] = {dk, dk, dv, dk, dk, dv};
+    const bool scalar[6] = {false, false, false, (flags & GDN2_FLAG_SCALAR_ALPHA) != 0,
+                            (flags & GDN2_FLAG_SCALAR_B) != 0, (flags & GDN2_FLAG_SCALAR_W) != 0};
+    const int esz[6] = {E, E, E, lp ? 4 : E, E, E};                // alpha: float32 log-decay under layer prep
+    const uint32_t fill[6] = {0, 0, 0, lp ? 0u : one_bits, 0, 0};  // no decay on widened channels
+    const void *in2[6];
+    void *grad2[6];
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 6; ++i) {
+      in2[i] = in[i];
+      grad2[i] = grad[i];
+      if (width[i] < d && !scalar[i] && T > 0) {
+        if (e == hipSuccess)
+          e = gdn2::launch_pad(in[i], wsr + rp.in[i], rows, 1, width[i], 1, d, esz[i], fill[i], st);
+        in2[i] = wsr + rp.in[i];
+        grad2[i] = wsr + rp.grad[i];
+      }
+    }
+    const void *dout2 = dout;
+    if (dv < d && T > 0) {
+      if (e == hipSuccess)
+        e = gdn2::launch_pad(dout, wsr + rp.dout, rows, 1, dv, 1, d, E, 0, st);
+      dout2 = wsr + rp.dout;
+    }
+    float *s0w = reinterpret_cast<float *>(wsr + rp.s0), *dsfw = reinterpret_cast<float *>(wsr + rp.dsf),
+          *ds0w = reinterpret_cast<float *>(wsr + rp.ds0);
+    if (S0 && e == hipSuccess)
+      e = gdn2::launch_pad(S0, s0w, units, dk, dv, d, d, 4, 0, st);
+    if (dS_final && e == hipSuccess)
+      e = gdn2::launch_pad(dS_final, dsfw, units, dk, dv, d, d, 4, 0, st);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
+    const gdn2_status_t s = gdn2_chunk_bwd(
+        in2[0], in2[1], in2[2], in2[3], in2[4], in2[5], S0 ? s0w : nullptr, cu_seqlens, B, T, H, d, d, num_seqs,
+        chunk, dt, flags, dout2, dS_final ? dsfw : nullptr, grad2[0], grad2[1], grad2[2], grad2[3], grad2[4],
+        grad2[5], dS0 ? ds0w : nullptr, wsr + rp.total, workspace_bytes - rp.total, stream);
+    if (s != GDN2_OK)
+      return s;  // the widened call's message stands
+    for (int i = 0; i < 6; ++i)
+      if (grad2[i] != grad[i] && e == hipSuccess)
+        e = gdn2::launch_pad(grad2[i], grad[i], rows, 1, d, 1, width[i], esz[i], 0, st);
+    if (dS0 && e == hipSuccess)
+      e = gdn2::launch_pad(ds0w, dS0, units, d, d, dk, dv, 4, 0, st);
+    if (e != hipSuccess)
+      return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   const bwd_plan plan = plan_bwd(dt, B, T, H, dk, N, chunk, packed);
   if (workspace_bytes < plan.total || !workspace)
     return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,

@@ -41,8 +41,8 @@
  *     cu_seqlens, NaN/Inf inputs) are not detected: NaN propagates to the
  *     outputs of its sequence and head.
  *   - Supported sizes: dk and dv each in {16, 32, 64, 128}; chunk in
- *     {16, 64}.  gdn2_chunk_fwd and gdn2_decode_step take dk != dv; the
- *     backward, the segment maps and their combine, and the allocation-free
+ *     {16, 64}.  gdn2_chunk_fwd, gdn2_chunk_bwd and gdn2_decode_step take
+ *     dk != dv; the segment maps and their combine, and the allocation-free
  *     forward take dk == dv (GDN2_ERR_UNSUPPORTED otherwise).  The decode
  *     step and the token-by-token path are built for every (dk, dv) pair.
  *     The chunked paths run a call with dk != dv on d = max(dk, dv): the
@@ -50,7 +50,8 @@
  *     channels that cannot reach the result (extra key channels with
  *     q = k = b = 0 and no decay, whose state rows stay zero; extra value
  *     channels with v = w = 0, whose state columns stay zero), the d x d
- *     call runs, and o and S_final are narrowed back.
+ *     call runs, and o and S_final (the backward: the gradients and dS0)
+ *     are narrowed back.
  *   - Decay range: any alpha in [0, 1], alpha = 0 (a full erase of that
  *     channel) included, on every path.  The chunked kernels build every
  *     decay factor from sums of log decays (never the difference of two
@@ -281,7 +282,9 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               gradients.
  *   dS0       : dL/dS0 [N, H, dk, dv] float32, or NULL.
  *   workspace : device scratch of at least gdn2_chunk_bwd_workspace_bytes(...)
- *               bytes; its contents on entry are irrelevant.
+ *               bytes; its contents on entry are irrelevant (with dk != dv
+ *               its front holds the widened inputs, dout, their gradients
+ *               and three d x d states per sequence-head).
  * The kernels recompute the forward's per-chunk quantities and the state
  * entering every chunk; no forward output needs to be kept.  For the shapes
  * where gdn2_chunk_fwd takes its segment schedule (a few long sequences),

@@ -174,7 +174,7 @@ def call_bwd(L, *, ptr=FAKE, B=1, T=64, H=1, dk=16, dv=16, N=0, chunk=16, dt=F32
 
 def test_bwd_rejects_before_launch(L):
     assert call_bwd(L, dk=24, dv=24) == 2
-    assert call_bwd(L, dk=64, dv=32) == 2
+    assert call_bwd(L, dk=64, dv=48) == 2
     assert call_bwd(L, chunk=32) == 2
     assert call_bwd(L, dt=7) == 2
     assert call_bwd(L, B=0) == 1
@@ -303,7 +303,7 @@ def test_workspace_bytes_rectangular_heads(L):
     """dk != dv: the square call's workspace on d = max(dk, dv) plus the
     widened copies of the narrower side and one d x d state per
     (sequence, head), each rounded up to 256 bytes."""
-    f = L.gdn2_chunk_fwd_workspace_bytes
+    f, fb = L.gdn2_chunk_fwd_workspace_bytes, L.gdn2_chunk_bwd_workspace_bytes
     for dk, dv in ((16, 64), (64, 16), (128, 64), (32, 128)):
         d = max(dk, dv)
         for B, T, H, n, C, dt in ((2, 200, 3, 0, 64, BF16), (1, 300, 4, 3, 16, F32)):
@@ -312,4 +312,10 @@ def test_workspace_bytes_rectangular_heads(L):
             N = n if n > 0 else B
             state = -(-N * H * d * d * 4 // 256) * 256
             assert f(B, T, H, dk, dv, n, C, dt) == sq + (4 if dk < d else 3) * slot + state
+            # the backward: an input and a gradient slot for each of the
+            # narrower side's tensors (q, k, alpha, b or v, w, plus dout),
+            # and three states: S0, dL/dS_final, dL/dS0
+            sqb = fb(B, T, H, d, d, n, C, dt)
+            assert fb(B, T, H, dk, dv, n, C, dt) == sqb + (8 if dk < d else 5) * slot + 3 * state
     assert f(2, 64, 2, 16, 48, 0, 64, BF16) == 0
+    assert fb(2, 64, 2, 16, 48, 0, 64, BF16) == 0

@@ -218,3 +218,74 @@ def test_bwd_rejects_path_and_rule_flags(g):
                                 grads["dout"].cuda().data_ptr(), None, *(o.data_ptr() for o in outs), None,
                                 ws.data_ptr(), ws.numel(), None)
         assert st == 2
+
+
+RECT_CASES = [  # dtype, dk, dv, chunk, B, T, H, s0, dS_final
+    ("f32", 16, 64, 16, 2, 77, 2, "normal", True),
+    ("f32", 128, 32, 64, 1, 130, 2, "normal", True),
+    ("bf16", 64, 128, 64, 2, 100, 2, None, True),
+    ("bf16", 128, 16, 64, 1, 150, 2, "normal", False),
+]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,chunk,B,T,H,s0,with_dS", RECT_CASES)
+def test_bwd_rect_heads(g, dtype, dk, dv, chunk, B, T, H, s0, with_dS):
+    """dk != dv: the square backward on max(dk, dv) over widened inputs,
+    every gradient and dL/dS0 narrowed back, against the oracle."""
+    seed = 140 + dk + 3 * dv + T
+    inp = gi.make_chunk_inputs(B, T, H, dk, dv, dtype, seed, s0=s0)
+    grads = gi.make_bwd_grads(B, T, H, dk, dv, dtype, seed, with_dS=with_dS)
+    print(f"case rect {dtype} dk={dk} dv={dv} C={chunk} B={B} T={T} H={H}", flush=True)
+    got = gpu_bwd(g, inp, grads, chunk)
+    ref = oracle.bwd(*(inp[n] for n in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"])
+    for name in GRADS + ("dS0",):
+        assert got[name].shape == np.asarray(ref[name]).shape, name
+    check(got, ref, TOL[dtype], f"rect {dtype} {dk}x{dv} C={chunk}")
+
+
+def test_bwd_rect_heads_gates_and_packed(g):
+    """dk != dv with b, w and alpha per (token, head) (their gradients are
+    [B, T, H], not widened) and with packed sequences."""
+    from oracle import layer_prep as lp
+    inp = gi.make_chunk_inputs(2, 120, 2, 64, 32, "f32", seed=151, s0="normal", scalar_beta=True)
+    grads = gi.make_bwd_grads(2, 120, 2, 64, 32, "f32", 151, with_dS=True)
+    full, compact = dict(inp), dict(inp)
+    for x in ("b", "w", "alpha"):
+        s = inp[x][..., 0].contiguous()
+        compact[x] = s
+        full[x] = s[..., None].expand_as(inp[x]).contiguous()
+    print("case rect per-token gates", flush=True)
+    got = gpu_bwd_raw(g, compact, grads, 64)
+    ref = oracle.bwd(*(full[n] for n in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"])
+    for name, x in (("db", "b"), ("dw", "w"), ("dalpha", "alpha")):
+        ref[name] = lp.sum_to_layout(ref[name], compact[x].float().numpy())
+    check(got, ref, TOL["f32"], "rect per-token gates")
+    lens = [70, 0, 1, 64, 130, 15]
+    cu = gi.cu_seqlens_from(lens)
+    inp = gi.make_chunk_inputs(1, int(cu[-1]), 2, 32, 128, "bf16", seed=152, s0="normal", num_seqs=len(lens))
+    grads = gi.make_bwd_grads(1, int(cu[-1]), 2, 32, 128, "bf16", 152, with_dS=True, num_seqs=len(lens))
+    print("case rect packed", flush=True)
+    got = gpu_bwd(g, inp, grads, 64, cu=cu)
+    ref = oracle.bwd(*(inp[n] for n in NAMES), grads["dout"], S0=inp["S0"], dS_final=grads["dS_final"],
+                     cu_seqlens=cu)
+    check(got, ref, TOL["bf16"], "rect packed")
+
+
+@pytest.mark.parametrize("dtype,dk,dv,scalar", [("f32", 32, 64, False), ("bf16", 128, 64, True)])
+def test_bwd_rect_heads_layer_prep(g, dtype, dk, dv, scalar):
+    """dk != dv under layer prep: the widened key channels carry log-decay 0
+    and zero q, k; the widened value channels zero v (their sigmoid gates
+    then act on zeros)."""
+    from oracle import layer_prep as lp
+    raw = gi.make_layer_inputs(2, 100, 2, dk, dv, dtype, seed=960 + dk, s0="normal", scalar_beta=scalar)
+    grads = gi.make_bwd_grads(2, 100, 2, dk, dv, dtype, seed=960 + dk)
+    prep = lp.layer_prep(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"])
+    width = {"q": dk, "k": dk, "alpha": dk, "b": dk, "w": dv}
+    full = {x: (prep[x][..., None] * np.ones(width[x]) if prep[x].ndim == 3 else prep[x]) for x in width}
+    print(f"case rect layer prep {dtype} dk={dk} dv={dv} scalar={scalar}", flush=True)
+    got = gpu_bwd_raw(g, raw, grads, 64, layer_prep=True)
+    gp = oracle.bwd(full["q"], full["k"], raw["v"], full["alpha"], full["b"], full["w"], grads["dout"],
+                    S0=raw["S0"], dS_final=grads["dS_final"])
+    ref = lp.layer_prep_bwd(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"], gp)
+    ref["dS0"] = gp["dS0"]
+    check(got, ref, TOL[dtype], f"rect layer prep {dtype} {dk}x{dv} scalar={scalar}")
