@@ -532,8 +532,9 @@ struct bwd_plan {
 bwd_plan plan_bwd(gdn2_dtype_t dt, int B, int T, int H, int d, int N, int chunk, bool packed) {
   bwd_plan p{};
   const size_t slots = static_cast<size_t>(num_slots_for(B, T, N, chunk, packed));
-  // a state as two sets of (d/16)^2 fragment tiles of the I/O type
-  const size_t sq = 2 * static_cast<size_t>(d) * d * (dt == GDN2_BF16 ? 2 : 4);
+  // a state as (d/16)^2 fragment tiles of the I/O type: one set (ColFrag)
+  // for bfloat16, two (ColFrag, RowFrag) for float32
+  const size_t sq = (dt == GDN2_BF16 ? 1 : 2) * static_cast<size_t>(d) * d * (dt == GDN2_BF16 ? 2 : 4);
   p.table = packed ? align256(static_cast<size_t>(N + 1) * sizeof(int32_t)) : 0;
   p.blocks = slots * H * chunk_block_bytes_rt(dt, d, chunk);
   p.states = align256(slots * H * sq);

@@ -183,7 +183,8 @@ __global__ void __launch_bounds__(64 * dstate_cfg<D>::NW) gdn2_bwd_dstate_kernel
     for (int kk = 0; kk < NK; ++kk) {
       dhf[kk] = F::from(dh[kk]);  // ColFrag(dH tile (kk, j))
       dhf[kk].st(dp + ST_::COL + ST_::off(kk, j), lane);
-      F::from(transpose_io(dhf[kk], eye, lane)).st(dp + ST_::ROW + ST_::off(kk, j), lane);
+      if constexpr (ST_::HAS_ROW)
+        F::from(transpose_io(dhf[kk], eye, lane)).st(dp + ST_::ROW + ST_::off(kk, j), lane);
     }
     F xf[NB];  // Kbar dH, ColFrag tiles (tt, j)
 #pragma unroll
@@ -817,7 +818,34 @@ __global__ void __launch_bounds__(64 * (C / 16)) gdn2_bwd_grad_kernel(bwd_args b
     }
   }
   lds_barrier();  // dO of the other sub-blocks (and the staged column layouts) are no longer read
-  stage_states(ST_::ROW);  // row layouts of S and dH, for dq, de, dk and d gamma_C
+  // row layouts of S and dH, for dq, de, dk and d gamma_C: staged from the
+  // stored copy, or (bfloat16 states carry the column layout only) re-laid
+  // in place, each wave turning its share of the staged tiles from ColFrag
+  // to RowFrag with one identity product per tile (exact)
+  if constexpr (ST_::HAS_ROW) {
+    stage_states(ST_::ROW);
+  } else {
+    static_assert(L::STAGE, "column-only states are read through the staged copy");
+    constexpr int NTILE = 2 * NK * NK, PER = (NTILE + NB - 1) / NB, BATCH = PER < 8 ? PER : 8;
+    const F eye = identity_colfrag<IO>(lane);
+    unsigned char *stg = smb + L::STG;
+#pragma unroll 1
+    for (int r0 = 0; r0 < PER; r0 += BATCH) {
+      F x[BATCH];
+#pragma unroll
+      for (int r = 0; r < BATCH; ++r) {
+        const int p = wv + NB * (r0 + r);
+        if (r0 + r < PER && p < NTILE)
+          x[r] = F::ld(stg + static_cast<size_t>(p) * F::TILE_BYTES, lane);
+      }
+#pragma unroll
+      for (int r = 0; r < BATCH; ++r) {
+        const int p = wv + NB * (r0 + r);
+        if (r0 + r < PER && p < NTILE)
+          F::from(transpose_io(x[r], eye, lane)).st(stg + static_cast<size_t>(p) * F::TILE_BYTES, lane);
+      }
+    }
+  }
 #pragma unroll
   for (int n = 0; n < NK; ++n)
     stm_row(DOZ, PDL, 16 * I, 16 * n, lane, dyv[n]);

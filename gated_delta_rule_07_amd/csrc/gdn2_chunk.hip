@@ -382,7 +382,8 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1, ST>::NCW + sc
         for (int j = 0; j < CPW; ++j) {
           const F sc = F::from(S[kk][j]);  // ColFrag(S tile (kk, vt0 + j))
           sc.st(sp + ST_::COL + ST_::off(kk, vt0 + j), lane);
-          F::from(transpose_io(sc, eye, lane)).st(sp + ST_::ROW + ST_::off(kk, vt0 + j), lane);
+          if constexpr (ST_::HAS_ROW)
+            F::from(transpose_io(sc, eye, lane)).st(sp + ST_::ROW + ST_::off(kk, vt0 + j), lane);
         }
     }
     // o goes through a global-address-space pointer so that the compiler

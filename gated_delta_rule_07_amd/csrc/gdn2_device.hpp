@@ -314,11 +314,15 @@ __device__ __forceinline__ f32x4 transpose_f32(f32x4 x, int lane) {
 
 // A dk x dv float32 state handed between the backward's kernels as fragment
 // tiles of the I/O type: the NK x NK tiles (kk, n) (rows 16kk.., columns
-// 16n..) as ColFrag, then the same tiles as RowFrag.  BYTES per chunk-head.
+// 16n..) as ColFrag, then (float32 only: HAS_ROW) the same tiles as RowFrag.
+// A bfloat16 reader forms the RowFrag of a tile from its ColFrag with one
+// identity product (transpose_frag, exact), which costs less than moving a
+// second copy through HBM.  BYTES per chunk-head.
 template <typename IO, int D> struct state_tiles {
   static constexpr int NK = D / 16;
   static constexpr size_t TB = frag<IO>::TILE_BYTES;
-  static constexpr size_t COL = 0, ROW = static_cast<size_t>(NK) * NK * TB, BYTES = 2 * ROW;
+  static constexpr bool HAS_ROW = sizeof(IO) != 2;
+  static constexpr size_t COL = 0, ROW = static_cast<size_t>(NK) * NK * TB, BYTES = (HAS_ROW ? 2 : 1) * ROW;
   __host__ __device__ static constexpr size_t off(int kk, int n) { return static_cast<size_t>(kk * NK + n) * TB; }
 };
 

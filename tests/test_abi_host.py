@@ -192,9 +192,10 @@ def test_bwd_rejects_before_launch(L):
 def test_bwd_workspace_bytes(L):
     n = L.gdn2_chunk_bwd_workspace_bytes(2, 200, 3, 64, 64, 0, 64, BF16)
     fwd = L.gdn2_chunk_fwd_workspace_bytes(2, 200, 3, 64, 64, 0, 64, BF16)
-    # the forward's blocks (its workspace less the chunk table) plus two
-    # float32 states per chunk-head (2 sequences x 4 chunks x 3 heads)
-    assert n >= fwd - 256 + 2 * (2 * 4 * 3) * 64 * 64 * 4
+    # the forward's blocks (its workspace less the chunk table) plus the
+    # entering state and the leaving-state gradient of every chunk-head
+    # (2 sequences x 4 chunks x 3 heads), each a set of bfloat16 tiles
+    assert n >= fwd - 256 + 2 * (2 * 4 * 3) * 64 * 64 * 2
     assert L.gdn2_chunk_bwd_workspace_bytes(2, 200, 3, 48, 48, 0, 64, BF16) == 0
     assert L.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 32, 32, 3, 16, F32) >= \
         L.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 32, 32, 0, 16, F32)
