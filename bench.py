@@ -20,7 +20,9 @@ In the same run (reported next to the headline, not in `value`):
     DeltaNet (also a per-(token, head) decay), and GDN-2's time over KDA's;
   * the same layer under the alternative reading R1 (chunked two-pass path);
   * the chunked backward (gdn2_chunk_bwd) on the same layer: its time per
-    step, per-kernel durations and the roofline of its dominant kernel;
+    step, per-kernel durations and the roofline of its dominant kernel, and
+    a training step (the forward, then the backward on the forward's
+    per-chunk blocks);
   * a context-parallel split of one 32768-token sequence into 8 segments:
     the per-rank segment map and re-run against the serial forward, and all
     eight on this GPU with the scan of the maps;
@@ -80,15 +82,15 @@ def bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
 
 
 # Algorithmic HBM bytes per token and head of the backward's kernels (bf16
-# elements; a state crosses HBM as two fragment-tile copies of d*d elements
-# per chunk, the same bytes as one float32 copy):
+# elements; a state crosses HBM as one fragment-tile copy of d*d elements
+# per chunk):
 #   path         : read q, k, v, alpha, b, w and dL/do once, write six gradients
 #   chunk_states : read -W, Kbar^T, Ut and gamma_C, write the entering state
 #   bwd_dstate   : read -W, Q', Kbar^T, gamma_C and dL/do, write the leaving-state gradient
 #   bwd_grad     : read the six inputs, dL/do, the state and its gradient, write six gradients
 def bwd_bytes_per_token_head(d: int, C: int, elem: int = 2) -> dict:
     gam = d * 4 / C
-    st = d * d * 4 / C
+    st = d * d * elem / C
     pb = p_bytes_per_token_head(C, elem)
     return {
         "path": 7 * d * elem + 6 * d * elem,
@@ -729,6 +731,24 @@ def main() -> int:
         kout = dict(gout, db=torch.empty_like(kin["b"]), dw=torch.empty_like(kin["w"]))
         sec_bk = timed_steps(lambda: g.chunk_bwd(*(kin[x] for x in NAMES), dout, chunk=C, workspace=wsb, out=kout),
                              bsteps, 2)
+        # a training step: the forward (two-pass path) into the backward's
+        # workspace, then the backward with the forward's blocks handed over
+        o_t = torch.empty_like(o)
+        Sf_t = torch.empty_like(Sf)
+
+        def fwd_into_wsb():
+            g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o_t, S_final=Sf_t, workspace=wsb, path="two_pass")
+
+        def bstep_prepared():
+            g.chunk_bwd(*(dev[x] for x in NAMES), dout, chunk=C, workspace=wsb, out=gout, prepared=True)
+
+        def train_step():
+            fwd_into_wsb()
+            bstep_prepared()
+
+        sec_train = timed_steps(train_step, bsteps, 2)
+        fwd_into_wsb()
+        sec_bp = timed_steps(bstep_prepared, bsteps, 2)
         bbyt = bwd_bytes_per_token_head(d, C)
         bdom = max(bkern, key=lambda k: bkern[k]["avg_us"])
         bach = bbyt[bdom] * tok_heads / (bkern[bdom]["avg_us"] * 1e-6) / 1e9
@@ -739,6 +759,11 @@ def main() -> int:
             "time_over_forward": round(sec_b / sec, 3),
             "kda_ms_per_step": round(sec_bk * 1e3, 4),
             "gdn2_over_kda_time": round(sec_b / sec_bk, 4),
+            "prepared_ms_per_step": round(sec_bp * 1e3, 4),
+            "train_step": {"workload": "forward (two-pass) into the backward's workspace, then the backward "
+                                       "with the forward's per-chunk blocks handed over",
+                           "ms_per_step": round(sec_train * 1e3, 4),
+                           "tokens_per_s": round(B * T / sec_train, 1)},
             "path_algorithmic_bytes": int(bbyt["path"] * tok_heads),
             "path_hbm_frac": round(bbyt["path"] * tok_heads / sec_b / 1e9 / HBM_PEAK_GBS, 4),
             "kernels": bkern,

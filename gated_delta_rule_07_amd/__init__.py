@@ -238,14 +238,17 @@ def bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int,
 
 def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
               chunk: int = 64, workspace=None, out=None, want_dS0: bool = True,
-              layer_prep: bool = False):
+              layer_prep: bool = False, prepared: bool = False):
     """Chunked backward of ``chunk_fwd``, for the same input modes (b, w,
     alpha per channel or [B, T, H]; ``layer_prep`` for the raw layer
     inputs).  Given dL/do (``dout``, like o) and dL/dS_final (or None for
     zero), returns a dict with dq, dk, dv, dalpha, db, dw (each like its
     input: the gradient with respect to the input as given) and dS0
     ([N, H, dk, dv] float32, or None when ``want_dS0`` is False).  ``out``
-    may hold preallocated tensors under those names."""
+    may hold preallocated tensors under those names.  ``prepared=True``
+    takes the per-chunk blocks a ``chunk_fwd(..., path="two_pass")`` left in
+    ``workspace`` (a backward-sized workspace, same inputs) instead of
+    recomputing them."""
     _require_device(q, k, v, alpha, b, w, dout, S0, dS_final, cu_seqlens)
     dt = _dtype_code(q)
     for t in (k, v, b, w, dout) + (() if layer_prep else (alpha,)):
@@ -258,7 +261,10 @@ def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=Non
     for t, name, full in ((k, "k", dk), (v, "v", dv), (dout, "dout", dv)):
         if tuple(t.shape) != (B, T, H, full):
             raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}]")
-    flags = _gate_flags(q, v, alpha, b, w) | (FLAG_LAYER_PREP if layer_prep else 0)
+    flags = (_gate_flags(q, v, alpha, b, w) | (FLAG_LAYER_PREP if layer_prep else 0)
+             | (FLAG_PREPARED if prepared else 0))
+    if prepared and workspace is None:
+        raise ValueError("prepared=True reads the given workspace")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")

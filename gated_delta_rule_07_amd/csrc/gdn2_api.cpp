@@ -387,7 +387,8 @@ struct seg_run {
 
 // Segment schedule of the backward.  The segments are whole chunks in
 // order, so their chunk slots are numbered as the call's own: the blocks,
-// states and state gradients land where the plain backward puts them.
+// states and state gradients land where the plain backward puts them (and
+// a forward's blocks, with `prepared`, are read where it left them).
 //   states: the segment maps from the prep's blocks, their scan from S0,
 //     and the states-mode scan of every segment from its entering state;
 //   state gradients: the reverse scan of every segment from zero gives
@@ -396,7 +397,7 @@ struct seg_run {
 //     dL/dS_final gives the gradient after every segment (and dL/dS0); the
 //     reverse scan of every segment from X(g) writes the final gradients.
 template <typename IO, int D, int C>
-hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, hipStream_t st) {
+hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, bool prepared, hipStream_t st) {
   hipError_t e = hipSuccess;
   const gdn2::chunk_args &a = ba.f;
   const int nseg = sg.N * sg.G;
@@ -422,7 +423,7 @@ hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, hip
     if ((e = gdn2::launch_chunk_table(scu, nseg, C_rt, stab, st)) != hipSuccess)
       return e;
   }
-  {
+  if (!prepared) {
     prof_scope p("chunk_prep", st);
     if ((e = gdn2::launch_chunk_prep<IO, D, C>(s, st)) != hipSuccess)
       return e;
@@ -464,7 +465,7 @@ hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, hip
 }
 
 template <typename IO, int D, int C>
-hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, hipStream_t st) {
+hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, bool prepared, hipStream_t st) {
   hipError_t e = hipSuccess;
   gdn2::chunk_args &a = ba.f;
   if (a.cu) {
@@ -474,13 +475,13 @@ hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, hipStream_t 
       return e;
   }
   if (sg) {
-    if ((e = run_bwd_segments<IO, D, C>(ba, C_rt, *sg, st)) != hipSuccess)
+    if ((e = run_bwd_segments<IO, D, C>(ba, C_rt, *sg, prepared, st)) != hipSuccess)
       return e;
     prof_scope p("bwd_grad", st);
     return gdn2::launch_bwd_grad<IO, D, C>(ba, st);
   }
   if (a.num_slots > 0) {
-    {
+    if (!prepared) {
       prof_scope p("chunk_prep", st);
       e = gdn2::launch_chunk_prep<IO, D, C>(a, st);
       if (e != hipSuccess)
@@ -506,10 +507,11 @@ hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, hipStream_t 
   return e;
 }
 
-hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, const seg_run *sg, hipStream_t st) {
+hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, const seg_run *sg, bool prepared,
+                        hipStream_t st) {
 #define GDN2_RB(IO, D, C) \
   if (d == D && c == C)   \
-    return run_bwd<IO, D, C>(ba, C, sg, st);
+    return run_bwd<IO, D, C>(ba, C, sg, prepared, st);
   if (dt == GDN2_F32) {
     GDN2_RB(float, 16, 16) GDN2_RB(float, 32, 16) GDN2_RB(float, 64, 16) GDN2_RB(float, 128, 16)
     GDN2_RB(float, 16, 64) GDN2_RB(float, 32, 64) GDN2_RB(float, 64, 64) GDN2_RB(float, 128, 64)
@@ -1032,9 +1034,15 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: unknown dtype %d", static_cast<int>(dt));
   const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
-  if (flags & ~gate_flags)
+  if (flags & ~(gate_flags | GDN2_FLAG_PREPARED))
     return fail(GDN2_ERR_UNSUPPORTED,
-                "gdn2_chunk_bwd: flags 0x%x: only the gate layout and layer prep flags apply to the backward", flags);
+                "gdn2_chunk_bwd: flags 0x%x: only the gate layout, layer prep and prepared-workspace flags apply "
+                "to the backward",
+                flags);
+  if ((flags & GDN2_FLAG_PREPARED) && dk != dv)
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_bwd: GDN2_FLAG_PREPARED needs dk == dv (the widened call lays its workspace out "
+                "differently from the forward's)");
   if (B <= 0 || T < 0 || H <= 0)
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_bwd: bad sizes B=%d T=%d H=%d", B, T, H);
   if (!supported_dim(dk) || !supported_dim(dv))
@@ -1195,7 +1203,8 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
       sgp = &sr;
     }
   }
-  const hipError_t e = dispatch_bwd(dt, dk, chunk, ba, sgp, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      dispatch_bwd(dt, dk, chunk, ba, sgp, (flags & GDN2_FLAG_PREPARED) != 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
   return ok();

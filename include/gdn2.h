@@ -146,8 +146,14 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1, GDN2_DTYPE_MAX_ENUM = 0x7FFFFFFF } g
  * workspace already holds every chunk's intermediates (they do not depend
  * on S0), so gdn2_chunk_fwd skips the per-chunk kernel and runs the state
  * scan alone; q .. w are checked but not read.  A workspace filled by
- * gdn2_chunk_fwd on the two-pass path serves the same way.  Any other
- * contents give undefined outputs. */
+ * gdn2_chunk_fwd on the two-pass path serves the same way.
+ * gdn2_chunk_bwd takes it too (dk == dv only): a training step that has
+ * run gdn2_chunk_fwd with GDN2_FLAG_TWO_PASS on the same inputs, sizes and
+ * gate flags, into the front of the backward's own workspace (at least
+ * gdn2_chunk_bwd_workspace_bytes), hands those intermediates to the
+ * backward, which then skips its own per-chunk kernel (it still reads
+ * q .. w for the gradients).  The results are those of the backward without
+ * the flag, bit for bit.  Any other contents give undefined outputs. */
 #define GDN2_FLAG_PREPARED (1u << 8)
 
 /* Size limits of every chunked entry point (gdn2_chunk_fwd, its
@@ -266,8 +272,10 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *   q .. cu_seqlens, B .. dt : the forward's inputs and sizes.
  *   flags     : GDN2_FLAG_SCALAR_B / _W / _ALPHA and GDN2_FLAG_LAYER_PREP,
  *               with the forward's meaning (inputs given per (token, head),
- *               or the raw layer inputs); the path and rule flags return
- *               GDN2_ERR_UNSUPPORTED.
+ *               or the raw layer inputs), and GDN2_FLAG_PREPARED (the
+ *               workspace's front holds the forward's per-chunk blocks, see
+ *               that flag; GDN2_ERR_UNSUPPORTED when dk != dv); the path and
+ *               rule flags return GDN2_ERR_UNSUPPORTED.
  *   dout      : dL/do [B, T, H, dv], element type dt.
  *   dS_final  : dL/dS_final [N, H, dk, dv] float32, or NULL for zero.
  *   dq, dk_out, dv_out, dalpha, db, dw : outputs, the gradients with respect
@@ -282,11 +290,13 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *               gradients.
  *   dS0       : dL/dS0 [N, H, dk, dv] float32, or NULL.
  *   workspace : device scratch of at least gdn2_chunk_bwd_workspace_bytes(...)
- *               bytes; its contents on entry are irrelevant (with dk != dv
- *               its front holds the widened inputs, dout, their gradients
- *               and three d x d states per sequence-head).
- * The kernels recompute the forward's per-chunk quantities and the state
- * entering every chunk; no forward output needs to be kept.  For the shapes
+ *               bytes; its contents on entry are irrelevant without
+ *               GDN2_FLAG_PREPARED (with dk != dv its front holds the
+ *               widened inputs, dout, their gradients and three d x d states
+ *               per sequence-head).
+ * The kernels recompute the forward's per-chunk quantities (unless
+ * GDN2_FLAG_PREPARED hands them over) and the state entering every chunk; no
+ * forward output needs to be kept.  For the shapes
  * where gdn2_chunk_fwd takes its segment schedule (a few long sequences),
  * given the workspace gdn2_chunk_bwd_workspace_bytes reports, both of the
  * backward's scans take it too: the states from the segment maps and their

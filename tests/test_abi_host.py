@@ -180,8 +180,11 @@ def test_bwd_rejects_before_launch(L):
     assert call_bwd(L, B=0) == 1
     assert call_bwd(L, T=-1) == 1
     # the backward takes no forward path or rule flag
-    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 8):
+    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 9):
         assert call_bwd(L, flags=flag) == 2
+    # the forward's blocks handed over: square heads only, still size-checked
+    assert call_bwd(L, flags=1 << 8, dk=16, dv=32) == 2
+    assert call_bwd(L, flags=1 << 8, ws_bytes=16) == 3
     assert call_bwd(L, dout=0x10008) == 1      # misaligned
     assert call_bwd(L, ws_bytes=16) == 3
     assert call_bwd(L, B=2, N=1) == 1          # num_seqs without cu_seqlens

@@ -289,3 +289,55 @@ def test_bwd_rect_heads_layer_prep(g, dtype, dk, dv, scalar):
     ref = lp.layer_prep_bwd(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"], gp)
     ref["dS0"] = gp["dS0"]
     check(got, ref, TOL[dtype], f"rect layer prep {dtype} {dk}x{dv} scalar={scalar}")
+
+
+PREPARED_CASES = [  # dtype, d, chunk, B, T, H, packed lengths (or None), gate layout
+    ("bf16", 128, 64, 2, 300, 3, None, "channel"),       # plain two-pass, ragged last chunk
+    ("f32", 64, 16, 1, 0, 2, [70, 0, 1, 130, 15], "channel"),   # packed, empty and 1-token sequences
+    ("bf16", 64, 64, 1, 8192, 4, None, "channel"),      # one long sequence: the segment schedule
+    ("bf16", 64, 64, 1, 0, 4, [9000, 8000], "channel"),       # packed long sequences: the segment schedule
+    ("bf16", 32, 64, 2, 200, 2, None, "kda"),            # b = w = beta per (token, head)
+]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,B,T,H,lens,gates", PREPARED_CASES)
+def test_bwd_prepared_from_forward(g, dtype, d, chunk, B, T, H, lens, gates):
+    """A training step's forward (two-pass path) into the backward's own
+    workspace, then the backward with the forward's blocks handed over: the
+    gradients and dS0 equal, bit for bit, those of the backward that
+    recomputes the blocks, and the forward's output is the plain forward's."""
+    seed = 700 + d + H
+    cu = None
+    if lens is not None:
+        cu = gi.cu_seqlens_from(lens)
+        T = int(cu[-1])
+    N = len(lens) if lens is not None else B
+    inp = gi.make_chunk_inputs(B, T, H, d, d, dtype, seed, s0="normal",
+                               **({"num_seqs": N} if lens is not None else {}))
+    grads = gi.make_bwd_grads(B, T, H, d, d, dtype, seed, with_dS=True,
+                              **({"num_seqs": N} if lens is not None else {}))
+    print(f"prepared case {dtype} d={d} C={chunk} B={B} T={T} H={H} packed={lens is not None} gates={gates}",
+          flush=True)
+    dev = {n: inp[n].cuda() for n in NAMES}
+    if gates == "kda":
+        beta = dev["b"][..., 0].contiguous()
+        dev["b"] = beta
+        dev["w"] = beta.clone()
+    S0 = inp["S0"].cuda()
+    dSf = grads["dS_final"].cuda()
+    dout = grads["dout"].cuda()
+    cud = None if cu is None else cu.cuda()
+    ns = N if cu is not None else 0
+    ws = torch.empty(g.bwd_workspace_bytes(B, T, H, d, d, ns, chunk, dev["q"].dtype), dtype=torch.uint8,
+                     device="cuda")
+    args = [dev[n] for n in NAMES]
+    ref = g.chunk_bwd(*args, dout, S0=S0, dS_final=dSf, cu_seqlens=cud, chunk=chunk)
+    ref = {k: v.clone() for k, v in ref.items() if v is not None}
+    o_plain, Sf_plain = g.chunk_fwd(*args, S0=S0, cu_seqlens=cud, chunk=chunk, path="two_pass")
+    ws.fill_(0xA5)  # the hand-over must not depend on what was there before the forward
+    o, Sf = g.chunk_fwd(*args, S0=S0, cu_seqlens=cud, chunk=chunk, path="two_pass", workspace=ws)
+    got = g.chunk_bwd(*args, dout, S0=S0, dS_final=dSf, cu_seqlens=cud, chunk=chunk, workspace=ws, prepared=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain) and torch.equal(Sf, Sf_plain)
+    for name, x in ref.items():
+        assert torch.equal(got[name], x), f"{name} differs from the recomputing backward"
