@@ -14,7 +14,8 @@ In the same run (reported next to the headline, not in `value`):
   * the T sweep at B*T = 32768 (T = 2K .. 32K) and the packed-sequence
     workload (lengths uniform in [256, 8192], 32768 tokens);
   * the decode step (256 sequences x 16 heads, 256 MiB fp32 state updated in
-    place), warm and with two alternating state buffers (512 MiB, more than
+    place): eager launches and HIP graph replays of the same loop, and its
+    kernel warm and with two alternating state buffers (512 MiB, more than
     the 256 MB last-level cache);
   * the same layer as KDA (b = w = beta per token and head) and as Gated
     DeltaNet (also a per-(token, head) decay), and GDN-2's time over KDA's;
@@ -672,10 +673,31 @@ def main() -> int:
             g.decode_step(*(ddev[x][i % c4["steps"]] for x in NAMES), states[i % len(states)],
                           out=od)
 
-        g.profile_enable(True)
+        # eager launches, no timing hooks
         sec_d = timed_steps(lambda: dstep([S_a]), args.decode_steps, 10)
+        # the same loop as HIP graph replays: one graph of c4["steps"]
+        # consecutive steps (each distinct input once, the state in place)
+        gsteps = c4["steps"]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for t in range(gsteps):
+                g.decode_step(*(ddev[x][t] for x in NAMES), S_a, out=od)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            for t in range(gsteps):
+                g.decode_step(*(ddev[x][t] for x in NAMES), S_a, out=od)
+        replays = max(1, args.decode_steps // gsteps)
+        sec_dg = timed_steps(dgraph.replay, replays, 2) / gsteps
+        del dgraph
+        # kernel durations: HIP events around every launch, in passes of their own
+        hooked = max(100, args.decode_steps // 5)
+        g.profile_enable(True)
+        timed_steps(lambda: dstep([S_a]), hooked, 10)
         dprof = g.profile_read(reset=True)
-        sec_dc = timed_steps(lambda: dstep([S_a, S_b]), args.decode_steps, 10)
+        timed_steps(lambda: dstep([S_a, S_b]), hooked, 10)
         dprof_c = g.profile_read(reset=True)
         g.profile_enable(False)
         dk_us = 1e3 * dprof["decode"][0] / dprof["decode"][1]
@@ -683,6 +705,8 @@ def main() -> int:
         out["decode"] = {
             "workload": "256 sequences x 16 heads, d=128, bf16 inputs, fp32 state in place",
             "steps": args.decode_steps, "us_per_step": round(sec_d * 1e6, 2),
+            "graph_us_per_step": round(sec_dg * 1e6, 2),
+            "graph": f"{replays} replays of one HIP graph of {gsteps} consecutive steps",
             "kernel_us": round(dk_us, 2),
             "algorithmic_bytes_per_step": step_bytes,
             "GBps": round(step_bytes / (dk_us * 1e-6) / 1e9, 1),
