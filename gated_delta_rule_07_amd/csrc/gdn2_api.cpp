@@ -171,13 +171,15 @@ template <typename IO, int D, int C> int choose_fused(long units, uint32_t flags
   return 0;
 }
 
+// table_ready: packed input whose chunk table is already in a.offsets (the
+// segment schedule's last step, after its maps)
 template <typename IO, int D, int C>
-hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, uint32_t flags, hipStream_t st) {
+hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, uint32_t flags, hipStream_t st, bool table_ready) {
   hipError_t e = hipSuccess;
   const int ng = choose_fused<IO, D, C>(static_cast<long>(a.num_seqs) * a.H, flags);
   if (ng < 0)
     return hipErrorInvalidConfiguration;
-  if (a.cu) {
+  if (a.cu && !table_ready) {
     prof_scope p("chunk_table", st);
     e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
     if (e != hipSuccess)
@@ -201,10 +203,10 @@ hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, uint32_t flags, hipStr
 }
 
 hipError_t dispatch_chunk(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, uint32_t flags,
-                          hipStream_t st) {
+                          hipStream_t st, bool table_ready = false) {
 #define GDN2_RC(IO, D, C) \
   if (d == D && c == C)   \
-    return run_chunk<IO, D, C>(a, C, flags, st);
+    return run_chunk<IO, D, C>(a, C, flags, st, table_ready);
   if (dt == GDN2_F32) {
     GDN2_RC(float, 16, 16) GDN2_RC(float, 32, 16) GDN2_RC(float, 64, 16) GDN2_RC(float, 128, 16)
     GDN2_RC(float, 16, 64) GDN2_RC(float, 32, 64) GDN2_RC(float, 64, 64) GDN2_RC(float, 128, 64)
@@ -590,18 +592,17 @@ hipError_t dispatch_segmap(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args
 // sequences (fixed-length or packed).  With few (sequence, head) units the
 // state scan, whose chunks run in order, occupies a fraction of the compute
 // units.  Every sequence is then cut into G segments of whole chunks: their
-// affine state maps (segment map kernel, on the prep's blocks), the
-// exclusive scan of each sequence's maps from its S0 (which also gives
-// S_final), and the state scan of every segment from its entering state on
-// the same blocks.  G = min(16, 128 / (N H), chunks / 16), with N sequences
-// of (on average) `chunks` chunks, puts about 128 (segment, head) units on
-// the GPU with segments of 16 chunks or more.  Measured on MI355X (bf16,
-// d = 128, one sequence): 16 heads x 32768
-// tokens 0.71 ms against 0.89 ms for the serial scan, 16 x 16384 0.38
-// against 0.47, 8 x 16384 0.23 against 0.34, 4 x 8192 0.10 against 0.16,
-// 4 x 65536 0.43 against 1.25; with 32 (sequence, head) units (32 heads,
-// or two sequences of 16 heads) the serial scan is as fast or faster, hence
-// the bounds below.
+// affine state maps (segment map kernel, on the prep's blocks; each
+// sequence's last segment needs none), the exclusive scan of each sequence's
+// maps from its S0, and the state scan of every segment from its entering
+// state on the same blocks (the last segment's scan gives S_final).
+// G = min(16, 128 / (N H), chunks / 16), with N sequences of (on average)
+// `chunks` chunks, puts about 128 (segment, head) units on the GPU with
+// segments of 16 chunks or more, for N H <= 32.  Measured on MI355X (bf16,
+// d = 128, one sequence): 16 heads x 32768 tokens 0.71 ms against 0.89 ms
+// for the serial scan, 16 x 16384 0.38 against 0.47, 8 x 16384 0.23 against
+// 0.34, 4 x 8192 0.10 against 0.16, 4 x 65536 0.43 against 1.25; two
+// sequences of 16384 x 16 heads (G = 4) 0.59 against 0.63.
 int seg_count(int nc, int units) {
   int g = 16;
   while (g > 1 && (g * units > 128 || 16 * g > nc))
@@ -625,7 +626,7 @@ seg_shape seg_shape_of(int B, int T, int num_seqs, int chunk, bool packed) {
 }
 
 bool use_segments(const seg_shape &x, int H) {
-  return x.N > 0 && x.T_total > 0 && static_cast<long>(x.N) * H <= 16 && x.nc >= 128 && seg_count(x.nc, x.N * H) >= 2;
+  return x.N > 0 && x.T_total > 0 && static_cast<long>(x.N) * H <= 32 && x.nc >= 128 && seg_count(x.nc, x.N * H) >= 2;
 }
 
 struct seg_plan {
@@ -695,15 +696,20 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   s.S0 = nullptr;
   s.o = nullptr;
   s.S_final = nullptr;
+  // the maps of every segment but each sequence's last, their scan from S0
+  // (no S_final: the last segment's own state scan gives it), then every
+  // segment's state scan from its entering state
+  s.seg_G = pl.G;
   e = dispatch_segmap(dt, d, chunk, s, Phi, Psi, st);
   if (e != hipSuccess)
     return e;
-  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, x.N, S_in, a.S_final, st);
+  e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, x.N, S_in, nullptr, st);
   if (e != hipSuccess)
     return e;
   s.S0 = S_in;
   s.o = a.o;
-  return dispatch_chunk(dt, d, chunk, s, GDN2_FLAG_TWO_PASS | GDN2_FLAG_PREPARED, st);
+  s.S_final = a.S_final;
+  return dispatch_chunk(dt, d, chunk, s, GDN2_FLAG_TWO_PASS | GDN2_FLAG_PREPARED, st, true);
 }
 
 // ------------------------------------------------------- no-alloc scratch --

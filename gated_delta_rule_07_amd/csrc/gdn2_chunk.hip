@@ -650,14 +650,17 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1, ST>::NCW + sc
       }
     }
   }
-  if (a.S_final) {
+  // S_final of the sequence (segment schedule: of the original sequence,
+  // from its last segment only)
+  if (a.S_final && (a.seg_G == 0 || n % a.seg_G == a.seg_G - 1)) {
+    const size_t fu = a.seg_G > 0 ? static_cast<size_t>(n / a.seg_G) * a.H + h : static_cast<size_t>(unit);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int j = 0; j < CPW; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          a.S_final[(static_cast<size_t>(unit) * D + 16 * kk + 4 * g + i) * D + 16 * (vt0 + j) + m] = S[kk][j][i];
+          a.S_final[(fu * D + 16 * kk + 4 * g + i) * D + 16 * (vt0 + j) + m] = S[kk][j][i];
   }
 }
 

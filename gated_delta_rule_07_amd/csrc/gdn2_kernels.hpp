@@ -26,6 +26,12 @@ struct chunk_args {
   size_t blk_bytes;
   uint32_t gates;    // GATE_* bits: inputs given per (token, head) instead of per channel
   void *states;      // backward only: state entering every chunk (state_tiles blocks, slot * H + h)
+  // Forward segment schedule: G > 0 when the call's sequences are segments,
+  // seg_G consecutive ones per original sequence.  The segment map then
+  // skips each sequence's last segment (no later segment needs its map),
+  // and the state scan writes S_final only for that last segment, at the
+  // original sequence's index.  0 otherwise.
+  int seg_G;
 };
 
 // chunk_args::gates: b, w or alpha is one value per (token, head), laid out

@@ -91,6 +91,8 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C, CW>::NW + segmap_c
   if (unit >= a.num_seqs * a.H)
     return;  // whole workgroup
   const int n = unit / a.H, h = unit - n * a.H;
+  if (a.seg_G > 0 && n % a.seg_G == a.seg_G - 1)
+    return;  // whole workgroup: the last segment's map is not needed
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   int c_begin, nchunks;
@@ -334,15 +336,24 @@ __global__ void __launch_bounds__((64 * (segmap_cfg<IO, D, C, CW>::NW + segmap_c
 // the next one is Phi_g^T S_in[g] + Psi_g, with Psi_g the gradient of the
 // state before g from g's own outputs; S_final receives the gradient of the
 // state before the first segment.
-template <int D, bool REV = false>
+// GC > 0: the segment count is GC (G is ignored) and the step loop is
+// unrolled whole, so that the maps loaded two steps ahead land in fresh
+// registers; with a run-time count the loop carries them in fixed registers
+// and each step waits for the loads it has just issued.
+template <int D, bool REV = false, int GC = 0>
 __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const float *__restrict__ Phi,
                                                                          const float *__restrict__ Psi,
-                                                                         const float *__restrict__ S0, int G, int H,
+                                                                         const float *__restrict__ S0, int G_rt, int H,
                                                                          int B, float *__restrict__ S_in,
                                                                          float *__restrict__ S_final) {
   constexpr int NK = D / 16;
+  const int G = GC > 0 ? GC : G_rt;
   __shared__ f32x4 col[NK][64];  // ColFrag of the state tiles (k2, j)
-  const int bh = static_cast<int>(blockIdx.x) / NK, j = static_cast<int>(blockIdx.x) % NK;
+  // consecutive workgroup ids go to the 8 XCDs in turn; the NK column tiles
+  // of one (sequence, head) all take ids of one XCD, whose L2 then serves
+  // their common reads of every Phi (grid: (B H rounded up to 8) x NK)
+  const int x = static_cast<int>(blockIdx.x), r = x >> 3;
+  const int bh = (r / NK) * 8 + (x & 7), j = r % NK;
   if (bh >= B * H)
     return;
   const int b = bh / H, h = bh - b * H;
@@ -359,8 +370,11 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     s[i] = S0 ? S0[static_cast<size_t>(bh) * D * D + at(i)] : 0.f;
-  f32x4 ph[NK], ps;  // RowFrag of Phi (REV: Phi^T) tiles (kk, k2); ColFrag of Psi tile (kk, j)
-  auto load = [&](int seg) {
+  // two sets of RowFrag(Phi) (REV: Phi^T) tiles (kk, k2) and ColFrag(Psi
+  // tile (kk, j)): each step's maps are loaded two steps ahead, so their
+  // latency hides under the two products in between
+  f32x4 phA[NK], psA, phB[NK], psB;
+  auto load = [&](int seg, f32x4(&ph)[NK], f32x4 &ps) {
     const size_t base = (static_cast<size_t>(seg) * H + h) * D * D;
 #pragma unroll
     for (int k2 = 0; k2 < NK; ++k2) {
@@ -377,14 +391,25 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
     for (int i = 0; i < 4; ++i)
       ps[i] = Psi[base + at(i)];
   };
-  if (G > 0)
-    load(REV ? G - 1 : 0);
-  for (int step = 0; step < G; ++step) {
-    const int seg = REV ? G - 1 - step : step;
+  auto seg_of = [&](int step) { return REV ? G - 1 - step : step; };
+  // products needed: one per segment, but the forward without S_final needs
+  // none for its last segment (whose map need not exist)
+  const int nprod = (!REV && !S_final) ? G - 1 : G;
+  if (nprod > 0)
+    load(seg_of(0), phA, psA);
+  if (nprod > 1)
+    load(seg_of(1), phB, psB);
+  // one step: S_in of the step's segment, then (if needed) the next state;
+  // the set it used is refilled with the maps two steps ahead (past the
+  // last product: its own maps again, no branch).  False: no more products.
+  auto step_fn = [&](int step, f32x4(&ph)[NK], f32x4 &ps) -> bool {
+    const int seg = seg_of(step);
     const size_t base = (static_cast<size_t>(seg) * H + h) * D * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       S_in[base + at(i)] = s[i];
+    if (step >= nprod)
+      return false;  // uniform over the workgroup
     col[kk][lane] = s;
     lds_barrier();
     f32x4 cph[NK];
@@ -392,15 +417,29 @@ __global__ void __launch_bounds__(64 * (D / 16)) gdn2_seg_combine_kernel(const f
     for (int k2 = 0; k2 < NK; ++k2)
       cph[k2] = ph[k2];
     f32x4 nw = ps;
-    if constexpr (REV)
-      load(seg > 0 ? seg - 1 : seg);  // the last step re-reads its own maps: no branch
-    else
-      load(seg + 1 < G ? seg + 1 : seg);
+    load(seg_of(step + 2 < nprod ? step + 2 : step), ph, ps);
 #pragma unroll
     for (int k2 = 0; k2 < NK; ++k2)
       mm<float>(nw, cph[k2], col[k2][lane]);
     lds_barrier();  // every wave has read the column before it is overwritten
     s = nw;
+    return true;
+  };
+  if constexpr (GC > 0) {
+#pragma unroll
+    for (int step = 0; step < GC; step += 2) {
+      if (!step_fn(step, phA, psA))
+        break;
+      if (step + 1 >= GC || !step_fn(step + 1, phB, psB))
+        break;
+    }
+  } else {
+    for (int step = 0; step < G; step += 2) {
+      if (!step_fn(step, phA, psA))
+        break;
+      if (step + 1 >= G || !step_fn(step + 1, phB, psB))
+        break;
+    }
   }
   if (S_final) {
 #pragma unroll
@@ -434,12 +473,26 @@ hipError_t launch_segmap(const chunk_args &a, float *Phi, float *Psi, hipStream_
 template <int D>
 hipError_t launch_seg_combine(const float *Phi, const float *Psi, const float *S0, int G, int H, int B,
                               float *S_in, float *S_final, hipStream_t st, bool reverse) {
+  const dim3 grid((B * H + 7) / 8 * 8 * (D / 16)), block(64 * (D / 16));
   if (reverse)
-    hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, true>), dim3(B * H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi,
-                       Psi, S0, G, H, B, S_in, S_final);
-  else
-    hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false>), dim3(B * H * (D / 16)), dim3(64 * (D / 16)), 0, st, Phi,
-                       Psi, S0, G, H, B, S_in, S_final);
+    hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, true>), grid, block, 0, st, Phi, Psi, S0, G, H, B, S_in, S_final);
+  else if (G == 2 || G == 4 || G == 8 || G == 16) {
+    // the segment schedule's counts, unrolled
+    if (G == 2)
+      hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false, 2>), grid, block, 0, st, Phi, Psi, S0, G, H, B, S_in,
+                         S_final);
+    else if (G == 4)
+      hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false, 4>), grid, block, 0, st, Phi, Psi, S0, G, H, B, S_in,
+                         S_final);
+    else if (G == 8)
+      hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false, 8>), grid, block, 0, st, Phi, Psi, S0, G, H, B, S_in,
+                         S_final);
+    else
+      hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false, 16>), grid, block, 0, st, Phi, Psi, S0, G, H, B, S_in,
+                         S_final);
+  } else {
+    hipLaunchKernelGGL((gdn2_seg_combine_kernel<D, false>), grid, block, 0, st, Phi, Psi, S0, G, H, B, S_in, S_final);
+  }
   return hipGetLastError();
 }
 

@@ -196,14 +196,15 @@ size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv,
  *               path flag the library runs the two-pass chunked kernels (all
  *               chunks in parallel, then the state scan).  For N
  *               sequences (B, or num_seqs packed) of at least 128 chunks (on
- *               average, packed) with N H <= 16, given the workspace
+ *               average, packed) with N H <= 32, given the workspace
  *               gdn2_chunk_fwd_workspace_bytes reports for them, the default
  *               path cuts every sequence into G = min(16, 128 / (N H),
- *               chunks / 16) segments of whole chunks (8 or 16; bounds
+ *               chunks / 16) segments of whole chunks (4, 8 or 16; bounds
  *               computed on the device from cu_seqlens when packed): the
- *               segments' state maps (as gdn2_chunk_segment_map), their scan
- *               from S0 (as gdn2_segment_combine, which also gives S_final),
- *               and every segment's state scan from its entering state, so
+ *               segments' state maps (as gdn2_chunk_segment_map; none for a
+ *               sequence's last segment), their scan from S0 (as
+ *               gdn2_segment_combine), and every segment's state scan from
+ *               its entering state (the last one's gives S_final), so
  *               that more compute units share the sequential scan; with a
  *               smaller workspace it runs the plain two-pass kernels.
  *               GDN2_FLAG_FUSED

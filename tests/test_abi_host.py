@@ -101,7 +101,7 @@ def test_workspace_bytes(L):
 
 
 def test_workspace_bytes_long_sequence(L):
-    # B sequences of 128 chunks or more with at most 16 (sequence, head)
+    # B sequences of 128 chunks or more with at most 32 (sequence, head)
     # units also reserve the segment schedule: G = min(16, 128 / (B H),
     # chunks / 16) segments per sequence (packed: the mean length), their
     # bounds, chunk table, blocks of the packed layout, and Phi, Psi, S_in.
@@ -133,11 +133,14 @@ def test_workspace_bytes_long_sequence(L):
     assert ws(2, 256 * C, 8) == max(plain(2, 256 * C, 8), seg(2, 256 * C, 8, 8))  # 16 (sequence, head) units
     assert ws(4, 200 * C, 2) == max(plain(4, 200 * C, 2), seg(4, 200 * C, 2, 8))
     assert ws(1, 127 * C, 16) == plain(1, 127 * C, 16)       # 127 chunks
-    assert ws(2, 32768, 16) == plain(2, 32768, 16)           # 32 units
-    assert ws(1, 32768, 17) == plain(1, 32768, 17)           # 17 heads
+    assert ws(2, 32768, 16) == max(plain(2, 32768, 16), seg(2, 32768, 16, 4))   # 32 units
+    assert ws(1, 32768, 17) == max(plain(1, 32768, 17), seg(1, 32768, 17, 4))   # 17 heads
+    assert ws(1, 32768, 33) == plain(1, 32768, 33)           # 33 units
+    assert ws(3, 32768, 11) == plain(3, 32768, 11)           # 33 units
     assert ws(1, 32768, 16, 1) == max(plain(1, 32768, 16), seg(1, 32768, 16, 8))   # one packed sequence
     assert ws(1, 32768, 8, 2) == max(plain(1, 32768, 8, 2), seg(2, 16384, 8, 8))   # two, 256 chunks on average
-    assert ws(1, 32768, 16, 2) == plain(1, 32768, 16, 2)     # 32 units
+    assert ws(1, 32768, 16, 2) == max(plain(1, 32768, 16, 2), seg(2, 16384, 16, 4))   # 32 units
+    assert ws(1, 32768, 11, 3) == plain(1, 32768, 11, 3)     # 33 units
     assert ws(1, 32768, 4, 3) == max(plain(1, 32768, 4, 3), seg(3, 0, 4, 8, total=32768))
 
 

@@ -100,9 +100,10 @@ def test_bwd_zero_length(g):
     ("f32", 32, 16, 1, 3000, 2, None),
     ("bf16", 64, 64, 2, 140 * 64 - 7, 4, None),
     ("f32", 32, 64, 1, None, 4, [30000, 0, 37, 5000]),
+    ("bf16", 32, 64, 2, 130 * 64 + 3, 16, None),
 ])
 def test_bwd_segment_schedule(g, dtype, d, chunk, B, T, H, lens):
-    """Sequences of 128 chunks or more with at most 16 (sequence, head)
+    """Sequences of 128 chunks or more with at most 32 (sequence, head)
     units: both scans of the backward take the segment schedule (the
     forward maps and their scan for the states; per-segment reverse scans
     from zero, the adjoint scan of the maps and the final reverse scans for

@@ -327,13 +327,15 @@ def test_sweep_all_units(g, T):
 
 @pytest.mark.parametrize("dtype,d,B,H,T", [("f32", 64, 1, 2, 512 * 64 + 100), ("bf16", 128, 1, 4, 512 * 64 + 37),
                                            ("bf16", 64, 1, 16, 130 * 64 + 5), ("bf16", 64, 2, 4, 130 * 64 + 5),
-                                           ("f32", 32, 4, 2, 160 * 64 - 3)])
+                                           ("f32", 32, 4, 2, 160 * 64 - 3), ("bf16", 64, 2, 16, 130 * 64 + 5),
+                                           ("f32", 32, 1, 32, 128 * 64 + 9)])
 def test_long_sequence_segment_schedule(g, dtype, d, B, H, T):
-    """Sequences of 128 chunks or more with at most 16 (sequence, head)
-    units on the default path: the library cuts every sequence into 8 or
-    16 segments (maps, the scan of each sequence's maps, every segment's
-    scan from its entering state).  Checked against the oracle with initial
-    states, ragged last segments, and S_final written over S0."""
+    """Sequences of 128 chunks or more with at most 32 (sequence, head)
+    units on the default path: the library cuts every sequence into 4, 8 or
+    16 segments (maps of all but the last, the scan of each sequence's maps,
+    every segment's scan from its entering state, S_final from the last).
+    Checked against the oracle with initial states, ragged last segments,
+    and S_final written over S0."""
     inp = gi.make_chunk_inputs(B, T, H, d, d, dtype, seed=41 + d + B, s0="normal", alpha_mean=8.0)
     print(f"case segment schedule {dtype} d={d} B={B} H={H} T={T}", flush=True)
     dd = to_dev(inp)
@@ -345,9 +347,10 @@ def test_long_sequence_segment_schedule(g, dtype, d, B, H, T):
 
 
 @pytest.mark.parametrize("dtype,d,H,lens", [("bf16", 64, 8, [512 * 64 + 21]),
-                                            ("f32", 64, 4, [30000, 0, 37, 5000])])
+                                            ("f32", 64, 4, [30000, 0, 37, 5000]),
+                                            ("bf16", 32, 8, [20000, 1, 0, 14000])])
 def test_long_packed_segment_schedule(g, dtype, d, H, lens):
-    """Packed input of at most 16 (sequence, head) units averaging 128
+    """Packed input of at most 32 (sequence, head) units averaging 128
     chunks or more: the segment bounds come from cu_seqlens on the device
     (G segments per sequence; short sequences leave empty segments, an empty
     sequence only empty ones).  Checked against the oracle."""
