@@ -113,8 +113,10 @@ __device__ __forceinline__ void rec_token_update(rec_smem<DK, DV> &sm,
   __syncthreads();
 }
 
-// grid: N*H workgroups; block: rec_shape::NT threads
-template <typename IO, int DK, int DV>
+// grid: N*H workgroups; block: rec_shape::NT threads.  STREAM: the state is
+// read and written with nontemporal hints (no allocation in the caches on
+// the way), for states too large to stay cache-resident between steps.
+template <typename IO, int DK, int DV, bool STREAM>
 __global__ void __launch_bounds__((rec_shape<DK, DV>::NT))
     gdn2_decode_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
                        const IO *__restrict__ v, const IO *__restrict__ al,
@@ -130,16 +132,23 @@ __global__ void __launch_bounds__((rec_shape<DK, DV>::NT))
   float *Su = S + static_cast<size_t>(u) * DK * DV;
   f32x4 s[R::PASSES];
 #pragma unroll
-  for (int p = 0; p < R::PASSES; ++p)
-    s[p] = *reinterpret_cast<const f32x4 *>(Su + (tr + R::RPP * p) * DV + 4 * tc);
+  for (int p = 0; p < R::PASSES; ++p) {
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(Su + (tr + R::RPP * p) * DV + 4 * tc);
+    s[p] = STREAM ? __builtin_nontemporal_load(src) : *src;
+  }
   rec_stage_token<IO, DK, DV>(sm, q + static_cast<size_t>(u) * DK, k + static_cast<size_t>(u) * DK,
                               v + static_cast<size_t>(u) * DV, al + static_cast<size_t>(u) * DK,
                               b + static_cast<size_t>(u) * DK, w + static_cast<size_t>(u) * DV, tid);
   __syncthreads();
   rec_token_update<IO, DK, DV>(sm, s, o + static_cast<size_t>(u) * DV, tid);
 #pragma unroll
-  for (int p = 0; p < R::PASSES; ++p)
-    *reinterpret_cast<f32x4 *>(Su + (tr + R::RPP * p) * DV + 4 * tc) = s[p];
+  for (int p = 0; p < R::PASSES; ++p) {
+    f32x4 *dst = reinterpret_cast<f32x4 *>(Su + (tr + R::RPP * p) * DV + 4 * tc);
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(s[p], dst);
+    else
+      *dst = s[p];
+  }
 }
 
 // grid: N*H workgroups (unit = n*H + h); block: rec_shape::NT threads.
@@ -200,11 +209,24 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const void
                          hipStream_t st) {
   typedef rec_shape<DK, DV> R;
   const int units = N * H;
-  hipLaunchKernelGGL((gdn2_decode_kernel<IO, DK, DV>), dim3(units), dim3(R::NT), 0, st,
-                     static_cast<const IO *>(q), static_cast<const IO *>(k),
-                     static_cast<const IO *>(v), static_cast<const IO *>(al),
-                     static_cast<const IO *>(b), static_cast<const IO *>(w), S,
-                     static_cast<IO *>(o), units);
+  // A state of 64 MiB or more is streamed: in a model's decode loop the
+  // layers' states take turns, so one this large is never cache-resident
+  // when its layer comes round again, and the hints let the reads and
+  // writes run at streaming rate (256 x 16 heads, d = 128, 256 MiB: 94.9 us
+  // per step against 107.3 us when another state of that size ran in
+  // between, but 80.4 us cached when the same state is stepped back to
+  // back).
+  const bool stream = static_cast<size_t>(units) * DK * DV * sizeof(float) >= (static_cast<size_t>(64) << 20);
+  if (stream)
+    hipLaunchKernelGGL((gdn2_decode_kernel<IO, DK, DV, true>), dim3(units), dim3(R::NT), 0, st,
+                       static_cast<const IO *>(q), static_cast<const IO *>(k), static_cast<const IO *>(v),
+                       static_cast<const IO *>(al), static_cast<const IO *>(b), static_cast<const IO *>(w), S,
+                       static_cast<IO *>(o), units);
+  else
+    hipLaunchKernelGGL((gdn2_decode_kernel<IO, DK, DV, false>), dim3(units), dim3(R::NT), 0, st,
+                       static_cast<const IO *>(q), static_cast<const IO *>(k), static_cast<const IO *>(v),
+                       static_cast<const IO *>(al), static_cast<const IO *>(b), static_cast<const IO *>(w), S,
+                       static_cast<IO *>(o), units);
   return hipGetLastError();
 }
 

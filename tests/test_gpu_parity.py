@@ -489,6 +489,26 @@ def test_decode_256x16_16_steps(g):
     assert es <= TOL["bf16"]
 
 
+def test_decode_streamed_equals_cached(g):
+    """A state of 64 MiB or more is stepped with nontemporal loads and
+    stores, a smaller one through the caches: the 256 x 16 heads state
+    (256 MiB) in one call and the same sequences in calls of 32 (32 MiB
+    each) give the same outputs and states, bit for bit."""
+    c = gi.WORKLOADS["decode_256x16_d128"]
+    dd = gi.make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], "bf16", c["seed"] + 1, steps=3)
+    dev = {n: dd[n].cuda() for n in NAMES}
+    S_all, S_part = dd["S"].cuda(), dd["S"].cuda()
+    print("case decode streamed against cached", flush=True)
+    for t in range(3):
+        o_all = g.decode_step(*(dev[n][t] for n in NAMES), S_all)
+        o_part = torch.empty_like(o_all)
+        for n0 in range(0, c["N"], 32):
+            g.decode_step(*(dev[n][t][n0:n0 + 32] for n in NAMES), S_part[n0:n0 + 32], out=o_part[n0:n0 + 32])
+        torch.cuda.synchronize()
+        assert torch.equal(o_all, o_part), f"step {t}: outputs differ"
+    assert torch.equal(S_all, S_part)
+
+
 def test_decode_steps_equal_chunk_forward(g):
     """T decode steps on the GPU agree with one chunked forward on the GPU."""
     dd = gi.make_decode_inputs(2, 2, 64, 64, "f32", seed=50, steps=40)
