@@ -468,12 +468,9 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # the headline: K timed steps with the library's timing hooks off
-    sec = timed_steps(step, args.steps, args.warmup)
-    # the timed output against the oracle (every element of o and S_final)
-    o_gpu = o.float().cpu().numpy()
-    S_gpu = Sf.cpu().numpy()
-    # per-kernel durations in a separate pass: the library's HIP events
+    # per-kernel durations first, in passes of their own (so that the
+    # headline below is timed on the clocks a running workload holds: the
+    # first milliseconds of load after idle run about 9 % slower): the library's HIP events
     # around every launch (an event between the two kernels delays the next
     # launch, the prep's by about 15 %)
     g.profile_enable(True)
@@ -497,6 +494,12 @@ def main() -> int:
                 "chunk_scan": {"avg_us": scan_us, "launches": args.steps}}
         duration_method = ("HIP events on the launch stream around K steps and around K scan-only "
                            "runs on the filled workspace; prep = step - scan")
+
+    # the headline: W warm-up steps, then K timed steps, the library's timing hooks off
+    sec = timed_steps(step, args.steps, args.warmup)
+    # the timed output against the oracle (every element of o and S_final)
+    o_gpu = o.float().cpu().numpy()
+    S_gpu = Sf.cpu().numpy()
 
     tok_heads = B * T * H
     fl = flops_per_token_head(d, C) * tok_heads
