@@ -119,7 +119,8 @@ def test_segment_map_gate_modes(g, case):
     check_map(got, ref, TOL["bf16"], f"map {case}")
 
 
-@pytest.mark.parametrize("d,G,H", [(16, 5, 3), (64, 4, 2), (128, 6, 2)])
+@pytest.mark.parametrize("d,G,H", [(16, 5, 3), (64, 4, 2), (128, 6, 2), (128, 8, 3), (32, 16, 2), (64, 2, 5),
+                                   (16, 1, 2)])
 def test_segment_combine(g, d, G, H):
     rng = np.random.default_rng(700 + d)
     # maps of the size real segments give: Phi contracts, Psi of order one
