@@ -418,11 +418,9 @@ hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, boo
   s.S0 = nullptr;
   s.S_final = nullptr;
   s.o = nullptr;
-  if ((e = gdn2::launch_seg_bounds(a.cu, scu, sg.G, a.T, sg.N, C_rt, st)) != hipSuccess)
-    return e;
   {
-    prof_scope p("chunk_table", st);
-    if ((e = gdn2::launch_chunk_table(scu, nseg, C_rt, stab, st)) != hipSuccess)
+    prof_scope p("segment_bounds", st);  // and their chunk table
+    if ((e = gdn2::launch_seg_bounds(a.cu, scu, sg.G, a.T, sg.N, C_rt, st, stab)) != hipSuccess)
       return e;
   }
   if (!prepared) {
@@ -553,9 +551,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // ------------------------------------------------------------ segment maps --
 template <typename IO, int D, int C>
-hipError_t run_segmap(const gdn2::chunk_args &a, int C_rt, float *Phi, float *Psi, hipStream_t st) {
+hipError_t run_segmap(const gdn2::chunk_args &a, int C_rt, float *Phi, float *Psi, hipStream_t st,
+                      bool table_ready) {
   hipError_t e = hipSuccess;
-  if (a.cu) {
+  if (a.cu && !table_ready) {
     prof_scope p("chunk_table", st);
     e = gdn2::launch_chunk_table(a.cu, a.num_seqs, C_rt, a.offsets, st);
     if (e != hipSuccess)
@@ -572,10 +571,10 @@ hipError_t run_segmap(const gdn2::chunk_args &a, int C_rt, float *Phi, float *Ps
 }
 
 hipError_t dispatch_segmap(gdn2_dtype_t dt, int d, int c, const gdn2::chunk_args &a, float *Phi, float *Psi,
-                           hipStream_t st) {
+                           hipStream_t st, bool table_ready = false) {
 #define GDN2_RS(IO, D, C) \
   if (d == D && c == C)   \
-    return run_segmap<IO, D, C>(a, C, Phi, Psi, st);
+    return run_segmap<IO, D, C>(a, C, Phi, Psi, st, table_ready);
   if (dt == GDN2_F32) {
     GDN2_RS(float, 16, 16) GDN2_RS(float, 32, 16) GDN2_RS(float, 64, 16) GDN2_RS(float, 128, 16)
     GDN2_RS(float, 16, 64) GDN2_RS(float, 32, 64) GDN2_RS(float, 64, 64) GDN2_RS(float, 128, 64)
@@ -682,7 +681,11 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   float *Phi = reinterpret_cast<float *>(ws + pl.cu + pl.table + pl.blocks);
   float *Psi = Phi + pl.map_bytes / sizeof(float);
   float *S_in = Psi + pl.map_bytes / sizeof(float);
-  hipError_t e = gdn2::launch_seg_bounds(a.cu, cu, pl.G, a.T, x.N, chunk, st);
+  hipError_t e = hipSuccess;
+  {
+    prof_scope p("segment_bounds", st);  // and their chunk table
+    e = gdn2::launch_seg_bounds(a.cu, cu, pl.G, a.T, x.N, chunk, st, reinterpret_cast<int32_t *>(ws + pl.cu));
+  }
   if (e != hipSuccess)
     return e;
   gdn2::chunk_args s = a;
@@ -700,7 +703,7 @@ hipError_t run_segments(gdn2_dtype_t dt, int d, int chunk, const gdn2::chunk_arg
   // (no S_final: the last segment's own state scan gives it), then every
   // segment's state scan from its entering state
   s.seg_G = pl.G;
-  e = dispatch_segmap(dt, d, chunk, s, Phi, Psi, st);
+  e = dispatch_segmap(dt, d, chunk, s, Phi, Psi, st, true);
   if (e != hipSuccess)
     return e;
   e = dispatch_combine(d, Phi, Psi, a.S0, pl.G, a.H, x.N, S_in, nullptr, st);

@@ -88,7 +88,9 @@ template <typename IO, int D, int C> hipError_t launch_segmap(const chunk_args &
 // seg_cu[0 .. B G] = the bounds of G segments of whole chunks (C tokens) of
 // each of B sequences laid end to end: packed ones given by cu, else B
 // sequences of T tokens (cu == nullptr).
-hipError_t launch_seg_bounds(const int32_t *cu, int32_t *seg_cu, int G, int T, int B, int C, hipStream_t st);
+// (offsets: also the segments' chunk table, [B G + 1], or nullptr)
+hipError_t launch_seg_bounds(const int32_t *cu, int32_t *seg_cu, int G, int T, int B, int C, hipStream_t st,
+                             int32_t *offsets = nullptr);
 // Exclusive scan of the G segment maps of each of B sequences, [B, G, H, D, D],
 // from S0 [B, H, D, D] (nullptr: zero).  reverse: the backward's adjoint
 // scan (Phi transposed, segments from the last; see the kernel).
