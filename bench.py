@@ -776,6 +776,16 @@ def main() -> int:
         sec_train = timed_steps(train_step, bsteps, 2)
         fwd_into_wsb()
         sec_bp = timed_steps(bstep_prepared, bsteps, 2)
+
+        # the same with the states kept by the forward's scan (the backward
+        # skips its states scan too)
+        def train_step_kept():
+            g.chunk_fwd(*(dev[x] for x in NAMES), chunk=C, out=o_t, S_final=Sf_t, workspace=wsb, path="two_pass",
+                        keep_states=True)
+            g.chunk_bwd(*(dev[x] for x in NAMES), dout, chunk=C, workspace=wsb, out=gout, prepared=True,
+                        states_kept=True)
+
+        sec_train_kept = timed_steps(train_step_kept, bsteps, 2)
         bbyt = bwd_bytes_per_token_head(d, C)
         bdom = max(bkern, key=lambda k: bkern[k]["avg_us"])
         bach = bbyt[bdom] * tok_heads / (bkern[bdom]["avg_us"] * 1e-6) / 1e9
@@ -790,7 +800,8 @@ def main() -> int:
             "train_step": {"workload": "forward (two-pass) into the backward's workspace, then the backward "
                                        "with the forward's per-chunk blocks handed over",
                            "ms_per_step": round(sec_train * 1e3, 4),
-                           "tokens_per_s": round(B * T / sec_train, 1)},
+                           "tokens_per_s": round(B * T / sec_train, 1),
+                           "states_kept_ms_per_step": round(sec_train_kept * 1e3, 4)},
             "path_algorithmic_bytes": int(bbyt["path"] * tok_heads),
             "path_hbm_frac": round(bbyt["path"] * tok_heads / sec_b / 1e9 / HBM_PEAK_GBS, 4),
             "kernels": bkern,

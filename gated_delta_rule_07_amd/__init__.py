@@ -41,6 +41,7 @@ FLAG_SCALAR_ALPHA = 1 << 6
 FLAG_LAYER_PREP = 1 << 0
 FLAG_RULE_R1 = 1 << 7
 FLAG_PREPARED = 1 << 8
+FLAG_KEEP_STATES = 1 << 9
 PATHS = {"auto": 0, "recurrent": FLAG_RECURRENT, "two_pass": FLAG_TWO_PASS, "fused": FLAG_FUSED}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
@@ -170,14 +171,17 @@ def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int, chu
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
               recurrent: bool = False, out=None, S_final=None, workspace=None,
               want_final: bool = True, path: str = "auto", layer_prep: bool = False,
-              rule: str = "R5", prepared: bool = False):
+              rule: str = "R5", prepared: bool = False, keep_states: bool = False):
     """Chunked forward.  ``path`` selects the kernels: "auto" (the library
     chooses), "fused" (single pass), "two_pass", or "recurrent" (token by
     token; also selected by ``recurrent=True``).  ``rule="R1"`` runs the
     alternative reading R1 (two-pass or token-by-token path).  ``prepared=True``
     runs the state scan alone on a ``workspace`` that ``segment_map`` (or a
-    two-pass ``chunk_fwd``) filled for the same inputs.  Returns (o,
-    S_final); S_final is None when ``want_final`` is False."""
+    two-pass ``chunk_fwd``) filled for the same inputs.  ``keep_states=True``
+    (two-pass path) also writes the state entering every chunk into a
+    backward-sized ``workspace``, for ``chunk_bwd(..., prepared=True,
+    states_kept=True)``.  Returns (o, S_final); S_final is None when
+    ``want_final`` is False."""
     if recurrent:
         path = "recurrent"
     _require_device(q, k, v, alpha, b, w, S0, cu_seqlens)
@@ -213,7 +217,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, chunk: int = 64,
     if prepared and workspace is None:
         raise ValueError("prepared=True reads the given workspace")
     flags = (PATHS[path] | gate_flags | (FLAG_LAYER_PREP if layer_prep else 0) | (FLAG_RULE_R1 if rule == "R1" else 0)
-             | (FLAG_PREPARED if prepared else 0))
+             | (FLAG_PREPARED if prepared else 0) | (FLAG_KEEP_STATES if keep_states else 0))
     ws_bytes = 0
     if path != "recurrent":
         ws_bytes = workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, chunk, q.dtype, flags)
@@ -238,7 +242,7 @@ def bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int,
 
 def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
               chunk: int = 64, workspace=None, out=None, want_dS0: bool = True,
-              layer_prep: bool = False, prepared: bool = False):
+              layer_prep: bool = False, prepared: bool = False, states_kept: bool = False):
     """Chunked backward of ``chunk_fwd``, for the same input modes (b, w,
     alpha per channel or [B, T, H]; ``layer_prep`` for the raw layer
     inputs).  Given dL/do (``dout``, like o) and dL/dS_final (or None for
@@ -248,7 +252,8 @@ def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=Non
     may hold preallocated tensors under those names.  ``prepared=True``
     takes the per-chunk blocks a ``chunk_fwd(..., path="two_pass")`` left in
     ``workspace`` (a backward-sized workspace, same inputs) instead of
-    recomputing them."""
+    recomputing them; with ``states_kept=True`` as well, the states that a
+    ``chunk_fwd(..., keep_states=True)`` kept there too."""
     _require_device(q, k, v, alpha, b, w, dout, S0, dS_final, cu_seqlens)
     dt = _dtype_code(q)
     for t in (k, v, b, w, dout) + (() if layer_prep else (alpha,)):
@@ -262,7 +267,7 @@ def chunk_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=Non
         if tuple(t.shape) != (B, T, H, full):
             raise ValueError(f"{name} must be [{B}, {T}, {H}, {full}]")
     flags = (_gate_flags(q, v, alpha, b, w) | (FLAG_LAYER_PREP if layer_prep else 0)
-             | (FLAG_PREPARED if prepared else 0))
+             | (FLAG_PREPARED if prepared else 0) | (FLAG_KEEP_STATES if states_kept else 0))
     if prepared and workspace is None:
         raise ValueError("prepared=True reads the given workspace")
     if cu_seqlens is not None:

@@ -197,7 +197,8 @@ hipError_t run_chunk(const gdn2::chunk_args &a, int C_rt, uint32_t flags, hipStr
   }
   {
     prof_scope p("chunk_scan", st);
-    e = gdn2::launch_chunk_scan<IO, D, C>(a, st);
+    e = (flags & GDN2_FLAG_KEEP_STATES) ? gdn2::launch_chunk_scan_keep<IO, D, C>(a, st)
+                                        : gdn2::launch_chunk_scan<IO, D, C>(a, st);
   }
   return e;
 }
@@ -398,8 +399,11 @@ struct seg_run {
 //     outputs; the adjoint scan X(g - 1) = Phi_g^T X(g) + Psi'_g from
 //     dL/dS_final gives the gradient after every segment (and dL/dS0); the
 //     reverse scan of every segment from X(g) writes the final gradients.
+// kept: a.states already holds the entering states (a forward's kept
+// states); the maps are still needed for the state gradients
 template <typename IO, int D, int C>
-hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, bool prepared, hipStream_t st) {
+hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, bool prepared, bool kept,
+                            hipStream_t st) {
   hipError_t e = hipSuccess;
   const gdn2::chunk_args &a = ba.f;
   const int nseg = sg.N * sg.G;
@@ -433,13 +437,14 @@ hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, boo
     if ((e = gdn2::launch_segmap<IO, D, C>(s, Phi, Psi, st)) != hipSuccess)
       return e;
   }
-  {
-    prof_scope p("segment_combine", st);
-    if ((e = gdn2::launch_seg_combine<D>(Phi, Psi, a.S0, sg.G, a.H, sg.N, S_in, nullptr, st, false)) != hipSuccess)
-      return e;
-  }
-  s.S0 = S_in;
-  {
+  if (!kept) {
+    {
+      prof_scope p("segment_combine", st);
+      if ((e = gdn2::launch_seg_combine<D>(Phi, Psi, a.S0, sg.G, a.H, sg.N, S_in, nullptr, st, false)) !=
+          hipSuccess)
+        return e;
+    }
+    s.S0 = S_in;
     prof_scope p("chunk_states", st);
     if ((e = gdn2::launch_chunk_states<IO, D, C>(s, st)) != hipSuccess)
       return e;
@@ -465,7 +470,7 @@ hipError_t run_bwd_segments(gdn2::bwd_args &ba, int C_rt, const seg_run &sg, boo
 }
 
 template <typename IO, int D, int C>
-hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, bool prepared, hipStream_t st) {
+hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, bool prepared, bool kept, hipStream_t st) {
   hipError_t e = hipSuccess;
   gdn2::chunk_args &a = ba.f;
   if (a.cu) {
@@ -475,7 +480,7 @@ hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, bool prepare
       return e;
   }
   if (sg) {
-    if ((e = run_bwd_segments<IO, D, C>(ba, C_rt, *sg, prepared, st)) != hipSuccess)
+    if ((e = run_bwd_segments<IO, D, C>(ba, C_rt, *sg, prepared, kept, st)) != hipSuccess)
       return e;
     prof_scope p("bwd_grad", st);
     return gdn2::launch_bwd_grad<IO, D, C>(ba, st);
@@ -487,7 +492,7 @@ hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, bool prepare
       if (e != hipSuccess)
         return e;
     }
-    {
+    if (!kept) {
       prof_scope p("chunk_states", st);
       e = gdn2::launch_chunk_states<IO, D, C>(a, st);
       if (e != hipSuccess)
@@ -508,10 +513,10 @@ hipError_t run_bwd(gdn2::bwd_args &ba, int C_rt, const seg_run *sg, bool prepare
 }
 
 hipError_t dispatch_bwd(gdn2_dtype_t dt, int d, int c, gdn2::bwd_args &ba, const seg_run *sg, bool prepared,
-                        hipStream_t st) {
+                        bool kept, hipStream_t st) {
 #define GDN2_RB(IO, D, C) \
   if (d == D && c == C)   \
-    return run_bwd<IO, D, C>(ba, C, sg, prepared, st);
+    return run_bwd<IO, D, C>(ba, C, sg, prepared, kept, st);
   if (dt == GDN2_F32) {
     GDN2_RB(float, 16, 16) GDN2_RB(float, 32, 16) GDN2_RB(float, 64, 16) GDN2_RB(float, 128, 16)
     GDN2_RB(float, 16, 64) GDN2_RB(float, 32, 64) GDN2_RB(float, 64, 64) GDN2_RB(float, 128, 64)
@@ -789,6 +794,8 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
 
 size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv, int num_seqs, int chunk,
                                             gdn2_dtype_t dt, uint32_t flags) {
+  if ((flags & GDN2_FLAG_KEEP_STATES) && !(flags & GDN2_FLAG_RECURRENT))
+    return dk == dv ? gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, chunk, dt) : 0;
   if ((flags & GDN2_FLAG_RULE_R1) && !(flags & GDN2_FLAG_RECURRENT) && dk != dv) {
     if (!supported_dim(dk) || !supported_dim(dv))
       return 0;
@@ -826,8 +833,17 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: unknown dtype %d", static_cast<int>(dt));
   const uint32_t path_flags = GDN2_FLAG_RECURRENT | GDN2_FLAG_TWO_PASS | GDN2_FLAG_FUSED;
   const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
-  if (flags & ~(path_flags | gate_flags | GDN2_FLAG_RULE_R1 | GDN2_FLAG_PREPARED))
+  if (flags & ~(path_flags | gate_flags | GDN2_FLAG_RULE_R1 | GDN2_FLAG_PREPARED | GDN2_FLAG_KEEP_STATES))
     return fail(GDN2_ERR_INVALID_ARGUMENT, "gdn2_chunk_fwd: unknown flags 0x%x", flags);
+  const bool keep = (flags & GDN2_FLAG_KEEP_STATES) != 0;
+  if (keep) {
+    if (flags & (GDN2_FLAG_RECURRENT | GDN2_FLAG_FUSED | GDN2_FLAG_RULE_R1))
+      return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: states are kept by the two-pass path of rule R5 only");
+    if (dk != dv)
+      return fail(GDN2_ERR_UNSUPPORTED,
+                  "gdn2_chunk_fwd: GDN2_FLAG_KEEP_STATES needs dk == dv (the backward's workspace layout)");
+    flags |= GDN2_FLAG_TWO_PASS;
+  }
   if (flags & GDN2_FLAG_PREPARED) {
     if (flags & (GDN2_FLAG_RECURRENT | GDN2_FLAG_FUSED))
       return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_fwd: a prepared workspace is read by the two-pass path only");
@@ -953,6 +969,13 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
                 "gdn2_chunk_fwd: workspace of %zu bytes is smaller than the %zu needed",
                 workspace_bytes, need_exact);
+  // kept states go where the backward keeps its states (after the table and
+  // the blocks, which sit where the forward puts them)
+  const bwd_plan kp = keep ? plan_bwd(dt, B, T, H, dk, N, chunk, packed) : bwd_plan{};
+  if (keep && (workspace_bytes < kp.table + kp.blocks + kp.states || !workspace))
+    return fail(GDN2_ERR_WORKSPACE_TOO_SMALL,
+                "gdn2_chunk_fwd: workspace of %zu bytes is smaller than the %zu needed to keep the states",
+                workspace_bytes, kp.table + kp.blocks + kp.states);
 
   gdn2::chunk_args a{};
   a.q = q;
@@ -983,6 +1006,8 @@ gdn2_status_t gdn2_chunk_fwd(const void *q, const void *k, const void *v, const 
     a.offsets = nullptr;
     a.blocks = ws;
   }
+  if (keep)
+    a.states = ws + kp.table + kp.blocks;
   if (T == 0) {
     // no tokens: the scan kernel alone copies S0 (or zeros) to S_final
     a.num_slots = 0;
@@ -1043,11 +1068,15 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
   if (dt != GDN2_F32 && dt != GDN2_BF16)
     return fail(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_bwd: unknown dtype %d", static_cast<int>(dt));
   const uint32_t gate_flags = GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_ALPHA | GDN2_FLAG_LAYER_PREP;
-  if (flags & ~(gate_flags | GDN2_FLAG_PREPARED))
+  if (flags & ~(gate_flags | GDN2_FLAG_PREPARED | GDN2_FLAG_KEEP_STATES))
     return fail(GDN2_ERR_UNSUPPORTED,
-                "gdn2_chunk_bwd: flags 0x%x: only the gate layout, layer prep and prepared-workspace flags apply "
-                "to the backward",
+                "gdn2_chunk_bwd: flags 0x%x: only the gate layout, layer prep, prepared-workspace and kept-states "
+                "flags apply to the backward",
                 flags);
+  if ((flags & GDN2_FLAG_KEEP_STATES) && !(flags & GDN2_FLAG_PREPARED))
+    return fail(GDN2_ERR_UNSUPPORTED,
+                "gdn2_chunk_bwd: GDN2_FLAG_KEEP_STATES comes with GDN2_FLAG_PREPARED (the forward's blocks and "
+                "states)");
   if ((flags & GDN2_FLAG_PREPARED) && dk != dv)
     return fail(GDN2_ERR_UNSUPPORTED,
                 "gdn2_chunk_bwd: GDN2_FLAG_PREPARED needs dk == dv (the widened call lays its workspace out "
@@ -1213,7 +1242,8 @@ gdn2_status_t gdn2_chunk_bwd(const void *q, const void *k, const void *v, const 
     }
   }
   const hipError_t e =
-      dispatch_bwd(dt, dk, chunk, ba, sgp, (flags & GDN2_FLAG_PREPARED) != 0, static_cast<hipStream_t>(stream));
+      dispatch_bwd(dt, dk, chunk, ba, sgp, (flags & GDN2_FLAG_PREPARED) != 0,
+                   (flags & GDN2_FLAG_KEEP_STATES) != 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN2_ERR_HIP, "gdn2_chunk_bwd: launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -168,11 +168,16 @@ template <typename IO, int D, int C, int NT, bool R1 = false, bool ST = false> s
 // With ST (states mode, used by the backward) the kernel writes, instead of
 // o, the state entering every chunk to a.states (chunk slot order, one
 // state_tiles block per chunk-head: fragment tiles of the I/O type).
+// With WS (keep states) the forward scan also writes the state entering
+// every chunk to a.states, as the states mode does, next to o: a training
+// step's forward hands them to the backward.  The state entering chunk
+// c + 1 is stored right after chunk c's update, where the output's
+// registers are dead (before the chunk it would raise the register peak).
 // With R1 it scans the blocks of rule R1 (r1_layout): O starts from the
 // stored O'' instead of P Ut, and the update adds the chunk's N tiles, which
 // each compute wave reads from the block at the start of the chunk:
 //   Z = -Ut' - W' S,  O = Q'' S + O'',  S <- Diag(gamma_C) S + Ebar^T Z + N.
-template <typename IO, int D, int C, int NT, bool ST = false, bool R1 = false>
+template <typename IO, int D, int C, int NT, bool ST = false, bool R1 = false, bool WS = false>
 __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1, ST>::NCW + scan_cfg<IO, D, C, NT, R1, ST>::NLW))
     gdn2_chunk_scan_kernel(chunk_args a) {
   typedef scan_cfg<IO, D, C, NT, R1, ST> K;
@@ -622,10 +627,28 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1, ST>::NCW + sc
     }
   };
 
+  // WS: the state entering chunk c (slot c_begin + c) as state_tiles
+  auto keep_state = [&](int c) {
+    if constexpr (WS) {
+      typedef state_tiles<IO, D> ST_;
+      unsigned char *sp =
+          reinterpret_cast<unsigned char *>(a.states) + (static_cast<size_t>(c_begin + c) * a.H + h) * ST_::BYTES;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          const F sc = F::from(S[kk][j]);  // ColFrag(S tile (kk, vt0 + j))
+          sc.st(sp + ST_::COL + ST_::off(kk, vt0 + j), lane);
+          if constexpr (ST_::HAS_ROW)
+            F::from(transpose_io(sc, eye, lane)).st(sp + ST_::ROW + ST_::off(kk, vt0 + j), lane);
+        }
+    }
+  };
   if (nchunks > 0) {
     F ucur[NB][CPW];
     if constexpr (!K::UO_LDS)
       tload(0, ucur);
+    keep_state(0);
     lds_barrier();  // chunk 0 is in buffer 0
     for (int c = 0; c < nchunks; ++c) {
       const unsigned char *sb = sbuf[c % NBUF];
@@ -638,6 +661,8 @@ __global__ void __launch_bounds__(64 * (scan_cfg<IO, D, C, NT, R1, ST>::NCW + sc
         chunk_step(sb, ucur, t0, len, c, std::true_type{});
       else
         chunk_step(sb, ucur, t0, len, c, std::false_type{});
+      if (c + 1 < nchunks)
+        keep_state(c + 1);
       if constexpr (NBUF == 1)
         lds_barrier();  // done with the only buffer
       lds_barrier();    // chunk c + 1 is in LDS
@@ -714,12 +739,12 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
   return hipGetLastError();
 }
 
-template <typename IO, int D, int C, int NT, bool ST, bool R1 = false>
+template <typename IO, int D, int C, int NT, bool ST, bool R1 = false, bool WS = false>
 hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
   typedef scan_cfg<IO, D, C, NT, R1, ST> K;
   const int units = a.num_seqs * a.H;
   const int units_pad = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT, ST, R1>), dim3(units_pad * K::NGRP),
+  hipLaunchKernelGGL((gdn2_chunk_scan_kernel<IO, D, C, NT, ST, R1, WS>), dim3(units_pad * K::NGRP),
                      dim3(64 * (K::NCW + K::NLW)), 0, st, a);
   return hipGetLastError();
 }
@@ -730,22 +755,22 @@ hipError_t launch_scan_nt(const chunk_args &a, hipStream_t st) {
 // sequential per-chunk path; many units get 4 tiles per workgroup.
 // float32 inputs with d = 128, C = 64 keep one tile per workgroup: their
 // wider fragments would not fit in the registers of the larger workgroups.
-template <typename IO, int D, int C, bool ST, bool R1 = false>
+template <typename IO, int D, int C, bool ST, bool R1 = false, bool WS = false>
 hipError_t launch_scan_any(const chunk_args &a, hipStream_t st) {
   constexpr int NK = D / 16;
   const long units = static_cast<long>(a.num_seqs) * a.H;
   if constexpr (sizeof(IO) == 4 && D * C >= 128 * 64) {
-    return launch_scan_nt<IO, D, C, 1, ST, R1>(a, st);
+    return launch_scan_nt<IO, D, C, 1, ST, R1, WS>(a, st);
   } else {
     if (units * NK <= 256)
-      return launch_scan_nt<IO, D, C, 1, ST, R1>(a, st);
+      return launch_scan_nt<IO, D, C, 1, ST, R1, WS>(a, st);
     if constexpr (NK >= 2) {
       if (NK < 4 || units * (NK / 2) <= 256)
-        return launch_scan_nt<IO, D, C, 2, ST, R1>(a, st);
+        return launch_scan_nt<IO, D, C, 2, ST, R1, WS>(a, st);
     }
     if constexpr (NK >= 4)
-      return launch_scan_nt<IO, D, C, 4, ST, R1>(a, st);
-    return launch_scan_nt<IO, D, C, 1, ST, R1>(a, st);
+      return launch_scan_nt<IO, D, C, 4, ST, R1, WS>(a, st);
+    return launch_scan_nt<IO, D, C, 1, ST, R1, WS>(a, st);
   }
 }
 
@@ -755,6 +780,10 @@ template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_ar
 
 template <typename IO, int D, int C> hipError_t launch_chunk_states(const chunk_args &a, hipStream_t st) {
   return launch_scan_any<IO, D, C, true>(a, st);
+}
+
+template <typename IO, int D, int C> hipError_t launch_chunk_scan_keep(const chunk_args &a, hipStream_t st) {
+  return launch_scan_any<IO, D, C, false, false, true>(a, st);
 }
 
 template <typename IO, int D, int C> hipError_t launch_chunk_scan_r1(const chunk_args &a, hipStream_t st) {
@@ -774,6 +803,7 @@ hipError_t launch_chunk_table(const int32_t *cu, int N, int C, int32_t *offsets,
   template hipError_t launch_chunk_prep<IO, D, C>(const chunk_args &, hipStream_t);         \
   template hipError_t launch_chunk_scan<IO, D, C>(const chunk_args &, hipStream_t);        \
   template hipError_t launch_chunk_states<IO, D, C>(const chunk_args &, hipStream_t);       \
+  template hipError_t launch_chunk_scan_keep<IO, D, C>(const chunk_args &, hipStream_t);    \
   template hipError_t launch_chunk_scan_r1<IO, D, C>(const chunk_args &, hipStream_t);
 
 GDN2_INST_CHUNK(float, 16, 16)

@@ -46,6 +46,9 @@ template <typename IO, int D, int C> hipError_t launch_chunk_prep(const chunk_ar
 template <typename IO, int D, int C> hipError_t launch_chunk_scan(const chunk_args &a, hipStream_t st);
 // the state scan in states mode: a.states instead of o (o is not written)
 template <typename IO, int D, int C> hipError_t launch_chunk_states(const chunk_args &a, hipStream_t st);
+// the forward scan that also writes the states-mode output (a.states): o,
+// S_final and the state entering every chunk
+template <typename IO, int D, int C> hipError_t launch_chunk_scan_keep(const chunk_args &a, hipStream_t st);
 // rule R1's state scan on the scan kernel above (bfloat16, even numbers of
 // 16-wide tiles in D and C; otherwise hipErrorNotSupported)
 template <typename IO, int D, int C> constexpr bool scan_r1_supported() {

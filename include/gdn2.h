@@ -155,6 +155,24 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1, GDN2_DTYPE_MAX_ENUM = 0x7FFFFFFF } g
  * q .. w for the gradients).  The results are those of the backward without
  * the flag, bit for bit.  Any other contents give undefined outputs. */
 #define GDN2_FLAG_PREPARED (1u << 8)
+/* Kept states, for a training step (dk == dv, two-pass path only; implies
+ * GDN2_FLAG_TWO_PASS; GDN2_ERR_UNSUPPORTED with GDN2_FLAG_RECURRENT,
+ * GDN2_FLAG_FUSED, GDN2_FLAG_RULE_R1 or dk != dv).  gdn2_chunk_fwd's state
+ * scan then also writes the state entering every chunk (the state the
+ * chunked recurrence carries between chunks: aixai.ru blog, section on how
+ * it is implemented in practice) into the workspace, where the backward
+ * keeps its states; the workspace must then hold at least
+ * gdn2_chunk_fwd_workspace_bytes_flags(..., flags) bytes (the backward's
+ * size), and the segment schedule is not taken.  gdn2_chunk_bwd takes the
+ * flag together with GDN2_FLAG_PREPARED (GDN2_ERR_UNSUPPORTED alone): the
+ * workspace holds the blocks and states of such a forward on the same
+ * inputs, S0, sizes and gate flags, and the backward skips its states scan
+ * too.  For shapes where the backward takes the segment schedule it still
+ * computes the segment maps (for the state gradients) but not the states;
+ * there the kept states (one scan) differ from the segment schedule's in
+ * rounding only.  At every other shape the gradients are those of the
+ * backward without the flags, bit for bit. */
+#define GDN2_FLAG_KEEP_STATES (1u << 9)
 
 /* Size limits of every chunked entry point (gdn2_chunk_fwd, its
  * allocation-free variant, gdn2_chunk_bwd, gdn2_chunk_segment_map): at most
@@ -174,8 +192,10 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
                                       int chunk, gdn2_dtype_t dt);
 
 /* The same for a given set of gdn2_chunk_fwd flags: with GDN2_FLAG_RULE_R1
- * on the chunked path the per-chunk blocks are larger; for every other set
- * of flags it equals gdn2_chunk_fwd_workspace_bytes. */
+ * on the chunked path the per-chunk blocks are larger; with
+ * GDN2_FLAG_KEEP_STATES it is gdn2_chunk_bwd_workspace_bytes (0 when
+ * dk != dv); for every other set of flags it equals
+ * gdn2_chunk_fwd_workspace_bytes. */
 size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv, int num_seqs,
                                             int chunk, gdn2_dtype_t dt, uint32_t flags);
 
@@ -191,8 +211,9 @@ size_t gdn2_chunk_fwd_workspace_bytes_flags(int B, int T, int H, int dk, int dv,
  *               sequence boundary.
  *   B, T, H, dk, dv, num_seqs, chunk, dt : sizes; chunk is the chunk length.
  *   flags     : at most one of GDN2_FLAG_RECURRENT, GDN2_FLAG_TWO_PASS,
- *               GDN2_FLAG_FUSED, plus any of the gate layout flags, and
- *               GDN2_FLAG_PREPARED (two-pass path implied).  With no
+ *               GDN2_FLAG_FUSED, plus any of the gate layout flags,
+ *               GDN2_FLAG_PREPARED and GDN2_FLAG_KEEP_STATES (both imply
+ *               the two-pass path).  With no
  *               path flag the library runs the two-pass chunked kernels (all
  *               chunks in parallel, then the state scan).  For N
  *               sequences (B, or num_seqs packed) of at least 128 chunks (on
@@ -273,10 +294,12 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *   q .. cu_seqlens, B .. dt : the forward's inputs and sizes.
  *   flags     : GDN2_FLAG_SCALAR_B / _W / _ALPHA and GDN2_FLAG_LAYER_PREP,
  *               with the forward's meaning (inputs given per (token, head),
- *               or the raw layer inputs), and GDN2_FLAG_PREPARED (the
+ *               or the raw layer inputs), GDN2_FLAG_PREPARED (the
  *               workspace's front holds the forward's per-chunk blocks, see
- *               that flag; GDN2_ERR_UNSUPPORTED when dk != dv); the path and
- *               rule flags return GDN2_ERR_UNSUPPORTED.
+ *               that flag; GDN2_ERR_UNSUPPORTED when dk != dv) and, with it,
+ *               GDN2_FLAG_KEEP_STATES (the workspace also holds the
+ *               forward's kept states); the path and rule flags return
+ *               GDN2_ERR_UNSUPPORTED.
  *   dout      : dL/do [B, T, H, dv], element type dt.
  *   dS_final  : dL/dS_final [N, H, dk, dv] float32, or NULL for zero.
  *   dq, dk_out, dv_out, dalpha, db, dw : outputs, the gradients with respect

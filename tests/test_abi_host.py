@@ -67,7 +67,13 @@ def test_fwd_rejects_before_launch(L):
     assert call_fwd(L, dt=7) == 2
     assert call_fwd(L, B=0) == 1
     assert call_fwd(L, T=-1) == 1
-    assert call_fwd(L, flags=1 << 9) == 1          # unknown flag
+    assert call_fwd(L, flags=1 << 10) == 1         # unknown flag
+    # kept states: two-pass path of rule R5, square heads, backward-sized workspace
+    for other in (1 << 1, 1 << 3, 1 << 7):
+        assert call_fwd(L, flags=(1 << 9) | other) == 2
+    assert call_fwd(L, flags=1 << 9, dk=16, dv=32) == 2
+    fwd_ws = L.gdn2_chunk_fwd_workspace_bytes(1, 64, 1, 16, 16, 0, 16, F32)
+    assert call_fwd(L, flags=1 << 9, ws_bytes=fwd_ws) == 3   # room for the blocks, not the states
     assert call_fwd(L, flags=(1 << 8) | (1 << 1)) == 2         # prepared workspace on the token-by-token path
     assert call_fwd(L, flags=(1 << 8) | (1 << 3)) == 2         # prepared workspace on the single-pass path
     assert call_fwd(L, flags=1 << 8, ws_bytes=100) == 3        # a prepared workspace is still size-checked
@@ -182,9 +188,11 @@ def test_bwd_rejects_before_launch(L):
     assert call_bwd(L, dt=7) == 2
     assert call_bwd(L, B=0) == 1
     assert call_bwd(L, T=-1) == 1
-    # the backward takes no forward path or rule flag
-    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 9):
+    # the backward takes no forward path or rule flag, nor kept states
+    # without the forward's blocks
+    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 9, 1 << 10):
         assert call_bwd(L, flags=flag) == 2
+    assert call_bwd(L, flags=(1 << 8) | (1 << 9), ws_bytes=16) == 3
     # the forward's blocks handed over: square heads only, still size-checked
     assert call_bwd(L, flags=1 << 8, dk=16, dv=32) == 2
     assert call_bwd(L, flags=1 << 8, ws_bytes=16) == 3
@@ -222,7 +230,7 @@ def test_segment_map_rejects_before_launch(L):
     assert call_segmap(L, B=0) == 1
     assert call_segmap(L, T=-1) == 1
     # path and rule flags do not apply to the map
-    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 8):
+    for flag in (1 << 1, 1 << 2, 1 << 3, 1 << 7, 1 << 8, 1 << 9):
         assert call_segmap(L, flags=flag) == 2
     assert call_segmap(L, phi=None) == 1
     assert call_segmap(L, psi=0x10004) == 1      # misaligned
@@ -326,3 +334,13 @@ def test_workspace_bytes_rectangular_heads(L):
             assert fb(B, T, H, dk, dv, n, C, dt) == sqb + (8 if dk < d else 5) * slot + 3 * state
     assert f(2, 64, 2, 16, 48, 0, 64, BF16) == 0
     assert fb(2, 64, 2, 16, 48, 0, 64, BF16) == 0
+
+
+def test_keep_states_workspace_bytes(L):
+    """With kept states the forward needs the backward's workspace (square
+    heads only)."""
+    f = L.gdn2_chunk_fwd_workspace_bytes_flags
+    f.restype = ctypes.c_size_t
+    for args in ((2, 200, 3, 64, 64, 0, 64, BF16), (1, 300, 2, 32, 32, 3, 16, F32)):
+        assert f(*args, 1 << 9) == L.gdn2_chunk_bwd_workspace_bytes(*args) > L.gdn2_chunk_fwd_workspace_bytes(*args)
+    assert f(2, 200, 3, 64, 32, 0, 64, BF16, 1 << 9) == 0

@@ -301,12 +301,19 @@ PREPARED_CASES = [  # dtype, d, chunk, B, T, H, packed lengths (or None), gate l
 ]
 
 
+@pytest.mark.parametrize("kept", [False, True], ids=["blocks", "blocks+states"])
 @pytest.mark.parametrize("dtype,d,chunk,B,T,H,lens,gates", PREPARED_CASES)
-def test_bwd_prepared_from_forward(g, dtype, d, chunk, B, T, H, lens, gates):
+def test_bwd_prepared_from_forward(g, dtype, d, chunk, B, T, H, lens, gates, kept):
     """A training step's forward (two-pass path) into the backward's own
-    workspace, then the backward with the forward's blocks handed over: the
-    gradients and dS0 equal, bit for bit, those of the backward that
-    recomputes the blocks, and the forward's output is the plain forward's."""
+    workspace, then the backward with the forward's blocks handed over (and,
+    with ``kept``, the states the forward kept): the gradients and dS0 equal,
+    bit for bit, those of the backward that recomputes them, and the
+    forward's output is the plain forward's.  Where the backward takes the
+    segment schedule (one or two long sequences) its own states come from
+    the segment maps, so the kept states (one scan) agree with them up to
+    rounding only: there the gradients are compared to 1e-2 of their
+    largest magnitude (bfloat16 outputs, 2^-8 relative rounding, can flip
+    by one unit)."""
     seed = 700 + d + H
     cu = None
     if lens is not None:
@@ -317,8 +324,8 @@ def test_bwd_prepared_from_forward(g, dtype, d, chunk, B, T, H, lens, gates):
                                **({"num_seqs": N} if lens is not None else {}))
     grads = gi.make_bwd_grads(B, T, H, d, d, dtype, seed, with_dS=True,
                               **({"num_seqs": N} if lens is not None else {}))
-    print(f"prepared case {dtype} d={d} C={chunk} B={B} T={T} H={H} packed={lens is not None} gates={gates}",
-          flush=True)
+    print(f"prepared case {dtype} d={d} C={chunk} B={B} T={T} H={H} packed={lens is not None} gates={gates} "
+          f"kept={kept}", flush=True)
     dev = {n: inp[n].cuda() for n in NAMES}
     if gates == "kda":
         beta = dev["b"][..., 0].contiguous()
@@ -336,9 +343,16 @@ def test_bwd_prepared_from_forward(g, dtype, d, chunk, B, T, H, lens, gates):
     ref = {k: v.clone() for k, v in ref.items() if v is not None}
     o_plain, Sf_plain = g.chunk_fwd(*args, S0=S0, cu_seqlens=cud, chunk=chunk, path="two_pass")
     ws.fill_(0xA5)  # the hand-over must not depend on what was there before the forward
-    o, Sf = g.chunk_fwd(*args, S0=S0, cu_seqlens=cud, chunk=chunk, path="two_pass", workspace=ws)
-    got = g.chunk_bwd(*args, dout, S0=S0, dS_final=dSf, cu_seqlens=cud, chunk=chunk, workspace=ws, prepared=True)
+    o, Sf = g.chunk_fwd(*args, S0=S0, cu_seqlens=cud, chunk=chunk, path="two_pass", workspace=ws,
+                        keep_states=kept)
+    got = g.chunk_bwd(*args, dout, S0=S0, dS_final=dSf, cu_seqlens=cud, chunk=chunk, workspace=ws, prepared=True,
+                      states_kept=kept)
     torch.cuda.synchronize()
     assert torch.equal(o, o_plain) and torch.equal(Sf, Sf_plain)
+    segment_shape = N * H <= 32 and (T if lens is None else T // N) >= 128 * chunk
     for name, x in ref.items():
-        assert torch.equal(got[name], x), f"{name} differs from the recomputing backward"
+        if kept and segment_shape:
+            err = (got[name].float() - x.float()).abs().max().item()
+            assert err <= 1e-2 * x.float().abs().max().item() + 1e-6, f"{name}: {err}"
+        else:
+            assert torch.equal(got[name], x), f"{name} differs from the recomputing backward"

@@ -107,15 +107,16 @@ def test_chunk_forward_in_a_graph(g, packed):
         assert torch.equal(o_g, o_e) and torch.equal(Sf_g, Sf_e), f"replay {r} differs"
 
 
-def test_training_step_in_a_graph(g):
+@pytest.mark.parametrize("kept", [False, True])
+def test_training_step_in_a_graph(g, kept):
     """Forward (two-pass) into the backward's workspace, then the backward on
-    the forward's blocks: one graph."""
+    the forward's blocks (and, with ``kept``, its kept states): one graph."""
     B, T, H, d, C = 2, 300, 3, 128, 64
     inp = gi.make_chunk_inputs(B, T, H, d, d, "bf16", seed=80, s0="normal")
     grads = gi.make_bwd_grads(B, T, H, d, d, "bf16", seed=80, with_dS=True)
     x = [inp[n].cuda() for n in NAMES]
     S0, dout, dSf = inp["S0"].cuda(), grads["dout"].cuda(), grads["dS_final"].cuda()
-    print(f"graph training step B={B} T={T} H={H} d={d}", flush=True)
+    print(f"graph training step B={B} T={T} H={H} d={d} kept={kept}", flush=True)
     ws = torch.empty(g.bwd_workspace_bytes(B, T, H, d, d, 0, C, torch.bfloat16), dtype=torch.uint8, device="cuda")
 
     o_e, Sf_e = g.chunk_fwd(*x, S0=S0, chunk=C)
@@ -127,8 +128,9 @@ def test_training_step_in_a_graph(g):
     gout = {k: torch.empty_like(v) for k, v in ref.items()}
 
     def step():
-        g.chunk_fwd(*x, S0=S0, chunk=C, out=o_g, S_final=Sf_g, workspace=ws, path="two_pass")
-        g.chunk_bwd(*x, dout, S0=S0, dS_final=dSf, chunk=C, workspace=ws, out=gout, prepared=True)
+        g.chunk_fwd(*x, S0=S0, chunk=C, out=o_g, S_final=Sf_g, workspace=ws, path="two_pass", keep_states=kept)
+        g.chunk_bwd(*x, dout, S0=S0, dS_final=dSf, chunk=C, workspace=ws, out=gout, prepared=True,
+                    states_kept=kept)
 
     gr = capture(step)
     for r in range(REPLAYS):
