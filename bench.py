@@ -208,7 +208,22 @@ def host_info() -> dict:
     name = p.name or f"{arch.split(':')[0]} (no marketing-name table on this host)"
     return {"cpu_model": cpu, "host_cpus": os.cpu_count(), "gpu_name": name,
             "gpu_arch": arch, "compute_units": p.multi_processor_count,
-            "gpu_memory_gib": round(p.total_memory / 2**30, 1)}
+            "gpu_memory_gib": round(p.total_memory / 2**30, 1), "gpu_clocks": gpu_clocks()}
+
+
+def gpu_clocks():
+    """The current clock levels rocm-smi reports for the first GPU (read
+    once, right after the headline's timed steps, while the clocks are
+    still up), or None when it cannot tell."""
+    import json
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
+        cards = json.loads(r.stdout)
+        card = cards[sorted(cards)[0]]
+        return {k.strip(" :"): v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
+    except Exception:  # absent tool, other output format: the line carries None
+        return None
 
 
 def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
